@@ -1,0 +1,144 @@
+"""Gated delta-rule linear attention on AMD Instinct MI355X (gfx950).
+
+Thin Python binding over libgdr.so (include/gdr.h).  PyTorch only provides device memory and
+the current stream; every step of the computation runs in the library's HIP kernels.  If the
+library is missing, every call raises: there is no CPU or eager fallback.
+
+    o, S_T = chunk_fwd(q, k, v, log_alpha, b, w, S0)      # prefill over T tokens
+    o = decode_step(q, k, v, log_alpha, b, w, S)           # one token, S updated in place
+
+Layouts: q, k [B,T,H,dk]; v [B,T,H,dv]; gates [B,T,H] (one value per token and head) or
+[B,T,H,dk] / [B,T,H,dv] (per channel) or None; states [B,H,dk,dv] float32.  q, k, v and the
+gates share one dtype, bfloat16 or float32.  The recurrence:
+
+    S_t = Diag(exp(log_alpha_t)) (I - k_t^T (b_t . k_t)) S_{t-1} + k_t^T (w_t . v_t)
+    o_t = q_t S_t
+
+("Recurrent Memory: Write, Erase, Decay, Read", section 05, with the Gated DeltaNet-2
+channel-wise erase and write gates).  ``order="decay_then_erase"`` applies the decay before the
+erase instead.
+"""
+from . import _native
+from ._native import GdrError, abi_version, make_problem, status_string
+
+__all__ = ["chunk_fwd", "decode_step", "abi_version", "status_string", "GdrError", "make_problem"]
+
+_ORDERS = {"erase_then_decay": _native.ERASE_THEN_DECAY, "decay_then_erase": _native.DECAY_THEN_ERASE}
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _io_dtype(t):
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return _native.GDR_BF16
+    if t.dtype == torch.float32:
+        return _native.GDR_FP32
+    raise TypeError("q/k/v must be bfloat16 or float32, got %s" % t.dtype)
+
+
+def _gate_kind(g, B, T, H, width, name, dtype, device):
+    if g is None:
+        return _native.GATE_NONE
+    if g.dtype != dtype or g.device != device:
+        raise TypeError("%s must be %s on %s" % (name, dtype, device))
+    if tuple(g.shape) == (B, T, H):
+        return _native.GATE_SCALAR
+    if tuple(g.shape) == (B, T, H, width):
+        return _native.GATE_CHANNEL
+    raise ValueError("%s has shape %s; expected %s or %s" % (name, tuple(g.shape), (B, T, H),
+                                                          (B, T, H, width)))
+
+
+def _ptr(t):
+    return 0 if t is None else t.data_ptr()
+
+
+def _check_contig(**tensors):
+    for name, t in tensors.items():
+        if t is not None and not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+
+
+def _stream(device):
+    torch = _torch()
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def chunk_fwd(q, k, v, log_alpha=None, b=None, w=None, S0=None, order="erase_then_decay",
+              out=None, final_state=True):
+    """Chunkwise prefill.  Returns (o [B,T,H,dv] in q's dtype, S_T [B,H,dk,dv] float32 or None).
+
+    ``S0`` (float32 [B,H,dk,dv] or None for zeros) is read before S_T is written; pass
+    ``final_state=S0`` to update the state in place."""
+    torch = _torch()
+    B, T, H, DK = q.shape
+    DV = v.shape[-1]
+    dt, dev = q.dtype, q.device
+    if k.shape != q.shape or tuple(v.shape[:3]) != (B, T, H):
+        raise ValueError("shape mismatch: q %s k %s v %s" % (tuple(q.shape), tuple(k.shape),
+                                                             tuple(v.shape)))
+    if k.dtype != dt or v.dtype != dt or k.device != dev or v.device != dev:
+        raise TypeError("q, k, v must share dtype and device")
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on a GPU")
+    ak = _gate_kind(log_alpha, B, T, H, DK, "log_alpha", dt, dev)
+    bk = _gate_kind(b, B, T, H, DK, "b", dt, dev)
+    wk = _gate_kind(w, B, T, H, DV, "w", dt, dev)
+    _check_contig(q=q, k=k, v=v, log_alpha=log_alpha, b=b, w=w, S0=S0, out=out)
+    if S0 is not None and (S0.dtype != torch.float32 or tuple(S0.shape) != (B, H, DK, DV)):
+        raise ValueError("S0 must be float32 [B,H,dk,dv]")
+    o = out if out is not None else torch.empty((B, T, H, DV), dtype=dt, device=dev)
+    if final_state is True:
+        S_T = torch.empty((B, H, DK, DV), dtype=torch.float32, device=dev)
+    elif final_state is False or final_state is None:
+        S_T = None
+    else:
+        S_T = final_state
+        _check_contig(final_state=S_T)
+    prob = make_problem(B, H, T, DK, DV, _io_dtype(q), ak, bk, wk, _ORDERS[order])
+    rc = _native.chunk_fwd_raw(prob, _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w),
+                               _ptr(S0), _ptr(o), _ptr(S_T), 0, 0, _stream(dev))
+    if rc != _native.GDR_OK:
+        raise GdrError(rc, "gdr_chunk_fwd")
+    return o, S_T
+
+
+def decode_step(q, k, v, log_alpha=None, b=None, w=None, S=None, order="erase_then_decay",
+                out=None):
+    """One decode step on tokens [B,1,H,*]; S [B,H,dk,dv] float32 is updated in place.
+    Returns o [B,1,H,dv]."""
+    torch = _torch()
+    if S is None:
+        raise ValueError("decode_step needs the state S")
+    B, T, H, DK = q.shape
+    DV = v.shape[-1]
+    if T != 1:
+        raise ValueError("decode_step takes one token per sequence (T = 1)")
+    dt, dev = q.dtype, q.device
+    if k.shape != q.shape or tuple(v.shape[:3]) != (B, 1, H):
+        raise ValueError("shape mismatch")
+    if k.dtype != dt or v.dtype != dt:
+        raise TypeError("q, k, v must share a dtype")
+    ak = _gate_kind(log_alpha, B, 1, H, DK, "log_alpha", dt, dev)
+    bk = _gate_kind(b, B, 1, H, DK, "b", dt, dev)
+    wk = _gate_kind(w, B, 1, H, DV, "w", dt, dev)
+    _check_contig(q=q, k=k, v=v, log_alpha=log_alpha, b=b, w=w, S=S, out=out)
+    if S.dtype != torch.float32 or tuple(S.shape) != (B, H, DK, DV):
+        raise ValueError("S must be float32 [B,H,dk,dv]")
+    o = out if out is not None else torch.empty((B, 1, H, DV), dtype=dt, device=dev)
+    prob = make_problem(B, H, 1, DK, DV, _io_dtype(q), ak, bk, wk, _ORDERS[order])
+    rc = _native.decode_step_raw(prob, _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b),
+                                 _ptr(w), _ptr(S), _ptr(o), _stream(dev))
+    if rc != _native.GDR_OK:
+        raise GdrError(rc, "gdr_decode_step")
+    return o
+
+
+def build():
+    """Compile libgdr.so in-tree for gfx950 (hipcc)."""
+    from .buildlib import build as _b
+    return _b()

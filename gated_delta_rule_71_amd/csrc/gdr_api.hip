@@ -1,0 +1,195 @@
+// C ABI of libgdr.so: argument validation and kernel dispatch.
+// Every check runs before the first HIP call, so a rejected call launches
+// nothing; the library keeps no mutable global state.
+#include <stdint.h>
+#include <string.h>
+
+#include "gdr.h"
+#include "gdr_common.h"
+
+#define GDR_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace gdr {
+template <typename IO>
+hipError_t launch_decode(const IO* q, const IO* k, const IO* v, const IO* la, const IO* bg,
+                         const IO* wg, float* S, IO* o, int64_t B, int64_t H, int64_t DK,
+                         int64_t DV, int alpha_kind, int b_kind, int w_kind, bool decay_first,
+                         hipStream_t stream);
+template <typename IO>
+hipError_t launch_prefill(const IO* q, const IO* k, const IO* v, const IO* la, const IO* bg,
+                          const IO* wg, const float* S0, IO* o, float* S_T, int64_t B, int64_t T,
+                          int64_t H, int64_t DK, int64_t DV, int alpha_kind, int b_kind,
+                          int w_kind, bool decay_first, hipStream_t stream);
+bool prefill_supported(int io_dtype, int64_t DK, int64_t DV, int alpha_kind, bool decay_first);
+}  // namespace gdr
+
+namespace {
+
+constexpr int64_t kMaxDim = int64_t(1) << 31;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range range_of(const void* p, int64_t bytes) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return Range{lo, lo + static_cast<uintptr_t>(bytes)};
+}
+
+bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.hi > a.lo && b.hi > b.lo; }
+
+int check_problem(const gdr_problem* p) {
+  if (p == nullptr) return GDR_ERR_INVALID_ARGUMENT;
+  if (p->struct_size != (int32_t)sizeof(gdr_problem) || p->reserved != 0)
+    return GDR_ERR_INVALID_ARGUMENT;
+  if (p->io_dtype != GDR_BF16 && p->io_dtype != GDR_FP32) return GDR_ERR_INVALID_ARGUMENT;
+  for (int32_t kind : {p->alpha_kind, p->b_kind, p->w_kind})
+    if (kind < GDR_GATE_NONE || kind > GDR_GATE_CHANNEL) return GDR_ERR_INVALID_ARGUMENT;
+  if (p->order != GDR_ERASE_THEN_DECAY && p->order != GDR_DECAY_THEN_ERASE)
+    return GDR_ERR_INVALID_ARGUMENT;
+  if (p->batch < 0 || p->heads < 0 || p->seqlen < 0 || p->dk <= 0 || p->dv <= 0)
+    return GDR_ERR_INVALID_ARGUMENT;
+  if (p->batch >= kMaxDim || p->heads >= kMaxDim || p->seqlen >= kMaxDim)
+    return GDR_ERR_INVALID_ARGUMENT;
+  if (p->dk != 16 && p->dk != 32 && p->dk != 64 && p->dk != 128) return GDR_ERR_UNSUPPORTED;
+  if (p->dv % 16 != 0 || p->dv > 256) return GDR_ERR_UNSUPPORTED;
+  if (p->chunk != 0 && p->chunk != 64) return GDR_ERR_UNSUPPORTED;
+  // index arithmetic inside the kernels is 64-bit; grids are 32-bit
+  if (p->batch * p->heads >= kMaxDim / 64) return GDR_ERR_UNSUPPORTED;
+  return GDR_OK;
+}
+
+// Pointer checks shared by both entry points.  `nt` = tokens per (batch, head).
+int check_tensors(const gdr_problem* p, int64_t nt, const void* q, const void* k, const void* v,
+                  const void* la, const void* b, const void* w, const void* o) {
+  const int64_t rows = p->batch * nt * p->heads;
+  if (rows == 0) return GDR_OK;
+  if (!q || !k || !v || !o) return GDR_ERR_INVALID_ARGUMENT;
+  if ((p->alpha_kind != GDR_GATE_NONE && !la) || (p->b_kind != GDR_GATE_NONE && !b) ||
+      (p->w_kind != GDR_GATE_NONE && !w))
+    return GDR_ERR_INVALID_ARGUMENT;
+  const void* ptrs[] = {q, k, v, o, p->alpha_kind ? la : nullptr, p->b_kind ? b : nullptr,
+                        p->w_kind ? w : nullptr};
+  for (const void* ptr : ptrs)
+    if (ptr && !aligned16(ptr)) return GDR_ERR_MISALIGNED;
+  const int64_t es = p->io_dtype == GDR_BF16 ? 2 : 4;
+  auto gate_bytes = [&](int32_t kind, int64_t width) {
+    return kind == GDR_GATE_SCALAR ? rows * es : rows * width * es;
+  };
+  const Range ro = range_of(o, rows * p->dv * es);
+  const Range ins[] = {range_of(q, rows * p->dk * es), range_of(k, rows * p->dk * es),
+                       range_of(v, rows * p->dv * es),
+                       p->alpha_kind ? range_of(la, gate_bytes(p->alpha_kind, p->dk)) : Range{0, 0},
+                       p->b_kind ? range_of(b, gate_bytes(p->b_kind, p->dk)) : Range{0, 0},
+                       p->w_kind ? range_of(w, gate_bytes(p->w_kind, p->dv)) : Range{0, 0}};
+  for (const Range& r : ins)
+    if (overlaps(ro, r)) return GDR_ERR_INVALID_ARGUMENT;
+  return GDR_OK;
+}
+
+const void* gate_ptr(int32_t kind, const void* ptr) { return kind == GDR_GATE_NONE ? nullptr : ptr; }
+
+}  // namespace
+
+GDR_EXPORT int gdr_abi_version(void) { return GDR_ABI_VERSION; }
+
+GDR_EXPORT const char* gdr_status_string(int status) {
+  switch (status) {
+    case GDR_OK: return "GDR_OK: success";
+    case GDR_ERR_INVALID_ARGUMENT:
+      return "GDR_ERR_INVALID_ARGUMENT: NULL pointer, negative size, bad enum value, struct_size "
+             "mismatch or overlapping output";
+    case GDR_ERR_UNSUPPORTED:
+      return "GDR_ERR_UNSUPPORTED: dk must be 16/32/64/128, dv a multiple of 16 up to 256, chunk 64";
+    case GDR_ERR_MISALIGNED: return "GDR_ERR_MISALIGNED: tensor pointers must be 16-byte aligned";
+    case GDR_ERR_WORKSPACE_TOO_SMALL: return "GDR_ERR_WORKSPACE_TOO_SMALL: workspace below the query";
+    case GDR_ERR_HIP: return "GDR_ERR_HIP: the HIP runtime reported an error at launch";
+    default: return "unknown gdr_status";
+  }
+}
+
+GDR_EXPORT size_t gdr_chunk_fwd_workspace_bytes(const gdr_problem* p) {
+  (void)p;
+  return 0;
+}
+
+GDR_EXPORT int gdr_chunk_fwd(const gdr_problem* p, const void* q, const void* k, const void* v,
+                             const void* log_alpha, const void* b, const void* w, const float* S0,
+                             void* o, float* S_T, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  int rc = check_problem(p);
+  if (rc != GDR_OK) return rc;
+  (void)workspace;
+  if (workspace_bytes < gdr_chunk_fwd_workspace_bytes(p)) return GDR_ERR_WORKSPACE_TOO_SMALL;
+  rc = check_tensors(p, p->seqlen, q, k, v, log_alpha, b, w, o);
+  if (rc != GDR_OK) return rc;
+  const int64_t nstate = p->batch * p->heads;
+  if (nstate == 0) return GDR_OK;
+  if ((S0 && !aligned16(S0)) || (S_T && !aligned16(S_T))) return GDR_ERR_MISALIGNED;
+  const int64_t sbytes = nstate * p->dk * p->dv * 4;
+  if (S0 && S_T && S0 != S_T && overlaps(range_of(S0, sbytes), range_of(S_T, sbytes)))
+    return GDR_ERR_INVALID_ARGUMENT;
+  const int64_t es = p->io_dtype == GDR_BF16 ? 2 : 4;
+  const int64_t rows = p->batch * p->seqlen * p->heads;
+  if (S_T && rows && overlaps(range_of(S_T, sbytes), range_of(o, rows * p->dv * es)))
+    return GDR_ERR_INVALID_ARGUMENT;
+  const bool decay_first = p->order == GDR_DECAY_THEN_ERASE;
+  if (!gdr::prefill_supported(p->io_dtype, p->dk, p->dv, p->alpha_kind, decay_first))
+    return GDR_ERR_UNSUPPORTED;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (p->io_dtype == GDR_BF16) {
+    using T = gdr::bf16_t;
+    e = gdr::launch_prefill<T>(
+        (const T*)q, (const T*)k, (const T*)v, (const T*)gate_ptr(p->alpha_kind, log_alpha),
+        (const T*)gate_ptr(p->b_kind, b), (const T*)gate_ptr(p->w_kind, w), S0, (T*)o, S_T,
+        p->batch, p->seqlen, p->heads, p->dk, p->dv, p->alpha_kind, p->b_kind, p->w_kind,
+        decay_first, s);
+  } else {
+    e = gdr::launch_prefill<float>(
+        (const float*)q, (const float*)k, (const float*)v,
+        (const float*)gate_ptr(p->alpha_kind, log_alpha), (const float*)gate_ptr(p->b_kind, b),
+        (const float*)gate_ptr(p->w_kind, w), S0, (float*)o, S_T, p->batch, p->seqlen, p->heads,
+        p->dk, p->dv, p->alpha_kind, p->b_kind, p->w_kind, decay_first, s);
+  }
+  return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
+}
+
+GDR_EXPORT int gdr_decode_step(const gdr_problem* p, const void* q, const void* k, const void* v,
+                               const void* log_alpha, const void* b, const void* w, float* S,
+                               void* o, void* stream) {
+  int rc = check_problem(p);
+  if (rc != GDR_OK) return rc;
+  if (p->seqlen != 1) return GDR_ERR_INVALID_ARGUMENT;
+  rc = check_tensors(p, 1, q, k, v, log_alpha, b, w, o);
+  if (rc != GDR_OK) return rc;
+  const int64_t nstate = p->batch * p->heads;
+  if (nstate == 0) return GDR_OK;
+  if (!S) return GDR_ERR_INVALID_ARGUMENT;
+  if (!aligned16(S)) return GDR_ERR_MISALIGNED;
+  const int64_t es = p->io_dtype == GDR_BF16 ? 2 : 4;
+  if (overlaps(range_of(S, nstate * p->dk * p->dv * 4), range_of(o, nstate * p->dv * es)))
+    return GDR_ERR_INVALID_ARGUMENT;
+  const bool decay_first = p->order == GDR_DECAY_THEN_ERASE;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (p->io_dtype == GDR_BF16) {
+    using T = gdr::bf16_t;
+    e = gdr::launch_decode<T>((const T*)q, (const T*)k, (const T*)v,
+                              (const T*)gate_ptr(p->alpha_kind, log_alpha),
+                              (const T*)gate_ptr(p->b_kind, b), (const T*)gate_ptr(p->w_kind, w), S,
+                              (T*)o, p->batch, p->heads, p->dk, p->dv, p->alpha_kind, p->b_kind,
+                              p->w_kind, decay_first, s);
+  } else {
+    e = gdr::launch_decode<float>((const float*)q, (const float*)k, (const float*)v,
+                                  (const float*)gate_ptr(p->alpha_kind, log_alpha),
+                                  (const float*)gate_ptr(p->b_kind, b),
+                                  (const float*)gate_ptr(p->w_kind, w), S, (float*)o, p->batch,
+                                  p->heads, p->dk, p->dv, p->alpha_kind, p->b_kind, p->w_kind,
+                                  decay_first, s);
+  }
+  return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
+}

@@ -1,0 +1,55 @@
+// Shared device helpers for the gfx950 kernels: bf16 <-> fp32 and typed I/O.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdr {
+
+// bf16 storage type as 16 raw bits; the arithmetic is always fp32.
+struct bf16_t {
+  uint16_t x;
+};
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// Round-to-nearest-even fp32 -> bf16 (NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+template <typename IO>
+struct io_traits;
+
+template <>
+struct io_traits<bf16_t> {
+  __device__ __forceinline__ static float load(const bf16_t* p, int64_t i) {
+    return bf16_to_f32(p[i].x);
+  }
+  __device__ __forceinline__ static void store(bf16_t* p, int64_t i, float f) {
+    p[i].x = f32_to_bf16(f);
+  }
+};
+
+template <>
+struct io_traits<float> {
+  __device__ __forceinline__ static float load(const float* p, int64_t i) { return p[i]; }
+  __device__ __forceinline__ static void store(float* p, int64_t i, float f) { p[i] = f; }
+};
+
+template <typename IO>
+__device__ __forceinline__ float ld(const IO* p, int64_t i) {
+  return io_traits<IO>::load(p, i);
+}
+template <typename IO>
+__device__ __forceinline__ void st(IO* p, int64_t i, float f) {
+  io_traits<IO>::store(p, i, f);
+}
+
+enum GateKind : int { kNone = 0, kScalar = 1, kChannel = 2 };
+
+}  // namespace gdr

@@ -1,0 +1,85 @@
+// Host entry for the chunkwise prefill: picks the kernel variant for a problem.
+#include <stdlib.h>
+
+#include "prefill_dispatch.h"
+
+namespace gdr {
+
+namespace {
+
+// MODE 0: scalar (or no) decay; 1: per-channel decay applied before the erase;
+// 2: per-channel decay applied after the erase (the unified equation's order).
+int prefill_mode(int alpha_kind, bool decay_first) {
+  if (alpha_kind != kChannel) return 0;
+  return decay_first ? 1 : 2;
+}
+
+template <typename OT>
+bool fits_dk(int64_t DK, int mode, int nsw) {
+  switch (DK) {
+    case 16: return prefill_fits<OT, 16>(mode, nsw);
+    case 32: return prefill_fits<OT, 32>(mode, nsw);
+    case 64: return prefill_fits<OT, 64>(mode, nsw);
+    case 128: return prefill_fits<OT, 128>(mode, nsw);
+    default: return false;
+  }
+}
+
+// State waves per workgroup for bf16: the widest slice (4, 2 or 1 x 16 columns) that
+// divides dv and fits in LDS, capped by GDR_PREFILL_NSW when that is set (tuning).
+int choose_nsw_bf16(int64_t DK, int64_t DV, int mode) {
+  int cap = 2;
+  if (const char* e = getenv("GDR_PREFILL_NSW")) {
+    const int v = atoi(e);
+    if (v == 1 || v == 2 || v == 4) cap = v;
+  }
+  for (int nsw = cap; nsw >= 1; nsw /= 2)
+    if (DV % (16 * nsw) == 0 && fits_dk<__bf16>(DK, mode, nsw)) return nsw;
+  return 0;
+}
+
+}  // namespace
+
+bool prefill_supported(int io_dtype, int64_t DK, int64_t DV, int alpha_kind, bool decay_first) {
+  const int mode = prefill_mode(alpha_kind, decay_first);
+  if (DV % 16 != 0) return false;
+  if (io_dtype == 0) return choose_nsw_bf16(DK, DV, mode) > 0;
+  return fits_dk<float>(DK, mode, 1);
+}
+
+template <typename IO>
+hipError_t launch_prefill(const IO* q, const IO* k, const IO* v, const IO* la, const IO* bg,
+                          const IO* wg, const float* S0, IO* o, float* S_T, int64_t B, int64_t T,
+                          int64_t H, int64_t DK, int64_t DV, int alpha_kind, int b_kind,
+                          int w_kind, bool decay_first, hipStream_t stream) {
+  const int mode = prefill_mode(alpha_kind, decay_first);
+  PrefillArgs<IO> a{q, k, v, la, bg, wg, S0, o, S_T, T, H, DV, alpha_kind, b_kind, w_kind, 1};
+  const int64_t nstate = B * H;
+  if constexpr (sizeof(IO) == 2) {
+    const int nsw = choose_nsw_bf16(DK, DV, mode);
+    if (nsw == 0) return hipErrorInvalidValue;
+    a.nsl = static_cast<int>(DV / (16 * nsw));
+    switch (DK) {
+      case 16: return prefill_bf16_dk16(a, nstate, mode, nsw, stream);
+      case 32: return prefill_bf16_dk32(a, nstate, mode, nsw, stream);
+      case 64: return prefill_bf16_dk64(a, nstate, mode, nsw, stream);
+      default: return prefill_bf16_dk128(a, nstate, mode, nsw, stream);
+    }
+  } else {
+    if (!fits_dk<float>(DK, mode, 1)) return hipErrorInvalidValue;
+    a.nsl = static_cast<int>(DV / 16);
+    return prefill_f32_any(a, nstate, DK, mode, 1, stream);
+  }
+}
+
+template hipError_t launch_prefill<bf16_t>(const bf16_t*, const bf16_t*, const bf16_t*,
+                                           const bf16_t*, const bf16_t*, const bf16_t*,
+                                           const float*, bf16_t*, float*, int64_t, int64_t,
+                                           int64_t, int64_t, int64_t, int, int, int, bool,
+                                           hipStream_t);
+template hipError_t launch_prefill<float>(const float*, const float*, const float*, const float*,
+                                          const float*, const float*, const float*, float*, float*,
+                                          int64_t, int64_t, int64_t, int64_t, int64_t, int, int,
+                                          int, bool, hipStream_t);
+
+}  // namespace gdr

@@ -1,0 +1,536 @@
+// Chunkwise prefill of the gated delta rule on gfx950: one fused kernel.
+//
+// One workgroup (4 waves) owns one (batch, head) state and a slice of DVS = 16*NSW value
+// columns; it walks the chunks of 64 tokens in order and keeps its slice of S in the
+// accumulator registers of NSW "state waves" (16 columns each) for the whole sequence.
+// Columns of S evolve independently (the transition multiplies S from the left:
+// "Recurrent Memory: Write, Erase, Decay, Read", section 05), which is what makes the
+// column slicing exact.
+//
+// Chunk form (derived by unrolling the recurrence over a chunk; section 03 of the same
+// page notes that the linear erase reassociates into a chunkwise-parallel form, section
+// 04 that the decay enters as prefix sums of log alpha, and the Gated DeltaNet-2 abstract
+// that a channel-wise decay is absorbed into separate erase factors).  With entering
+// state S, local prefix sums G_t of log alpha (G_0 = 0), c = b . k and x = w . v:
+//
+// MODE 0 (scalar decay, either order) and MODE 1 (per-channel decay applied before the
+// erase) are rank one per token: u_t = x_t - c_t Diag(alpha_t) S_{t-1}, S_t = Diag(alpha_t)
+// S_{t-1} + k_t^T u_t.  With Chat_t = c_t e^{G_t}, Khat_i = k_i e^{-G_i}, Qhat_t = q_t e^{G_t},
+// Kbar_i = k_i e^{G_n - G_i} and A = strict_tril(Chat Khat^T), M = tril(Qhat Khat^T):
+//     (I + A) R = Chat S - X                 (R = -U)
+//     O = Qhat S - M R,     S' = e^{G_n} . S - Kbar^T R
+// MODE 2 (per-channel decay after the erase, the unified equation's order): the erase
+// of token i uses the decay-absorbed key alpha_i . k_i while the write uses k_i, so two
+// key families appear.  With Chat_t = c_t e^{G_{t-1}}, Phat_i = k_i e^{-G_{i-1}},
+// Pbar_i = k_i e^{G_n - G_{i-1}}, L_P = strict_tril(Chat Phat^T), L_K = strict_tril(Chat
+// Khat^T), M_QK = tril(Qhat Khat^T), M_QP = tril(Qhat Phat^T):
+//     (I + L_P) R = Chat S + L_K X           (R_t = c_t S_{t-1}, the erase reads)
+//     O  = Qhat S + M_QK X - M_QP R,   S' = e^{G_n} . S + Kbar^T X - Pbar^T R
+//
+// Per-channel exponentials are split around a reference G_ref = G_31 (mid-chunk) in the
+// products that do not involve S (e^{G_t - G_ref} on row operands, e^{G_ref - G_i} on
+// column operands, each factor clamped at e^80), and the S-side products use the same row
+// operands against e^{G_ref} . S.  Scalar decay uses the exact pairwise mask
+// e^{G_t - G_i} instead.
+//
+// The unit-lower-triangular solve runs as blocked forward substitution over 16-row
+// blocks on the state waves (R_i = T_ii (V_i - sum_{m<i} L_im R_m)), with the four
+// 16x16 diagonal inverses T_ii computed once per chunk in fp32 by substitution.
+//
+// Phases per chunk (barriers between): A gate prefix sums and scaled operands into LDS;
+// B Gram tiles on MFMA; C diagonal inverses; D state waves: S-side products, solve,
+// read-out, state update.
+#pragma once
+#include "gdr_common.h"
+#include "mfma.h"
+
+namespace gdr {
+
+constexpr int kLdsLimit = 163840;  // bytes of LDS one gfx950 workgroup may use
+
+template <typename OT, int DK, int NSW, int MODE>
+struct PrefillLayout {
+  static constexpr int C = 64;
+  static constexpr int DVS = 16 * NSW;
+  static constexpr int LDT = DK + 8;  // row pitch of token-major operands (elements)
+  static constexpr int LDD = C + 8;   // row pitch of channel-major / 64-wide arrays
+  static constexpr int LDI = 24;      // row pitch of the diagonal inverses
+  static constexpr int ES = sizeof(OT);
+  static constexpr bool TWO = MODE == 2;
+  static constexpr int NCG = DK / 8;  // 8-channel groups in the gate preparation
+  static constexpr int NSEG = (256 / NCG) < C ? (256 / NCG) : C;
+  static constexpr int TPS = C / NSEG;  // tokens per thread in the gate preparation
+  static constexpr int SEG_BYTES = NSEG * DK * 4;
+  static constexpr int GRAM_BYTES = C * LDD * ES;
+  static constexpr int oQ = 0;                                   // Qhat   [C][LDT]
+  static constexpr int oC = oQ + C * LDT * ES;                   // Chat   [C][LDT]
+  static constexpr int oK = oC + C * LDT * ES;                   // Khat   [C][LDT]
+  static constexpr int oP = oK + C * LDT * ES;                   // Phat   [C][LDT] (MODE 2)
+  static constexpr int oDP = oP + (TWO ? C * LDT * ES : 0);      // -Pbar^T / -Kbar^T [DK][LDD]
+  static constexpr int oDK = oDP + DK * LDD * ES;                // Kbar^T [DK][LDD] (MODE 2)
+  static constexpr int oX = oDK + (TWO ? DK * LDD * ES : 0);     // X^T    [DVS][LDD]
+  static constexpr int oGA = oX + DVS * LDD * ES;                // -L (solve) / segment sums
+  static constexpr int oGM = oGA + (GRAM_BYTES > SEG_BYTES ? GRAM_BYTES : SEG_BYTES);  // -M
+  static constexpr int oGLK = oGM + GRAM_BYTES;                  // L_K (MODE 2)
+  static constexpr int oGMQK = oGLK + (TWO ? GRAM_BYTES : 0);    // M_QK (MODE 2)
+  static constexpr int oINV = oGMQK + (TWO ? GRAM_BYTES : 0);    // T_ii [4][16][LDI]
+  static constexpr int oLD = oINV + 4 * 16 * LDI * ES;           // fp32 L_ii [4][16][17]
+  static constexpr int oF = oLD + 4 * 16 * 17 * 4;               // fp32 per-channel / per-token
+  static constexpr int NF = MODE == 0 ? 2 * C + 8 : 4 * DK;
+  static constexpr int total = oF + NF * 4;
+  static constexpr bool fits = total <= kLdsLimit;
+};
+
+template <typename IO>
+struct PrefillArgs {
+  const IO* q;
+  const IO* k;
+  const IO* v;
+  const IO* la;
+  const IO* bg;
+  const IO* wg;
+  const float* S0;
+  IO* o;
+  float* S_T;
+  int64_t T, H, DV;
+  int alpha_kind, b_kind, w_kind;
+  int nsl;  // value slices per state
+};
+
+// 8 consecutive I/O elements starting at p (16-byte aligned for bf16) as fp32.
+__device__ __forceinline__ void load8f(const bf16_t* p, float* out) {
+  const uint4 u = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    out[2 * j] = __uint_as_float(w[j] << 16);
+    out[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void load8f(const float* p, float* out) {
+  const float4 a = reinterpret_cast<const float4*>(p)[0];
+  const float4 b = reinterpret_cast<const float4*>(p)[1];
+  out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+  out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
+}
+
+template <typename OT>
+__device__ __forceinline__ void lds_store8(OT* p, const float* v) {
+  typename Mma<OT>::F8 f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) f[j] = to_ot<OT>(v[j]);
+  *reinterpret_cast<typename Mma<OT>::F8*>(p) = f;
+}
+
+__device__ __forceinline__ float exp_clamped(float x) { return __expf(fminf(x, 80.f)); }
+
+template <typename IO, typename OT, int DK, int NSW, int MODE>
+__global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs<IO> a) {
+  using L = PrefillLayout<OT, DK, NSW, MODE>;
+  using MM = Mma<OT>;
+  using F8 = typename MM::F8;
+  static_assert(L::fits, "LDS layout exceeds the gfx950 workgroup limit");
+  constexpr int C = L::C, DVS = L::DVS, LDT = L::LDT, LDD = L::LDD, LDI = L::LDI;
+  constexpr int NTD = DK / 16;         // 16-row tiles of the state slice
+  constexpr int NKB = (DK + 31) / 32;  // 32-wide k blocks over dk
+  constexpr bool TWO = MODE == 2;
+
+  __shared__ __attribute__((aligned(32))) unsigned char smem[L::total];
+  OT* tQ = reinterpret_cast<OT*>(smem + L::oQ);
+  OT* tC = reinterpret_cast<OT*>(smem + L::oC);
+  OT* tK = reinterpret_cast<OT*>(smem + L::oK);
+  OT* tP = reinterpret_cast<OT*>(smem + L::oP);
+  OT* dP = reinterpret_cast<OT*>(smem + L::oDP);
+  OT* dK = reinterpret_cast<OT*>(smem + L::oDK);
+  OT* xT = reinterpret_cast<OT*>(smem + L::oX);
+  OT* gA = reinterpret_cast<OT*>(smem + L::oGA);
+  float* segtot = reinterpret_cast<float*>(smem + L::oGA);  // aliases gA (phase A only)
+  OT* gM = reinterpret_cast<OT*>(smem + L::oGM);
+  OT* gLK = reinterpret_cast<OT*>(smem + L::oGLK);
+  OT* gMQK = reinterpret_cast<OT*>(smem + L::oGMQK);
+  OT* dInv = reinterpret_cast<OT*>(smem + L::oINV);
+  float* Ld = reinterpret_cast<float*>(smem + L::oLD);
+  float* fF = reinterpret_cast<float*>(smem + L::oF);
+  // MODE 0: fF = [G_t (64) | e^{G_t} (64) | e^{G_n}];  MODE 1/2: [G_ref | G_n | e^{G_ref} | e^{G_n}]
+  float* sG = fF;
+  float* sEG = fF + C;
+  float* sEGn = fF + 2 * C;
+  float* fRef = fF;
+  float* fGn = fF + DK;
+  float* fEref = fF + 2 * DK;
+  float* fEGn = fF + 3 * DK;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, l16 = lane & 15;
+
+  // Block -> (state, slice).  Blocks are dealt round-robin to the 8 XCDs; consecutive
+  // pairs p land on one XCD, so the slices of one head share that XCD's L2.
+  const int64_t nb = gridDim.x, bid = blockIdx.x;
+  const int64_t p = (nb % 8 == 0) ? (bid % 8) * (nb / 8) + bid / 8 : bid;
+  const int64_t bh = p / a.nsl;
+  const int sl = static_cast<int>(p % a.nsl);
+  const int64_t bi = bh / a.H, hi = bh % a.H;
+  const int64_t DV = a.DV;
+  const int64_t col0 = static_cast<int64_t>(sl) * DVS;
+
+  // Gram outputs: tiles above the diagonal are never written and must read as zero.
+  {
+    float* z = reinterpret_cast<float*>(smem + L::oGM);
+    const int nz = (L::oINV - L::oGM) / 4;
+    for (int i = tid; i < nz; i += 256) z[i] = 0.f;
+  }
+
+  const bool sside = wave < NSW;
+  const int nloc = 16 * wave + l16;  // state wave: local value column
+  const int64_t sbase = bh * DK * DV + col0 + nloc;
+  f32x4 S[NTD];
+#pragma unroll
+  for (int tl = 0; tl < NTD; ++tl) {
+    S[tl] = zero4();
+    if (sside && a.S0 != nullptr) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) S[tl][i] = a.S0[sbase + (int64_t)(16 * tl + 4 * g + i) * DV];
+    }
+  }
+
+  const int64_t nch = (a.T + C - 1) / C;
+  for (int64_t ch = 0; ch < nch; ++ch) {
+    const int64_t t0 = ch * C;
+    const int nval = static_cast<int>(a.T - t0 < C ? a.T - t0 : C);
+    auto row_of = [&](int t) -> int64_t { return (bi * a.T + t0 + t) * a.H + hi; };
+    __syncthreads();  // the previous chunk's readers of every LDS array are done
+
+    // ---------------- phase A: X^T, gate prefix sums, scaled operands ----------------
+    {
+      constexpr int NXG = DVS / 8;
+      for (int idx = tid; idx < NXG * C; idx += 256) {
+        const int xg = idx % NXG, t = idx / NXG;
+        float x[8];
+        if (t < nval) {
+          const int64_t r = row_of(t);
+          load8f(a.v + r * DV + col0 + xg * 8, x);
+          if (a.w_kind == kChannel) {
+            float w[8];
+            load8f(a.wg + r * DV + col0 + xg * 8, w);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) x[j] *= w[j];
+          } else if (a.w_kind == kScalar) {
+            const float w = ld(a.wg, r);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) x[j] *= w;
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) x[j] = 0.f;
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) xT[(xg * 8 + j) * LDD + t] = to_ot<OT>(x[j]);
+      }
+    }
+
+    constexpr int NCG = L::NCG, NSEG = L::NSEG, TPS = L::TPS;
+    const int cg = tid % NCG, ts = tid / NCG;
+    const bool act = ts < NSEG;
+    const int d0 = cg * 8;
+    float la8[TPS][8], G8[TPS][8];
+    if (MODE == 0) {
+      if (wave == 0) {
+        float x = 0.f;
+        if (lane < nval && a.alpha_kind != kNone) x = ld(a.la, row_of(lane));
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const float y = __shfl_up(x, off);
+          if (lane >= off) x += y;
+        }
+        sG[lane] = x;
+        sEG[lane] = __expf(x);
+        if (lane == 63) sEGn[0] = __expf(x);
+      }
+    } else {
+      if (act) {
+        float run[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < TPS; ++u) {
+          const int t = ts * TPS + u;
+          if (t < nval) {
+            load8f(a.la + row_of(t) * DK + d0, la8[u]);
+          } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) la8[u][j] = 0.f;
+          }
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            run[j] += la8[u][j];
+            G8[u][j] = run[j];
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) segtot[ts * DK + d0 + j] = run[j];
+      }
+      __syncthreads();
+      if (tid < DK) {
+        float run = 0.f;
+        for (int s = 0; s < NSEG; ++s) {
+          const float tv = segtot[s * DK + tid];
+          segtot[s * DK + tid] = run;
+          run += tv;
+        }
+        const float ref = segtot[(NSEG / 2) * DK + tid];
+        fRef[tid] = ref;
+        fGn[tid] = run;
+        fEref[tid] = __expf(ref);
+        fEGn[tid] = __expf(run);
+      }
+    }
+    __syncthreads();
+
+    if (act) {
+      float off[8], ref[8], gn[8];
+      if (MODE != 0) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          off[j] = segtot[ts * DK + d0 + j];
+          ref[j] = fRef[d0 + j];
+          gn[j] = fGn[d0 + j];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < TPS; ++u) {
+        const int t = ts * TPS + u;
+        float q[8], k[8], c[8];
+        if (t < nval) {
+          const int64_t r = row_of(t);
+          load8f(a.q + r * DK + d0, q);
+          load8f(a.k + r * DK + d0, k);
+          if (a.b_kind == kChannel) {
+            load8f(a.bg + r * DK + d0, c);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) c[j] *= k[j];
+          } else {
+            const float bs = a.b_kind == kScalar ? ld(a.bg, r) : 0.f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) c[j] = bs * k[j];
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) q[j] = k[j] = c[j] = 0.f;
+        }
+        float oq[8], oc[8], ok[8], op[8], odp[8], odk[8];
+        if (MODE == 0) {
+          const float fk = __expf(sG[C - 1] - sG[t]);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            oq[j] = q[j];
+            oc[j] = c[j];
+            ok[j] = k[j];
+            odp[j] = -k[j] * fk;
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const float G = G8[u][j] + off[j];
+            const float eq = exp_clamped(G - ref[j]);
+            oq[j] = q[j] * eq;
+            ok[j] = k[j] * exp_clamped(ref[j] - G);
+            if (MODE == 1) {
+              oc[j] = c[j] * eq;
+              odp[j] = -k[j] * __expf(gn[j] - G);
+            } else {
+              const float Gp = G - la8[u][j];
+              oc[j] = c[j] * exp_clamped(Gp - ref[j]);
+              op[j] = k[j] * exp_clamped(ref[j] - Gp);
+              odp[j] = -k[j] * __expf(gn[j] - Gp);
+              odk[j] = k[j] * __expf(gn[j] - G);
+            }
+          }
+        }
+        lds_store8(tQ + t * LDT + d0, oq);
+        lds_store8(tC + t * LDT + d0, oc);
+        lds_store8(tK + t * LDT + d0, ok);
+        if (TWO) lds_store8(tP + t * LDT + d0, op);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          dP[(d0 + j) * LDD + t] = to_ot<OT>(odp[j]);
+          if (TWO) dK[(d0 + j) * LDD + t] = to_ot<OT>(odk[j]);
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---------------- phase B: Gram tiles of the lower triangle ----------------
+    {
+      constexpr int NPROD = TWO ? 4 : 2;
+      for (int job = wave; job < NPROD * 10; job += 4) {
+        const int prod = job / 10, tix = job % 10;
+        const int ta = tix >= 6 ? 3 : tix >= 3 ? 2 : tix >= 1 ? 1 : 0;
+        const int tb = tix - ta * (ta + 1) / 2;
+        // MODE 0/1: 0 = C x K (strict, solve), 1 = Q x K (incl, read-out)
+        // MODE 2:   0 = C x P (strict, solve), 1 = C x K (strict), 2 = Q x K, 3 = Q x P (incl)
+        const OT* rows = (prod == 0 || (TWO && prod == 1)) ? tC : tQ;
+        const OT* cols = TWO ? ((prod == 0 || prod == 3) ? tP : tK) : tK;
+        const bool strict = TWO ? prod <= 1 : prod == 0;
+        const OT* ar = rows + (16 * ta + l16) * LDT;
+        const OT* br = cols + (16 * tb + l16) * LDT;
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+          acc = MM::mma8(lds_std_frag(ar, 32 * kb, g, DK), lds_std_frag(br, 32 * kb, g, DK), acc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * ta + 4 * g + i, cc = 16 * tb + l16;
+          const bool keep = strict ? (cc < r) : (cc <= r);
+          float val = 0.f;
+          if (keep) {
+            val = acc[i];
+            if (MODE == 0) val *= __expf(sG[r] - sG[cc]);
+          }
+          if (prod == 0) {
+            if (ta > tb)
+              gA[r * LDD + cc] = to_ot<OT>(-val);
+            else
+              Ld[(ta * 16 + (r & 15)) * 17 + (cc & 15)] = val;
+          } else if (!TWO || prod == 3) {
+            gM[r * LDD + cc] = to_ot<OT>(-val);
+          } else if (prod == 1) {
+            gLK[r * LDD + cc] = to_ot<OT>(val);
+          } else {
+            gMQK[r * LDD + cc] = to_ot<OT>(val);
+          }
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---------------- phase C: inverses of the four 16x16 diagonal blocks ----------------
+    if (wave == 0) {
+      const int blk = g, j = l16;
+      float x[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float s = (i == j) ? 1.f : 0.f;
+#pragma unroll
+        for (int m = 0; m < i; ++m) s -= Ld[(blk * 16 + i) * 17 + m] * x[m];
+        x[i] = s;
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) dInv[(blk * 16 + i) * LDI + j] = to_ot<OT>(x[i]);
+    }
+    __syncthreads();
+
+    // ---------------- phase D: state waves ----------------
+    if (sside) {
+      // (1) S (scaled by e^{G_ref} for a per-channel decay) as B fragments, tile-pair order
+      F8 sf[NKB];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int tl = 2 * kb + (j >> 2), i = j & 3;
+          float val = 0.f;
+          if (tl < NTD) {
+            val = S[tl][i];
+            if (MODE != 0) val *= fEref[16 * tl + 4 * g + i];
+          }
+          sf[kb][j] = to_ot<OT>(val);
+        }
+      }
+      // (2) V = Chat S, O = Qhat S
+      f32x4 V[4], O[4];
+#pragma unroll
+      for (int ta = 0; ta < 4; ++ta) {
+        V[ta] = zero4();
+        O[ta] = zero4();
+        const OT* cr = tC + (16 * ta + l16) * LDT;
+        const OT* qr = tQ + (16 * ta + l16) * LDT;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          V[ta] = MM::mma8(lds_pair_frag(cr, 32 * kb, g, DK), sf[kb], V[ta]);
+          O[ta] = MM::mma8(lds_pair_frag(qr, 32 * kb, g, DK), sf[kb], O[ta]);
+        }
+        if (MODE == 0) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float e = sEG[16 * ta + 4 * g + i];
+            V[ta][i] *= e;
+            O[ta][i] *= e;
+          }
+        }
+      }
+      // (3) value side: MODE 0/1 subtract X; MODE 2 add L_K X and M_QK X
+      const OT* xr = xT + nloc * LDD;
+      F8 xf[2];
+      xf[0] = lds_load8(xr + 8 * g);
+      xf[1] = lds_load8(xr + 32 + 8 * g);
+      if (!TWO) {
+#pragma unroll
+        for (int ta = 0; ta < 4; ++ta)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) V[ta][i] -= static_cast<float>(xr[16 * ta + 4 * g + i]);
+      } else {
+#pragma unroll
+        for (int ta = 0; ta < 4; ++ta) {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) {
+            if (kb == 1 && ta < 2) continue;
+            V[ta] = MM::mma8(lds_load8(gLK + (16 * ta + l16) * LDD + 32 * kb + 8 * g), xf[kb], V[ta]);
+            O[ta] = MM::mma8(lds_load8(gMQK + (16 * ta + l16) * LDD + 32 * kb + 8 * g), xf[kb], O[ta]);
+          }
+        }
+      }
+      // (4) blocked forward substitution: R_i = T_ii (V_i - sum_{m<i} L_im R_m)
+      f32x4 R[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int m = 0; m < i; ++m)
+          V[i] = MM::mma4(lds_load4(gA + (16 * i + l16) * LDD + 16 * m + 4 * g),
+                          acc_frag4<OT>(R[m]), V[i]);
+        R[i] = MM::mma4(lds_load4(dInv + (16 * i + l16) * LDI + 4 * g), acc_frag4<OT>(V[i]),
+                        zero4());
+      }
+      F8 rf[2];
+      rf[0] = acc_pair_frag<OT>(R[0], R[1]);
+      rf[1] = acc_pair_frag<OT>(R[2], R[3]);
+      // (5) O -= M R   (gM holds -M)
+#pragma unroll
+      for (int ta = 0; ta < 4; ++ta) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          if (kb == 1 && ta < 2) continue;
+          O[ta] = MM::mma8(lds_pair_frag(gM + (16 * ta + l16) * LDD, 32 * kb, g, C), rf[kb], O[ta]);
+        }
+      }
+      // (6) read-out
+#pragma unroll
+      for (int ta = 0; ta < 4; ++ta)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = 16 * ta + 4 * g + i;
+          if (t < nval) st(a.o, row_of(t) * DV + col0 + nloc, O[ta][i]);
+        }
+      // (7) S <- e^{G_n} . S (+ Kbar^T X) - P^T R   (dP holds -P^T)
+#pragma unroll
+      for (int tl = 0; tl < NTD; ++tl) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) S[tl][i] *= (MODE == 0) ? sEGn[0] : fEGn[16 * tl + 4 * g + i];
+        const OT* pr = dP + (16 * tl + l16) * LDD;
+        if (TWO) {
+          const OT* kr = dK + (16 * tl + l16) * LDD;
+          S[tl] = MM::mma8(lds_load8(kr + 8 * g), xf[0], S[tl]);
+          S[tl] = MM::mma8(lds_load8(kr + 32 + 8 * g), xf[1], S[tl]);
+        }
+        S[tl] = MM::mma8(lds_pair_frag(pr, 0, g, C), rf[0], S[tl]);
+        S[tl] = MM::mma8(lds_pair_frag(pr, 32, g, C), rf[1], S[tl]);
+      }
+    }
+  }
+
+  if (sside && a.S_T != nullptr) {
+#pragma unroll
+    for (int tl = 0; tl < NTD; ++tl)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a.S_T[sbase + (int64_t)(16 * tl + 4 * g + i) * DV] = S[tl][i];
+  }
+}
+
+}  // namespace gdr

@@ -1,0 +1,138 @@
+/*
+ * gdr.h -- C ABI of libgdr.so: the generalized gated delta-rule recurrence on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation (row-vector convention, one dk x dv fp32 state S per
+ * (batch, head)):
+ *
+ *   S_t = Diag(alpha_t) (I - k_t^T (b_t . k_t)) S_{t-1} + k_t^T (w_t . v_t)
+ *   o_t = q_t S_t
+ *
+ * "Recurrent Memory: Write, Erase, Decay, Read", section 05 (the unified
+ * equation: decay x erase x state + write) with the read of section 01; the
+ * erase gate b_t (key side) and the write gate w_t (value side) are the
+ * channel-wise gates of the Gated DeltaNet-2 abstract, which reduce to the
+ * single beta of section 05 when b_t = w_t = beta_t.  The read sees the
+ * token's own write ("How Linear Attention Remembers", Analytical Framework:
+ * o_t = q_t^T S_t).  With GDR_DECAY_THEN_ERASE the decay is applied to
+ * S_{t-1} before the erase reads it instead; the two orders coincide for a
+ * scalar alpha.
+ *
+ * Special settings (same section 05): b = 0, alpha = 1 is linear attention;
+ * b = w = beta, alpha = 1 is DeltaNet; b = 0 with a decay is GLA / Mamba-2;
+ * scalar alpha with b = w = beta is Gated DeltaNet; per-channel alpha with
+ * b = w = beta is KDA; per-channel alpha, b and w is Gated DeltaNet-2.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All tensor pointers are DEVICE pointers owned by the caller, row-major and
+ *   contiguous, 16-byte aligned.  The library never allocates, frees or keeps
+ *   them.  Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *   stream); outputs are valid once the stream has reached the call.
+ * - Per-token tensors are laid out [B, T, H, D]: q, k [B,T,H,dk];
+ *   v, o [B,T,H,dv].  Gates: log_alpha [B,T,H] (SCALAR) or [B,T,H,dk]
+ *   (CHANNEL); b [B,T,H] or [B,T,H,dk]; w [B,T,H] or [B,T,H,dv].  A gate of
+ *   kind NONE ignores its pointer (may be NULL) and means alpha = 1, b = 0,
+ *   w = 1.  Gates are given as log alpha (<= 0 for a contraction; any finite
+ *   value is accepted) and as plain values for b and w (no sigmoid is applied).
+ * - q, k, v, the gates and o share io_dtype (bf16 or fp32).  The state is fp32
+ *   [B, H, dk, dv] (dv fastest).  Arithmetic is fp32 with bf16 (GDR_BF16) or
+ *   fp32 (GDR_FP32) matrix-core operands.
+ * - Validation happens before any HIP call; a call that fails validation
+ *   launches nothing and touches no memory.  A failed kernel launch returns
+ *   GDR_ERR_HIP.  No exception or abort crosses the ABI.  The library keeps no
+ *   mutable global state; concurrent calls on different streams are safe when
+ *   their buffers do not overlap.
+ * - NaN or Inf in the inputs propagate to the outputs; they are not detected.
+ */
+#ifndef GDR_H_
+#define GDR_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDR_ABI_VERSION 1
+
+typedef enum {
+  GDR_OK = 0,
+  GDR_ERR_INVALID_ARGUMENT = 1, /* NULL pointer, negative size, bad enum, struct_size */
+  GDR_ERR_UNSUPPORTED = 2,      /* valid but not built: dk, dv or chunk outside the list below */
+  GDR_ERR_MISALIGNED = 3,       /* a tensor pointer is not 16-byte aligned */
+  GDR_ERR_WORKSPACE_TOO_SMALL = 4,
+  GDR_ERR_HIP = 5               /* the HIP runtime reported an error at launch */
+} gdr_status;
+
+typedef enum { GDR_BF16 = 0, GDR_FP32 = 1 } gdr_dtype;
+typedef enum { GDR_GATE_NONE = 0, GDR_GATE_SCALAR = 1, GDR_GATE_CHANNEL = 2 } gdr_gate;
+typedef enum { GDR_ERASE_THEN_DECAY = 0, GDR_DECAY_THEN_ERASE = 1 } gdr_order;
+
+/* Problem description.  Set struct_size = sizeof(gdr_problem).
+ * Supported: dk in {16, 32, 64, 128}; dv a multiple of 16 in [16, 256];
+ * chunk == 64 (0 selects 64); batch, heads >= 0; seqlen >= 0 (any value: a
+ * ragged last chunk is padded with identity tokens inside the kernel). */
+typedef struct {
+  int32_t struct_size;
+  int32_t io_dtype;   /* gdr_dtype */
+  int64_t batch, heads, seqlen, dk, dv;
+  int32_t chunk;      /* chunk length of the prefill's chunkwise form */
+  int32_t alpha_kind; /* gdr_gate */
+  int32_t b_kind;     /* gdr_gate */
+  int32_t w_kind;     /* gdr_gate */
+  int32_t order;      /* gdr_order */
+  int32_t reserved;   /* must be 0 */
+} gdr_problem;
+
+/* ABI version of the loaded library (GDR_ABI_VERSION). */
+int gdr_abi_version(void);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* gdr_status_string(int status);
+
+/* Workspace bytes gdr_chunk_fwd needs for `p` (0 when none); 0 also for an
+ * invalid problem.  The current kernels keep every intermediate on chip, so
+ * this is 0 for every supported problem. */
+size_t gdr_chunk_fwd_workspace_bytes(const gdr_problem* p);
+
+/*
+ * Chunkwise prefill: runs the recurrence over all p->seqlen tokens of every
+ * (batch, head) from S0 and returns every read-out o_t and the final state.
+ *   q, k, v, log_alpha, b, w   inputs as described above (device, read only)
+ *   S0     [B,H,dk,dv] fp32 initial state; NULL means zeros
+ *   o      [B,T,H,dv] io_dtype output; must not overlap any input
+ *   S_T    [B,H,dk,dv] fp32 final state; NULL means "not needed"; may alias S0
+ *          (in-place update), must not partially overlap it
+ *   workspace, workspace_bytes  device scratch of at least
+ *          gdr_chunk_fwd_workspace_bytes(p) bytes (may be NULL when that is 0)
+ * Method: the chunkwise form the "Recurrent Memory" post points to in
+ * section 03 (the erase is linear, so a chunk of tokens reassociates into
+ * matrix products and one unit-lower-triangular solve) with the decay entering
+ * through prefix sums of log alpha (section 04) and, for a per-channel decay,
+ * folded into separate erase factors as the Gated DeltaNet-2 abstract
+ * describes.  The result equals the token-by-token recurrence up to rounding.
+ */
+int gdr_chunk_fwd(const gdr_problem* p, const void* q, const void* k, const void* v,
+                  const void* log_alpha, const void* b, const void* w, const float* S0,
+                  void* o, float* S_T, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * One decode step (p->seqlen must be 1): for every (batch, head) applies the
+ * recurrence to the single token and updates S in place.
+ *   q, k, v, log_alpha, b, w   [B,1,H,*] inputs (same layouts with T = 1)
+ *   S      [B,H,dk,dv] fp32 state, read and overwritten in place
+ *   o      [B,1,H,dv] io_dtype read-out; must not overlap any input or S
+ * One pass over S: the two dk-reductions (the erase read (b . k) S and the
+ * query read) share a single read of S, then the updated S is written once.
+ * "Recurrent Memory", section 03 (read, delta, write back) and section 05.
+ */
+int gdr_decode_step(const gdr_problem* p, const void* q, const void* k, const void* v,
+                    const void* log_alpha, const void* b, const void* w, float* S, void* o,
+                    void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GDR_H_ */
