@@ -1,0 +1,229 @@
+"""Benchmark: chunkwise prefill of the Gated DeltaNet workload (B=4, H=16, T=4096, d_k=d_v=128,
+chunk 64, bf16 inputs, fp32 state) and the Gated DeltaNet-2 decode step (256 x 32 states, 1000
+steps), on one MI355X, through the C ABI.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gdn|kda|gdn2]
+                    [--decode-steps N] [--no-cpu-baseline] [--no-decode]
+
+Prints ONE JSON line.  `value` is prefill tokens/s (B*T / time per call) with inputs resident in
+HBM; a step is one gdr_chunk_fwd call over the whole batch.  Two input sets alternate between
+calls so that the 256 MB Infinity Cache cannot serve a call from the previous one.
+`roofline` is for the prefill kernel: algorithmic HBM bytes per launch (inputs read once,
+o and S_T written once, S0 read once) divided by the mean kernel time from HIP events on the
+launch stream, against MI355X's 8 TB/s; `mfma_frac` is algorithmic FLOP per second against the
+2.5166 PFLOP/s dense bf16 peak.  `decode` reports state GB/s for the decode workload (the
+state is read and written once per step).  `cpu_baseline` times the fp64 oracle on the host.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2516.6
+METRIC = "prefill tokens/s + %bf16 MFMA peak; decode state GB/s + %HBM peak"
+
+
+def flops_per_head_token(d, C, channel_two_factor):
+    """Algorithmic FLOP of the chunk form per (head, token); triangular products count half.
+    Rank-one form: 6d^2 + 5Cd + C^2/3; per-channel decay applied after the erase:
+    8d^2 + 9Cd + C^2/3."""
+    if channel_two_factor:
+        return 8 * d * d + 9 * C * d + C * C / 3.0
+    return 6 * d * d + 5 * C * d + C * C / 3.0
+
+
+def prefill_bytes(wl):
+    """Minimal HBM bytes of one prefill call: every input read once, o and S_T written once."""
+    es = 2 if wl.dtype == "bf16" else 4
+    rows = wl.B * wl.T * wl.H
+    gate = {"none": 0, "scalar": 1, "channel": wl.DK}
+    n = rows * (2 * wl.DK + 2 * wl.DV) * es  # q, k, v, o
+    n += rows * gate[wl.alpha] * es
+    if wl.shared_beta:
+        n += rows * es if wl.b != "none" else 0
+    else:
+        n += rows * gate[wl.b] * es
+        n += rows * {"none": 0, "scalar": 1, "channel": wl.DV}[wl.w] * es
+    state = wl.B * wl.H * wl.DK * wl.DV * 4
+    n += state * (2 if wl.s0_std > 0 else 1)  # S0 read (if any) and S_T written
+    return n
+
+
+def decode_bytes(wl):
+    es = 2
+    n_state = wl.B * wl.H
+    state = n_state * wl.DK * wl.DV * 4
+    io = n_state * (wl.DK * 4 + wl.DV * 3) * es  # q, k, log alpha, b; v, w, o
+    return 2 * state + io
+
+
+def time_prefill(wl, steps, warmup, dev):
+    import torch
+    import gated_delta_rule_71_amd as gdr
+    import synth
+    sets = []
+    for s in range(2):
+        x = synth.make_prefill(wl, seed=wl.seed + 17 * s)
+        sets.append({n: (None if t is None else t.to(dev)) for n, t in x.items()})
+    outs = [torch.empty((wl.B, wl.T, wl.H, wl.DV), dtype=sets[0]["q"].dtype, device=dev)
+            for _ in range(2)]
+    S_T = [torch.empty((wl.B, wl.H, wl.DK, wl.DV), dtype=torch.float32, device=dev) for _ in range(2)]
+
+    def call(i):
+        g = sets[i % 2]
+        gdr.chunk_fwd(g["q"], g["k"], g["v"], g["log_alpha"], g["b"], g["w"], g["S0"],
+                      out=outs[i % 2], final_state=S_T[i % 2])
+
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        call(i)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))  # ms, one launch each
+    mean = sum(per) / len(per)
+    return dict(wall_s=wall, mean_ms=mean, median_ms=per[len(per) // 2], p10_ms=per[len(per) // 10],
+                p90_ms=per[(9 * len(per)) // 10])
+
+
+def time_decode(wl, n_steps, dev):
+    import torch
+    import gated_delta_rule_71_amd as gdr
+    import synth
+    S = synth.make_decode_state(wl, dev)
+    st = synth.make_decode_steps(wl, n_steps, dev)
+    o = torch.empty((wl.B, 1, wl.H, wl.DV), dtype=torch.bfloat16, device=dev)
+
+    def call(i):
+        gdr.decode_step(st["q"][i], st["k"][i], st["v"][i], st["log_alpha"][i], st["b"][i],
+                        st["w"][i], S, out=o)
+
+    for i in range(min(20, n_steps)):
+        call(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(n_steps):
+        call(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n_steps
+    del st
+    return ms
+
+
+def cpu_baseline(wl):
+    """The fp64 oracle, as it stands, on the host cores, on the whole prefill workload."""
+    import oracle
+    import synth
+    cores = len(os.sched_getaffinity(0))
+    threads = min(cores, 16)
+    x = synth.make_prefill(wl)
+    t0 = time.perf_counter()
+    oracle.forward(x["q"], x["k"], x["v"], x["log_alpha"], x["b"], x["w"], x["S0"], n_threads=threads)
+    dt = time.perf_counter() - t0
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": wl.B * wl.T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "whole %s workload (B=%d, H=%d, T=%d), fp64 recurrence, %.1f s wall on %s"
+                      % (wl.name, wl.B, wl.H, wl.T, dt, model or "host")}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="gdn", choices=["gdn", "kda", "gdn2"])
+    ap.add_argument("--decode-steps", type=int, default=None)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run a plain 1 GiB device copy (read 1 GiB, write 1 GiB): the "
+                         "reference dispatch that scales rocprofv3 FETCH_SIZE / WRITE_SIZE")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the recurrence runs per (batch, head) state with no "
+              "communication, and this build has no multi-GPU path (--gpus %d requested)"
+              % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    dev = torch.device("cuda:0")
+    if args.calibrate_copy:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    wl = synth.WORKLOADS[args.workload]
+    two = wl.alpha == "channel"  # erase-then-decay with a per-channel decay: two key families
+    pf = time_prefill(wl, args.steps, args.warmup, dev)
+    tokens = wl.B * wl.T
+    sec = pf["mean_ms"] * 1e-3
+    flops = flops_per_head_token(wl.DK, 64, two) * wl.B * wl.T * wl.H
+    nbytes = prefill_bytes(wl)
+    achieved_gbs = nbytes / sec / 1e9
+    out = {
+        "metric": METRIC,
+        "value": tokens / sec,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": pf["wall_s"] * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; shapes of the %s workload)" % wl.name,
+        "config": {"workload": wl.name, "batch": wl.B, "heads": wl.H, "seq_len": wl.T,
+                   "d_k": wl.DK, "d_v": wl.DV, "chunk": 64, "state": "fp32",
+                   "decay": wl.alpha, "erase_gate": wl.b, "write_gate": wl.w},
+        "kernel_ms": {"mean": pf["mean_ms"], "median": pf["median_ms"], "p10": pf["p10_ms"],
+                      "p90": pf["p90_ms"]},
+        "mfma_frac": flops / sec / (PEAK_BF16_TFLOPS * 1e12),
+        "tflops": flops / sec / 1e12,
+        "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved_gbs / PEAK_HBM_GBS, "traffic": None},
+    }
+    if not args.no_decode:
+        dw = synth.WORKLOADS["decode"]
+        n = args.decode_steps or dw.steps
+        ms = time_decode(dw, n, dev)
+        db = decode_bytes(dw)
+        gbs = db / (ms * 1e-3) / 1e9
+        out["decode"] = {"workload": "decode", "batch": dw.B, "heads": dw.H, "d_k": dw.DK,
+                         "d_v": dw.DV, "steps": n, "us_per_step": ms * 1e3,
+                         "states_per_s": dw.B * dw.H / (ms * 1e-3), "value": gbs, "unit": "GB/s",
+                         "hbm_frac": gbs / PEAK_HBM_GBS, "bytes_per_step": db}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -109,7 +109,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs<IO> a) {
     sh_dot[wave][0] = dot_qk;
     sh_dot[wave][1] = dot_gamma;
   }
-  __syncthreads();
+  lds_barrier();
 
   // 3) both dk-reductions from the same registers
   float r[4] = {0.f, 0.f, 0.f, 0.f}, y[4] = {0.f, 0.f, 0.f, 0.f};
@@ -136,7 +136,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs<IO> a) {
       sh_red[wave][1][cq * 4 + j] = y[j];
     }
   }
-  __syncthreads();
+  lds_barrier();
   for (int n = tid; n < NCB; n += NT) {
     float rs = 0.f, ys = 0.f;
 #pragma unroll
@@ -147,7 +147,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs<IO> a) {
     sh_r[n] = rs;
     sh_y[n] = ys;
   }
-  __syncthreads();
+  lds_barrier();
 
   // 4) update in registers, write S back once
   float rv[4], xv[4];

@@ -52,4 +52,14 @@ __device__ __forceinline__ void st(IO* p, int64_t i, float f) {
 
 enum GateKind : int { kNone = 0, kScalar = 1, kChannel = 2 };
 
+// Workgroup barrier that orders LDS accesses only.  __syncthreads() also carries a
+// workgroup-scope release fence, which on gfx950 waits for every outstanding global load and
+// store of the wave (vmcnt(0)); the kernels here share data between waves through LDS alone,
+// so global prefetches and output stores may stay in flight across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 }  // namespace gdr

@@ -5,7 +5,16 @@
 
 namespace gdr {
 
+bool prefill_scalar_ok(int64_t T, int64_t H, int64_t DK, int64_t DV, int b_kind);
+hipError_t prefill_scalar_launch(PrefillArgs<bf16_t> a, int64_t nstate, int64_t DK, hipStream_t s);
+
 namespace {
+
+// GDR_PREFILL_PIPE=0 selects the generic kernel for scalar-decay problems (comparisons only).
+bool pipelined_enabled() {
+  const char* e = getenv("GDR_PREFILL_PIPE");
+  return !(e && e[0] == '0');
+}
 
 // MODE 0: scalar (or no) decay; 1: per-channel decay applied before the erase;
 // 2: per-channel decay applied after the erase (the unified equation's order).
@@ -56,6 +65,8 @@ hipError_t launch_prefill(const IO* q, const IO* k, const IO* v, const IO* la, c
   PrefillArgs<IO> a{q, k, v, la, bg, wg, S0, o, S_T, T, H, DV, alpha_kind, b_kind, w_kind, 1};
   const int64_t nstate = B * H;
   if constexpr (sizeof(IO) == 2) {
+    if (mode == 0 && prefill_scalar_ok(T, H, DK, DV, b_kind) && pipelined_enabled())
+      return prefill_scalar_launch(a, nstate, DK, stream);
     const int nsw = choose_nsw_bf16(DK, DV, mode);
     if (nsw == 0) return hipErrorInvalidValue;
     a.nsl = static_cast<int>(DV / (16 * nsw));

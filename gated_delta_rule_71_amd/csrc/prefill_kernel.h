@@ -44,6 +44,11 @@
 #include "gdr_common.h"
 #include "mfma.h"
 
+// Phase markers: no-ops unless a profiling build defines GDR_MARK before including this file.
+#ifndef GDR_MARK
+#define GDR_MARK(id) ((void)0)
+#endif
+
 namespace gdr {
 
 constexpr int kLdsLimit = 163840;  // bytes of LDS one gfx950 workgroup may use
@@ -198,7 +203,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs<IO> a) {
     const int64_t t0 = ch * C;
     const int nval = static_cast<int>(a.T - t0 < C ? a.T - t0 : C);
     auto row_of = [&](int t) -> int64_t { return (bi * a.T + t0 + t) * a.H + hi; };
-    __syncthreads();  // the previous chunk's readers of every LDS array are done
+    lds_barrier();  // the previous chunk's readers of every LDS array are done
+    GDR_MARK(0);
 
     // ---------------- phase A: X^T, gate prefix sums, scaled operands ----------------
     {
@@ -267,7 +273,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs<IO> a) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) segtot[ts * DK + d0 + j] = run[j];
       }
-      __syncthreads();
+      lds_barrier();
       if (tid < DK) {
         float run = 0.f;
         for (int s = 0; s < NSEG; ++s) {
@@ -282,8 +288,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs<IO> a) {
         fEGn[tid] = __expf(run);
       }
     }
-    __syncthreads();
+    lds_barrier();
 
+    GDR_MARK(1);
     if (act) {
       float off[8], ref[8], gn[8];
       if (MODE != 0) {
@@ -355,7 +362,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs<IO> a) {
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
+    GDR_MARK(2);
 
     // ---------------- phase B: Gram tiles of the lower triangle ----------------
     {
@@ -399,7 +407,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs<IO> a) {
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
+    GDR_MARK(3);
 
     // ---------------- phase C: inverses of the four 16x16 diagonal blocks ----------------
     if (wave == 0) {
@@ -415,7 +424,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs<IO> a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) dInv[(blk * 16 + i) * LDI + j] = to_ot<OT>(x[i]);
     }
-    __syncthreads();
+    lds_barrier();
+    GDR_MARK(4);
 
     // ---------------- phase D: state waves ----------------
     if (sside) {
@@ -523,6 +533,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs<IO> a) {
         S[tl] = MM::mma8(lds_pair_frag(pr, 32, g, C), rf[1], S[tl]);
       }
     }
+    GDR_MARK(5);
   }
 
   if (sside && a.S_T != nullptr) {
