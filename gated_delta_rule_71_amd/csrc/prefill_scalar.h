@@ -40,12 +40,18 @@ struct ScalarLayout {
   static constexpr int oI = oM + C * LDD * 2;
   static constexpr int oS = oI + 4 * 16 * LDI * 2;  // fp32: G, e^G, e^{Gn-G}, beta (64 each), e^Gn
   static constexpr int BUF = oS + (4 * C + 4) * 4;   // bytes per buffer
-  static constexpr int oLD = 2 * BUF;                // fp32 diagonal blocks of A [4][16][17]
-  static constexpr int total = oLD + 4 * 16 * 17 * 4;
+  static constexpr int LDL = 20;                     // column pitch of the fp32 diagonal blocks
+  static constexpr int oLD = 2 * BUF;                // fp32 diagonal blocks of A, column-major
+  static constexpr int total = oLD + 4 * 16 * LDL * 4;
   static constexpr bool fits = total <= kLdsLimit;
 };
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Channel-major rows (k^T) and value rows (X^T) hold 64 tokens; quads of 4 tokens are stored at
+// quad ^ key(row) so that transposed writes from lanes with different rows hit different banks.
+// Reads of 4 (or 8) consecutive tokens stay contiguous.
+__device__ __forceinline__ int swz(int row_key, int t) { return (((t >> 2) ^ row_key) << 2) | (t & 3); }
 
 // Raw buffer resource over `bytes` bytes from `base` (gfx9 descriptor word 3).  Loads past the
 // range return zero and stores past it are dropped, which pads the ragged last chunk.
@@ -67,7 +73,7 @@ __device__ __forceinline__ uint16_t buf_load_u16(__amdgpu_buffer_rsrc_t r, uint3
 // for i < t (off-diagonal blocks to gA as -A, diagonal blocks to Ld in fp32); prod 1:
 // M = q_t . k_i e^{G_t - G_i} for i <= t, stored as -M.  All fragments are read before the
 // first MFMA.
-template <int DK, int RA, int RB, int LDT, int LDD, int LDA>
+template <int DK, int RA, int RB, int LDT, int LDD, int LDA, int LDL>
 __device__ __forceinline__ void scalar_gram_pair(const __bf16* rows, const __bf16* tK, int prod,
                                                  int g, int l16, const float* sc, __bf16* gA,
                                                  __bf16* gM, float* Ld) {
@@ -76,28 +82,44 @@ __device__ __forceinline__ void scalar_gram_pair(const __bf16* rows, const __bf1
   constexpr int C = 64, NKB = DK / 32, NT = RA + RB + 2;
   auto tile_a = [](int j) { return j <= RA ? RA : RB; };
   auto tile_b = [](int j) { return j <= RA ? j : j - RA - 1; };
-  // epilogue of tile j: decay mask, beta, and the stores (software-pipelined one tile behind)
+  // Tiles are computed transposed (k block as the A operand) so that each lane ends up with four
+  // consecutive columns of one output row: one 8-byte store.  The diagonal tiles of A are
+  // computed upright and stored column-major in fp32 for the inverse.
+  auto diag_a = [&](int j) { return prod == 0 && tile_a(j) == tile_b(j); };
   auto epilogue = [&](int j, const f32x4& acc) {
     const int ta = tile_a(j), tb = tile_b(j);
-    const int cc = 16 * tb + l16;
-    const float gc = sc[cc];
-    const float4 gr4 = *reinterpret_cast<const float4*>(sc + 16 * ta + 4 * g);
-    const float4 br4 = *reinterpret_cast<const float4*>(sc + 3 * C + 16 * ta + 4 * g);
-    const float gr[4] = {gr4.x, gr4.y, gr4.z, gr4.w}, br[4] = {br4.x, br4.y, br4.z, br4.w};
+    if (diag_a(j)) {
+      const int cc = 16 * tb + l16;
+      const float gc = sc[cc];
+      const float4 gr4 = *reinterpret_cast<const float4*>(sc + 16 * ta + 4 * g);
+      const float4 br4 = *reinterpret_cast<const float4*>(sc + 3 * C + 16 * ta + 4 * g);
+      const float gr[4] = {gr4.x, gr4.y, gr4.z, gr4.w}, br[4] = {br4.x, br4.y, br4.z, br4.w};
+      float4 o;
+      float* ov = reinterpret_cast<float*>(&o);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * ta + 4 * g + i;
+        ov[i] = cc < r ? acc[i] * __expf(fminf(gr[i] - gc, 0.f)) * br[i] : 0.f;
+      }
+      *reinterpret_cast<float4*>(Ld + (ta * 16 + l16) * LDL + 4 * g) = o;  // column l16, rows 4g..
+      return;
+    }
+    const int r = 16 * ta + l16, cc0 = 16 * tb + 4 * g;
+    const float gr = sc[r], br = prod == 0 ? sc[3 * C + r] : 1.f;
+    const float4 gc4 = *reinterpret_cast<const float4*>(sc + cc0);
+    const float gc[4] = {gc4.x, gc4.y, gc4.z, gc4.w};
+    bf16x4 o;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r = 16 * ta + 4 * g + i;
+      const int cc = cc0 + i;
       const bool keep = prod == 0 ? (cc < r) : (cc <= r);
-      const float val =
-          keep ? acc[i] * __expf(fminf(gr[i] - gc, 0.f)) * (prod == 0 ? br[i] : 1.f) : 0.f;
-      if (prod == 1) {
-        gM[r * LDD + cc] = static_cast<__bf16>(-val);
-      } else if (ta > tb) {
-        gA[(r - 16) * LDA + cc] = static_cast<__bf16>(-val);
-      } else {
-        Ld[(ta * 16 + (r & 15)) * 17 + (cc & 15)] = val;
-      }
+      o[i] = static_cast<__bf16>(keep ? -acc[i] * __expf(fminf(gr - gc[i], 0.f)) * br : 0.f);
     }
+    // element stores: writing the four values as one 8-byte store gave wrong M rows on the
+    // dk <= 64 instantiations (not understood; element stores verified on every shape tested)
+    __bf16* dst = prod == 1 ? gM + r * LDD + cc0 : gA + (r - 16) * LDA + cc0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dst[i] = o[i];
   };
   F8 rf[NKB], cb[2][NKB];
 #pragma unroll
@@ -119,8 +141,13 @@ __device__ __forceinline__ void scalar_gram_pair(const __bf16* rows, const __bf1
         cb[(j + 1) & 1][kb] = lds_load8(tK + (16 * nb + l16) * LDT + 32 * kb + 8 * g);
     }
     acc[j & 1] = zero4();
+    if (diag_a(j)) {
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) acc[j & 1] = MM::mma8(rf[kb], cb[j & 1][kb], acc[j & 1]);
+      for (int kb = 0; kb < NKB; ++kb) acc[j & 1] = MM::mma8(rf[kb], cb[j & 1][kb], acc[j & 1]);
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) acc[j & 1] = MM::mma8(cb[j & 1][kb], rf[kb], acc[j & 1]);
+    }
     if (j > 0) epilogue(j - 1, acc[(j - 1) & 1]);
   }
   epilogue(NT - 1, acc[(NT - 1) & 1]);
@@ -143,8 +170,8 @@ __global__ __launch_bounds__(256 + 64 * NSW) void prefill_scalar_kernel(PrefillA
   __shared__ __attribute__((aligned(32))) unsigned char smem[L::total];
   float* Ld = reinterpret_cast<float*>(smem + L::oLD);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = lane >> 4, l16 = lane & 15;
+  const int tid = threadIdx.x, wave = tid >> 6;
+  int lane = tid & 63, g = lane >> 4, l16 = lane & 15;
   const bool key = wave < 4;
 
   const int64_t nb = gridDim.x, bid = blockIdx.x;
@@ -239,7 +266,8 @@ __global__ __launch_bounds__(256 + 64 * NSW) void prefill_scalar_kernel(PrefillA
       uint16_t* kTu = reinterpret_cast<uint16_t*>(kT);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        uint16_t* dst = kTu + (cg * 8 + e) * LDD + tb;
+        const int row = cg * 8 + e;
+        uint16_t* dst = kTu + row * LDD + swz((row >> 3) & 15, tb);
         if constexpr (IPT == 4) {
           *reinterpret_cast<uint2*>(dst) =
               make_uint2(kh[e][0] | (uint32_t(kh[e][1]) << 16), kh[e][2] | (uint32_t(kh[e][3]) << 16));
@@ -266,7 +294,7 @@ __global__ __launch_bounds__(256 + 64 * NSW) void prefill_scalar_kernel(PrefillA
           for (int e = 0; e < 8; ++e) v8[e] *= bf16_to_f32(pws[j]);
         }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) xT[(xg * 8 + e) * LDD + t] = static_cast<__bf16>(v8[e]);
+        for (int e = 0; e < 8; ++e) xT[(xg * 8 + e) * LDD + swz(2 * xg, t)] = static_cast<__bf16>(v8[e]);
       }
     }
     if (wave == 0) {
@@ -297,9 +325,9 @@ __global__ __launch_bounds__(256 + 64 * NSW) void prefill_scalar_kernel(PrefillA
     const int prod = wave >> 1;  // 0: A from k k^T, 1: M from q k^T; row blocks {0,3} or {1,2}
     const __bf16* rows = prod == 0 ? tK : tQ;
     if (wave & 1)
-      scalar_gram_pair<DK, 1, 2, LDT, LDD, LDA>(rows, tK, prod, g, l16, sc, gA, gM, Ld);
+      scalar_gram_pair<DK, 1, 2, LDT, LDD, LDA, L::LDL>(rows, tK, prod, g, l16, sc, gA, gM, Ld);
     else
-      scalar_gram_pair<DK, 0, 3, LDT, LDD, LDA>(rows, tK, prod, g, l16, sc, gA, gM, Ld);
+      scalar_gram_pair<DK, 0, 3, LDT, LDD, LDA, L::LDL>(rows, tK, prod, g, l16, sc, gA, gM, Ld);
   };
 
   // ---------------- key phase 3: inverses of the diagonal blocks of (I + A) ----------------
@@ -311,14 +339,25 @@ __global__ __launch_bounds__(256 + 64 * NSW) void prefill_scalar_kernel(PrefillA
     if (wave < 2 && lane < 32) {
       const int blk = (lane < 16) ? (wave == 0 ? 0 : 1) : (wave == 0 ? 3 : 2);
       const int j = l16;
+      // column sweep: once x_m is final, every later x_i drops L[i][m] x_m (independent FMAs);
+      // column m+1 is read while column m is applied
       float x[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float* row = Ld + (blk * 16 + i) * 17;
-        float s2 = (i == j) ? 1.f : 0.f;
+      for (int i = 0; i < 16; ++i) x[i] = (i == j) ? 1.f : 0.f;
+      float4 col[2][4];
+      auto load_col = [&](int m, float4* c) {
+        const float* p = Ld + (blk * 16 + m) * L::LDL;
 #pragma unroll
-        for (int m = 0; m < i; ++m) s2 -= row[m] * x[m];
-        x[i] = s2;
+        for (int q4 = 0; q4 < 4; ++q4)
+          if (4 * q4 + 3 > m) c[q4] = *reinterpret_cast<const float4*>(p + 4 * q4);
+      };
+      load_col(0, col[0]);
+#pragma unroll
+      for (int m = 0; m < 15; ++m) {
+        if (m + 1 < 15) load_col(m + 1, col[(m + 1) & 1]);
+        const float* cv = reinterpret_cast<const float*>(col[m & 1]);
+#pragma unroll
+        for (int i = m + 1; i < 16; ++i) x[i] -= cv[i] * x[m];
       }
 #pragma unroll
       for (int i = 0; i < 16; ++i) dInv[(blk * 16 + i) * LDI + j] = static_cast<__bf16>(x[i]);
@@ -354,6 +393,11 @@ __global__ __launch_bounds__(256 + 64 * NSW) void prefill_scalar_kernel(PrefillA
   lds_barrier();
 
   for (int64_t ch = 0; ch < nch; ++ch) {
+    // Lane indices are made opaque once per chunk so that the compiler recomputes the
+    // lane-dependent LDS addresses inside the loop instead of holding dozens of them (and the
+    // identity used by the inverse) in registers across it, which spilled to scratch; every
+    // scratch reload waits for all outstanding global loads and defeated the prefetch.
+    asm volatile("" : "+v"(lane), "+v"(g), "+v"(l16));
     const int64_t t0 = ch * C;
     unsigned char* B = buf(ch);
     const float* sc = reinterpret_cast<const float*>(B + L::oS);
@@ -386,7 +430,8 @@ __global__ __launch_bounds__(256 + 64 * NSW) void prefill_scalar_kernel(PrefillA
         if (ta < 3) load_tile(ta + 1, kf[(ta + 1) & 1], qf[(ta + 1) & 1]);
         const float4 e4 = *reinterpret_cast<const float4*>(sc + C + 16 * ta + 4 * g);
         const float4 b4 = *reinterpret_cast<const float4*>(sc + 3 * C + 16 * ta + 4 * g);
-        const bf16x4 x4 = *reinterpret_cast<const bf16x4*>(xT + nloc * LDD + 16 * ta + 4 * g);
+        const bf16x4 x4 =
+            *reinterpret_cast<const bf16x4*>(xT + nloc * LDD + swz(2 * (nloc >> 3), 16 * ta + 4 * g));
         V[ta] = zero4();
         O[ta] = zero4();
 #pragma unroll
@@ -401,6 +446,7 @@ __global__ __launch_bounds__(256 + 64 * NSW) void prefill_scalar_kernel(PrefillA
           O[ta][i] *= e[i];
         }
       }
+      GDR_MARK(4);
       const __bf16* gA = reinterpret_cast<const __bf16*>(B + L::oA);
       const __bf16* gM = reinterpret_cast<const __bf16*>(B + L::oM);
       const __bf16* dInv = reinterpret_cast<const __bf16*>(B + L::oI);
@@ -427,6 +473,7 @@ __global__ __launch_bounds__(256 + 64 * NSW) void prefill_scalar_kernel(PrefillA
       }
       const F8 rf0 = acc_pair_frag<__bf16>(R[0], R[1]);
       const F8 rf1 = acc_pair_frag<__bf16>(R[2], R[3]);
+      GDR_MARK(5);
       {
         f32x4 Rs[4];
 #pragma unroll
@@ -457,16 +504,28 @@ __global__ __launch_bounds__(256 + 64 * NSW) void prefill_scalar_kernel(PrefillA
     GDR_MARK(2);
     if (key) {
       if (ch + 2 < nch) prefetch(ch + 2);
+      GDR_MARK(4);
       if (more) {
         key_gram(ch + 1);
+        GDR_MARK(5);
         key_inverse(ch + 1);
       }
     } else {
       const __bf16* kT = reinterpret_cast<const __bf16*>(B + L::oKT);
       F8 kf[2][2];
       auto load_kt = [&](int tl, F8* o) {
-        o[0] = lds_pair_frag(kT + (16 * tl + l16) * LDD, 0, g, C);
-        o[1] = lds_pair_frag(kT + (16 * tl + l16) * LDD, 32, g, C);
+        const int row = 16 * tl + l16, key = (row >> 3) & 15;
+        const __bf16* kr = kT + row * LDD;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const bf16x4 lo = lds_load4(kr + swz(key, 32 * kb + 4 * g));
+          const bf16x4 hi = lds_load4(kr + swz(key, 32 * kb + 16 + 4 * g));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            o[kb][e] = lo[e];
+            o[kb][4 + e] = hi[e];
+          }
+        }
       };
       load_kt(0, kf[0]);
       const F8 rf0 = rsf[0], rf1 = rsf[1];
