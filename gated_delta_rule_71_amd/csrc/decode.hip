@@ -20,6 +20,8 @@
 
 namespace gdr {
 
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
 template <typename IO>
 struct DecodeArgs {
   const IO* q;
@@ -66,11 +68,14 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs<IO> a) {
   const int64_t col0 = (blk % a.ncb_per_state) * NCB;
   float* Sp = a.S + bh * DK * a.DV + col0;
 
-  // 1) issue the state loads first: they are the only long-latency traffic
-  float4 s[NPASS];
+  // 1) issue the state loads first: they are the only long-latency traffic.  The state is
+  // streamed (read once, written once per step, far larger than the caches), so both
+  // directions use nontemporal accesses.
+  f32x4v s[NPASS];
 #pragma unroll
   for (int p = 0; p < NPASS; ++p)
-    s[p] = *reinterpret_cast<const float4*>(Sp + (int64_t)(p * RPP + rr) * a.DV + cq * 4);
+    s[p] = __builtin_nontemporal_load(
+        reinterpret_cast<const f32x4v*>(Sp + (int64_t)(p * RPP + rr) * a.DV + cq * 4));
 
   // 2) per-channel vectors of this token
   float dot_qk = 0.f, dot_gamma = 0.f;
@@ -117,8 +122,11 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs<IO> a) {
   for (int p = 0; p < NPASS; ++p) {
     const int d = p * RPP + rr;
     const float cp = sh_cp[d], qa = sh_qa[d];
-    r[0] += cp * s[p].x; r[1] += cp * s[p].y; r[2] += cp * s[p].z; r[3] += cp * s[p].w;
-    y[0] += qa * s[p].x; y[1] += qa * s[p].y; y[2] += qa * s[p].z; y[3] += qa * s[p].w;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      r[j] += cp * s[p][j];
+      y[j] += qa * s[p][j];
+    }
   }
   // rows that share a column live in the same wave at lane strides of TPR
 #pragma unroll
@@ -160,12 +168,10 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs<IO> a) {
   for (int p = 0; p < NPASS; ++p) {
     const int d = p * RPP + rr;
     const float al = sh_al[d], kp = sh_kp[d], kd = sh_k[d];
-    float4 o4;
-    o4.x = al * s[p].x - kp * rv[0] + kd * xv[0];
-    o4.y = al * s[p].y - kp * rv[1] + kd * xv[1];
-    o4.z = al * s[p].z - kp * rv[2] + kd * xv[2];
-    o4.w = al * s[p].w - kp * rv[3] + kd * xv[3];
-    *reinterpret_cast<float4*>(Sp + (int64_t)d * a.DV + cq * 4) = o4;
+    f32x4v o4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o4[j] = al * s[p][j] - kp * rv[j] + kd * xv[j];
+    __builtin_nontemporal_store(o4, reinterpret_cast<f32x4v*>(Sp + (int64_t)d * a.DV + cq * 4));
   }
 
   // 5) read-out

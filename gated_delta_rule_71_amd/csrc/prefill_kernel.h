@@ -81,7 +81,7 @@ struct PrefillLayout {
   static constexpr int oINV = oGMQK + (TWO ? GRAM_BYTES : 0);    // T_ii [4][16][LDI]
   static constexpr int oLD = oINV + 4 * 16 * LDI * ES;           // fp32 L_ii [4][16][17]
   static constexpr int oF = oLD + 4 * 16 * 17 * 4;               // fp32 per-channel / per-token
-  static constexpr int NF = MODE == 0 ? 2 * C + 8 : 4 * DK;
+  static constexpr int NF = MODE == 0 ? 2 * C + 8 : 4 * DK + 4;  // + robust-chunk flag
   static constexpr int total = oF + NF * 4;
   static constexpr bool fits = total <= kLdsLimit;
 };
@@ -164,6 +164,10 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs<IO> a) {
   float* fGn = fF + DK;
   float* fEref = fF + 2 * DK;
   float* fEGn = fF + 3 * DK;
+  int* sRobust = reinterpret_cast<int*>(fF + 4 * DK);  // MODE 1/2: this chunk takes the exact path
+  // Largest |G_t - G_ref| (per channel, within a chunk) for which the split exponentials stay
+  // below the e^80 clamp; chunks beyond it run token by token (robust path, exact).
+  constexpr float kSpanLimit = 76.f;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, l16 = lane & 15;
@@ -203,6 +207,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs<IO> a) {
     const int64_t t0 = ch * C;
     const int nval = static_cast<int>(a.T - t0 < C ? a.T - t0 : C);
     auto row_of = [&](int t) -> int64_t { return (bi * a.T + t0 + t) * a.H + hi; };
+    if (MODE != 0 && tid == 0) sRobust[0] = 0;
     lds_barrier();  // the previous chunk's readers of every LDS array are done
     GDR_MARK(0);
 
@@ -286,9 +291,11 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs<IO> a) {
         fGn[tid] = run;
         fEref[tid] = __expf(ref);
         fEGn[tid] = __expf(run);
+        if (fmaxf(fabsf(ref), fabsf(run - ref)) > kSpanLimit || !(run == run)) sRobust[0] = 1;
       }
     }
     lds_barrier();
+    const bool robust = MODE != 0 && sRobust[0] != 0;
 
     GDR_MARK(1);
     if (act) {
@@ -351,6 +358,16 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs<IO> a) {
             }
           }
         }
+        if (MODE != 0 && robust) {
+          // exact path: raw q, c = b . k, k and log alpha, token-major
+          OT* laArr = TWO ? tP : dP;
+          const int lpitch = TWO ? LDT : ((C * LDT <= DK * LDD) ? LDT : DK);
+          lds_store8(tQ + t * LDT + d0, q);
+          lds_store8(tC + t * LDT + d0, c);
+          lds_store8(tK + t * LDT + d0, k);
+          lds_store8(laArr + t * lpitch + d0, la8[u]);
+          continue;
+        }
         lds_store8(tQ + t * LDT + d0, oq);
         lds_store8(tC + t * LDT + d0, oc);
         lds_store8(tK + t * LDT + d0, ok);
@@ -366,7 +383,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs<IO> a) {
     GDR_MARK(2);
 
     // ---------------- phase B: Gram tiles of the lower triangle ----------------
-    {
+    if (!robust) {
       constexpr int NPROD = TWO ? 4 : 2;
       for (int job = wave; job < NPROD * 10; job += 4) {
         const int prod = job / 10, tix = job % 10;
@@ -411,7 +428,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs<IO> a) {
     GDR_MARK(3);
 
     // ---------------- phase C: inverses of the four 16x16 diagonal blocks ----------------
-    if (wave == 0) {
+    if (wave == 0 && !robust) {
       const int blk = g, j = l16;
       float x[16];
 #pragma unroll
@@ -427,8 +444,62 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs<IO> a) {
     lds_barrier();
     GDR_MARK(4);
 
+    // ---------------- phase D (exact path): token by token, fp32 ----------------
+    // The recurrence itself on this wave's 16 columns: each lane holds rows 16*tl + 4g + i of
+    // column nloc, so the two dk-reductions are a partial sum plus two cross-lane-group adds.
+    if (MODE != 0 && robust && sside) {
+      const OT* laArr = TWO ? tP : dP;
+      const int lpitch = TWO ? LDT : ((C * LDT <= DK * LDD) ? LDT : DK);
+      for (int t = 0; t < nval; ++t) {
+        float qd[NTD][4], kd[NTD][4], cd[NTD][4], al[NTD][4];
+#pragma unroll
+        for (int tl = 0; tl < NTD; ++tl) {
+          const int d = 16 * tl + 4 * g;
+          const auto q4 = lds_load4(tQ + t * LDT + d);
+          const auto k4 = lds_load4(tK + t * LDT + d);
+          const auto c4 = lds_load4(tC + t * LDT + d);
+          const auto l4 = lds_load4(laArr + t * lpitch + d);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            qd[tl][i] = static_cast<float>(q4[i]);
+            kd[tl][i] = static_cast<float>(k4[i]);
+            cd[tl][i] = static_cast<float>(c4[i]);
+            al[tl][i] = __expf(static_cast<float>(l4[i]));
+          }
+        }
+        const float x = static_cast<float>(xT[nloc * LDD + t]);
+        if (!TWO) {  // decay first
+#pragma unroll
+          for (int tl = 0; tl < NTD; ++tl)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) S[tl][i] *= al[tl][i];
+        }
+        float r = 0.f;
+#pragma unroll
+        for (int tl = 0; tl < NTD; ++tl)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) r += cd[tl][i] * S[tl][i];
+        r += __shfl_xor(r, 16);
+        r += __shfl_xor(r, 32);
+        float y = 0.f;
+#pragma unroll
+        for (int tl = 0; tl < NTD; ++tl)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float sv = S[tl][i] - kd[tl][i] * r;
+            if (TWO) sv *= al[tl][i];
+            sv += kd[tl][i] * x;
+            S[tl][i] = sv;
+            y += qd[tl][i] * sv;
+          }
+        y += __shfl_xor(y, 16);
+        y += __shfl_xor(y, 32);
+        if (g == 0) st(a.o, row_of(t) * DV + col0 + nloc, y);
+      }
+    }
+
     // ---------------- phase D: state waves ----------------
-    if (sside) {
+    if (sside && !robust) {
       // (1) S (scaled by e^{G_ref} for a per-channel decay) as B fragments, tile-pair order
       F8 sf[NKB];
 #pragma unroll
