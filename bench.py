@@ -10,7 +10,8 @@ HBM; a step is one gdr_chunk_fwd call over the whole batch.  Two input sets alte
 calls so that the 256 MB Infinity Cache cannot serve a call from the previous one.
 `roofline` is for the prefill kernel: algorithmic HBM bytes per launch (inputs read once,
 o and S_T written once, S0 read once) divided by the mean kernel time from HIP events on the
-launch stream, against MI355X's 8 TB/s; `mfma_frac` is algorithmic FLOP per second against the
+launch stream, against MI355X's 8 TB/s; `traffic` is the measured HBM bytes per launch from
+profiles/hbm_counters.txt when that file was recorded on the current kernel sources, else null; `mfma_frac` is algorithmic FLOP per second against the
 2.5166 PFLOP/s dense bf16 peak.  `decode` reports state GB/s for the decode workload (the
 state is read and written once per step).  `cpu_baseline` times the fp64 oracle on the host.
 """
@@ -60,6 +61,41 @@ def decode_bytes(wl):
     state = n_state * wl.DK * wl.DV * 4
     io = n_state * (wl.DK * 4 + wl.DV * 3) * es  # q, k, log alpha, b; v, w, o
     return 2 * state + io
+
+
+def kernel_source_digest():
+    """SHA-256 over the kernel sources and the build script: HBM counter figures recorded for
+    other sources no longer describe the kernels that run."""
+    import hashlib
+    h = hashlib.sha256()
+    pkg = os.path.join(ROOT, "gated_delta_rule_71_amd")
+    files = sorted(os.path.join("csrc", f) for f in os.listdir(os.path.join(pkg, "csrc")))
+    for rel in files + ["buildlib.py"]:
+        h.update(rel.encode())
+        with open(os.path.join(pkg, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(key):
+    """HBM bytes per launch for `key` ("prefill:<workload>" or "decode:<workload>") from the
+    committed rocprofv3 counter summary, scaled by the calibration copy; None when the summary
+    is absent, has no such entry, or was taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", "hbm_counters.txt")
+    try:
+        lines = open(path).read().splitlines()
+    except OSError:
+        return None
+    digest, found = None, None
+    for line in lines:
+        f = line.split()
+        if len(f) == 2 and f[0] == "source_sha256":
+            digest = f[1]
+        elif len(f) >= 3 and f[0] == "traffic" and f[1] == key:
+            found = float(f[2])
+    if digest != kernel_source_digest():
+        return None
+    return found
 
 
 def time_prefill(wl, steps, warmup, dev):
@@ -176,7 +212,7 @@ def main():
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         for _ in range(2):
-            dst.copy_(src)
+            torch.mul(src, 1.0, out=dst)  # one elementwise kernel: reads 1 GiB, writes 1 GiB
         torch.cuda.synchronize()
         del src, dst
     wl = synth.WORKLOADS[args.workload]
@@ -208,7 +244,9 @@ def main():
         "mfma_frac": flops / sec / (PEAK_BF16_TFLOPS * 1e12),
         "tflops": flops / sec / 1e12,
         "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": achieved_gbs / PEAK_HBM_GBS, "traffic": None},
+                     "frac": achieved_gbs / PEAK_HBM_GBS,
+                     "traffic": recorded_traffic("prefill:" + wl.name),
+                     "algorithmic_bytes": nbytes},
     }
     if not args.no_decode:
         dw = synth.WORKLOADS["decode"]
@@ -219,7 +257,8 @@ def main():
         out["decode"] = {"workload": "decode", "batch": dw.B, "heads": dw.H, "d_k": dw.DK,
                          "d_v": dw.DV, "steps": n, "us_per_step": ms * 1e3,
                          "states_per_s": dw.B * dw.H / (ms * 1e-3), "value": gbs, "unit": "GB/s",
-                         "hbm_frac": gbs / PEAK_HBM_GBS, "bytes_per_step": db}
+                         "hbm_frac": gbs / PEAK_HBM_GBS, "bytes_per_step": db,
+                         "traffic": recorded_traffic("decode:decode")}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(out), flush=True)
