@@ -119,6 +119,70 @@ __device__ __forceinline__ void load8f(const float* p, float* out) {
   out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
 }
 
+// Raw buffer resource over `bytes` bytes from `base` (gfx9 descriptor word 3).  Loads past the
+// range return zero and stores past it are dropped, which pads the ragged last chunk.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+// Raw 16-bit load; converted to fp32 only where the value is used, so that issuing the load
+// does not wait for it.
+__device__ __forceinline__ uint16_t buf_load_u16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+
+// Eight consecutive I/O elements held in registers in their I/O encoding: a prefetch issues the
+// load and nothing waits for it until the values are converted.
+template <typename IO>
+struct Raw8;
+template <>
+struct Raw8<bf16_t> {
+  uint4 u;
+};
+template <>
+struct Raw8<float> {
+  float4 a, b;
+};
+__device__ __forceinline__ Raw8<bf16_t> raw8_load(const bf16_t* p) {
+  return {*reinterpret_cast<const uint4*>(p)};
+}
+__device__ __forceinline__ Raw8<float> raw8_load(const float* p) {
+  const float4* q = reinterpret_cast<const float4*>(p);
+  return {q[0], q[1]};
+}
+__device__ __forceinline__ void raw8_zero(Raw8<bf16_t>& r) { r.u = make_uint4(0, 0, 0, 0); }
+__device__ __forceinline__ void raw8_zero(Raw8<float>& r) {
+  r.a = make_float4(0.f, 0.f, 0.f, 0.f);
+  r.b = r.a;
+}
+__device__ __forceinline__ void raw8_cvt(const Raw8<bf16_t>& r, float* out) {
+  load8f(reinterpret_cast<const bf16_t*>(&r.u), out);
+}
+__device__ __forceinline__ void raw8_cvt(const Raw8<float>& r, float* out) {
+  out[0] = r.a.x; out[1] = r.a.y; out[2] = r.a.z; out[3] = r.a.w;
+  out[4] = r.b.x; out[5] = r.b.y; out[6] = r.b.z; out[7] = r.b.w;
+}
+__device__ __forceinline__ void raw8_buf(Raw8<bf16_t>& r, __amdgpu_buffer_rsrc_t rs, uint32_t off) {
+  r.u = buf_load16(rs, off);
+}
+__device__ __forceinline__ void raw8_buf(Raw8<float>& r, __amdgpu_buffer_rsrc_t rs, uint32_t off) {
+  r.a = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+  r.b = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16, 0, 0));
+}
+__device__ __forceinline__ void raw1_buf(bf16_t& x, __amdgpu_buffer_rsrc_t rs, uint32_t off) {
+  x.x = buf_load_u16(rs, off);
+}
+__device__ __forceinline__ void raw1_buf(float& x, __amdgpu_buffer_rsrc_t rs, uint32_t off) {
+  x = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
+}
+__device__ __forceinline__ float raw1_cvt(bf16_t x) { return bf16_to_f32(x.x); }
+__device__ __forceinline__ float raw1_cvt(float x) { return x; }
+__device__ __forceinline__ void raw1_zero(bf16_t& x) { x.x = 0; }
+__device__ __forceinline__ void raw1_zero(float& x) { x = 0.f; }
+
 template <typename OT>
 __device__ __forceinline__ void lds_store8(OT* p, const float* v) {
   typename Mma<OT>::F8 f;
@@ -128,6 +192,49 @@ __device__ __forceinline__ void lds_store8(OT* p, const float* v) {
 }
 
 __device__ __forceinline__ float exp_clamped(float x) { return __expf(fminf(x, 80.f)); }
+
+// Channel-major rows (k^T, X^T) hold 64 tokens; quads of 4 tokens are stored at quad ^ key(row)
+// so that transposed writes from lanes with different rows hit different banks.  Reads of 4
+// consecutive tokens from a quad boundary stay contiguous.
+__device__ __forceinline__ int swz(int row_key, int t) { return (((t >> 2) ^ row_key) << 2) | (t & 3); }
+
+// N (1, 2 or 4) consecutive elements as one LDS store.
+template <int N>
+__device__ __forceinline__ void lds_store_run(__bf16* p, const __bf16* v) {
+  uint32_t h[N];
+#pragma unroll
+  for (int j = 0; j < N; ++j) h[j] = __builtin_bit_cast(uint16_t, v[j]);
+  if constexpr (N == 4) {
+    *reinterpret_cast<uint2*>(p) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+  } else if constexpr (N == 2) {
+    *reinterpret_cast<uint32_t*>(p) = h[0] | (h[1] << 16);
+  } else {
+    p[0] = v[0];
+  }
+}
+template <int N>
+__device__ __forceinline__ void lds_store_run(float* p, const float* v) {
+  if constexpr (N == 4) {
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  } else if constexpr (N == 2) {
+    *reinterpret_cast<float2*>(p) = make_float2(v[0], v[1]);
+  } else {
+    p[0] = v[0];
+  }
+}
+
+// Fragment from two 4-element runs of an LDS row (k = 4 consecutive values each).
+template <typename OT>
+__device__ __forceinline__ typename Mma<OT>::F8 lds_two_quads(const OT* row, int pa, int pb) {
+  const typename Mma<OT>::F4 lo = lds_load4(row + pa), hi = lds_load4(row + pb);
+  typename Mma<OT>::F8 f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    f[j] = lo[j];
+    f[4 + j] = hi[j];
+  }
+  return f;
+}
 
 template <typename IO, typename OT, int DK, int NSW, int MODE>
 __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs<IO> a) {
@@ -169,8 +276,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs<IO> a) {
   // below the e^80 clamp; chunks beyond it run token by token (robust path, exact).
   constexpr float kSpanLimit = 76.f;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = lane >> 4, l16 = lane & 15;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches on it
+  int lane = tid & 63, g = lane >> 4, l16 = lane & 15;
 
   // Block -> (state, slice).  Blocks are dealt round-robin to the 8 XCDs; consecutive
   // pairs p land on one XCD, so the slices of one head share that XCD's L2.
@@ -203,7 +311,72 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs<IO> a) {
   }
 
   const int64_t nch = (a.T + C - 1) / C;
+
+  // ---------------- prefetch registers ----------------
+  // Each thread holds, for the next chunk: channels d0..d0+7 of tokens ts*TPS.. (q, k, b, log
+  // alpha) and one 8-column group of one token of v and w.  Loaded while the current chunk
+  // computes; tokens past the end read as zero (identity padding).
+  constexpr int NCG = L::NCG, NSEG = L::NSEG, TPS = L::TPS;
+  constexpr int NXG = DVS / 8;
+  constexpr int XPT = (NXG * C + 255) / 256;
+  int ts = tid / NCG, d0 = (tid % NCG) * 8;
+  const bool act = ts < NSEG;
+  Raw8<IO> pq[TPS], pk[TPS], pb[TPS], pla[TPS], pv[XPT], pw[XPT];
+  IO pbs[TPS], pws[XPT], pla0;
+  // Buffer resources are rebased at each chunk's first token, so offsets stay below 64 token
+  // rows whatever T is; rows past the last token fall outside the range and load as zero.
+  constexpr uint32_t ES = sizeof(IO);
+  const uint32_t hdk = static_cast<uint32_t>(a.H * DK) * ES, hdv = static_cast<uint32_t>(a.H * DV) * ES;
+  const uint32_t h1 = static_cast<uint32_t>(a.H) * ES;
+  auto prefetch = [&](int64_t c) {
+    const int64_t t0 = c * C;
+    const int64_t rr = (bi * a.T + t0) * a.H + hi;  // row of the chunk's first token
+    const int64_t left = a.T - t0;                  // tokens from t0 to the end, >= 1
+    auto range = [&](int64_t width) -> uint32_t {
+      const int64_t bytes = ((left - 1) * a.H + 1) * width * ES;
+      return static_cast<uint32_t>(bytes < 0x7fffffff ? bytes : 0x7fffffff);
+    };
+    // Every load is issued unconditionally (no branch, so no wait at a join): a gate kind that
+    // is absent gets an empty range and inactive lanes an out-of-range offset; both read zero.
+    const uint32_t oob = 0x80000000u;
+    const uint32_t vb = range(DV) - static_cast<uint32_t>(col0) * ES;
+    const auto rv = make_rsrc(a.v + rr * DV + col0, vb);
+    const auto rwc = make_rsrc(a.w_kind == kChannel ? a.wg + rr * DV + col0 : a.v, a.w_kind == kChannel ? vb : 0u);
+    const auto rws = make_rsrc(a.w_kind == kScalar ? a.wg + rr : a.v, a.w_kind == kScalar ? range(1) : 0u);
+    const auto rq = make_rsrc(a.q + rr * DK, range(DK));
+    const auto rk = make_rsrc(a.k + rr * DK, range(DK));
+    const auto rbc = make_rsrc(a.b_kind == kChannel ? a.bg + rr * DK : a.q, a.b_kind == kChannel ? range(DK) : 0u);
+    const auto rbs = make_rsrc(a.b_kind == kScalar ? a.bg + rr : a.q, a.b_kind == kScalar ? range(1) : 0u);
+    const auto rla = make_rsrc(a.alpha_kind == kChannel ? a.la + rr * DK : (a.alpha_kind == kScalar ? a.la + rr : a.q),
+                               a.alpha_kind == kChannel ? range(DK) : (a.alpha_kind == kScalar ? range(1) : 0u));
+#pragma unroll
+    for (int j = 0; j < XPT; ++j) {
+      const int item = tid + 256 * j;
+      const uint32_t t = item / NXG, xg = item % NXG;
+      const bool in = item < NXG * C;
+      const uint32_t xo = in ? t * hdv + xg * 8 * ES : oob;
+      raw8_buf(pv[j], rv, xo);
+      raw8_buf(pw[j], rwc, xo);
+      raw1_buf(pws[j], rws, in ? t * h1 : oob);
+    }
+    if (MODE == 0) raw1_buf(pla0, rla, wave == 0 ? static_cast<uint32_t>(lane) * h1 : oob);
+#pragma unroll
+    for (int u = 0; u < TPS; ++u) {
+      const uint32_t t = ts * TPS + u;
+      const uint32_t ko = act ? t * hdk + d0 * ES : oob;
+      raw8_buf(pq[u], rq, ko);
+      raw8_buf(pk[u], rk, ko);
+      raw8_buf(pb[u], rbc, ko);
+      raw1_buf(pbs[u], rbs, act ? t * h1 : oob);
+      if (MODE != 0) raw8_buf(pla[u], rla, ko);
+    }
+  };
+  if (nch > 0) prefetch(0);
+
   for (int64_t ch = 0; ch < nch; ++ch) {
+    // Opaque per chunk: keeps the compiler from hoisting every per-lane LDS address out of the
+    // chunk loop, which would hold them in registers for the whole kernel.
+    asm volatile("" : "+v"(lane), "+v"(g), "+v"(l16), "+v"(ts), "+v"(d0));
     const int64_t t0 = ch * C;
     const int nval = static_cast<int>(a.T - t0 < C ? a.T - t0 : C);
     auto row_of = [&](int t) -> int64_t { return (bi * a.T + t0 + t) * a.H + hi; };
@@ -212,42 +385,32 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs<IO> a) {
     GDR_MARK(0);
 
     // ---------------- phase A: X^T, gate prefix sums, scaled operands ----------------
-    {
-      constexpr int NXG = DVS / 8;
-      for (int idx = tid; idx < NXG * C; idx += 256) {
-        const int xg = idx % NXG, t = idx / NXG;
+#pragma unroll
+    for (int j = 0; j < XPT; ++j) {
+      const int item = tid + 256 * j;
+      if (item < NXG * C) {
+        const int xg = item % NXG, t = item / NXG;
         float x[8];
-        if (t < nval) {
-          const int64_t r = row_of(t);
-          load8f(a.v + r * DV + col0 + xg * 8, x);
-          if (a.w_kind == kChannel) {
-            float w[8];
-            load8f(a.wg + r * DV + col0 + xg * 8, w);
+        raw8_cvt(pv[j], x);
+        if (a.w_kind == kChannel) {
+          float w[8];
+          raw8_cvt(pw[j], w);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) x[j] *= w[j];
-          } else if (a.w_kind == kScalar) {
-            const float w = ld(a.wg, r);
+          for (int e = 0; e < 8; ++e) x[e] *= w[e];
+        } else if (a.w_kind == kScalar) {
+          const float w = raw1_cvt(pws[j]);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) x[j] *= w;
-          }
-        } else {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) x[j] = 0.f;
+          for (int e = 0; e < 8; ++e) x[e] *= w;
         }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) xT[(xg * 8 + j) * LDD + t] = to_ot<OT>(x[j]);
+        for (int e = 0; e < 8; ++e) xT[(xg * 8 + e) * LDD + t] = to_ot<OT>(x[e]);
       }
     }
 
-    constexpr int NCG = L::NCG, NSEG = L::NSEG, TPS = L::TPS;
-    const int cg = tid % NCG, ts = tid / NCG;
-    const bool act = ts < NSEG;
-    const int d0 = cg * 8;
     float la8[TPS][8], G8[TPS][8];
     if (MODE == 0) {
       if (wave == 0) {
-        float x = 0.f;
-        if (lane < nval && a.alpha_kind != kNone) x = ld(a.la, row_of(lane));
+        float x = raw1_cvt(pla0);
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
           const float y = __shfl_up(x, off);
@@ -262,13 +425,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs<IO> a) {
         float run[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int u = 0; u < TPS; ++u) {
-          const int t = ts * TPS + u;
-          if (t < nval) {
-            load8f(a.la + row_of(t) * DK + d0, la8[u]);
-          } else {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) la8[u][j] = 0.f;
-          }
+          raw8_cvt(pla[u], la8[u]);
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             run[j] += la8[u][j];
@@ -308,26 +465,21 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs<IO> a) {
           gn[j] = fGn[d0 + j];
         }
       }
+      OT pdp[8][TPS], pdk[8][TPS];
 #pragma unroll
       for (int u = 0; u < TPS; ++u) {
         const int t = ts * TPS + u;
         float q[8], k[8], c[8];
-        if (t < nval) {
-          const int64_t r = row_of(t);
-          load8f(a.q + r * DK + d0, q);
-          load8f(a.k + r * DK + d0, k);
-          if (a.b_kind == kChannel) {
-            load8f(a.bg + r * DK + d0, c);
+        raw8_cvt(pq[u], q);
+        raw8_cvt(pk[u], k);
+        if (a.b_kind == kChannel) {
+          raw8_cvt(pb[u], c);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) c[j] *= k[j];
-          } else {
-            const float bs = a.b_kind == kScalar ? ld(a.bg, r) : 0.f;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) c[j] = bs * k[j];
-          }
+          for (int j = 0; j < 8; ++j) c[j] *= k[j];
         } else {
+          const float bs = a.b_kind == kScalar ? raw1_cvt(pbs[u]) : 0.f;
 #pragma unroll
-          for (int j = 0; j < 8; ++j) q[j] = k[j] = c[j] = 0.f;
+          for (int j = 0; j < 8; ++j) c[j] = bs * k[j];
         }
         float oq[8], oc[8], ok[8], op[8], odp[8], odk[8];
         if (MODE == 0) {
@@ -374,32 +526,57 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs<IO> a) {
         if (TWO) lds_store8(tP + t * LDT + d0, op);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          dP[(d0 + j) * LDD + t] = to_ot<OT>(odp[j]);
-          if (TWO) dK[(d0 + j) * LDD + t] = to_ot<OT>(odk[j]);
+          pdp[j][u] = to_ot<OT>(odp[j]);
+          if (TWO) pdk[j][u] = to_ot<OT>(odk[j]);
+        }
+      }
+      if (!(MODE != 0 && robust)) {
+        // channel-major rows d0..d0+7: this thread's TPS tokens as one store per row
+        const int pos = swz((d0 >> 3) & 15, ts * TPS);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          lds_store_run<TPS>(dP + (d0 + j) * LDD + pos, pdp[j]);
+          if (TWO) lds_store_run<TPS>(dK + (d0 + j) * LDD + pos, pdk[j]);
         }
       }
     }
     lds_barrier();
     GDR_MARK(2);
+    if (ch + 1 < nch) prefetch(ch + 1);
 
     // ---------------- phase B: Gram tiles of the lower triangle ----------------
+    // 20 jobs = 2 row operands x 10 tile pairs (ta >= tb), 5 per wave.  Row operand 0 is Chat
+    // (the solve products), 1 is Qhat (the read-out products).  MODE 0/1: one product per job
+    // against Khat.  MODE 2: two products sharing the row fragment, against Phat and Khat
+    // (job 0: L_P, L_K; job 1: M_QK, M_QP).  The next job's fragments are loaded before the
+    // current job's MFMAs.
     if (!robust) {
-      constexpr int NPROD = TWO ? 4 : 2;
-      for (int job = wave; job < NPROD * 10; job += 4) {
-        const int prod = job / 10, tix = job % 10;
-        const int ta = tix >= 6 ? 3 : tix >= 3 ? 2 : tix >= 1 ? 1 : 0;
-        const int tb = tix - ta * (ta + 1) / 2;
-        // MODE 0/1: 0 = C x K (strict, solve), 1 = Q x K (incl, read-out)
-        // MODE 2:   0 = C x P (strict, solve), 1 = C x K (strict), 2 = Q x K, 3 = Q x P (incl)
-        const OT* rows = (prod == 0 || (TWO && prod == 1)) ? tC : tQ;
-        const OT* cols = TWO ? ((prod == 0 || prod == 3) ? tP : tK) : tK;
-        const bool strict = TWO ? prod <= 1 : prod == 0;
-        const OT* ar = rows + (16 * ta + l16) * LDT;
-        const OT* br = cols + (16 * tb + l16) * LDT;
-        f32x4 acc = zero4();
+      constexpr int JPW = 5;
+      F8 fa[2][NKB], fb[2][NKB], fc[2][NKB];
+      auto job_of = [&](int jj, int& grp, int& ta, int& tb) {
+        const int job = wave + 4 * jj;
+        grp = job / 10;
+        const int tix = job % 10;
+        ta = tix >= 6 ? 3 : tix >= 3 ? 2 : tix >= 1 ? 1 : 0;
+        tb = tix - ta * (ta + 1) / 2;
+      };
+      auto load_job = [&](int jj, int bsel) {
+        int grp, ta, tb;
+        job_of(jj, grp, ta, tb);
+        const OT* ar = (grp == 0 ? tC : tQ) + (16 * ta + l16) * LDT;
+        const OT* br = ((TWO && grp == 0) ? tP : tK) + (16 * tb + l16) * LDT;
+        const OT* cr = (grp == 0 ? tK : tP) + (16 * tb + l16) * LDT;
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-          acc = MM::mma8(lds_std_frag(ar, 32 * kb, g, DK), lds_std_frag(br, 32 * kb, g, DK), acc);
+        for (int kb = 0; kb < NKB; ++kb) {
+          fa[bsel][kb] = lds_std_frag(ar, 32 * kb, g, DK);
+          fb[bsel][kb] = lds_std_frag(br, 32 * kb, g, DK);
+          if (TWO) fc[bsel][kb] = lds_std_frag(cr, 32 * kb, g, DK);
+        }
+      };
+      // which: 0 = solve matrix (strict; off-diagonal -> gA as -L, diagonal -> Ld in fp32),
+      // 1 = M used with R (inclusive, stored as -M), 2 = L_K (strict), 3 = M_QK (inclusive)
+      auto store_tile = [&](int which, int ta, int tb, const f32x4& acc) {
+        const bool strict = which == 0 || which == 2;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 16 * ta + 4 * g + i, cc = 16 * tb + l16;
@@ -409,18 +586,38 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs<IO> a) {
             val = acc[i];
             if (MODE == 0) val *= __expf(sG[r] - sG[cc]);
           }
-          if (prod == 0) {
+          if (which == 0) {
             if (ta > tb)
               gA[r * LDD + cc] = to_ot<OT>(-val);
             else
               Ld[(ta * 16 + (r & 15)) * 17 + (cc & 15)] = val;
-          } else if (!TWO || prod == 3) {
+          } else if (which == 1) {
             gM[r * LDD + cc] = to_ot<OT>(-val);
-          } else if (prod == 1) {
+          } else if (which == 2) {
             gLK[r * LDD + cc] = to_ot<OT>(val);
           } else {
             gMQK[r * LDD + cc] = to_ot<OT>(val);
           }
+        }
+      };
+      load_job(0, 0);
+#pragma unroll
+      for (int jj = 0; jj < JPW; ++jj) {
+        const int cur = jj & 1;
+        if (jj + 1 < JPW) load_job(jj + 1, cur ^ 1);
+        int grp, ta, tb;
+        job_of(jj, grp, ta, tb);
+        f32x4 acc1 = zero4(), acc2 = zero4();
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          acc1 = MM::mma8(fa[cur][kb], fb[cur][kb], acc1);
+          if (TWO) acc2 = MM::mma8(fa[cur][kb], fc[cur][kb], acc2);
+        }
+        if (TWO) {
+          store_tile(grp == 0 ? 0 : 3, ta, tb, acc1);
+          store_tile(grp == 0 ? 2 : 1, ta, tb, acc2);
+        } else {
+          store_tile(grp == 0 ? 0 : 1, ta, tb, acc1);
         }
       }
     }
@@ -594,14 +791,15 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs<IO> a) {
       for (int tl = 0; tl < NTD; ++tl) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) S[tl][i] *= (MODE == 0) ? sEGn[0] : fEGn[16 * tl + 4 * g + i];
+        const int key = (2 * tl + (l16 >> 3)) & 15;  // swizzle key of row 16 tl + l16
         const OT* pr = dP + (16 * tl + l16) * LDD;
         if (TWO) {
           const OT* kr = dK + (16 * tl + l16) * LDD;
-          S[tl] = MM::mma8(lds_load8(kr + 8 * g), xf[0], S[tl]);
-          S[tl] = MM::mma8(lds_load8(kr + 32 + 8 * g), xf[1], S[tl]);
+          S[tl] = MM::mma8(lds_two_quads(kr, swz(key, 8 * g), swz(key, 8 * g + 4)), xf[0], S[tl]);
+          S[tl] = MM::mma8(lds_two_quads(kr, swz(key, 32 + 8 * g), swz(key, 36 + 8 * g)), xf[1], S[tl]);
         }
-        S[tl] = MM::mma8(lds_pair_frag(pr, 0, g, C), rf[0], S[tl]);
-        S[tl] = MM::mma8(lds_pair_frag(pr, 32, g, C), rf[1], S[tl]);
+        S[tl] = MM::mma8(lds_two_quads(pr, swz(key, 4 * g), swz(key, 16 + 4 * g)), rf[0], S[tl]);
+        S[tl] = MM::mma8(lds_two_quads(pr, swz(key, 32 + 4 * g), swz(key, 48 + 4 * g)), rf[1], S[tl]);
       }
     }
     GDR_MARK(5);

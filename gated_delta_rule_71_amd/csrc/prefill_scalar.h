@@ -48,25 +48,6 @@ struct ScalarLayout {
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-// Channel-major rows (k^T) and value rows (X^T) hold 64 tokens; quads of 4 tokens are stored at
-// quad ^ key(row) so that transposed writes from lanes with different rows hit different banks.
-// Reads of 4 (or 8) consecutive tokens stay contiguous.
-__device__ __forceinline__ int swz(int row_key, int t) { return (((t >> 2) ^ row_key) << 2) | (t & 3); }
-
-// Raw buffer resource over `bytes` bytes from `base` (gfx9 descriptor word 3).  Loads past the
-// range return zero and stores past it are dropped, which pads the ragged last chunk.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                           0x00020000);
-}
-__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
-// Raw 16-bit load; converted to fp32 only where the value is used, so that issuing the load
-// does not wait for it.
-__device__ __forceinline__ uint16_t buf_load_u16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
-}
 
 // Gram tiles of one key wave: row blocks RA and RB (16 rows each) of `rows` (k or q) against
 // the 16-row column blocks of k at or below them.  prod 0: A = beta_t k_t . k_i e^{G_t - G_i}
