@@ -116,6 +116,32 @@ __device__ __forceinline__ typename Mma<OT>::F8 lds_std_frag(const OT* row, int 
   return f;
 }
 
+// The same two loads with the range known at compile time: when KMAX is a multiple of 32
+// every lane's k lies in range and the loads are unconditional (no branch per fragment).
+template <int KMAX, typename OT>
+__device__ __forceinline__ typename Mma<OT>::F8 lds_pair_frag_k(const OT* row, int k0, int g) {
+  if constexpr (KMAX % 32 == 0) {
+    typename Mma<OT>::F8 f;
+    const typename Mma<OT>::F4 lo = lds_load4(row + k0 + 4 * g), hi = lds_load4(row + k0 + 16 + 4 * g);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f[j] = lo[j];
+      f[4 + j] = hi[j];
+    }
+    return f;
+  } else {
+    return lds_pair_frag(row, k0, g, KMAX);
+  }
+}
+template <int KMAX, typename OT>
+__device__ __forceinline__ typename Mma<OT>::F8 lds_std_frag_k(const OT* row, int k0, int g) {
+  if constexpr (KMAX % 32 == 0) {
+    return lds_load8(row + k0 + 8 * g);
+  } else {
+    return lds_std_frag(row, k0, g, KMAX);
+  }
+}
+
 // B fragment (tile-pair order) from two stacked accumulator tiles.
 template <typename OT>
 __device__ __forceinline__ typename Mma<OT>::F8 acc_pair_frag(const f32x4& lo, const f32x4& hi) {

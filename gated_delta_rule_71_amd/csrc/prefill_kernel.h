@@ -79,8 +79,9 @@ struct PrefillLayout {
   static constexpr int oGLK = oGM + GRAM_BYTES;                  // L_K (MODE 2)
   static constexpr int oGMQK = oGLK + (TWO ? GRAM_BYTES : 0);    // M_QK (MODE 2)
   static constexpr int oINV = oGMQK + (TWO ? GRAM_BYTES : 0);    // T_ii [4][16][LDI]
-  static constexpr int oLD = oINV + 4 * 16 * LDI * ES;           // fp32 L_ii [4][16][17]
-  static constexpr int oF = oLD + 4 * 16 * 17 * 4;               // fp32 per-channel / per-token
+  static constexpr int LDL = 20;                                 // column pitch of L_ii
+  static constexpr int oLD = oINV + 4 * 16 * LDI * ES;           // fp32 L_ii, column-major [4][16][LDL]
+  static constexpr int oF = oLD + 4 * 16 * LDL * 4;              // fp32 per-channel / per-token
   static constexpr int NF = MODE == 0 ? 2 * C + 8 : 4 * DK + 4;  // + robust-chunk flag
   static constexpr int total = oF + NF * 4;
   static constexpr bool fits = total <= kLdsLimit;
@@ -177,6 +178,12 @@ __device__ __forceinline__ void raw1_buf(bf16_t& x, __amdgpu_buffer_rsrc_t rs, u
 }
 __device__ __forceinline__ void raw1_buf(float& x, __amdgpu_buffer_rsrc_t rs, uint32_t off) {
   x = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
+}
+__device__ __forceinline__ void buf_store1(bf16_t*, __amdgpu_buffer_rsrc_t rs, uint32_t off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(v), rs, off, 0, 0);
+}
+__device__ __forceinline__ void buf_store1(float*, __amdgpu_buffer_rsrc_t rs, uint32_t off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rs, off, 0, 0);
 }
 __device__ __forceinline__ float raw1_cvt(bf16_t x) { return bf16_to_f32(x.x); }
 __device__ __forceinline__ float raw1_cvt(float x) { return x; }
@@ -456,13 +463,13 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs<IO> a) {
 
     GDR_MARK(1);
     if (act) {
-      float off[8], ref[8], gn[8];
+      float off[8], ref[8], egr[8];
       if (MODE != 0) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           off[j] = segtot[ts * DK + d0 + j];
           ref[j] = fRef[d0 + j];
-          gn[j] = fGn[d0 + j];
+          egr[j] = __expf(fGn[d0 + j] - ref[j]);  // e^{G_n - G_ref}
         }
       }
       OT pdp[8][TPS], pdk[8][TPS];
@@ -482,6 +489,16 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs<IO> a) {
           for (int j = 0; j < 8; ++j) c[j] = bs * k[j];
         }
         float oq[8], oc[8], ok[8], op[8], odp[8], odk[8];
+        if (MODE != 0 && robust) {
+          // exact path: raw q, c = b . k, k and log alpha, token-major
+          OT* laArr = TWO ? tP : dP;
+          const int lpitch = TWO ? LDT : ((C * LDT <= DK * LDD) ? LDT : DK);
+          lds_store8(tQ + t * LDT + d0, q);
+          lds_store8(tC + t * LDT + d0, c);
+          lds_store8(tK + t * LDT + d0, k);
+          lds_store8(laArr + t * lpitch + d0, la8[u]);
+          continue;
+        }
         if (MODE == 0) {
           const float fk = __expf(sG[C - 1] - sG[t]);
 #pragma unroll
@@ -492,33 +509,28 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs<IO> a) {
             odp[j] = -k[j] * fk;
           }
         } else {
+          // A chunk on this path has every |G_t - G_ref| and |G_n - G_ref| within the span
+          // limit, so each factor below stays inside the fp32 range; reciprocals replace the
+          // exponentials of negated arguments.
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             const float G = G8[u][j] + off[j];
-            const float eq = exp_clamped(G - ref[j]);
+            const float eq = __expf(G - ref[j]);          // e^{G_t - G_ref}
+            const float er = __builtin_amdgcn_rcpf(eq);   // e^{G_ref - G_t}
             oq[j] = q[j] * eq;
-            ok[j] = k[j] * exp_clamped(ref[j] - G);
+            ok[j] = k[j] * er;
             if (MODE == 1) {
               oc[j] = c[j] * eq;
-              odp[j] = -k[j] * __expf(gn[j] - G);
+              odp[j] = -(ok[j] * egr[j]);                 // -k e^{G_n - G_t}
             } else {
-              const float Gp = G - la8[u][j];
-              oc[j] = c[j] * exp_clamped(Gp - ref[j]);
-              op[j] = k[j] * exp_clamped(ref[j] - Gp);
-              odp[j] = -k[j] * __expf(gn[j] - Gp);
-              odk[j] = k[j] * __expf(gn[j] - G);
+              const float ep = __expf(G - la8[u][j] - ref[j]);  // e^{G_{t-1} - G_ref}
+              const float epr = __builtin_amdgcn_rcpf(ep);
+              oc[j] = c[j] * ep;
+              op[j] = k[j] * epr;
+              odp[j] = -(op[j] * egr[j]);                 // -k e^{G_n - G_{t-1}}
+              odk[j] = ok[j] * egr[j];                    // k e^{G_n - G_t}
             }
           }
-        }
-        if (MODE != 0 && robust) {
-          // exact path: raw q, c = b . k, k and log alpha, token-major
-          OT* laArr = TWO ? tP : dP;
-          const int lpitch = TWO ? LDT : ((C * LDT <= DK * LDD) ? LDT : DK);
-          lds_store8(tQ + t * LDT + d0, q);
-          lds_store8(tC + t * LDT + d0, c);
-          lds_store8(tK + t * LDT + d0, k);
-          lds_store8(laArr + t * lpitch + d0, la8[u]);
-          continue;
         }
         lds_store8(tQ + t * LDT + d0, oq);
         lds_store8(tC + t * LDT + d0, oc);
@@ -542,7 +554,6 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs<IO> a) {
     }
     lds_barrier();
     GDR_MARK(2);
-    if (ch + 1 < nch) prefetch(ch + 1);
 
     // ---------------- phase B: Gram tiles of the lower triangle ----------------
     // 20 jobs = 2 row operands x 10 tile pairs (ta >= tb), 5 per wave.  Row operand 0 is Chat
@@ -568,14 +579,26 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs<IO> a) {
         const OT* cr = (grp == 0 ? tK : tP) + (16 * tb + l16) * LDT;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
-          fa[bsel][kb] = lds_std_frag(ar, 32 * kb, g, DK);
-          fb[bsel][kb] = lds_std_frag(br, 32 * kb, g, DK);
-          if (TWO) fc[bsel][kb] = lds_std_frag(cr, 32 * kb, g, DK);
+          fa[bsel][kb] = lds_std_frag_k<DK>(ar, 32 * kb, g);
+          fb[bsel][kb] = lds_std_frag_k<DK>(br, 32 * kb, g);
+          if (TWO) fc[bsel][kb] = lds_std_frag_k<DK>(cr, 32 * kb, g);
         }
       };
       // which: 0 = solve matrix (strict; off-diagonal -> gA as -L, diagonal -> Ld in fp32),
       // 1 = M used with R (inclusive, stored as -M), 2 = L_K (strict), 3 = M_QK (inclusive)
       auto store_tile = [&](int which, int ta, int tb, const f32x4& acc) {
+        if (ta > tb) {  // below the diagonal block: every entry is kept (uniform branch)
+          const int r0 = 16 * ta + 4 * g, cc = 16 * tb + l16;
+          OT* dst = (which == 0 ? gA : which == 1 ? gM : which == 2 ? gLK : gMQK) + r0 * LDD + cc;
+          const float sgn = which <= 1 ? -1.f : 1.f;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float val = acc[i] * sgn;
+            if (MODE == 0) val *= __expf(sG[r0 + i] - sG[cc]);
+            dst[i * LDD] = to_ot<OT>(val);
+          }
+          return;
+        }
         const bool strict = which == 0 || which == 2;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -590,7 +613,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs<IO> a) {
             if (ta > tb)
               gA[r * LDD + cc] = to_ot<OT>(-val);
             else
-              Ld[(ta * 16 + (r & 15)) * 17 + (cc & 15)] = val;
+              Ld[(ta * 16 + (cc & 15)) * L::LDL + (r & 15)] = val;
           } else if (which == 1) {
             gM[r * LDD + cc] = to_ot<OT>(-val);
           } else if (which == 2) {
@@ -625,21 +648,37 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs<IO> a) {
     GDR_MARK(3);
 
     // ---------------- phase C: inverses of the four 16x16 diagonal blocks ----------------
-    if (wave == 0 && !robust) {
+    // The next chunk's loads are issued where each wave would otherwise wait: waves 0-2 while
+    // wave 3 inverts, wave 3 at the start of phase D.
+    if (wave != 3 && ch + 1 < nch) prefetch(ch + 1);
+    // Lane (blk, j) solves column j of block blk by a column sweep: once x_m is final, every
+    // later x_i drops L[i][m] x_m (independent FMAs); column m+1 is read while m is applied.
+    if (wave == 3 && !robust) {
       const int blk = g, j = l16;
       float x[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float s = (i == j) ? 1.f : 0.f;
+      for (int i = 0; i < 16; ++i) x[i] = (i == j) ? 1.f : 0.f;
+      float4 col[2][4];
+      auto load_col = [&](int m, float4* cv) {
+        const float* p = Ld + (blk * 16 + m) * L::LDL;
 #pragma unroll
-        for (int m = 0; m < i; ++m) s -= Ld[(blk * 16 + i) * 17 + m] * x[m];
-        x[i] = s;
+        for (int q4 = 0; q4 < 4; ++q4)
+          if (4 * q4 + 3 > m) cv[q4] = *reinterpret_cast<const float4*>(p + 4 * q4);
+      };
+      load_col(0, col[0]);
+#pragma unroll
+      for (int m = 0; m < 15; ++m) {
+        if (m + 1 < 15) load_col(m + 1, col[(m + 1) & 1]);
+        const float* cv = reinterpret_cast<const float*>(col[m & 1]);
+#pragma unroll
+        for (int i = m + 1; i < 16; ++i) x[i] -= cv[i] * x[m];
       }
 #pragma unroll
       for (int i = 0; i < 16; ++i) dInv[(blk * 16 + i) * LDI + j] = to_ot<OT>(x[i]);
     }
     lds_barrier();
     GDR_MARK(4);
+    if (wave == 3 && ch + 1 < nch) prefetch(ch + 1);
 
     // ---------------- phase D (exact path): token by token, fp32 ----------------
     // The recurrence itself on this wave's 16 columns: each lane holds rows 16*tl + 4g + i of
@@ -699,6 +738,11 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs<IO> a) {
     if (sside && !robust) {
       // (1) S (scaled by e^{G_ref} for a per-channel decay) as B fragments, tile-pair order
       F8 sf[NKB];
+      float4 er4[NTD];
+      if (MODE != 0) {
+#pragma unroll
+        for (int tl = 0; tl < NTD; ++tl) er4[tl] = *reinterpret_cast<const float4*>(fEref + 16 * tl + 4 * g);
+      }
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
@@ -707,7 +751,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs<IO> a) {
           float val = 0.f;
           if (tl < NTD) {
             val = S[tl][i];
-            if (MODE != 0) val *= fEref[16 * tl + 4 * g + i];
+            if (MODE != 0) val *= reinterpret_cast<const float*>(&er4[tl])[i];
           }
           sf[kb][j] = to_ot<OT>(val);
         }
@@ -722,15 +766,16 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs<IO> a) {
         const OT* qr = tQ + (16 * ta + l16) * LDT;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
-          V[ta] = MM::mma8(lds_pair_frag(cr, 32 * kb, g, DK), sf[kb], V[ta]);
-          O[ta] = MM::mma8(lds_pair_frag(qr, 32 * kb, g, DK), sf[kb], O[ta]);
+          V[ta] = MM::mma8(lds_pair_frag_k<DK>(cr, 32 * kb, g), sf[kb], V[ta]);
+          O[ta] = MM::mma8(lds_pair_frag_k<DK>(qr, 32 * kb, g), sf[kb], O[ta]);
         }
         if (MODE == 0) {
+          const float4 e4 = *reinterpret_cast<const float4*>(sEG + 16 * ta + 4 * g);
+          const float e[4] = {e4.x, e4.y, e4.z, e4.w};
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float e = sEG[16 * ta + 4 * g + i];
-            V[ta][i] *= e;
-            O[ta][i] *= e;
+            V[ta][i] *= e[i];
+            O[ta][i] *= e[i];
           }
         }
       }
@@ -741,9 +786,11 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs<IO> a) {
       xf[1] = lds_load8(xr + 32 + 8 * g);
       if (!TWO) {
 #pragma unroll
-        for (int ta = 0; ta < 4; ++ta)
+        for (int ta = 0; ta < 4; ++ta) {
+          const auto x4 = lds_load4(xr + 16 * ta + 4 * g);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) V[ta][i] -= static_cast<float>(xr[16 * ta + 4 * g + i]);
+          for (int i = 0; i < 4; ++i) V[ta][i] -= static_cast<float>(x4[i]);
+        }
       } else {
 #pragma unroll
         for (int ta = 0; ta < 4; ++ta) {
@@ -775,22 +822,37 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs<IO> a) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           if (kb == 1 && ta < 2) continue;
-          O[ta] = MM::mma8(lds_pair_frag(gM + (16 * ta + l16) * LDD, 32 * kb, g, C), rf[kb], O[ta]);
+          O[ta] = MM::mma8(lds_pair_frag_k<C>(gM + (16 * ta + l16) * LDD, 32 * kb, g), rf[kb], O[ta]);
         }
       }
       // (6) read-out
+      // rows past the last token fall outside the buffer range and are dropped
+      {
+        const int64_t rr = (bi * a.T + t0) * a.H + hi;
+        const int64_t bytes = (((a.T - t0) - 1) * a.H + 1) * DV * static_cast<int64_t>(sizeof(IO)) -
+                              col0 * static_cast<int64_t>(sizeof(IO));
+        const auto ro = make_rsrc(a.o + rr * DV + col0, static_cast<uint32_t>(bytes < 0x7fffffff ? bytes : 0x7fffffff));
+        const uint32_t hdvo = static_cast<uint32_t>(a.H * DV) * sizeof(IO);
 #pragma unroll
-      for (int ta = 0; ta < 4; ++ta)
+        for (int ta = 0; ta < 4; ++ta)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int t = 16 * ta + 4 * g + i;
-          if (t < nval) st(a.o, row_of(t) * DV + col0 + nloc, O[ta][i]);
-        }
+          for (int i = 0; i < 4; ++i)
+            buf_store1(a.o, ro, (16 * ta + 4 * g + i) * hdvo + nloc * sizeof(IO), O[ta][i]);
+      }
       // (7) S <- e^{G_n} . S (+ Kbar^T X) - P^T R   (dP holds -P^T)
 #pragma unroll
       for (int tl = 0; tl < NTD; ++tl) {
+        if (MODE == 0) {
+          const float e = sEGn[0];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) S[tl][i] *= (MODE == 0) ? sEGn[0] : fEGn[16 * tl + 4 * g + i];
+          for (int i = 0; i < 4; ++i) S[tl][i] *= e;
+        } else {
+          const float4 e4 = *reinterpret_cast<const float4*>(fEGn + 16 * tl + 4 * g);
+          S[tl][0] *= e4.x;
+          S[tl][1] *= e4.y;
+          S[tl][2] *= e4.z;
+          S[tl][3] *= e4.w;
+        }
         const int key = (2 * tl + (l16 >> 3)) & 15;  // swizzle key of row 16 tl + l16
         const OT* pr = dP + (16 * tl + l16) * LDD;
         if (TWO) {
