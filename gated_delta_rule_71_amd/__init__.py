@@ -69,11 +69,12 @@ def _stream(device):
 
 
 def chunk_fwd(q, k, v, log_alpha=None, b=None, w=None, S0=None, order="erase_then_decay",
-              out=None, final_state=True):
+              out=None, final_state=True, workspace=None):
     """Chunkwise prefill.  Returns (o [B,T,H,dv] in q's dtype, S_T [B,H,dk,dv] float32 or None).
 
     ``S0`` (float32 [B,H,dk,dv] or None for zeros) is read before S_T is written; pass
-    ``final_state=S0`` to update the state in place."""
+    ``final_state=S0`` to update the state in place.  ``workspace`` is an optional uint8
+    device tensor of at least ``workspace_bytes(...)`` bytes; one is allocated when absent."""
     torch = _torch()
     B, T, H, DK = q.shape
     DV = v.shape[-1]
@@ -100,11 +101,29 @@ def chunk_fwd(q, k, v, log_alpha=None, b=None, w=None, S0=None, order="erase_the
         S_T = final_state
         _check_contig(final_state=S_T)
     prob = make_problem(B, H, T, DK, DV, _io_dtype(q), ak, bk, wk, _ORDERS[order])
+    need = _native.workspace_bytes(prob)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev) if need else None
+    elif workspace.device != dev or workspace.numel() * workspace.element_size() < need:
+        raise ValueError("workspace must be a device tensor of at least %d bytes" % need)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     rc = _native.chunk_fwd_raw(prob, _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w),
-                               _ptr(S0), _ptr(o), _ptr(S_T), 0, 0, _stream(dev))
+                               _ptr(S0), _ptr(o), _ptr(S_T), _ptr(workspace), ws_bytes,
+                               _stream(dev))
     if rc != _native.GDR_OK:
         raise GdrError(rc, "gdr_chunk_fwd")
     return o, S_T
+
+
+def workspace_bytes(q, v, log_alpha=None, b=None, w=None, order="erase_then_decay"):
+    """Workspace bytes ``chunk_fwd`` needs for these inputs (0 when it needs none)."""
+    B, T, H, DK = q.shape
+    DV = v.shape[-1]
+    ak = _gate_kind(log_alpha, B, T, H, DK, "log_alpha", q.dtype, q.device)
+    bk = _gate_kind(b, B, T, H, DK, "b", q.dtype, q.device)
+    wk = _gate_kind(w, B, T, H, DV, "w", q.dtype, q.device)
+    return _native.workspace_bytes(make_problem(B, H, T, DK, DV, _io_dtype(q), ak, bk, wk,
+                                                _ORDERS[order]))
 
 
 def decode_step(q, k, v, log_alpha=None, b=None, w=None, S=None, order="erase_then_decay",

@@ -19,8 +19,10 @@ template <typename IO>
 hipError_t launch_prefill(const IO* q, const IO* k, const IO* v, const IO* la, const IO* bg,
                           const IO* wg, const float* S0, IO* o, float* S_T, int64_t B, int64_t T,
                           int64_t H, int64_t DK, int64_t DV, int alpha_kind, int b_kind,
-                          int w_kind, bool decay_first, hipStream_t stream);
+                          int w_kind, bool decay_first, void* workspace, hipStream_t stream);
 bool prefill_supported(int io_dtype, int64_t DK, int64_t DV, int alpha_kind, bool decay_first);
+size_t prefill_workspace_bytes(int io_dtype, int64_t nstate, int64_t T, int64_t DK, int64_t DV,
+                               int alpha_kind, int b_kind);
 }  // namespace gdr
 
 namespace {
@@ -111,8 +113,9 @@ GDR_EXPORT const char* gdr_status_string(int status) {
 }
 
 GDR_EXPORT size_t gdr_chunk_fwd_workspace_bytes(const gdr_problem* p) {
-  (void)p;
-  return 0;
+  if (check_problem(p) != GDR_OK) return 0;
+  return gdr::prefill_workspace_bytes(p->io_dtype, p->batch * p->heads, p->seqlen, p->dk, p->dv,
+                                      p->alpha_kind, p->b_kind);
 }
 
 GDR_EXPORT int gdr_chunk_fwd(const gdr_problem* p, const void* q, const void* k, const void* v,
@@ -121,8 +124,6 @@ GDR_EXPORT int gdr_chunk_fwd(const gdr_problem* p, const void* q, const void* k,
                              void* stream) {
   int rc = check_problem(p);
   if (rc != GDR_OK) return rc;
-  (void)workspace;
-  if (workspace_bytes < gdr_chunk_fwd_workspace_bytes(p)) return GDR_ERR_WORKSPACE_TOO_SMALL;
   rc = check_tensors(p, p->seqlen, q, k, v, log_alpha, b, w, o);
   if (rc != GDR_OK) return rc;
   const int64_t nstate = p->batch * p->heads;
@@ -138,6 +139,10 @@ GDR_EXPORT int gdr_chunk_fwd(const gdr_problem* p, const void* q, const void* k,
   const bool decay_first = p->order == GDR_DECAY_THEN_ERASE;
   if (!gdr::prefill_supported(p->io_dtype, p->dk, p->dv, p->alpha_kind, decay_first))
     return GDR_ERR_UNSUPPORTED;
+  const size_t need = gdr_chunk_fwd_workspace_bytes(p);
+  if (workspace_bytes < need) return GDR_ERR_WORKSPACE_TOO_SMALL;
+  if (need > 0 && workspace == nullptr) return GDR_ERR_INVALID_ARGUMENT;
+  if (need > 0 && !aligned16(workspace)) return GDR_ERR_MISALIGNED;
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;
@@ -147,13 +152,13 @@ GDR_EXPORT int gdr_chunk_fwd(const gdr_problem* p, const void* q, const void* k,
         (const T*)q, (const T*)k, (const T*)v, (const T*)gate_ptr(p->alpha_kind, log_alpha),
         (const T*)gate_ptr(p->b_kind, b), (const T*)gate_ptr(p->w_kind, w), S0, (T*)o, S_T,
         p->batch, p->seqlen, p->heads, p->dk, p->dv, p->alpha_kind, p->b_kind, p->w_kind,
-        decay_first, s);
+        decay_first, workspace, s);
   } else {
     e = gdr::launch_prefill<float>(
         (const float*)q, (const float*)k, (const float*)v,
         (const float*)gate_ptr(p->alpha_kind, log_alpha), (const float*)gate_ptr(p->b_kind, b),
         (const float*)gate_ptr(p->w_kind, w), S0, (float*)o, S_T, p->batch, p->seqlen, p->heads,
-        p->dk, p->dv, p->alpha_kind, p->b_kind, p->w_kind, decay_first, s);
+        p->dk, p->dv, p->alpha_kind, p->b_kind, p->w_kind, decay_first, workspace, s);
   }
   return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
 }

@@ -1,5 +1,6 @@
 // Host entry for the chunkwise prefill: picks the kernel variant for a problem.
 #include <stdlib.h>
+#include <string.h>
 
 #include "prefill_dispatch.h"
 
@@ -7,13 +8,22 @@ namespace gdr {
 
 bool prefill_scalar_ok(int64_t T, int64_t H, int64_t DK, int64_t DV, int b_kind);
 hipError_t prefill_scalar_launch(PrefillArgs<bf16_t> a, int64_t nstate, int64_t DK, hipStream_t s);
+bool prefill_wy_ok(int64_t DK, int64_t DV, int b_kind);
+size_t prefill_wy_workspace_bytes(int64_t nstate, int64_t T, int64_t DK, int64_t DV);
+hipError_t prefill_wy_launch(const PrefillArgs<bf16_t>& p, int64_t nstate, int64_t DK,
+                             void* workspace, hipStream_t s);
 
 namespace {
 
-// GDR_PREFILL_PIPE=0 selects the generic kernel for scalar-decay problems (comparisons only).
-bool pipelined_enabled() {
-  const char* e = getenv("GDR_PREFILL_PIPE");
-  return !(e && e[0] == '0');
+// Kernel family for bf16 scalar-decay problems: "wy" (default: chunk-local kernel + state
+// kernel through a workspace), "fused" (one pipelined kernel, no workspace) or "generic"
+// (the all-modes kernel).  Set through GDR_PREFILL_IMPL for comparisons.
+enum class ScalarImpl { kWy, kFused, kGeneric };
+ScalarImpl scalar_impl() {
+  const char* e = getenv("GDR_PREFILL_IMPL");
+  if (e && strcmp(e, "fused") == 0) return ScalarImpl::kFused;
+  if (e && strcmp(e, "generic") == 0) return ScalarImpl::kGeneric;
+  return ScalarImpl::kWy;
 }
 
 // MODE 0: scalar (or no) decay; 1: per-channel decay applied before the erase;
@@ -49,6 +59,14 @@ int choose_nsw_bf16(int64_t DK, int64_t DV, int mode) {
 
 }  // namespace
 
+size_t prefill_workspace_bytes(int io_dtype, int64_t nstate, int64_t T, int64_t DK, int64_t DV,
+                               int alpha_kind, int b_kind) {
+  if (io_dtype == 0 && alpha_kind != kChannel && prefill_wy_ok(DK, DV, b_kind) &&
+      scalar_impl() == ScalarImpl::kWy)
+    return prefill_wy_workspace_bytes(nstate, T, DK, DV);
+  return 0;
+}
+
 bool prefill_supported(int io_dtype, int64_t DK, int64_t DV, int alpha_kind, bool decay_first) {
   const int mode = prefill_mode(alpha_kind, decay_first);
   if (DV % 16 != 0) return false;
@@ -60,13 +78,18 @@ template <typename IO>
 hipError_t launch_prefill(const IO* q, const IO* k, const IO* v, const IO* la, const IO* bg,
                           const IO* wg, const float* S0, IO* o, float* S_T, int64_t B, int64_t T,
                           int64_t H, int64_t DK, int64_t DV, int alpha_kind, int b_kind,
-                          int w_kind, bool decay_first, hipStream_t stream) {
+                          int w_kind, bool decay_first, void* workspace, hipStream_t stream) {
   const int mode = prefill_mode(alpha_kind, decay_first);
   PrefillArgs<IO> a{q, k, v, la, bg, wg, S0, o, S_T, T, H, DV, alpha_kind, b_kind, w_kind, 1};
   const int64_t nstate = B * H;
   if constexpr (sizeof(IO) == 2) {
-    if (mode == 0 && prefill_scalar_ok(T, H, DK, DV, b_kind) && pipelined_enabled())
-      return prefill_scalar_launch(a, nstate, DK, stream);
+    if (mode == 0) {
+      const ScalarImpl impl = scalar_impl();
+      if (impl == ScalarImpl::kWy && prefill_wy_ok(DK, DV, b_kind))
+        return prefill_wy_launch(a, nstate, DK, workspace, stream);
+      if (impl == ScalarImpl::kFused && prefill_scalar_ok(T, H, DK, DV, b_kind))
+        return prefill_scalar_launch(a, nstate, DK, stream);
+    }
     const int nsw = choose_nsw_bf16(DK, DV, mode);
     if (nsw == 0) return hipErrorInvalidValue;
     a.nsl = static_cast<int>(DV / (16 * nsw));
@@ -86,11 +109,11 @@ hipError_t launch_prefill(const IO* q, const IO* k, const IO* v, const IO* la, c
 template hipError_t launch_prefill<bf16_t>(const bf16_t*, const bf16_t*, const bf16_t*,
                                            const bf16_t*, const bf16_t*, const bf16_t*,
                                            const float*, bf16_t*, float*, int64_t, int64_t,
-                                           int64_t, int64_t, int64_t, int, int, int, bool,
+                                           int64_t, int64_t, int64_t, int, int, int, bool, void*,
                                            hipStream_t);
 template hipError_t launch_prefill<float>(const float*, const float*, const float*, const float*,
                                           const float*, const float*, const float*, float*, float*,
                                           int64_t, int64_t, int64_t, int64_t, int64_t, int, int,
-                                          int, bool, hipStream_t);
+                                          int, bool, void*, hipStream_t);
 
 }  // namespace gdr

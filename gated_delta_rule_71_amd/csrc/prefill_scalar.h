@@ -10,12 +10,13 @@
 // Erase, Decay, Read": section 03 for the linear, reassociable erase and section 04 for the
 // decay as prefix sums of log alpha; the scalar gate of section 05's Gated DeltaNet setting.)
 //
-// Workgroup = 4 key waves + NSW state waves.  Iteration c of the chunk loop has three
-// barrier-separated intervals; in each, the key waves prepare chunk c+1 in one LDS buffer while
-// the state waves consume chunk c from the other:
-//     1: key: operands of c+1 from prefetched registers, then prefetch c+2 | state: K S, Q S
-//     2: key: Gram tiles of c+1 (A, M, fp32 diagonal blocks of A)          | state: solve, O
-//     3: key: inverses of the 16x16 diagonal blocks of (I + A) for c+1      | state: S update
+// Workgroup = 4 key waves + NSW state waves.  Operands live in two LDS buffers (chunk c in one,
+// c+1 in the other).  Iteration c of the chunk loop has three barrier-separated intervals:
+//     1: key waves 0-1: inverses of the 16x16 diagonal blocks of (I + A) for c;
+//        key waves 2-3: M tiles of c                             | state: K S, Q S of c
+//     2: key: operands of c+1 from prefetched registers           | state: solve of c
+//     3: key: prefetch c+2; waves 0-1: A tiles (and the fp32 diagonal blocks) of c+1
+//                                                                 | state: O of c, S update
 #pragma once
 #include "gdr_common.h"
 #include "mfma.h"
@@ -151,7 +152,8 @@ __global__ __launch_bounds__(256 + 64 * NSW) void prefill_scalar_kernel(PrefillA
   __shared__ __attribute__((aligned(32))) unsigned char smem[L::total];
   float* Ld = reinterpret_cast<float*>(smem + L::oLD);
 
-  const int tid = threadIdx.x, wave = tid >> 6;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches on it
   int lane = tid & 63, g = lane >> 4, l16 = lane & 15;
   const bool key = wave < 4;
 
@@ -360,17 +362,14 @@ __global__ __launch_bounds__(256 + 64 * NSW) void prefill_scalar_kernel(PrefillA
   }
   F8 rsf[2];  // -R e^{G_n - G_t} as B fragments: from the solve to the state update
 
-  // ---------------- prologue: chunk 0 ----------------
+  // ---------------- prologue: operands and A tiles of chunk 0 ----------------
   if (key && nch > 0) {
     prefetch(0);
     key_operands(0);
   }
   lds_barrier();
   if (key && nch > 1) prefetch(1);
-  if (key && nch > 0) {
-    key_gram(0);
-    key_inverse(0);
-  }
+  if (key && wave < 2 && nch > 0) key_gram(0);
   lds_barrier();
 
   for (int64_t ch = 0; ch < nch; ++ch) {
@@ -383,16 +382,20 @@ __global__ __launch_bounds__(256 + 64 * NSW) void prefill_scalar_kernel(PrefillA
     unsigned char* B = buf(ch);
     const float* sc = reinterpret_cast<const float*>(B + L::oS);
     const bool more = ch + 1 < nch;
+    f32x4 V[4], O[4], R[4];
+    F8 rf0, rf1;
 
-    // ---- interval 1 ----
+    // ---- interval 1: inverse and M tiles of chunk ch | K S and Q S ----
     GDR_MARK(0);
     if (key) {
-      if (more) key_operands(ch + 1);
+      if (wave < 2)
+        key_inverse(ch);
+      else
+        key_gram(ch);
     } else {
       const __bf16* tQ = reinterpret_cast<const __bf16*>(B + L::oQ);
       const __bf16* tK = reinterpret_cast<const __bf16*>(B + L::oK);
       const __bf16* xT = reinterpret_cast<const __bf16*>(B + L::oX);
-      f32x4 V[4], O[4];
       F8 sf[NKB];
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) sf[kb] = acc_pair_frag<__bf16>(S[2 * kb], S[2 * kb + 1]);
@@ -401,8 +404,8 @@ __global__ __launch_bounds__(256 + 64 * NSW) void prefill_scalar_kernel(PrefillA
       auto load_tile = [&](int ta, F8* kfo, F8* qfo) {
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
-          kfo[kb] = lds_pair_frag(tK + (16 * ta + l16) * LDT, 32 * kb, g, DK);
-          qfo[kb] = lds_pair_frag(tQ + (16 * ta + l16) * LDT, 32 * kb, g, DK);
+          kfo[kb] = lds_pair_frag_k<DK>(tK + (16 * ta + l16) * LDT, 32 * kb, g);
+          qfo[kb] = lds_pair_frag_k<DK>(tQ + (16 * ta + l16) * LDT, 32 * kb, g);
         }
       };
       load_tile(0, kf[0], qf[0]);
@@ -427,14 +430,18 @@ __global__ __launch_bounds__(256 + 64 * NSW) void prefill_scalar_kernel(PrefillA
           O[ta][i] *= e[i];
         }
       }
-      GDR_MARK(4);
+    }
+    GDR_MARK(1);
+    lds_barrier();
+
+    // ---- interval 2: operands of chunk ch+1 | solve ----
+    GDR_MARK(2);
+    if (key) {
+      if (more) key_operands(ch + 1);
+    } else {
       const __bf16* gA = reinterpret_cast<const __bf16*>(B + L::oA);
-      const __bf16* gM = reinterpret_cast<const __bf16*>(B + L::oM);
       const __bf16* dInv = reinterpret_cast<const __bf16*>(B + L::oI);
-      // all operand fragments of the solve and of M R up front
-      f32x4 R[4];
       bf16x4 af[6], tf[4];
-      F8 mf[6];
 #pragma unroll
       for (int i = 0, n = 0; i < 4; ++i) {
         tf[i] = lds_load4(dInv + (16 * i + l16) * LDI + 4 * g);
@@ -442,57 +449,41 @@ __global__ __launch_bounds__(256 + 64 * NSW) void prefill_scalar_kernel(PrefillA
         for (int m = 0; m < i; ++m, ++n) af[n] = lds_load4(gA + (16 * i - 16 + l16) * LDA + 16 * m + 4 * g);
       }
 #pragma unroll
-      for (int ta = 0, n = 0; ta < 4; ++ta) {
-        mf[n++] = lds_pair_frag(gM + (16 * ta + l16) * LDD, 0, g, C);
-        if (ta >= 2) mf[n++] = lds_pair_frag(gM + (16 * ta + l16) * LDD, 32, g, C);
-      }
-#pragma unroll
       for (int i = 0, n = 0; i < 4; ++i) {
 #pragma unroll
         for (int m = 0; m < i; ++m, ++n) V[i] = MM::mma4(af[n], acc_frag4<__bf16>(R[m]), V[i]);
         R[i] = MM::mma4(tf[i], acc_frag4<__bf16>(V[i]), zero4());
       }
-      const F8 rf0 = acc_pair_frag<__bf16>(R[0], R[1]);
-      const F8 rf1 = acc_pair_frag<__bf16>(R[2], R[3]);
-      GDR_MARK(5);
-      {
-        f32x4 Rs[4];
+      rf0 = acc_pair_frag<__bf16>(R[0], R[1]);
+      rf1 = acc_pair_frag<__bf16>(R[2], R[3]);
+      f32x4 Rs[4];
 #pragma unroll
-        for (int ta = 0; ta < 4; ++ta) {
-          const float4 r4 = *reinterpret_cast<const float4*>(sc + 2 * C + 16 * ta + 4 * g);
-          const float rr[4] = {r4.x, r4.y, r4.z, r4.w};
+      for (int ta = 0; ta < 4; ++ta) {
+        const float4 r4 = *reinterpret_cast<const float4*>(sc + 2 * C + 16 * ta + 4 * g);
+        const float rr[4] = {r4.x, r4.y, r4.z, r4.w};
 #pragma unroll
-          for (int i = 0; i < 4; ++i) Rs[ta][i] = -R[ta][i] * rr[i];
-        }
-        rsf[0] = acc_pair_frag<__bf16>(Rs[0], Rs[1]);
-        rsf[1] = acc_pair_frag<__bf16>(Rs[2], Rs[3]);
+        for (int i = 0; i < 4; ++i) Rs[ta][i] = -R[ta][i] * rr[i];
       }
-#pragma unroll
-      for (int ta = 0, n = 0; ta < 4; ++ta) {
-        O[ta] = MM::mma8(mf[n++], rf0, O[ta]);
-        if (ta >= 2) O[ta] = MM::mma8(mf[n++], rf1, O[ta]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t t = static_cast<uint32_t>(t0) + 16 * ta + 4 * g + i;
-          __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(O[ta][i]), ro, t * hdv2 + nloc * 2, 0, 0);
-        }
-      }
+      rsf[0] = acc_pair_frag<__bf16>(Rs[0], Rs[1]);
+      rsf[1] = acc_pair_frag<__bf16>(Rs[2], Rs[3]);
     }
-    GDR_MARK(1);
+    GDR_MARK(3);
     lds_barrier();
 
-    // ---- interval 2 ----
-    GDR_MARK(2);
+    // ---- interval 3: prefetch, A tiles of chunk ch+1 | O and S update ----
+    GDR_MARK(4);
     if (key) {
       if (ch + 2 < nch) prefetch(ch + 2);
-      GDR_MARK(4);
-      if (more) {
-        key_gram(ch + 1);
-        GDR_MARK(5);
-        key_inverse(ch + 1);
-      }
+      if (wave < 2 && more) key_gram(ch + 1);
     } else {
+      const __bf16* gM = reinterpret_cast<const __bf16*>(B + L::oM);
       const __bf16* kT = reinterpret_cast<const __bf16*>(B + L::oKT);
+      F8 mf[6];
+#pragma unroll
+      for (int ta = 0, n = 0; ta < 4; ++ta) {
+        mf[n++] = lds_pair_frag_k<C>(gM + (16 * ta + l16) * LDD, 0, g);
+        if (ta >= 2) mf[n++] = lds_pair_frag_k<C>(gM + (16 * ta + l16) * LDD, 32, g);
+      }
       F8 kf[2][2];
       auto load_kt = [&](int tl, F8* o) {
         const int row = 16 * tl + l16, key = (row >> 3) & 15;
@@ -509,18 +500,28 @@ __global__ __launch_bounds__(256 + 64 * NSW) void prefill_scalar_kernel(PrefillA
         }
       };
       load_kt(0, kf[0]);
-      const F8 rf0 = rsf[0], rf1 = rsf[1];
+#pragma unroll
+      for (int ta = 0, n = 0; ta < 4; ++ta) {
+        O[ta] = MM::mma8(mf[n++], rf0, O[ta]);
+        if (ta >= 2) O[ta] = MM::mma8(mf[n++], rf1, O[ta]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t t = static_cast<uint32_t>(t0) + 16 * ta + 4 * g + i;
+          __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(O[ta][i]), ro, t * hdv2 + nloc * 2, 0, 0);
+        }
+      }
+      const F8 sf0 = rsf[0], sf1 = rsf[1];
       const float egn = sc[4 * C];
 #pragma unroll
       for (int tl = 0; tl < NTD; ++tl) {
         if (tl + 1 < NTD) load_kt(tl + 1, kf[(tl + 1) & 1]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) S[tl][i] *= egn;
-        S[tl] = MM::mma8(kf[tl & 1][0], rf0, S[tl]);
-        S[tl] = MM::mma8(kf[tl & 1][1], rf1, S[tl]);
+        S[tl] = MM::mma8(kf[tl & 1][0], sf0, S[tl]);
+        S[tl] = MM::mma8(kf[tl & 1][1], sf1, S[tl]);
       }
     }
-    GDR_MARK(3);
+    GDR_MARK(5);
     lds_barrier();
   }
 

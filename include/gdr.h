@@ -93,8 +93,13 @@ int gdr_abi_version(void);
 const char* gdr_status_string(int status);
 
 /* Workspace bytes gdr_chunk_fwd needs for `p` (0 when none); 0 also for an
- * invalid problem.  The current kernels keep every intermediate on chip, so
- * this is 0 for every supported problem. */
+ * invalid problem.  bf16 problems with a scalar (or no) decay and a scalar
+ * (or no) erase gate run as a chunk-local kernel plus a per-state kernel that
+ * exchange, per 64-token chunk of every (batch, head), W and U (64 x dk and
+ * 64 x dv bf16), the masked 64 x 64 read-out matrix (bf16) and the 64 gate
+ * prefix sums (fp32), each array 256-byte aligned: about
+ * B * ceil(T/64) * H * (128 dk + 128 dv + 8448) bytes.  Other problems need
+ * none.  The caller owns the buffer; its contents on entry do not matter. */
 size_t gdr_chunk_fwd_workspace_bytes(const gdr_problem* p);
 
 /*
@@ -106,7 +111,9 @@ size_t gdr_chunk_fwd_workspace_bytes(const gdr_problem* p);
  *   S_T    [B,H,dk,dv] fp32 final state; NULL means "not needed"; may alias S0
  *          (in-place update), must not partially overlap it
  *   workspace, workspace_bytes  device scratch of at least
- *          gdr_chunk_fwd_workspace_bytes(p) bytes (may be NULL when that is 0)
+ *          gdr_chunk_fwd_workspace_bytes(p) bytes, 16-byte aligned (may be NULL
+ *          when that is 0); GDR_ERR_WORKSPACE_TOO_SMALL when smaller.  Calls
+ *          that share one workspace must not overlap in time.
  * Method: the chunkwise form the "Recurrent Memory" post points to in
  * section 03 (the erase is linear, so a chunk of tokens reassociates into
  * matrix products and one unit-lower-triangular solve) with the decay entering

@@ -115,7 +115,22 @@ def test_empty_problem_is_a_no_op():
 
 
 def test_workspace_query_and_decode_validation():
-    assert N.workspace_bytes(prob()) == 0
+    assert N.workspace_bytes(prob()) == 0  # per-channel gates: everything stays on chip
+    # scalar decay in bf16: W, U (64 x dk, 64 x dv bf16), -M (64 x 64 bf16) and G (64 fp32)
+    # per 64-token chunk of every (batch, head), each array rounded up to 256 bytes
+    sp = prob(alpha_kind=N.GATE_SCALAR, b_kind=N.GATE_SCALAR, w_kind=N.GATE_SCALAR)
+    chunks = 2 * 3 * 2  # batch 2, heads 3, ceil(70 / 64) = 2
+    r = lambda n: (n + 255) // 256 * 256
+    need = r(chunks * 64 * 128 * 2) + r(chunks * 64 * 128 * 2) + r(chunks * 64 * 64 * 2) + r(chunks * 64 * 4)
+    assert N.workspace_bytes(sp) == need
+    assert N.workspace_bytes(prob(alpha_kind=N.GATE_SCALAR, b_kind=N.GATE_SCALAR, w_kind=N.GATE_SCALAR,
+                                  io_dtype=N.GDR_FP32, dk=32, dv=32)) == 0
+    a = big_apart()
+    args = [a[n] for n in ("q", "k", "v", "la", "b", "w", "S0", "o", "S_T")]
+    ws = 10 * (1 << 32)
+    assert N.chunk_fwd_raw(sp, *args, ws, need - 1, 0) == N.GDR_ERR_WORKSPACE_TOO_SMALL
+    assert N.chunk_fwd_raw(sp, *args, 0, need, 0) == N.GDR_ERR_INVALID_ARGUMENT
+    assert N.chunk_fwd_raw(sp, *args, ws + 8, need, 0) == N.GDR_ERR_MISALIGNED
     p = prob(seqlen=2)
     step = 1 << 32
     rc = N.decode_step_raw(p, step, 2 * step, 3 * step, 4 * step, 5 * step, 6 * step, 7 * step,
