@@ -23,6 +23,9 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 CFLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-fvisibility=hidden",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: the kernels scale and convert accumulators with
+    # vector ALU ops, which would otherwise copy them out of and back into AGPRs every chunk
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wno-unused-variable", "-Wno-unused-but-set-variable",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
