@@ -22,7 +22,7 @@ hipError_t launch_prefill(const IO* q, const IO* k, const IO* v, const IO* la, c
                           int w_kind, bool decay_first, void* workspace, hipStream_t stream);
 bool prefill_supported(int io_dtype, int64_t DK, int64_t DV, int alpha_kind, bool decay_first);
 size_t prefill_workspace_bytes(int io_dtype, int64_t nstate, int64_t T, int64_t DK, int64_t DV,
-                               int alpha_kind, int b_kind);
+                               int alpha_kind, int b_kind, bool decay_first);
 }  // namespace gdr
 
 namespace {
@@ -115,7 +115,7 @@ GDR_EXPORT const char* gdr_status_string(int status) {
 GDR_EXPORT size_t gdr_chunk_fwd_workspace_bytes(const gdr_problem* p) {
   if (check_problem(p) != GDR_OK) return 0;
   return gdr::prefill_workspace_bytes(p->io_dtype, p->batch * p->heads, p->seqlen, p->dk, p->dv,
-                                      p->alpha_kind, p->b_kind);
+                                      p->alpha_kind, p->b_kind, p->order == GDR_DECAY_THEN_ERASE);
 }
 
 GDR_EXPORT int gdr_chunk_fwd(const gdr_problem* p, const void* q, const void* k, const void* v,

@@ -12,12 +12,17 @@ bool prefill_wy_ok(int64_t DK, int64_t DV, int b_kind);
 size_t prefill_wy_workspace_bytes(int64_t nstate, int64_t T, int64_t DK, int64_t DV);
 hipError_t prefill_wy_launch(const PrefillArgs<bf16_t>& p, int64_t nstate, int64_t DK,
                              void* workspace, hipStream_t s);
+bool prefill_wyc_ok(int64_t DK, int64_t DV);
+size_t prefill_wyc_workspace_bytes(int64_t nstate, int64_t T, int64_t DK, int64_t DV, bool two);
+hipError_t prefill_wyc_launch(const PrefillArgs<bf16_t>& p, int64_t nstate, int64_t DK, bool two,
+                              void* workspace, hipStream_t s);
 
 namespace {
 
-// Kernel family for bf16 scalar-decay problems: "wy" (default: chunk-local kernel + state
-// kernel through a workspace), "fused" (one pipelined kernel, no workspace) or "generic"
-// (the all-modes kernel).  Set through GDR_PREFILL_IMPL for comparisons.
+// Kernel family for bf16 problems: "wy" (default: chunk-local kernel + state kernel through a
+// workspace), "fused" (one pipelined kernel per problem, no workspace: the scalar-decay kernel or
+// the all-modes kernel) or "generic" (the all-modes kernel).  Set through GDR_PREFILL_IMPL for
+// comparisons.
 enum class ScalarImpl { kWy, kFused, kGeneric };
 ScalarImpl scalar_impl() {
   const char* e = getenv("GDR_PREFILL_IMPL");
@@ -60,11 +65,11 @@ int choose_nsw_bf16(int64_t DK, int64_t DV, int mode) {
 }  // namespace
 
 size_t prefill_workspace_bytes(int io_dtype, int64_t nstate, int64_t T, int64_t DK, int64_t DV,
-                               int alpha_kind, int b_kind) {
-  if (io_dtype == 0 && alpha_kind != kChannel && prefill_wy_ok(DK, DV, b_kind) &&
-      scalar_impl() == ScalarImpl::kWy)
-    return prefill_wy_workspace_bytes(nstate, T, DK, DV);
-  return 0;
+                               int alpha_kind, int b_kind, bool decay_first) {
+  if (io_dtype != 0 || scalar_impl() != ScalarImpl::kWy) return 0;
+  if (alpha_kind != kChannel)
+    return prefill_wy_ok(DK, DV, b_kind) ? prefill_wy_workspace_bytes(nstate, T, DK, DV) : 0;
+  return prefill_wyc_ok(DK, DV) ? prefill_wyc_workspace_bytes(nstate, T, DK, DV, !decay_first) : 0;
 }
 
 bool prefill_supported(int io_dtype, int64_t DK, int64_t DV, int alpha_kind, bool decay_first) {
@@ -89,6 +94,8 @@ hipError_t launch_prefill(const IO* q, const IO* k, const IO* v, const IO* la, c
         return prefill_wy_launch(a, nstate, DK, workspace, stream);
       if (impl == ScalarImpl::kFused && prefill_scalar_ok(T, H, DK, DV, b_kind))
         return prefill_scalar_launch(a, nstate, DK, stream);
+    } else if (scalar_impl() == ScalarImpl::kWy && prefill_wyc_ok(DK, DV)) {
+      return prefill_wyc_launch(a, nstate, DK, mode == 2, workspace, stream);
     }
     const int nsw = choose_nsw_bf16(DK, DV, mode);
     if (nsw == 0) return hipErrorInvalidValue;
