@@ -48,8 +48,9 @@ struct WycArgs {
   __bf16* Pn;  // [cix][dk][64]  -Pbar^T (MODE 1: -Kbar^T)
   __bf16* Kb;  // [cix][dk][64]  Kbar^T (MODE 2)
   __bf16* Mn;  // [cix][64][64]  -M_QP (MODE 1: -M), zero above the diagonal
-  __bf16* Y;   // [cix][64][dv]  Y
+  __bf16* Y;   // [cix][dv][64]  Y^T
   __bf16* Z;   // [cix][64][dv]  Z (MODE 2)
+  __bf16* Xt;  // [cix][dv][64]  X^T (MODE 2)
   float* Egn;  // [cix][dk]      e^{G_n}
   int* flag;   // [cix]          1: exact token path
   int64_t T, H, DV, nch;
@@ -230,6 +231,7 @@ __global__ __launch_bounds__(256) void wyc_prep_kernel(WycArgs a) {
     a.Egn[cix * DK + tid] = __expf(run);
     if (fmaxf(fabsf(ref), fabsf(run - ref)) > kWycSpanLimit || !(run == run)) sFlag[0] = 1;
   }
+  GDR_PMARK(0);
   lds_barrier();
   const bool robust = sFlag[0] != 0;
   if (tid == 0) a.flag[cix] = robust ? 1 : 0;
@@ -245,7 +247,6 @@ __global__ __launch_bounds__(256) void wyc_prep_kernel(WycArgs a) {
       eref[j] = fEref[d0 + j];
       egr[j] = fEgr[d0 + j];
     }
-    __bf16 pnT[8][TPS], kbT[8][TPS];
 #pragma unroll
     for (int u = 0; u < TPS; ++u) {
       const int t = ts * TPS + u;
@@ -275,11 +276,8 @@ __global__ __launch_bounds__(256) void wyc_prep_kernel(WycArgs a) {
           const float epr = __builtin_amdgcn_rcpf(ep);
           oc[j] = static_cast<__bf16>(cc[j] * ep);
           op[j] = static_cast<__bf16>(k[j] * epr);
-          pnT[j][u] = static_cast<__bf16>(-(k[j] * epr * egr[j]));  // -k e^{G_n - G_{t-1}}
-          kbT[j][u] = static_cast<__bf16>(k[j] * er * egr[j]);      // k e^{G_n - G_t}
         } else {
           oc[j] = static_cast<__bf16>(cc[j] * eq);
-          pnT[j][u] = static_cast<__bf16>(-(k[j] * er * egr[j]));   // -k e^{G_n - G_t}
         }
       }
       *reinterpret_cast<bf16x8*>(tQ + t * LDT + d0) = oq;
@@ -288,16 +286,11 @@ __global__ __launch_bounds__(256) void wyc_prep_kernel(WycArgs a) {
       if (TWO) *reinterpret_cast<bf16x8*>(tP + t * LDT + d0) = op;
       *reinterpret_cast<bf16x8*>(a.Qp + (cix * C + t) * DK + d0) = oqp;
     }
-    // channel-major rows d0..d0+7, this thread's TPS tokens per store
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      lds_store_run<TPS>(reinterpret_cast<__bf16*>(a.Pn) + (cix * DK + d0 + j) * C + ts * TPS, pnT[j]);
-      if (TWO) lds_store_run<TPS>(reinterpret_cast<__bf16*>(a.Kb) + (cix * DK + d0 + j) * C + ts * TPS, kbT[j]);
-    }
   }
   // tiles above the diagonal of -M, L_K and M_QK are never written by the Gram phase but are
   // read as zero by the products below (the three arrays are contiguous)
   for (int i = tid; i < (L::oT - L::oM) / 4; i += 256) reinterpret_cast<uint32_t*>(gM)[i] = 0u;
+  GDR_PMARK(1);
   lds_barrier();
 
   // ---- Gram tiles: 20 jobs = 2 row operands x 10 tile pairs, 5 per wave ----
@@ -373,6 +366,7 @@ __global__ __launch_bounds__(256) void wyc_prep_kernel(WycArgs a) {
       }
     }
   }
+  GDR_PMARK(2);
   lds_barrier();
 
   // ---- diagonal inverses (waves 0-1) | -M_QP out (waves 2-3) ----
@@ -384,9 +378,39 @@ __global__ __launch_bounds__(256) void wyc_prep_kernel(WycArgs a) {
       const int r = item >> 3, part = item & 7;
       *reinterpret_cast<uint4*>(Mo + r * C + part * 8) = *reinterpret_cast<const uint4*>(gM + r * LDD + part * 8);
     }
+    if (TWO) {  // X^T out: item = column * 8 + part holds tokens 8 part .. 8 part + 7
+      __bf16* Xo = a.Xt + cix * DV * C;
+      for (int item = tid - 128; item < DV * 8; item += 128) {
+        const int col = item >> 3, part = item & 7;
+        bf16x8 xv;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xv[e] = tX[(8 * part + e) * LDX + col];
+        *reinterpret_cast<bf16x8*>(Xo + col * C + 8 * part) = xv;
+      }
+    }
   }
+  GDR_PMARK(3);
   lds_barrier();
 
+  // ---- -Pbar^T (and Kbar^T) out: the split Phat (Khat) columns times e^{G_n - G_ref}; 16-byte
+  // pieces of channel rows, so every store instruction writes whole row segments ----
+  {
+    __bf16* Po = a.Pn + cix * DK * C;
+    __bf16* Ko = a.Kb + cix * DK * C;
+    const __bf16* src = TWO ? tP : tK;
+    for (int item = tid; item < DK * 8; item += 256) {
+      const int d = item >> 3, part = item & 7;
+      const float f = fEgr[d];
+      bf16x8 pv, kv;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        pv[e] = static_cast<__bf16>(-static_cast<float>(src[(8 * part + e) * LDT + d]) * f);
+        if (TWO) kv[e] = static_cast<__bf16>(static_cast<float>(tK[(8 * part + e) * LDT + d]) * f);
+      }
+      *reinterpret_cast<bf16x8*>(Po + d * C + 8 * part) = pv;
+      if (TWO) *reinterpret_cast<bf16x8*>(Ko + d * C + 8 * part) = kv;
+    }
+  }
   // ---- T = (I + L_P)^{-1}: wave j solves column block j on the identity ----
   {
     const int j = wave;
@@ -413,6 +437,7 @@ __global__ __launch_bounds__(256) void wyc_prep_kernel(WycArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) tT[(16 * i + 4 * g + e) * LDD + 16 * j + l16] = static_cast<__bf16>(R[i][e]);
   }
+  GDR_PMARK(4);
   lds_barrier();
 
   // ---- products, as transposed tiles so that each lane stores four consecutive columns ----
@@ -444,6 +469,25 @@ __global__ __launch_bounds__(256) void wyc_prep_kernel(WycArgs a) {
       if (ta >= 2) out[ta] = MM::mma8(af[1], bf[n++], out[ta]);
     }
     (void)strict;
+  };
+  // upright tiles of (lower-triangular 64 x 64 A-side matrix) x (64 x 16 B-side tile): out[ta] lane
+  // holds D[token 16 ta + 4 g + i][column l16]
+  auto up_product = [&](const F8* af, const F8* bf, f32x4* out) {
+#pragma unroll
+    for (int ta = 0, n = 0; ta < 4; ++ta) {
+      out[ta] = MM::mma8(af[n++], bf[0], zero4());
+      if (ta >= 2) out[ta] = MM::mma8(af[n++], bf[1], out[ta]);
+    }
+  };
+  // upright tiles out as a [column][64] array: four consecutive tokens per 8-byte store
+  auto store_up_t = [&](__bf16* dst, int col0c, const f32x4* t4, float sgn) {
+#pragma unroll
+    for (int ta = 0; ta < 4; ++ta) {
+      bf16x4 ob;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ob[i] = static_cast<__bf16>(t4[ta][i] * sgn);
+      *reinterpret_cast<bf16x4*>(dst + (col0c + l16) * C + 16 * ta + 4 * g) = ob;
+    }
   };
   auto store_tr = [&](__bf16* dst, int64_t pitch, int col0c, const f32x4* t4, float sgn) {
 #pragma unroll
@@ -490,8 +534,8 @@ __global__ __launch_bounds__(256) void wyc_prep_kernel(WycArgs a) {
         lf[0] = acc_pair_frag<__bf16>(LKX[0], LKX[1]);
         lf[1] = acc_pair_frag<__bf16>(LKX[2], LKX[3]);
         f32x4 D[4];
-        tr_product(lf, tfr, false, D);
-        store_tr(Yo, DV, 16 * ct, D, 1.f);
+        up_product(tfr, lf, D);
+        store_up_t(Yo, 16 * ct, D, 1.f);
         tr_product(xf, mqf, false, D);
         store_tr(Zo, DV, 16 * ct, D, 1.f);
       }
@@ -501,11 +545,12 @@ __global__ __launch_bounds__(256) void wyc_prep_kernel(WycArgs a) {
         F8 xf[2];
         col_frags(tX, LDX, col, 1.f, xf);
         f32x4 D[4];
-        tr_product(xf, tfr, false, D);
-        store_tr(Yo, DV, 16 * ct, D, -1.f);
+        up_product(tfr, xf, D);
+        store_up_t(Yo, 16 * ct, D, -1.f);
       }
     }
   }
+  GDR_PMARK(5);
 }
 
 // ------------------------------------------------------------------ state kernel
@@ -640,7 +685,7 @@ __global__ __launch_bounds__(192) void wyc_state_kernel(WycArgs a) {
       sc[tid] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(re, tid * 4, 0, 0));
     }
     if (tid == 0) reinterpret_cast<int*>(sc + DK)[0] = robust;
-    if (TWO || robust) store_x(c, xT);
+    if (robust) store_x(c, xT);
     if (robust) {
       // raw c = b . k and log alpha rows, token-major
       const int64_t t0 = c * C, rr = (bi * T + t0) * H + hi;
@@ -674,11 +719,12 @@ __global__ __launch_bounds__(192) void wyc_state_kernel(WycArgs a) {
       return;
     }
     const auto rp = make_rsrc(a.Pn + cix * DK * C, DK * C * 2);
-    const auto rkb = make_rsrc(TWO ? a.Kb + cix * DK * C : a.Pn, DK * C * 2);
     const auto rm = make_rsrc(a.Mn + cix * C * C, C * C * 2);
-    const auto ry = make_rsrc(a.Y + cix * C * DV + col0, static_cast<uint32_t>((C * DV - col0) * 2));
+    const auto ry = make_rsrc(a.Y + (cix * DV + col0) * C, DVS * C * 2);
+    const auto rx = make_rsrc(TWO ? a.Xt + (cix * DV + col0) * C : a.Y, DVS * C * 2);
     const auto rz = make_rsrc(TWO ? a.Z + cix * C * DV + col0 : a.Y, static_cast<uint32_t>((C * DV - col0) * 2));
-    uint4 pp[CPT], pkb[CPT], pm[MPT], py[XPT], pz[XPT];
+    const auto rkb = make_rsrc(TWO ? a.Kb + cix * DK * C : a.Pn, DK * C * 2);
+    uint4 pp[CPT], pkb[CPT], pm[MPT], py[XPT], px[XPT], pz[XPT];
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
       pp[j] = buf_load16(rp, (tid + NLT * j) * 16);
@@ -690,9 +736,12 @@ __global__ __launch_bounds__(192) void wyc_state_kernel(WycArgs a) {
     for (int j = 0; j < XPT; ++j) {
       const int item = tid + NLT * j;
       const uint32_t t = item / NXG, xg = item % NXG;
-      const uint32_t off = item < C * NXG ? (t * DV + xg * 8) * 2 : oob;
-      py[j] = buf_load16(ry, off);
-      if (TWO) pz[j] = buf_load16(rz, off);
+      const bool in = item < C * NXG;
+      py[j] = buf_load16(ry, in ? item * 16 : oob);  // [DVS][64]: item = column * 8 + part
+      if (TWO) {
+        px[j] = buf_load16(rx, in ? item * 16 : oob);
+        pz[j] = buf_load16(rz, in ? (t * DV + xg * 8) * 2 : oob);
+      }
     }
     // [dk][64] arrays: item = row * 8 + part holds tokens 8 part .. 8 part + 7 of row `row`
 #pragma unroll
@@ -716,15 +765,18 @@ __global__ __launch_bounds__(192) void wyc_state_kernel(WycArgs a) {
     for (int j = 0; j < XPT; ++j) {
       const int item = tid + NLT * j;
       if (item < C * NXG) {
-        const int t = item / NXG, xg = item % NXG;
-        const uint32_t w4[4] = {py[j].x, py[j].y, py[j].z, py[j].w};
-        uint16_t* yTu = reinterpret_cast<uint16_t*>(yT);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          yTu[(xg * 8 + 2 * e) * LDD + swz(2 * xg, t)] = static_cast<uint16_t>(w4[e] & 0xffffu);
-          yTu[(xg * 8 + 2 * e + 1) * LDD + swz(2 * xg, t)] = static_cast<uint16_t>(w4[e] >> 16);
+        // [column][64] slices: tokens 8 part .. 8 part + 7 of one column as two swizzled quads
+        const int col = item >> 3, part = item & 7, key = 2 * (col >> 3);
+        __bf16* yr = yT + col * LDD;
+        *reinterpret_cast<uint2*>(yr + swz(key, 8 * part)) = make_uint2(py[j].x, py[j].y);
+        *reinterpret_cast<uint2*>(yr + swz(key, 8 * part + 4)) = make_uint2(py[j].z, py[j].w);
+        if (TWO) {
+          __bf16* xr = xT + col * LDD;
+          *reinterpret_cast<uint2*>(xr + swz(key, 8 * part)) = make_uint2(px[j].x, px[j].y);
+          *reinterpret_cast<uint2*>(xr + swz(key, 8 * part + 4)) = make_uint2(px[j].z, px[j].w);
+          const int t = item / NXG, xg = item % NXG;
+          *reinterpret_cast<uint4*>(zs + t * LDZ + xg * 8) = pz[j];
         }
-        if (TWO) *reinterpret_cast<uint4*>(zs + t * LDZ + xg * 8) = pz[j];
       }
     }
   };
@@ -989,6 +1041,7 @@ __global__ __launch_bounds__(192) void wyc_state_kernel(WycArgs a) {
     asm volatile("" : "+v"(lane), "+v"(g), "+v"(l16));
     const bool more = ch + 1 < nch;
     int robust = 0;
+    GDR_MARK(0);
     if (loader) {
       if (more) {
         nflag = read_flag(ch + 1);
@@ -1001,13 +1054,17 @@ __global__ __launch_bounds__(192) void wyc_state_kernel(WycArgs a) {
       else
         qs_ws();
     }
+    GDR_MARK(1);
     lds_barrier();
+    GDR_MARK(2);
     if (loader) {
       if (more) store_set1(ch + 1, nflag);
     } else if (!robust) {
       second(ch);
     }
+    GDR_MARK(3);
     lds_barrier();
+    GDR_MARK(4);
   }
 
   if (!loader && a.S_T != nullptr) {

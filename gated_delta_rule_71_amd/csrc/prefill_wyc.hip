@@ -7,8 +7,8 @@ namespace {
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 struct WycSizes {
-  size_t W, Qp, Pn, Kb, Mn, Y, Z, Egn, flag;
-  size_t total() const { return W + Qp + Pn + Kb + Mn + Y + Z + Egn + flag; }
+  size_t W, Qp, Pn, Kb, Mn, Y, Z, Xt, Egn, flag;
+  size_t total() const { return W + Qp + Pn + Kb + Mn + Y + Z + Xt + Egn + flag; }
 };
 
 WycSizes wyc_sizes(int64_t nstate, int64_t T, int64_t DK, int64_t DV, bool two) {
@@ -21,6 +21,7 @@ WycSizes wyc_sizes(int64_t nstate, int64_t T, int64_t DK, int64_t DV, bool two) 
   s.Mn = align256(ch * 64 * 64 * 2);
   s.Y = align256(ch * 64 * DV * 2);
   s.Z = two ? s.Y : 0;
+  s.Xt = two ? s.Y : 0;
   s.Egn = align256(ch * DK * 4);
   s.flag = align256(ch * 4);
   return s;
@@ -92,6 +93,8 @@ hipError_t prefill_wyc_launch(const PrefillArgs<bf16_t>& p, int64_t nstate, int6
   ws += z.Y;
   a.Z = reinterpret_cast<__bf16*>(ws);
   ws += z.Z;
+  a.Xt = reinterpret_cast<__bf16*>(ws);
+  ws += z.Xt;
   a.Egn = reinterpret_cast<float*>(ws);
   ws += z.Egn;
   a.flag = reinterpret_cast<int*>(ws);

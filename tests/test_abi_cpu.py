@@ -116,14 +116,14 @@ def test_empty_problem_is_a_no_op():
 
 def test_workspace_query_and_decode_validation():
     # per-channel decay (erase then decay): W, Qhat (64 x dk), -Pbar^T, Kbar^T (dk x 64), -M_QP
-    # (64 x 64), Y, Z (64 x dv) in bf16, e^{G_n} (dk fp32) and a flag per 64-token chunk of every
-    # (batch, head); decay-then-erase drops Kbar^T and Z
+    # (64 x 64), Y^T, Z, X^T (64 x dv) in bf16, e^{G_n} (dk fp32) and a flag per 64-token chunk of
+    # every (batch, head); decay-then-erase drops Kbar^T, Z and X^T
     r = lambda n: (n + 255) // 256 * 256
     ch = 2 * 3 * 2
     two = 2 * r(ch * 64 * 128 * 2) + 2 * r(ch * 128 * 64 * 2) + r(ch * 64 * 64 * 2) + \
-        2 * r(ch * 64 * 128 * 2) + r(ch * 128 * 4) + r(ch * 4)
+        3 * r(ch * 64 * 128 * 2) + r(ch * 128 * 4) + r(ch * 4)
     assert N.workspace_bytes(prob()) == two
-    one = two - r(ch * 128 * 64 * 2) - r(ch * 64 * 128 * 2)
+    one = two - r(ch * 128 * 64 * 2) - 2 * r(ch * 64 * 128 * 2)
     assert N.workspace_bytes(prob(order=N.DECAY_THEN_ERASE)) == one
     # scalar decay in bf16: W, U (64 x dk, 64 x dv bf16), -M (64 x 64 bf16) and G (64 fp32)
     # per 64-token chunk of every (batch, head), each array rounded up to 256 bytes
