@@ -8,11 +8,15 @@ steps), on one MI355X, through the C ABI.
 Prints ONE JSON line.  `value` is prefill tokens/s (B*T / time per call) with inputs resident in
 HBM; a step is one gdr_chunk_fwd call over the whole batch.  Two input sets alternate between
 calls so that the 256 MB Infinity Cache cannot serve a call from the previous one.
-`roofline` is for the prefill kernel: algorithmic HBM bytes per launch (inputs read once,
-o and S_T written once, S0 read once) divided by the mean kernel time from HIP events on the
-launch stream, against MI355X's 8 TB/s; `traffic` is the measured HBM bytes per launch from
-profiles/hbm_counters.txt when that file was recorded on the current kernel sources, else null; `mfma_frac` is algorithmic FLOP per second against the
-2.5166 PFLOP/s dense bf16 peak.  `decode` reports state GB/s for the decode workload (the
+`roofline` is for one prefill call, which for bf16 inputs is two kernel launches (a chunk-local
+kernel over every chunk, then a per-state kernel that carries the state across chunks through a
+workspace): algorithmic HBM bytes per call (inputs read once, o and S_T written once, S0 read
+once) divided by the mean call time from HIP events on the launch stream, against MI355X's
+8 TB/s.  `phases` splits the call with an event recorded between the two launches
+(gdr_chunk_fwd_marked).  `traffic` is the measured HBM bytes per call (per kernel under
+`phases`) from profiles/hbm_counters.txt when that file was recorded on the current kernel
+sources, else null.  `mfma_frac` is algorithmic FLOP per second against the 2.5166 PFLOP/s
+dense bf16 peak.  `decode` reports state GB/s for the decode workload (the
 state is read and written once per step).  `cpu_baseline` times the fp64 oracle on the host.
 """
 import argparse
@@ -78,7 +82,8 @@ def kernel_source_digest():
 
 
 def recorded_traffic(key):
-    """HBM bytes per launch for `key` ("prefill:<workload>" or "decode:<workload>") from the
+    """HBM bytes per launch for `key` ("prefill:<workload>" for a whole call, "prefill_prep:" and
+    "prefill_state:" for its two kernels, or "decode:<workload>") from the
     committed rocprofv3 counter summary, scaled by the calibration copy; None when the summary
     is absent, has no such entry, or was taken on other kernel sources."""
     path = os.path.join(ROOT, "profiles", "hbm_counters.txt")
@@ -110,29 +115,39 @@ def time_prefill(wl, steps, warmup, dev):
             for _ in range(2)]
     S_T = [torch.empty((wl.B, wl.H, wl.DK, wl.DV), dtype=torch.float32, device=dev) for _ in range(2)]
 
-    def call(i):
+    need = gdr.workspace_bytes(sets[0]["q"], sets[0]["v"], sets[0]["log_alpha"], sets[0]["b"],
+                               sets[0]["w"])
+    ws = torch.empty((max(1, need),), dtype=torch.uint8, device=dev)
+
+    def call(i, mark=None):
         g = sets[i % 2]
         gdr.chunk_fwd(g["q"], g["k"], g["v"], g["log_alpha"], g["b"], g["w"], g["S0"],
-                      out=outs[i % 2], final_state=S_T[i % 2])
+                      out=outs[i % 2], final_state=S_T[i % 2], workspace=ws, phase_event=mark)
 
     for i in range(warmup):
         call(i)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    mids = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for e in mids:
+        e.record(stream)  # creates the HIP events before the timed region
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
         starts[i].record(stream)
-        call(i)
+        call(i, mids[i])
         ends[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))  # ms, one launch each
+    per = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))  # ms, one call each
+    prep = [s.elapsed_time(m) for s, m in zip(starts, mids)]       # chunk-local kernel
+    state = [m.elapsed_time(e) for m, e in zip(mids, ends)]        # per-state kernel
     mean = sum(per) / len(per)
     return dict(wall_s=wall, mean_ms=mean, median_ms=per[len(per) // 2], p10_ms=per[len(per) // 10],
-                p90_ms=per[(9 * len(per)) // 10])
+                p90_ms=per[(9 * len(per)) // 10], prep_ms=sum(prep) / len(prep),
+                state_ms=sum(state) / len(state), workspace_bytes=need)
 
 
 def time_decode(wl, n_steps, dev):
@@ -246,7 +261,13 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved_gbs / PEAK_HBM_GBS,
                      "traffic": recorded_traffic("prefill:" + wl.name),
-                     "algorithmic_bytes": nbytes},
+                     "algorithmic_bytes": nbytes,
+                     "scope": "one gdr_chunk_fwd call: chunk-local kernel then per-state kernel"},
+        "phases": {"chunk_local": {"ms": pf["prep_ms"],
+                                   "traffic": recorded_traffic("prefill_prep:" + wl.name)},
+                   "state": {"ms": pf["state_ms"],
+                             "traffic": recorded_traffic("prefill_state:" + wl.name)}},
+        "workspace_bytes": pf["workspace_bytes"],
     }
     if not args.no_decode:
         dw = synth.WORKLOADS["decode"]

@@ -69,12 +69,14 @@ def _stream(device):
 
 
 def chunk_fwd(q, k, v, log_alpha=None, b=None, w=None, S0=None, order="erase_then_decay",
-              out=None, final_state=True, workspace=None):
+              out=None, final_state=True, workspace=None, phase_event=None):
     """Chunkwise prefill.  Returns (o [B,T,H,dv] in q's dtype, S_T [B,H,dk,dv] float32 or None).
 
     ``S0`` (float32 [B,H,dk,dv] or None for zeros) is read before S_T is written; pass
     ``final_state=S0`` to update the state in place.  ``workspace`` is an optional uint8
-    device tensor of at least ``workspace_bytes(...)`` bytes; one is allocated when absent."""
+    device tensor of at least ``workspace_bytes(...)`` bytes; one is allocated when absent.
+    ``phase_event`` (a torch.cuda.Event) is recorded between the chunk-local kernel and the
+    per-state kernel, for timing the two separately."""
     torch = _torch()
     B, T, H, DK = q.shape
     DV = v.shape[-1]
@@ -107,9 +109,17 @@ def chunk_fwd(q, k, v, log_alpha=None, b=None, w=None, S0=None, order="erase_the
     elif workspace.device != dev or workspace.numel() * workspace.element_size() < need:
         raise ValueError("workspace must be a device tensor of at least %d bytes" % need)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    rc = _native.chunk_fwd_raw(prob, _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w),
-                               _ptr(S0), _ptr(o), _ptr(S_T), _ptr(workspace), ws_bytes,
-                               _stream(dev))
+    if phase_event is None:
+        rc = _native.chunk_fwd_raw(prob, _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b),
+                                   _ptr(w), _ptr(S0), _ptr(o), _ptr(S_T), _ptr(workspace),
+                                   ws_bytes, _stream(dev))
+    else:
+        if not phase_event.cuda_event:  # torch creates the HIP event at its first record
+            phase_event.record(torch.cuda.current_stream(dev))
+        rc = _native.chunk_fwd_marked_raw(prob, _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
+                                          _ptr(b), _ptr(w), _ptr(S0), _ptr(o), _ptr(S_T),
+                                          _ptr(workspace), ws_bytes, _stream(dev),
+                                          phase_event.cuda_event)
     if rc != _native.GDR_OK:
         raise GdrError(rc, "gdr_chunk_fwd")
     return o, S_T

@@ -16,7 +16,7 @@ GATE_NONE, GATE_SCALAR, GATE_CHANNEL = 0, 1, 2
 ERASE_THEN_DECAY, DECAY_THEN_ERASE = 0, 1
 
 EXPORTED = ("gdr_abi_version", "gdr_status_string", "gdr_chunk_fwd_workspace_bytes",
-            "gdr_chunk_fwd", "gdr_decode_step")
+            "gdr_chunk_fwd", "gdr_chunk_fwd_marked", "gdr_decode_step")
 
 
 class GdrProblem(ctypes.Structure):
@@ -70,6 +70,8 @@ def lib():
         L.gdr_chunk_fwd_workspace_bytes.argtypes = [pp]
         L.gdr_chunk_fwd.restype = ctypes.c_int
         L.gdr_chunk_fwd.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.gdr_chunk_fwd_marked.restype = ctypes.c_int
+        L.gdr_chunk_fwd_marked.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
         L.gdr_decode_step.restype = ctypes.c_int
         L.gdr_decode_step.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         _lib = L
@@ -93,6 +95,15 @@ def chunk_fwd_raw(problem, q, k, v, la, b, w, S0, o, S_T, ws, ws_bytes, stream):
     return lib().gdr_chunk_fwd(ctypes.byref(problem), q or None, k or None, v or None, la or None,
                                b or None, w or None, S0 or None, o or None, S_T or None,
                                ws or None, ws_bytes, stream or None)
+
+
+def chunk_fwd_marked_raw(problem, q, k, v, la, b, w, S0, o, S_T, ws, ws_bytes, stream, event):
+    """chunk_fwd_raw that also records the HIP event `event` (raw handle) between the
+    chunk-local and the per-state kernel.  Returns the status."""
+    return lib().gdr_chunk_fwd_marked(ctypes.byref(problem), q or None, k or None, v or None,
+                                      la or None, b or None, w or None, S0 or None, o or None,
+                                      S_T or None, ws or None, ws_bytes, stream or None,
+                                      event or None)
 
 
 def decode_step_raw(problem, q, k, v, la, b, w, S, o, stream):

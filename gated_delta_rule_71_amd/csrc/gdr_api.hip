@@ -19,7 +19,8 @@ template <typename IO>
 hipError_t launch_prefill(const IO* q, const IO* k, const IO* v, const IO* la, const IO* bg,
                           const IO* wg, const float* S0, IO* o, float* S_T, int64_t B, int64_t T,
                           int64_t H, int64_t DK, int64_t DV, int alpha_kind, int b_kind,
-                          int w_kind, bool decay_first, void* workspace, hipStream_t stream);
+                          int w_kind, bool decay_first, void* workspace, hipEvent_t mark,
+                          hipStream_t stream);
 bool prefill_supported(int io_dtype, int64_t DK, int64_t DV, int alpha_kind, bool decay_first);
 size_t prefill_workspace_bytes(int io_dtype, int64_t nstate, int64_t T, int64_t DK, int64_t DV,
                                int alpha_kind, int b_kind, bool decay_first);
@@ -118,10 +119,10 @@ GDR_EXPORT size_t gdr_chunk_fwd_workspace_bytes(const gdr_problem* p) {
                                       p->alpha_kind, p->b_kind, p->order == GDR_DECAY_THEN_ERASE);
 }
 
-GDR_EXPORT int gdr_chunk_fwd(const gdr_problem* p, const void* q, const void* k, const void* v,
-                             const void* log_alpha, const void* b, const void* w, const float* S0,
-                             void* o, float* S_T, void* workspace, size_t workspace_bytes,
-                             void* stream) {
+namespace {
+int chunk_fwd(const gdr_problem* p, const void* q, const void* k, const void* v,
+              const void* log_alpha, const void* b, const void* w, const float* S0, void* o,
+              float* S_T, void* workspace, size_t workspace_bytes, void* stream, void* mark) {
   int rc = check_problem(p);
   if (rc != GDR_OK) return rc;
   rc = check_tensors(p, p->seqlen, q, k, v, log_alpha, b, w, o);
@@ -152,15 +153,34 @@ GDR_EXPORT int gdr_chunk_fwd(const gdr_problem* p, const void* q, const void* k,
         (const T*)q, (const T*)k, (const T*)v, (const T*)gate_ptr(p->alpha_kind, log_alpha),
         (const T*)gate_ptr(p->b_kind, b), (const T*)gate_ptr(p->w_kind, w), S0, (T*)o, S_T,
         p->batch, p->seqlen, p->heads, p->dk, p->dv, p->alpha_kind, p->b_kind, p->w_kind,
-        decay_first, workspace, s);
+        decay_first, workspace, static_cast<hipEvent_t>(mark), s);
   } else {
     e = gdr::launch_prefill<float>(
         (const float*)q, (const float*)k, (const float*)v,
         (const float*)gate_ptr(p->alpha_kind, log_alpha), (const float*)gate_ptr(p->b_kind, b),
         (const float*)gate_ptr(p->w_kind, w), S0, (float*)o, S_T, p->batch, p->seqlen, p->heads,
-        p->dk, p->dv, p->alpha_kind, p->b_kind, p->w_kind, decay_first, workspace, s);
+        p->dk, p->dv, p->alpha_kind, p->b_kind, p->w_kind, decay_first, workspace,
+        static_cast<hipEvent_t>(mark), s);
   }
   return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
+}
+}  // namespace
+
+GDR_EXPORT int gdr_chunk_fwd(const gdr_problem* p, const void* q, const void* k, const void* v,
+                             const void* log_alpha, const void* b, const void* w, const float* S0,
+                             void* o, float* S_T, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  return chunk_fwd(p, q, k, v, log_alpha, b, w, S0, o, S_T, workspace, workspace_bytes, stream,
+                   nullptr);
+}
+
+GDR_EXPORT int gdr_chunk_fwd_marked(const gdr_problem* p, const void* q, const void* k,
+                                    const void* v, const void* log_alpha, const void* b,
+                                    const void* w, const float* S0, void* o, float* S_T,
+                                    void* workspace, size_t workspace_bytes, void* stream,
+                                    void* phase_event) {
+  return chunk_fwd(p, q, k, v, log_alpha, b, w, S0, o, S_T, workspace, workspace_bytes, stream,
+                   phase_event);
 }
 
 GDR_EXPORT int gdr_decode_step(const gdr_problem* p, const void* q, const void* k, const void* v,

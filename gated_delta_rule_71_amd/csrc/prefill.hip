@@ -11,11 +11,11 @@ hipError_t prefill_scalar_launch(PrefillArgs<bf16_t> a, int64_t nstate, int64_t 
 bool prefill_wy_ok(int64_t DK, int64_t DV, int b_kind);
 size_t prefill_wy_workspace_bytes(int64_t nstate, int64_t T, int64_t DK, int64_t DV);
 hipError_t prefill_wy_launch(const PrefillArgs<bf16_t>& p, int64_t nstate, int64_t DK,
-                             void* workspace, hipStream_t s);
+                             void* workspace, hipEvent_t mark, hipStream_t s);
 bool prefill_wyc_ok(int64_t DK, int64_t DV);
 size_t prefill_wyc_workspace_bytes(int64_t nstate, int64_t T, int64_t DK, int64_t DV, bool two);
 hipError_t prefill_wyc_launch(const PrefillArgs<bf16_t>& p, int64_t nstate, int64_t DK, bool two,
-                              void* workspace, hipStream_t s);
+                              void* workspace, hipEvent_t mark, hipStream_t s);
 
 namespace {
 
@@ -62,6 +62,11 @@ int choose_nsw_bf16(int64_t DK, int64_t DV, int mode) {
   return 0;
 }
 
+// The optional phase marker of a single-kernel problem goes before its one launch.
+hipError_t record_mark(hipEvent_t mark, hipStream_t stream) {
+  return mark != nullptr ? hipEventRecord(mark, stream) : hipSuccess;
+}
+
 }  // namespace
 
 size_t prefill_workspace_bytes(int io_dtype, int64_t nstate, int64_t T, int64_t DK, int64_t DV,
@@ -83,7 +88,8 @@ template <typename IO>
 hipError_t launch_prefill(const IO* q, const IO* k, const IO* v, const IO* la, const IO* bg,
                           const IO* wg, const float* S0, IO* o, float* S_T, int64_t B, int64_t T,
                           int64_t H, int64_t DK, int64_t DV, int alpha_kind, int b_kind,
-                          int w_kind, bool decay_first, void* workspace, hipStream_t stream) {
+                          int w_kind, bool decay_first, void* workspace, hipEvent_t mark,
+                          hipStream_t stream) {
   const int mode = prefill_mode(alpha_kind, decay_first);
   PrefillArgs<IO> a{q, k, v, la, bg, wg, S0, o, S_T, T, H, DV, alpha_kind, b_kind, w_kind, 1};
   const int64_t nstate = B * H;
@@ -91,14 +97,17 @@ hipError_t launch_prefill(const IO* q, const IO* k, const IO* v, const IO* la, c
     if (mode == 0) {
       const ScalarImpl impl = scalar_impl();
       if (impl == ScalarImpl::kWy && prefill_wy_ok(DK, DV, b_kind))
-        return prefill_wy_launch(a, nstate, DK, workspace, stream);
-      if (impl == ScalarImpl::kFused && prefill_scalar_ok(T, H, DK, DV, b_kind))
+        return prefill_wy_launch(a, nstate, DK, workspace, mark, stream);
+      if (impl == ScalarImpl::kFused && prefill_scalar_ok(T, H, DK, DV, b_kind)) {
+        if (const hipError_t e = record_mark(mark, stream); e != hipSuccess) return e;
         return prefill_scalar_launch(a, nstate, DK, stream);
+      }
     } else if (scalar_impl() == ScalarImpl::kWy && prefill_wyc_ok(DK, DV)) {
-      return prefill_wyc_launch(a, nstate, DK, mode == 2, workspace, stream);
+      return prefill_wyc_launch(a, nstate, DK, mode == 2, workspace, mark, stream);
     }
     const int nsw = choose_nsw_bf16(DK, DV, mode);
     if (nsw == 0) return hipErrorInvalidValue;
+    if (const hipError_t e = record_mark(mark, stream); e != hipSuccess) return e;
     a.nsl = static_cast<int>(DV / (16 * nsw));
     switch (DK) {
       case 16: return prefill_bf16_dk16(a, nstate, mode, nsw, stream);
@@ -108,6 +117,7 @@ hipError_t launch_prefill(const IO* q, const IO* k, const IO* v, const IO* la, c
     }
   } else {
     if (!fits_dk<float>(DK, mode, 1)) return hipErrorInvalidValue;
+    if (const hipError_t e = record_mark(mark, stream); e != hipSuccess) return e;
     a.nsl = static_cast<int>(DV / 16);
     return prefill_f32_any(a, nstate, DK, mode, 1, stream);
   }
@@ -117,10 +127,10 @@ template hipError_t launch_prefill<bf16_t>(const bf16_t*, const bf16_t*, const b
                                            const bf16_t*, const bf16_t*, const bf16_t*,
                                            const float*, bf16_t*, float*, int64_t, int64_t,
                                            int64_t, int64_t, int64_t, int, int, int, bool, void*,
-                                           hipStream_t);
+                                           hipEvent_t, hipStream_t);
 template hipError_t launch_prefill<float>(const float*, const float*, const float*, const float*,
                                           const float*, const float*, const float*, float*, float*,
                                           int64_t, int64_t, int64_t, int64_t, int64_t, int, int,
-                                          int, bool, void*, hipStream_t);
+                                          int, bool, void*, hipEvent_t, hipStream_t);
 
 }  // namespace gdr

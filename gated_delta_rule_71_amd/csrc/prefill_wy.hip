@@ -22,7 +22,7 @@ size_t prefill_wy_workspace_bytes(int64_t nstate, int64_t T, int64_t DK, int64_t
 
 namespace {
 template <int DK>
-hipError_t launch_dk(WyArgs a, int64_t nstate, hipStream_t s) {
+hipError_t launch_dk(WyArgs a, int64_t nstate, hipEvent_t mark, hipStream_t s) {
   const int64_t nprep = nstate * a.nch;
   if (nprep > 0) {
     if (a.DV <= 128)
@@ -30,6 +30,10 @@ hipError_t launch_dk(WyArgs a, int64_t nstate, hipStream_t s) {
     else
       hipLaunchKernelGGL((wy_prep_kernel<DK, 256>), dim3((unsigned)nprep), dim3(256), 0, s, a);
     const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (mark != nullptr) {
+    const hipError_t e = hipEventRecord(mark, s);
     if (e != hipSuccess) return e;
   }
   if (a.DV % 32 == 0) {
@@ -44,7 +48,7 @@ hipError_t launch_dk(WyArgs a, int64_t nstate, hipStream_t s) {
 }  // namespace
 
 hipError_t prefill_wy_launch(const PrefillArgs<bf16_t>& p, int64_t nstate, int64_t DK,
-                             void* workspace, hipStream_t s) {
+                             void* workspace, hipEvent_t mark, hipStream_t s) {
   WyArgs a{};
   a.q = p.q;
   a.k = p.k;
@@ -72,9 +76,9 @@ hipError_t prefill_wy_launch(const PrefillArgs<bf16_t>& p, int64_t nstate, int64
   ws += align256(chunks * 64 * 64 * 2);
   a.G = reinterpret_cast<float*>(ws);
   switch (DK) {
-    case 32: return launch_dk<32>(a, nstate, s);
-    case 64: return launch_dk<64>(a, nstate, s);
-    default: return launch_dk<128>(a, nstate, s);
+    case 32: return launch_dk<32>(a, nstate, mark, s);
+    case 64: return launch_dk<64>(a, nstate, mark, s);
+    default: return launch_dk<128>(a, nstate, mark, s);
   }
 }
 

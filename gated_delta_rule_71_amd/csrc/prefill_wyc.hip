@@ -28,7 +28,7 @@ WycSizes wyc_sizes(int64_t nstate, int64_t T, int64_t DK, int64_t DV, bool two) 
 }
 
 template <int DK, int MODE>
-hipError_t launch_mode(WycArgs a, int64_t nstate, hipStream_t s) {
+hipError_t launch_mode(WycArgs a, int64_t nstate, hipEvent_t mark, hipStream_t s) {
   const int64_t nprep = nstate * a.nch;
   if (nprep > 0) {
     if (a.DV <= 128)
@@ -36,6 +36,10 @@ hipError_t launch_mode(WycArgs a, int64_t nstate, hipStream_t s) {
     else
       hipLaunchKernelGGL((wyc_prep_kernel<DK, 256, MODE>), dim3((unsigned)nprep), dim3(256), 0, s, a);
     const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (mark != nullptr) {
+    const hipError_t e = hipEventRecord(mark, s);
     if (e != hipSuccess) return e;
   }
   // 32-column slices when that still gives a workgroup per compute unit, else 16 columns
@@ -60,7 +64,7 @@ size_t prefill_wyc_workspace_bytes(int64_t nstate, int64_t T, int64_t DK, int64_
 }
 
 hipError_t prefill_wyc_launch(const PrefillArgs<bf16_t>& p, int64_t nstate, int64_t DK, bool two,
-                              void* workspace, hipStream_t s) {
+                              void* workspace, hipEvent_t mark, hipStream_t s) {
   WycArgs a{};
   a.q = p.q;
   a.k = p.k;
@@ -99,9 +103,9 @@ hipError_t prefill_wyc_launch(const PrefillArgs<bf16_t>& p, int64_t nstate, int6
   ws += z.Egn;
   a.flag = reinterpret_cast<int*>(ws);
   switch (DK) {
-    case 32: return two ? launch_mode<32, 2>(a, nstate, s) : launch_mode<32, 1>(a, nstate, s);
-    case 64: return two ? launch_mode<64, 2>(a, nstate, s) : launch_mode<64, 1>(a, nstate, s);
-    default: return two ? launch_mode<128, 2>(a, nstate, s) : launch_mode<128, 1>(a, nstate, s);
+    case 32: return two ? launch_mode<32, 2>(a, nstate, mark, s) : launch_mode<32, 1>(a, nstate, mark, s);
+    case 64: return two ? launch_mode<64, 2>(a, nstate, mark, s) : launch_mode<64, 1>(a, nstate, mark, s);
+    default: return two ? launch_mode<128, 2>(a, nstate, mark, s) : launch_mode<128, 1>(a, nstate, mark, s);
   }
 }
 

@@ -93,13 +93,23 @@ int gdr_abi_version(void);
 const char* gdr_status_string(int status);
 
 /* Workspace bytes gdr_chunk_fwd needs for `p` (0 when none); 0 also for an
- * invalid problem.  bf16 problems with a scalar (or no) decay and a scalar
- * (or no) erase gate run as a chunk-local kernel plus a per-state kernel that
- * exchange, per 64-token chunk of every (batch, head), W and U (64 x dk and
- * 64 x dv bf16), the masked 64 x 64 read-out matrix (bf16) and the 64 gate
- * prefix sums (fp32), each array 256-byte aligned: about
- * B * ceil(T/64) * H * (128 dk + 128 dv + 8448) bytes.  Other problems need
- * none.  The caller owns the buffer; its contents on entry do not matter. */
+ * invalid problem.  bf16 problems with dk in {32, 64, 128} run as a
+ * chunk-local kernel plus a per-state kernel that exchange per-chunk matrices
+ * through the workspace, each array 256-byte aligned; per 64-token chunk of
+ * every (batch, head) that is:
+ *   scalar (or no) decay, scalar (or no) erase gate: W and U (64 x dk and
+ *     64 x dv bf16), the masked 64 x 64 read-out matrix (bf16) and the 64 gate
+ *     prefix sums (fp32): 128 dk + 128 dv + 8448 bytes;
+ *   per-channel decay, decay applied before the erase: W, the decay-scaled
+ *     query, the decay-scaled erase keys (each 64 x dk bf16), the 64 x 64
+ *     read-out matrix, Y (dv x 64 bf16), the dk chunk decays (fp32) and a
+ *     flag: 388 dk + 128 dv + 8196 bytes;
+ *   per-channel decay, erase then decay: as above plus a second decay-scaled
+ *     key array (64 x dk), Z (64 x dv) and the written values (dv x 64):
+ *     516 dk + 384 dv + 8196 bytes.
+ * The scalar-decay form with a per-channel erase gate, the dk = 16 and the
+ * fp32 problems run as one kernel and need none.  The caller owns the buffer;
+ * its contents on entry do not matter. */
 size_t gdr_chunk_fwd_workspace_bytes(const gdr_problem* p);
 
 /*
@@ -124,6 +134,20 @@ size_t gdr_chunk_fwd_workspace_bytes(const gdr_problem* p);
 int gdr_chunk_fwd(const gdr_problem* p, const void* q, const void* k, const void* v,
                   const void* log_alpha, const void* b, const void* w, const float* S0,
                   void* o, float* S_T, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * gdr_chunk_fwd with a timing marker.  When `phase_event` (a hipEvent_t) is
+ * not NULL it is recorded on `stream` between the chunk-local kernel and the
+ * per-state kernel, or just before the one kernel of a problem that runs as
+ * one.  With events recorded before and after the call, the caller can time
+ * the two phases separately.  No event is recorded when the call fails
+ * validation or when B * H is 0.  Otherwise identical to gdr_chunk_fwd;
+ * GDR_ERR_HIP when the record fails.
+ */
+int gdr_chunk_fwd_marked(const gdr_problem* p, const void* q, const void* k, const void* v,
+                         const void* log_alpha, const void* b, const void* w, const float* S0,
+                         void* o, float* S_T, void* workspace, size_t workspace_bytes,
+                         void* stream, void* phase_event);
 
 /*
  * One decode step (p->seqlen must be 1): for every (batch, head) applies the

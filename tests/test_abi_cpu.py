@@ -108,6 +108,21 @@ def test_overlaps_rejected():
     assert call(prob(), **ptrs) == N.GDR_ERR_INVALID_ARGUMENT
 
 
+def test_marked_entry_validates_like_the_plain_one():
+    # the timing-marker variant shares every check; the (fake) event is never recorded here
+    ev = 1 << 40
+    cases = [(prob(), big_apart()), (prob(dk=96), big_apart()), (prob(batch=0), big_apart()),
+             (prob(), dict(big_apart(), q=0)), (prob(), dict(big_apart(), o=big_apart()["v"] + 64))]
+    for p, ptrs in cases:
+        a = dict(q=A, k=A * 2, v=A * 3, la=A * 4, b=A * 5, w=A * 6, S0=A * 7, o=A * 8, S_T=A * 9)
+        a.update(ptrs)
+        plain = call(p, **ptrs)
+        marked = N.chunk_fwd_marked_raw(p, a["q"], a["k"], a["v"], a["la"], a["b"], a["w"],
+                                        a["S0"], a["o"], a["S_T"], 0, 0, 0, ev)
+        assert marked == plain
+    assert plain == N.GDR_ERR_INVALID_ARGUMENT
+
+
 def test_empty_problem_is_a_no_op():
     # nothing to do: returns OK without touching the (fake) pointers or the GPU
     assert call(prob(batch=0), **big_apart()) == N.GDR_OK

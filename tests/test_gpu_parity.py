@@ -231,3 +231,31 @@ def test_channel_workloads_sampled(dev, name):
     eo, es = errors(o_sel, S_sel, o_ref, S_ref)
     say("%s sampled: max|do|=%.3e rel|dS|=%.3e" % (name, eo, es))
     assert eo <= TOL["bf16"][0] and es <= TOL["bf16"][1]
+
+
+# ------------------------------------------------------------------ the timing-marker entry point
+
+
+@pytest.mark.parametrize("kind,dtype", [("gdn", "bf16"), ("gdn2", "bf16"), ("kda", "fp32")])
+def test_marked_call_matches_plain_call(dev, kind, dtype):
+    """gdr_chunk_fwd_marked runs the same kernels as gdr_chunk_fwd (identical bits) and records
+    its event between the start and the end of the call."""
+    import gated_delta_rule_71_amd as gdr
+    from gpu_util import to_dev
+    wl = case(kind, T=200, D=64 if dtype == "bf16" else 32, dtype=dtype)
+    say("marked", kind, dtype, wl)
+    g = to_dev(synth.make_prefill(wl), dev)
+    args = (g["q"], g["k"], g["v"], g["log_alpha"], g["b"], g["w"], g["S0"])
+    o1, S1 = gdr.chunk_fwd(*args)
+    stream = torch.cuda.current_stream(dev)
+    e0, em, e1 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    e0.record(stream)
+    o2, S2 = gdr.chunk_fwd(*args, phase_event=em)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+    t_a, t_b = e0.elapsed_time(em), em.elapsed_time(e1)
+    say("phases: %.4f ms + %.4f ms" % (t_a, t_b))
+    assert t_a >= 0.0 and t_b > 0.0
+    x = synth.make_prefill(wl)
+    check(x, o2, S2, "erase_then_decay", TOL[dtype], "marked %s %s" % (kind, dtype))
