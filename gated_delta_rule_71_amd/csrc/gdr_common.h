@@ -62,4 +62,12 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Workgroup barrier that waits only for this wave's LDS instructions: direct-to-LDS loads it
+// has in flight stay in flight (the fence of lds_barrier would drain them).  Whoever consumes
+// such loads waits for them (s_waitcnt vmcnt) before an earlier barrier.  The memory clobber
+// keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier_keep_vm() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 }  // namespace gdr

@@ -52,6 +52,9 @@
 namespace gdr {
 
 constexpr int kLdsLimit = 163840;  // bytes of LDS one gfx950 workgroup may use
+// s_waitcnt immediate that waits for vmcnt = 0 only (gfx9 encoding: vmcnt in bits 3:0 and
+// 15:14, expcnt in bits 6:4, lgkmcnt in bits 11:8; the last two left at their maxima)
+constexpr int kWaitVmcnt0 = 0x0F70;
 
 template <typename OT, int DK, int NSW, int MODE>
 struct PrefillLayout {
@@ -128,6 +131,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 }
 __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ void buf_store16(__amdgpu_buffer_rsrc_t r, uint32_t off, uint4 v) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, 0);
 }
 // Raw 16-bit load; converted to fp32 only where the value is used, so that issuing the load
 // does not wait for it.

@@ -12,8 +12,9 @@
 // R stacks the erase reads r_t (the negated "new values" of the delta rule).  The pairwise mask
 // e^{G_t - G_i} <= 1 makes every factor safe for any gate values.
 //
-// The chunk-local kernel writes W and U (bf16), -M (bf16) and G (fp32) to a workspace; the
-// state kernel streams them back, so the serial chain per chunk holds only S-dependent MFMAs.
+// The chunk-local kernel writes W, U and -M (bf16) and e^{G_t}, e^{G_n - G_t}, e^{G_n} (fp32) to
+// a workspace; the state kernel copies them, with the q and k rows, into LDS by direct-to-LDS
+// loads, so its serial chain per chunk holds only S-dependent MFMAs.
 #pragma once
 #include "gdr_common.h"
 #include "mfma.h"
@@ -43,11 +44,13 @@ struct WyArgs {
   __bf16* W;  // [B*H][nch][64][dk]
   __bf16* U;  // [B*H][nch][64][dv]
   __bf16* M;  // [B*H][nch][64][64], holds -M (zero above the diagonal)
-  float* G;   // [B*H][nch][64]
+  float* E;   // [B*H][nch][kWyE]: e^{G_t} and e^{G_n - G_t} for the 64 tokens, e^{G_n}, 3 zeros
   int64_t T, H, DV, nch;
   int alpha_kind, b_kind, w_kind;
   int nsl;  // value slices per state (state kernel)
 };
+
+constexpr int kWyE = 132;  // floats per chunk in WyArgs::E (33 pieces of 16 bytes)
 
 // Byte range of `width`-element rows from a chunk's first token to the last token of its state.
 __device__ __forceinline__ uint32_t wy_range(int64_t left, int64_t H, int64_t width) {
@@ -104,15 +107,15 @@ struct WyPrepLayout {
   static constexpr int oM = oA + 48 * LDA * 2;
   static constexpr int oI = oM + C * LDD * 2;
   static constexpr int oLD = oI + 4 * 16 * LDI * 2;
-  static constexpr int oS = oLD + 4 * 16 * LDL * 4;  // fp32: G, e^G, -, beta (64 each)
+  static constexpr int oS = oLD + 4 * 16 * LDL * 4;  // fp32: G, e^G, e^{G_n - G}, beta (64 each)
   static constexpr int total = oS + 4 * C * 4;
   static constexpr bool fits = total <= kLdsLimit;
 };
 
 // One workgroup per (state, chunk).  Phases (barriers between): inputs into LDS and gate prefix
 // sums; Gram tiles (waves 0-1: A, waves 2-3: M); diagonal inverses (waves 0-1) while waves 2-3
-// write -M out; blocked forward substitution for the 16-column tiles of W and U, each wave
-// owning whole column tiles (R_i = T_ii (B_i - sum_{m<i} A_im R_m), B the scaled k or x tile).
+// write -M out; T = (I + A)^{-1} by blocked forward substitution on the identity; W = T B_k and
+// U = T X, each wave owning whole 16-column tiles (B_k the k tile scaled by beta_t e^{G_t}).
 template <int DK, int DVP>
 __global__ __launch_bounds__(256) void wy_prep_kernel(WyArgs a) {
   using L = WyPrepLayout<DK, DVP>;
@@ -225,10 +228,15 @@ __global__ __launch_bounds__(256) void wy_prep_kernel(WyArgs a) {
       const float y = __shfl_up(x, off);
       if (lane >= off) x += y;
     }
+    const float gn = __shfl(x, 63);
+    const float ex = __expf(x);
     sc[lane] = x;
-    sc[C + lane] = __expf(x);
+    sc[C + lane] = ex;
+    sc[2 * C + lane] = __expf(gn - x);
     sc[3 * C + lane] = bf16_to_f32(bev);
-    a.G[cix * C + lane] = x;
+    a.E[cix * kWyE + lane] = ex;
+    a.E[cix * kWyE + C + lane] = sc[2 * C + lane];
+    if (lane < kWyE - 2 * C) a.E[cix * kWyE + 2 * C + lane] = lane == 0 ? __expf(gn) : 0.f;
   }
   GDR_PMARK(0);
   lds_barrier();
@@ -377,50 +385,124 @@ __global__ __launch_bounds__(256) void wy_prep_kernel(WyArgs a) {
 
 // ------------------------------------------------------------------ state kernel
 
-template <int DK, int NCT>
+// One 16-byte direct-to-LDS load per lane: lane L's piece lands at lds + 16 L (the LDS address
+// must be the same for the whole wave); pieces outside the buffer range arrive as zeros.
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, unsigned char* lds, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, off,
+                                           0, 0, 0);
+}
+
+// Row-major bf16 arrays of NCHR 16-byte pieces per row live in LDS without padding, the pieces
+// of each row permuted by XOR with a key of the row.  A fragment read touches 16 rows at once:
+// either 16 consecutive rows (NAT: row bits 0-3 vary) or the rows of perm_row below (PERM: bits
+// 0, 1, 3 and 4 vary); the key takes those bits so that the 16 pieces read land in 16 distinct
+// bank groups (rows of 256, 128 or 64 bytes).
+template <int NCHR, bool PERM>
+__device__ __forceinline__ int swz_key(int row) {
+  if constexpr (NCHR == 16) return PERM ? ((row & 3) | ((row >> 1) & 12)) : (row & 15);
+  else if constexpr (NCHR == 8) return PERM ? (((row >> 1) & 1) | ((row >> 2) & 6)) : ((row >> 1) & 7);
+  else if constexpr (NCHR == 4) return PERM ? ((row >> 3) & 3) : ((row >> 2) & 3);
+  else return PERM ? ((row >> 3) & 1) : ((row >> 3) & 1);
+}
+
+// Row m of 16-row tile `tile` when the tile's accumulator rows 4 g + i are to hold rows whose
+// pair-fragment k slots (tiles 2 kb and 2 kb + 1, rows 4 g + i) are the 8 consecutive rows
+// 32 kb + 8 g .. 32 kb + 8 g + 7: one 16-byte read then gives a lane its whole fragment.
+__device__ __forceinline__ int perm_row(int tile, int m) {
+  return 32 * (tile >> 1) + 4 * (tile & 1) + 8 * (m >> 2) + (m & 3);
+}
+
+// A row-major global array (row stride `stride` bytes) is copied into that form 64 pieces per
+// instruction: LDS piece s holds piece (s mod NCHR) ^ key of row s / NCHR.  dma_offsets gives a
+// lane's source offsets (the same for every chunk, so they are computed once); dma_rows issues
+// the copies.
+template <int NCHR, bool PERM, int NPIECE>
+__device__ __forceinline__ void dma_offsets(uint32_t stride, int lane, uint32_t* off) {
+  static_assert(NPIECE % 64 == 0, "whole instructions only");
+#pragma unroll
+  for (int i = 0; i < NPIECE / 64; ++i) {
+    const int s = 64 * i + lane, row = s / NCHR, piece = (s % NCHR) ^ swz_key<NCHR, PERM>(row);
+    off[i] = static_cast<uint32_t>(row) * stride + static_cast<uint32_t>(piece) * 16u;
+  }
+}
+template <int NPIECE>
+__device__ __forceinline__ void dma_rows(__amdgpu_buffer_rsrc_t r, unsigned char* lds, const uint32_t* off) {
+#pragma unroll
+  for (int i = 0; i < NPIECE / 64; ++i) lds_dma16(r, lds + 1024 * i, off[i]);
+}
+
+// Byte address of piece `piece` of row `row` of such an array.
+template <int NCHR, bool PERM>
+__device__ __forceinline__ const unsigned char* swz_addr(const unsigned char* base, int row, int piece) {
+  return base + row * NCHR * 16 + ((piece ^ swz_key<NCHR, PERM>(row)) << 4);
+}
+
+// Transposing 8-byte LDS read (gfx950): within each group of 16 lanes, lane 4 a + b receives
+// element b of the 8-byte vectors that lanes a, a + 4, a + 8 and a + 12 of the group point at.
+__device__ __forceinline__ bf16x4 lds_read_tr4(const unsigned char* p) {
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16*)(const_cast<unsigned char*>(p)));
+  return __builtin_bit_cast(bf16x4, r);
+}
+
+// The 16-byte piece `piece` of row `row` of such an array.
+template <int NCHR, bool PERM>
+__device__ __forceinline__ Mma<__bf16>::F8 lds_piece(const unsigned char* base, int row, int piece) {
+  return *reinterpret_cast<const Mma<__bf16>::F8*>(base + row * NCHR * 16 +
+                                                   ((piece ^ swz_key<NCHR, PERM>(row)) << 4));
+}
+
+template <int DK, int DVS>
 struct WyStateLayout {
   static constexpr int C = 64;
-  static constexpr int DVS = 16 * NCT;
-  static constexpr int LDT = DK + 8;  // q and W rows
-  static constexpr int LDD = C + 8;   // k^T rows, -M rows, U^T rows
-  static constexpr int oQ = 0;
-  static constexpr int oW = oQ + C * LDT * 2;
-  static constexpr int oKT = oW + C * LDT * 2;
-  static constexpr int oM = oKT + DK * LDD * 2;
-  static constexpr int oU = oM + C * LDD * 2;
-  static constexpr int oS = oU + DVS * LDD * 2;  // fp32: e^{G_t}, e^{G_n - G_t} (64 each), e^{G_n}
-  static constexpr int BUF = oS + (2 * C + 4) * 4;
-  static constexpr int total = 2 * BUF;
+  static constexpr int NCQ = DK / 8;  // 16-byte pieces per q / W row
+  static constexpr int NCC = C / 8;   // pieces per row of the token-minor arrays
+  static constexpr int NCU = DVS / 8;  // pieces per row of the U slice
+  static constexpr int NBUF = 2;              // chunk buffers
+  static constexpr int oQ = 0;                // q rows [64][dk]
+  static constexpr int oW = oQ + C * DK * 2;  // W rows [64][dk]
+  static constexpr int oK = oW + C * DK * 2;  // k rows [64][dk]
+  static constexpr int oM = oK + C * DK * 2;  // -M rows [64][64]
+  static constexpr int oU = oM + C * C * 2;   // U rows of the slice [64][DVS]
+  static constexpr int oE = oU + C * DVS * 2; // e^{G_t}, e^{G_n - G_t} (64 each), e^{G_n}: fp32
+  static constexpr int BUF = oE + 1024;
+  static constexpr int LDO = DVS + 8;         // O rows (16-byte aligned)
+  static constexpr int oO = NBUF * BUF;       // two O buffers [64][LDO]
+  static constexpr int total = oO + 2 * C * LDO * 2;
   static constexpr bool fits = total <= kLdsLimit;
 };
 
-// Workgroup = 2 loader waves and one state wave, for one state and a slice of DVS = 16 NCT value
-// columns; the state wave holds that slice of S in its accumulators as NCT column tiles, so every
-// A fragment read from LDS feeds NCT products.  Per chunk c (one barrier): the loaders write chunk
-// c+1 into one LDS buffer from registers and issue the loads of chunk c+2, while the state wave
-// consumes chunk c from the other buffer:
-//     O = diag(e^{G_t}) Q S,  V = W S,  R = V - U,
-//     S <- e^{G_n} S - K^T diag(e^{G_n - G_t}) R,  O -= M R,  O out.
-template <int DK, int NCT>
-__global__ __launch_bounds__(192) void wy_state_kernel(WyArgs a) {
-  using L = WyStateLayout<DK, NCT>;
+// Workgroup = 2 loader waves and NSW state waves for one state and a slice of DVS = 16 NCT NSW
+// value columns; state wave j holds columns 16 NCT j .. 16 NCT (j + 1) - 1 of the slice in its
+// accumulators as NCT column tiles.  Chunk c's operands sit in LDS buffer c mod 2, filled by
+// direct-to-LDS loads that loader wave c mod 2 issues a whole chunk ahead, so the loads never
+// stall the chain and no loader registers hold data.  Two barriers per chunk c:
+//   up to A: the state waves read every operand of chunk c into registers;
+//   A to B:  the state waves compute
+//              V = W S,  R = V - U,  S <- e^{G_n} S - K^T diag(e^{G_n - G_t}) R,
+//              O = diag(e^{G_t}) Q S - M R
+//            and leave O in an LDS buffer; loader wave c mod 2 refills buffer c mod 2 with
+//            chunk c+2, and the other loader wave copies the O rows of chunk c-1 to HBM and
+//            waits for its loads of chunk c+1.
+template <int DK, int NCT, int NSW>
+__global__ __launch_bounds__(64 * (2 + NSW)) void wy_state_kernel(WyArgs a) {
+  constexpr int DVS = 16 * NCT * NSW;
+  using L = WyStateLayout<DK, DVS>;
   using MM = Mma<__bf16>;
   using F8 = MM::F8;
   static_assert(L::fits, "LDS layout exceeds the gfx950 workgroup limit");
   static_assert(DK % 32 == 0, "dk must be a multiple of 32");
-  constexpr int C = L::C, DVS = L::DVS, LDT = L::LDT, LDD = L::LDD;
+  constexpr int C = L::C, NCQ = L::NCQ, NCC = L::NCC;
   constexpr int NTD = DK / 16, NKB = DK / 32;
-  constexpr int NLT = 128;  // loader threads (waves 0 and 1)
-  constexpr int NCG = DK / 8, IPT = C * NCG / NLT;
-  constexpr int NXG = DVS / 8, XPT = (C * NXG + NLT - 1) / NLT;
-  constexpr int MPT = C * C / 8 / NLT;  // 16-byte items of -M per loader thread
 
-  __shared__ __attribute__((aligned(32))) unsigned char smem[L::total];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[L::total];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   int lane = tid & 63, g = lane >> 4, l16 = lane & 15;
   const bool loader = wave < 2;
+  const int cb = loader ? 0 : 16 * NCT * (wave - 2);  // this state wave's first column in the slice
 
   const int64_t nb = gridDim.x, bid = blockIdx.x;
   const int64_t p = (nb % 8 == 0) ? (bid % 8) * (nb / 8) + bid / 8 : bid;
@@ -432,105 +514,54 @@ __global__ __launch_bounds__(192) void wy_state_kernel(WyArgs a) {
   const uint32_t hdk = static_cast<uint32_t>(H * DK * 2), hdv = static_cast<uint32_t>(H * DV * 2);
 
   auto buf = [&](int64_t c) -> unsigned char* { return smem + (c & 1) * L::BUF; };
+  auto obuf = [&](int64_t c) -> __bf16* {
+    return reinterpret_cast<__bf16*>(smem + L::oO + (c & 1) * C * L::LDO * 2);
+  };
 
-  // ---------------- loader registers ----------------
-  uint4 pq[IPT], pk[IPT], pw[IPT], pm[MPT], pu[XPT];
-  float pg = 0.f;
-  auto prefetch = [&](int64_t c) {
+  // ---------------- loader waves ----------------
+  // per-lane source offsets of the copies, computed once
+  constexpr int NQI = C * NCQ / 64, NMI = C * NCC / 64, NUI = C * L::NCU / 64;
+  uint32_t offQ[NQI], offW[NQI], offK[NQI], offM[NMI], offU[NUI];
+  {
+    const int dl = tid & 63;
+    dma_offsets<NCQ, false, C * NCQ>(hdk, dl, offQ);
+    dma_offsets<NCQ, true, C * NCQ>(DK * 2, dl, offW);
+    dma_offsets<NCQ, true, C * NCQ>(hdk, dl, offK);
+    dma_offsets<NCC, false, C * NCC>(C * 2, dl, offM);
+    dma_offsets<L::NCU, true, C * L::NCU>(static_cast<uint32_t>(DV * 2), dl, offU);
+  }
+  // chunk c's operands into buffer c mod 2 (q and k rows past the last token arrive as zeros)
+  auto dma_chunk = [&](int64_t c) {
+    unsigned char* B = buf(c);
+    const int64_t t0 = c * C, rr = (bi * T + t0) * H + hi, cix = bh * nch + c;
+    dma_rows<C * NCQ>(make_rsrc(a.q + rr * DK, wy_range(T - t0, H, DK)), B + L::oQ, offQ);
+    dma_rows<C * NCQ>(make_rsrc(a.W + cix * C * DK, C * DK * 2), B + L::oW, offW);
+    dma_rows<C * NCQ>(make_rsrc(a.k + rr * DK, wy_range(T - t0, H, DK)), B + L::oK, offK);
+    dma_rows<C * NCC>(make_rsrc(a.M + cix * C * C, C * C * 2), B + L::oM, offM);
+    dma_rows<C * L::NCU>(make_rsrc(a.U + cix * C * DV + col0, static_cast<uint32_t>((C * DV - col0) * 2)),
+                         B + L::oU, offU);
+    if (lane < kWyE / 4) lds_dma16(make_rsrc(a.E + cix * kWyE, kWyE * 4), B + L::oE, lane * 16);
+  };
+  // O rows of chunk c from its LDS buffer to HBM, 16 bytes per store; rows past the last token
+  // are dropped by the range
+  auto store_o = [&](int64_t c) {
+    constexpr int NOG = DVS / 8, OPT = C * NOG / 64;
+    const __bf16* oO = obuf(c);
     const int64_t t0 = c * C;
     const int64_t rr = (bi * T + t0) * H + hi;
-    const int64_t cix = bh * nch + c;
-    const auto rq = make_rsrc(a.q + rr * DK, wy_range(T - t0, H, DK));
-    const auto rk = make_rsrc(a.k + rr * DK, wy_range(T - t0, H, DK));
-    const auto rw = make_rsrc(a.W + cix * C * DK, C * DK * 2);
-    const auto rm = make_rsrc(a.M + cix * C * C, C * C * 2);
-    const auto ru = make_rsrc(a.U + cix * C * DV + col0, static_cast<uint32_t>((C * DV - col0) * 2));
+    const int64_t bytes = ((T - t0 - 1) * H + 1) * DV * 2 - col0 * 2;
+    const auto ro = make_rsrc(a.o + rr * DV + col0, static_cast<uint32_t>(bytes < 0x7fffffff ? bytes : 0x7fffffff));
 #pragma unroll
-    for (int j = 0; j < IPT; ++j) {
-      const uint32_t t = (tid / NCG) * IPT + j, cg = tid % NCG;
-      pq[j] = buf_load16(rq, t * hdk + cg * 16);
-      pk[j] = buf_load16(rk, t * hdk + cg * 16);
-      pw[j] = buf_load16(rw, (t * DK + cg * 8) * 2);
-    }
-#pragma unroll
-    for (int j = 0; j < MPT; ++j) pm[j] = buf_load16(rm, (tid + NLT * j) * 16);
-#pragma unroll
-    for (int j = 0; j < XPT; ++j) {
-      const int item = tid + NLT * j;
-      const uint32_t t = item / NXG, xg = item % NXG;
-      pu[j] = buf_load16(ru, item < C * NXG ? (t * DV + xg * 8) * 2 : 0x80000000u);
-    }
-    if (wave == 0) {
-      const auto rg = make_rsrc(a.G + cix * C, C * 4);
-      pg = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, lane * 4, 0, 0));
+    for (int j = 0; j < OPT; ++j) {
+      const int item = lane + 64 * j, t = item / NOG, part = item % NOG;
+      buf_store16(ro, t * hdv + part * 16, *reinterpret_cast<const uint4*>(oO + t * L::LDO + part * 8));
     }
   };
 
-  auto store = [&](int64_t c) {
-    unsigned char* B = buf(c);
-    __bf16* tQ = reinterpret_cast<__bf16*>(B + L::oQ);
-    __bf16* tW = reinterpret_cast<__bf16*>(B + L::oW);
-    __bf16* kT = reinterpret_cast<__bf16*>(B + L::oKT);
-    __bf16* gM = reinterpret_cast<__bf16*>(B + L::oM);
-    __bf16* uT = reinterpret_cast<__bf16*>(B + L::oU);
-    float* sc = reinterpret_cast<float*>(B + L::oS);
-    const int cg = tid % NCG, tb = (tid / NCG) * IPT;
-    uint16_t kh[8][IPT];
-#pragma unroll
-    for (int j = 0; j < IPT; ++j) {
-      *reinterpret_cast<uint4*>(tQ + (tb + j) * LDT + cg * 8) = pq[j];
-      *reinterpret_cast<uint4*>(tW + (tb + j) * LDT + cg * 8) = pw[j];
-      const uint32_t w4[4] = {pk[j].x, pk[j].y, pk[j].z, pk[j].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        kh[2 * e][j] = static_cast<uint16_t>(w4[e] & 0xffffu);
-        kh[2 * e + 1][j] = static_cast<uint16_t>(w4[e] >> 16);
-      }
-    }
-    uint16_t* kTu = reinterpret_cast<uint16_t*>(kT);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int row = cg * 8 + e;
-      if constexpr (IPT >= 4) {
-#pragma unroll
-        for (int q4 = 0; q4 < IPT / 4; ++q4)
-          *reinterpret_cast<uint2*>(kTu + row * LDD + swz((row >> 3) & 15, tb + 4 * q4)) =
-              make_uint2(kh[e][4 * q4] | (uint32_t(kh[e][4 * q4 + 1]) << 16),
-                         kh[e][4 * q4 + 2] | (uint32_t(kh[e][4 * q4 + 3]) << 16));
-      } else {
-        *reinterpret_cast<uint32_t*>(kTu + row * LDD + swz((row >> 3) & 15, tb)) =
-            kh[e][0] | (uint32_t(kh[e][1]) << 16);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < MPT; ++j) {
-      const int item = tid + NLT * j, r = item >> 3, part = item & 7;
-      *reinterpret_cast<uint4*>(gM + r * LDD + part * 8) = pm[j];
-    }
-#pragma unroll
-    for (int j = 0; j < XPT; ++j) {
-      const int item = tid + NLT * j;
-      if (item < C * NXG) {
-        const int t = item / NXG, xg = item % NXG;
-        const uint32_t w4[4] = {pu[j].x, pu[j].y, pu[j].z, pu[j].w};
-        uint16_t* uTu = reinterpret_cast<uint16_t*>(uT);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          uTu[(xg * 8 + 2 * e) * LDD + swz(2 * xg, t)] = static_cast<uint16_t>(w4[e] & 0xffffu);
-          uTu[(xg * 8 + 2 * e + 1) * LDD + swz(2 * xg, t)] = static_cast<uint16_t>(w4[e] >> 16);
-        }
-      }
-    }
-    if (wave == 0) {
-      const float gn = __shfl(pg, 63);
-      sc[lane] = __expf(pg);
-      sc[C + lane] = __expf(gn - pg);
-      if (lane == 0) sc[2 * C] = __expf(gn);
-    }
-  };
-
-  // ---------------- chain and output waves ----------------
-  // S[ct][tl]: column tile ct (local columns 16 ct + l16), rows 16 tl + 4 g + i
+  // ---------------- state waves ----------------
+  // S[ct][tl]: column tile ct (slice columns cb + 16 ct + l16); accumulator row 4 g + i holds
+  // channel perm_row(tl, 4 g + i), so that the pair fragment of tiles 2 kb, 2 kb + 1 carries
+  // channels 32 kb + 8 g .. 32 kb + 8 g + 7 (one 16-byte piece of a q or W row)
   f32x4 S[NCT][NTD];
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct)
@@ -538,113 +569,112 @@ __global__ __launch_bounds__(192) void wy_state_kernel(WyArgs a) {
     for (int tl = 0; tl < NTD; ++tl) {
       S[ct][tl] = zero4();
       if (!loader && a.S0 != nullptr) {
-        const int64_t sb = bh * DK * DV + col0 + 16 * ct + l16;
+        const int64_t sb = bh * DK * DV + col0 + cb + 16 * ct + l16;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) S[ct][tl][i] = a.S0[sb + (int64_t)(16 * tl + 4 * g + i) * DV];
+        for (int i = 0; i < 4; ++i) S[ct][tl][i] = a.S0[sb + (int64_t)perm_row(tl, 4 * g + i) * DV];
       }
     }
+  // Complete the initial-state loads here, on every path, so that the chunk loop never waits
+  // on vector memory for the accumulators.
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
-  // S <- e^{G_n} S + K^T rs   (rs = -R e^{G_n - G_t} as two tile-pair fragments per column tile)
-  auto state_update = [&](const unsigned char* B, const F8 (*rs)[2]) {
-    const __bf16* kT = reinterpret_cast<const __bf16*>(B + L::oKT);
-    const float egn = reinterpret_cast<const float*>(B + L::oS)[2 * C];
-    F8 kf[4][2];  // ring: tiles tl+1..tl+3 are in flight while tile tl multiplies
-    auto load_kt = [&](int tl, F8* o) {
-      const int row = 16 * tl + l16, key = (row >> 3) & 15;
-      const __bf16* kr = kT + row * LDD;
+  // operands, one set for the S chain and one for the read-out:
+  //   aw: W rows perm_row(ta, l16) (V tile ta's accumulator row 4 g + i is then token
+  //       perm_row(ta, 4 g + i), and R's pair fragments carry tokens 32 kb + 8 g ..), channels
+  //       32 kb + 8 g ..;  aq: q rows 16 ta + l16, channels 32 kb + 8 g ..;  mf: -M rows
+  //       16 ta + l16, tokens 32 kb + 8 g ..  (one 16-byte read each)
+  //   kf: K^T as A fragments, rows = channels perm_row(tl, l16) (S's channel order), tokens
+  //       32 kb + 8 g .., by two transposing reads of the k rows: source lane (a, m) = (l16 & 3,
+  //       l16 >> 2) of group g points at token 32 kb + 8 g + 4 h + m, channels
+  //       perm_row(tl, 4 a) ..;  uv: U at the tokens of V tile ta, this lane's column, the same way
+  //   eg: e^{G_t} of this lane's O rows;  dd: e^{G_n - G_t} at V tile ta's tokens;  egn: e^{G_n}
+  F8 aw[NKB][4], aq[NKB][4], kf[2][NTD], mf[6];
+  bf16x4 uv[NCT][4];
+  float eg[4], egn = 0.f;
+  float4 dd[4];
+  auto read_chain = [&](int64_t c) {
+    const unsigned char* B = buf(c);
+    const int ta_ = l16 & 3, m_ = l16 >> 2;  // this lane's role as a transposing-read source
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x4 lo = lds_load4(kr + swz(key, 32 * kb + 4 * g));
-        const bf16x4 hi = lds_load4(kr + swz(key, 32 * kb + 16 + 4 * g));
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          o[kb][e] = lo[e];
-          o[kb][4 + e] = hi[e];
-        }
-      }
-    };
-#pragma unroll
-    for (int tl = 0; tl < 3 && tl < NTD; ++tl) load_kt(tl, kf[tl]);
-#pragma unroll
-    for (int tl = 0; tl < NTD; ++tl) {
-      if (tl + 3 < NTD) load_kt(tl + 3, kf[(tl + 3) & 3]);
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) S[ct][tl][i] *= egn;
-        S[ct][tl] = MM::mma8(kf[tl & 3][0], rs[ct][0], S[ct][tl]);
-        S[ct][tl] = MM::mma8(kf[tl & 3][1], rs[ct][1], S[ct][tl]);
-      }
-    }
-  };
-
-  // D[ct] = A S[ct] for A (64 x dk, row-major in LDS) as four 16-row tiles; all A fragments are
-  // read first, and each feeds the NCT column tiles
-  // Ot[ct][ta] = (Q S[ct])^T tiles (S as the A operand, the same fragments as B, so a lane holds
-  // four consecutive columns of one row of Q S) and V[ct][ta] = W S[ct] tiles, as one stream of
-  // eight 16-row tiles (Q then W) with three tiles in flight ahead of the one multiplying
-  auto qs_ws = [&](const __bf16* tQ, const __bf16* tW, f32x4 (*Ot)[4], f32x4 (*V)[4]) {
-    F8 sf[NCT][NKB];
+      for (int ta = 0; ta < 4; ++ta) aw[kb][ta] = lds_piece<NCQ, true>(B + L::oW, perm_row(ta, l16), 4 * kb + g);
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
+      const int col = cb + 16 * ct + 4 * ta_;
+#pragma unroll
+      for (int ta = 0; ta < 4; ++ta)
+        uv[ct][ta] = lds_read_tr4(swz_addr<L::NCU, true>(B + L::oU, perm_row(ta, 4 * g + m_), col >> 3) + 8 * ((col >> 2) & 1));
+    }
+    const float* E = reinterpret_cast<const float*>(B + L::oE);
+#pragma unroll
+    for (int ta = 0; ta < 4; ++ta) dd[ta] = *reinterpret_cast<const float4*>(E + C + perm_row(ta, 4 * g));
+    egn = E[2 * C];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int tl = 0; tl < NTD; ++tl) {
+        const int piece = 4 * (tl >> 1) + ta_;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int row = 32 * kb + 8 * g + 4 * h + m_;
+          const bf16x4 v = lds_read_tr4(swz_addr<NCQ, true>(B + L::oK, row, piece) + 8 * (tl & 1));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) kf[kb][tl][4 * h + e] = v[e];
+        }
+      }
+  };
+  auto read_out = [&](int64_t c) {
+    const unsigned char* B = buf(c);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int ta = 0; ta < 4; ++ta) aq[kb][ta] = lds_piece<NCQ, false>(B + L::oQ, 16 * ta + l16, 4 * kb + g);
+#pragma unroll
+    for (int ta = 0, n = 0; ta < 4; ++ta) {
+      mf[n++] = lds_piece<NCC, false>(B + L::oM, 16 * ta + l16, g);
+      if (ta >= 2) mf[n++] = lds_piece<NCC, false>(B + L::oM, 16 * ta + l16, 4 + g);
+    }
+    const float* E = reinterpret_cast<const float*>(B + L::oE);
+#pragma unroll
+    for (int ta = 0; ta < 4; ++ta) eg[ta] = E[16 * ta + l16];
+  };
+
+  // each product runs k-step by k-step across its independent output tiles, so consecutive
+  // MFMAs never wait on each other; the chain that carries S (V, R, the update) comes first
+  F8 sf[NCT][NKB];  // S of the chunk start as bf16 operand fragments
+  F8 rf[NCT][2];    // R (tokens as k)
+  auto chain = [&](int64_t c) {
+    [[maybe_unused]] const int64_t ch = c;  // for the phase markers
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) sf[ct][kb] = acc_pair_frag<__bf16>(S[ct][2 * kb], S[ct][2 * kb + 1]);
+    // V = W S
+    f32x4 V[NCT][4];
 #pragma unroll
-      for (int ta = 0; ta < 4; ++ta) {
-        Ot[ct][ta] = zero4();
-        V[ct][ta] = zero4();
-      }
-    }
-    F8 af[4][NKB];
-    auto load_a = [&](int j, F8* o) {
-      const __bf16* rows = (j < 4 ? tQ : tW) + (16 * (j & 3) + l16) * LDT;
+    for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) o[kb] = lds_pair_frag_k<DK>(rows, 32 * kb, g);
-    };
+      for (int ta = 0; ta < 4; ++ta) V[ct][ta] = zero4();
 #pragma unroll
-    for (int j = 0; j < 3; ++j) load_a(j, af[j]);
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (j + 3 < 8) load_a(j + 3, af[(j + 3) & 3]);
-      const int ta = j & 3;
+      for (int ta = 0; ta < 4; ++ta)
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-          if (j < 4)
-            Ot[ct][ta] = MM::mma8(sf[ct][kb], af[j & 3][kb], Ot[ct][ta]);
-          else
-            V[ct][ta] = MM::mma8(af[j & 3][kb], sf[ct][kb], V[ct][ta]);
-        }
-    }
-  };
-
-  auto state_chunk = [&](int64_t c) {
-    [[maybe_unused]] const int64_t ch = c;  // for the phase markers
-    const unsigned char* B = buf(c);
-    const __bf16* uT = reinterpret_cast<const __bf16*>(B + L::oU);
-    const __bf16* gM = reinterpret_cast<const __bf16*>(B + L::oM);
-    const float* sc = reinterpret_cast<const float*>(B + L::oS);
-    // O^T tiles: Ot[ct][ta] lane (g, l16) holds O[16 ta + l16][16 ct + 4 g + i]
-    f32x4 Ot[NCT][4], V[NCT][4];
-    qs_ws(reinterpret_cast<const __bf16*>(B + L::oQ), reinterpret_cast<const __bf16*>(B + L::oW), Ot, V);
+        for (int ct = 0; ct < NCT; ++ct) V[ct][ta] = MM::mma8(aw[kb][ta], sf[ct][kb], V[ct][ta]);
     GDR_MARK(3);
-    F8 rf[NCT][2], rs[NCT][2];
+    // R = V - U (read-out operand) and -R e^{G_n - G_t} (state-update operand), tokens as k
+    F8 rs[NCT][2];
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
-      const int n = 16 * ct + l16;
       f32x4 R[4], Rs[4];
 #pragma unroll
       for (int ta = 0; ta < 4; ++ta) {
-        const bf16x4 u4 = *reinterpret_cast<const bf16x4*>(uT + n * LDD + swz(2 * (n >> 3), 16 * ta + 4 * g));
-        const float4 d4 = *reinterpret_cast<const float4*>(sc + C + 16 * ta + 4 * g);
-        const float d[4] = {d4.x, d4.y, d4.z, d4.w};
-        const float e = sc[16 * ta + l16];
+        const float d[4] = {dd[ta].x, dd[ta].y, dd[ta].z, dd[ta].w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          R[ta][i] = V[ct][ta][i] - static_cast<float>(u4[i]);
+          R[ta][i] = V[ct][ta][i] - static_cast<float>(uv[ct][ta][i]);
           Rs[ta][i] = -R[ta][i] * d[i];
-          Ot[ct][ta][i] *= e;
         }
       }
       rf[ct][0] = acc_pair_frag<__bf16>(R[0], R[1]);
@@ -652,69 +682,105 @@ __global__ __launch_bounds__(192) void wy_state_kernel(WyArgs a) {
       rs[ct][0] = acc_pair_frag<__bf16>(Rs[0], Rs[1]);
       rs[ct][1] = acc_pair_frag<__bf16>(Rs[2], Rs[3]);
     }
-    F8 mf[6];
-#pragma unroll
-    for (int ta = 0, n = 0; ta < 4; ++ta) {
-      mf[n++] = lds_pair_frag_k<C>(gM + (16 * ta + l16) * LDD, 0, g);
-      if (ta >= 2) mf[n++] = lds_pair_frag_k<C>(gM + (16 * ta + l16) * LDD, 32, g);
-    }
-    state_update(B, rs);
-    GDR_MARK(4);
-    // O^T += R^T (-M)^T (gM holds -M), then O out, four columns of one token per 8-byte store;
-    // rows past the last token are dropped by the range
-    const int64_t t0 = c * C;
-    const int64_t rr = (bi * T + t0) * H + hi;
-    const int64_t bytes = ((T - t0 - 1) * H + 1) * DV * 2 - col0 * 2;
-    const auto ro = make_rsrc(a.o + rr * DV + col0, static_cast<uint32_t>(bytes < 0x7fffffff ? bytes : 0x7fffffff));
+    // S <- e^{G_n} S + K^T (-R e^{G_n - G_t})
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-      for (int ta = 0, n = 0; ta < 4; ++ta) {
-        Ot[ct][ta] = MM::mma8(rf[ct][0], mf[n++], Ot[ct][ta]);
-        if (ta >= 2) Ot[ct][ta] = MM::mma8(rf[ct][1], mf[n++], Ot[ct][ta]);
+      for (int tl = 0; tl < NTD; ++tl)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) S[ct][tl][i] *= egn;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int tl = 0; tl < NTD; ++tl)
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) S[ct][tl] = MM::mma8(kf[kb][tl], rs[ct][kb], S[ct][tl]);
+    GDR_MARK(4);
+  };
+  auto read_out_compute = [&](int64_t c) {
+    // O^T tiles: Ot[ct][ta] lane (g, l16) holds O[16 ta + l16][16 ct + 4 g + i];
+    // O^T = (Q S)^T diag(e^{G_t}) + R^T (-M)^T
+    f32x4 Ot[NCT][4];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int ta = 0; ta < 4; ++ta) Ot[ct][ta] = zero4();
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int ta = 0; ta < 4; ++ta)
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) Ot[ct][ta] = MM::mma8(sf[ct][kb], aq[kb][ta], Ot[ct][ta]);
+#pragma unroll
+    for (int ta = 0; ta < 4; ++ta)
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Ot[ct][ta][i] *= eg[ta];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int ta = 2 * kb; ta < 4; ++ta) {  // -M is lower triangular: tokens 32.. only reach ta >= 2
+        const int m = kb == 0 ? (ta < 2 ? ta : 2 * ta - 2) : 2 * ta - 1;  // (ta, kb) in mf
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) Ot[ct][ta] = MM::mma8(rf[ct][kb], mf[m], Ot[ct][ta]);
+      }
+    // O rows into the chunk's O buffer, four columns of one token per 8-byte write
+    __bf16* oO = obuf(c);
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int ta = 0; ta < 4; ++ta) {
         bf16x4 ob;
 #pragma unroll
         for (int i = 0; i < 4; ++i) ob[i] = static_cast<__bf16>(Ot[ct][ta][i]);
-        typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, ob), ro,
-                                              (16 * ta + l16) * hdv + (16 * ct + 4 * g) * 2, 0, 0);
+        *reinterpret_cast<bf16x4*>(oO + (16 * ta + l16) * L::LDO + cb + 16 * ct + 4 * g) = ob;
       }
   };
 
   // ---------------- pipeline ----------------
-  // The loaders fetch and write chunk c+1 within iteration c: their registers are not live
-  // across the loop, which leaves the state wave's accumulators in ordinary VGPRs.
-  if (loader && nch > 0) {
-    prefetch(0);
-    store(0);
+  if (nch > 0) {
+    if (wave == 0) {
+      dma_chunk(0);
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    }
+    if (wave == 1 && nch > 1) dma_chunk(1);
   }
   lds_barrier();
   for (int64_t ch = 0; ch < nch; ++ch) {
     // opaque per chunk: keeps lane-dependent LDS addresses from being hoisted out of the loop
     asm volatile("" : "+v"(lane), "+v"(g), "+v"(l16));
     GDR_MARK(0);
-    if (loader) {
-      if (ch + 1 < nch) {
-        prefetch(ch + 1);
-        store(ch + 1);
-      }
-      GDR_MARK(3);
-    } else {
-      state_chunk(ch);
+    if (!loader) {
+      read_chain(ch);
+      read_out(ch);
     }
+    lds_barrier_keep_vm();  // A: buffer ch mod 2 is free
     GDR_MARK(1);
-    lds_barrier();
+    if (loader) {
+      if (wave == static_cast<int>(ch & 1)) {
+        if (ch + 2 < nch) dma_chunk(ch + 2);
+      } else {
+        if (ch > 0) store_o(ch - 1);
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // this wave's loads of chunk ch+1
+      }
+    } else {
+      chain(ch);
+      read_out_compute(ch);
+    }
     GDR_MARK(2);
+    lds_barrier_keep_vm();  // B: chunk ch+1 is in buffer (ch+1) mod 2, O of chunk ch in its O buffer
   }
+  if (wave == 0 && nch > 0) store_o(nch - 1);
 
   if (!loader && a.S_T != nullptr) {
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
-      const int64_t sb = bh * DK * DV + col0 + 16 * ct + l16;
+      const int64_t sb = bh * DK * DV + col0 + cb + 16 * ct + l16;
 #pragma unroll
       for (int tl = 0; tl < NTD; ++tl)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) a.S_T[sb + (int64_t)(16 * tl + 4 * g + i) * DV] = S[ct][tl][i];
+        for (int i = 0; i < 4; ++i) a.S_T[sb + (int64_t)perm_row(tl, 4 * g + i) * DV] = S[ct][tl][i];
     }
   }
 }

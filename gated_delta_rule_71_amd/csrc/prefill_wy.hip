@@ -14,10 +14,12 @@ bool prefill_wy_ok(int64_t DK, int64_t DV, int b_kind) {
          b_kind != kChannel;
 }
 
+// Per 64-token chunk: W (64 x dk), U (64 x dv), -M (64 x 64), all bf16, and kWyE floats of
+// exponentials; each array 256-byte aligned.
 size_t prefill_wy_workspace_bytes(int64_t nstate, int64_t T, int64_t DK, int64_t DV) {
   const size_t chunks = static_cast<size_t>(nstate) * static_cast<size_t>((T + 63) / 64);
   return align256(chunks * 64 * DK * 2) + align256(chunks * 64 * DV * 2) +
-         align256(chunks * 64 * 64 * 2) + align256(chunks * 64 * 4);
+         align256(chunks * 64 * 64 * 2) + align256(chunks * kWyE * 4);
 }
 
 namespace {
@@ -36,12 +38,13 @@ hipError_t launch_dk(WyArgs a, int64_t nstate, hipEvent_t mark, hipStream_t s) {
     const hipError_t e = hipEventRecord(mark, s);
     if (e != hipSuccess) return e;
   }
+  // two state waves of 16 columns each (one LDS copy of a chunk feeds both), else one
   if (a.DV % 32 == 0) {
     a.nsl = static_cast<int>(a.DV / 32);
-    hipLaunchKernelGGL((wy_state_kernel<DK, 2>), dim3((unsigned)(nstate * a.nsl)), dim3(192), 0, s, a);
+    hipLaunchKernelGGL((wy_state_kernel<DK, 1, 2>), dim3((unsigned)(nstate * a.nsl)), dim3(256), 0, s, a);
   } else {
     a.nsl = static_cast<int>(a.DV / 16);
-    hipLaunchKernelGGL((wy_state_kernel<DK, 1>), dim3((unsigned)(nstate * a.nsl)), dim3(192), 0, s, a);
+    hipLaunchKernelGGL((wy_state_kernel<DK, 1, 1>), dim3((unsigned)(nstate * a.nsl)), dim3(192), 0, s, a);
   }
   return hipGetLastError();
 }
@@ -74,7 +77,7 @@ hipError_t prefill_wy_launch(const PrefillArgs<bf16_t>& p, int64_t nstate, int64
   ws += align256(chunks * 64 * p.DV * 2);
   a.M = reinterpret_cast<__bf16*>(ws);
   ws += align256(chunks * 64 * 64 * 2);
-  a.G = reinterpret_cast<float*>(ws);
+  a.E = reinterpret_cast<float*>(ws);
   switch (DK) {
     case 32: return launch_dk<32>(a, nstate, mark, s);
     case 64: return launch_dk<64>(a, nstate, mark, s);

@@ -97,9 +97,9 @@ const char* gdr_status_string(int status);
  * chunk-local kernel plus a per-state kernel that exchange per-chunk matrices
  * through the workspace, each array 256-byte aligned; per 64-token chunk of
  * every (batch, head) that is:
- *   scalar (or no) decay, scalar (or no) erase gate: W and U (64 x dk and
- *     64 x dv bf16), the masked 64 x 64 read-out matrix (bf16) and the 64 gate
- *     prefix sums (fp32): 128 dk + 128 dv + 8448 bytes;
+ *   scalar (or no) decay, scalar (or no) erase gate: W (64 x dk), U (64 x dv)
+ *     and the masked 64 x 64 read-out matrix, all bf16, and 132 floats of gate
+ *     exponentials: 128 dk + 128 dv + 8720 bytes;
  *   per-channel decay, decay applied before the erase: W, the decay-scaled
  *     query, the decay-scaled erase keys (each 64 x dk bf16), the 64 x 64
  *     read-out matrix, Y (dv x 64 bf16), the dk chunk decays (fp32) and a

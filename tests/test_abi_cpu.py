@@ -140,12 +140,13 @@ def test_workspace_query_and_decode_validation():
     assert N.workspace_bytes(prob()) == two
     one = two - r(ch * 128 * 64 * 2) - 2 * r(ch * 64 * 128 * 2)
     assert N.workspace_bytes(prob(order=N.DECAY_THEN_ERASE)) == one
-    # scalar decay in bf16: W, U (64 x dk, 64 x dv bf16), -M (64 x 64 bf16) and G (64 fp32)
-    # per 64-token chunk of every (batch, head), each array rounded up to 256 bytes
+    # scalar decay in bf16: W (64 x dk), U (64 x dv), -M (64 x 64), all bf16, and 132 fp32 gate
+    # exponentials per 64-token chunk of every (batch, head), each array rounded up to 256 bytes
     sp = prob(alpha_kind=N.GATE_SCALAR, b_kind=N.GATE_SCALAR, w_kind=N.GATE_SCALAR)
     chunks = 2 * 3 * 2  # batch 2, heads 3, ceil(70 / 64) = 2
     r = lambda n: (n + 255) // 256 * 256
-    need = r(chunks * 64 * 128 * 2) + r(chunks * 64 * 128 * 2) + r(chunks * 64 * 64 * 2) + r(chunks * 64 * 4)
+    need = r(chunks * 64 * 128 * 2) + r(chunks * 64 * 128 * 2) + r(chunks * 64 * 64 * 2) + \
+        r(chunks * 132 * 4)
     assert N.workspace_bytes(sp) == need
     assert N.workspace_bytes(prob(alpha_kind=N.GATE_SCALAR, b_kind=N.GATE_SCALAR, w_kind=N.GATE_SCALAR,
                                   io_dtype=N.GDR_FP32, dk=32, dv=32)) == 0
