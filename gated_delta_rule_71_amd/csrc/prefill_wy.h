@@ -58,6 +58,15 @@ __device__ __forceinline__ uint32_t wy_range(int64_t left, int64_t H, int64_t wi
   return static_cast<uint32_t>(bytes < 0x7fffffff ? bytes : 0x7fffffff);
 }
 
+// Transposing 8-byte LDS read (gfx950): within each group of 16 lanes, lane 4 a + b receives
+// element b of the 8-byte vectors that lanes a, a + 4, a + 8 and a + 12 of the group point at.
+__device__ __forceinline__ bf16x4 lds_read_tr4(const unsigned char* p) {
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16*)(const_cast<unsigned char*>(p)));
+  return __builtin_bit_cast(bf16x4, r);
+}
+
 // Inverses of the four 16x16 unit-lower-triangular diagonal blocks of (I + A), from their strict
 // lower parts in Ld (fp32, column-major [4][16][LDL]).  Runs on lanes 0-31 of waves 0 and 1:
 // lane (block, j) solves column j by a column sweep (once x_m is final, every later x_i drops
@@ -159,6 +168,10 @@ __global__ __launch_bounds__(256) void wy_prep_kernel(WyArgs a) {
   // the buffer range (zero) and absent gate kinds an empty range
   constexpr int XPT = C * (DVP / 8) / 256;  // x items per thread at the widest dv
   const int nxg = static_cast<int>(DV / 8);
+  // item / nxg for item < 2048 and nxg <= 32, without a division: with M = ceil(2^16 / nxg),
+  // (item M) >> 16 is exact because item (M - 2^16 / nxg) / 2^16 < 1 / 32 <= 1 / nxg
+  const uint32_t xdm = (65536u + static_cast<uint32_t>(nxg) - 1u) / static_cast<uint32_t>(nxg);
+  auto xdiv = [&](uint32_t item) { return (item * xdm) >> 16; };
   const uint32_t oob = 0x80000000u;
   const auto rwc = make_rsrc(a.w_kind == kChannel ? a.wg + rr * DV : a.v,
                              a.w_kind == kChannel ? wy_range(left, H, DV) : 0u);
@@ -181,7 +194,7 @@ __global__ __launch_bounds__(256) void wy_prep_kernel(WyArgs a) {
   for (int j = 0; j < XPT; ++j) {
     const int item = tid + 256 * j;
     const bool in = item < C * nxg;
-    const uint32_t t = in ? item / nxg : 0, xg = in ? item % nxg : 0;
+    const uint32_t t = in ? xdiv(item) : 0, xg = in ? item - t * nxg : 0;
     vv[j] = buf_load16(rv, in ? t * hdv + xg * 16 : oob);
     wv[j] = buf_load16(rwc, in ? t * hdv + xg * 16 : oob);
     wsv[j] = buf_load_u16(rws, in ? t * h1 : oob);
@@ -189,7 +202,7 @@ __global__ __launch_bounds__(256) void wy_prep_kernel(WyArgs a) {
   const uint16_t lav = buf_load_u16(rla, lane * h1), bev = buf_load_u16(rb, lane * h1);
 
   // M tiles above the diagonal are never written and must read as zero
-  for (int i = tid; i < C * LDD / 2; i += 256) reinterpret_cast<uint32_t*>(gM)[i] = 0u;
+  for (int i = tid; i < C * LDD / 8; i += 256) reinterpret_cast<uint4*>(gM)[i] = make_uint4(0, 0, 0, 0);
 #pragma unroll
   for (int j = 0; j < IPT; ++j) {
     const int item = tid + 256 * j;
@@ -201,7 +214,7 @@ __global__ __launch_bounds__(256) void wy_prep_kernel(WyArgs a) {
   for (int j = 0; j < XPT; ++j) {
     const int item = tid + 256 * j;
     if (item < C * nxg) {
-      const int t = item / nxg, xg = item % nxg;
+      const int t = static_cast<int>(xdiv(item)), xg = item - t * nxg;
       float x[8];
       load8f(reinterpret_cast<const bf16_t*>(&vv[j]), x);
       if (a.w_kind == kChannel) {
@@ -298,9 +311,13 @@ __global__ __launch_bounds__(256) void wy_prep_kernel(WyArgs a) {
   }
   lds_barrier();
 
-  // W = T diag(beta e^G) K and U = T X, one 16-column tile at a time (no chain: T is known).
-  // B fragments gather 8 tokens of one column (tile-pair order); the result overwrites the
-  // same columns (each wave owns whole column tiles), to be written out coalesced below.
+  // W = T diag(beta e^G) K and U = T X, one 16-column tile at a time (no chain: T is known), as
+  // transposed tiles W^T = (diag(beta e^G) K)^T T^T, each wave owning whole column tiles.  The A
+  // fragments (8 tokens of one column, tile-pair order) come from two transposing reads of the
+  // token-major rows per k-block (source lane (a, m) = (l16 & 3, l16 >> 2) of group g points at
+  // token 32 ks + 16 h + 4 g + m, columns 16 ct + 4 a ..); each lane then holds four consecutive
+  // columns of one token and overwrites them in place with one 8-byte write per token tile, to be
+  // written out coalesced below.
   {
     const __bf16* tT = gM;
     F8 tf[6];
@@ -309,7 +326,7 @@ __global__ __launch_bounds__(256) void wy_prep_kernel(WyArgs a) {
       tf[n++] = lds_pair_frag_k<C>(tT + (16 * ta + l16) * LDD, 0, g);
       if (ta >= 2) tf[n++] = lds_pair_frag_k<C>(tT + (16 * ta + l16) * LDD, 32, g);
     }
-    float sw[2][8];  // beta_t e^{G_t} of the tokens of this lane's B fragments
+    float sw[2][8];  // beta_t e^{G_t} of the tokens of this lane's fragments
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
@@ -317,48 +334,54 @@ __global__ __launch_bounds__(256) void wy_prep_kernel(WyArgs a) {
         const int t = 32 * ks + 4 * g + (e & 3) + (e >> 2) * 16;
         sw[ks][e] = sc[3 * C + t] * sc[C + t];
       }
-    auto gemm_tile = [&](__bf16* base, int pitch, int col, bool scale) {
-      F8 bf[2];
+    const int a_ = l16 & 3, m_ = l16 >> 2;
+    auto gemm_tile = [&](__bf16* base, int pitch, int ct, bool scale) {
+      F8 af[2];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int t = 32 * ks + 4 * g + (e & 3) + (e >> 2) * 16;
-          const float x = static_cast<float>(base[t * pitch + col]);
-          bf[ks][e] = static_cast<__bf16>(scale ? x * sw[ks][e] : x);
+        for (int h = 0; h < 2; ++h) {
+          const bf16x4 v = lds_read_tr4(reinterpret_cast<const unsigned char*>(
+              base + (32 * ks + 16 * h + 4 * g + m_) * pitch + 16 * ct + 4 * a_));
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            af[ks][4 * h + e] = scale ? static_cast<__bf16>(static_cast<float>(v[e]) * sw[ks][4 * h + e]) : v[e];
         }
-      f32x4 D[4];
+      f32x4 D[4];  // D[ta] lane (g, l16): columns 16 ct + 4 g + i of token 16 ta + l16
 #pragma unroll
       for (int ta = 0, n = 0; ta < 4; ++ta) {
-        D[ta] = MM::mma8(tf[n++], bf[0], zero4());
-        if (ta >= 2) D[ta] = MM::mma8(tf[n++], bf[1], D[ta]);
+        D[ta] = MM::mma8(af[0], tf[n++], zero4());
+        if (ta >= 2) D[ta] = MM::mma8(af[1], tf[n++], D[ta]);
       }
 #pragma unroll
-      for (int ta = 0; ta < 4; ++ta)
+      for (int ta = 0; ta < 4; ++ta) {
+        bf16x4 ob;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) base[(16 * ta + 4 * g + e) * pitch + col] = static_cast<__bf16>(D[ta][e]);
+        for (int i = 0; i < 4; ++i) ob[i] = static_cast<__bf16>(D[ta][i]);
+        *reinterpret_cast<bf16x4*>(base + (16 * ta + l16) * pitch + 16 * ct + 4 * g) = ob;
+      }
     };
     // tile loops without a per-tile guard where the counts divide evenly over the four waves,
     // so that the loads of every tile of a wave are issued together
     if constexpr (DK / 16 % 4 == 0) {
 #pragma unroll
-      for (int r = 0; r < DK / 64; ++r) gemm_tile(tK, LDT, 16 * (wave + 4 * r) + l16, true);
+      for (int r = 0; r < DK / 64; ++r) gemm_tile(tK, LDT, wave + 4 * r, true);
     } else {
 #pragma unroll
       for (int r = 0; r < (DK / 16 + 3) / 4; ++r) {
         const int ct = wave + 4 * r;
-        if (ct < DK / 16) gemm_tile(tK, LDT, 16 * ct + l16, true);
+        if (ct < DK / 16) gemm_tile(tK, LDT, ct, true);
       }
     }
     const int nct_u = static_cast<int>(DV / 16);
     if (nct_u == DVP / 16) {
 #pragma unroll
-      for (int r = 0; r < DVP / 64; ++r) gemm_tile(tX, LDX, 16 * (wave + 4 * r) + l16, false);
+      for (int r = 0; r < DVP / 64; ++r) gemm_tile(tX, LDX, wave + 4 * r, false);
     } else {
 #pragma unroll
       for (int r = 0; r < DVP / 64; ++r) {
         const int ct = wave + 4 * r;
-        if (ct < nct_u) gemm_tile(tX, LDX, 16 * ct + l16, false);
+        if (ct < nct_u) gemm_tile(tX, LDX, ct, false);
       }
     }
   }
@@ -375,9 +398,8 @@ __global__ __launch_bounds__(256) void wy_prep_kernel(WyArgs a) {
       *reinterpret_cast<uint4*>(Wo + t * DK + cg * 8) = *reinterpret_cast<const uint4*>(tK + t * LDT + cg * 8);
     }
     __bf16* Uo = a.U + cix * C * DV;
-    const int nxg = static_cast<int>(DV / 8);
     for (int item = tid; item < C * nxg; item += 256) {
-      const int t = item / nxg, xg = item % nxg;
+      const int t = static_cast<int>(xdiv(item)), xg = item - t * nxg;
       *reinterpret_cast<uint4*>(Uo + t * DV + xg * 8) = *reinterpret_cast<const uint4*>(tX + t * LDX + xg * 8);
     }
   }
@@ -435,15 +457,6 @@ __device__ __forceinline__ void dma_rows(__amdgpu_buffer_rsrc_t r, unsigned char
 template <int NCHR, bool PERM>
 __device__ __forceinline__ const unsigned char* swz_addr(const unsigned char* base, int row, int piece) {
   return base + row * NCHR * 16 + ((piece ^ swz_key<NCHR, PERM>(row)) << 4);
-}
-
-// Transposing 8-byte LDS read (gfx950): within each group of 16 lanes, lane 4 a + b receives
-// element b of the 8-byte vectors that lanes a, a + 4, a + 8 and a + 12 of the group point at.
-__device__ __forceinline__ bf16x4 lds_read_tr4(const unsigned char* p) {
-  typedef short v4i16 __attribute__((ext_vector_type(4)));
-  const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) v4i16*)(const_cast<unsigned char*>(p)));
-  return __builtin_bit_cast(bf16x4, r);
 }
 
 // The 16-byte piece `piece` of row `row` of such an array.
