@@ -125,7 +125,10 @@ struct WyPrepLayout {
 // sums; Gram tiles (waves 0-1: A, waves 2-3: M); diagonal inverses (waves 0-1) while waves 2-3
 // write -M out; T = (I + A)^{-1} by blocked forward substitution on the identity; W = T B_k and
 // U = T X, each wave owning whole 16-column tiles (B_k the k tile scaled by beta_t e^{G_t}).
-template <int DK, int DVP>
+//
+// Without an erase gate (ERASE false: b = 0, linear attention with a scalar or no decay) the
+// Gram A vanishes, T = I, W = 0 and U = X: only M, U and the exponentials are formed.
+template <int DK, int DVP, bool ERASE>
 __global__ __launch_bounds__(256) void wy_prep_kernel(WyArgs a) {
   using L = WyPrepLayout<DK, DVP>;
   using MM = Mma<__bf16>;
@@ -255,7 +258,7 @@ __global__ __launch_bounds__(256) void wy_prep_kernel(WyArgs a) {
   lds_barrier();
 
   // Gram tiles: waves 0-1 A (solve, with the fp32 diagonal blocks to Ld), waves 2-3 M
-  {
+  if (ERASE || wave >= 2) {
     const int prod = wave >> 1;
     const __bf16* rows = prod == 0 ? tK : tQ;
     if (wave & 1)
@@ -267,7 +270,7 @@ __global__ __launch_bounds__(256) void wy_prep_kernel(WyArgs a) {
   lds_barrier();
 
   if (wave < 2) {
-    if (lane < 32) wy_diag_inverses<LDL, LDI>(Ld, dInv, wave, lane, l16);
+    if (ERASE && lane < 32) wy_diag_inverses<LDL, LDI>(Ld, dInv, wave, lane, l16);
   } else {
     // -M out: 64 rows of 128 bytes, 16 bytes per item
     __bf16* Mo = a.M + cix * C * C;
@@ -283,7 +286,7 @@ __global__ __launch_bounds__(256) void wy_prep_kernel(WyArgs a) {
   // T = (I + A)^{-1}: wave j solves column block j by blocked forward substitution on the
   // identity (T_jj, then T_ij = -T_ii sum_{j<=m<i} A_im T_mj), as bf16 into the M array,
   // which has been written out above and has T's shape
-  {
+  if constexpr (ERASE) {
     __bf16* tT = gM;
     const int j = wave;
     bf16x4 af[6], tf[4];
@@ -318,7 +321,7 @@ __global__ __launch_bounds__(256) void wy_prep_kernel(WyArgs a) {
   // token 32 ks + 16 h + 4 g + m, columns 16 ct + 4 a ..); each lane then holds four consecutive
   // columns of one token and overwrites them in place with one 8-byte write per token tile, to be
   // written out coalesced below.
-  {
+  if constexpr (ERASE) {
     const __bf16* tT = gM;
     F8 tf[6];
 #pragma unroll
@@ -388,14 +391,14 @@ __global__ __launch_bounds__(256) void wy_prep_kernel(WyArgs a) {
   GDR_PMARK(3);
   lds_barrier();
 
-  // W and U out, 16 bytes per item
+  // W and U out (without the erase, U = X), 16 bytes per item
   {
     __bf16* Wo = a.W + cix * C * DK;
 #pragma unroll
     for (int j = 0; j < IPT; ++j) {
       const int item = tid + 256 * j;
       const int t = item / NCG, cg = item % NCG;
-      *reinterpret_cast<uint4*>(Wo + t * DK + cg * 8) = *reinterpret_cast<const uint4*>(tK + t * LDT + cg * 8);
+      if (ERASE) *reinterpret_cast<uint4*>(Wo + t * DK + cg * 8) = *reinterpret_cast<const uint4*>(tK + t * LDT + cg * 8);
     }
     __bf16* Uo = a.U + cix * C * DV;
     for (int item = tid; item < C * nxg; item += 256) {
@@ -498,7 +501,9 @@ struct WyStateLayout {
 //            and leave O in an LDS buffer; loader wave c mod 2 refills buffer c mod 2 with
 //            chunk c+2, and the other loader wave copies the O rows of chunk c-1 to HBM and
 //            waits for its loads of chunk c+1.
-template <int DK, int NCT, int NSW>
+//
+// Without an erase gate (ERASE false) W = 0: V and W's loads drop out and R = -U.
+template <int DK, int NCT, int NSW, bool ERASE>
 __global__ __launch_bounds__(64 * (2 + NSW)) void wy_state_kernel(WyArgs a) {
   constexpr int DVS = 16 * NCT * NSW;
   using L = WyStateLayout<DK, DVS>;
@@ -548,7 +553,7 @@ __global__ __launch_bounds__(64 * (2 + NSW)) void wy_state_kernel(WyArgs a) {
     unsigned char* B = buf(c);
     const int64_t t0 = c * C, rr = (bi * T + t0) * H + hi, cix = bh * nch + c;
     dma_rows<C * NCQ>(make_rsrc(a.q + rr * DK, wy_range(T - t0, H, DK)), B + L::oQ, offQ);
-    dma_rows<C * NCQ>(make_rsrc(a.W + cix * C * DK, C * DK * 2), B + L::oW, offW);
+    if (ERASE) dma_rows<C * NCQ>(make_rsrc(a.W + cix * C * DK, C * DK * 2), B + L::oW, offW);
     dma_rows<C * NCQ>(make_rsrc(a.k + rr * DK, wy_range(T - t0, H, DK)), B + L::oK, offK);
     dma_rows<C * NCC>(make_rsrc(a.M + cix * C * C, C * C * 2), B + L::oM, offM);
     dma_rows<C * L::NCU>(make_rsrc(a.U + cix * C * DV + col0, static_cast<uint32_t>((C * DV - col0) * 2)),
@@ -611,7 +616,8 @@ __global__ __launch_bounds__(64 * (2 + NSW)) void wy_state_kernel(WyArgs a) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int ta = 0; ta < 4; ++ta) aw[kb][ta] = lds_piece<NCQ, true>(B + L::oW, perm_row(ta, l16), 4 * kb + g);
+      for (int ta = 0; ta < 4; ++ta)
+        if (ERASE) aw[kb][ta] = lds_piece<NCQ, true>(B + L::oW, perm_row(ta, l16), 4 * kb + g);
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
       const int col = cb + 16 * ct + 4 * ta_;
@@ -674,7 +680,8 @@ __global__ __launch_bounds__(64 * (2 + NSW)) void wy_state_kernel(WyArgs a) {
 #pragma unroll
       for (int ta = 0; ta < 4; ++ta)
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) V[ct][ta] = MM::mma8(aw[kb][ta], sf[ct][kb], V[ct][ta]);
+        for (int ct = 0; ct < NCT; ++ct)
+          if (ERASE) V[ct][ta] = MM::mma8(aw[kb][ta], sf[ct][kb], V[ct][ta]);
     GDR_MARK(3);
     // R = V - U (read-out operand) and -R e^{G_n - G_t} (state-update operand), tokens as k
     F8 rs[NCT][2];

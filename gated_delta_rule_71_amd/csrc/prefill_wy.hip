@@ -23,14 +23,14 @@ size_t prefill_wy_workspace_bytes(int64_t nstate, int64_t T, int64_t DK, int64_t
 }
 
 namespace {
-template <int DK>
+template <int DK, bool ERASE>
 hipError_t launch_dk(WyArgs a, int64_t nstate, hipEvent_t mark, hipStream_t s) {
   const int64_t nprep = nstate * a.nch;
   if (nprep > 0) {
     if (a.DV <= 128)
-      hipLaunchKernelGGL((wy_prep_kernel<DK, 128>), dim3((unsigned)nprep), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((wy_prep_kernel<DK, 128, ERASE>), dim3((unsigned)nprep), dim3(256), 0, s, a);
     else
-      hipLaunchKernelGGL((wy_prep_kernel<DK, 256>), dim3((unsigned)nprep), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((wy_prep_kernel<DK, 256, ERASE>), dim3((unsigned)nprep), dim3(256), 0, s, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -41,10 +41,10 @@ hipError_t launch_dk(WyArgs a, int64_t nstate, hipEvent_t mark, hipStream_t s) {
   // two state waves of 16 columns each (one LDS copy of a chunk feeds both), else one
   if (a.DV % 32 == 0) {
     a.nsl = static_cast<int>(a.DV / 32);
-    hipLaunchKernelGGL((wy_state_kernel<DK, 1, 2>), dim3((unsigned)(nstate * a.nsl)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((wy_state_kernel<DK, 1, 2, ERASE>), dim3((unsigned)(nstate * a.nsl)), dim3(256), 0, s, a);
   } else {
     a.nsl = static_cast<int>(a.DV / 16);
-    hipLaunchKernelGGL((wy_state_kernel<DK, 1, 1>), dim3((unsigned)(nstate * a.nsl)), dim3(192), 0, s, a);
+    hipLaunchKernelGGL((wy_state_kernel<DK, 1, 1, ERASE>), dim3((unsigned)(nstate * a.nsl)), dim3(192), 0, s, a);
   }
   return hipGetLastError();
 }
@@ -78,10 +78,11 @@ hipError_t prefill_wy_launch(const PrefillArgs<bf16_t>& p, int64_t nstate, int64
   a.M = reinterpret_cast<__bf16*>(ws);
   ws += align256(chunks * 64 * 64 * 2);
   a.E = reinterpret_cast<float*>(ws);
+  const bool erase = p.b_kind != kNone;  // without an erase gate: W = 0, U = X
   switch (DK) {
-    case 32: return launch_dk<32>(a, nstate, mark, s);
-    case 64: return launch_dk<64>(a, nstate, mark, s);
-    default: return launch_dk<128>(a, nstate, mark, s);
+    case 32: return erase ? launch_dk<32, true>(a, nstate, mark, s) : launch_dk<32, false>(a, nstate, mark, s);
+    case 64: return erase ? launch_dk<64, true>(a, nstate, mark, s) : launch_dk<64, false>(a, nstate, mark, s);
+    default: return erase ? launch_dk<128, true>(a, nstate, mark, s) : launch_dk<128, false>(a, nstate, mark, s);
   }
 }
 

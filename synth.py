@@ -60,6 +60,10 @@ WORKLOADS = {
                      0.02, 1003),
     "decode": Workload("decode", 256, 32, 1, 128, 128, "bf16", CHANNEL, CHANNEL, CHANNEL, False, -2.0,
                        0.02, 1004, steps=1000),
+    # erase off (b = 0): linear attention with a scalar data-dependent decay (Mamba-2 style) at
+    # the Gated DeltaNet shapes; w = 1
+    "mamba2": Workload("mamba2", 4, 16, 4096, 128, 128, "bf16", SCALAR, NONE, NONE, False, -2.0, 0.0,
+                       1005),
 }
 
 

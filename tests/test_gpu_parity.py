@@ -204,13 +204,14 @@ def test_decode_workload_subset(dev):
 # ------------------------------------------------------------------ full-size prefill workloads
 
 
-def test_gdn_workload_full(dev):
-    wl = synth.WORKLOADS["gdn"]
-    say("gdn workload", wl)
+@pytest.mark.parametrize("name", ["gdn", "mamba2"])
+def test_scalar_decay_workloads_full(dev, name):
+    wl = synth.WORKLOADS[name]
+    say("%s workload" % name, wl)
     x = synth.make_prefill(wl)
     o, S = run_gpu_prefill(x, dev)
     torch.cuda.synchronize()
-    check(x, o, S, "erase_then_decay", TOL["bf16"], "gdn full")
+    check(x, o, S, "erase_then_decay", TOL["bf16"], "%s full" % name)
 
 
 @pytest.mark.parametrize("name", ["kda", "gdn2"])
