@@ -178,6 +178,35 @@ def time_decode(wl, n_steps, dev):
     return ms
 
 
+def time_hooks(wl, dev, positions=64, reps=5):
+    """State decomposition ("How Linear Attention Remembers", Analytical Framework): C_i^(t) of
+    `positions` evenly spaced positions at the last token, batch row 0 of the workload, one
+    hooks.contributions call (positions x T tokens x H heads of recurrence)."""
+    import torch
+    import synth
+    from gated_delta_rule_71_amd import hooks
+    x = synth.make_prefill(wl.with_(B=1))
+    g = {n: (None if t is None else t.to(dev)) for n, t in x.items()}
+    pos = [int(round(i * (wl.T - 1) / (positions - 1))) for i in range(positions)]
+    run = lambda: hooks.contributions(g["q"], g["k"], g["v"], g["log_alpha"], g["b"], g["w"],
+                                      positions=pos, t=wl.T - 1)
+    run()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    return {"what": "C_i^(t) for %d positions at t = T-1, one sequence of the %s workload"
+                    % (positions, wl.name),
+            "positions": positions, "ms_per_call": ms,
+            "head_tokens_per_s": positions * wl.T * wl.H / (ms * 1e-3),
+            "contributions_per_s": positions * wl.H / (ms * 1e-3)}
+
+
 def cpu_baseline(wl):
     """The fp64 oracle, as it stands, on the host cores, on the whole prefill workload."""
     import oracle
@@ -210,6 +239,8 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=None)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--hooks", action="store_true",
+                    help="also time the state-decomposition hook (64 positions, one sequence)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 1 GiB device copy (read 1 GiB, write 1 GiB): the "
                          "reference dispatch that scales rocprofv3 FETCH_SIZE / WRITE_SIZE")
@@ -280,6 +311,8 @@ def main():
                          "states_per_s": dw.B * dw.H / (ms * 1e-3), "value": gbs, "unit": "GB/s",
                          "hbm_frac": gbs / PEAK_HBM_GBS, "bytes_per_step": db,
                          "traffic": recorded_traffic("decode:decode")}
+    if args.hooks:
+        out["hooks"] = time_hooks(wl, dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(out), flush=True)

@@ -72,6 +72,31 @@ def recurrence_operator(q, k, v, log_alpha=None, b=None, w=None, S0=None, order=
     return o, S
 
 
+def contribution(q, k, v, log_alpha=None, b=None, w=None, i=0, t=None, order=0, write=None):
+    """C_i^(t) = (T_t o ... o T_{i+1})(W_i), C_i^(i) = W_i ("How Linear Attention Remembers",
+    Analytical Framework), with T_j(S) = A_j S as in recurrence_operator and the rank-one write
+    W_i = k_i^T (w_i . v_i), or W_i = k^T x for write = (k, x) given per (batch, head) as
+    arrays [B, H, DK] and [B, H, DV].  Returns [B, H, DK, DV] float64."""
+    q, k, v, la, bb, ww, (B, T, H, DK, DV) = _unpack(q, k, v, log_alpha, b, w)
+    t = T - 1 if t is None else t
+    C = np.zeros((B, H, DK, DV))
+    eye = np.eye(DK)
+    for bi in range(B):
+        for hi in range(H):
+            if write is None:
+                Ci = np.outer(k[bi, i, hi], ww[bi, i, hi] * v[bi, i, hi])
+            else:
+                Ci = np.outer(np.asarray(write[0], dtype=np.float64)[bi, hi],
+                              np.asarray(write[1], dtype=np.float64)[bi, hi])
+            for j in range(i + 1, t + 1):
+                kt, ct = k[bi, j, hi], bb[bi, j, hi] * k[bi, j, hi]
+                Dm = np.diag(np.exp(la[bi, j, hi]))
+                E = eye - np.outer(kt, ct)
+                Ci = (Dm @ E if order == 0 else E @ Dm) @ Ci
+            C[bi, hi] = Ci
+    return C
+
+
 def linear_attention_masked(q, k, x):
     """Erase off, alpha = 1: O = tril(Q K^T) X per (batch, head)."""
     q, k, x = (np.asarray(a, dtype=np.float64) for a in (q, k, x))

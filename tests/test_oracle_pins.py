@@ -341,6 +341,34 @@ def test_linearity_and_decomposition():
     np.testing.assert_allclose(S_b, S_1 + S_2, rtol=1e-11, atol=1e-12)
 
 
+@pytest.mark.parametrize("order", [0, 1])
+def test_contributions_sum_to_the_state(order):
+    """[HLAR] Analytical Framework: S_t = sum_{i <= t} C_i^(t) from a zero state, where
+    C_i^(t) = (T_t o ... o T_{i+1})(W_i).  The reference contributions (transition operators
+    composed from the definition) must add up to the C oracle's state at every t tested, and
+    a write blocked at x (w_x = 0) must leave S_t - C_x^(t)."""
+    c = rand_case(B=1, T=23, H=2, seed=31, s0=False)
+    for t in (0, 9, 22):
+        cut = {n: (None if a is None else a[:, :t + 1]) for n, a in c.items() if n != "S0"}
+        _, S = oracle.forward(cut["q"], cut["k"], cut["v"], cut["log_alpha"], cut["b"], cut["w"],
+                              None, order=order)
+        total = sum(ref.contribution(c["q"], c["k"], c["v"], c["log_alpha"], c["b"], c["w"],
+                                     i=i, t=t, order=order) for i in range(t + 1))
+        np.testing.assert_allclose(total, S, rtol=1e-10, atol=1e-12)
+    x, t = 5, 22
+    wb = c["w"].copy()
+    wb[:, x] = 0
+    _, S = oracle.forward(c["q"], c["k"], c["v"], c["log_alpha"], c["b"], c["w"], None, order=order)
+    _, Sb = oracle.forward(c["q"], c["k"], c["v"], c["log_alpha"], c["b"], wb, None, order=order)
+    Cx = ref.contribution(c["q"], c["k"], c["v"], c["log_alpha"], c["b"], c["w"], i=x, t=t, order=order)
+    np.testing.assert_allclose(Sb, S - Cx, rtol=1e-10, atol=1e-12)
+    # the contribution of the last token is its own write, k_t^T (w_t . v_t)
+    Ct = ref.contribution(c["q"], c["k"], c["v"], c["log_alpha"], c["b"], c["w"], i=t, t=t, order=order)
+    W = np.einsum("bhk,bhv->bhkv", c["k"][:, t].astype(np.float64),
+                  c["w"][:, t].astype(np.float64) * c["v"][:, t].astype(np.float64))
+    np.testing.assert_allclose(Ct, W, rtol=1e-12, atol=1e-14)
+
+
 def test_resume_from_intermediate_state():
     """[HLAR]: S_t depends only on S_{t-1} and token t, so running [0, T1) and then [T1, T)
     from the state reached equals one run."""
