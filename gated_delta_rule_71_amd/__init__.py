@@ -7,7 +7,8 @@ library is missing, every call raises: there is no CPU or eager fallback.
     o, S_T = chunk_fwd(q, k, v, log_alpha, b, w, S0)      # prefill over T tokens
     o = decode_step(q, k, v, log_alpha, b, w, S)           # one token, S updated in place
 
-Layouts: q, k [B,T,H,dk]; v [B,T,H,dv]; gates [B,T,H] (one value per token and head) or
+Layouts: q, k [B,T,Hqk,dk]; v [B,T,H,dv] (H a multiple of Hqk: grouped key / value heads, value
+head h reading q / k head h // (H // Hqk)); gates [B,T,H] (one value per token and head) or
 [B,T,H,dk] / [B,T,H,dv] (per channel) or None; states [B,H,dk,dv] float32.  q, k, v and the
 gates share one dtype, bfloat16 or float32.  The recurrence:
 
@@ -78,12 +79,12 @@ def chunk_fwd(q, k, v, log_alpha=None, b=None, w=None, S0=None, order="erase_the
     ``phase_event`` (a torch.cuda.Event) is recorded between the chunk-local kernel and the
     per-state kernel, for timing the two separately."""
     torch = _torch()
-    B, T, H, DK = q.shape
-    DV = v.shape[-1]
+    B, T, HQ, DK = q.shape
+    H, DV = v.shape[2], v.shape[-1]
     dt, dev = q.dtype, q.device
-    if k.shape != q.shape or tuple(v.shape[:3]) != (B, T, H):
-        raise ValueError("shape mismatch: q %s k %s v %s" % (tuple(q.shape), tuple(k.shape),
-                                                             tuple(v.shape)))
+    if k.shape != q.shape or tuple(v.shape[:2]) != (B, T) or HQ == 0 or H % HQ != 0:
+        raise ValueError("shape mismatch: q %s k %s v %s (v heads must be a multiple of q / k "
+                         "heads)" % (tuple(q.shape), tuple(k.shape), tuple(v.shape)))
     if k.dtype != dt or v.dtype != dt or k.device != dev or v.device != dev:
         raise TypeError("q, k, v must share dtype and device")
     if dev.type != "cuda":
@@ -102,7 +103,8 @@ def chunk_fwd(q, k, v, log_alpha=None, b=None, w=None, S0=None, order="erase_the
     else:
         S_T = final_state
         _check_contig(final_state=S_T)
-    prob = make_problem(B, H, T, DK, DV, _io_dtype(q), ak, bk, wk, _ORDERS[order])
+    prob = make_problem(B, H, T, DK, DV, _io_dtype(q), ak, bk, wk, _ORDERS[order],
+                        qk_heads=0 if HQ == H else HQ)
     need = _native.workspace_bytes(prob)
     if workspace is None:
         workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev) if need else None
@@ -127,13 +129,13 @@ def chunk_fwd(q, k, v, log_alpha=None, b=None, w=None, S0=None, order="erase_the
 
 def workspace_bytes(q, v, log_alpha=None, b=None, w=None, order="erase_then_decay"):
     """Workspace bytes ``chunk_fwd`` needs for these inputs (0 when it needs none)."""
-    B, T, H, DK = q.shape
-    DV = v.shape[-1]
+    B, T, HQ, DK = q.shape
+    H, DV = v.shape[2], v.shape[-1]
     ak = _gate_kind(log_alpha, B, T, H, DK, "log_alpha", q.dtype, q.device)
     bk = _gate_kind(b, B, T, H, DK, "b", q.dtype, q.device)
     wk = _gate_kind(w, B, T, H, DV, "w", q.dtype, q.device)
     return _native.workspace_bytes(make_problem(B, H, T, DK, DV, _io_dtype(q), ak, bk, wk,
-                                                _ORDERS[order]))
+                                                _ORDERS[order], qk_heads=0 if HQ == H else HQ))
 
 
 def decode_step(q, k, v, log_alpha=None, b=None, w=None, S=None, order="erase_then_decay",
@@ -143,13 +145,13 @@ def decode_step(q, k, v, log_alpha=None, b=None, w=None, S=None, order="erase_th
     torch = _torch()
     if S is None:
         raise ValueError("decode_step needs the state S")
-    B, T, H, DK = q.shape
-    DV = v.shape[-1]
+    B, T, HQ, DK = q.shape
+    H, DV = v.shape[2], v.shape[-1]
     if T != 1:
         raise ValueError("decode_step takes one token per sequence (T = 1)")
     dt, dev = q.dtype, q.device
-    if k.shape != q.shape or tuple(v.shape[:3]) != (B, 1, H):
-        raise ValueError("shape mismatch")
+    if k.shape != q.shape or tuple(v.shape[:2]) != (B, 1) or HQ == 0 or H % HQ != 0:
+        raise ValueError("shape mismatch (v heads must be a multiple of q / k heads)")
     if k.dtype != dt or v.dtype != dt:
         raise TypeError("q, k, v must share a dtype")
     ak = _gate_kind(log_alpha, B, 1, H, DK, "log_alpha", dt, dev)
@@ -159,7 +161,8 @@ def decode_step(q, k, v, log_alpha=None, b=None, w=None, S=None, order="erase_th
     if S.dtype != torch.float32 or tuple(S.shape) != (B, H, DK, DV):
         raise ValueError("S must be float32 [B,H,dk,dv]")
     o = out if out is not None else torch.empty((B, 1, H, DV), dtype=dt, device=dev)
-    prob = make_problem(B, H, 1, DK, DV, _io_dtype(q), ak, bk, wk, _ORDERS[order])
+    prob = make_problem(B, H, 1, DK, DV, _io_dtype(q), ak, bk, wk, _ORDERS[order],
+                        qk_heads=0 if HQ == H else HQ)
     rc = _native.decode_step_raw(prob, _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b),
                                  _ptr(w), _ptr(S), _ptr(o), _stream(dev))
     if rc != _native.GDR_OK:

@@ -33,14 +33,14 @@ class GdrProblem(ctypes.Structure):
         ("b_kind", ctypes.c_int32),
         ("w_kind", ctypes.c_int32),
         ("order", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("qk_heads", ctypes.c_int32),
     ]
 
 
 def make_problem(batch, heads, seqlen, dk, dv, io_dtype=GDR_BF16, alpha_kind=GATE_NONE,
-                 b_kind=GATE_NONE, w_kind=GATE_NONE, order=ERASE_THEN_DECAY, chunk=64):
+                 b_kind=GATE_NONE, w_kind=GATE_NONE, order=ERASE_THEN_DECAY, chunk=64, qk_heads=0):
     return GdrProblem(ctypes.sizeof(GdrProblem), io_dtype, batch, heads, seqlen, dk, dv, chunk,
-                      alpha_kind, b_kind, w_kind, order, 0)
+                      alpha_kind, b_kind, w_kind, order, qk_heads)
 
 
 class GdrError(RuntimeError):

@@ -36,6 +36,7 @@ struct DecodeArgs {
   int64_t DV;
   int alpha_kind, b_kind, w_kind;
   int ncb_per_state;  // DV / NCB
+  int64_t Hk;         // q / k heads (H is a multiple): value head h reads q / k head h / (H / Hk)
 };
 
 template <int NCB, int DK>
@@ -79,9 +80,10 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs<IO> a) {
 
   // 2) per-channel vectors of this token
   float dot_qk = 0.f, dot_gamma = 0.f;
+  const int64_t bqk = (bh / a.H) * a.Hk + (bh % a.H) / (a.H / a.Hk);  // this state's q / k row
   for (int d = tid; d < DK; d += NT) {
     const int64_t i = bh * DK + d;
-    const float qd = ld(a.q, i), kd = ld(a.k, i);
+    const float qd = ld(a.q, bqk * DK + d), kd = ld(a.k, bqk * DK + d);
     const float lad = a.alpha_kind == kNone ? 0.f : ld(a.la, a.alpha_kind == kScalar ? bh : i);
     const float bd = a.b_kind == kNone ? 0.f : ld(a.bg, a.b_kind == kScalar ? bh : i);
     const float al = __expf(lad);
@@ -220,10 +222,10 @@ static hipError_t launch_decode_dk(DecodeArgs<IO> a, int64_t n_states, bool deca
 // Host launcher; arguments are validated by the caller (gdr_api.hip).
 template <typename IO>
 hipError_t launch_decode(const IO* q, const IO* k, const IO* v, const IO* la, const IO* bg,
-                         const IO* wg, float* S, IO* o, int64_t B, int64_t H, int64_t DK,
-                         int64_t DV, int alpha_kind, int b_kind, int w_kind, bool decay_first,
-                         hipStream_t stream) {
-  DecodeArgs<IO> a{q, k, v, la, bg, wg, S, o, H, DV, alpha_kind, b_kind, w_kind, 1};
+                         const IO* wg, float* S, IO* o, int64_t B, int64_t H, int64_t Hk,
+                         int64_t DK, int64_t DV, int alpha_kind, int b_kind, int w_kind,
+                         bool decay_first, hipStream_t stream) {
+  DecodeArgs<IO> a{q, k, v, la, bg, wg, S, o, H, DV, alpha_kind, b_kind, w_kind, 1, Hk};
   const int64_t n = B * H;
   switch (DK) {
     case 16: return launch_decode_dk<IO, 16>(a, n, decay_first, stream);
@@ -236,11 +238,11 @@ hipError_t launch_decode(const IO* q, const IO* k, const IO* v, const IO* la, co
 
 template hipError_t launch_decode<bf16_t>(const bf16_t*, const bf16_t*, const bf16_t*,
                                           const bf16_t*, const bf16_t*, const bf16_t*, float*,
-                                          bf16_t*, int64_t, int64_t, int64_t, int64_t, int, int,
-                                          int, bool, hipStream_t);
+                                          bf16_t*, int64_t, int64_t, int64_t, int64_t, int64_t, int,
+                                          int, int, bool, hipStream_t);
 template hipError_t launch_decode<float>(const float*, const float*, const float*, const float*,
                                          const float*, const float*, float*, float*, int64_t,
-                                         int64_t, int64_t, int64_t, int, int, int, bool,
+                                         int64_t, int64_t, int64_t, int64_t, int, int, int, bool,
                                          hipStream_t);
 
 }  // namespace gdr

@@ -12,15 +12,15 @@
 namespace gdr {
 template <typename IO>
 hipError_t launch_decode(const IO* q, const IO* k, const IO* v, const IO* la, const IO* bg,
-                         const IO* wg, float* S, IO* o, int64_t B, int64_t H, int64_t DK,
-                         int64_t DV, int alpha_kind, int b_kind, int w_kind, bool decay_first,
-                         hipStream_t stream);
+                         const IO* wg, float* S, IO* o, int64_t B, int64_t H, int64_t Hk,
+                         int64_t DK, int64_t DV, int alpha_kind, int b_kind, int w_kind,
+                         bool decay_first, hipStream_t stream);
 template <typename IO>
 hipError_t launch_prefill(const IO* q, const IO* k, const IO* v, const IO* la, const IO* bg,
                           const IO* wg, const float* S0, IO* o, float* S_T, int64_t B, int64_t T,
-                          int64_t H, int64_t DK, int64_t DV, int alpha_kind, int b_kind,
-                          int w_kind, bool decay_first, void* workspace, hipEvent_t mark,
-                          hipStream_t stream);
+                          int64_t H, int64_t Hk, int64_t DK, int64_t DV, int alpha_kind,
+                          int b_kind, int w_kind, bool decay_first, void* workspace,
+                          hipEvent_t mark, hipStream_t stream);
 bool prefill_supported(int io_dtype, int64_t DK, int64_t DV, int alpha_kind, bool decay_first);
 size_t prefill_workspace_bytes(int io_dtype, int64_t nstate, int64_t T, int64_t DK, int64_t DV,
                                int alpha_kind, int b_kind, bool decay_first);
@@ -45,7 +45,8 @@ bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.hi > a.
 
 int check_problem(const gdr_problem* p) {
   if (p == nullptr) return GDR_ERR_INVALID_ARGUMENT;
-  if (p->struct_size != (int32_t)sizeof(gdr_problem) || p->reserved != 0)
+  if (p->struct_size != (int32_t)sizeof(gdr_problem)) return GDR_ERR_INVALID_ARGUMENT;
+  if (p->qk_heads < 0 || (p->qk_heads > 0 && p->heads % p->qk_heads != 0))
     return GDR_ERR_INVALID_ARGUMENT;
   if (p->io_dtype != GDR_BF16 && p->io_dtype != GDR_FP32) return GDR_ERR_INVALID_ARGUMENT;
   for (int32_t kind : {p->alpha_kind, p->b_kind, p->w_kind})
@@ -65,9 +66,13 @@ int check_problem(const gdr_problem* p) {
 }
 
 // Pointer checks shared by both entry points.  `nt` = tokens per (batch, head).
+// q / k heads of a validated problem
+int64_t qk_heads(const gdr_problem* p) { return p->qk_heads > 0 ? p->qk_heads : p->heads; }
+
 int check_tensors(const gdr_problem* p, int64_t nt, const void* q, const void* k, const void* v,
                   const void* la, const void* b, const void* w, const void* o) {
   const int64_t rows = p->batch * nt * p->heads;
+  const int64_t qk_rows = p->batch * nt * qk_heads(p);
   if (rows == 0) return GDR_OK;
   if (!q || !k || !v || !o) return GDR_ERR_INVALID_ARGUMENT;
   if ((p->alpha_kind != GDR_GATE_NONE && !la) || (p->b_kind != GDR_GATE_NONE && !b) ||
@@ -82,7 +87,7 @@ int check_tensors(const gdr_problem* p, int64_t nt, const void* q, const void* k
     return kind == GDR_GATE_SCALAR ? rows * es : rows * width * es;
   };
   const Range ro = range_of(o, rows * p->dv * es);
-  const Range ins[] = {range_of(q, rows * p->dk * es), range_of(k, rows * p->dk * es),
+  const Range ins[] = {range_of(q, qk_rows * p->dk * es), range_of(k, qk_rows * p->dk * es),
                        range_of(v, rows * p->dv * es),
                        p->alpha_kind ? range_of(la, gate_bytes(p->alpha_kind, p->dk)) : Range{0, 0},
                        p->b_kind ? range_of(b, gate_bytes(p->b_kind, p->dk)) : Range{0, 0},
@@ -152,14 +157,14 @@ int chunk_fwd(const gdr_problem* p, const void* q, const void* k, const void* v,
     e = gdr::launch_prefill<T>(
         (const T*)q, (const T*)k, (const T*)v, (const T*)gate_ptr(p->alpha_kind, log_alpha),
         (const T*)gate_ptr(p->b_kind, b), (const T*)gate_ptr(p->w_kind, w), S0, (T*)o, S_T,
-        p->batch, p->seqlen, p->heads, p->dk, p->dv, p->alpha_kind, p->b_kind, p->w_kind,
+        p->batch, p->seqlen, p->heads, qk_heads(p), p->dk, p->dv, p->alpha_kind, p->b_kind, p->w_kind,
         decay_first, workspace, static_cast<hipEvent_t>(mark), s);
   } else {
     e = gdr::launch_prefill<float>(
         (const float*)q, (const float*)k, (const float*)v,
         (const float*)gate_ptr(p->alpha_kind, log_alpha), (const float*)gate_ptr(p->b_kind, b),
         (const float*)gate_ptr(p->w_kind, w), S0, (float*)o, S_T, p->batch, p->seqlen, p->heads,
-        p->dk, p->dv, p->alpha_kind, p->b_kind, p->w_kind, decay_first, workspace,
+        qk_heads(p), p->dk, p->dv, p->alpha_kind, p->b_kind, p->w_kind, decay_first, workspace,
         static_cast<hipEvent_t>(mark), s);
   }
   return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
@@ -206,14 +211,14 @@ GDR_EXPORT int gdr_decode_step(const gdr_problem* p, const void* q, const void* 
     e = gdr::launch_decode<T>((const T*)q, (const T*)k, (const T*)v,
                               (const T*)gate_ptr(p->alpha_kind, log_alpha),
                               (const T*)gate_ptr(p->b_kind, b), (const T*)gate_ptr(p->w_kind, w), S,
-                              (T*)o, p->batch, p->heads, p->dk, p->dv, p->alpha_kind, p->b_kind,
+                              (T*)o, p->batch, p->heads, qk_heads(p), p->dk, p->dv, p->alpha_kind, p->b_kind,
                               p->w_kind, decay_first, s);
   } else {
     e = gdr::launch_decode<float>((const float*)q, (const float*)k, (const float*)v,
                                   (const float*)gate_ptr(p->alpha_kind, log_alpha),
                                   (const float*)gate_ptr(p->b_kind, b),
                                   (const float*)gate_ptr(p->w_kind, w), S, (float*)o, p->batch,
-                                  p->heads, p->dk, p->dv, p->alpha_kind, p->b_kind, p->w_kind,
+                                  p->heads, qk_heads(p), p->dk, p->dv, p->alpha_kind, p->b_kind, p->w_kind,
                                   decay_first, s);
   }
   return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;

@@ -87,18 +87,18 @@ bool prefill_supported(int io_dtype, int64_t DK, int64_t DV, int alpha_kind, boo
 template <typename IO>
 hipError_t launch_prefill(const IO* q, const IO* k, const IO* v, const IO* la, const IO* bg,
                           const IO* wg, const float* S0, IO* o, float* S_T, int64_t B, int64_t T,
-                          int64_t H, int64_t DK, int64_t DV, int alpha_kind, int b_kind,
-                          int w_kind, bool decay_first, void* workspace, hipEvent_t mark,
-                          hipStream_t stream) {
+                          int64_t H, int64_t Hk, int64_t DK, int64_t DV, int alpha_kind,
+                          int b_kind, int w_kind, bool decay_first, void* workspace,
+                          hipEvent_t mark, hipStream_t stream) {
   const int mode = prefill_mode(alpha_kind, decay_first);
-  PrefillArgs<IO> a{q, k, v, la, bg, wg, S0, o, S_T, T, H, DV, alpha_kind, b_kind, w_kind, 1};
+  PrefillArgs<IO> a{q, k, v, la, bg, wg, S0, o, S_T, T, H, DV, alpha_kind, b_kind, w_kind, 1, Hk};
   const int64_t nstate = B * H;
   if constexpr (sizeof(IO) == 2) {
     if (mode == 0) {
       const ScalarImpl impl = scalar_impl();
       if (impl == ScalarImpl::kWy && prefill_wy_ok(DK, DV, b_kind))
         return prefill_wy_launch(a, nstate, DK, workspace, mark, stream);
-      if (impl == ScalarImpl::kFused && prefill_scalar_ok(T, H, DK, DV, b_kind)) {
+      if (impl == ScalarImpl::kFused && Hk == H && prefill_scalar_ok(T, H, DK, DV, b_kind)) {
         if (const hipError_t e = record_mark(mark, stream); e != hipSuccess) return e;
         return prefill_scalar_launch(a, nstate, DK, stream);
       }
@@ -126,11 +126,12 @@ hipError_t launch_prefill(const IO* q, const IO* k, const IO* v, const IO* la, c
 template hipError_t launch_prefill<bf16_t>(const bf16_t*, const bf16_t*, const bf16_t*,
                                            const bf16_t*, const bf16_t*, const bf16_t*,
                                            const float*, bf16_t*, float*, int64_t, int64_t,
-                                           int64_t, int64_t, int64_t, int, int, int, bool, void*,
+                                           int64_t, int64_t, int64_t, int64_t, int, int, int,
+                                           bool, void*,
                                            hipEvent_t, hipStream_t);
 template hipError_t launch_prefill<float>(const float*, const float*, const float*, const float*,
                                           const float*, const float*, const float*, float*, float*,
-                                          int64_t, int64_t, int64_t, int64_t, int64_t, int, int,
-                                          int, bool, void*, hipEvent_t, hipStream_t);
+                                          int64_t, int64_t, int64_t, int64_t, int64_t, int64_t, int,
+                                          int, int, bool, void*, hipEvent_t, hipStream_t);
 
 }  // namespace gdr

@@ -103,7 +103,8 @@ struct PrefillArgs {
   float* S_T;
   int64_t T, H, DV;
   int alpha_kind, b_kind, w_kind;
-  int nsl;  // value slices per state
+  int nsl;     // value slices per state
+  int64_t Hk;  // q / k heads (H is a multiple): value head h reads q / k head h / (H / Hk)
 };
 
 // 8 consecutive I/O elements starting at p (16-byte aligned for bf16) as fp32.
@@ -341,7 +342,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs<IO> a) {
   // rows whatever T is; rows past the last token fall outside the range and load as zero.
   constexpr uint32_t ES = sizeof(IO);
   const uint32_t hdk = static_cast<uint32_t>(a.H * DK) * ES, hdv = static_cast<uint32_t>(a.H * DV) * ES;
+  const uint32_t hqk = static_cast<uint32_t>(a.Hk * DK) * ES;  // token stride of q and k
   const uint32_t h1 = static_cast<uint32_t>(a.H) * ES;
+  const int64_t hq = hi / (a.H / a.Hk);                         // this state's q / k head
   auto prefetch = [&](int64_t c) {
     const int64_t t0 = c * C;
     const int64_t rr = (bi * a.T + t0) * a.H + hi;  // row of the chunk's first token
@@ -357,8 +360,11 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs<IO> a) {
     const auto rv = make_rsrc(a.v + rr * DV + col0, vb);
     const auto rwc = make_rsrc(a.w_kind == kChannel ? a.wg + rr * DV + col0 : a.v, a.w_kind == kChannel ? vb : 0u);
     const auto rws = make_rsrc(a.w_kind == kScalar ? a.wg + rr : a.v, a.w_kind == kScalar ? range(1) : 0u);
-    const auto rq = make_rsrc(a.q + rr * DK, range(DK));
-    const auto rk = make_rsrc(a.k + rr * DK, range(DK));
+    const int64_t rqk = (bi * a.T + t0) * a.Hk + hq;  // q / k row of the chunk's first token
+    const int64_t qkb = ((left - 1) * a.Hk + 1) * DK * ES;
+    const uint32_t qkr = static_cast<uint32_t>(qkb < 0x7fffffff ? qkb : 0x7fffffff);
+    const auto rq = make_rsrc(a.q + rqk * DK, qkr);
+    const auto rk = make_rsrc(a.k + rqk * DK, qkr);
     const auto rbc = make_rsrc(a.b_kind == kChannel ? a.bg + rr * DK : a.q, a.b_kind == kChannel ? range(DK) : 0u);
     const auto rbs = make_rsrc(a.b_kind == kScalar ? a.bg + rr : a.q, a.b_kind == kScalar ? range(1) : 0u);
     const auto rla = make_rsrc(a.alpha_kind == kChannel ? a.la + rr * DK : (a.alpha_kind == kScalar ? a.la + rr : a.q),
@@ -378,8 +384,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs<IO> a) {
     for (int u = 0; u < TPS; ++u) {
       const uint32_t t = ts * TPS + u;
       const uint32_t ko = act ? t * hdk + d0 * ES : oob;
-      raw8_buf(pq[u], rq, ko);
-      raw8_buf(pk[u], rk, ko);
+      const uint32_t qo = act ? t * hqk + d0 * ES : oob;
+      raw8_buf(pq[u], rq, qo);
+      raw8_buf(pk[u], rk, qo);
       raw8_buf(pb[u], rbc, ko);
       raw1_buf(pbs[u], rbs, act ? t * h1 : oob);
       if (MODE != 0) raw8_buf(pla[u], rla, ko);

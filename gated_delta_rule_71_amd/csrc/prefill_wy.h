@@ -47,7 +47,8 @@ struct WyArgs {
   float* E;   // [B*H][nch][kWyE]: e^{G_t} and e^{G_n - G_t} for the 64 tokens, e^{G_n}, 3 zeros
   int64_t T, H, DV, nch;
   int alpha_kind, b_kind, w_kind;
-  int nsl;  // value slices per state (state kernel)
+  int nsl;     // value slices per state (state kernel)
+  int64_t Hk;  // q / k heads (H is a multiple): value head h reads q / k head h / (H / Hk)
 };
 
 constexpr int kWyE = 132;  // floats per chunk in WyArgs::E (33 pieces of 16 bytes)
@@ -161,10 +162,11 @@ __global__ __launch_bounds__(256) void wy_prep_kernel(WyArgs a) {
   const int64_t cix = bh * nch + c;             // chunk index in the workspace
 
   // inputs: rows past the last token read as zero (identity padding)
-  const auto rq = make_rsrc(a.q + rr * DK, wy_range(left, H, DK));
-  const auto rk = make_rsrc(a.k + rr * DK, wy_range(left, H, DK));
+  const int64_t rqk = (bi * a.T + t0) * a.Hk + hi / (H / a.Hk);  // q / k row of the first token
+  const auto rq = make_rsrc(a.q + rqk * DK, wy_range(left, a.Hk, DK));
+  const auto rk = make_rsrc(a.k + rqk * DK, wy_range(left, a.Hk, DK));
   const auto rv = make_rsrc(a.v + rr * DV, wy_range(left, H, DV));
-  const uint32_t hdk = static_cast<uint32_t>(H * DK * 2), hdv = static_cast<uint32_t>(H * DV * 2);
+  const uint32_t hdk = static_cast<uint32_t>(a.Hk * DK * 2), hdv = static_cast<uint32_t>(H * DV * 2);
   const uint32_t h1 = static_cast<uint32_t>(H * 2);
 
   // every global load is issued before the first use: out-of-range items get an offset past
@@ -529,7 +531,9 @@ __global__ __launch_bounds__(64 * (2 + NSW)) void wy_state_kernel(WyArgs a) {
   const int64_t bi = bh / a.H, hi = bh % a.H;
   const int64_t DV = a.DV, H = a.H, T = a.T, nch = a.nch;
   const int64_t col0 = static_cast<int64_t>(sl) * DVS;
-  const uint32_t hdk = static_cast<uint32_t>(H * DK * 2), hdv = static_cast<uint32_t>(H * DV * 2);
+  // token stride of q and k (the only [B, T, H?, dk] arrays read here), and of o
+  const uint32_t hdk = static_cast<uint32_t>(a.Hk * DK * 2), hdv = static_cast<uint32_t>(H * DV * 2);
+  const int64_t hq = hi / (H / a.Hk);  // this state's q / k head
 
   auto buf = [&](int64_t c) -> unsigned char* { return smem + (c & 1) * L::BUF; };
   auto obuf = [&](int64_t c) -> __bf16* {
@@ -551,10 +555,10 @@ __global__ __launch_bounds__(64 * (2 + NSW)) void wy_state_kernel(WyArgs a) {
   // chunk c's operands into buffer c mod 2 (q and k rows past the last token arrive as zeros)
   auto dma_chunk = [&](int64_t c) {
     unsigned char* B = buf(c);
-    const int64_t t0 = c * C, rr = (bi * T + t0) * H + hi, cix = bh * nch + c;
-    dma_rows<C * NCQ>(make_rsrc(a.q + rr * DK, wy_range(T - t0, H, DK)), B + L::oQ, offQ);
+    const int64_t t0 = c * C, rr = (bi * T + t0) * a.Hk + hq, cix = bh * nch + c;
+    dma_rows<C * NCQ>(make_rsrc(a.q + rr * DK, wy_range(T - t0, a.Hk, DK)), B + L::oQ, offQ);
     if (ERASE) dma_rows<C * NCQ>(make_rsrc(a.W + cix * C * DK, C * DK * 2), B + L::oW, offW);
-    dma_rows<C * NCQ>(make_rsrc(a.k + rr * DK, wy_range(T - t0, H, DK)), B + L::oK, offK);
+    dma_rows<C * NCQ>(make_rsrc(a.k + rr * DK, wy_range(T - t0, a.Hk, DK)), B + L::oK, offK);
     dma_rows<C * NCC>(make_rsrc(a.M + cix * C * C, C * C * 2), B + L::oM, offM);
     dma_rows<C * L::NCU>(make_rsrc(a.U + cix * C * DV + col0, static_cast<uint32_t>((C * DV - col0) * 2)),
                          B + L::oU, offU);

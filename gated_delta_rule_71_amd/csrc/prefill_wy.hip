@@ -65,6 +65,7 @@ hipError_t prefill_wy_launch(const PrefillArgs<bf16_t>& p, int64_t nstate, int64
   a.T = p.T;
   a.H = p.H;
   a.DV = p.DV;
+  a.Hk = p.Hk;
   a.nch = (p.T + 63) / 64;
   a.alpha_kind = p.alpha_kind;
   a.b_kind = p.b_kind;

@@ -55,7 +55,8 @@ struct WycArgs {
   int* flag;   // [cix]          1: exact token path
   int64_t T, H, DV, nch;
   int b_kind, w_kind;
-  int nsl;  // value slices per state (state kernel)
+  int nsl;     // value slices per state (state kernel)
+  int64_t Hk;  // q / k heads (H is a multiple): value head h reads q / k head h / (H / Hk)
 };
 
 constexpr float kWycSpanLimit = 76.f;
@@ -141,8 +142,10 @@ __global__ __launch_bounds__(256) void wyc_prep_kernel(WycArgs a) {
   const uint32_t oob = 0x80000000u;
   const uint32_t hdk = static_cast<uint32_t>(H * DK * 2), hdv = static_cast<uint32_t>(H * DV * 2);
   const uint32_t h1 = static_cast<uint32_t>(H * 2);
-  const auto rq = make_rsrc(a.q + rr * DK, wy_range(left, H, DK));
-  const auto rk = make_rsrc(a.k + rr * DK, wy_range(left, H, DK));
+  const uint32_t hqk = static_cast<uint32_t>(a.Hk * DK * 2);      // token stride of q and k
+  const int64_t rqk = (bi * a.T + t0) * a.Hk + hi / (H / a.Hk);  // their row of the first token
+  const auto rq = make_rsrc(a.q + rqk * DK, wy_range(left, a.Hk, DK));
+  const auto rk = make_rsrc(a.k + rqk * DK, wy_range(left, a.Hk, DK));
   const auto rla = make_rsrc(a.la + rr * DK, wy_range(left, H, DK));
   const auto rbc = make_rsrc(a.b_kind == kChannel ? a.bg + rr * DK : a.q, a.b_kind == kChannel ? wy_range(left, H, DK) : 0u);
   const auto rbs = make_rsrc(a.b_kind == kScalar ? a.bg + rr : a.q, a.b_kind == kScalar ? wy_range(left, H, 1) : 0u);
@@ -155,8 +158,9 @@ __global__ __launch_bounds__(256) void wyc_prep_kernel(WycArgs a) {
   for (int u = 0; u < TPS; ++u) {
     const uint32_t t = ts * TPS + u;
     const uint32_t off = act ? t * hdk + d0 * 2 : oob;
-    pq[u] = buf_load16(rq, off);
-    pk[u] = buf_load16(rk, off);
+    const uint32_t qo = act ? t * hqk + d0 * 2 : oob;
+    pq[u] = buf_load16(rq, qo);
+    pk[u] = buf_load16(rk, qo);
     pb[u] = buf_load16(rbc, off);
     pl[u] = buf_load16(rla, off);
     pbs[u] = buf_load_u16(rbs, act ? t * h1 : oob);
@@ -621,6 +625,8 @@ __global__ __launch_bounds__(192) void wyc_state_kernel(WycArgs a) {
   const int64_t DV = a.DV, H = a.H, T = a.T, nch = a.nch;
   const int64_t col0 = static_cast<int64_t>(sl) * DVS;
   const uint32_t hdk = static_cast<uint32_t>(H * DK * 2), hdv = static_cast<uint32_t>(H * DV * 2);
+  const uint32_t hqk = static_cast<uint32_t>(a.Hk * DK * 2);  // token stride of q and k
+  const int64_t hq = hi / (H / a.Hk);                        // this state's q / k head
   const uint32_t h1 = static_cast<uint32_t>(H * 2);
   const uint32_t oob = 0x80000000u;
 
@@ -688,15 +694,15 @@ __global__ __launch_bounds__(192) void wyc_state_kernel(WycArgs a) {
     if (robust) store_x(c, xT);
     if (robust) {
       // raw c = b . k and log alpha rows, token-major
-      const int64_t t0 = c * C, rr = (bi * T + t0) * H + hi;
-      const auto rk = make_rsrc(a.k + rr * DK, wy_range(T - t0, H, DK));
+      const int64_t t0 = c * C, rr = (bi * T + t0) * H + hi, rqk = (bi * T + t0) * a.Hk + hq;
+      const auto rk = make_rsrc(a.k + rqk * DK, wy_range(T - t0, a.Hk, DK));
       const auto rla = make_rsrc(a.la + rr * DK, wy_range(T - t0, H, DK));
       const auto rbc = make_rsrc(a.b_kind == kChannel ? a.bg + rr * DK : a.q, a.b_kind == kChannel ? wy_range(T - t0, H, DK) : 0u);
       const auto rbs = make_rsrc(a.b_kind == kScalar ? a.bg + rr : a.q, a.b_kind == kScalar ? wy_range(T - t0, H, 1) : 0u);
 #pragma unroll
       for (int j = 0; j < IPT; ++j) {
         const uint32_t t = (tid / NCG) * IPT + j, cg = tid % NCG;
-        const uint4 kk = buf_load16(rk, t * hdk + cg * 16);
+        const uint4 kk = buf_load16(rk, t * hqk + cg * 16);
         const uint4 bb = buf_load16(rbc, t * hdk + cg * 16);
         const uint16_t bs = buf_load_u16(rbs, t * h1);
         float k8[8], c8[8];
@@ -783,10 +789,10 @@ __global__ __launch_bounds__(192) void wyc_state_kernel(WycArgs a) {
   // set 1 of chunk c: Qhat and W rows (exact path: raw q and k rows)
   auto store_set1 = [&](int64_t c, int robust) {
     const int64_t cix = bh * nch + c;
-    const int64_t t0 = c * C, rr = (bi * T + t0) * H + hi;
-    const auto ra = robust ? make_rsrc(a.q + rr * DK, wy_range(T - t0, H, DK)) : make_rsrc(a.Qp + cix * C * DK, C * DK * 2);
-    const auto rb = robust ? make_rsrc(a.k + rr * DK, wy_range(T - t0, H, DK)) : make_rsrc(a.W + cix * C * DK, C * DK * 2);
-    const uint32_t pitch = robust ? hdk : DK * 2;
+    const int64_t t0 = c * C, rqk = (bi * T + t0) * a.Hk + hq;
+    const auto ra = robust ? make_rsrc(a.q + rqk * DK, wy_range(T - t0, a.Hk, DK)) : make_rsrc(a.Qp + cix * C * DK, C * DK * 2);
+    const auto rb = robust ? make_rsrc(a.k + rqk * DK, wy_range(T - t0, a.Hk, DK)) : make_rsrc(a.W + cix * C * DK, C * DK * 2);
+    const uint32_t pitch = robust ? hqk : DK * 2;
     uint4 pa[IPT], pb[IPT];
 #pragma unroll
     for (int j = 0; j < IPT; ++j) {

@@ -78,6 +78,7 @@ hipError_t prefill_wyc_launch(const PrefillArgs<bf16_t>& p, int64_t nstate, int6
   a.T = p.T;
   a.H = p.H;
   a.DV = p.DV;
+  a.Hk = p.Hk;
   a.nch = (p.T + 63) / 64;
   a.b_kind = p.b_kind;
   a.w_kind = p.w_kind;

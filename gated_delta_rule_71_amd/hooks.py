@@ -53,8 +53,8 @@ def contributions(q, k, v, log_alpha=None, b=None, w=None, positions=(0,), t=Non
     the state after token t.  One ``chunk_fwd`` call over len(positions) * B sequences of t + 1
     tokens, each keeping a single write."""
     torch = _torch()
-    B, T, H, DK = q.shape
-    DV = v.shape[-1]
+    B, T, _, DK = q.shape
+    H, DV = v.shape[2], v.shape[-1]
     t = T - 1 if t is None else int(t)
     pos = [int(i) for i in positions]
     if not 0 <= t < T or any(not 0 <= i <= t for i in pos):
@@ -82,7 +82,7 @@ def block_write(q, k, v, log_alpha=None, b=None, w=None, S0=None, position=0, he
     """The recurrence with the write at `position` removed (for the listed heads, or all).
     Returns (o, S_T) like ``chunk_fwd``."""
     torch = _torch()
-    B, T, H, _ = q.shape
+    B, T, H = v.shape[:3]
     wf = _write_gate(w, v, B, T, H).clone()
     hs = slice(None) if heads is None else torch.as_tensor(heads, device=v.device)
     if wf.dim() == 3:
@@ -103,7 +103,7 @@ def replace_write(q, k, v, log_alpha=None, b=None, w=None, S0=None, position=0, 
     torch = _torch()
     if donor is None:
         raise ValueError("replace_write needs the donor's tensors")
-    B, T, H, _ = q.shape
+    B, T, H = v.shape[:3]
     wf = _write_gate(w, v, B, T, H)
     dw = _write_gate(donor.get("w"), donor["v"], B, T, H)
     if dw.dim() != wf.dim():

@@ -29,8 +29,8 @@
  *   contiguous, 16-byte aligned.  The library never allocates, frees or keeps
  *   them.  Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
  *   stream); outputs are valid once the stream has reached the call.
- * - Per-token tensors are laid out [B, T, H, D]: q, k [B,T,H,dk];
- *   v, o [B,T,H,dv].  Gates: log_alpha [B,T,H] (SCALAR) or [B,T,H,dk]
+ * - Per-token tensors are laid out [B, T, H, D]: q, k [B,T,Hqk,dk] with
+ *   Hqk = qk_heads (or H when that is 0); v, o [B,T,H,dv].  Gates: log_alpha [B,T,H] (SCALAR) or [B,T,H,dk]
  *   (CHANNEL); b [B,T,H] or [B,T,H,dk]; w [B,T,H] or [B,T,H,dv].  A gate of
  *   kind NONE ignores its pointer (may be NULL) and means alpha = 1, b = 0,
  *   w = 1.  Gates are given as log alpha (<= 0 for a contraction; any finite
@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define GDR_ABI_VERSION 1
+#define GDR_ABI_VERSION 2
 
 typedef enum {
   GDR_OK = 0,
@@ -83,7 +83,9 @@ typedef struct {
   int32_t b_kind;     /* gdr_gate */
   int32_t w_kind;     /* gdr_gate */
   int32_t order;      /* gdr_order */
-  int32_t reserved;   /* must be 0 */
+  int32_t qk_heads;   /* heads of q and k: 0 = `heads`; otherwise `heads` must be a multiple of
+                         it, and value head h reads q / k head h / (heads / qk_heads) (grouped
+                         key / value heads) */
 } gdr_problem;
 
 /* ABI version of the loaded library (GDR_ABI_VERSION). */

@@ -32,7 +32,7 @@ def test_struct_layout_matches_header():
 
 
 def test_version_and_status_strings():
-    assert N.abi_version() == 1
+    assert N.abi_version() == 2
     for s in range(6):
         assert N.status_string(s).startswith("GDR_")
     assert "unknown" in N.status_string(99)
@@ -61,7 +61,8 @@ def big_apart():
 
 @pytest.mark.parametrize("field,value,status", [
     ("struct_size", 8, N.GDR_ERR_INVALID_ARGUMENT),
-    ("reserved", 1, N.GDR_ERR_INVALID_ARGUMENT),
+    ("qk_heads", 2, N.GDR_ERR_INVALID_ARGUMENT),   # 3 value heads are not a multiple of 2
+    ("qk_heads", -1, N.GDR_ERR_INVALID_ARGUMENT),
     ("io_dtype", 7, N.GDR_ERR_INVALID_ARGUMENT),
     ("alpha_kind", 3, N.GDR_ERR_INVALID_ARGUMENT),
     ("order", 2, N.GDR_ERR_INVALID_ARGUMENT),

@@ -260,3 +260,49 @@ def test_marked_call_matches_plain_call(dev, kind, dtype):
     assert t_a >= 0.0 and t_b > 0.0
     x = synth.make_prefill(wl)
     check(x, o2, S2, "erase_then_decay", TOL[dtype], "marked %s %s" % (kind, dtype))
+
+
+# ------------------------------------------------------------------ grouped key / value heads
+
+
+def grouped(x, G):
+    """Inputs whose q and k have H / G heads (value head h reads q / k head h // G): the kernel's
+    copy keeps every G-th q / k head, the oracle's repeats those G times."""
+    xq = dict(x)
+    for n in ("q", "k"):
+        xq[n] = x[n][:, :, ::G].contiguous()
+    xr = dict(x)
+    for n in ("q", "k"):
+        xr[n] = xq[n].repeat_interleave(G, dim=2)
+    return xq, xr
+
+
+@pytest.mark.parametrize("kind,D,dtype", [("gdn", 128, "bf16"), ("kda", 64, "bf16"), ("gdn2", 128, "bf16"),
+                                          ("mamba2", 64, "bf16"), ("gdn", 16, "bf16"), ("gdn2", 32, "fp32")])
+def test_prefill_grouped_heads(dev, kind, D, dtype):
+    import gated_delta_rule_71_amd as gdr
+    from gpu_util import to_dev
+    wl = case(kind, B=2, H=4, T=200, D=D, dtype=dtype)
+    say("grouped heads", kind, D, dtype)
+    xq, xr = grouped(synth.make_prefill(wl), 2)
+    g = to_dev(xq, dev)
+    o, S = gdr.chunk_fwd(g["q"], g["k"], g["v"], g["log_alpha"], g["b"], g["w"], g["S0"])
+    torch.cuda.synchronize()
+    check(xr, o, S, "erase_then_decay", TOL[dtype], "grouped %s d%d %s" % (kind, D, dtype))
+
+
+def test_decode_grouped_heads(dev):
+    import gated_delta_rule_71_amd as gdr
+    from gpu_util import to_dev
+    wl = case("gdn2", B=3, H=4, T=5, D=128, s0=0.02)
+    xq, xr = grouped(synth.make_prefill(wl), 4)
+    g = to_dev(xq, dev)
+    S = g["S0"].clone()
+    outs = []
+    for t in range(wl.T):
+        sl = lambda a: None if a is None else a[:, t:t + 1].contiguous()
+        outs.append(gdr.decode_step(sl(g["q"]), sl(g["k"]), sl(g["v"]), sl(g["log_alpha"]),
+                                    sl(g["b"]), sl(g["w"]), S))
+    torch.cuda.synchronize()
+    o = torch.cat(outs, dim=1)
+    check(xr, o, S, "erase_then_decay", TOL["bf16"], "grouped decode")
