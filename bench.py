@@ -2,7 +2,7 @@
 chunk 64, bf16 inputs, fp32 state) and the Gated DeltaNet-2 decode step (256 x 32 states, 1000
 steps), on one MI355X, through the C ABI.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gdn|kda|gdn2|mamba2]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gdn|kda|gdn2|mamba2|gdn_gqa]
                     [--decode-steps N] [--no-cpu-baseline] [--no-decode]
 
 Prints ONE JSON line.  `value` is prefill tokens/s (B*T / time per call) with inputs resident in
@@ -46,8 +46,9 @@ def prefill_bytes(wl):
     """Minimal HBM bytes of one prefill call: every input read once, o and S_T written once."""
     es = 2 if wl.dtype == "bf16" else 4
     rows = wl.B * wl.T * wl.H
+    qk_rows = wl.B * wl.T * (wl.HK or wl.H)
     gate = {"none": 0, "scalar": 1, "channel": wl.DK}
-    n = rows * (2 * wl.DK + 2 * wl.DV) * es  # q, k, v, o
+    n = qk_rows * 2 * wl.DK * es + rows * 2 * wl.DV * es  # q, k; v, o
     n += rows * gate[wl.alpha] * es
     if wl.shared_beta:
         n += rows * es if wl.b != "none" else 0
@@ -213,7 +214,7 @@ def cpu_baseline(wl):
     import synth
     cores = len(os.sched_getaffinity(0))
     threads = min(cores, 16)
-    x = synth.make_prefill(wl)
+    x = synth.expand_heads(synth.make_prefill(wl), wl.H)
     t0 = time.perf_counter()
     oracle.forward(x["q"], x["k"], x["v"], x["log_alpha"], x["b"], x["w"], x["S0"], n_threads=threads)
     dt = time.perf_counter() - t0
@@ -235,7 +236,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="gdn", choices=["gdn", "kda", "gdn2", "mamba2"])
+    ap.add_argument("--workload", default="gdn", choices=["gdn", "kda", "gdn2", "mamba2", "gdn_gqa"])
     ap.add_argument("--decode-steps", type=int, default=None)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -282,7 +283,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded; shapes of the %s workload)" % wl.name,
-        "config": {"workload": wl.name, "batch": wl.B, "heads": wl.H, "seq_len": wl.T,
+        "config": {"workload": wl.name, "batch": wl.B, "heads": wl.H, "qk_heads": wl.HK or wl.H,
+                   "seq_len": wl.T,
                    "d_k": wl.DK, "d_v": wl.DV, "chunk": 64, "state": "fp32",
                    "decay": wl.alpha, "erase_gate": wl.b, "write_gate": wl.w},
         "kernel_ms": {"mean": pf["mean_ms"], "median": pf["median_ms"], "p10": pf["p10_ms"],

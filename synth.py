@@ -47,6 +47,7 @@ class Workload:
     s0_std: float       # 0 -> S0 = 0
     seed: int
     steps: int = 0      # decode workloads: consecutive steps
+    HK: int = 0         # q / k heads (0: H); H a multiple of HK (grouped key / value heads)
 
     def with_(self, **kw):
         return replace(self, **kw)
@@ -64,6 +65,9 @@ WORKLOADS = {
     # the Gated DeltaNet shapes; w = 1
     "mamba2": Workload("mamba2", 4, 16, 4096, 128, 128, "bf16", SCALAR, NONE, NONE, False, -2.0, 0.0,
                        1005),
+    # Gated DeltaNet gates with grouped heads: 32 value heads sharing 16 query / key heads
+    "gdn_gqa": Workload("gdn_gqa", 4, 32, 4096, 128, 128, "bf16", SCALAR, SCALAR, SCALAR, True, -2.0,
+                        0.0, 1006, HK=16),
 }
 
 
@@ -87,7 +91,7 @@ def _l2rows(x):
 
 def make_prefill(wl, seed=None):
     """Host-side inputs for one prefill call.  Returns a dict of CPU torch tensors:
-    q, k [B,T,H,DK]; v [B,T,H,DV]; log_alpha, b, w ([B,T,H], [B,T,H,D] or None) in the
+    q, k [B,T,HK or H,DK]; v [B,T,H,DV]; log_alpha, b, w ([B,T,H], [B,T,H,D] or None) in the
     workload's I/O dtype; S0 [B,H,DK,DV] float32 or None."""
     import torch
     rng = np.random.default_rng(wl.seed if seed is None else seed)
@@ -97,8 +101,9 @@ def make_prefill(wl, seed=None):
     def normal(*shape):
         return rng.standard_normal(shape, dtype=f32)
 
-    q = _l2rows(normal(B, T, H, DK))
-    k = _l2rows(normal(B, T, H, DK))
+    HQ = wl.HK or H
+    q = _l2rows(normal(B, T, HQ, DK))
+    k = _l2rows(normal(B, T, HQ, DK))
     v = normal(B, T, H, DV)
     gshape = {NONE: None, SCALAR: (B, T, H), CHANNEL: (B, T, H, DK)}
     la = None if wl.alpha == NONE else _neg_softplus(normal(*gshape[wl.alpha]) + f32(wl.mu)).astype(f32)
@@ -123,6 +128,17 @@ def make_prefill(wl, seed=None):
                S0=None if S0 is None else torch.from_numpy(S0))
     if wl.shared_beta and b is not None and w is not None:
         out["w"] = out["b"]  # one beta buffer serves as both gates
+    return out
+
+
+def expand_heads(x, H):
+    """q and k repeated per group so that every value head has its own copy (value head h reads
+    q / k head h // (H // HK)); other entries unchanged."""
+    out = dict(x)
+    for n in ("q", "k"):
+        G = H // x[n].shape[2]
+        if G > 1:
+            out[n] = x[n].repeat_interleave(G, dim=2)
     return out
 
 

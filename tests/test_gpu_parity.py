@@ -204,14 +204,14 @@ def test_decode_workload_subset(dev):
 # ------------------------------------------------------------------ full-size prefill workloads
 
 
-@pytest.mark.parametrize("name", ["gdn", "mamba2"])
+@pytest.mark.parametrize("name", ["gdn", "mamba2", "gdn_gqa"])
 def test_scalar_decay_workloads_full(dev, name):
     wl = synth.WORKLOADS[name]
     say("%s workload" % name, wl)
     x = synth.make_prefill(wl)
     o, S = run_gpu_prefill(x, dev)
     torch.cuda.synchronize()
-    check(x, o, S, "erase_then_decay", TOL["bf16"], "%s full" % name)
+    check(synth.expand_heads(x, wl.H), o, S, "erase_then_decay", TOL["bf16"], "%s full" % name)
 
 
 @pytest.mark.parametrize("name", ["kda", "gdn2"])
