@@ -425,7 +425,7 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, unsigned cha
 // 0, 1, 3 and 4 vary); the key takes those bits so that the 16 pieces read land in 16 distinct
 // bank groups (rows of 256, 128 or 64 bytes).
 template <int NCHR, bool PERM>
-__device__ __forceinline__ int swz_key(int row) {
+__host__ __device__ constexpr inline int swz_key(int row) {
   if constexpr (NCHR == 16) return PERM ? ((row & 3) | ((row >> 1) & 12)) : (row & 15);
   else if constexpr (NCHR == 8) return PERM ? (((row >> 1) & 1) | ((row >> 2) & 6)) : ((row >> 1) & 7);
   else if constexpr (NCHR == 4) return PERM ? ((row >> 3) & 3) : ((row >> 2) & 3);
@@ -457,6 +457,41 @@ __device__ __forceinline__ void dma_rows(__amdgpu_buffer_rsrc_t r, unsigned char
 #pragma unroll
   for (int i = 0; i < NPIECE / 64; ++i) lds_dma16(r, lds + 1024 * i, off[i]);
 }
+
+// The same copies with fewer lane registers: instruction i covers rows (64 / NCHR) i .., and a
+// lane's piece pattern repeats every P instructions (P = 1, 2 or 4 for these keys), so a lane keeps
+// P offsets and instruction i adds the uniform row offset of i - i mod P as the scalar offset.
+// (instruction i covers rows R = (64 / NCHR) i + lane / NCHR; the key reads row bits 0-3 (NAT,
+// NCHR 16), 0, 1, 3, 4 (PERM, 16), 1-3 (NAT, 8), 1, 3, 4 (PERM, 8), 2, 3 (NAT, 4), 3, 4 (PERM, 4)
+// or 3 (2), so the bits of R above lane / NCHR that it reads fix the period)
+template <int NCHR, bool PERM, int NPIECE>
+struct DmaPlan {
+  static_assert(NPIECE % 64 == 0, "whole instructions only");
+  static constexpr int NI = NPIECE / 64;
+  // (instruction i covers rows (64 / NCHR) i + lane / NCHR; the key reads row bits 0-3 (NAT,
+  // NCHR 16), 0, 1, 3, 4 (PERM, 16), 1-3 (NAT, 8), 1, 3, 4 (PERM, 8), 2, 3 (NAT, 4), 3, 4 (PERM, 4)
+  // or 3 (2), so the row bits above lane / NCHR that it reads fix the period)
+  static constexpr int PERIOD = NCHR == 16 ? (PERM ? 8 : 4) : NCHR == 8 ? (PERM ? 4 : 2) : NCHR == 4 ? (PERM ? 2 : 1) : 1;
+  static constexpr int P = PERIOD < NI ? PERIOD : NI;
+  // (a fixed bound: a bound that depends on the template arguments here keeps the host pass of
+  // hipcc from emitting the launch stubs of kernels that hold a plan)
+  uint32_t off[8];
+  static_assert(P <= 8, "period above the fixed bound");
+  __device__ __forceinline__ void init(uint32_t stride, int lane) {
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+      const int s = 64 * i + lane, row = s / NCHR, piece = (s % NCHR) ^ swz_key<NCHR, PERM>(row);
+      off[i] = static_cast<uint32_t>(row) * stride + static_cast<uint32_t>(piece) * 16u;
+    }
+  }
+  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t r, unsigned char* lds, uint32_t stride) const {
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r, (__attribute__((address_space(3))) void*)(lds + 1024 * i), 16, off[i % P],
+          static_cast<int>(static_cast<uint32_t>((64 / NCHR) * (i - i % P)) * stride), 0, 0);
+  }
+};
 
 // Byte address of piece `piece` of row `row` of such an array.
 template <int NCHR, bool PERM>

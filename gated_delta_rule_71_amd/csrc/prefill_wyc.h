@@ -21,9 +21,17 @@
 //
 // The Gram products use the same factors split around G_ref = G_31 (e^{G_t - G_ref} on row
 // operands, e^{G_ref - G_i} on column operands) so that every factor stays inside the fp32
-// range; W, Qhat, Pbar and Kbar themselves only carry e^{non-positive} factors.  A chunk whose
-// prefix sums span more than kSpanLimit nats (or are not finite) is flagged, and the state kernel
-// runs it token by token from the raw inputs instead (exact for any gate values).
+// range; W, Qhat, Pbar and Kbar themselves only carry e^{non-positive} factors.
+//
+// Substituting R into the read-out and the update turns each chunk into an affine map of the
+// state it starts from (R is never formed in the state kernel):
+//   S' = e^{G_n} . S + A' S + D,   O = Q' S + Z',
+//   A' = -Pbar^T W,  D = Kbar^T X - Pbar^T Y,  Q' = Qhat - M_QP W,  Z' = Z - M_QP Y
+// (MODE 1: Pbar -> Kbar, M_QP -> M and no Kbar^T X, Z terms).  The chunk-local kernel forms these
+// four matrices; the state kernel then does two products per chunk.  A chunk whose prefix sums
+// span more than kWycSpanLimit nats (or are not finite) is flagged, and the chunk-local kernel
+// forms its four matrices by running the recurrence over the chunk token by token in fp32 from
+// the identity (A) and from zero (D) instead: exact for any gate values.
 #pragma once
 #include "gdr_common.h"
 #include "mfma.h"
@@ -42,16 +50,12 @@ struct WycArgs {
   const float* S0;
   bf16_t* o;
   float* S_T;
-  // workspace, per chunk index cix = state * nch + chunk
-  __bf16* W;   // [cix][64][dk]  W
-  __bf16* Qp;  // [cix][64][dk]  Qhat (unsplit)
-  __bf16* Pn;  // [cix][dk][64]  -Pbar^T (MODE 1: -Kbar^T)
-  __bf16* Kb;  // [cix][dk][64]  Kbar^T (MODE 2)
-  __bf16* Mn;  // [cix][64][64]  -M_QP (MODE 1: -M), zero above the diagonal
-  __bf16* Y;   // [cix][dv][64]  Y^T
-  __bf16* Z;   // [cix][64][dv]  Z (MODE 2)
-  __bf16* Xt;  // [cix][dv][64]  X^T (MODE 2)
-  float* Egn;  // [cix][dk]      e^{G_n}
+  // workspace, per chunk index cix = state * nch + chunk: the affine chunk map
+  __bf16* Qd;  // [cix][64][dk]  Q'
+  __bf16* Ad;  // [cix][dk][dk]  A'
+  __bf16* Dt;  // [cix][dv][dk]  D^T
+  __bf16* Zd;  // [cix][64][dv]  Z'
+  float* Egn;  // [cix][dk + 4]  e^{G_n}, then the flag (as int) and 3 unused
   int* flag;   // [cix]          1: exact token path
   int64_t T, H, DV, nch;
   int b_kind, w_kind;
@@ -92,7 +96,85 @@ struct WycPrepLayout {
   static constexpr int oF = oSEG + NSEG * DK * 4;           // fp32 G_ref, e^{G_ref}, e^{G_n - G_ref} [DK] each; flag
   static constexpr int total = oF + (3 * DK + 4) * 4;
   static constexpr bool fits = total <= kLdsLimit;
+  static_assert(oF % 16 == 0, "the per-channel factors are read as float4");
 };
+
+// The affine map of a flagged chunk from the recurrence itself, token by token in fp32: thread
+// j < dk carries column j of the transition product A (started from the identity; its outputs
+// q_t A_t are row t of Q'), threads 128 + j carry value column v = j, j + 128 of the state D
+// started from zero (outputs q_t D_t: Z').  Every lane reads the same raw row at once.  Rows past
+// the last token are zero (alpha = 1, no erase, no write), so all 64 rows run.
+template <int DK, int LDT, int LDX, bool TWO>
+__device__ __forceinline__ void wyc_exact_chunk(const WycArgs& a, int64_t cix, const __bf16* rQ,
+                                                const __bf16* rK, const __bf16* rC, const __bf16* rL,
+                                                const __bf16* tX, float egn_own, int tid) {
+  constexpr int C = 64;
+  const int64_t DV = a.DV;
+  // one column s through the chunk; col_x < 0: no write (the transition); y_t = q_t s_t to yout
+  auto run = [&](float (&s)[DK], int col_x, __bf16* yout, int64_t ypitch) {
+    for (int t = 0; t < C; ++t) {
+      float r = 0.f;  // c_t s (after the decay in MODE 1)
+#pragma unroll
+      for (int p = 0; p < DK / 8; ++p) {
+        float c8[8];
+        load8f(reinterpret_cast<const bf16_t*>(rC + t * LDT + 8 * p), c8);
+        if (!TWO) {
+          float l8[8];
+          load8f(reinterpret_cast<const bf16_t*>(rL + t * DK + 8 * p), l8);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) s[8 * p + e] *= __expf(l8[e]);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) r += c8[e] * s[8 * p + e];
+      }
+      const float x = col_x >= 0 ? static_cast<float>(tX[t * LDX + col_x]) : 0.f;
+      float y = 0.f;
+#pragma unroll
+      for (int p = 0; p < DK / 8; ++p) {
+        float k8[8], q8[8], l8[8];
+        load8f(reinterpret_cast<const bf16_t*>(rK + t * LDT + 8 * p), k8);
+        load8f(reinterpret_cast<const bf16_t*>(rQ + t * LDT + 8 * p), q8);
+        if (TWO) load8f(reinterpret_cast<const bf16_t*>(rL + t * DK + 8 * p), l8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float sv = s[8 * p + e] - k8[e] * r;
+          if (TWO) sv *= __expf(l8[e]);
+          sv += k8[e] * x;
+          s[8 * p + e] = sv;
+          y += q8[e] * sv;
+        }
+      }
+      yout[t * ypitch] = static_cast<__bf16>(y);
+    }
+  };
+  const int j = tid & 127;
+  if (tid < 128) {
+    if (j < DK) {
+      float s[DK];
+#pragma unroll
+      for (int i = 0; i < DK; ++i) s[i] = i == j ? 1.f : 0.f;
+      run(s, -1, a.Qd + cix * C * DK + j, DK);
+      __bf16* Ao = a.Ad + cix * DK * DK + j;  // A' = A - diag(e^{G_n}), column j (egn_own: channel j)
+#pragma unroll
+      for (int i = 0; i < DK; ++i) Ao[i * DK] = static_cast<__bf16>(s[i] - (i == j ? egn_own : 0.f));
+    }
+  } else {
+    for (int v = j; v < DV; v += 128) {
+      float s[DK];
+#pragma unroll
+      for (int i = 0; i < DK; ++i) s[i] = 0.f;
+      run(s, v, a.Zd + cix * C * DV + v, DV);
+      __bf16* Do = a.Dt + (cix * DV + v) * DK;  // row v of D^T
+#pragma unroll
+      for (int p = 0; p < DK / 8; ++p) {
+        bf16x8 d8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) d8[e] = static_cast<__bf16>(s[8 * p + e]);
+        *reinterpret_cast<bf16x8*>(Do + 8 * p) = d8;
+      }
+    }
+  }
+}
 
 template <int DK, int DVP, int MODE>
 __global__ __launch_bounds__(256) void wyc_prep_kernel(WycArgs a) {
@@ -104,7 +186,7 @@ __global__ __launch_bounds__(256) void wyc_prep_kernel(WycArgs a) {
   constexpr bool TWO = L::TWO;
   constexpr int C = L::C, LDT = L::LDT, LDX = L::LDX, LDD = L::LDD, LDA = L::LDA, LDI = L::LDI,
                 LDL = L::LDL;
-  constexpr int NCG = L::NCG, NSEG = L::NSEG, TPS = L::TPS, NKB = DK / 32;
+  constexpr int NCG = L::NCG, NSEG = L::NSEG, TPS = L::TPS, NKB = DK / 32, NTD = DK / 16;
 
   __shared__ __attribute__((aligned(32))) unsigned char smem[L::total];
   __bf16* tQ = reinterpret_cast<__bf16*>(smem + L::oQ);
@@ -221,6 +303,7 @@ __global__ __launch_bounds__(256) void wyc_prep_kernel(WycArgs a) {
   }
   if (tid == 0) sFlag[0] = 0;
   lds_barrier();
+  float egn_own = 0.f;  // e^{G_n} of channel tid
   if (tid < DK) {
     float run = 0.f;
     for (int s = 0; s < NSEG; ++s) {
@@ -232,14 +315,52 @@ __global__ __launch_bounds__(256) void wyc_prep_kernel(WycArgs a) {
     fRef[tid] = ref;
     fEref[tid] = __expf(ref);
     fEgr[tid] = __expf(run - ref);
-    a.Egn[cix * DK + tid] = __expf(run);
-    if (fmaxf(fabsf(ref), fabsf(run - ref)) > kWycSpanLimit || !(run == run)) sFlag[0] = 1;
+    egn_own = __expf(run);
+    a.Egn[cix * (DK + 4) + tid] = egn_own;
+    if (!(fabsf(ref) <= kWycSpanLimit && fabsf(run - ref) <= kWycSpanLimit)) sFlag[0] = 1;  // NaN, inf too
   }
   GDR_PMARK(0);
   lds_barrier();
   const bool robust = sFlag[0] != 0;
-  if (tid == 0) a.flag[cix] = robust ? 1 : 0;
-  if (robust) return;  // the state kernel runs this chunk token by token from the raw inputs
+  if (tid < 4) {
+    reinterpret_cast<int*>(a.Egn + cix * (DK + 4) + DK)[tid] = tid == 0 && robust ? 1 : 0;
+    if (tid == 0) a.flag[cix] = robust ? 1 : 0;
+  }
+  if (robust) {
+    // raw rows into LDS: q, k, c = b . k and log alpha (bf16) beside the x rows
+    __bf16* rQ = tQ;
+    __bf16* rK = tK;
+    __bf16* rC = tC;
+    __bf16* rL = gA;  // [64][DK], inside the (here unused) Gram and inverse arrays
+    static_assert(L::oI - L::oA >= C * DK * 2, "log alpha rows need the Gram and inverse arrays");
+    if (act) {
+#pragma unroll
+      for (int u = 0; u < TPS; ++u) {
+        const int t = ts * TPS + u;
+        float k[8], cc[8];
+        load8f(reinterpret_cast<const bf16_t*>(&pk[u]), k);
+        if (a.b_kind == kChannel) {
+          load8f(reinterpret_cast<const bf16_t*>(&pb[u]), cc);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) cc[j] *= k[j];
+        } else {
+          const float bs = a.b_kind == kScalar ? bf16_to_f32(pbs[u]) : 0.f;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) cc[j] = bs * k[j];
+        }
+        bf16x8 cb;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) cb[j] = static_cast<__bf16>(cc[j]);
+        *reinterpret_cast<uint4*>(rQ + t * LDT + d0) = pq[u];
+        *reinterpret_cast<uint4*>(rK + t * LDT + d0) = pk[u];
+        *reinterpret_cast<bf16x8*>(rC + t * LDT + d0) = cb;
+        *reinterpret_cast<uint4*>(rL + t * DK + d0) = pl[u];
+      }
+    }
+    lds_barrier();
+    wyc_exact_chunk<DK, LDT, LDX, TWO>(a, cix, rQ, rK, rC, rL, tX, egn_own, tid);
+    return;
+  }
 
   // ---- operands: split Gram operands into LDS; Qhat, -Pbar^T, Kbar^T out to the workspace ----
   if (act) {
@@ -266,7 +387,7 @@ __global__ __launch_bounds__(256) void wyc_prep_kernel(WycArgs a) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) cc[j] = bs * k[j];
       }
-      bf16x8 oq, oc, ok, op, oqp;
+      bf16x8 oq, oc, ok, op;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const float G = G8[u][j] + off[j];
@@ -274,7 +395,6 @@ __global__ __launch_bounds__(256) void wyc_prep_kernel(WycArgs a) {
         const float er = __builtin_amdgcn_rcpf(eq);   // e^{G_ref - G_t}
         oq[j] = static_cast<__bf16>(q[j] * eq);
         ok[j] = static_cast<__bf16>(k[j] * er);
-        oqp[j] = static_cast<__bf16>(q[j] * eq * eref[j]);  // q e^{G_t}
         if (TWO) {
           const float ep = __expf(G - la8[u][j] - ref[j]);  // e^{G_{t-1} - G_ref}
           const float epr = __builtin_amdgcn_rcpf(ep);
@@ -288,7 +408,6 @@ __global__ __launch_bounds__(256) void wyc_prep_kernel(WycArgs a) {
       *reinterpret_cast<bf16x8*>(tC + t * LDT + d0) = oc;
       *reinterpret_cast<bf16x8*>(tK + t * LDT + d0) = ok;
       if (TWO) *reinterpret_cast<bf16x8*>(tP + t * LDT + d0) = op;
-      *reinterpret_cast<bf16x8*>(a.Qp + (cix * C + t) * DK + d0) = oqp;
     }
   }
   // tiles above the diagonal of -M, L_K and M_QK are never written by the Gram phase but are
@@ -373,48 +492,11 @@ __global__ __launch_bounds__(256) void wyc_prep_kernel(WycArgs a) {
   GDR_PMARK(2);
   lds_barrier();
 
-  // ---- diagonal inverses (waves 0-1) | -M_QP out (waves 2-3) ----
-  if (wave < 2) {
-    if (lane < 32) wy_diag_inverses<LDL, LDI>(Ld, dInv, wave, lane, l16);
-  } else {
-    __bf16* Mo = a.Mn + cix * C * C;
-    for (int item = tid - 128; item < C * 8; item += 128) {
-      const int r = item >> 3, part = item & 7;
-      *reinterpret_cast<uint4*>(Mo + r * C + part * 8) = *reinterpret_cast<const uint4*>(gM + r * LDD + part * 8);
-    }
-    if (TWO) {  // X^T out: item = column * 8 + part holds tokens 8 part .. 8 part + 7
-      __bf16* Xo = a.Xt + cix * DV * C;
-      for (int item = tid - 128; item < DV * 8; item += 128) {
-        const int col = item >> 3, part = item & 7;
-        bf16x8 xv;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) xv[e] = tX[(8 * part + e) * LDX + col];
-        *reinterpret_cast<bf16x8*>(Xo + col * C + 8 * part) = xv;
-      }
-    }
-  }
+  // ---- diagonal inverses (waves 0-1) ----
+  if (wave < 2 && lane < 32) wy_diag_inverses<LDL, LDI>(Ld, dInv, wave, lane, l16);
   GDR_PMARK(3);
   lds_barrier();
 
-  // ---- -Pbar^T (and Kbar^T) out: the split Phat (Khat) columns times e^{G_n - G_ref}; 16-byte
-  // pieces of channel rows, so every store instruction writes whole row segments ----
-  {
-    __bf16* Po = a.Pn + cix * DK * C;
-    __bf16* Ko = a.Kb + cix * DK * C;
-    const __bf16* src = TWO ? tP : tK;
-    for (int item = tid; item < DK * 8; item += 256) {
-      const int d = item >> 3, part = item & 7;
-      const float f = fEgr[d];
-      bf16x8 pv, kv;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        pv[e] = static_cast<__bf16>(-static_cast<float>(src[(8 * part + e) * LDT + d]) * f);
-        if (TWO) kv[e] = static_cast<__bf16>(static_cast<float>(tK[(8 * part + e) * LDT + d]) * f);
-      }
-      *reinterpret_cast<bf16x8*>(Po + d * C + 8 * part) = pv;
-      if (TWO) *reinterpret_cast<bf16x8*>(Ko + d * C + 8 * part) = kv;
-    }
-  }
   // ---- T = (I + L_P)^{-1}: wave j solves column block j on the identity ----
   {
     const int j = wave;
@@ -444,8 +526,9 @@ __global__ __launch_bounds__(256) void wyc_prep_kernel(WycArgs a) {
   GDR_PMARK(4);
   lds_barrier();
 
-  // ---- products, as transposed tiles so that each lane stores four consecutive columns ----
-  // B fragments of T^T (and of L_K^T, M_QK^T) are pair fragments of the rows of T (L_K, M_QK).
+  // ---- the affine chunk map ----
+  // B fragments of T^T (and of L_K^T, M_QK^T, -M^T) are pair fragments of the rows of T (L_K,
+  // M_QK, -M); every column tile below is one wave's, kept in registers from product to product.
   auto row_frags = [&](const __bf16* m, F8* f) {  // 6 fragments: lower-triangular 64 x 64
 #pragma unroll
     for (int ta = 0, n = 0; ta < 4; ++ta) {
@@ -453,104 +536,158 @@ __global__ __launch_bounds__(256) void wyc_prep_kernel(WycArgs a) {
       if (ta >= 2) f[n++] = lds_pair_frag_k<C>(m + (16 * ta + l16) * LDD, 32, g);
     }
   };
-  // column tile of a token-major LDS array as A fragments: 8 tokens (tile-pair order) of column
-  // col per lane, times `scale`
+  // column tile of a token-major LDS array as A (or B) fragments: 8 tokens (tile-pair order) of
+  // column col per lane, times `scale` (two transposing reads per 32-token block: source lane
+  // (a, m) = (l16 & 3, l16 >> 2) of group g points at token 32 ks + 16 h + 4 g + m, columns
+  // col - l16 + 4 a ..)
   auto col_frags = [&](const __bf16* base, int pitch, int col, float scale, F8* f) {
+    const int c0 = col - l16 + 4 * (l16 & 3), m_ = l16 >> 2;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int t = 32 * ks + 4 * g + (e & 3) + (e >> 2) * 16;
-        f[ks][e] = static_cast<__bf16>(static_cast<float>(base[t * pitch + col]) * scale);
+      for (int h = 0; h < 2; ++h) {
+        const bf16x4 v = lds_read_tr4(reinterpret_cast<const unsigned char*>(
+            base + (32 * ks + 16 * h + 4 * g + m_) * pitch + c0));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) f[ks][4 * h + e] = static_cast<__bf16>(static_cast<float>(v[e]) * scale);
       }
   };
   // D^T tiles of (lower-triangular 64 x 64 B-side matrix) x (A-side 64 x 16 tile): out[ta] lane
   // holds D[token 16 ta + l16][column 4 g + i]
-  auto tr_product = [&](const F8* af, const F8* bf, bool strict, f32x4* out) {
+  auto tr_product = [&](const F8* af, const F8* bf, f32x4* out, bool acc) {
 #pragma unroll
     for (int ta = 0, n = 0; ta < 4; ++ta) {
-      out[ta] = MM::mma8(af[0], bf[n++], zero4());
+      out[ta] = MM::mma8(af[0], bf[n++], acc ? out[ta] : zero4());
       if (ta >= 2) out[ta] = MM::mma8(af[1], bf[n++], out[ta]);
     }
-    (void)strict;
   };
-  // upright tiles of (lower-triangular 64 x 64 A-side matrix) x (64 x 16 B-side tile): out[ta] lane
-  // holds D[token 16 ta + 4 g + i][column l16]
-  auto up_product = [&](const F8* af, const F8* bf, f32x4* out) {
+  // upright tiles of (lower-triangular 64 x 64 A-side matrix) x (64 x 16 B-side tile), as the
+  // two pair fragments (tokens as k) of the product: lane holds tokens 32 ks + 4 g + (e & 3) +
+  // 16 (e >> 2) of column l16, times sgn
+  auto up_frags = [&](const F8* af, const F8* bf, float sgn, F8* out) {
+    f32x4 D[4];
 #pragma unroll
     for (int ta = 0, n = 0; ta < 4; ++ta) {
-      out[ta] = MM::mma8(af[n++], bf[0], zero4());
-      if (ta >= 2) out[ta] = MM::mma8(af[n++], bf[1], out[ta]);
+      D[ta] = MM::mma8(af[n++], bf[0], zero4());
+      if (ta >= 2) D[ta] = MM::mma8(af[n++], bf[1], D[ta]);
     }
+    if (sgn != 1.f)
+#pragma unroll
+      for (int ta = 0; ta < 4; ++ta)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) D[ta][i] *= sgn;
+    out[0] = acc_pair_frag<__bf16>(D[0], D[1]);
+    out[1] = acc_pair_frag<__bf16>(D[2], D[3]);
   };
-  // upright tiles out as a [column][64] array: four consecutive tokens per 8-byte store
-  auto store_up_t = [&](__bf16* dst, int col0c, const f32x4* t4, float sgn) {
+  auto store4 = [&](__bf16* dst, const f32x4& v) {
+    bf16x4 ob;
 #pragma unroll
-    for (int ta = 0; ta < 4; ++ta) {
-      bf16x4 ob;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) ob[i] = static_cast<__bf16>(t4[ta][i] * sgn);
-      *reinterpret_cast<bf16x4*>(dst + (col0c + l16) * C + 16 * ta + 4 * g) = ob;
-    }
-  };
-  auto store_tr = [&](__bf16* dst, int64_t pitch, int col0c, const f32x4* t4, float sgn) {
-#pragma unroll
-    for (int ta = 0; ta < 4; ++ta) {
-      bf16x4 ob;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) ob[i] = static_cast<__bf16>(t4[ta][i] * sgn);
-      *reinterpret_cast<bf16x4*>(dst + (16 * ta + l16) * pitch + col0c + 4 * g) = ob;
-    }
+    for (int i = 0; i < 4; ++i) ob[i] = static_cast<__bf16>(v[i]);
+    *reinterpret_cast<bf16x4*>(dst) = ob;
   };
   {
-    F8 tfr[6];
-    row_frags(tT, tfr);
-    // W = T Chat (unsplit: the split Chat times e^{G_ref} per channel)
-    __bf16* Wo = a.W + cix * C * DK;
-    for (int ct = wave; ct < DK / 16; ct += 4) {
-      const int col = 16 * ct + l16;
-      F8 cf[2];
-      col_frags(tC, LDT, col, fEref[col], cf);
-      f32x4 D[4];
-      tr_product(cf, tfr, false, D);
-      store_tr(Wo, DK, 16 * ct, D, 1.f);
-    }
+    // (1) this wave's W column tiles (W = T Chat, the split Chat times e^{G_ref} per channel) as
+    //     pair fragments, and Q' = Qhat - M W from them: lane holds Q'[16 ta + l16][16 ct + 4 g + i]
+    //     (Qhat = split Q times e^{G_ref})
+    // (2) this wave's value column tiles X and Y = T L_K X (MODE 1: -T X) as pair fragments, and
+    //     Z' = M_QK X - M Y: lane holds Z'[16 ta + l16][16 cv + 4 g + i]
+    // (3) channel tile by channel tile, -Pbar (MODE 1: -Kbar) and Kbar with channels as rows, then
+    //     A' = -Pbar^T W:          lane holds A'[16 tl + l16][16 ct + 4 g + i]
+    //     D = Kbar^T X - Pbar^T Y: lane holds D[16 tl + 4 g + i][16 cv + l16], i.e. row 16 cv + l16
+    //                              of D^T, four consecutive channels
+    constexpr int WPW = (NTD + 3) / 4;        // W tiles per wave (at most)
+    constexpr int VPW = (DVP / 16 + 3) / 4;   // value tiles per wave (at most)
     const int nct_u = static_cast<int>(DV / 16);
-    __bf16* Yo = a.Y + cix * C * DV;
-    if (TWO) {
-      F8 lkf[6], mqf[6];
-      row_frags(gLK, lkf);
-      row_frags(gMQK, mqf);
-      __bf16* Zo = a.Z + cix * C * DV;
-      for (int ct = wave; ct < nct_u; ct += 4) {
-        const int col = 16 * ct + l16;
-        F8 xf[2];
-        col_frags(tX, LDX, col, 1.f, xf);
-        // L_K X as upright tiles (lane: rows 16 ta + 4 g + i, column col), whose tile pairs are
-        // the A fragments of (T L_K X)^T
-        f32x4 LKX[4];
+    F8 wf[WPW][2], xf[VPW][2], yf[VPW][2];
+    {
+      F8 tfr[6], mnf[6];
+      row_frags(tT, tfr);
+      row_frags(gM, mnf);
+      __bf16* Qo = a.Qd + cix * C * DK;
 #pragma unroll
-        for (int ta = 0, n = 0; ta < 4; ++ta) {
-          LKX[ta] = MM::mma8(lkf[n++], xf[0], zero4());
-          if (ta >= 2) LKX[ta] = MM::mma8(lkf[n++], xf[1], LKX[ta]);
+      for (int w = 0; w < WPW; ++w) {
+        const int ct = wave + 4 * w;
+        if (ct < NTD) {
+          const int col = 16 * ct + l16;
+          F8 cf[2];
+          col_frags(tC, LDT, col, fEref[col], cf);
+          up_frags(tfr, cf, 1.f, wf[w]);
+          f32x4 Qt[4];
+          tr_product(wf[w], mnf, Qt, false);
+          const float4 er = *reinterpret_cast<const float4*>(fEref + 16 * ct + 4 * g);
+#pragma unroll
+          for (int ta = 0; ta < 4; ++ta) {
+            const bf16x4 q4 = *reinterpret_cast<const bf16x4*>(tQ + (16 * ta + l16) * LDT + 16 * ct + 4 * g);
+            Qt[ta][0] += static_cast<float>(q4[0]) * er.x;
+            Qt[ta][1] += static_cast<float>(q4[1]) * er.y;
+            Qt[ta][2] += static_cast<float>(q4[2]) * er.z;
+            Qt[ta][3] += static_cast<float>(q4[3]) * er.w;
+            store4(Qo + (16 * ta + l16) * DK + 16 * ct + 4 * g, Qt[ta]);
+          }
         }
-        F8 lf[2];
-        lf[0] = acc_pair_frag<__bf16>(LKX[0], LKX[1]);
-        lf[1] = acc_pair_frag<__bf16>(LKX[2], LKX[3]);
-        f32x4 D[4];
-        up_product(tfr, lf, D);
-        store_up_t(Yo, 16 * ct, D, 1.f);
-        tr_product(xf, mqf, false, D);
-        store_tr(Zo, DV, 16 * ct, D, 1.f);
       }
-    } else {
-      for (int ct = wave; ct < nct_u; ct += 4) {
-        const int col = 16 * ct + l16;
-        F8 xf[2];
-        col_frags(tX, LDX, col, 1.f, xf);
-        f32x4 D[4];
-        up_product(tfr, xf, D);
-        store_up_t(Yo, 16 * ct, D, -1.f);
+      GDR_PMARK(6);
+      F8 lkf[6], mqf[6];
+      if (TWO) {
+        row_frags(gLK, lkf);
+        row_frags(gMQK, mqf);
+      }
+      __bf16* Zo = a.Zd + cix * C * DV;
+#pragma unroll
+      for (int w = 0; w < VPW; ++w) {
+        const int cv = wave + 4 * w;
+        if (cv < nct_u) {
+          col_frags(tX, LDX, 16 * cv + l16, 1.f, xf[w]);
+          if (TWO) {
+            F8 lf[2];
+            up_frags(lkf, xf[w], 1.f, lf);
+            up_frags(tfr, lf, 1.f, yf[w]);
+          } else {
+            up_frags(tfr, xf[w], -1.f, yf[w]);
+          }
+          f32x4 Zt[4];
+          tr_product(yf[w], mnf, Zt, false);
+          if (TWO) tr_product(xf[w], mqf, Zt, true);
+#pragma unroll
+          for (int ta = 0; ta < 4; ++ta) store4(Zo + (16 * ta + l16) * DV + 16 * cv + 4 * g, Zt[ta]);
+        }
+      }
+    }
+    GDR_PMARK(7);
+    __bf16* Ao = a.Ad + cix * DK * DK;
+    __bf16* Do = a.Dt + cix * DV * DK;
+    const __bf16* pn_src = TWO ? tP : tK;
+#pragma unroll 2
+    for (int tl = 0; tl < NTD; ++tl) {
+      const int ch = 16 * tl + l16;
+      F8 pf[2], kf[2];
+      col_frags(pn_src, LDT, ch, -fEgr[ch], pf);
+      if (TWO) col_frags(tK, LDT, ch, fEgr[ch], kf);
+      f32x4 acc[WPW + VPW];
+#pragma unroll
+      for (int w = 0; w < WPW; ++w) {
+        acc[w] = MM::mma8(wf[w][0], pf[0], zero4());
+        acc[w] = MM::mma8(wf[w][1], pf[1], acc[w]);
+      }
+#pragma unroll
+      for (int w = 0; w < VPW; ++w) {
+        f32x4& d = acc[WPW + w];
+        d = MM::mma8(pf[0], yf[w][0], zero4());
+        d = MM::mma8(pf[1], yf[w][1], d);
+        if (TWO) {
+          d = MM::mma8(kf[0], xf[w][0], d);
+          d = MM::mma8(kf[1], xf[w][1], d);
+        }
+      }
+#pragma unroll
+      for (int w = 0; w < WPW; ++w) {
+        const int ct = wave + 4 * w;
+        if (ct < NTD) store4(Ao + (16 * tl + l16) * DK + 16 * ct + 4 * g, acc[w]);
+      }
+#pragma unroll
+      for (int w = 0; w < VPW; ++w) {
+        const int cv = wave + 4 * w;
+        if (cv < nct_u) store4(Do + (16 * cv + l16) * DK + 16 * tl + 4 * g, acc[WPW + w]);
       }
     }
   }
@@ -559,63 +696,52 @@ __global__ __launch_bounds__(256) void wyc_prep_kernel(WycArgs a) {
 
 // ------------------------------------------------------------------ state kernel
 
-template <int DK, int NCT, int MODE>
+// One chunk buffer: the chunk's affine map, in the swizzled form of DmaPlan (prefill_wy.h).
+template <int DK, int DVS>
 struct WycStateLayout {
-  static constexpr bool TWO = MODE == 2;
   static constexpr int C = 64;
-  static constexpr int DVS = 16 * NCT;
-  static constexpr int LDT = DK + 8;
-  static constexpr int LDD = C + 8;
-  static constexpr int LDZ = DVS + 8;
-  static constexpr int CHT = (DK * LDD > C * LDT ? DK * LDD : C * LDT) * 2;  // channel-major or token-major
-  // set 1 (single buffer): Qhat rows and W rows (raw q and k rows on the exact path)
-  static constexpr int oQ = 0;
-  static constexpr int oW = oQ + C * LDT * 2;
-  static constexpr int SET1 = oW + C * LDT * 2;
-  // set 2 (two buffers), offsets within a buffer
-  static constexpr int oP = 0;              // -Pbar^T [dk][LDD] (exact path: c rows [64][LDT])
-  static constexpr int oKb = oP + CHT;      // Kbar^T (exact path: log alpha rows)
-  static constexpr int oM = oKb + CHT;      // -M [64][LDD]
-  static constexpr int oY = oM + C * LDD * 2;     // Y^T [DVS][LDD]
-  static constexpr int oZ = oY + DVS * LDD * 2;   // Z rows [64][LDZ] (MODE 2)
-  static constexpr int oX = oZ + (TWO ? C * LDZ * 2 : 0);  // X^T [DVS][LDD]
-  static constexpr int oS = oX + DVS * LDD * 2;   // fp32 e^{G_n} [dk], flag
-  static constexpr int BUF = oS + (DK + 4) * 4;
-  static constexpr int total = SET1 + 2 * BUF;
+  static constexpr int NCQ = DK / 8;   // 16-byte pieces per row of dk channels
+  static constexpr int NCU = DVS / 8;  // pieces per row of a value slice
+  static constexpr int oA = 0;                    // A' [dk][dk], rows read in perm_row order
+  static constexpr int oQ = oA + DK * DK * 2;     // Q' [64][dk]
+  static constexpr int oD = oQ + C * DK * 2;      // D^T slice [DVS][dk]
+  static constexpr int oZ = oD + DVS * DK * 2;    // Z' slice [64][DVS]
+  static constexpr int oE = oZ + C * DVS * 2;     // e^{G_n} [dk] fp32 (+ flag)
+  static constexpr int BUF = oE + ((DK + 4) * 4 + 255) / 256 * 256;
+  static constexpr int oO = 2 * BUF;              // O rows of one chunk [64][DVS]
+  static constexpr int total = oO + C * DVS * 2;
   static constexpr bool fits = total <= kLdsLimit;
 };
 
-// Workgroup = 2 loader waves and one state wave for one state and DVS = 16 NCT value columns.
-// Per chunk c, two barrier-separated intervals:
-//   1: loaders write set 2 of chunk c+1 (its own buffer); state: Qhat S and W S of chunk c (or
-//      the whole chunk token by token when it is flagged)
-//   2: loaders write set 1 of chunk c+1 (Qhat, W: the state wave is done with them);
-//      state: R = W S + Y, O = Qhat S + Z - M R out, S <- e^{G_n} . S (+ Kbar^T X) - Pbar^T R
-template <int DK, int NCT, int MODE>
-__global__ __launch_bounds__(192) void wyc_state_kernel(WycArgs a) {
-  using L = WycStateLayout<DK, NCT, MODE>;
+// Workgroup = 2 loader waves and NSW state waves for one state and a slice of DVS = 16 NSW value
+// columns; state wave j holds columns 16 j .. 16 j + 15 of the slice.  Chunk c's map sits in LDS
+// buffer c mod 2, filled by direct-to-LDS loads that loader wave c mod 2 issues a whole chunk
+// ahead.  Two barriers per chunk c:
+//   up to A: the state waves compute, from S_b = bf16(S),
+//              O = Q' S_b (+ Z' later),   S <- e^{G_n} . S + D + A' S_b;
+//            loader wave c mod 2 copies the O rows of chunk c-1 from the O buffer to HBM;
+//   A to B:  the state waves write O + Z' into the O buffer; loader wave c mod 2 refills buffer
+//            c mod 2 with chunk c+2 and the other waits for its loads of chunk c+1.
+// The state waves issue no global stores in the loop, and the loader wave that reads the O buffer
+// has no loads in flight when it does.
+template <int DK, int NSW>
+__global__ __launch_bounds__(64 * (2 + NSW)) void wyc_state_kernel(WycArgs a) {
+  constexpr int DVS = 16 * NSW;
+  using L = WycStateLayout<DK, DVS>;
   using MM = Mma<__bf16>;
   using F8 = MM::F8;
   static_assert(L::fits, "LDS layout exceeds the gfx950 workgroup limit");
   static_assert(DK % 32 == 0, "dk must be a multiple of 32");
-  constexpr bool TWO = L::TWO;
-  constexpr int C = L::C, DVS = L::DVS, LDT = L::LDT, LDD = L::LDD, LDZ = L::LDZ;
+  constexpr int C = L::C, NCQ = L::NCQ, NCU = L::NCU;
   constexpr int NTD = DK / 16, NKB = DK / 32;
-  constexpr int NLT = 128;
-  constexpr int NCG = DK / 8, IPT = C * NCG / NLT;   // 16-byte row items per loader thread
-  constexpr int CPT = DK * (C / 8) / NLT;            // 16-byte items of a [dk][64] array
-  constexpr int MPT = C * C / 8 / NLT;
-  constexpr int NXG = DVS / 8, XPT = (C * NXG + NLT - 1) / NLT;
 
-  __shared__ __attribute__((aligned(32))) unsigned char smem[L::total];
-  __bf16* tQ = reinterpret_cast<__bf16*>(smem + L::oQ);
-  __bf16* tW = reinterpret_cast<__bf16*>(smem + L::oW);
-  auto buf = [&](int64_t c) -> unsigned char* { return smem + L::SET1 + (c & 1) * L::BUF; };
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[L::total];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   int lane = tid & 63, g = lane >> 4, l16 = lane & 15;
   const bool loader = wave < 2;
+  const int cb = loader ? 0 : 16 * (wave - 2);  // this state wave's first column in the slice
 
   const int64_t nb = gridDim.x, bid = blockIdx.x;
   const int64_t p = (nb % 8 == 0) ? (bid % 8) * (nb / 8) + bid / 8 : bid;
@@ -624,464 +750,162 @@ __global__ __launch_bounds__(192) void wyc_state_kernel(WycArgs a) {
   const int64_t bi = bh / a.H, hi = bh % a.H;
   const int64_t DV = a.DV, H = a.H, T = a.T, nch = a.nch;
   const int64_t col0 = static_cast<int64_t>(sl) * DVS;
-  const uint32_t hdk = static_cast<uint32_t>(H * DK * 2), hdv = static_cast<uint32_t>(H * DV * 2);
-  const uint32_t hqk = static_cast<uint32_t>(a.Hk * DK * 2);  // token stride of q and k
-  const int64_t hq = hi / (H / a.Hk);                        // this state's q / k head
-  const uint32_t h1 = static_cast<uint32_t>(H * 2);
-  const uint32_t oob = 0x80000000u;
+  const uint32_t hdv = static_cast<uint32_t>(H * DV * 2);
 
-  // ---------------- loaders ----------------
-  auto read_flag = [&](int64_t c) -> int {
-    const auto rf = make_rsrc(a.flag + bh * nch + c, 4);
-    return __builtin_amdgcn_readfirstlane(__builtin_amdgcn_raw_buffer_load_b32(rf, 0, 0, 0));
-  };
-  // x = w . v for this slice, transposed into X^T (value column major, swizzled token quads)
-  auto store_x = [&](int64_t c, __bf16* xT) {
-    const int64_t t0 = c * C, rr = (bi * T + t0) * H + hi;
-    const uint32_t vb = wy_range(T - t0, H, DV) - static_cast<uint32_t>(col0) * 2;
-    const auto rv = make_rsrc(a.v + rr * DV + col0, vb);
-    const auto rwc = make_rsrc(a.w_kind == kChannel ? a.wg + rr * DV + col0 : a.v, a.w_kind == kChannel ? vb : 0u);
-    const auto rws = make_rsrc(a.w_kind == kScalar ? a.wg + rr : a.v, a.w_kind == kScalar ? wy_range(T - t0, H, 1) : 0u);
-    uint4 vv[XPT], ww[XPT];
-    uint16_t wsv[XPT];
-#pragma unroll
-    for (int j = 0; j < XPT; ++j) {
-      const int item = tid + NLT * j;
-      const bool in = item < C * NXG;
-      const uint32_t t = item / NXG, xg = item % NXG;
-      vv[j] = buf_load16(rv, in ? t * hdv + xg * 16 : oob);
-      ww[j] = buf_load16(rwc, in ? t * hdv + xg * 16 : oob);
-      wsv[j] = buf_load_u16(rws, in ? t * h1 : oob);
-    }
-#pragma unroll
-    for (int j = 0; j < XPT; ++j) {
-      const int item = tid + NLT * j;
-      if (item < C * NXG) {
-        const int t = item / NXG, xg = item % NXG;
-        float x[8];
-        load8f(reinterpret_cast<const bf16_t*>(&vv[j]), x);
-        if (a.w_kind == kChannel) {
-          float w8[8];
-          load8f(reinterpret_cast<const bf16_t*>(&ww[j]), w8);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) x[e] *= w8[e];
-        } else if (a.w_kind == kScalar) {
-          const float ws = bf16_to_f32(wsv[j]);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) x[e] *= ws;
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) xT[(xg * 8 + e) * LDD + swz(2 * xg, t)] = static_cast<__bf16>(x[e]);
-      }
-    }
-  };
-  // set 2 of chunk c: -Pbar^T, Kbar^T, -M, Y^T, Z, X^T, e^{G_n}, flag (exact path: c, log alpha, X^T)
-  auto store_set2 = [&](int64_t c, int robust) {
+  auto buf = [&](int64_t c) -> unsigned char* { return smem + (c & 1) * L::BUF; };
+  __bf16* oO = reinterpret_cast<__bf16*>(smem + L::oO);
+
+  // ---------------- loader waves ----------------
+  DmaPlan<NCQ, true, DK * NCQ> plA;
+  DmaPlan<NCQ, false, C * NCQ> plQ;
+  DmaPlan<NCQ, false, DVS * NCQ> plD;
+  DmaPlan<NCU, false, C * NCU> plZ;
+  const uint32_t sq = DK * 2, su = static_cast<uint32_t>(DV * 2);
+  {
+    const int dl = tid & 63;
+    plA.init(sq, dl);
+    plQ.init(sq, dl);
+    plD.init(sq, dl);
+    plZ.init(su, dl);
+  }
+  auto dma_chunk = [&](int64_t c) {
     unsigned char* B = buf(c);
-    __bf16* tP = reinterpret_cast<__bf16*>(B + L::oP);
-    __bf16* tKb = reinterpret_cast<__bf16*>(B + L::oKb);
-    __bf16* gM = reinterpret_cast<__bf16*>(B + L::oM);
-    __bf16* yT = reinterpret_cast<__bf16*>(B + L::oY);
-    __bf16* zs = reinterpret_cast<__bf16*>(B + L::oZ);
-    __bf16* xT = reinterpret_cast<__bf16*>(B + L::oX);
-    float* sc = reinterpret_cast<float*>(B + L::oS);
     const int64_t cix = bh * nch + c;
-    if (tid < DK) {
-      const auto re = make_rsrc(a.Egn + cix * DK, DK * 4);
-      sc[tid] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(re, tid * 4, 0, 0));
-    }
-    if (tid == 0) reinterpret_cast<int*>(sc + DK)[0] = robust;
-    if (robust) store_x(c, xT);
-    if (robust) {
-      // raw c = b . k and log alpha rows, token-major
-      const int64_t t0 = c * C, rr = (bi * T + t0) * H + hi, rqk = (bi * T + t0) * a.Hk + hq;
-      const auto rk = make_rsrc(a.k + rqk * DK, wy_range(T - t0, a.Hk, DK));
-      const auto rla = make_rsrc(a.la + rr * DK, wy_range(T - t0, H, DK));
-      const auto rbc = make_rsrc(a.b_kind == kChannel ? a.bg + rr * DK : a.q, a.b_kind == kChannel ? wy_range(T - t0, H, DK) : 0u);
-      const auto rbs = make_rsrc(a.b_kind == kScalar ? a.bg + rr : a.q, a.b_kind == kScalar ? wy_range(T - t0, H, 1) : 0u);
-#pragma unroll
-      for (int j = 0; j < IPT; ++j) {
-        const uint32_t t = (tid / NCG) * IPT + j, cg = tid % NCG;
-        const uint4 kk = buf_load16(rk, t * hqk + cg * 16);
-        const uint4 bb = buf_load16(rbc, t * hdk + cg * 16);
-        const uint16_t bs = buf_load_u16(rbs, t * h1);
-        float k8[8], c8[8];
-        load8f(reinterpret_cast<const bf16_t*>(&kk), k8);
-        if (a.b_kind == kChannel) {
-          load8f(reinterpret_cast<const bf16_t*>(&bb), c8);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) c8[e] *= k8[e];
-        } else {
-          const float b1 = a.b_kind == kScalar ? bf16_to_f32(bs) : 0.f;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) c8[e] = b1 * k8[e];
-        }
-        bf16x8 cb;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) cb[e] = static_cast<__bf16>(c8[e]);
-        *reinterpret_cast<bf16x8*>(tP + t * LDT + cg * 8) = cb;
-        *reinterpret_cast<uint4*>(tKb + t * LDT + cg * 8) = buf_load16(rla, t * hdk + cg * 16);
-      }
-      return;
-    }
-    const auto rp = make_rsrc(a.Pn + cix * DK * C, DK * C * 2);
-    const auto rm = make_rsrc(a.Mn + cix * C * C, C * C * 2);
-    const auto ry = make_rsrc(a.Y + (cix * DV + col0) * C, DVS * C * 2);
-    const auto rx = make_rsrc(TWO ? a.Xt + (cix * DV + col0) * C : a.Y, DVS * C * 2);
-    const auto rz = make_rsrc(TWO ? a.Z + cix * C * DV + col0 : a.Y, static_cast<uint32_t>((C * DV - col0) * 2));
-    const auto rkb = make_rsrc(TWO ? a.Kb + cix * DK * C : a.Pn, DK * C * 2);
-    uint4 pp[CPT], pkb[CPT], pm[MPT], py[XPT], px[XPT], pz[XPT];
-#pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-      pp[j] = buf_load16(rp, (tid + NLT * j) * 16);
-      if (TWO) pkb[j] = buf_load16(rkb, (tid + NLT * j) * 16);
-    }
-#pragma unroll
-    for (int j = 0; j < MPT; ++j) pm[j] = buf_load16(rm, (tid + NLT * j) * 16);
-#pragma unroll
-    for (int j = 0; j < XPT; ++j) {
-      const int item = tid + NLT * j;
-      const uint32_t t = item / NXG, xg = item % NXG;
-      const bool in = item < C * NXG;
-      py[j] = buf_load16(ry, in ? item * 16 : oob);  // [DVS][64]: item = column * 8 + part
-      if (TWO) {
-        px[j] = buf_load16(rx, in ? item * 16 : oob);
-        pz[j] = buf_load16(rz, in ? (t * DV + xg * 8) * 2 : oob);
-      }
-    }
-    // [dk][64] arrays: item = row * 8 + part holds tokens 8 part .. 8 part + 7 of row `row`
-#pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-      const int item = tid + NLT * j, row = item >> 3, part = item & 7, key = (row >> 3) & 15;
-      __bf16* dp = tP + row * LDD;
-      *reinterpret_cast<uint2*>(dp + swz(key, 8 * part)) = make_uint2(pp[j].x, pp[j].y);
-      *reinterpret_cast<uint2*>(dp + swz(key, 8 * part + 4)) = make_uint2(pp[j].z, pp[j].w);
-      if (TWO) {
-        __bf16* dk = tKb + row * LDD;
-        *reinterpret_cast<uint2*>(dk + swz(key, 8 * part)) = make_uint2(pkb[j].x, pkb[j].y);
-        *reinterpret_cast<uint2*>(dk + swz(key, 8 * part + 4)) = make_uint2(pkb[j].z, pkb[j].w);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < MPT; ++j) {
-      const int item = tid + NLT * j, r = item >> 3, part = item & 7;
-      *reinterpret_cast<uint4*>(gM + r * LDD + part * 8) = pm[j];
-    }
-#pragma unroll
-    for (int j = 0; j < XPT; ++j) {
-      const int item = tid + NLT * j;
-      if (item < C * NXG) {
-        // [column][64] slices: tokens 8 part .. 8 part + 7 of one column as two swizzled quads
-        const int col = item >> 3, part = item & 7, key = 2 * (col >> 3);
-        __bf16* yr = yT + col * LDD;
-        *reinterpret_cast<uint2*>(yr + swz(key, 8 * part)) = make_uint2(py[j].x, py[j].y);
-        *reinterpret_cast<uint2*>(yr + swz(key, 8 * part + 4)) = make_uint2(py[j].z, py[j].w);
-        if (TWO) {
-          __bf16* xr = xT + col * LDD;
-          *reinterpret_cast<uint2*>(xr + swz(key, 8 * part)) = make_uint2(px[j].x, px[j].y);
-          *reinterpret_cast<uint2*>(xr + swz(key, 8 * part + 4)) = make_uint2(px[j].z, px[j].w);
-          const int t = item / NXG, xg = item % NXG;
-          *reinterpret_cast<uint4*>(zs + t * LDZ + xg * 8) = pz[j];
-        }
-      }
-    }
+    plA.issue(make_rsrc(a.Ad + cix * DK * DK, DK * DK * 2), B + L::oA, sq);
+    plQ.issue(make_rsrc(a.Qd + cix * C * DK, C * DK * 2), B + L::oQ, sq);
+    plD.issue(make_rsrc(a.Dt + (cix * DV + col0) * DK, DVS * DK * 2), B + L::oD, sq);
+    plZ.issue(make_rsrc(a.Zd + cix * C * DV + col0, static_cast<uint32_t>((C * DV - col0) * 2)), B + L::oZ, su);
+    if (lane < (DK + 4) / 4) lds_dma16(make_rsrc(a.Egn + cix * (DK + 4), (DK + 4) * 4), B + L::oE, lane * 16);
   };
-  // set 1 of chunk c: Qhat and W rows (exact path: raw q and k rows)
-  auto store_set1 = [&](int64_t c, int robust) {
-    const int64_t cix = bh * nch + c;
-    const int64_t t0 = c * C, rqk = (bi * T + t0) * a.Hk + hq;
-    const auto ra = robust ? make_rsrc(a.q + rqk * DK, wy_range(T - t0, a.Hk, DK)) : make_rsrc(a.Qp + cix * C * DK, C * DK * 2);
-    const auto rb = robust ? make_rsrc(a.k + rqk * DK, wy_range(T - t0, a.Hk, DK)) : make_rsrc(a.W + cix * C * DK, C * DK * 2);
-    const uint32_t pitch = robust ? hqk : DK * 2;
-    uint4 pa[IPT], pb[IPT];
-#pragma unroll
-    for (int j = 0; j < IPT; ++j) {
-      const uint32_t t = (tid / NCG) * IPT + j, cg = tid % NCG;
-      pa[j] = buf_load16(ra, t * pitch + cg * 16);
-      pb[j] = buf_load16(rb, t * pitch + cg * 16);
-    }
-#pragma unroll
-    for (int j = 0; j < IPT; ++j) {
-      const uint32_t t = (tid / NCG) * IPT + j, cg = tid % NCG;
-      *reinterpret_cast<uint4*>(tQ + t * LDT + cg * 8) = pa[j];
-      *reinterpret_cast<uint4*>(tW + t * LDT + cg * 8) = pb[j];
-    }
-  };
-
-  // ---------------- state wave ----------------
-  f32x4 S[NCT][NTD];
-#pragma unroll
-  for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-    for (int tl = 0; tl < NTD; ++tl) {
-      S[ct][tl] = zero4();
-      if (!loader && a.S0 != nullptr) {
-        const int64_t sb = bh * DK * DV + col0 + 16 * ct + l16;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) S[ct][tl][i] = a.S0[sb + (int64_t)(16 * tl + 4 * g + i) * DV];
-      }
-    }
-  f32x4 Ot[NCT][4], V[NCT][4];  // across the two intervals of a chunk
-
-  // Ot = (Qhat S)^T tiles and V = W S tiles: one stream of eight 16-row tiles (Qhat then W)
-  auto qs_ws = [&]() {
-    F8 sf[NCT][NKB];
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) sf[ct][kb] = acc_pair_frag<__bf16>(S[ct][2 * kb], S[ct][2 * kb + 1]);
-#pragma unroll
-      for (int ta = 0; ta < 4; ++ta) {
-        Ot[ct][ta] = zero4();
-        V[ct][ta] = zero4();
-      }
-    }
-    F8 af[4][NKB];
-    auto load_a = [&](int j, F8* o) {
-      const __bf16* rows = (j < 4 ? tQ : tW) + (16 * (j & 3) + l16) * LDT;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) o[kb] = lds_pair_frag_k<DK>(rows, 32 * kb, g);
-    };
-#pragma unroll
-    for (int j = 0; j < 3; ++j) load_a(j, af[j]);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (j + 3 < 8) load_a(j + 3, af[(j + 3) & 3]);
-      const int ta = j & 3;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-          if (j < 4)
-            Ot[ct][ta] = MM::mma8(sf[ct][kb], af[j & 3][kb], Ot[ct][ta]);
-          else
-            V[ct][ta] = MM::mma8(af[j & 3][kb], sf[ct][kb], V[ct][ta]);
-        }
-    }
-  };
-
-  // A operand tiles of a channel-major [dk][64] array (swizzled token quads), tile-pair order
-  auto load_ct = [&](const __bf16* arr, int tl, F8* o) {
-    const int row = 16 * tl + l16, key = (row >> 3) & 15;
-    const __bf16* kr = arr + row * LDD;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const bf16x4 lo = lds_load4(kr + swz(key, 32 * kb + 4 * g));
-      const bf16x4 hi = lds_load4(kr + swz(key, 32 * kb + 16 + 4 * g));
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        o[kb][e] = lo[e];
-        o[kb][4 + e] = hi[e];
-      }
-    }
-  };
-
-  auto second = [&](int64_t c) {
-    const unsigned char* B = buf(c);
-    const __bf16* tP = reinterpret_cast<const __bf16*>(B + L::oP);
-    const __bf16* tKb = reinterpret_cast<const __bf16*>(B + L::oKb);
-    const __bf16* gM = reinterpret_cast<const __bf16*>(B + L::oM);
-    const __bf16* yT = reinterpret_cast<const __bf16*>(B + L::oY);
-    const __bf16* zs = reinterpret_cast<const __bf16*>(B + L::oZ);
-    const __bf16* xT = reinterpret_cast<const __bf16*>(B + L::oX);
-    const float* sc = reinterpret_cast<const float*>(B + L::oS);
-    F8 mf[6];
-#pragma unroll
-    for (int ta = 0, n = 0; ta < 4; ++ta) {
-      mf[n++] = lds_pair_frag_k<C>(gM + (16 * ta + l16) * LDD, 0, g);
-      if (ta >= 2) mf[n++] = lds_pair_frag_k<C>(gM + (16 * ta + l16) * LDD, 32, g);
-    }
-    // R = V + Y as tile-pair fragments; X fragments for Kbar^T X
-    F8 rf[NCT][2], xf[NCT][2];
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      const int n = 16 * ct + l16;
-      f32x4 R[4];
-#pragma unroll
-      for (int ta = 0; ta < 4; ++ta) {
-        const bf16x4 y4 = *reinterpret_cast<const bf16x4*>(yT + n * LDD + swz(2 * (n >> 3), 16 * ta + 4 * g));
-#pragma unroll
-        for (int i = 0; i < 4; ++i) R[ta][i] = V[ct][ta][i] + static_cast<float>(y4[i]);
-      }
-      rf[ct][0] = acc_pair_frag<__bf16>(R[0], R[1]);
-      rf[ct][1] = acc_pair_frag<__bf16>(R[2], R[3]);
-      if (TWO) {
-        const int key = 2 * (n >> 3);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const bf16x4 lo = lds_load4(xT + n * LDD + swz(key, 32 * kb + 4 * g));
-          const bf16x4 hi = lds_load4(xT + n * LDD + swz(key, 32 * kb + 16 + 4 * g));
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            xf[ct][kb][e] = lo[e];
-            xf[ct][kb][4 + e] = hi[e];
-          }
-        }
-      }
-    }
-    // O^T += Z^T + R^T (-M)^T, then O out (four columns of one token per 8-byte store)
+  // O rows of chunk c from the O buffer to HBM, 16 bytes per store; rows past the last token are
+  // dropped by the range
+  auto store_o = [&](int64_t c) {
     const int64_t t0 = c * C;
     const int64_t rr = (bi * T + t0) * H + hi;
     const int64_t bytes = ((T - t0 - 1) * H + 1) * DV * 2 - col0 * 2;
     const auto ro = make_rsrc(a.o + rr * DV + col0, static_cast<uint32_t>(bytes < 0x7fffffff ? bytes : 0x7fffffff));
-    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-      for (int ta = 0, n = 0; ta < 4; ++ta) {
-        Ot[ct][ta] = MM::mma8(rf[ct][0], mf[n++], Ot[ct][ta]);
-        if (ta >= 2) Ot[ct][ta] = MM::mma8(rf[ct][1], mf[n++], Ot[ct][ta]);
-        if (TWO) {
-          const bf16x4 z4 = *reinterpret_cast<const bf16x4*>(zs + (16 * ta + l16) * LDZ + 16 * ct + 4 * g);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) Ot[ct][ta][i] += static_cast<float>(z4[i]);
-        }
-        bf16x4 ob;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ob[i] = static_cast<__bf16>(Ot[ct][ta][i]);
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, ob), ro,
-                                              (16 * ta + l16) * hdv + (16 * ct + 4 * g) * 2, 0, 0);
-      }
-    // S <- e^{G_n} . S (+ Kbar^T X) + (-Pbar^T) R
-    F8 pf[4][2], kf[4][2];
-#pragma unroll
-    for (int tl = 0; tl < 3; ++tl) {
-      load_ct(tP, tl, pf[tl]);
-      if (TWO) load_ct(tKb, tl, kf[tl]);
-    }
-#pragma unroll
-    for (int tl = 0; tl < NTD; ++tl) {
-      if (tl + 3 < NTD) {
-        load_ct(tP, tl + 3, pf[(tl + 3) & 3]);
-        if (TWO) load_ct(tKb, tl + 3, kf[(tl + 3) & 3]);
-      }
-      const float4 e4 = *reinterpret_cast<const float4*>(sc + 16 * tl + 4 * g);
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        S[ct][tl][0] *= e4.x;
-        S[ct][tl][1] *= e4.y;
-        S[ct][tl][2] *= e4.z;
-        S[ct][tl][3] *= e4.w;
-        if (TWO) {
-          S[ct][tl] = MM::mma8(kf[tl & 3][0], xf[ct][0], S[ct][tl]);
-          S[ct][tl] = MM::mma8(kf[tl & 3][1], xf[ct][1], S[ct][tl]);
-        }
-        S[ct][tl] = MM::mma8(pf[tl & 3][0], rf[ct][0], S[ct][tl]);
-        S[ct][tl] = MM::mma8(pf[tl & 3][1], rf[ct][1], S[ct][tl]);
-      }
+    for (int j = 0; j < C * NCU / 64; ++j) {
+      const int item = lane + 64 * j, t = item / NCU, part = item % NCU;
+      buf_store16(ro, t * hdv + part * 16, *reinterpret_cast<const uint4*>(oO + t * DVS + part * 8));
     }
   };
 
-  // the recurrence itself, token by token in fp32, for a flagged chunk: each lane holds rows
-  // 16 tl + 4 g + i of its columns, so both dk-reductions are a partial sum plus two
-  // cross-lane-group adds
-  auto exact = [&](int64_t c) {
+  // ---------------- state waves ----------------
+  // S[tl]: accumulator row 4 g + i holds channel perm_row(tl, 4 g + i) of column cb + l16, so
+  // that the pair fragment of tiles 2 kb, 2 kb + 1 carries channels 32 kb + 8 g .. 32 kb + 8 g + 7
+  f32x4 S[NTD];
+#pragma unroll
+  for (int tl = 0; tl < NTD; ++tl) {
+    S[tl] = zero4();
+    if (!loader && a.S0 != nullptr) {
+      const int64_t sb = bh * DK * DV + col0 + cb + l16;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) S[tl][i] = a.S0[sb + (int64_t)perm_row(tl, 4 * g + i) * DV];
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+
+  // Operands (one 16-byte read each): A' rows perm_row(tl, l16) (S's channel order) and Q' rows
+  // 16 ta + l16, channels 32 kb + 8 g ..;  D^T row cb + l16 and e^{G_n} at this lane's channels;
+  // Z' row 16 ta + l16, columns cb + 4 g ..
+  f32x4 Ot[4];
+  bf16x4 zv[4];
+  auto compute = [&](int64_t c) {
     const unsigned char* B = buf(c);
-    const __bf16* tC = reinterpret_cast<const __bf16*>(B + L::oP);
-    const __bf16* tLa = reinterpret_cast<const __bf16*>(B + L::oKb);
-    const __bf16* xT = reinterpret_cast<const __bf16*>(B + L::oX);
-    const int64_t t0 = c * C;
-    const int nval = static_cast<int>(T - t0 < C ? T - t0 : C);
-    const int64_t rr = (bi * T + t0) * H + hi;
-    for (int t = 0; t < nval; ++t) {
-      float qd[NTD][4], kd[NTD][4], cd[NTD][4], al[NTD][4];
+    F8 fa[2][NTD], fq[2][4];
+    auto read_k = [&](int kb, int r) {
 #pragma unroll
-      for (int tl = 0; tl < NTD; ++tl) {
-        const int d = 16 * tl + 4 * g;
-        const bf16x4 q4 = lds_load4(tQ + t * LDT + d);
-        const bf16x4 k4 = lds_load4(tW + t * LDT + d);
-        const bf16x4 c4 = lds_load4(tC + t * LDT + d);
-        const bf16x4 l4 = lds_load4(tLa + t * LDT + d);
+      for (int tl = 0; tl < NTD; ++tl) fa[r][tl] = lds_piece<NCQ, true>(B + L::oA, perm_row(tl, l16), 4 * kb + g);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          qd[tl][i] = static_cast<float>(q4[i]);
-          kd[tl][i] = static_cast<float>(k4[i]);
-          cd[tl][i] = static_cast<float>(c4[i]);
-          al[tl][i] = __expf(static_cast<float>(l4[i]));
-        }
-      }
+      for (int ta = 0; ta < 4; ++ta) fq[r][ta] = lds_piece<NCQ, false>(B + L::oQ, 16 * ta + l16, 4 * kb + g);
+    };
+    read_k(0, 0);
+    const float* E = reinterpret_cast<const float*>(B + L::oE);
+    float4 e4[NTD];
+    bf16x4 d4[NTD];
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        const int n = 16 * ct + l16;
-        const float x = static_cast<float>(xT[n * LDD + swz(2 * (n >> 3), t)]);
-        if (!TWO) {  // decay first
+    for (int tl = 0; tl < NTD; ++tl) {
+      e4[tl] = *reinterpret_cast<const float4*>(E + perm_row(tl, 4 * g));
+      d4[tl] = *reinterpret_cast<const bf16x4*>(swz_addr<NCQ, false>(B + L::oD, cb + l16, 4 * (tl >> 1) + g) + 8 * (tl & 1));
+    }
+    F8 sf[NKB];
 #pragma unroll
-          for (int tl = 0; tl < NTD; ++tl)
+    for (int kb = 0; kb < NKB; ++kb) sf[kb] = acc_pair_frag<__bf16>(S[2 * kb], S[2 * kb + 1]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) S[ct][tl][i] *= al[tl][i];
-        }
-        float r = 0.f;
+    for (int tl = 0; tl < NTD; ++tl) {
+      S[tl][0] = S[tl][0] * e4[tl].x + static_cast<float>(d4[tl][0]);
+      S[tl][1] = S[tl][1] * e4[tl].y + static_cast<float>(d4[tl][1]);
+      S[tl][2] = S[tl][2] * e4[tl].z + static_cast<float>(d4[tl][2]);
+      S[tl][3] = S[tl][3] * e4[tl].w + static_cast<float>(d4[tl][3]);
+    }
 #pragma unroll
-        for (int tl = 0; tl < NTD; ++tl)
+    for (int ta = 0; ta < 4; ++ta) Ot[ta] = zero4();
 #pragma unroll
-          for (int i = 0; i < 4; ++i) r += cd[tl][i] * S[ct][tl][i];
-        r += __shfl_xor(r, 16);
-        r += __shfl_xor(r, 32);
-        float y = 0.f;
+    for (int kb = 0; kb < NKB; ++kb) {
+      if (kb + 1 < NKB) read_k(kb + 1, (kb + 1) & 1);
 #pragma unroll
-        for (int tl = 0; tl < NTD; ++tl)
+      for (int tl = 0; tl < NTD; ++tl) S[tl] = MM::mma8(fa[kb & 1][tl], sf[kb], S[tl]);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float sv = S[ct][tl][i] - kd[tl][i] * r;
-            if (TWO) sv *= al[tl][i];
-            sv += kd[tl][i] * x;
-            S[ct][tl][i] = sv;
-            y += qd[tl][i] * sv;
-          }
-        y += __shfl_xor(y, 16);
-        y += __shfl_xor(y, 32);
-        if (g == 0) a.o[(rr + static_cast<int64_t>(t) * H) * DV + col0 + n].x = f32_to_bf16(y);
-      }
+      for (int ta = 0; ta < 4; ++ta) Ot[ta] = MM::mma8(sf[kb], fq[kb & 1][ta], Ot[ta]);
+    }
+    const int col = cb + 4 * g;
+#pragma unroll
+    for (int ta = 0; ta < 4; ++ta)
+      zv[ta] = *reinterpret_cast<const bf16x4*>(swz_addr<NCU, false>(B + L::oZ, 16 * ta + l16, col >> 3) + 8 * ((col >> 2) & 1));
+  };
+  // Ot[ta] lane (g, l16) holds O[16 ta + l16][cb + 4 g + i]
+  auto write_o = [&]() {
+#pragma unroll
+    for (int ta = 0; ta < 4; ++ta) {
+      bf16x4 ob;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ob[i] = static_cast<__bf16>(Ot[ta][i] + static_cast<float>(zv[ta][i]));
+      *reinterpret_cast<bf16x4*>(oO + (16 * ta + l16) * DVS + cb + 4 * g) = ob;
     }
   };
 
   // ---------------- pipeline ----------------
-  int nflag = 0;  // loaders: flag of the chunk whose set 1 comes next
-  if (loader && nch > 0) {
-    nflag = read_flag(0);
-    store_set2(0, nflag);
-    store_set1(0, nflag);
+  if (nch > 0) {
+    if (wave == 0) {
+      dma_chunk(0);
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    }
+    if (wave == 1 && nch > 1) dma_chunk(1);
   }
   lds_barrier();
   for (int64_t ch = 0; ch < nch; ++ch) {
+    // opaque per chunk: keeps lane-dependent LDS addresses from being hoisted out of the loop
     asm volatile("" : "+v"(lane), "+v"(g), "+v"(l16));
-    const bool more = ch + 1 < nch;
-    int robust = 0;
     GDR_MARK(0);
-    if (loader) {
-      if (more) {
-        nflag = read_flag(ch + 1);
-        store_set2(ch + 1, nflag);
-      }
-    } else {
-      robust = reinterpret_cast<const int*>(reinterpret_cast<const float*>(buf(ch) + L::oS) + DK)[0];
-      if (robust)
-        exact(ch);
-      else
-        qs_ws();
-    }
+    if (!loader)
+      compute(ch);
+    else if (wave == static_cast<int>(ch & 1) && ch > 0)
+      store_o(ch - 1);
     GDR_MARK(1);
-    lds_barrier();
+    lds_barrier_keep_vm();  // A: buffer ch mod 2 and the O buffer are free
     GDR_MARK(2);
     if (loader) {
-      if (more) store_set1(ch + 1, nflag);
-    } else if (!robust) {
-      second(ch);
+      if (wave == static_cast<int>(ch & 1)) {
+        if (ch + 2 < nch) dma_chunk(ch + 2);
+      } else {
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // this wave's loads of chunk ch+1
+      }
+    } else {
+      write_o();
     }
     GDR_MARK(3);
-    lds_barrier();
+    lds_barrier_keep_vm();  // B: chunk ch+1 is in buffer (ch+1) mod 2, O of chunk ch in the O buffer
     GDR_MARK(4);
   }
+  if (wave == 0 && nch > 0) store_o(nch - 1);
 
   if (!loader && a.S_T != nullptr) {
+    const int64_t sb = bh * DK * DV + col0 + cb + l16;
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      const int64_t sb = bh * DK * DV + col0 + 16 * ct + l16;
+    for (int tl = 0; tl < NTD; ++tl)
 #pragma unroll
-      for (int tl = 0; tl < NTD; ++tl)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) a.S_T[sb + (int64_t)(16 * tl + 4 * g + i) * DV] = S[ct][tl][i];
-    }
+      for (int i = 0; i < 4; ++i) a.S_T[sb + (int64_t)perm_row(tl, 4 * g + i) * DV] = S[tl][i];
   }
 }
 

@@ -7,24 +7,28 @@ namespace {
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 struct WycSizes {
-  size_t W, Qp, Pn, Kb, Mn, Y, Z, Xt, Egn, flag;
-  size_t total() const { return W + Qp + Pn + Kb + Mn + Y + Z + Xt + Egn + flag; }
+  size_t Qd, Ad, Dt, Zd, Egn, flag;
+  size_t total() const { return Qd + Ad + Dt + Zd + Egn + flag; }
 };
 
-WycSizes wyc_sizes(int64_t nstate, int64_t T, int64_t DK, int64_t DV, bool two) {
+// per chunk: Q' (64 x dk), A' (dk x dk), D^T (dv x dk), Z' (64 x dv) in bf16, dk + 4 floats, a flag
+WycSizes wyc_sizes(int64_t nstate, int64_t T, int64_t DK, int64_t DV) {
   const size_t ch = static_cast<size_t>(nstate) * static_cast<size_t>((T + 63) / 64);
   WycSizes s;
-  s.W = align256(ch * 64 * DK * 2);
-  s.Qp = s.W;
-  s.Pn = align256(ch * DK * 64 * 2);
-  s.Kb = two ? s.Pn : 0;
-  s.Mn = align256(ch * 64 * 64 * 2);
-  s.Y = align256(ch * 64 * DV * 2);
-  s.Z = two ? s.Y : 0;
-  s.Xt = two ? s.Y : 0;
-  s.Egn = align256(ch * DK * 4);
+  s.Qd = align256(ch * 64 * DK * 2);
+  s.Ad = align256(ch * DK * DK * 2);
+  s.Dt = align256(ch * DV * DK * 2);
+  s.Zd = align256(ch * 64 * DV * 2);
+  s.Egn = align256(ch * (DK + 4) * 4);
   s.flag = align256(ch * 4);
   return s;
+}
+
+template <int DK, int NSW>
+void launch_state(WycArgs a, int64_t nstate, hipStream_t s) {
+  a.nsl = static_cast<int>(a.DV / (16 * NSW));
+  hipLaunchKernelGGL((wyc_state_kernel<DK, NSW>), dim3((unsigned)(nstate * a.nsl)), dim3(64 * (2 + NSW)), 0,
+                     s, a);
 }
 
 template <int DK, int MODE>
@@ -42,14 +46,15 @@ hipError_t launch_mode(WycArgs a, int64_t nstate, hipEvent_t mark, hipStream_t s
     const hipError_t e = hipEventRecord(mark, s);
     if (e != hipSuccess) return e;
   }
-  // 32-column slices when that still gives a workgroup per compute unit, else 16 columns
-  if (a.DV % 32 == 0 && nstate * (a.DV / 32) >= 256) {
-    a.nsl = static_cast<int>(a.DV / 32);
-    hipLaunchKernelGGL((wyc_state_kernel<DK, 2, MODE>), dim3((unsigned)(nstate * a.nsl)), dim3(192), 0, s, a);
-  } else {
-    a.nsl = static_cast<int>(a.DV / 16);
-    hipLaunchKernelGGL((wyc_state_kernel<DK, 1, MODE>), dim3((unsigned)(nstate * a.nsl)), dim3(192), 0, s, a);
-  }
+  // the widest value slice (64, 32 or 16 columns: one state wave per 16) that still gives a
+  // workgroup per compute unit, else the narrowest (the most workgroups)
+  const int64_t DV = a.DV;
+  if (DV % 64 == 0 && nstate * (DV / 64) >= 256)
+    launch_state<DK, 4>(a, nstate, s);
+  else if (DV % 32 == 0 && nstate * (DV / 32) >= 256)
+    launch_state<DK, 2>(a, nstate, s);
+  else
+    launch_state<DK, 1>(a, nstate, s);
   return hipGetLastError();
 }
 }  // namespace
@@ -60,7 +65,8 @@ bool prefill_wyc_ok(int64_t DK, int64_t DV) {
 }
 
 size_t prefill_wyc_workspace_bytes(int64_t nstate, int64_t T, int64_t DK, int64_t DV, bool two) {
-  return wyc_sizes(nstate, T, DK, DV, two).total();
+  (void)two;
+  return wyc_sizes(nstate, T, DK, DV).total();
 }
 
 hipError_t prefill_wyc_launch(const PrefillArgs<bf16_t>& p, int64_t nstate, int64_t DK, bool two,
@@ -82,24 +88,16 @@ hipError_t prefill_wyc_launch(const PrefillArgs<bf16_t>& p, int64_t nstate, int6
   a.nch = (p.T + 63) / 64;
   a.b_kind = p.b_kind;
   a.w_kind = p.w_kind;
-  const WycSizes z = wyc_sizes(nstate, p.T, DK, p.DV, two);
+  const WycSizes z = wyc_sizes(nstate, p.T, DK, p.DV);
   unsigned char* ws = static_cast<unsigned char*>(workspace);
-  a.W = reinterpret_cast<__bf16*>(ws);
-  ws += z.W;
-  a.Qp = reinterpret_cast<__bf16*>(ws);
-  ws += z.Qp;
-  a.Pn = reinterpret_cast<__bf16*>(ws);
-  ws += z.Pn;
-  a.Kb = reinterpret_cast<__bf16*>(ws);
-  ws += z.Kb;
-  a.Mn = reinterpret_cast<__bf16*>(ws);
-  ws += z.Mn;
-  a.Y = reinterpret_cast<__bf16*>(ws);
-  ws += z.Y;
-  a.Z = reinterpret_cast<__bf16*>(ws);
-  ws += z.Z;
-  a.Xt = reinterpret_cast<__bf16*>(ws);
-  ws += z.Xt;
+  a.Qd = reinterpret_cast<__bf16*>(ws);
+  ws += z.Qd;
+  a.Ad = reinterpret_cast<__bf16*>(ws);
+  ws += z.Ad;
+  a.Dt = reinterpret_cast<__bf16*>(ws);
+  ws += z.Dt;
+  a.Zd = reinterpret_cast<__bf16*>(ws);
+  ws += z.Zd;
   a.Egn = reinterpret_cast<float*>(ws);
   ws += z.Egn;
   a.flag = reinterpret_cast<int*>(ws);

@@ -102,13 +102,11 @@ const char* gdr_status_string(int status);
  *   scalar (or no) decay, scalar (or no) erase gate: W (64 x dk), U (64 x dv)
  *     and the masked 64 x 64 read-out matrix, all bf16, and 132 floats of gate
  *     exponentials: 128 dk + 128 dv + 8720 bytes;
- *   per-channel decay, decay applied before the erase: W, the decay-scaled
- *     query, the decay-scaled erase keys (each 64 x dk bf16), the 64 x 64
- *     read-out matrix, Y (dv x 64 bf16), the dk chunk decays (fp32) and a
- *     flag: 388 dk + 128 dv + 8196 bytes;
- *   per-channel decay, erase then decay: as above plus a second decay-scaled
- *     key array (64 x dk), Z (64 x dv) and the written values (dv x 64):
- *     516 dk + 384 dv + 8196 bytes.
+ *   per-channel decay (either order): the chunk's affine map of the state,
+ *     S' = diag(decay) S + A S + D with read-out O = Q S + Z: A (dk x dk),
+ *     Q (64 x dk), D (dv x dk) and Z (64 x dv) in bf16, the dk chunk decays
+ *     plus 4 (fp32) and a flag:
+ *     2 dk^2 + 2 dk dv + 132 dk + 128 dv + 20 bytes.
  * The scalar-decay form with a per-channel erase gate, the dk = 16 and the
  * fp32 problems run as one kernel and need none.  The caller owns the buffer;
  * its contents on entry do not matter. */

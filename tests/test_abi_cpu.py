@@ -131,16 +131,15 @@ def test_empty_problem_is_a_no_op():
 
 
 def test_workspace_query_and_decode_validation():
-    # per-channel decay (erase then decay): W, Qhat (64 x dk), -Pbar^T, Kbar^T (dk x 64), -M_QP
-    # (64 x 64), Y^T, Z, X^T (64 x dv) in bf16, e^{G_n} (dk fp32) and a flag per 64-token chunk of
-    # every (batch, head); decay-then-erase drops Kbar^T, Z and X^T
+    # per-channel decay (either order): the chunk's affine map A' (dk x dk), Q' (64 x dk), D^T
+    # (dv x dk), Z' (64 x dv) in bf16, e^{G_n} (dk + 4 fp32) and a flag per 64-token chunk of every
+    # (batch, head), each array rounded up to 256 bytes
     r = lambda n: (n + 255) // 256 * 256
     ch = 2 * 3 * 2
-    two = 2 * r(ch * 64 * 128 * 2) + 2 * r(ch * 128 * 64 * 2) + r(ch * 64 * 64 * 2) + \
-        3 * r(ch * 64 * 128 * 2) + r(ch * 128 * 4) + r(ch * 4)
+    two = r(ch * 128 * 128 * 2) + r(ch * 64 * 128 * 2) + r(ch * 128 * 128 * 2) + \
+        r(ch * 64 * 128 * 2) + r(ch * 132 * 4) + r(ch * 4)
     assert N.workspace_bytes(prob()) == two
-    one = two - r(ch * 128 * 64 * 2) - 2 * r(ch * 64 * 128 * 2)
-    assert N.workspace_bytes(prob(order=N.DECAY_THEN_ERASE)) == one
+    assert N.workspace_bytes(prob(order=N.DECAY_THEN_ERASE)) == two
     # scalar decay in bf16: W (64 x dk), U (64 x dv), -M (64 x 64), all bf16, and 132 fp32 gate
     # exponentials per 64-token chunk of every (batch, head), each array rounded up to 256 bytes
     sp = prob(alpha_kind=N.GATE_SCALAR, b_kind=N.GATE_SCALAR, w_kind=N.GATE_SCALAR)

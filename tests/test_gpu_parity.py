@@ -134,6 +134,26 @@ def test_prefill_extreme_gates(dev):
     check(x, o, S, "erase_then_decay", TOL["bf16"], "extreme scalar")
 
 
+@pytest.mark.parametrize("order", ["erase_then_decay", "decay_then_erase"])
+@pytest.mark.parametrize("kind,DV", [("gdn2", 128), ("kda", 128), ("kda", 48)])
+def test_prefill_flagged_chunks_mixed(dev, kind, DV, order):
+    """Chunks whose per-channel gate prefix sums span past the range of the chunk form (log alpha
+    = -7 over a chunk spans 448 nats) run token by token.  Here they sit between ordinary chunks
+    of the same state, past the 64th chunk, and in the ragged last chunk."""
+    T = 64 * 66 + 17
+    wl = case(kind, B=1, H=2, T=T, DV=DV)
+    x = synth.make_prefill(wl)
+    la = x["log_alpha"].clone()
+    for c in (1, 2, 40, 65, 66):
+        la[:, 64 * c:64 * (c + 1)] = -7.0
+    x["log_alpha"] = la
+    say("flagged chunks", kind, "dv", DV, order)
+    o, S = run_gpu_prefill(x, dev, order=order)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all() and torch.isfinite(S).all()
+    check(x, o, S, order, TOL["bf16"], "flagged %s dv=%d %s" % (kind, DV, order))
+
+
 # ------------------------------------------------------------------ decode
 
 
