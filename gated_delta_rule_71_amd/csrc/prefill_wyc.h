@@ -50,7 +50,8 @@ struct WycArgs {
   const float* S0;
   bf16_t* o;
   float* S_T;
-  // workspace, per chunk index cix = state * nch + chunk: the affine chunk map
+  // workspace, per chunk index cix = state * nch + chunk: the affine chunk map, each matrix as
+  // 16 x 16 tiles of 512 bytes (tiled16 below), so that an MFMA output tile is one contiguous store
   __bf16* Qd;  // [cix][64][dk]  Q'
   __bf16* Ad;  // [cix][dk][dk]  A'
   __bf16* Dt;  // [cix][dv][dk]  D^T
@@ -64,6 +65,12 @@ struct WycArgs {
 };
 
 constexpr float kWycSpanLimit = 76.f;
+
+// Element (r, c) of a matrix with ncols columns (a multiple of 16) stored as 16 x 16 tiles of 512
+// bytes: row-major inside a tile, tiles row-major.
+__host__ __device__ constexpr inline int64_t tiled16(int64_t r, int64_t c, int64_t ncols) {
+  return ((r >> 4) * (ncols >> 4) + (c >> 4)) * 256 + (r & 15) * 16 + (c & 15);
+}
 
 // ------------------------------------------------------------------ chunk-local kernel
 
@@ -110,8 +117,9 @@ __device__ __forceinline__ void wyc_exact_chunk(const WycArgs& a, int64_t cix, c
                                                 const __bf16* tX, float egn_own, int tid) {
   constexpr int C = 64;
   const int64_t DV = a.DV;
-  // one column s through the chunk; col_x < 0: no write (the transition); y_t = q_t s_t to yout
-  auto run = [&](float (&s)[DK], int col_x, __bf16* yout, int64_t ypitch) {
+  // one column s through the chunk; col_x < 0: no write (the transition); y_t = q_t s_t to element
+  // (t, ycol) of yout (tiled, ypitch columns)
+  auto run = [&](float (&s)[DK], int col_x, __bf16* yout, int ycol, int64_t ypitch) {
     for (int t = 0; t < C; ++t) {
       float r = 0.f;  // c_t s (after the decay in MODE 1)
 #pragma unroll
@@ -144,7 +152,7 @@ __device__ __forceinline__ void wyc_exact_chunk(const WycArgs& a, int64_t cix, c
           y += q8[e] * sv;
         }
       }
-      yout[t * ypitch] = static_cast<__bf16>(y);
+      yout[tiled16(t, ycol, ypitch)] = static_cast<__bf16>(y);
     }
   };
   const int j = tid & 127;
@@ -153,24 +161,24 @@ __device__ __forceinline__ void wyc_exact_chunk(const WycArgs& a, int64_t cix, c
       float s[DK];
 #pragma unroll
       for (int i = 0; i < DK; ++i) s[i] = i == j ? 1.f : 0.f;
-      run(s, -1, a.Qd + cix * C * DK + j, DK);
-      __bf16* Ao = a.Ad + cix * DK * DK + j;  // A' = A - diag(e^{G_n}), column j (egn_own: channel j)
+      run(s, -1, a.Qd + cix * C * DK, j, DK);
+      __bf16* Ao = a.Ad + cix * DK * DK;  // A' = A - diag(e^{G_n}), column j (egn_own: channel j)
 #pragma unroll
-      for (int i = 0; i < DK; ++i) Ao[i * DK] = static_cast<__bf16>(s[i] - (i == j ? egn_own : 0.f));
+      for (int i = 0; i < DK; ++i) Ao[tiled16(i, j, DK)] = static_cast<__bf16>(s[i] - (i == j ? egn_own : 0.f));
     }
   } else {
     for (int v = j; v < DV; v += 128) {
       float s[DK];
 #pragma unroll
       for (int i = 0; i < DK; ++i) s[i] = 0.f;
-      run(s, v, a.Zd + cix * C * DV + v, DV);
-      __bf16* Do = a.Dt + (cix * DV + v) * DK;  // row v of D^T
+      run(s, v, a.Zd + cix * C * DV, v, DV);
+      __bf16* Do = a.Dt + cix * DV * DK;  // row v of D^T
 #pragma unroll
       for (int p = 0; p < DK / 8; ++p) {
         bf16x8 d8;
 #pragma unroll
         for (int e = 0; e < 8; ++e) d8[e] = static_cast<__bf16>(s[8 * p + e]);
-        *reinterpret_cast<bf16x8*>(Do + 8 * p) = d8;
+        *reinterpret_cast<bf16x8*>(Do + tiled16(v, 8 * p, DK)) = d8;
       }
     }
   }
@@ -537,10 +545,10 @@ __global__ __launch_bounds__(256) void wyc_prep_kernel(WycArgs a) {
     }
   };
   // column tile of a token-major LDS array as A (or B) fragments: 8 tokens (tile-pair order) of
-  // column col per lane, times `scale` (two transposing reads per 32-token block: source lane
+  // column col per lane (two transposing reads per 32-token block: source lane
   // (a, m) = (l16 & 3, l16 >> 2) of group g points at token 32 ks + 16 h + 4 g + m, columns
   // col - l16 + 4 a ..)
-  auto col_frags = [&](const __bf16* base, int pitch, int col, float scale, F8* f) {
+  auto col_frags = [&](const __bf16* base, int pitch, int col, F8* f) {
     const int c0 = col - l16 + 4 * (l16 & 3), m_ = l16 >> 2;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
@@ -549,9 +557,10 @@ __global__ __launch_bounds__(256) void wyc_prep_kernel(WycArgs a) {
         const bf16x4 v = lds_read_tr4(reinterpret_cast<const unsigned char*>(
             base + (32 * ks + 16 * h + 4 * g + m_) * pitch + c0));
 #pragma unroll
-        for (int e = 0; e < 4; ++e) f[ks][4 * h + e] = static_cast<__bf16>(static_cast<float>(v[e]) * scale);
+        for (int e = 0; e < 4; ++e) f[ks][4 * h + e] = v[e];
       }
   };
+
   // D^T tiles of (lower-triangular 64 x 64 B-side matrix) x (A-side 64 x 16 tile): out[ta] lane
   // holds D[token 16 ta + l16][column 4 g + i]
   auto tr_product = [&](const F8* af, const F8* bf, f32x4* out, bool acc) {
@@ -563,7 +572,7 @@ __global__ __launch_bounds__(256) void wyc_prep_kernel(WycArgs a) {
   };
   // upright tiles of (lower-triangular 64 x 64 A-side matrix) x (64 x 16 B-side tile), as the
   // two pair fragments (tokens as k) of the product: lane holds tokens 32 ks + 4 g + (e & 3) +
-  // 16 (e >> 2) of column l16, times sgn
+  // 16 (e >> 2) of column l16, times sgn (a factor of that column)
   auto up_frags = [&](const F8* af, const F8* bf, float sgn, F8* out) {
     f32x4 D[4];
 #pragma unroll
@@ -571,11 +580,10 @@ __global__ __launch_bounds__(256) void wyc_prep_kernel(WycArgs a) {
       D[ta] = MM::mma8(af[n++], bf[0], zero4());
       if (ta >= 2) D[ta] = MM::mma8(af[n++], bf[1], D[ta]);
     }
-    if (sgn != 1.f)
 #pragma unroll
-      for (int ta = 0; ta < 4; ++ta)
+    for (int ta = 0; ta < 4; ++ta)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) D[ta][i] *= sgn;
+      for (int i = 0; i < 4; ++i) D[ta][i] *= sgn;
     out[0] = acc_pair_frag<__bf16>(D[0], D[1]);
     out[1] = acc_pair_frag<__bf16>(D[2], D[3]);
   };
@@ -591,7 +599,7 @@ __global__ __launch_bounds__(256) void wyc_prep_kernel(WycArgs a) {
     //     (Qhat = split Q times e^{G_ref})
     // (2) this wave's value column tiles X and Y = T L_K X (MODE 1: -T X) as pair fragments, and
     //     Z' = M_QK X - M Y: lane holds Z'[16 ta + l16][16 cv + 4 g + i]
-    // (3) channel tile by channel tile, -Pbar (MODE 1: -Kbar) and Kbar with channels as rows, then
+    // (3) channel tile by channel tile, Phat (MODE 1: Khat) and Khat with channels as rows, then
     //     A' = -Pbar^T W:          lane holds A'[16 tl + l16][16 ct + 4 g + i]
     //     D = Kbar^T X - Pbar^T Y: lane holds D[16 tl + 4 g + i][16 cv + l16], i.e. row 16 cv + l16
     //                              of D^T, four consecutive channels
@@ -610,8 +618,8 @@ __global__ __launch_bounds__(256) void wyc_prep_kernel(WycArgs a) {
         if (ct < NTD) {
           const int col = 16 * ct + l16;
           F8 cf[2];
-          col_frags(tC, LDT, col, fEref[col], cf);
-          up_frags(tfr, cf, 1.f, wf[w]);
+          col_frags(tC, LDT, col, cf);
+          up_frags(tfr, cf, fEref[col], wf[w]);
           f32x4 Qt[4];
           tr_product(wf[w], mnf, Qt, false);
           const float4 er = *reinterpret_cast<const float4*>(fEref + 16 * ct + 4 * g);
@@ -622,7 +630,7 @@ __global__ __launch_bounds__(256) void wyc_prep_kernel(WycArgs a) {
             Qt[ta][1] += static_cast<float>(q4[1]) * er.y;
             Qt[ta][2] += static_cast<float>(q4[2]) * er.z;
             Qt[ta][3] += static_cast<float>(q4[3]) * er.w;
-            store4(Qo + (16 * ta + l16) * DK + 16 * ct + 4 * g, Qt[ta]);
+            store4(Qo + tiled16(16 * ta + l16, 16 * ct + 4 * g, DK), Qt[ta]);
           }
         }
       }
@@ -637,7 +645,7 @@ __global__ __launch_bounds__(256) void wyc_prep_kernel(WycArgs a) {
       for (int w = 0; w < VPW; ++w) {
         const int cv = wave + 4 * w;
         if (cv < nct_u) {
-          col_frags(tX, LDX, 16 * cv + l16, 1.f, xf[w]);
+          col_frags(tX, LDX, 16 * cv + l16, xf[w]);
           if (TWO) {
             F8 lf[2];
             up_frags(lkf, xf[w], 1.f, lf);
@@ -649,7 +657,7 @@ __global__ __launch_bounds__(256) void wyc_prep_kernel(WycArgs a) {
           tr_product(yf[w], mnf, Zt, false);
           if (TWO) tr_product(xf[w], mqf, Zt, true);
 #pragma unroll
-          for (int ta = 0; ta < 4; ++ta) store4(Zo + (16 * ta + l16) * DV + 16 * cv + 4 * g, Zt[ta]);
+          for (int ta = 0; ta < 4; ++ta) store4(Zo + tiled16(16 * ta + l16, 16 * cv + 4 * g, DV), Zt[ta]);
         }
       }
     }
@@ -659,35 +667,49 @@ __global__ __launch_bounds__(256) void wyc_prep_kernel(WycArgs a) {
     const __bf16* pn_src = TWO ? tP : tK;
 #pragma unroll 2
     for (int tl = 0; tl < NTD; ++tl) {
-      const int ch = 16 * tl + l16;
+      // the split rows as they are; their per-channel factor e^{G_n - G_ref} scales the rows of
+      // A' and D afterwards (lane: channel 16 tl + l16 of A', 16 tl + 4 g + i of D)
       F8 pf[2], kf[2];
-      col_frags(pn_src, LDT, ch, -fEgr[ch], pf);
-      if (TWO) col_frags(tK, LDT, ch, fEgr[ch], kf);
+      col_frags(pn_src, LDT, 16 * tl + l16, pf);
+      if (TWO) col_frags(tK, LDT, 16 * tl + l16, kf);
       f32x4 acc[WPW + VPW];
+      const float fa = -fEgr[16 * tl + l16];
+      const float4 fd = *reinterpret_cast<const float4*>(fEgr + 16 * tl + 4 * g);
 #pragma unroll
       for (int w = 0; w < WPW; ++w) {
         acc[w] = MM::mma8(wf[w][0], pf[0], zero4());
         acc[w] = MM::mma8(wf[w][1], pf[1], acc[w]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[w][i] *= fa;
       }
 #pragma unroll
       for (int w = 0; w < VPW; ++w) {
         f32x4& d = acc[WPW + w];
         d = MM::mma8(pf[0], yf[w][0], zero4());
         d = MM::mma8(pf[1], yf[w][1], d);
-        if (TWO) {
-          d = MM::mma8(kf[0], xf[w][0], d);
-          d = MM::mma8(kf[1], xf[w][1], d);
+        if (TWO) {  // Khat^T X - Phat^T Y
+          f32x4 dk = MM::mma8(kf[0], xf[w][0], zero4());
+          dk = MM::mma8(kf[1], xf[w][1], dk);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) d[i] = dk[i] - d[i];
+        } else {  // -Khat^T Y
+#pragma unroll
+          for (int i = 0; i < 4; ++i) d[i] = -d[i];
         }
+        d[0] *= fd.x;
+        d[1] *= fd.y;
+        d[2] *= fd.z;
+        d[3] *= fd.w;
       }
 #pragma unroll
       for (int w = 0; w < WPW; ++w) {
         const int ct = wave + 4 * w;
-        if (ct < NTD) store4(Ao + (16 * tl + l16) * DK + 16 * ct + 4 * g, acc[w]);
+        if (ct < NTD) store4(Ao + tiled16(16 * tl + l16, 16 * ct + 4 * g, DK), acc[w]);
       }
 #pragma unroll
       for (int w = 0; w < VPW; ++w) {
         const int cv = wave + 4 * w;
-        if (cv < nct_u) store4(Do + (16 * cv + l16) * DK + 16 * tl + 4 * g, acc[WPW + w]);
+        if (cv < nct_u) store4(Do + tiled16(16 * cv + l16, 16 * tl + 4 * g, DK), acc[WPW + w]);
       }
     }
   }
@@ -696,7 +718,37 @@ __global__ __launch_bounds__(256) void wyc_prep_kernel(WycArgs a) {
 
 // ------------------------------------------------------------------ state kernel
 
-// One chunk buffer: the chunk's affine map, in the swizzled form of DmaPlan (prefill_wy.h).
+// Direct-to-LDS copies of a tiled16 matrix into the swizzled row-major LDS form of DmaPlan
+// (prefill_wy.h): LDS piece s holds piece (s mod NCHR) ^ key of row s / NCHR, fetched from its tile
+// (tile rows `trs` bytes apart).  A lane's offsets repeat every P instructions (the key's row
+// period, 16 or 32 rows, over the rows an instruction covers), shifted by whole tile rows.
+template <int NCHR, bool PERM, int NPIECE>
+struct TiledPlan {
+  static_assert(NPIECE % 64 == 0, "whole instructions only");
+  static constexpr int NI = NPIECE / 64;
+  static constexpr int RPI = 64 / NCHR;  // rows per instruction
+  static constexpr int PERIOD = NCHR == 16 ? (PERM ? 8 : 4) : NCHR == 8 ? (PERM ? 4 : 2) : NCHR == 4 ? (PERM ? 2 : 1) : 1;
+  static constexpr int P = PERIOD < NI ? PERIOD : NI;
+  uint32_t off[8];  // (a fixed bound: see DmaPlan)
+  static_assert(P <= 8, "period above the fixed bound");
+  __device__ __forceinline__ void init(uint32_t trs, int lane) {
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+      const int s = 64 * i + lane, row = s / NCHR, piece = (s % NCHR) ^ swz_key<NCHR, PERM>(row);
+      off[i] = static_cast<uint32_t>(row >> 4) * trs + static_cast<uint32_t>(piece >> 1) * 512u +
+               static_cast<uint32_t>(row & 15) * 32u + static_cast<uint32_t>(piece & 1) * 16u;
+    }
+  }
+  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t r, unsigned char* lds, uint32_t trs) const {
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r, (__attribute__((address_space(3))) void*)(lds + 1024 * i), 16, off[i % P],
+          static_cast<int>(static_cast<uint32_t>(RPI * (i - i % P) / 16) * trs), 0, 0);
+  }
+};
+
+// One chunk buffer: the chunk's affine map, rows in the swizzled form above.
 template <int DK, int DVS>
 struct WycStateLayout {
   static constexpr int C = 64;
@@ -756,25 +808,27 @@ __global__ __launch_bounds__(64 * (2 + NSW)) void wyc_state_kernel(WycArgs a) {
   __bf16* oO = reinterpret_cast<__bf16*>(smem + L::oO);
 
   // ---------------- loader waves ----------------
-  DmaPlan<NCQ, true, DK * NCQ> plA;
-  DmaPlan<NCQ, false, C * NCQ> plQ;
-  DmaPlan<NCQ, false, DVS * NCQ> plD;
-  DmaPlan<NCU, false, C * NCU> plZ;
-  const uint32_t sq = DK * 2, su = static_cast<uint32_t>(DV * 2);
+  TiledPlan<NCQ, true, DK * NCQ> plA;
+  TiledPlan<NCQ, false, C * NCQ> plQ;
+  TiledPlan<NCQ, false, DVS * NCQ> plD;
+  TiledPlan<NCU, false, C * NCU> plZ;
+  const uint32_t tq = DK / 16 * 512, tu = static_cast<uint32_t>(DV / 16 * 512);  // tile row strides
   {
     const int dl = tid & 63;
-    plA.init(sq, dl);
-    plQ.init(sq, dl);
-    plD.init(sq, dl);
-    plZ.init(su, dl);
+    plA.init(tq, dl);
+    plQ.init(tq, dl);
+    plD.init(tq, dl);
+    plZ.init(tu, dl);
   }
   auto dma_chunk = [&](int64_t c) {
     unsigned char* B = buf(c);
     const int64_t cix = bh * nch + c;
-    plA.issue(make_rsrc(a.Ad + cix * DK * DK, DK * DK * 2), B + L::oA, sq);
-    plQ.issue(make_rsrc(a.Qd + cix * C * DK, C * DK * 2), B + L::oQ, sq);
-    plD.issue(make_rsrc(a.Dt + (cix * DV + col0) * DK, DVS * DK * 2), B + L::oD, sq);
-    plZ.issue(make_rsrc(a.Zd + cix * C * DV + col0, static_cast<uint32_t>((C * DV - col0) * 2)), B + L::oZ, su);
+    plA.issue(make_rsrc(a.Ad + cix * DK * DK, DK * DK * 2), B + L::oA, tq);
+    plQ.issue(make_rsrc(a.Qd + cix * C * DK, C * DK * 2), B + L::oQ, tq);
+    // the slice's rows of D^T are whole tile rows; its columns of Z' start at tile column col0 / 16
+    plD.issue(make_rsrc(a.Dt + cix * DV * DK + col0 * DK, DVS * DK * 2), B + L::oD, tq);
+    plZ.issue(make_rsrc(a.Zd + cix * C * DV + col0 * 16, static_cast<uint32_t>((C * DV - col0 * 16) * 2)),
+              B + L::oZ, tu);
     if (lane < (DK + 4) / 4) lds_dma16(make_rsrc(a.Egn + cix * (DK + 4), (DK + 4) * 4), B + L::oE, lane * 16);
   };
   // O rows of chunk c from the O buffer to HBM, 16 bytes per store; rows past the last token are
