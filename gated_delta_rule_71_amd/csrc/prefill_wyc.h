@@ -776,8 +776,9 @@ struct WycStateLayout {
 //            c mod 2 with chunk c+2 and the other waits for its loads of chunk c+1.
 // The state waves issue no global stores in the loop, and the loader wave that reads the O buffer
 // has no loads in flight when it does.
+// (one workgroup per compute unit by its LDS: the scheduler may spend registers on latency)
 template <int DK, int NSW>
-__global__ __launch_bounds__(64 * (2 + NSW)) void wyc_state_kernel(WycArgs a) {
+__global__ __launch_bounds__(64 * (2 + NSW)) __attribute__((amdgpu_waves_per_eu(1, 1))) void wyc_state_kernel(WycArgs a) {
   constexpr int DVS = 16 * NSW;
   using L = WycStateLayout<DK, DVS>;
   using MM = Mma<__bf16>;
@@ -820,10 +821,15 @@ __global__ __launch_bounds__(64 * (2 + NSW)) void wyc_state_kernel(WycArgs a) {
     plD.init(tq, dl);
     plZ.init(tu, dl);
   }
-  auto dma_chunk = [&](int64_t c) {
+  // a chunk's copies in two parts: dma_b (A', half the bytes) is issued a phase later than dma_a,
+  // so that neither part holds up a barrier (see the pipeline below)
+  auto dma_b = [&](int64_t c) {
+    const int64_t cix = bh * nch + c;
+    plA.issue(make_rsrc(a.Ad + cix * DK * DK, DK * DK * 2), buf(c) + L::oA, tq);
+  };
+  auto dma_a = [&](int64_t c) {
     unsigned char* B = buf(c);
     const int64_t cix = bh * nch + c;
-    plA.issue(make_rsrc(a.Ad + cix * DK * DK, DK * DK * 2), B + L::oA, tq);
     plQ.issue(make_rsrc(a.Qd + cix * C * DK, C * DK * 2), B + L::oQ, tq);
     // the slice's rows of D^T are whole tile rows; its columns of Z' start at tile column col0 / 16
     plD.issue(make_rsrc(a.Dt + cix * DV * DK + col0 * DK, DVS * DK * 2), B + L::oD, tq);
@@ -867,7 +873,9 @@ __global__ __launch_bounds__(64 * (2 + NSW)) void wyc_state_kernel(WycArgs a) {
   bf16x4 zv[4];
   auto compute = [&](int64_t c) {
     const unsigned char* B = buf(c);
-    F8 fa[2][NTD], fq[2][4];
+    // fragments of k-step kb in ring slot kb mod 3, read two k-steps ahead of their products
+    constexpr int NR = NKB < 3 ? NKB : 3;
+    F8 fa[NR][NTD], fq[NR][4];
     auto read_k = [&](int kb, int r) {
 #pragma unroll
       for (int tl = 0; tl < NTD; ++tl) fa[r][tl] = lds_piece<NCQ, true>(B + L::oA, perm_row(tl, l16), 4 * kb + g);
@@ -875,6 +883,7 @@ __global__ __launch_bounds__(64 * (2 + NSW)) void wyc_state_kernel(WycArgs a) {
       for (int ta = 0; ta < 4; ++ta) fq[r][ta] = lds_piece<NCQ, false>(B + L::oQ, 16 * ta + l16, 4 * kb + g);
     };
     read_k(0, 0);
+    if (NKB > 1) read_k(1, 1);
     const float* E = reinterpret_cast<const float*>(B + L::oE);
     float4 e4[NTD];
     bf16x4 d4[NTD];
@@ -897,11 +906,13 @@ __global__ __launch_bounds__(64 * (2 + NSW)) void wyc_state_kernel(WycArgs a) {
     for (int ta = 0; ta < 4; ++ta) Ot[ta] = zero4();
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      if (kb + 1 < NKB) read_k(kb + 1, (kb + 1) & 1);
+      if (kb + 2 < NKB) read_k(kb + 2, (kb + 2) % NR);
+      __builtin_amdgcn_sched_barrier(0);  // the reads stay ahead of this k-step's products
 #pragma unroll
-      for (int tl = 0; tl < NTD; ++tl) S[tl] = MM::mma8(fa[kb & 1][tl], sf[kb], S[tl]);
+      for (int tl = 0; tl < NTD; ++tl) S[tl] = MM::mma8(fa[kb % NR][tl], sf[kb], S[tl]);
 #pragma unroll
-      for (int ta = 0; ta < 4; ++ta) Ot[ta] = MM::mma8(sf[kb], fq[kb & 1][ta], Ot[ta]);
+      for (int ta = 0; ta < 4; ++ta) Ot[ta] = MM::mma8(sf[kb], fq[kb % NR][ta], Ot[ta]);
+      __builtin_amdgcn_sched_barrier(0);
     }
     const int col = cb + 4 * g;
 #pragma unroll
@@ -920,28 +931,39 @@ __global__ __launch_bounds__(64 * (2 + NSW)) void wyc_state_kernel(WycArgs a) {
   };
 
   // ---------------- pipeline ----------------
+  // Chunk c+1's copies: dma_a by loader wave (c+1) mod 2 right after barrier A of chunk c-1 (the
+  // buffer is free from there), dma_b by the same wave while the state waves compute chunk c, and
+  // that wave waits for both between barriers A and B of chunk c.  The other loader wave copies
+  // the O rows of chunk c-1 out while chunk c computes.
   if (nch > 0) {
     if (wave == 0) {
-      dma_chunk(0);
+      dma_a(0);
+      dma_b(0);
       __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     }
-    if (wave == 1 && nch > 1) dma_chunk(1);
+    if (wave == 1 && nch > 1) {
+      dma_a(1);
+      dma_b(1);
+    }
   }
   lds_barrier();
   for (int64_t ch = 0; ch < nch; ++ch) {
     // opaque per chunk: keeps lane-dependent LDS addresses from being hoisted out of the loop
     asm volatile("" : "+v"(lane), "+v"(g), "+v"(l16));
     GDR_MARK(0);
-    if (!loader)
+    if (!loader) {
       compute(ch);
-    else if (wave == static_cast<int>(ch & 1) && ch > 0)
-      store_o(ch - 1);
+    } else if (wave == static_cast<int>(ch & 1)) {
+      if (ch > 0) store_o(ch - 1);
+    } else if (ch > 0 && ch + 1 < nch) {
+      dma_b(ch + 1);
+    }
     GDR_MARK(1);
     lds_barrier_keep_vm();  // A: buffer ch mod 2 and the O buffer are free
     GDR_MARK(2);
     if (loader) {
       if (wave == static_cast<int>(ch & 1)) {
-        if (ch + 2 < nch) dma_chunk(ch + 2);
+        if (ch + 2 < nch) dma_a(ch + 2);
       } else {
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // this wave's loads of chunk ch+1
       }
