@@ -749,24 +749,37 @@ struct TiledPlan {
 };
 
 // One chunk buffer: the chunk's affine map, rows in the swizzled form above.
-template <int DK, int DVS>
+template <int DK, int DVS, int NXW>
 struct WycStateLayout {
   static constexpr int C = 64;
   static constexpr int NCQ = DK / 8;   // 16-byte pieces per row of dk channels
   static constexpr int NCU = DVS / 8;  // pieces per row of a value slice
-  static constexpr int oA = 0;                    // A' [dk][dk], rows read in perm_row order
-  static constexpr int oQ = oA + DK * DK * 2;     // Q' [64][dk]
+  static constexpr int AS = DK * DK * 2;          // one A' slot [dk][dk], rows read in perm_row order
+  // a chunk buffer (two of them)
+  static constexpr int oQ = 0;                    // Q' [64][dk]
   static constexpr int oD = oQ + C * DK * 2;      // D^T slice [DVS][dk]
   static constexpr int oZ = oD + DVS * DK * 2;    // Z' slice [64][DVS]
   static constexpr int oE = oZ + C * DVS * 2;     // e^{G_n} [dk] fp32 (+ flag)
   static constexpr int BUF = oE + ((DK + 4) * 4 + 255) / 256 * 256;
-  static constexpr int oO = 2 * BUF;              // O rows of one chunk [64][DVS]
-  static constexpr int total = oO + C * DVS * 2;
+  static constexpr int XW = DK / 64 * 1024;       // one wave's bf16 S half (its pair fragments, 16 bytes a lane)
+  static constexpr int REST = 2 * BUF + C * DVS * 2 + 2 * NXW * XW;
+  static constexpr int NA = 3 * AS + REST <= kLdsLimit ? 3 : 2;  // A' slots
+  static constexpr int oB = NA * AS;              // the two chunk buffers
+  static constexpr int oO = oB + 2 * BUF;         // O rows of one chunk [64][DVS]
+  static constexpr int oX = oO + C * DVS * 2;     // bf16 S halves exchanged: [2][NXW waves][XW]
+  static constexpr int total = oX + 2 * NXW * XW;
   static constexpr bool fits = total <= kLdsLimit;
 };
 
-// Workgroup = 2 loader waves and NSW state waves for one state and a slice of DVS = 16 NSW value
-// columns; state wave j holds columns 16 j .. 16 j + 15 of the slice.  Chunk c's map sits in LDS
+// s_waitcnt immediate that waits until at most n vector memory operations are outstanding
+constexpr int wait_vmcnt(int n) { return 0x0F70 | (n & 0xF) | (((n >> 4) & 3) << 14); }
+
+// Workgroup = 2 loader waves and NSW x SPLIT state waves for one state and a slice of DVS = 16 NSW
+// value columns; state wave j holds columns 16 (j / SPLIT) .. + 15 of the slice and, with SPLIT = 2,
+// only half of S's channels (rows): the S update needs all of bf16(S), so the two waves of a
+// column group swap their bf16 halves through LDS once per chunk (written at the end of a
+// chunk's products, read at the start of the next one's: barriers A and B lie between), and each
+// takes half of O's token rows.  Chunk c's map sits in LDS
 // buffer c mod 2, filled by direct-to-LDS loads that loader wave c mod 2 issues a whole chunk
 // ahead.  Two barriers per chunk c:
 //   up to A: the state waves compute, from S_b = bf16(S),
@@ -777,16 +790,18 @@ struct WycStateLayout {
 // The state waves issue no global stores in the loop, and the loader wave that reads the O buffer
 // has no loads in flight when it does.
 // (one workgroup per compute unit by its LDS: the scheduler may spend registers on latency)
-template <int DK, int NSW>
-__global__ __launch_bounds__(64 * (2 + NSW)) __attribute__((amdgpu_waves_per_eu(1, 1))) void wyc_state_kernel(WycArgs a) {
+template <int DK, int NSW, int SPLIT>
+__global__ __launch_bounds__(64 * (2 + NSW * SPLIT)) __attribute__((amdgpu_waves_per_eu(1, 1))) void wyc_state_kernel(WycArgs a) {
   constexpr int DVS = 16 * NSW;
-  using L = WycStateLayout<DK, DVS>;
+  using L = WycStateLayout<DK, DVS, SPLIT == 2 ? NSW * 2 : 0>;
   using MM = Mma<__bf16>;
   using F8 = MM::F8;
   static_assert(L::fits, "LDS layout exceeds the gfx950 workgroup limit");
   static_assert(DK % 32 == 0, "dk must be a multiple of 32");
+  static_assert(SPLIT == 1 || (SPLIT == 2 && DK >= 64), "rows split in halves of whole k-steps");
   constexpr int C = L::C, NCQ = L::NCQ, NCU = L::NCU;
   constexpr int NTD = DK / 16, NKB = DK / 32;
+  constexpr int NTH = NTD / SPLIT, NKH = NKB / SPLIT, NTA = 4 / SPLIT;  // this wave's tiles, k-steps, O tiles
 
   __shared__ __attribute__((aligned(1024))) unsigned char smem[L::total];
 
@@ -794,7 +809,9 @@ __global__ __launch_bounds__(64 * (2 + NSW)) __attribute__((amdgpu_waves_per_eu(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   int lane = tid & 63, g = lane >> 4, l16 = lane & 15;
   const bool loader = wave < 2;
-  const int cb = loader ? 0 : 16 * (wave - 2);  // this state wave's first column in the slice
+  const int sw = loader ? 0 : wave - 2;         // state wave index
+  const int cb = 16 * (sw / SPLIT);             // its first column in the slice
+  const int rh = sw % SPLIT;                    // its half of the channels (rows): tiles rh NTH ..
 
   const int64_t nb = gridDim.x, bid = blockIdx.x;
   const int64_t p = (nb % 8 == 0) ? (bid % 8) * (nb / 8) + bid / 8 : bid;
@@ -805,7 +822,8 @@ __global__ __launch_bounds__(64 * (2 + NSW)) __attribute__((amdgpu_waves_per_eu(
   const int64_t col0 = static_cast<int64_t>(sl) * DVS;
   const uint32_t hdv = static_cast<uint32_t>(H * DV * 2);
 
-  auto buf = [&](int64_t c) -> unsigned char* { return smem + (c & 1) * L::BUF; };
+  auto buf = [&](int64_t c) -> unsigned char* { return smem + L::oB + (c & 1) * L::BUF; };
+  auto aslot = [&](int64_t c) -> unsigned char* { return smem + (c % L::NA) * L::AS; };
   __bf16* oO = reinterpret_cast<__bf16*>(smem + L::oO);
 
   // ---------------- loader waves ----------------
@@ -821,11 +839,11 @@ __global__ __launch_bounds__(64 * (2 + NSW)) __attribute__((amdgpu_waves_per_eu(
     plD.init(tq, dl);
     plZ.init(tu, dl);
   }
-  // a chunk's copies in two parts: dma_b (A', half the bytes) is issued a phase later than dma_a,
-  // so that neither part holds up a barrier (see the pipeline below)
+  // a chunk's copies in two parts: dma_b (A', half the bytes, into its own slot) and dma_a (the
+  // rest, into the chunk buffer); see the pipeline below
   auto dma_b = [&](int64_t c) {
     const int64_t cix = bh * nch + c;
-    plA.issue(make_rsrc(a.Ad + cix * DK * DK, DK * DK * 2), buf(c) + L::oA, tq);
+    plA.issue(make_rsrc(a.Ad + cix * DK * DK, DK * DK * 2), aslot(c), tq);
   };
   auto dma_a = [&](int64_t c) {
     unsigned char* B = buf(c);
@@ -852,136 +870,176 @@ __global__ __launch_bounds__(64 * (2 + NSW)) __attribute__((amdgpu_waves_per_eu(
   };
 
   // ---------------- state waves ----------------
-  // S[tl]: accumulator row 4 g + i holds channel perm_row(tl, 4 g + i) of column cb + l16, so
-  // that the pair fragment of tiles 2 kb, 2 kb + 1 carries channels 32 kb + 8 g .. 32 kb + 8 g + 7
-  f32x4 S[NTD];
+  // S[u] (u = tl - rh NTH): accumulator row 4 g + i holds channel perm_row(tl, 4 g + i) of column
+  // cb + l16, so that the pair fragment of tiles 2 kb, 2 kb + 1 carries channels 32 kb + 8 g ..
+  // 32 kb + 8 g + 7 (k-steps rh NKH .. are this wave's own)
+  f32x4 S[NTH];
 #pragma unroll
-  for (int tl = 0; tl < NTD; ++tl) {
-    S[tl] = zero4();
+  for (int u = 0; u < NTH; ++u) {
+    S[u] = zero4();
     if (!loader && a.S0 != nullptr) {
       const int64_t sb = bh * DK * DV + col0 + cb + l16;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) S[tl][i] = a.S0[sb + (int64_t)perm_row(tl, 4 * g + i) * DV];
+      for (int i = 0; i < 4; ++i) S[u][i] = a.S0[sb + (int64_t)perm_row(rh * NTH + u, 4 * g + i) * DV];
     }
   }
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
+  // this wave's bf16 S half into exchange slot `slot` (SPLIT = 2), as its pair fragments
+  F8 sown[NKH];
+  auto make_own = [&]() {
+#pragma unroll
+    for (int h = 0; h < NKH; ++h) sown[h] = acc_pair_frag<__bf16>(S[2 * h], S[2 * h + 1]);
+  };
+  auto put_own = [&](int slot) {
+    if constexpr (SPLIT == 2) {
+      unsigned char* X = smem + L::oX + (slot * NSW * 2 + sw) * L::XW;
+#pragma unroll
+      for (int h = 0; h < NKH; ++h) *reinterpret_cast<F8*>(X + h * 1024 + lane * 16) = sown[h];
+    }
+  };
+  if (!loader) {
+    make_own();
+    put_own(0);
+  }
+
   // Operands (one 16-byte read each): A' rows perm_row(tl, l16) (S's channel order) and Q' rows
   // 16 ta + l16, channels 32 kb + 8 g ..;  D^T row cb + l16 and e^{G_n} at this lane's channels;
   // Z' row 16 ta + l16, columns cb + 4 g ..
-  f32x4 Ot[4];
-  bf16x4 zv[4];
+  f32x4 Ot[NTA];
+  bf16x4 zv[NTA];
   auto compute = [&](int64_t c) {
     const unsigned char* B = buf(c);
+    const unsigned char* A = aslot(c);
     // fragments of k-step kb in ring slot kb mod 3, read two k-steps ahead of their products
     constexpr int NR = NKB < 3 ? NKB : 3;
-    F8 fa[NR][NTD], fq[NR][4];
+    F8 fa[NR][NTH], fq[NR][NTA];
     auto read_k = [&](int kb, int r) {
 #pragma unroll
-      for (int tl = 0; tl < NTD; ++tl) fa[r][tl] = lds_piece<NCQ, true>(B + L::oA, perm_row(tl, l16), 4 * kb + g);
+      for (int u = 0; u < NTH; ++u) fa[r][u] = lds_piece<NCQ, true>(A, perm_row(rh * NTH + u, l16), 4 * kb + g);
 #pragma unroll
-      for (int ta = 0; ta < 4; ++ta) fq[r][ta] = lds_piece<NCQ, false>(B + L::oQ, 16 * ta + l16, 4 * kb + g);
+      for (int t = 0; t < NTA; ++t) fq[r][t] = lds_piece<NCQ, false>(B + L::oQ, 16 * (rh * NTA + t) + l16, 4 * kb + g);
     };
     read_k(0, 0);
     if (NKB > 1) read_k(1, 1);
-    const float* E = reinterpret_cast<const float*>(B + L::oE);
-    float4 e4[NTD];
-    bf16x4 d4[NTD];
-#pragma unroll
-    for (int tl = 0; tl < NTD; ++tl) {
-      e4[tl] = *reinterpret_cast<const float4*>(E + perm_row(tl, 4 * g));
-      d4[tl] = *reinterpret_cast<const bf16x4*>(swz_addr<NCQ, false>(B + L::oD, cb + l16, 4 * (tl >> 1) + g) + 8 * (tl & 1));
-    }
+    // bf16(S) for every k-step: this wave's own, and the other half from its partner
     F8 sf[NKB];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) sf[kb] = acc_pair_frag<__bf16>(S[2 * kb], S[2 * kb + 1]);
+    for (int kb = 0; kb < NKB; ++kb) {
+      if (kb / NKH == rh) {
+        sf[kb] = sown[kb % NKH];
+      } else if constexpr (SPLIT == 2) {
+        const unsigned char* X = smem + L::oX + ((int)(c & 1) * NSW * 2 + (sw ^ 1)) * L::XW;
+        sf[kb] = *reinterpret_cast<const F8*>(X + (kb % NKH) * 1024 + lane * 16);
+      }
+    }
+    const float* E = reinterpret_cast<const float*>(B + L::oE);
+    float4 e4[NTH];
+    bf16x4 d4[NTH];
 #pragma unroll
-    for (int tl = 0; tl < NTD; ++tl) {
-      S[tl][0] = S[tl][0] * e4[tl].x + static_cast<float>(d4[tl][0]);
-      S[tl][1] = S[tl][1] * e4[tl].y + static_cast<float>(d4[tl][1]);
-      S[tl][2] = S[tl][2] * e4[tl].z + static_cast<float>(d4[tl][2]);
-      S[tl][3] = S[tl][3] * e4[tl].w + static_cast<float>(d4[tl][3]);
+    for (int u = 0; u < NTH; ++u) {
+      const int tl = rh * NTH + u;
+      e4[u] = *reinterpret_cast<const float4*>(E + perm_row(tl, 4 * g));
+      d4[u] = *reinterpret_cast<const bf16x4*>(swz_addr<NCQ, false>(B + L::oD, cb + l16, 4 * (tl >> 1) + g) + 8 * (tl & 1));
     }
 #pragma unroll
-    for (int ta = 0; ta < 4; ++ta) Ot[ta] = zero4();
+    for (int u = 0; u < NTH; ++u) {
+      S[u][0] = S[u][0] * e4[u].x + static_cast<float>(d4[u][0]);
+      S[u][1] = S[u][1] * e4[u].y + static_cast<float>(d4[u][1]);
+      S[u][2] = S[u][2] * e4[u].z + static_cast<float>(d4[u][2]);
+      S[u][3] = S[u][3] * e4[u].w + static_cast<float>(d4[u][3]);
+    }
+#pragma unroll
+    for (int t = 0; t < NTA; ++t) Ot[t] = zero4();
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       if (kb + 2 < NKB) read_k(kb + 2, (kb + 2) % NR);
       __builtin_amdgcn_sched_barrier(0);  // the reads stay ahead of this k-step's products
 #pragma unroll
-      for (int tl = 0; tl < NTD; ++tl) S[tl] = MM::mma8(fa[kb % NR][tl], sf[kb], S[tl]);
+      for (int u = 0; u < NTH; ++u) S[u] = MM::mma8(fa[kb % NR][u], sf[kb], S[u]);
 #pragma unroll
-      for (int ta = 0; ta < 4; ++ta) Ot[ta] = MM::mma8(sf[kb], fq[kb % NR][ta], Ot[ta]);
+      for (int t = 0; t < NTA; ++t) Ot[t] = MM::mma8(sf[kb], fq[kb % NR][t], Ot[t]);
       __builtin_amdgcn_sched_barrier(0);
     }
     const int col = cb + 4 * g;
 #pragma unroll
-    for (int ta = 0; ta < 4; ++ta)
-      zv[ta] = *reinterpret_cast<const bf16x4*>(swz_addr<NCU, false>(B + L::oZ, 16 * ta + l16, col >> 3) + 8 * ((col >> 2) & 1));
+    for (int t = 0; t < NTA; ++t)
+      zv[t] = *reinterpret_cast<const bf16x4*>(swz_addr<NCU, false>(B + L::oZ, 16 * (rh * NTA + t) + l16, col >> 3) + 8 * ((col >> 2) & 1));
+    // the next chunk's bf16(S), this wave's half, for both waves of the pair
+    make_own();
+    put_own(static_cast<int>((c + 1) & 1));
   };
-  // Ot[ta] lane (g, l16) holds O[16 ta + l16][cb + 4 g + i]
+  // Ot[t] lane (g, l16) holds O[16 ta + l16][cb + 4 g + i], ta = rh NTA + t
   auto write_o = [&]() {
 #pragma unroll
-    for (int ta = 0; ta < 4; ++ta) {
+    for (int t = 0; t < NTA; ++t) {
       bf16x4 ob;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) ob[i] = static_cast<__bf16>(Ot[ta][i] + static_cast<float>(zv[ta][i]));
-      *reinterpret_cast<bf16x4*>(oO + (16 * ta + l16) * DVS + cb + 4 * g) = ob;
+      for (int i = 0; i < 4; ++i) ob[i] = static_cast<__bf16>(Ot[t][i] + static_cast<float>(zv[t][i]));
+      *reinterpret_cast<bf16x4*>(oO + (16 * (rh * NTA + t) + l16) * DVS + cb + 4 * g) = ob;
     }
   };
 
   // ---------------- pipeline ----------------
-  // Chunk c+1's copies: dma_a by loader wave (c+1) mod 2 right after barrier A of chunk c-1 (the
-  // buffer is free from there), dma_b by the same wave while the state waves compute chunk c, and
-  // that wave waits for both between barriers A and B of chunk c.  The other loader wave copies
-  // the O rows of chunk c-1 out while chunk c computes.
+  // Loader wave 0 issues every A' copy (dma_b), NA - 1 chunks ahead, while the state waves
+  // compute (the slot of chunk c + NA - 1 held chunk c - 1, used before barrier A of chunk c - 1),
+  // and between barriers A and B of chunk c waits until chunk c+1's copy is in.  Loader wave 1
+  // issues the rest of chunk c+2 (dma_a) between barriers A and B of chunk c (its buffer is free
+  // from A), and while chunk c computes waits for its copies of chunk c+1 and then copies the O
+  // rows of chunk c-1 out.  Vector memory loads complete in order, so a wait for "at most n in
+  // flight" covers every load older than the last n.
+  constexpr int NIA = decltype(plA)::NI;
   if (nch > 0) {
     if (wave == 0) {
       dma_a(0);
-      dma_b(0);
-      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      for (int k = 0; k < L::NA - 1 && k < nch; ++k) dma_b(k);
     }
-    if (wave == 1 && nch > 1) {
-      dma_a(1);
-      dma_b(1);
-    }
+    if (wave == 1 && nch > 1) dma_a(1);
+    if (loader) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   }
   lds_barrier();
   for (int64_t ch = 0; ch < nch; ++ch) {
     // opaque per chunk: keeps lane-dependent LDS addresses from being hoisted out of the loop
     asm volatile("" : "+v"(lane), "+v"(g), "+v"(l16));
     GDR_MARK(0);
+    const bool ahead = ch + L::NA - 1 < nch;  // wave 0 issues A' of chunk ch + NA - 1 now
     if (!loader) {
       compute(ch);
-    } else if (wave == static_cast<int>(ch & 1)) {
+    } else if (wave == 0) {
+      if (ahead) dma_b(ch + L::NA - 1);
+    } else {
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // its copies of chunk ch+1 (and older stores)
       if (ch > 0) store_o(ch - 1);
-    } else if (ch > 0 && ch + 1 < nch) {
-      dma_b(ch + 1);
     }
     GDR_MARK(1);
-    lds_barrier_keep_vm();  // A: buffer ch mod 2 and the O buffer are free
+    lds_barrier_keep_vm();  // A: buffer ch mod 2, A' slot ch mod NA and the O buffer are free
     GDR_MARK(2);
-    if (loader) {
-      if (wave == static_cast<int>(ch & 1)) {
-        if (ch + 2 < nch) dma_a(ch + 2);
-      } else {
-        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // this wave's loads of chunk ch+1
-      }
-    } else {
+    if (!loader) {
       write_o();
+    } else if (wave == 0) {
+      // A' of chunk ch+1 in; only the A' copies issued after it may still be in flight
+      if (ahead && L::NA == 3)
+        __builtin_amdgcn_s_waitcnt(wait_vmcnt(NIA));
+      else
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    } else {
+      if (ch + 2 < nch) dma_a(ch + 2);
     }
     GDR_MARK(3);
-    lds_barrier_keep_vm();  // B: chunk ch+1 is in buffer (ch+1) mod 2, O of chunk ch in the O buffer
+    lds_barrier_keep_vm();  // B: chunk ch+1 is in, O of chunk ch in the O buffer
     GDR_MARK(4);
   }
-  if (wave == 0 && nch > 0) store_o(nch - 1);
+  if (wave == 1 && nch > 0) {
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    store_o(nch - 1);
+  }
 
   if (!loader && a.S_T != nullptr) {
     const int64_t sb = bh * DK * DV + col0 + cb + l16;
 #pragma unroll
-    for (int tl = 0; tl < NTD; ++tl)
+    for (int u = 0; u < NTH; ++u)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a.S_T[sb + (int64_t)perm_row(tl, 4 * g + i) * DV] = S[tl][i];
+      for (int i = 0; i < 4; ++i) a.S_T[sb + (int64_t)perm_row(rh * NTH + u, 4 * g + i) * DV] = S[u][i];
   }
 }
 

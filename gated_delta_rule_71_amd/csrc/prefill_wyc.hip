@@ -24,11 +24,14 @@ WycSizes wyc_sizes(int64_t nstate, int64_t T, int64_t DK, int64_t DV) {
   return s;
 }
 
+// SPLIT = 2: two state waves per 16 columns, each with half of the channels (d_k >= 64, up to 32
+// columns a workgroup by LDS)
 template <int DK, int NSW>
 void launch_state(WycArgs a, int64_t nstate, hipStream_t s) {
   a.nsl = static_cast<int>(a.DV / (16 * NSW));
-  hipLaunchKernelGGL((wyc_state_kernel<DK, NSW>), dim3((unsigned)(nstate * a.nsl)), dim3(64 * (2 + NSW)), 0,
-                     s, a);
+  constexpr int SPLIT = (DK >= 64 && NSW <= 2) ? 2 : 1;
+  hipLaunchKernelGGL((wyc_state_kernel<DK, NSW, SPLIT>), dim3((unsigned)(nstate * a.nsl)),
+                     dim3(64 * (2 + NSW * SPLIT)), 0, s, a);
 }
 
 template <int DK, int MODE>
