@@ -33,6 +33,7 @@
 // forms its four matrices by running the recurrence over the chunk token by token in fp32 from
 // the identity (A) and from zero (D) instead: exact for any gate values.
 #pragma once
+#include <type_traits>
 #include "gdr_common.h"
 #include "mfma.h"
 #include "prefill_kernel.h"
@@ -74,8 +75,8 @@ __host__ __device__ constexpr inline int64_t tiled16(int64_t r, int64_t c, int64
 
 // ------------------------------------------------------------------ chunk-local kernel
 
-template <int DK, int DVP, int MODE>
-struct WycPrepLayout {
+template <int DK, int DVP, int MODE, int NSEGX>
+struct WycPrepLayoutN {
   static constexpr bool TWO = MODE == 2;
   static constexpr int C = 64;
   static constexpr int LDT = DK + 8;
@@ -85,7 +86,7 @@ struct WycPrepLayout {
   static constexpr int LDI = 24;
   static constexpr int LDL = 20;
   static constexpr int NCG = DK / 8;
-  static constexpr int NSEG = (256 / NCG) < C ? (256 / NCG) : C;
+  static constexpr int NSEG = NSEGX;  // token segments of the prefix sums (threads NSEG * NCG)
   static constexpr int TPS = C / NSEG;
   static constexpr int oQ = 0;                              // split Qhat  [64][LDT]
   static constexpr int oC = oQ + C * LDT * 2;               // split Chat  [64][LDT]
@@ -105,44 +106,59 @@ struct WycPrepLayout {
   static constexpr bool fits = total <= kLdsLimit;
   static_assert(oF % 16 == 0, "the per-channel factors are read as float4");
 };
+// 512 threads; the prefix sums over as many token segments as there are threads for (NT / NCG,
+// at most 64) when their LDS fits, else half as many
+template <int DK, int DVP, int MODE>
+struct WycPrepLayoutSel {
+  static constexpr int NT = 512;
+  static constexpr int NS1 = (NT / (DK / 8)) < 64 ? (NT / (DK / 8)) : 64;
+  using type = typename std::conditional<WycPrepLayoutN<DK, DVP, MODE, NS1>::fits, WycPrepLayoutN<DK, DVP, MODE, NS1>,
+                                         WycPrepLayoutN<DK, DVP, MODE, NS1 / 2>>::type;
+};
+template <int DK, int DVP, int MODE>
+using WycPrepLayout = typename WycPrepLayoutSel<DK, DVP, MODE>::type;
 
-// The affine map of a flagged chunk from the recurrence itself, token by token in fp32: thread
-// j < dk carries column j of the transition product A (started from the identity; its outputs
-// q_t A_t are row t of Q'), threads 128 + j carry value column v = j, j + 128 of the state D
-// started from zero (outputs q_t D_t: Z').  Every lane reads the same raw row at once.  Rows past
-// the last token are zero (alpha = 1, no erase, no write), so all 64 rows run.
+// The affine map of a flagged chunk from the recurrence itself, token by token in fp32.  Two
+// adjacent lanes share a column, 64 channels each (the dot products are the pair's two partial
+// sums): lane pairs 0 .. 127 carry column j of the transition product A (started from the
+// identity; its outputs q_t A_t are row t of Q'), lane pairs 128 .. 255 carry value column
+// v (and v + 128) of the state D started from zero (outputs q_t D_t: Z').  Every lane pair reads
+// the same raw row at once.  Rows past the last token are zero (alpha = 1, no erase, no write),
+// so all 64 rows run.
 template <int DK, int LDT, int LDX, bool TWO>
 __device__ __forceinline__ void wyc_exact_chunk(const WycArgs& a, int64_t cix, const __bf16* rQ,
                                                 const __bf16* rK, const __bf16* rC, const __bf16* rL,
-                                                const __bf16* tX, float egn_own, int tid) {
-  constexpr int C = 64;
+                                                const __bf16* tX, const float* fEgn, int tid) {
+  constexpr int C = 64, DH = DK / 2;
   const int64_t DV = a.DV;
+  const int hf = tid & 1, pr = tid >> 1, d0 = hf * DH;  // this lane's channels d0 .. d0 + DH - 1
   // one column s through the chunk; col_x < 0: no write (the transition); y_t = q_t s_t to element
-  // (t, ycol) of yout (tiled, ypitch columns)
-  auto run = [&](float (&s)[DK], int col_x, __bf16* yout, int ycol, int64_t ypitch) {
+  // (t, ycol) of yout (tiled, ypitch columns), by the even lane
+  auto run = [&](float (&s)[DH], int col_x, __bf16* yout, int ycol, int64_t ypitch) {
     for (int t = 0; t < C; ++t) {
       float r = 0.f;  // c_t s (after the decay in MODE 1)
 #pragma unroll
-      for (int p = 0; p < DK / 8; ++p) {
+      for (int p = 0; p < DH / 8; ++p) {
         float c8[8];
-        load8f(reinterpret_cast<const bf16_t*>(rC + t * LDT + 8 * p), c8);
+        load8f(reinterpret_cast<const bf16_t*>(rC + t * LDT + d0 + 8 * p), c8);
         if (!TWO) {
           float l8[8];
-          load8f(reinterpret_cast<const bf16_t*>(rL + t * DK + 8 * p), l8);
+          load8f(reinterpret_cast<const bf16_t*>(rL + t * DK + d0 + 8 * p), l8);
 #pragma unroll
           for (int e = 0; e < 8; ++e) s[8 * p + e] *= __expf(l8[e]);
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e) r += c8[e] * s[8 * p + e];
       }
+      r += __shfl_xor(r, 1);
       const float x = col_x >= 0 ? static_cast<float>(tX[t * LDX + col_x]) : 0.f;
       float y = 0.f;
 #pragma unroll
-      for (int p = 0; p < DK / 8; ++p) {
+      for (int p = 0; p < DH / 8; ++p) {
         float k8[8], q8[8], l8[8];
-        load8f(reinterpret_cast<const bf16_t*>(rK + t * LDT + 8 * p), k8);
-        load8f(reinterpret_cast<const bf16_t*>(rQ + t * LDT + 8 * p), q8);
-        if (TWO) load8f(reinterpret_cast<const bf16_t*>(rL + t * DK + 8 * p), l8);
+        load8f(reinterpret_cast<const bf16_t*>(rK + t * LDT + d0 + 8 * p), k8);
+        load8f(reinterpret_cast<const bf16_t*>(rQ + t * LDT + d0 + 8 * p), q8);
+        if (TWO) load8f(reinterpret_cast<const bf16_t*>(rL + t * DK + d0 + 8 * p), l8);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           float sv = s[8 * p + e] - k8[e] * r;
@@ -152,40 +168,44 @@ __device__ __forceinline__ void wyc_exact_chunk(const WycArgs& a, int64_t cix, c
           y += q8[e] * sv;
         }
       }
-      yout[tiled16(t, ycol, ypitch)] = static_cast<__bf16>(y);
+      y += __shfl_xor(y, 1);
+      if (hf == 0) yout[tiled16(t, ycol, ypitch)] = static_cast<__bf16>(y);
     }
   };
-  const int j = tid & 127;
-  if (tid < 128) {
+  if (pr < 128) {
+    const int j = pr;
     if (j < DK) {
-      float s[DK];
+      float s[DH];
 #pragma unroll
-      for (int i = 0; i < DK; ++i) s[i] = i == j ? 1.f : 0.f;
+      for (int i = 0; i < DH; ++i) s[i] = d0 + i == j ? 1.f : 0.f;
       run(s, -1, a.Qd + cix * C * DK, j, DK);
-      __bf16* Ao = a.Ad + cix * DK * DK;  // A' = A - diag(e^{G_n}), column j (egn_own: channel j)
+      // A' = A - diag(e^{G_n}), column j
+      const float egn_j = fEgn[j];
+      __bf16* Ao = a.Ad + cix * DK * DK;
 #pragma unroll
-      for (int i = 0; i < DK; ++i) Ao[tiled16(i, j, DK)] = static_cast<__bf16>(s[i] - (i == j ? egn_own : 0.f));
+      for (int i = 0; i < DH; ++i)
+        Ao[tiled16(d0 + i, j, DK)] = static_cast<__bf16>(s[i] - (d0 + i == j ? egn_j : 0.f));
     }
   } else {
-    for (int v = j; v < DV; v += 128) {
-      float s[DK];
+    for (int v = pr - 128; v < DV; v += 128) {
+      float s[DH];
 #pragma unroll
-      for (int i = 0; i < DK; ++i) s[i] = 0.f;
+      for (int i = 0; i < DH; ++i) s[i] = 0.f;
       run(s, v, a.Zd + cix * C * DV, v, DV);
-      __bf16* Do = a.Dt + cix * DV * DK;  // row v of D^T
+      __bf16* Do = a.Dt + cix * DV * DK;  // row v of D^T, this lane's channels
 #pragma unroll
-      for (int p = 0; p < DK / 8; ++p) {
+      for (int p = 0; p < DH / 8; ++p) {
         bf16x8 d8;
 #pragma unroll
         for (int e = 0; e < 8; ++e) d8[e] = static_cast<__bf16>(s[8 * p + e]);
-        *reinterpret_cast<bf16x8*>(Do + tiled16(v, 8 * p, DK)) = d8;
+        *reinterpret_cast<bf16x8*>(Do + tiled16(v, d0 + 8 * p, DK)) = d8;
       }
     }
   }
 }
 
 template <int DK, int DVP, int MODE>
-__global__ __launch_bounds__(256) void wyc_prep_kernel(WycArgs a) {
+__global__ __launch_bounds__(512) void wyc_prep_kernel(WycArgs a) {
   using L = WycPrepLayout<DK, DVP, MODE>;
   using MM = Mma<__bf16>;
   using F8 = MM::F8;
@@ -195,6 +215,7 @@ __global__ __launch_bounds__(256) void wyc_prep_kernel(WycArgs a) {
   constexpr int C = L::C, LDT = L::LDT, LDX = L::LDX, LDD = L::LDD, LDA = L::LDA, LDI = L::LDI,
                 LDL = L::LDL;
   constexpr int NCG = L::NCG, NSEG = L::NSEG, TPS = L::TPS, NKB = DK / 32, NTD = DK / 16;
+  constexpr int NT = 512, NW = NT / 64;  // threads, waves
 
   __shared__ __attribute__((aligned(32))) unsigned char smem[L::total];
   __bf16* tQ = reinterpret_cast<__bf16*>(smem + L::oQ);
@@ -255,13 +276,13 @@ __global__ __launch_bounds__(256) void wyc_prep_kernel(WycArgs a) {
     pl[u] = buf_load16(rla, off);
     pbs[u] = buf_load_u16(rbs, act ? t * h1 : oob);
   }
-  constexpr int XPT = C * (DVP / 8) / 256;
+  constexpr int XPT = C * (DVP / 8) / NT;
   const int nxg = static_cast<int>(DV / 8);
   uint4 pv[XPT], pw[XPT];
   uint16_t pws[XPT];
 #pragma unroll
   for (int j = 0; j < XPT; ++j) {
-    const int item = tid + 256 * j;
+    const int item = tid + NT * j;
     const bool in = item < C * nxg;
     const uint32_t t = in ? item / nxg : 0, xg = in ? item % nxg : 0;
     pv[j] = buf_load16(rv, in ? t * hdv + xg * 16 : oob);
@@ -288,7 +309,7 @@ __global__ __launch_bounds__(256) void wyc_prep_kernel(WycArgs a) {
   // X rows (x = w . v) meanwhile
 #pragma unroll
   for (int j = 0; j < XPT; ++j) {
-    const int item = tid + 256 * j;
+    const int item = tid + NT * j;
     if (item < C * nxg) {
       const int t = item / nxg, xg = item % nxg;
       float x[8];
@@ -335,6 +356,7 @@ __global__ __launch_bounds__(256) void wyc_prep_kernel(WycArgs a) {
     if (tid == 0) a.flag[cix] = robust ? 1 : 0;
   }
   if (robust) {
+    if (tid < DK) fEgr[tid] = egn_own;  // (e^{G_n - G_ref} is not needed here: e^{G_n} in its place)
     // raw rows into LDS: q, k, c = b . k and log alpha (bf16) beside the x rows
     __bf16* rQ = tQ;
     __bf16* rK = tK;
@@ -366,7 +388,7 @@ __global__ __launch_bounds__(256) void wyc_prep_kernel(WycArgs a) {
       }
     }
     lds_barrier();
-    wyc_exact_chunk<DK, LDT, LDX, TWO>(a, cix, rQ, rK, rC, rL, tX, egn_own, tid);
+    wyc_exact_chunk<DK, LDT, LDX, TWO>(a, cix, rQ, rK, rC, rL, tX, fEgr, tid);
     return;
   }
 
@@ -420,16 +442,16 @@ __global__ __launch_bounds__(256) void wyc_prep_kernel(WycArgs a) {
   }
   // tiles above the diagonal of -M, L_K and M_QK are never written by the Gram phase but are
   // read as zero by the products below (the three arrays are contiguous)
-  for (int i = tid; i < (L::oT - L::oM) / 4; i += 256) reinterpret_cast<uint32_t*>(gM)[i] = 0u;
+  for (int i = tid; i < (L::oT - L::oM) / 4; i += NT) reinterpret_cast<uint32_t*>(gM)[i] = 0u;
   GDR_PMARK(1);
   lds_barrier();
 
-  // ---- Gram tiles: 20 jobs = 2 row operands x 10 tile pairs, 5 per wave ----
+  // ---- Gram tiles: 20 jobs = 2 row operands x 10 tile pairs, job wave + NW jj ----
   {
-    constexpr int JPW = 5;
+    constexpr int JPW = (20 + NW - 1) / NW;
     F8 fa[2][NKB], fb[2][NKB], fc[2][NKB];
     auto job_of = [&](int jj, int& grp, int& ta, int& tb) {
-      const int job = wave + 4 * jj;
+      const int job = wave + NW * jj;
       grp = job / 10;
       const int tix = job % 10;
       ta = tix >= 6 ? 3 : tix >= 3 ? 2 : tix >= 1 ? 1 : 0;
@@ -479,8 +501,9 @@ __global__ __launch_bounds__(256) void wyc_prep_kernel(WycArgs a) {
     load_job(0, 0);
 #pragma unroll
     for (int jj = 0; jj < JPW; ++jj) {
+      if (wave + NW * jj >= 20) break;  // (uniform)
       const int cur = jj & 1;
-      if (jj + 1 < JPW) load_job(jj + 1, cur ^ 1);
+      if (jj + 1 < JPW && wave + NW * (jj + 1) < 20) load_job(jj + 1, cur ^ 1);
       int grp, ta, tb;
       job_of(jj, grp, ta, tb);
       f32x4 acc1 = zero4(), acc2 = zero4();
@@ -505,8 +528,8 @@ __global__ __launch_bounds__(256) void wyc_prep_kernel(WycArgs a) {
   GDR_PMARK(3);
   lds_barrier();
 
-  // ---- T = (I + L_P)^{-1}: wave j solves column block j on the identity ----
-  {
+  // ---- T = (I + L_P)^{-1}: wave j < 4 solves column block j on the identity ----
+  if (wave < 4) {
     const int j = wave;
     bf16x4 af[6], tf[4];
 #pragma unroll
@@ -603,8 +626,8 @@ __global__ __launch_bounds__(256) void wyc_prep_kernel(WycArgs a) {
     //     A' = -Pbar^T W:          lane holds A'[16 tl + l16][16 ct + 4 g + i]
     //     D = Kbar^T X - Pbar^T Y: lane holds D[16 tl + 4 g + i][16 cv + l16], i.e. row 16 cv + l16
     //                              of D^T, four consecutive channels
-    constexpr int WPW = (NTD + 3) / 4;        // W tiles per wave (at most)
-    constexpr int VPW = (DVP / 16 + 3) / 4;   // value tiles per wave (at most)
+    constexpr int WPW = (NTD + NW - 1) / NW;        // W tiles per wave (at most)
+    constexpr int VPW = (DVP / 16 + NW - 1) / NW;   // value tiles per wave (at most)
     const int nct_u = static_cast<int>(DV / 16);
     F8 wf[WPW][2], xf[VPW][2], yf[VPW][2];
     {
@@ -614,7 +637,7 @@ __global__ __launch_bounds__(256) void wyc_prep_kernel(WycArgs a) {
       __bf16* Qo = a.Qd + cix * C * DK;
 #pragma unroll
       for (int w = 0; w < WPW; ++w) {
-        const int ct = wave + 4 * w;
+        const int ct = wave + NW * w;
         if (ct < NTD) {
           const int col = 16 * ct + l16;
           F8 cf[2];
@@ -643,7 +666,7 @@ __global__ __launch_bounds__(256) void wyc_prep_kernel(WycArgs a) {
       __bf16* Zo = a.Zd + cix * C * DV;
 #pragma unroll
       for (int w = 0; w < VPW; ++w) {
-        const int cv = wave + 4 * w;
+        const int cv = wave + NW * w;
         if (cv < nct_u) {
           col_frags(tX, LDX, 16 * cv + l16, xf[w]);
           if (TWO) {
@@ -703,12 +726,12 @@ __global__ __launch_bounds__(256) void wyc_prep_kernel(WycArgs a) {
       }
 #pragma unroll
       for (int w = 0; w < WPW; ++w) {
-        const int ct = wave + 4 * w;
+        const int ct = wave + NW * w;
         if (ct < NTD) store4(Ao + tiled16(16 * tl + l16, 16 * ct + 4 * g, DK), acc[w]);
       }
 #pragma unroll
       for (int w = 0; w < VPW; ++w) {
-        const int cv = wave + 4 * w;
+        const int cv = wave + NW * w;
         if (cv < nct_u) store4(Do + tiled16(16 * cv + l16, 16 * tl + 4 * g, DK), acc[WPW + w]);
       }
     }

@@ -39,9 +39,9 @@ hipError_t launch_mode(WycArgs a, int64_t nstate, hipEvent_t mark, hipStream_t s
   const int64_t nprep = nstate * a.nch;
   if (nprep > 0) {
     if (a.DV <= 128)
-      hipLaunchKernelGGL((wyc_prep_kernel<DK, 128, MODE>), dim3((unsigned)nprep), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((wyc_prep_kernel<DK, 128, MODE>), dim3((unsigned)nprep), dim3(512), 0, s, a);
     else
-      hipLaunchKernelGGL((wyc_prep_kernel<DK, 256, MODE>), dim3((unsigned)nprep), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((wyc_prep_kernel<DK, 256, MODE>), dim3((unsigned)nprep), dim3(512), 0, s, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
