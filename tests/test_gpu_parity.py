@@ -154,6 +154,36 @@ def test_prefill_flagged_chunks_mixed(dev, kind, DV, order):
     check(x, o, S, order, TOL["bf16"], "flagged %s dv=%d %s" % (kind, DV, order))
 
 
+@pytest.mark.parametrize("order", ["erase_then_decay", "decay_then_erase"])
+@pytest.mark.parametrize("B,H,DV", [(8, 16, 128), (4, 16, 256)])
+def test_prefill_channel_wide_slices(dev, B, H, DV, order):
+    """Enough states that every workgroup of the per-channel state kernel takes a 64-column slice
+    (states x d_v / 64 >= 256), with d_v = 256 taking the wide chunk-local kernel too."""
+    wl = case("gdn2", B=B, H=H, T=130, D=128, DV=DV, seed=21)
+    x = synth.make_prefill(wl)
+    say("wide slices", B, H, DV, order)
+    o, S = run_gpu_prefill(x, dev, order=order)
+    torch.cuda.synchronize()
+    check(x, o, S, order, TOL["bf16"], "wide slices B=%d H=%d dv=%d %s" % (B, H, DV, order))
+
+
+@pytest.mark.parametrize("order", ["erase_then_decay", "decay_then_erase"])
+@pytest.mark.parametrize("D", [32, 64])
+def test_prefill_flagged_chunks_small_dk(dev, D, order):
+    """Flagged chunks (log alpha = -7 over a chunk) at d_k = 32 and 64, next to ordinary ones."""
+    wl = case("kda", B=1, H=2, T=64 * 3 + 9, D=D, seed=23)
+    x = synth.make_prefill(wl)
+    la = x["log_alpha"].clone()
+    la[:, 64:128] = -7.0
+    la[:, 192:] = -7.0
+    x["log_alpha"] = la
+    say("flagged chunks dk", D, order)
+    o, S = run_gpu_prefill(x, dev, order=order)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all() and torch.isfinite(S).all()
+    check(x, o, S, order, TOL["bf16"], "flagged dk=%d %s" % (D, order))
+
+
 # ------------------------------------------------------------------ decode
 
 
