@@ -2,7 +2,7 @@
 chunk 64, bf16 inputs, fp32 state) and the Gated DeltaNet-2 decode step (256 x 32 states, 1000
 steps), on one MI355X, through the C ABI.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gdn|kda|gdn2|mamba2|gdn_gqa]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gdn|kda|gdn2|mamba2|gla|gdn_gqa]
                     [--decode-steps N] [--no-cpu-baseline] [--no-decode]
 
 Prints ONE JSON line.  `value` is prefill tokens/s (B*T / time per call) with inputs resident in
@@ -33,10 +33,13 @@ PEAK_BF16_TFLOPS = 2516.6
 METRIC = "prefill tokens/s + %bf16 MFMA peak; decode state GB/s + %HBM peak"
 
 
-def flops_per_head_token(d, C, channel_two_factor):
+def flops_per_head_token(d, C, channel_two_factor, erase=True):
     """Algorithmic FLOP of the chunk form per (head, token); triangular products count half.
     Rank-one form: 6d^2 + 5Cd + C^2/3; per-channel decay applied after the erase:
-    8d^2 + 9Cd + C^2/3."""
+    8d^2 + 9Cd + C^2/3; no erase gate (Gram, its product with the values, K^T X and Q S):
+    4d^2 + 2Cd."""
+    if not erase:
+        return 4 * d * d + 2 * C * d
     if channel_two_factor:
         return 8 * d * d + 9 * C * d + C * C / 3.0
     return 6 * d * d + 5 * C * d + C * C / 3.0
@@ -236,7 +239,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="gdn", choices=["gdn", "kda", "gdn2", "mamba2", "gdn_gqa"])
+    ap.add_argument("--workload", default="gdn", choices=["gdn", "kda", "gdn2", "mamba2", "gla", "gdn_gqa"])
     ap.add_argument("--decode-steps", type=int, default=None)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -267,7 +270,7 @@ def main():
     pf = time_prefill(wl, args.steps, args.warmup, dev)
     tokens = wl.B * wl.T
     sec = pf["mean_ms"] * 1e-3
-    flops = flops_per_head_token(wl.DK, 64, two) * wl.B * wl.T * wl.H
+    flops = flops_per_head_token(wl.DK, 64, two, wl.b != "none") * wl.B * wl.T * wl.H
     nbytes = prefill_bytes(wl)
     achieved_gbs = nbytes / sec / 1e9
     out = {

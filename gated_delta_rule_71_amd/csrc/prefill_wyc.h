@@ -739,6 +739,318 @@ __global__ __launch_bounds__(512) void wyc_prep_kernel(WycArgs a) {
   GDR_PMARK(5);
 }
 
+// ------------------------------------------------------------------ no erase gate
+
+// Per-channel decay without an erase gate (b = 0: gated linear attention): T = I, W = Y = 0 and
+// A' = 0, so the chunk map is Q' = Qhat, D = Kbar^T X and Z' = M X with M = tril(Qhat Khat^T)
+// (either order of the missing erase and the decay gives the same recurrence).  One Gram product
+// per chunk and no solve.  A chunk whose prefix sums span too far for the split Gram forms D and
+// Z' token by token instead (Q' = q e^{G_t} never overflows and is formed the same way for every
+// chunk).  256 threads.
+template <int DK, int DVP>
+struct WygPrepLayout {
+  static constexpr int C = 64;
+  static constexpr int LDT = DK + 8;
+  static constexpr int LDX = DVP + 8;
+  static constexpr int LDD = C + 8;
+  static constexpr int NCG = DK / 8;
+  static constexpr int NSEG = (256 / NCG) < C ? (256 / NCG) : C;
+  static constexpr int TPS = C / NSEG;
+  static constexpr int oQ = 0;                     // split Qhat [64][LDT] (flagged: q rows)
+  static constexpr int oK = oQ + C * LDT * 2;      // split Khat [64][LDT] (flagged: k rows)
+  static constexpr int oX = oK + C * LDT * 2;      // X rows [64][LDX]
+  static constexpr int oM = oX + C * LDX * 2;      // M [64][LDD] (flagged: log alpha rows [64][DK], with the next)
+  static constexpr int oSEG = oM + C * LDD * 2;    // fp32 segment sums [NSEG][DK]
+  static constexpr int oF = oSEG + NSEG * DK * 4;  // fp32 G_ref, e^{G_ref}, e^{G_n - G_ref} [DK] each; flag
+  static constexpr int total = oF + (3 * DK + 4) * 4;
+  static constexpr bool fits = total <= kLdsLimit;
+  static_assert(oF - oM >= C * DK * 2, "log alpha rows of a flagged chunk need the M and segment arrays");
+};
+
+template <int DK, int DVP>
+__global__ __launch_bounds__(256) void wyg_prep_kernel(WycArgs a) {
+  using L = WygPrepLayout<DK, DVP>;
+  using MM = Mma<__bf16>;
+  using F8 = MM::F8;
+  static_assert(L::fits, "LDS layout exceeds the gfx950 workgroup limit");
+  static_assert(DK % 32 == 0, "dk must be a multiple of 32");
+  constexpr int C = L::C, LDT = L::LDT, LDX = L::LDX, LDD = L::LDD;
+  constexpr int NCG = L::NCG, NSEG = L::NSEG, TPS = L::TPS, NKB = DK / 32, NTD = DK / 16;
+
+  __shared__ __attribute__((aligned(32))) unsigned char smem[L::total];
+  __bf16* tQ = reinterpret_cast<__bf16*>(smem + L::oQ);
+  __bf16* tK = reinterpret_cast<__bf16*>(smem + L::oK);
+  __bf16* tX = reinterpret_cast<__bf16*>(smem + L::oX);
+  __bf16* gM = reinterpret_cast<__bf16*>(smem + L::oM);
+  float* segtot = reinterpret_cast<float*>(smem + L::oSEG);
+  float* fRef = reinterpret_cast<float*>(smem + L::oF);
+  float* fEref = fRef + DK;
+  float* fEgr = fRef + 2 * DK;  // e^{G_n - G_ref}
+  int* sFlag = reinterpret_cast<int*>(fRef + 3 * DK);
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, g = lane >> 4, l16 = lane & 15;
+  const int64_t nch = a.nch, DV = a.DV, H = a.H;
+  const int64_t bh = blockIdx.x / nch, c = blockIdx.x % nch;
+  const int64_t bi = bh / H, hi = bh % H;
+  const int64_t t0 = c * C;
+  const int64_t rr = (bi * a.T + t0) * H + hi;
+  const int64_t left = a.T - t0;
+  const int64_t cix = bh * nch + c;
+  const int ts = tid / NCG, d0 = (tid % NCG) * 8;
+  const bool act = ts < NSEG;
+
+  // ---- loads: every load first; out-of-range rows and absent gate kinds read zero ----
+  const uint32_t oob = 0x80000000u;
+  const uint32_t hdk = static_cast<uint32_t>(H * DK * 2), hdv = static_cast<uint32_t>(H * DV * 2);
+  const uint32_t h1 = static_cast<uint32_t>(H * 2);
+  const uint32_t hqk = static_cast<uint32_t>(a.Hk * DK * 2);
+  const int64_t rqk = (bi * a.T + t0) * a.Hk + hi / (H / a.Hk);
+  const auto rq = make_rsrc(a.q + rqk * DK, wy_range(left, a.Hk, DK));
+  const auto rk = make_rsrc(a.k + rqk * DK, wy_range(left, a.Hk, DK));
+  const auto rla = make_rsrc(a.la + rr * DK, wy_range(left, H, DK));
+  const auto rv = make_rsrc(a.v + rr * DV, wy_range(left, H, DV));
+  const auto rwc = make_rsrc(a.w_kind == kChannel ? a.wg + rr * DV : a.v, a.w_kind == kChannel ? wy_range(left, H, DV) : 0u);
+  const auto rws = make_rsrc(a.w_kind == kScalar ? a.wg + rr : a.v, a.w_kind == kScalar ? wy_range(left, H, 1) : 0u);
+  uint4 pq[TPS], pk[TPS], pl[TPS];
+#pragma unroll
+  for (int u = 0; u < TPS; ++u) {
+    const uint32_t t = ts * TPS + u;
+    pq[u] = buf_load16(rq, act ? t * hqk + d0 * 2 : oob);
+    pk[u] = buf_load16(rk, act ? t * hqk + d0 * 2 : oob);
+    pl[u] = buf_load16(rla, act ? t * hdk + d0 * 2 : oob);
+  }
+  constexpr int XPT = C * (DVP / 8) / 256;
+  const int nxg = static_cast<int>(DV / 8);
+  uint4 pv[XPT], pw[XPT];
+  uint16_t pws[XPT];
+#pragma unroll
+  for (int j = 0; j < XPT; ++j) {
+    const int item = tid + 256 * j;
+    const bool in = item < C * nxg;
+    const uint32_t t = in ? item / nxg : 0, xg = in ? item % nxg : 0;
+    pv[j] = buf_load16(rv, in ? t * hdv + xg * 16 : oob);
+    pw[j] = buf_load16(rwc, in ? t * hdv + xg * 16 : oob);
+    pws[j] = buf_load_u16(rws, in ? t * h1 : oob);
+  }
+
+  // ---- gate prefix sums; X rows ----
+  float G8[TPS][8];
+  if (act) {
+    float run[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < TPS; ++u) {
+      float la8[8];
+      load8f(reinterpret_cast<const bf16_t*>(&pl[u]), la8);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        run[j] += la8[j];
+        G8[u][j] = run[j];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) segtot[ts * DK + d0 + j] = run[j];
+  }
+#pragma unroll
+  for (int j = 0; j < XPT; ++j) {
+    const int item = tid + 256 * j;
+    if (item < C * nxg) {
+      const int t = item / nxg, xg = item % nxg;
+      float x[8];
+      load8f(reinterpret_cast<const bf16_t*>(&pv[j]), x);
+      if (a.w_kind == kChannel) {
+        float w8[8];
+        load8f(reinterpret_cast<const bf16_t*>(&pw[j]), w8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] *= w8[e];
+      } else if (a.w_kind == kScalar) {
+        const float ws = bf16_to_f32(pws[j]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] *= ws;
+      }
+      bf16x8 xb;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xb[e] = static_cast<__bf16>(x[e]);
+      *reinterpret_cast<bf16x8*>(tX + t * LDX + xg * 8) = xb;
+    }
+  }
+  if (tid == 0) sFlag[0] = 0;
+  lds_barrier();
+  if (tid < DK) {
+    float run = 0.f;
+    for (int s = 0; s < NSEG; ++s) {
+      const float tv = segtot[s * DK + tid];
+      segtot[s * DK + tid] = run;
+      run += tv;
+    }
+    const float ref = segtot[(NSEG / 2) * DK + tid];  // G_31
+    fRef[tid] = ref;
+    fEref[tid] = __expf(ref);
+    fEgr[tid] = __expf(run - ref);
+    a.Egn[cix * (DK + 4) + tid] = __expf(run);
+    if (!(fabsf(ref) <= kWycSpanLimit && fabsf(run - ref) <= kWycSpanLimit)) sFlag[0] = 1;  // NaN, inf too
+  }
+  lds_barrier();
+  const bool robust = sFlag[0] != 0;
+  if (tid < 4) {
+    reinterpret_cast<int*>(a.Egn + cix * (DK + 4) + DK)[tid] = tid == 0 && robust ? 1 : 0;
+    if (tid == 0) a.flag[cix] = robust ? 1 : 0;
+  }
+
+  // ---- operands: Q' = q e^{G_t} straight out (tiled); split Qhat, Khat into LDS (flagged: raw
+  // q, k and log alpha rows) ----
+  if (act) {
+    float off[8], ref[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      off[j] = segtot[ts * DK + d0 + j];
+      ref[j] = fRef[d0 + j];
+    }
+#pragma unroll
+    for (int u = 0; u < TPS; ++u) {
+      const int t = ts * TPS + u;
+      float q[8], k[8];
+      load8f(reinterpret_cast<const bf16_t*>(&pq[u]), q);
+      load8f(reinterpret_cast<const bf16_t*>(&pk[u]), k);
+      bf16x8 oq, ok, oqp;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float G = G8[u][j] + off[j];
+        oqp[j] = static_cast<__bf16>(q[j] * __expf(G));  // q e^{G_t}
+        if (!robust) {
+          const float eq = __expf(G - ref[j]);  // e^{G_t - G_ref}
+          oq[j] = static_cast<__bf16>(q[j] * eq);
+          ok[j] = static_cast<__bf16>(k[j] * __builtin_amdgcn_rcpf(eq));
+        }
+      }
+      *reinterpret_cast<bf16x8*>(a.Qd + cix * C * DK + tiled16(t, d0, DK)) = oqp;
+      if (robust) {
+        *reinterpret_cast<uint4*>(tQ + t * LDT + d0) = pq[u];
+        *reinterpret_cast<uint4*>(tK + t * LDT + d0) = pk[u];
+      } else {
+        *reinterpret_cast<bf16x8*>(tQ + t * LDT + d0) = oq;
+        *reinterpret_cast<bf16x8*>(tK + t * LDT + d0) = ok;
+      }
+    }
+  }
+  // tiles above the diagonal of M are never written by the Gram phase but are read as zero
+  if (!robust)
+    for (int i = tid; i < C * LDD / 8; i += 256) reinterpret_cast<uint4*>(gM)[i] = make_uint4(0, 0, 0, 0);
+  lds_barrier();  // (the raw log alpha rows of a flagged chunk overwrite the segment sums)
+  if (robust) {
+    __bf16* rL = gM;  // [64][DK] over the M and segment arrays
+    if (act) {
+#pragma unroll
+      for (int u = 0; u < TPS; ++u) *reinterpret_cast<uint4*>(rL + (ts * TPS + u) * DK + d0) = pl[u];
+    }
+    lds_barrier();
+    // D and Z' from the recurrence without erase, token by token in fp32: lane pairs of 64
+    // channels each carry value column v of the state from zero
+    constexpr int DH = DK / 2;
+    const int hf = tid & 1, pr = tid >> 1, c0 = hf * DH;
+    for (int v = pr; v < DV; v += 128) {
+      float sv[DH];
+#pragma unroll
+      for (int i = 0; i < DH; ++i) sv[i] = 0.f;
+      for (int t = 0; t < C; ++t) {
+        const float x = static_cast<float>(tX[t * LDX + v]);
+        float y = 0.f;
+#pragma unroll
+        for (int p = 0; p < DH / 8; ++p) {
+          float k8[8], q8[8], l8[8];
+          load8f(reinterpret_cast<const bf16_t*>(tK + t * LDT + c0 + 8 * p), k8);
+          load8f(reinterpret_cast<const bf16_t*>(tQ + t * LDT + c0 + 8 * p), q8);
+          load8f(reinterpret_cast<const bf16_t*>(rL + t * DK + c0 + 8 * p), l8);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float s_ = sv[8 * p + e] * __expf(l8[e]) + k8[e] * x;
+            sv[8 * p + e] = s_;
+            y += q8[e] * s_;
+          }
+        }
+        y += __shfl_xor(y, 1);
+        if (hf == 0) a.Zd[cix * C * DV + tiled16(t, v, DV)] = static_cast<__bf16>(y);
+      }
+      __bf16* Do = a.Dt + cix * DV * DK;
+#pragma unroll
+      for (int p = 0; p < DH / 8; ++p) {
+        bf16x8 d8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) d8[e] = static_cast<__bf16>(sv[8 * p + e]);
+        *reinterpret_cast<bf16x8*>(Do + tiled16(v, c0 + 8 * p, DK)) = d8;
+      }
+    }
+    return;
+  }
+
+  // ---- M = tril(Qhat Khat^T): 10 tile pairs over the 4 waves ----
+  for (int job = wave; job < 10; job += 4) {
+    const int ta = job >= 6 ? 3 : job >= 3 ? 2 : job >= 1 ? 1 : 0, tb = job - ta * (ta + 1) / 2;
+    const __bf16* ar = tQ + (16 * ta + l16) * LDT;
+    const __bf16* br = tK + (16 * tb + l16) * LDT;
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) acc = MM::mma8(lds_load8(ar + 32 * kb + 8 * g), lds_load8(br + 32 * kb + 8 * g), acc);
+    const int r0 = 16 * ta + 4 * g, cc = 16 * tb + l16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) gM[(r0 + i) * LDD + cc] = static_cast<__bf16>(cc <= r0 + i ? acc[i] : 0.f);
+  }
+  lds_barrier();
+
+  // ---- products per value column tile: Z' = M X (lane: Z'[16 ta + l16][16 cv + 4 g + i]) and
+  // D = Kbar^T X = e^{G_n - G_ref} . (Khat^T X) (lane: D[16 tl + 4 g + i][16 cv + l16]) ----
+  auto col_frags = [&](const __bf16* base, int pitch, int col, F8* f) {
+    const int cx = col - l16 + 4 * (l16 & 3), m_ = l16 >> 2;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const bf16x4 v = lds_read_tr4(reinterpret_cast<const unsigned char*>(base + (32 * ks + 16 * h + 4 * g + m_) * pitch + cx));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) f[ks][4 * h + e] = v[e];
+      }
+  };
+  F8 mf[6];
+#pragma unroll
+  for (int ta = 0, n = 0; ta < 4; ++ta) {
+    mf[n++] = lds_pair_frag_k<C>(gM + (16 * ta + l16) * LDD, 0, g);
+    if (ta >= 2) mf[n++] = lds_pair_frag_k<C>(gM + (16 * ta + l16) * LDD, 32, g);
+  }
+  auto store4 = [&](__bf16* dst, const f32x4& v) {
+    bf16x4 ob;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ob[i] = static_cast<__bf16>(v[i]);
+    *reinterpret_cast<bf16x4*>(dst) = ob;
+  };
+  const int nct_u = static_cast<int>(DV / 16);
+  __bf16* Zo = a.Zd + cix * C * DV;
+  __bf16* Do = a.Dt + cix * DV * DK;
+  for (int cv = wave; cv < nct_u; cv += 4) {
+    F8 xf[2];
+    col_frags(tX, LDX, 16 * cv + l16, xf);
+#pragma unroll
+    for (int ta = 0, n = 0; ta < 4; ++ta) {
+      f32x4 z = MM::mma8(xf[0], mf[n++], zero4());
+      if (ta >= 2) z = MM::mma8(xf[1], mf[n++], z);
+      store4(Zo + tiled16(16 * ta + l16, 16 * cv + 4 * g, DV), z);
+    }
+#pragma unroll 2
+    for (int tl = 0; tl < NTD; ++tl) {
+      F8 kf[2];
+      col_frags(tK, LDT, 16 * tl + l16, kf);
+      f32x4 d = MM::mma8(kf[0], xf[0], zero4());
+      d = MM::mma8(kf[1], xf[1], d);
+      const float4 fd = *reinterpret_cast<const float4*>(fEgr + 16 * tl + 4 * g);
+      d[0] *= fd.x;
+      d[1] *= fd.y;
+      d[2] *= fd.z;
+      d[3] *= fd.w;
+      store4(Do + tiled16(16 * cv + l16, 16 * tl + 4 * g, DK), d);
+    }
+  }
+}
+
 // ------------------------------------------------------------------ state kernel
 
 // Direct-to-LDS copies of a tiled16 matrix into the swizzled row-major LDS form of DmaPlan
@@ -771,8 +1083,8 @@ struct TiledPlan {
   }
 };
 
-// One chunk buffer: the chunk's affine map, rows in the swizzled form above.
-template <int DK, int DVS, int NXW>
+// One chunk buffer: the chunk's affine map, rows in the swizzled form above (AZ: A' = 0, no slots).
+template <int DK, int DVS, int NXW, bool AZ = false>
 struct WycStateLayout {
   static constexpr int C = 64;
   static constexpr int NCQ = DK / 8;   // 16-byte pieces per row of dk channels
@@ -786,7 +1098,7 @@ struct WycStateLayout {
   static constexpr int BUF = oE + ((DK + 4) * 4 + 255) / 256 * 256;
   static constexpr int XW = DK / 64 * 1024;       // one wave's bf16 S half (its pair fragments, 16 bytes a lane)
   static constexpr int REST = 2 * BUF + C * DVS * 2 + 2 * NXW * XW;
-  static constexpr int NA = 3 * AS + REST <= kLdsLimit ? 3 : 2;  // A' slots
+  static constexpr int NA = AZ ? 0 : 3 * AS + REST <= kLdsLimit ? 3 : 2;  // A' slots
   static constexpr int oB = NA * AS;              // the two chunk buffers
   static constexpr int oO = oB + 2 * BUF;         // O rows of one chunk [64][DVS]
   static constexpr int oX = oO + C * DVS * 2;     // bf16 S halves exchanged: [2][NXW waves][XW]
@@ -812,11 +1124,12 @@ constexpr int wait_vmcnt(int n) { return 0x0F70 | (n & 0xF) | (((n >> 4) & 3) <<
 //            c mod 2 with chunk c+2 and the other waits for its loads of chunk c+1.
 // The state waves issue no global stores in the loop, and the loader wave that reads the O buffer
 // has no loads in flight when it does.
+// AZ (no erase gate: A' = 0): no A' copies or products, S <- e^{G_n} . S + D.
 // (one workgroup per compute unit by its LDS: the scheduler may spend registers on latency)
-template <int DK, int NSW, int SPLIT>
+template <int DK, int NSW, int SPLIT, bool AZ>
 __global__ __launch_bounds__(64 * (2 + NSW * SPLIT)) __attribute__((amdgpu_waves_per_eu(1, 1))) void wyc_state_kernel(WycArgs a) {
   constexpr int DVS = 16 * NSW;
-  using L = WycStateLayout<DK, DVS, SPLIT == 2 ? NSW * 2 : 0>;
+  using L = WycStateLayout<DK, DVS, SPLIT == 2 ? NSW * 2 : 0, AZ>;
   using MM = Mma<__bf16>;
   using F8 = MM::F8;
   static_assert(L::fits, "LDS layout exceeds the gfx950 workgroup limit");
@@ -846,7 +1159,7 @@ __global__ __launch_bounds__(64 * (2 + NSW * SPLIT)) __attribute__((amdgpu_waves
   const uint32_t hdv = static_cast<uint32_t>(H * DV * 2);
 
   auto buf = [&](int64_t c) -> unsigned char* { return smem + L::oB + (c & 1) * L::BUF; };
-  auto aslot = [&](int64_t c) -> unsigned char* { return smem + (c % L::NA) * L::AS; };
+  auto aslot = [&](int64_t c) -> unsigned char* { return smem + (AZ ? 0 : (c % L::NA) * L::AS); };
   __bf16* oO = reinterpret_cast<__bf16*>(smem + L::oO);
 
   // ---------------- loader waves ----------------
@@ -938,8 +1251,9 @@ __global__ __launch_bounds__(64 * (2 + NSW * SPLIT)) __attribute__((amdgpu_waves
     constexpr int NR = NKB < 3 ? NKB : 3;
     F8 fa[NR][NTH], fq[NR][NTA];
     auto read_k = [&](int kb, int r) {
+      if constexpr (!AZ)
 #pragma unroll
-      for (int u = 0; u < NTH; ++u) fa[r][u] = lds_piece<NCQ, true>(A, perm_row(rh * NTH + u, l16), 4 * kb + g);
+        for (int u = 0; u < NTH; ++u) fa[r][u] = lds_piece<NCQ, true>(A, perm_row(rh * NTH + u, l16), 4 * kb + g);
 #pragma unroll
       for (int t = 0; t < NTA; ++t) fq[r][t] = lds_piece<NCQ, false>(B + L::oQ, 16 * (rh * NTA + t) + l16, 4 * kb + g);
     };
@@ -978,8 +1292,9 @@ __global__ __launch_bounds__(64 * (2 + NSW * SPLIT)) __attribute__((amdgpu_waves
     for (int kb = 0; kb < NKB; ++kb) {
       if (kb + 2 < NKB) read_k(kb + 2, (kb + 2) % NR);
       __builtin_amdgcn_sched_barrier(0);  // the reads stay ahead of this k-step's products
+      if constexpr (!AZ)
 #pragma unroll
-      for (int u = 0; u < NTH; ++u) S[u] = MM::mma8(fa[kb % NR][u], sf[kb], S[u]);
+        for (int u = 0; u < NTH; ++u) S[u] = MM::mma8(fa[kb % NR][u], sf[kb], S[u]);
 #pragma unroll
       for (int t = 0; t < NTA; ++t) Ot[t] = MM::mma8(sf[kb], fq[kb % NR][t], Ot[t]);
       __builtin_amdgcn_sched_barrier(0);
@@ -1015,7 +1330,8 @@ __global__ __launch_bounds__(64 * (2 + NSW * SPLIT)) __attribute__((amdgpu_waves
   if (nch > 0) {
     if (wave == 0) {
       dma_a(0);
-      for (int k = 0; k < L::NA - 1 && k < nch; ++k) dma_b(k);
+      if constexpr (!AZ)
+        for (int k = 0; k < L::NA - 1 && k < nch; ++k) dma_b(k);
     }
     if (wave == 1 && nch > 1) dma_a(1);
     if (loader) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
@@ -1025,7 +1341,7 @@ __global__ __launch_bounds__(64 * (2 + NSW * SPLIT)) __attribute__((amdgpu_waves
     // opaque per chunk: keeps lane-dependent LDS addresses from being hoisted out of the loop
     asm volatile("" : "+v"(lane), "+v"(g), "+v"(l16));
     GDR_MARK(0);
-    const bool ahead = ch + L::NA - 1 < nch;  // wave 0 issues A' of chunk ch + NA - 1 now
+    const bool ahead = !AZ && ch + L::NA - 1 < nch;  // wave 0 issues A' of chunk ch + NA - 1 now
     if (!loader) {
       compute(ch);
     } else if (wave == 0) {

@@ -26,22 +26,31 @@ WycSizes wyc_sizes(int64_t nstate, int64_t T, int64_t DK, int64_t DV) {
 
 // SPLIT = 2: two state waves per 16 columns, each with half of the channels (d_k >= 64, up to 32
 // columns a workgroup by LDS)
-template <int DK, int NSW>
+template <int DK, int NSW, bool AZ>
 void launch_state(WycArgs a, int64_t nstate, hipStream_t s) {
   a.nsl = static_cast<int>(a.DV / (16 * NSW));
   constexpr int SPLIT = (DK >= 64 && NSW <= 2) ? 2 : 1;
-  hipLaunchKernelGGL((wyc_state_kernel<DK, NSW, SPLIT>), dim3((unsigned)(nstate * a.nsl)),
+  hipLaunchKernelGGL((wyc_state_kernel<DK, NSW, SPLIT, AZ>), dim3((unsigned)(nstate * a.nsl)),
                      dim3(64 * (2 + NSW * SPLIT)), 0, s, a);
 }
 
+// MODE 0: no erase gate (either order), 1: erase then decay, 2: decay then erase
 template <int DK, int MODE>
 hipError_t launch_mode(WycArgs a, int64_t nstate, hipEvent_t mark, hipStream_t s) {
+  constexpr bool AZ = MODE == 0;
   const int64_t nprep = nstate * a.nch;
   if (nprep > 0) {
-    if (a.DV <= 128)
-      hipLaunchKernelGGL((wyc_prep_kernel<DK, 128, MODE>), dim3((unsigned)nprep), dim3(512), 0, s, a);
-    else
-      hipLaunchKernelGGL((wyc_prep_kernel<DK, 256, MODE>), dim3((unsigned)nprep), dim3(512), 0, s, a);
+    if constexpr (AZ) {
+      if (a.DV <= 128)
+        hipLaunchKernelGGL((wyg_prep_kernel<DK, 128>), dim3((unsigned)nprep), dim3(256), 0, s, a);
+      else
+        hipLaunchKernelGGL((wyg_prep_kernel<DK, 256>), dim3((unsigned)nprep), dim3(256), 0, s, a);
+    } else {
+      if (a.DV <= 128)
+        hipLaunchKernelGGL((wyc_prep_kernel<DK, 128, MODE>), dim3((unsigned)nprep), dim3(512), 0, s, a);
+      else
+        hipLaunchKernelGGL((wyc_prep_kernel<DK, 256, MODE>), dim3((unsigned)nprep), dim3(512), 0, s, a);
+    }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -53,11 +62,11 @@ hipError_t launch_mode(WycArgs a, int64_t nstate, hipEvent_t mark, hipStream_t s
   // workgroup per compute unit, else the narrowest (the most workgroups)
   const int64_t DV = a.DV;
   if (DV % 64 == 0 && nstate * (DV / 64) >= 256)
-    launch_state<DK, 4>(a, nstate, s);
+    launch_state<DK, 4, AZ>(a, nstate, s);
   else if (DV % 32 == 0 && nstate * (DV / 32) >= 256)
-    launch_state<DK, 2>(a, nstate, s);
+    launch_state<DK, 2, AZ>(a, nstate, s);
   else
-    launch_state<DK, 1>(a, nstate, s);
+    launch_state<DK, 1, AZ>(a, nstate, s);
   return hipGetLastError();
 }
 }  // namespace
@@ -104,10 +113,15 @@ hipError_t prefill_wyc_launch(const PrefillArgs<bf16_t>& p, int64_t nstate, int6
   a.Egn = reinterpret_cast<float*>(ws);
   ws += z.Egn;
   a.flag = reinterpret_cast<int*>(ws);
+  // without an erase gate both orders are the same recurrence, and A' = 0
+  const int mode = p.b_kind == kNone ? 0 : two ? 2 : 1;
   switch (DK) {
-    case 32: return two ? launch_mode<32, 2>(a, nstate, mark, s) : launch_mode<32, 1>(a, nstate, mark, s);
-    case 64: return two ? launch_mode<64, 2>(a, nstate, mark, s) : launch_mode<64, 1>(a, nstate, mark, s);
-    default: return two ? launch_mode<128, 2>(a, nstate, mark, s) : launch_mode<128, 1>(a, nstate, mark, s);
+    case 32: return mode == 0 ? launch_mode<32, 0>(a, nstate, mark, s)
+                    : mode == 2 ? launch_mode<32, 2>(a, nstate, mark, s) : launch_mode<32, 1>(a, nstate, mark, s);
+    case 64: return mode == 0 ? launch_mode<64, 0>(a, nstate, mark, s)
+                    : mode == 2 ? launch_mode<64, 2>(a, nstate, mark, s) : launch_mode<64, 1>(a, nstate, mark, s);
+    default: return mode == 0 ? launch_mode<128, 0>(a, nstate, mark, s)
+                    : mode == 2 ? launch_mode<128, 2>(a, nstate, mark, s) : launch_mode<128, 1>(a, nstate, mark, s);
   }
 }
 

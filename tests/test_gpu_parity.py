@@ -135,7 +135,7 @@ def test_prefill_extreme_gates(dev):
 
 
 @pytest.mark.parametrize("order", ["erase_then_decay", "decay_then_erase"])
-@pytest.mark.parametrize("kind,DV", [("gdn2", 128), ("kda", 128), ("kda", 48)])
+@pytest.mark.parametrize("kind,DV", [("gdn2", 128), ("kda", 128), ("kda", 48), ("gla", 128), ("gla", 48)])
 def test_prefill_flagged_chunks_mixed(dev, kind, DV, order):
     """Chunks whose per-channel gate prefix sums span past the range of the chunk form (log alpha
     = -7 over a chunk spans 448 nats) run token by token.  Here they sit between ordinary chunks
@@ -156,32 +156,34 @@ def test_prefill_flagged_chunks_mixed(dev, kind, DV, order):
 
 @pytest.mark.parametrize("order", ["erase_then_decay", "decay_then_erase"])
 @pytest.mark.parametrize("B,H,DV", [(8, 16, 128), (4, 16, 256)])
-def test_prefill_channel_wide_slices(dev, B, H, DV, order):
+@pytest.mark.parametrize("kind", ["gdn2", "gla"])
+def test_prefill_channel_wide_slices(dev, kind, B, H, DV, order):
     """Enough states that every workgroup of the per-channel state kernel takes a 64-column slice
     (states x d_v / 64 >= 256), with d_v = 256 taking the wide chunk-local kernel too."""
-    wl = case("gdn2", B=B, H=H, T=130, D=128, DV=DV, seed=21)
+    wl = case(kind, B=B, H=H, T=130, D=128, DV=DV, seed=21)
     x = synth.make_prefill(wl)
-    say("wide slices", B, H, DV, order)
+    say("wide slices", kind, B, H, DV, order)
     o, S = run_gpu_prefill(x, dev, order=order)
     torch.cuda.synchronize()
-    check(x, o, S, order, TOL["bf16"], "wide slices B=%d H=%d dv=%d %s" % (B, H, DV, order))
+    check(x, o, S, order, TOL["bf16"], "wide slices %s B=%d H=%d dv=%d %s" % (kind, B, H, DV, order))
 
 
 @pytest.mark.parametrize("order", ["erase_then_decay", "decay_then_erase"])
 @pytest.mark.parametrize("D", [32, 64])
-def test_prefill_flagged_chunks_small_dk(dev, D, order):
+@pytest.mark.parametrize("kind", ["kda", "gla"])
+def test_prefill_flagged_chunks_small_dk(dev, kind, D, order):
     """Flagged chunks (log alpha = -7 over a chunk) at d_k = 32 and 64, next to ordinary ones."""
-    wl = case("kda", B=1, H=2, T=64 * 3 + 9, D=D, seed=23)
+    wl = case(kind, B=1, H=2, T=64 * 3 + 9, D=D, seed=23)
     x = synth.make_prefill(wl)
     la = x["log_alpha"].clone()
     la[:, 64:128] = -7.0
     la[:, 192:] = -7.0
     x["log_alpha"] = la
-    say("flagged chunks dk", D, order)
+    say("flagged chunks dk", kind, D, order)
     o, S = run_gpu_prefill(x, dev, order=order)
     torch.cuda.synchronize()
     assert torch.isfinite(o.float()).all() and torch.isfinite(S).all()
-    check(x, o, S, order, TOL["bf16"], "flagged dk=%d %s" % (D, order))
+    check(x, o, S, order, TOL["bf16"], "flagged %s dk=%d %s" % (kind, D, order))
 
 
 # ------------------------------------------------------------------ decode
@@ -264,7 +266,7 @@ def test_scalar_decay_workloads_full(dev, name):
     check(synth.expand_heads(x, wl.H), o, S, "erase_then_decay", TOL["bf16"], "%s full" % name)
 
 
-@pytest.mark.parametrize("name", ["kda", "gdn2"])
+@pytest.mark.parametrize("name", ["kda", "gdn2", "gla"])
 def test_channel_workloads_sampled(dev, name):
     wl = synth.WORKLOADS[name]
     say("%s workload (sampled states)" % name, wl)
