@@ -15,12 +15,15 @@ Two parts, written independently of each other and of the HIP path:
 * ``reference`` -- NumPy fp64 twins used to pin the C oracle: the same
   recurrence in operator form, the closed forms of its special settings and
   the chunkwise (WY) algebra.
+* ``backward`` -- the adjoint of the token loop in NumPy fp64: gradients of
+  every input given the gradients of the outputs and of the final state.
 """
 from .native import KIND_CHANNEL, KIND_NONE, KIND_SCALAR, ORDER_DECAY_THEN_ERASE, \
     ORDER_ERASE_THEN_DECAY, build, forward, library_path
 from . import reference
+from .backward import backward
 
 __all__ = [
-    "forward", "build", "library_path", "reference", "KIND_NONE", "KIND_SCALAR",
+    "forward", "backward", "build", "library_path", "reference", "KIND_NONE", "KIND_SCALAR",
     "KIND_CHANNEL", "ORDER_ERASE_THEN_DECAY", "ORDER_DECAY_THEN_ERASE",
 ]
