@@ -6,6 +6,7 @@ library is missing, every call raises: there is no CPU or eager fallback.
 
     o, S_T = chunk_fwd(q, k, v, log_alpha, b, w, S0)      # prefill over T tokens
     o = decode_step(q, k, v, log_alpha, b, w, S)           # one token, S updated in place
+    grads = chunk_bwd(q, k, v, log_alpha, b, w, S0, do, dS_T)  # gradients of the prefill
 
 Layouts: q, k [B,T,Hqk,dk]; v [B,T,H,dv] (H a multiple of Hqk: grouped key / value heads, value
 head h reading q / k head h // (H // Hqk)); gates [B,T,H] (one value per token and head) or
@@ -22,7 +23,7 @@ erase instead.
 from . import _native
 from ._native import GdrError, abi_version, make_problem, status_string
 
-__all__ = ["chunk_fwd", "decode_step", "abi_version", "status_string", "GdrError", "make_problem"]
+__all__ = ["chunk_fwd", "chunk_bwd", "decode_step", "abi_version", "status_string", "GdrError", "make_problem"]
 
 _ORDERS = {"erase_then_decay": _native.ERASE_THEN_DECAY, "decay_then_erase": _native.DECAY_THEN_ERASE}
 
@@ -125,6 +126,54 @@ def chunk_fwd(q, k, v, log_alpha=None, b=None, w=None, S0=None, order="erase_the
     if rc != _native.GDR_OK:
         raise GdrError(rc, "gdr_chunk_fwd")
     return o, S_T
+
+
+def chunk_bwd(q, k, v, log_alpha=None, b=None, w=None, S0=None, do=None, dS_T=None,
+              order="erase_then_decay", workspace=None):
+    """Gradients of ``chunk_fwd`` for the output gradient ``do`` ([B,T,H,dv], q's dtype) and the
+    final-state gradient ``dS_T`` (float32 [B,H,dk,dv] or None).  Returns a dict with dq, dk, dv
+    (q's dtype), dlog_alpha, db, dw (shaped like the gates; None for an absent gate) and dS0
+    (float32).  With one shared beta passed as both b and w, its gradient is db + dw.  Raises
+    GdrError(GDR_ERR_UNSUPPORTED) outside bf16 with a scalar or no decay, dv <= 128 and one q / k
+    head per value head."""
+    torch = _torch()
+    B, T, HQ, DK = q.shape
+    H, DV = v.shape[2], v.shape[-1]
+    dt, dev = q.dtype, q.device
+    if k.shape != q.shape or tuple(v.shape[:2]) != (B, T) or HQ == 0 or H % HQ != 0:
+        raise ValueError("shape mismatch: q %s k %s v %s" % (tuple(q.shape), tuple(k.shape), tuple(v.shape)))
+    if k.dtype != dt or v.dtype != dt or k.device != dev or v.device != dev:
+        raise TypeError("q, k, v must share dtype and device")
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on a GPU")
+    if do is None or tuple(do.shape) != tuple(v.shape) or do.dtype != dt or do.device != dev:
+        raise ValueError("do must be %s like v %s" % (dt, tuple(v.shape)))
+    ak = _gate_kind(log_alpha, B, T, H, DK, "log_alpha", dt, dev)
+    bk = _gate_kind(b, B, T, H, DK, "b", dt, dev)
+    wk = _gate_kind(w, B, T, H, DV, "w", dt, dev)
+    _check_contig(q=q, k=k, v=v, log_alpha=log_alpha, b=b, w=w, S0=S0, do=do, dS_T=dS_T)
+    for name, st in (("S0", S0), ("dS_T", dS_T)):
+        if st is not None and (st.dtype != torch.float32 or tuple(st.shape) != (B, H, DK, DV)):
+            raise ValueError("%s must be float32 [B,H,dk,dv]" % name)
+    prob = make_problem(B, H, T, DK, DV, _io_dtype(q), ak, bk, wk, _ORDERS[order],
+                        qk_heads=0 if HQ == H else HQ)
+    need = _native.bwd_workspace_bytes(prob)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    elif workspace.device != dev or workspace.numel() * workspace.element_size() < need:
+        raise ValueError("workspace must be a device tensor of at least %d bytes" % need)
+    like = lambda x: None if x is None else torch.empty_like(x)
+    g = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
+         "dlog_alpha": like(log_alpha), "db": like(b), "dw": like(w),
+         "dS0": torch.empty((B, H, DK, DV), dtype=torch.float32, device=dev)}
+    rc = _native.chunk_bwd_raw(prob, _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w),
+                               _ptr(S0), _ptr(do), _ptr(dS_T), _ptr(g["dq"]), _ptr(g["dk"]),
+                               _ptr(g["dv"]), _ptr(g["dlog_alpha"]), _ptr(g["db"]), _ptr(g["dw"]),
+                               _ptr(g["dS0"]), _ptr(workspace),
+                               workspace.numel() * workspace.element_size(), _stream(dev))
+    if rc != _native.GDR_OK:
+        raise GdrError(rc, "gdr_chunk_bwd")
+    return g
 
 
 def workspace_bytes(q, v, log_alpha=None, b=None, w=None, order="erase_then_decay"):

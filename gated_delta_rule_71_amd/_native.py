@@ -16,7 +16,8 @@ GATE_NONE, GATE_SCALAR, GATE_CHANNEL = 0, 1, 2
 ERASE_THEN_DECAY, DECAY_THEN_ERASE = 0, 1
 
 EXPORTED = ("gdr_abi_version", "gdr_status_string", "gdr_chunk_fwd_workspace_bytes",
-            "gdr_chunk_fwd", "gdr_chunk_fwd_marked", "gdr_decode_step")
+            "gdr_chunk_fwd", "gdr_chunk_fwd_marked", "gdr_decode_step", "gdr_chunk_bwd_workspace_bytes",
+            "gdr_chunk_bwd")
 
 
 class GdrProblem(ctypes.Structure):
@@ -74,6 +75,10 @@ def lib():
         L.gdr_chunk_fwd_marked.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
         L.gdr_decode_step.restype = ctypes.c_int
         L.gdr_decode_step.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.gdr_chunk_bwd_workspace_bytes.restype = sz
+        L.gdr_chunk_bwd_workspace_bytes.argtypes = [pp]
+        L.gdr_chunk_bwd.restype = ctypes.c_int
+        L.gdr_chunk_bwd.argtypes = [pp] + [vp] * 17 + [sz, vp]
         _lib = L
     return _lib
 
@@ -110,3 +115,16 @@ def decode_step_raw(problem, q, k, v, la, b, w, S, o, stream):
     return lib().gdr_decode_step(ctypes.byref(problem), q or None, k or None, v or None,
                                  la or None, b or None, w or None, S or None, o or None,
                                  stream or None)
+
+
+def bwd_workspace_bytes(problem):
+    return lib().gdr_chunk_bwd_workspace_bytes(ctypes.byref(problem))
+
+
+def chunk_bwd_raw(problem, q, k, v, la, b, w, S0, dO, dS_T, dq, dk, dv, dla, db, dw, dS0, ws,
+                  ws_bytes, stream):
+    """gdr_chunk_bwd with integer device addresses (0 = NULL).  Returns the status."""
+    n = lambda x: x or None
+    return lib().gdr_chunk_bwd(ctypes.byref(problem), n(q), n(k), n(v), n(la), n(b), n(w), n(S0),
+                               n(dO), n(dS_T), n(dq), n(dk), n(dv), n(dla), n(db), n(dw), n(dS0),
+                               n(ws), ws_bytes, n(stream))

@@ -1,0 +1,759 @@
+// Backward pass of the chunk form for a scalar decay (or none), bf16 I/O, d_v <= 128.
+//
+// The recurrence ("Recurrent Memory: Write, Erase, Decay, Read", section 05, with the Gated
+// DeltaNet-2 gates) over one chunk of C = 64 tokens, from the state S_0 that enters it, is, with
+// g_t the chunk-local prefix sum of log alpha, gamma_t = e^{g_t}, c_t = b_t . k_t, x_t = w_t . v_t:
+//
+//   (I + L) U = X - Diag(gamma) C S_0,   L[t][s] = e^{g_t - g_s} c_t . k_s   (s < t)
+//   O = Diag(gamma) Q S_0 + M U,         M[t][s] = e^{g_t - g_s} q_t . k_s   (s <= t)
+//   S_n = gamma_n S_0 + K_n^T U,         K_n[s] = e^{g_n - g_s} k_s
+//
+// (a scalar decay commutes with the erase, so both orders of the pages are this one map).  Its
+// adjoint, given dO and the gradient dS_n of the state that leaves the chunk:
+//
+//   dU = M^T dO + K_n dS_n,   dV = T^T dU (T = (I + L)^{-1}),   dX = dV
+//   dM = tril(dO U^T),        dL = -strict_tril(dV U^T)
+//   dq = (dM . Gamma) K + Diag(gamma) dO S_0^T
+//   dc = (dL . Gamma) K - Diag(gamma) dV S_0^T
+//   dk = (dM . Gamma)^T Q + (dL . Gamma)^T C + Diag(e^{g_n - g_s}) U dS_n^T + b . dc
+//   dS_0 = gamma_n dS_n + (Diag(gamma) Q)^T dO - (Diag(gamma) C)^T dV
+//
+// and the gradient of g_t collects every factor e^{+-g}: the row sums minus the column sums of
+// dM . M and dL . L, gamma_t (q_t . dQ_t + c_t . dC_t), -e^{g_n - g_t} k_t . dK_t, and at t = n
+// the terms of gamma_n and of every e^{g_n - g_s}; d log alpha_t is its suffix sum in the chunk.
+//
+// Kernels (one call):
+//   1. the per-channel chunk-local kernel (the decay broadcast over channels) forms each chunk's
+//      affine map S_n = Ahat S_0 + D, O = Q' S_0 + Z' with Ahat = Diag(e^{G_n}) + A';
+//   2. bwd_chain_kernel<DK, false>: S_c = Ahat S_{c-1} + D chunk by chunk, storing S_{c-1};
+//   3. bwd_chain_kernel<DK, true>:  dS_{c-1} = Ahat^T dS_c + Q'^T dO_c in reverse, storing dS_c;
+//   4. bwd_local_kernel<DK>: every chunk at once, the adjoint above from S_{c-1} and dS_c.
+// The checkpoints are bf16, in two tiled layouts each: rows (S[dk][dv]) for products that
+// contract over the value columns, and transposed (S^T[dv][dk]) for those over the channels.
+#pragma once
+
+#include "prefill_wyc.h"
+
+namespace gdr {
+
+struct BwdArgs {
+  const bf16_t* q;
+  const bf16_t* k;
+  const bf16_t* v;
+  const bf16_t* la;
+  const bf16_t* bg;
+  const bf16_t* wg;
+  const bf16_t* dO;
+  const float* S0;
+  const float* dST;
+  bf16_t* dq;
+  bf16_t* dk;
+  bf16_t* dv;
+  bf16_t* dla;
+  bf16_t* db;
+  bf16_t* dw;
+  float* dS0;
+  // the chunk maps (per-channel chunk-local kernel) and the checkpoints, per chunk index
+  // cix = state * nch + chunk, tiled16 as the workspace of the per-channel forward
+  const __bf16* Qd;  // [cix][64][dk]   Q'
+  const __bf16* Ad;  // [cix][dk][dk]   A'
+  const __bf16* Dt;  // [cix][dv][dk]   D^T
+  const float* Egn;  // [cix][dk + 4]   e^{G_n}
+  __bf16* SR;        // [cix][dk][dv]   S_{c-1}
+  __bf16* ST;        // [cix][dv][dk]   S_{c-1}^T
+  __bf16* GR;        // [cix][dk][dv]   dS_c
+  __bf16* GT;        // [cix][dv][dk]   dS_c^T
+  int64_t T, H, DV, nch;
+  int alpha_kind, b_kind, w_kind;
+};
+
+// Transposing fragment of a tiled16 LDS matrix: lane (g, l16) gets element [k0 + 4 g + e] and
+// [k0 + 16 + 4 g + e] (tile-pair order, e < 4) of column `col`, i.e. a row of the transpose.
+// ncols: the matrix's column count.
+__device__ __forceinline__ Mma<__bf16>::F8 tiled_col_frag(const __bf16* m, int ncols, int col, int k0,
+                                                          int g, int l16) {
+  Mma<__bf16>::F8 f;
+  const int nt = ncols >> 4, ct = col >> 4;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int r = k0 + 16 * h + 4 * g + (l16 >> 2);
+    const __bf16* p = m + ((r >> 4) * nt + ct) * 256 + (r & 15) * 16 + 4 * (l16 & 3);
+    const bf16x4 v = lds_read_tr4(reinterpret_cast<const unsigned char*>(p));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) f[4 * h + e] = v[e];
+  }
+  return f;
+}
+
+// Row fragment of a tiled16 matrix (LDS or global): elements [row][k0 + 4 g + e] and
+// [row][k0 + 16 + 4 g + e].  `hi` false: the upper four read as zero (past the last column).
+__device__ __forceinline__ Mma<__bf16>::F8 tiled_row_frag(const __bf16* m, int ncols, int row, int k0,
+                                                          int g, bool hi = true) {
+  Mma<__bf16>::F8 f;
+  const __bf16* p0 = m + tiled16(row, k0 + 4 * g, ncols);
+  const bf16x4 lo = *reinterpret_cast<const bf16x4*>(p0);
+  bf16x4 up;
+  if (hi) {
+    up = *reinterpret_cast<const bf16x4*>(m + tiled16(row, k0 + 16 + 4 * g, ncols));
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) up[e] = static_cast<__bf16>(0.f);
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    f[e] = lo[e];
+    f[4 + e] = up[e];
+  }
+  return f;
+}
+
+// Transposing fragment of a row-major LDS array (pitch in elements): column `col`, rows
+// k0 + 4 g + e and k0 + 16 + 4 g + e.
+__device__ __forceinline__ Mma<__bf16>::F8 lds_col_frag(const __bf16* base, int pitch, int col, int k0,
+                                                        int g, int l16) {
+  Mma<__bf16>::F8 f;
+  const int c0 = col - l16 + 4 * (l16 & 3), m_ = l16 >> 2;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const bf16x4 v = lds_read_tr4(reinterpret_cast<const unsigned char*>(base + (k0 + 16 * h + 4 * g + m_) * pitch + c0));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) f[4 * h + e] = v[e];
+  }
+  return f;
+}
+
+// ------------------------------------------------------------------ chains over the chunks
+
+// One workgroup per (state, 16 value columns); DK / 32 waves, wave w holding S's channel tiles
+// 2 w and 2 w + 1 of the slice (the k-step w of the products).  Per chunk: the bf16 state goes to
+// LDS for the other waves (two exchange slots, so one barrier a chunk) and to the checkpoints;
+// the chunk's A' (and, in reverse, Q' and the dO slice) were staged in LDS during the previous
+// chunk; each wave forms its tiles of
+//   forward: S <- e^{G_n} . S + A' S + D
+//   reverse: S <- e^{G_n} . S + A'^T S + Q'^T dO
+// and stages the next chunk's operands from registers loaded before the products.
+template <int DK, bool REV>
+__global__ __launch_bounds__(2 * DK) void bwd_chain_kernel(BwdArgs a) {
+  using MM = Mma<__bf16>;
+  using F8 = MM::F8;
+  constexpr int C = 64, NKB = DK / 32, NTD = DK / 16, NT = 64 * NKB;
+  constexpr int AB = DK * DK * 2, QB = C * DK * 2, OB = C * 16 * 2;
+  constexpr int BUF = AB + (REV ? QB + OB : 0);
+  constexpr int NA16 = AB / 16 / NT, NQ16 = QB / 16 / NT, NO16 = (128 + NT - 1) / NT;
+  static_assert(AB % (16 * NT) == 0 && QB % (16 * NT) == 0, "whole pieces per thread");
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * BUF + 2 * NKB * 1024];
+
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t DV = a.DV, H = a.H, nch = a.nch;
+  const int64_t nsl = DV / 16;
+  const int64_t bh = blockIdx.x / nsl;
+  const int sl = static_cast<int>(blockIdx.x % nsl);
+  const int64_t bi = bh / H, hi = bh % H;
+  const int col = 16 * sl + l16;  // this lane's value column
+
+  f32x4 S[2];
+  {
+    const float* init = REV ? a.dST : a.S0;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        S[u][i] = init ? init[(bh * DK + 16 * (2 * w + u) + 4 * g + i) * DV + col] : 0.f;
+  }
+
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));  // (a vector type stays in registers)
+  u32x4 ra[NA16], rq[REV ? NQ16 : 1], ro[NO16];
+  // (always inlined: the arrays stay in registers)
+  auto fetch = [&](int64_t c) __attribute__((always_inline)) {
+    const int64_t cix = bh * nch + c;
+    const u32x4* A = reinterpret_cast<const u32x4*>(a.Ad + cix * DK * DK);
+#pragma unroll
+    for (int j = 0; j < NA16; ++j) ra[j] = A[tid + NT * j];
+    if constexpr (REV) {
+      const u32x4* Q = reinterpret_cast<const u32x4*>(a.Qd + cix * C * DK);
+#pragma unroll
+      for (int j = 0; j < NQ16; ++j) rq[j] = Q[tid + NT * j];
+      const int64_t t0 = c * C;
+      const auto rd = make_rsrc(a.dO + ((bi * a.T + t0) * H + hi) * DV + 16 * sl, wy_range(a.T - t0, H, DV));
+      const uint32_t hdv = static_cast<uint32_t>(H * DV * 2);
+#pragma unroll
+      for (int j = 0; j < NO16; ++j) {
+        const int p = tid + NT * j;  // piece: token p / 2, half p % 2
+        ro[j] = __builtin_bit_cast(u32x4, buf_load16(rd, p < 128 ? (p >> 1) * hdv + (p & 1) * 16 : 0x80000000u));
+      }
+    }
+  };
+  auto stage = [&](int b) __attribute__((always_inline)) {
+    unsigned char* B = smem + b * BUF;
+#pragma unroll
+    for (int j = 0; j < NA16; ++j) *reinterpret_cast<u32x4*>(B + (tid + NT * j) * 16) = ra[j];
+    if constexpr (REV) {
+#pragma unroll
+      for (int j = 0; j < NQ16; ++j) *reinterpret_cast<u32x4*>(B + AB + (tid + NT * j) * 16) = rq[j];
+#pragma unroll
+      for (int j = 0; j < NO16; ++j) {
+        const int p = tid + NT * j;
+        if (p < 128) *reinterpret_cast<u32x4*>(B + AB + QB + p * 16) = ro[j];
+      }
+    }
+  };
+
+  if (nch > 0) {
+    fetch(REV ? nch - 1 : 0);
+    stage(0);
+  }
+  for (int64_t it = 0; it < nch; ++it) {
+    const int64_t c = REV ? nch - 1 - it : it;
+    const int64_t cix = bh * nch + c;
+    const int bs = static_cast<int>(it & 1);
+    // this wave's bf16 tiles to the exchange slot and the checkpoints
+    *reinterpret_cast<F8*>(smem + 2 * BUF + (bs * NKB + w) * 1024 + lane * 16) = acc_pair_frag<__bf16>(S[0], S[1]);
+    __bf16* ckR = (REV ? a.GR : a.SR) + cix * DK * DV;
+    __bf16* ckT = (REV ? a.GT : a.ST) + cix * DV * DK;
+    float4 e4[2];
+    bf16x4 d4[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int tl = 2 * w + u;
+      bf16x4 s4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s4[i] = static_cast<__bf16>(S[u][i]);
+      *reinterpret_cast<bf16x4*>(ckT + tiled16(col, 16 * tl + 4 * g, DK)) = s4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ckR[tiled16(16 * tl + 4 * g + i, col, DV)] = s4[i];
+      e4[u] = *reinterpret_cast<const float4*>(a.Egn + cix * (DK + 4) + 16 * tl + 4 * g);
+      if (!REV) d4[u] = *reinterpret_cast<const bf16x4*>(a.Dt + cix * DV * DK + tiled16(col, 16 * tl + 4 * g, DK));
+    }
+    if (it + 1 < nch) fetch(REV ? c - 1 : c + 1);
+    lds_barrier();  // the exchange slot and the staged operands of chunk c are in
+
+    const unsigned char* B = smem + bs * BUF;
+    const __bf16* sA = reinterpret_cast<const __bf16*>(B);
+    F8 sf[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) sf[kb] = *reinterpret_cast<const F8*>(smem + 2 * BUF + (bs * NKB + kb) * 1024 + lane * 16);
+    f32x4 acc[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      acc[u][0] = S[u][0] * e4[u].x + (REV ? 0.f : static_cast<float>(d4[u][0]));
+      acc[u][1] = S[u][1] * e4[u].y + (REV ? 0.f : static_cast<float>(d4[u][1]));
+      acc[u][2] = S[u][2] * e4[u].z + (REV ? 0.f : static_cast<float>(d4[u][2]));
+      acc[u][3] = S[u][3] * e4[u].w + (REV ? 0.f : static_cast<float>(d4[u][3]));
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int tl = 2 * w + u;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const F8 af = REV ? tiled_col_frag(sA, DK, 16 * tl + l16, 32 * kb, g, l16)
+                          : tiled_row_frag(sA, DK, 16 * tl + l16, 32 * kb, g);
+        acc[u] = MM::mma8(af, sf[kb], acc[u]);
+      }
+    }
+    if constexpr (REV) {
+      const __bf16* sQ = reinterpret_cast<const __bf16*>(B + AB);
+      const __bf16* sO = reinterpret_cast<const __bf16*>(B + AB + QB);
+      F8 of[2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) of[ks] = lds_col_frag(sO, 16, l16, 32 * ks, g, l16);
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+          acc[u] = MM::mma8(tiled_col_frag(sQ, DK, 16 * (2 * w + u) + l16, 32 * ks, g, l16), of[ks], acc[u]);
+    }
+    S[0] = acc[0];
+    S[1] = acc[1];
+    if (it + 1 < nch) stage(bs ^ 1);
+  }
+  if (REV && a.dS0 != nullptr) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a.dS0[(bh * DK + 16 * (2 * w + u) + 4 * g + i) * DV + col] = S[u][i];
+  }
+}
+
+// ------------------------------------------------------------------ chunk-local adjoint
+
+template <int DK>
+struct BwdLocalLayout {
+  static constexpr int C = 64, DVP = 128;
+  static constexpr int LDT = DK + 8, LDX = DVP + 8, LDD = C + 8, LDA = 56, LDI = 24, LDL = 20;
+  static constexpr int oQ = 0;                      // q rows
+  static constexpr int oK = oQ + C * LDT * 2;       // k rows
+  static constexpr int oC = oK + C * LDT * 2;       // c = b . k rows
+  static constexpr int oX = oC + C * LDT * 2;       // x = w . v, then V, then dV
+  static constexpr int oO = oX + C * LDX * 2;       // dO rows
+  static constexpr int oU = oO + C * LDX * 2;       // U
+  static constexpr int oDU = oU + C * LDX * 2;      // dU
+  static constexpr int oM = oDU + C * LDX * 2;      // M, then dM . Gamma
+  static constexpr int oT = oM + C * LDD * 2;       // T, then dL . Gamma
+  static constexpr int oA = oT + C * LDD * 2;       // -L below the diagonal blocks (rows 16 ..)
+  static constexpr int oI = oA + 48 * LDA * 2;      // inverses of the diagonal blocks
+  static constexpr int oLD = oI + C * LDI * 2;      // fp32 diagonal blocks of L, column-major
+  static constexpr int oF = oLD + C * LDL * 4;      // fp32 g, gamma, dg, b (scalar), dw and db sums
+  static constexpr int total = oF + 6 * C * 4;
+  static constexpr bool fits = total <= kLdsLimit;
+};
+
+template <int DK>
+__global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a) {
+  using L = BwdLocalLayout<DK>;
+  using MM = Mma<__bf16>;
+  using F8 = MM::F8;
+  static_assert(L::fits, "LDS layout exceeds the gfx950 workgroup limit");
+  constexpr int C = L::C, LDT = L::LDT, LDX = L::LDX, LDD = L::LDD, LDA = L::LDA, LDI = L::LDI, LDL = L::LDL;
+  constexpr int NKB = DK / 32, NTD = DK / 16;
+
+  __shared__ __attribute__((aligned(32))) unsigned char smem[L::total];
+  __bf16* sQ = reinterpret_cast<__bf16*>(smem + L::oQ);
+  __bf16* sK = reinterpret_cast<__bf16*>(smem + L::oK);
+  __bf16* sC = reinterpret_cast<__bf16*>(smem + L::oC);
+  __bf16* sX = reinterpret_cast<__bf16*>(smem + L::oX);
+  __bf16* sO = reinterpret_cast<__bf16*>(smem + L::oO);
+  __bf16* sU = reinterpret_cast<__bf16*>(smem + L::oU);
+  __bf16* sDU = reinterpret_cast<__bf16*>(smem + L::oDU);
+  __bf16* sM = reinterpret_cast<__bf16*>(smem + L::oM);
+  __bf16* tT = reinterpret_cast<__bf16*>(smem + L::oT);
+  __bf16* gA = reinterpret_cast<__bf16*>(smem + L::oA);
+  __bf16* dInv = reinterpret_cast<__bf16*>(smem + L::oI);
+  float* Ld = reinterpret_cast<float*>(smem + L::oLD);
+  float* fg = reinterpret_cast<float*>(smem + L::oF);  // g_t
+  float* fga = fg + C;                                  // gamma_t
+  float* fdg = fg + 2 * C;                              // d g_t
+  float* fb = fg + 3 * C;                               // scalar b_t
+  float* fdw = fg + 4 * C;                              // row sums of dw (scalar w), then of db
+
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t nch = a.nch, DV = a.DV, H = a.H;
+  const int64_t bh = blockIdx.x / nch, c = blockIdx.x % nch;
+  const int64_t bi = bh / H, hi = bh % H;
+  const int64_t t0 = c * C, left = a.T - t0;
+  const int64_t rr = (bi * a.T + t0) * H + hi;
+  const int64_t cix = bh * nch + c;
+  const int NCV = static_cast<int>(DV / 16), NKV = static_cast<int>((DV + 31) / 32);
+  const __bf16* SR = a.SR + cix * DK * DV;
+  const __bf16* ST = a.ST + cix * DV * DK;
+  const __bf16* GR = a.GR + cix * DK * DV;
+  const __bf16* GT = a.GT + cix * DV * DK;
+
+  // ---- inputs into LDS; the gate prefix sums ----
+  const uint32_t oob = 0x80000000u;
+  const uint32_t hdk = static_cast<uint32_t>(H * DK * 2), hdv = static_cast<uint32_t>(H * DV * 2), h1 = static_cast<uint32_t>(H * 2);
+  const uint32_t rng_k = wy_range(left, H, DK), rng_v = wy_range(left, H, DV), rng_1 = wy_range(left, H, 1);
+  const auto rq = make_rsrc(a.q + rr * DK, rng_k);
+  const auto rk = make_rsrc(a.k + rr * DK, rng_k);
+  const auto rbc = make_rsrc(a.b_kind == kChannel ? a.bg + rr * DK : a.q, a.b_kind == kChannel ? rng_k : 0u);
+  const auto rbs = make_rsrc(a.b_kind == kScalar ? a.bg + rr : a.q, a.b_kind == kScalar ? rng_1 : 0u);
+  const auto rv = make_rsrc(a.v + rr * DV, rng_v);
+  const auto rwc = make_rsrc(a.w_kind == kChannel ? a.wg + rr * DV : a.v, a.w_kind == kChannel ? rng_v : 0u);
+  const auto rws = make_rsrc(a.w_kind == kScalar ? a.wg + rr : a.v, a.w_kind == kScalar ? rng_1 : 0u);
+  const auto rdo = make_rsrc(a.dO + rr * DV, rng_v);
+  const auto rla = make_rsrc(a.alpha_kind == kScalar ? a.la + rr : a.q, a.alpha_kind == kScalar ? rng_1 : 0u);
+  for (int item = tid; item < C * (DK / 8); item += 256) {
+    const int t = item / (DK / 8), d0 = (item % (DK / 8)) * 8;
+    const uint32_t off = t * hdk + d0 * 2;
+    const uint4 uq = buf_load16(rq, off), uk = buf_load16(rk, off);
+    float kf[8], cf[8];
+    load8f(reinterpret_cast<const bf16_t*>(&uk), kf);
+    if (a.b_kind == kChannel) {
+      const uint4 ub = buf_load16(rbc, off);
+      load8f(reinterpret_cast<const bf16_t*>(&ub), cf);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) cf[j] *= kf[j];
+    } else {
+      const float bs = a.b_kind == kScalar ? bf16_to_f32(buf_load_u16(rbs, t * h1)) : 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) cf[j] = bs * kf[j];
+    }
+    bf16x8 cb;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) cb[j] = static_cast<__bf16>(cf[j]);
+    *reinterpret_cast<uint4*>(sQ + t * LDT + d0) = uq;
+    *reinterpret_cast<uint4*>(sK + t * LDT + d0) = uk;
+    *reinterpret_cast<bf16x8*>(sC + t * LDT + d0) = cb;
+  }
+  // value rows, zero past d_v (up to the next multiple of 32, the contraction step)
+  for (int item = tid; item < C * (L::DVP / 8); item += 256) {
+    const int t = item / (L::DVP / 8), x0 = (item % (L::DVP / 8)) * 8;
+    bf16x8 xb, ob;
+    const bf16x8 zero8 = {};
+    if (x0 < DV) {
+      const uint32_t off = t * hdv + x0 * 2;
+      const uint4 uv = buf_load16(rv, off), ud = buf_load16(rdo, off);
+      float xf[8];
+      load8f(reinterpret_cast<const bf16_t*>(&uv), xf);
+      if (a.w_kind == kChannel) {
+        const uint4 uw = buf_load16(rwc, off);
+        float wf[8];
+        load8f(reinterpret_cast<const bf16_t*>(&uw), wf);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) xf[j] *= wf[j];
+      } else if (a.w_kind == kScalar) {
+        const float ws = bf16_to_f32(buf_load_u16(rws, t * h1));
+#pragma unroll
+        for (int j = 0; j < 8; ++j) xf[j] *= ws;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) xb[j] = static_cast<__bf16>(xf[j]);
+      ob = __builtin_bit_cast(bf16x8, ud);
+    } else {
+      xb = zero8;
+      ob = zero8;
+    }
+    *reinterpret_cast<bf16x8*>(sX + t * LDX + x0) = xb;
+    *reinterpret_cast<bf16x8*>(sO + t * LDX + x0) = ob;
+    *reinterpret_cast<bf16x8*>(sU + t * LDX + x0) = zero8;
+    *reinterpret_cast<bf16x8*>(sDU + t * LDX + x0) = zero8;
+  }
+  for (int i = tid; i < C * LDD / 8; i += 256) reinterpret_cast<uint4*>(sM)[i] = make_uint4(0, 0, 0, 0);
+  if (wave == 0) {
+    // inclusive prefix sum of log alpha over the chunk (lane = token)
+    float x = a.alpha_kind == kScalar ? bf16_to_f32(buf_load_u16(rla, lane * h1)) : 0.f;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const float y = __shfl_up(x, d);
+      if (lane >= d) x += y;
+    }
+    fg[lane] = x;
+    fga[lane] = __expf(x);
+    fdg[lane] = 0.f;
+    fb[lane] = a.b_kind == kScalar ? bf16_to_f32(buf_load_u16(rbs, lane * h1)) : 0.f;
+    fdw[lane] = 0.f;
+    fdw[C + lane] = 0.f;
+  }
+  lds_barrier();
+  const float gn = fg[C - 1];
+
+  // ---- Gram tiles: M = Gamma . tril(Q K^T) (bf16), L = Gamma . strict_tril(C K^T) as -L below
+  // the diagonal blocks and fp32 diagonal blocks ----
+  for (int job = wave; job < 20; job += 4) {
+    const int grp = job / 10, tix = job % 10;
+    const int ta = tix >= 6 ? 3 : tix >= 3 ? 2 : tix >= 1 ? 1 : 0, tb = tix - ta * (ta + 1) / 2;
+    const __bf16* ar = (grp == 0 ? sQ : sC) + (16 * ta + l16) * LDT;
+    const __bf16* br = sK + (16 * tb + l16) * LDT;
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) acc = MM::mma8(lds_load8(ar + 32 * kb + 8 * g), lds_load8(br + 32 * kb + 8 * g), acc);
+    const int s = 16 * tb + l16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 16 * ta + 4 * g + i;
+      const bool keep = grp == 0 ? s <= t : s < t;
+      const float val = keep ? acc[i] * __expf(fg[t] - fg[s]) : 0.f;
+      if (grp == 0)
+        sM[t * LDD + s] = static_cast<__bf16>(val);
+      else if (ta > tb)
+        gA[(t - 16) * LDA + s] = static_cast<__bf16>(-val);
+      else
+        Ld[(ta * 16 + (s & 15)) * LDL + (t & 15)] = val;
+    }
+  }
+  lds_barrier();
+  if (wave < 2 && lane < 32) wy_diag_inverses<LDL, LDI>(Ld, dInv, wave, lane, l16);
+  lds_barrier();
+  // ---- T = (I + L)^{-1}: wave j forms column block j by blocked forward substitution ----
+  {
+    const int j = wave;
+    bf16x4 af[6], tf[4];
+#pragma unroll
+    for (int i = 0, n = 0; i < 4; ++i) {
+      tf[i] = lds_load4(dInv + (16 * i + l16) * LDI + 4 * g);
+#pragma unroll
+      for (int m = 0; m < i; ++m, ++n) af[n] = lds_load4(gA + (16 * i - 16 + l16) * LDA + 16 * m + 4 * g);
+    }
+    f32x4 R[4];
+#pragma unroll
+    for (int i = 0, n = 0; i < 4; ++i) {
+      f32x4 acc;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = (i == j && 4 * g + e == l16) ? 1.f : 0.f;
+#pragma unroll
+      for (int m = 0; m < i; ++m, ++n)
+        if (m >= j) acc = MM::mma4(af[n], acc_frag4<__bf16>(R[m]), acc);
+      R[i] = i < j ? zero4() : MM::mma4(tf[i], acc_frag4<__bf16>(acc), zero4());
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) tT[(16 * i + 4 * g + e) * LDD + 16 * j + l16] = static_cast<__bf16>(R[i][e]);
+  }
+  // ---- V = X - Diag(gamma) C S_0, in place of X (wave: value tiles cv = wave, wave + 4) ----
+  for (int cv = wave; cv < NCV; cv += 4) {
+    F8 sf[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) sf[kb] = tiled_row_frag(ST, DK, 16 * cv + l16, 32 * kb, g);
+#pragma unroll
+    for (int ta = 0; ta < 4; ++ta) {
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) acc = MM::mma8(lds_pair_frag_k<DK>(sC + (16 * ta + l16) * LDT, 32 * kb, g), sf[kb], acc);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 16 * ta + 4 * g + i;
+        __bf16& x = sX[t * LDX + 16 * cv + l16];
+        x = static_cast<__bf16>(static_cast<float>(x) - fga[t] * acc[i]);
+      }
+    }
+  }
+  lds_barrier();
+  // ---- U = T V ----
+  for (int cv = wave; cv < NCV; cv += 4) {
+    F8 vf[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) vf[ks] = lds_col_frag(sX, LDX, 16 * cv + l16, 32 * ks, g, l16);
+#pragma unroll
+    for (int ta = 0; ta < 4; ++ta) {
+      f32x4 acc = MM::mma8(lds_pair_frag_k<C>(tT + (16 * ta + l16) * LDD, 0, g), vf[0], zero4());
+      if (ta >= 2) acc = MM::mma8(lds_pair_frag_k<C>(tT + (16 * ta + l16) * LDD, 32, g), vf[1], acc);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sU[(16 * ta + 4 * g + i) * LDX + 16 * cv + l16] = static_cast<__bf16>(acc[i]);
+    }
+  }
+  // ---- dU = M^T dO + K_n dS_n (M^T row s: tokens t >= s) ----
+  for (int cv = wave; cv < NCV; cv += 4) {
+    F8 gf[NKB], of[2];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) gf[kb] = tiled_row_frag(GT, DK, 16 * cv + l16, 32 * kb, g);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) of[ks] = lds_col_frag(sO, LDX, 16 * cv + l16, 32 * ks, g, l16);
+#pragma unroll
+    for (int ta = 0; ta < 4; ++ta) {
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) acc = MM::mma8(lds_pair_frag_k<DK>(sK + (16 * ta + l16) * LDT, 32 * kb, g), gf[kb], acc);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] *= __expf(gn - fg[16 * ta + 4 * g + i]);
+      if (ta < 2) acc = MM::mma8(lds_col_frag(sM, LDD, 16 * ta + l16, 0, g, l16), of[0], acc);
+      acc = MM::mma8(lds_col_frag(sM, LDD, 16 * ta + l16, 32, g, l16), of[1], acc);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sDU[(16 * ta + 4 * g + i) * LDX + 16 * cv + l16] = static_cast<__bf16>(acc[i]);
+    }
+  }
+  lds_barrier();
+  // ---- dV = T^T dU, in place of V (T^T row s: tokens t >= s) ----
+  for (int cv = wave; cv < NCV; cv += 4) {
+    F8 df[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) df[ks] = lds_col_frag(sDU, LDX, 16 * cv + l16, 32 * ks, g, l16);
+#pragma unroll
+    for (int ta = 0; ta < 4; ++ta) {
+      f32x4 acc = zero4();
+      if (ta < 2) acc = MM::mma8(lds_col_frag(tT, LDD, 16 * ta + l16, 0, g, l16), df[0], acc);
+      acc = MM::mma8(lds_col_frag(tT, LDD, 16 * ta + l16, 32, g, l16), df[1], acc);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sX[(16 * ta + 4 * g + i) * LDX + 16 * cv + l16] = static_cast<__bf16>(acc[i]);
+    }
+  }
+  lds_barrier();
+
+  // row sums (over the 16 lanes of a group) and column sums (over the 4 groups and the 4
+  // accumulator rows) of a 16 x 16 tile, added to fdg: + rows of tile row ta, - columns of tb
+  auto dg_rows = [&](int ta, f32x4 r) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float x = r[i];
+      x += __shfl_xor(x, 1);
+      x += __shfl_xor(x, 2);
+      x += __shfl_xor(x, 4);
+      x += __shfl_xor(x, 8);
+      if (l16 == 0) atomicAdd(&fdg[16 * ta + 4 * g + i], x);
+    }
+  };
+  auto dg_cols = [&](int tb, const f32x4& r) {
+    float x = r[0] + r[1] + r[2] + r[3];
+    x += __shfl_xor(x, 16);
+    x += __shfl_xor(x, 32);
+    if (g == 0) atomicAdd(&fdg[16 * tb + l16], -x);
+  };
+  // ---- dM = tril(dO U^T) and dL = -strict_tril(dV U^T); their products with M and L go to dg,
+  // dM . Gamma replaces M and dL . Gamma replaces T ----
+  for (int job = wave; job < 20; job += 4) {
+    const int grp = job / 10, tix = job % 10;
+    const int ta = tix >= 6 ? 3 : tix >= 3 ? 2 : tix >= 1 ? 1 : 0, tb = tix - ta * (ta + 1) / 2;
+    const __bf16* ar = (grp == 0 ? sO : sX) + (16 * ta + l16) * LDX;
+    const __bf16* br = sU + (16 * tb + l16) * LDX;
+    f32x4 acc = zero4();
+    for (int kv = 0; kv < NKV; ++kv) acc = MM::mma8(lds_pair_frag_k<L::DVP>(ar, 32 * kv, g), lds_pair_frag_k<L::DVP>(br, 32 * kv, g), acc);
+    const int s = 16 * tb + l16;
+    f32x4 e;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 16 * ta + 4 * g + i;
+      const bool keep = grp == 0 ? s <= t : s < t;
+      const float d = keep ? (grp == 0 ? acc[i] : -acc[i]) : 0.f;
+      float m;
+      if (grp == 0)
+        m = static_cast<float>(sM[t * LDD + s]);
+      else
+        m = ta > tb ? -static_cast<float>(gA[(t - 16) * LDA + s]) : Ld[(ta * 16 + (s & 15)) * LDL + (t & 15)];
+      e[i] = d * m;
+      const __bf16 dG = static_cast<__bf16>(keep ? d * __expf(fg[t] - fg[s]) : 0.f);
+      if (grp == 0)
+        sM[t * LDD + s] = dG;
+      else
+        tT[t * LDD + s] = dG;
+    }
+    dg_rows(ta, e);
+    dg_cols(tb, e);
+  }
+  lds_barrier();
+
+  // ---- dq, dc, dk tiles (wave: channel tiles tl = wave, wave + 4; all four token tiles) ----
+  const auto sq_ = make_rsrc(a.dq + rr * DK, rng_k);
+  const auto sk_ = make_rsrc(a.dk + rr * DK, rng_k);
+  const auto sb_ = make_rsrc(a.b_kind == kChannel ? a.db + rr * DK : a.dq, a.b_kind == kChannel ? rng_k : 0u);
+  float sdot = 0.f;  // <S_0, dS_n> over this wave's channel tiles
+  for (int tl = wave; tl < NTD; tl += 4) {
+    const int ch = 16 * tl + l16;
+    F8 s0f[4], gnf[4];  // rows ch of S_0 and dS_n, k = value columns
+    for (int kv = 0; kv < NKV; ++kv) {
+      const bool hiok = 32 * kv + 16 < DV;
+      s0f[kv] = tiled_row_frag(SR, static_cast<int>(DV), ch, 32 * kv, g, hiok);
+      gnf[kv] = tiled_row_frag(GR, static_cast<int>(DV), ch, 32 * kv, g, hiok);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sdot += static_cast<float>(s0f[kv][e]) * static_cast<float>(gnf[kv][e]);
+    }
+    F8 kf[2], qf[2], cf[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      kf[ks] = lds_col_frag(sK, LDT, ch, 32 * ks, g, l16);
+      qf[ks] = lds_col_frag(sQ, LDT, ch, 32 * ks, g, l16);
+      cf[ks] = lds_col_frag(sC, LDT, ch, 32 * ks, g, l16);
+    }
+#pragma unroll
+    for (int ta = 0; ta < 4; ++ta) {
+      f32x4 aq = zero4(), ac = zero4(), ak = zero4();
+      for (int kv = 0; kv < NKV; ++kv) {
+        aq = MM::mma8(lds_pair_frag_k<L::DVP>(sO + (16 * ta + l16) * LDX, 32 * kv, g), s0f[kv], aq);
+        ac = MM::mma8(lds_pair_frag_k<L::DVP>(sX + (16 * ta + l16) * LDX, 32 * kv, g), s0f[kv], ac);
+        ak = MM::mma8(lds_pair_frag_k<L::DVP>(sU + (16 * ta + l16) * LDX, 32 * kv, g), gnf[kv], ak);
+      }
+      f32x4 e;
+      float ksum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 16 * ta + 4 * g + i;
+        const float ga = fga[t], gk = __expf(gn - fg[t]);
+        aq[i] *= ga;    // gamma_t dO S_0^T
+        ac[i] *= -ga;   // -gamma_t dV S_0^T
+        ak[i] *= gk;    // e^{g_n - g_t} U dS_n^T
+        const float kv_ = static_cast<float>(sK[t * LDT + ch]);
+        e[i] = static_cast<float>(sQ[t * LDT + ch]) * aq[i] + static_cast<float>(sC[t * LDT + ch]) * ac[i] - kv_ * ak[i];
+        ksum += kv_ * ak[i];
+      }
+      dg_rows(ta, e);
+      // the end-of-chunk factor e^{g_n}: sum over every k_s . dK_n[s]
+      ksum += __shfl_xor(ksum, 1);
+      ksum += __shfl_xor(ksum, 2);
+      ksum += __shfl_xor(ksum, 4);
+      ksum += __shfl_xor(ksum, 8);
+      ksum += __shfl_xor(ksum, 16);
+      ksum += __shfl_xor(ksum, 32);
+      if (lane == 0) atomicAdd(&fdg[C - 1], ksum);
+      // intra-chunk terms (dM . Gamma and dL . Gamma are lower triangular)
+      const __bf16* dmr = sM + (16 * ta + l16) * LDD;
+      const __bf16* dlr = tT + (16 * ta + l16) * LDD;
+      aq = MM::mma8(lds_pair_frag_k<C>(dmr, 0, g), kf[0], aq);
+      ac = MM::mma8(lds_pair_frag_k<C>(dlr, 0, g), kf[0], ac);
+      if (ta >= 2) {
+        aq = MM::mma8(lds_pair_frag_k<C>(dmr, 32, g), kf[1], aq);
+        ac = MM::mma8(lds_pair_frag_k<C>(dlr, 32, g), kf[1], ac);
+      }
+      if (ta < 2) {
+        ak = MM::mma8(lds_col_frag(sM, LDD, 16 * ta + l16, 0, g, l16), qf[0], ak);
+        ak = MM::mma8(lds_col_frag(tT, LDD, 16 * ta + l16, 0, g, l16), cf[0], ak);
+      }
+      ak = MM::mma8(lds_col_frag(sM, LDD, 16 * ta + l16, 32, g, l16), qf[1], ak);
+      ak = MM::mma8(lds_col_frag(tT, LDD, 16 * ta + l16, 32, g, l16), cf[1], ak);
+      // c = b . k: dk += b . dc, db = k . dc
+      float bsum[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 16 * ta + 4 * g + i;
+        const uint32_t off = t * hdk + ch * 2;
+        const float kv_ = static_cast<float>(sK[t * LDT + ch]);
+        float bv = 0.f;
+        if (a.b_kind == kChannel)
+          bv = bf16_to_f32(buf_load_u16(rbc, off));
+        else if (a.b_kind == kScalar)
+          bv = fb[t];
+        ak[i] += bv * ac[i];
+        bsum[i] = kv_ * ac[i];
+        buf_store1((bf16_t*)nullptr, sq_, off, aq[i]);
+        buf_store1((bf16_t*)nullptr, sk_, off, ak[i]);
+        if (a.b_kind == kChannel) buf_store1((bf16_t*)nullptr, sb_, off, bsum[i]);
+      }
+      if (a.b_kind == kScalar) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float x = bsum[i];
+          x += __shfl_xor(x, 1);
+          x += __shfl_xor(x, 2);
+          x += __shfl_xor(x, 4);
+          x += __shfl_xor(x, 8);
+          if (l16 == 0) atomicAdd(&fdw[C + 16 * ta + 4 * g + i], x);
+        }
+      }
+    }
+  }
+  // gamma_n <S_0, dS_n>
+  sdot += __shfl_xor(sdot, 1);
+  sdot += __shfl_xor(sdot, 2);
+  sdot += __shfl_xor(sdot, 4);
+  sdot += __shfl_xor(sdot, 8);
+  sdot += __shfl_xor(sdot, 16);
+  sdot += __shfl_xor(sdot, 32);
+  if (lane == 0) atomicAdd(&fdg[C - 1], __expf(gn) * sdot);
+  // ---- dv = w . dV and dw = v . dV ----
+  const auto sv_ = make_rsrc(a.dv + rr * DV, rng_v);
+  const auto swc = make_rsrc(a.w_kind == kChannel ? a.dw + rr * DV : a.dv, a.w_kind == kChannel ? rng_v : 0u);
+  for (int item = tid; item < C * (DV / 8); item += 256) {
+    const int t = item / static_cast<int>(DV / 8), x0 = (item % static_cast<int>(DV / 8)) * 8;
+    const uint32_t off = t * hdv + x0 * 2;
+    float dx[8], vv[8], ww[8];
+    load8f(reinterpret_cast<const bf16_t*>(sX + t * LDX + x0), dx);
+    const uint4 uv = buf_load16(rv, off);
+    load8f(reinterpret_cast<const bf16_t*>(&uv), vv);
+    if (a.w_kind == kChannel) {
+      const uint4 uw = buf_load16(rwc, off);
+      load8f(reinterpret_cast<const bf16_t*>(&uw), ww);
+    } else {
+      const float ws = a.w_kind == kScalar ? bf16_to_f32(buf_load_u16(rws, t * h1)) : 1.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) ww[j] = ws;
+    }
+    bf16x8 ov, ow;
+    float wsum = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      ov[j] = static_cast<__bf16>(dx[j] * ww[j]);
+      ow[j] = static_cast<__bf16>(dx[j] * vv[j]);
+      wsum += dx[j] * vv[j];
+    }
+    buf_store16(sv_, off, __builtin_bit_cast(uint4, ov));
+    if (a.w_kind == kChannel) buf_store16(swc, off, __builtin_bit_cast(uint4, ow));
+    if (a.w_kind == kScalar) atomicAdd(&fdw[t], wsum);
+  }
+  lds_barrier();
+  // ---- per-token outputs: d log alpha (suffix sums of dg in the chunk), scalar db and dw ----
+  if (wave == 0) {
+    const uint32_t off = lane * h1;
+    if (a.alpha_kind == kScalar) {
+      float x = fdg[lane];
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const float y = __shfl_down(x, d);
+        if (lane + d < 64) x += y;
+      }
+      buf_store1((bf16_t*)nullptr, make_rsrc(a.dla + rr, rng_1), off, x);
+    }
+    if (a.b_kind == kScalar) buf_store1((bf16_t*)nullptr, make_rsrc(a.db + rr, rng_1), off, fdw[C + lane]);
+    if (a.w_kind == kScalar) buf_store1((bf16_t*)nullptr, make_rsrc(a.dw + rr, rng_1), off, fdw[lane]);
+  }
+}
+
+}  // namespace gdr

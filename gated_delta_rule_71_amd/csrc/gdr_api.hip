@@ -22,6 +22,14 @@ hipError_t launch_prefill(const IO* q, const IO* k, const IO* v, const IO* la, c
                           int b_kind, int w_kind, bool decay_first, void* workspace,
                           hipEvent_t mark, hipStream_t stream);
 bool prefill_supported(int io_dtype, int64_t DK, int64_t DV, int alpha_kind, bool decay_first);
+bool backward_supported(int io_dtype_bf16, int64_t DK, int64_t DV, int alpha_kind, bool shared_qk);
+size_t backward_workspace_bytes(int64_t nstate, int64_t T, int64_t DK, int64_t DV);
+hipError_t launch_backward(const bf16_t* q, const bf16_t* k, const bf16_t* v, const bf16_t* la,
+                           const bf16_t* bg, const bf16_t* wg, const float* S0, const bf16_t* dO,
+                           const float* dST, bf16_t* dq, bf16_t* dk, bf16_t* dv, bf16_t* dla,
+                           bf16_t* db, bf16_t* dw, float* dS0, int64_t B, int64_t T, int64_t H,
+                           int64_t DK, int64_t DV, int alpha_kind, int b_kind, int w_kind,
+                           void* workspace, hipStream_t s);
 size_t prefill_workspace_bytes(int io_dtype, int64_t nstate, int64_t T, int64_t DK, int64_t DV,
                                int alpha_kind, int b_kind, bool decay_first);
 }  // namespace gdr
@@ -221,5 +229,78 @@ GDR_EXPORT int gdr_decode_step(const gdr_problem* p, const void* q, const void* 
                                   p->heads, qk_heads(p), p->dk, p->dv, p->alpha_kind, p->b_kind, p->w_kind,
                                   decay_first, s);
   }
+  return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
+}
+
+namespace {
+bool bwd_supported(const gdr_problem* p) {
+  return gdr::backward_supported(p->io_dtype == GDR_BF16, p->dk, p->dv, p->alpha_kind,
+                                 qk_heads(p) == p->heads);
+}
+}  // namespace
+
+GDR_EXPORT size_t gdr_chunk_bwd_workspace_bytes(const gdr_problem* p) {
+  if (check_problem(p) != GDR_OK || !bwd_supported(p)) return 0;
+  return gdr::backward_workspace_bytes(p->batch * p->heads, p->seqlen, p->dk, p->dv);
+}
+
+GDR_EXPORT int gdr_chunk_bwd(const gdr_problem* p, const void* q, const void* k, const void* v,
+                             const void* log_alpha, const void* b, const void* w, const float* S0,
+                             const void* dO, const float* dS_T, void* dq, void* dk, void* dv,
+                             void* dlog_alpha, void* db, void* dw, float* dS0, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  int rc = check_problem(p);
+  if (rc != GDR_OK) return rc;
+  // the forward's inputs against one of the outputs (dv), then every output pairwise below
+  rc = check_tensors(p, p->seqlen, q, k, v, log_alpha, b, w, dv);
+  if (rc != GDR_OK) return rc;
+  if (!bwd_supported(p)) return GDR_ERR_UNSUPPORTED;
+  const int64_t nstate = p->batch * p->heads;
+  const int64_t rows = p->batch * p->seqlen * p->heads;
+  if (nstate == 0) return GDR_OK;
+  const int64_t sbytes = nstate * p->dk * p->dv * 4;
+  if (rows > 0) {
+    if (!dO || !dq || !dk) return GDR_ERR_INVALID_ARGUMENT;
+    if ((p->alpha_kind != GDR_GATE_NONE && !dlog_alpha) || (p->b_kind != GDR_GATE_NONE && !db) ||
+        (p->w_kind != GDR_GATE_NONE && !dw))
+      return GDR_ERR_INVALID_ARGUMENT;
+  }
+  const void* dla_ = gate_ptr(p->alpha_kind, dlog_alpha);
+  const void* db_ = gate_ptr(p->b_kind, db);
+  const void* dw_ = gate_ptr(p->w_kind, dw);
+  for (const void* ptr : {(const void*)S0, dO, (const void*)dS_T, (const void*)dq, (const void*)dk,
+                          dla_, db_, dw_, (const void*)dS0, (const void*)workspace})
+    if (ptr && !aligned16(ptr)) return GDR_ERR_MISALIGNED;
+  auto gate_bytes = [&](int32_t kind, int64_t width) {
+    return kind == GDR_GATE_SCALAR ? rows * 2 : kind == GDR_GATE_CHANNEL ? rows * width * 2 : 0;
+  };
+  const Range outs[] = {range_of(dq, dq ? rows * p->dk * 2 : 0), range_of(dk, dk ? rows * p->dk * 2 : 0),
+                        range_of(dv, rows * p->dv * 2),
+                        range_of(dla_, gate_bytes(p->alpha_kind, p->dk)),
+                        range_of(db_, gate_bytes(p->b_kind, p->dk)),
+                        range_of(dw_, gate_bytes(p->w_kind, p->dv)),
+                        range_of(dS0, dS0 ? sbytes : 0)};
+  const Range ins[] = {range_of(q, rows * p->dk * 2), range_of(k, rows * p->dk * 2),
+                       range_of(v, rows * p->dv * 2),
+                       range_of(gate_ptr(p->alpha_kind, log_alpha), gate_bytes(p->alpha_kind, p->dk)),
+                       range_of(gate_ptr(p->b_kind, b), gate_bytes(p->b_kind, p->dk)),
+                       range_of(gate_ptr(p->w_kind, w), gate_bytes(p->w_kind, p->dv)),
+                       range_of(S0, S0 ? sbytes : 0), range_of(dO, dO ? rows * p->dv * 2 : 0),
+                       range_of(dS_T, dS_T ? sbytes : 0)};
+  for (size_t i = 0; i < sizeof(outs) / sizeof(outs[0]); ++i) {
+    for (const Range& r : ins)
+      if (overlaps(outs[i], r)) return GDR_ERR_INVALID_ARGUMENT;
+    for (size_t j = i + 1; j < sizeof(outs) / sizeof(outs[0]); ++j)
+      if (overlaps(outs[i], outs[j])) return GDR_ERR_INVALID_ARGUMENT;
+  }
+  const size_t need = gdr_chunk_bwd_workspace_bytes(p);
+  if (workspace_bytes < need) return GDR_ERR_WORKSPACE_TOO_SMALL;
+  if (need > 0 && workspace == nullptr) return GDR_ERR_INVALID_ARGUMENT;
+  using T = gdr::bf16_t;
+  const hipError_t e = gdr::launch_backward(
+      (const T*)q, (const T*)k, (const T*)v, (const T*)gate_ptr(p->alpha_kind, log_alpha),
+      (const T*)gate_ptr(p->b_kind, b), (const T*)gate_ptr(p->w_kind, w), S0, (const T*)dO, dS_T,
+      (T*)dq, (T*)dk, (T*)dv, (T*)dla_, (T*)db_, (T*)dw_, dS0, p->batch, p->seqlen, p->heads, p->dk,
+      p->dv, p->alpha_kind, p->b_kind, p->w_kind, workspace, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
 }

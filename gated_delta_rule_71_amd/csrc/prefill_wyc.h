@@ -61,6 +61,8 @@ struct WycArgs {
   int* flag;   // [cix]          1: exact token path
   int64_t T, H, DV, nch;
   int b_kind, w_kind;
+  int alpha_kind;  // kChannel; kScalar (one log alpha per token, broadcast over the channels) and
+                   // kNone (alpha = 1) in the chunk-local kernel with an erase gate only
   int nsl;     // value slices per state (state kernel)
   int64_t Hk;  // q / k heads (H is a multiple): value head h reads q / k head h / (H / Hk)
 };
@@ -257,7 +259,8 @@ __global__ __launch_bounds__(512) void wyc_prep_kernel(WycArgs a) {
   const int64_t rqk = (bi * a.T + t0) * a.Hk + hi / (H / a.Hk);  // their row of the first token
   const auto rq = make_rsrc(a.q + rqk * DK, wy_range(left, a.Hk, DK));
   const auto rk = make_rsrc(a.k + rqk * DK, wy_range(left, a.Hk, DK));
-  const auto rla = make_rsrc(a.la + rr * DK, wy_range(left, H, DK));
+  const auto rla = make_rsrc(a.alpha_kind == kChannel ? a.la + rr * DK : a.q, a.alpha_kind == kChannel ? wy_range(left, H, DK) : 0u);
+  const auto rlas = make_rsrc(a.alpha_kind == kScalar ? a.la + rr : a.q, a.alpha_kind == kScalar ? wy_range(left, H, 1) : 0u);
   const auto rbc = make_rsrc(a.b_kind == kChannel ? a.bg + rr * DK : a.q, a.b_kind == kChannel ? wy_range(left, H, DK) : 0u);
   const auto rbs = make_rsrc(a.b_kind == kScalar ? a.bg + rr : a.q, a.b_kind == kScalar ? wy_range(left, H, 1) : 0u);
   const auto rv = make_rsrc(a.v + rr * DV, wy_range(left, H, DV));
@@ -275,6 +278,11 @@ __global__ __launch_bounds__(512) void wyc_prep_kernel(WycArgs a) {
     pb[u] = buf_load16(rbc, off);
     pl[u] = buf_load16(rla, off);
     pbs[u] = buf_load_u16(rbs, act ? t * h1 : oob);
+    if (a.alpha_kind == kScalar) {  // one log alpha per token on every channel
+      const uint32_t h = buf_load_u16(rlas, act ? t * h1 : oob);
+      const uint32_t w2 = h | (h << 16);
+      pl[u] = make_uint4(w2, w2, w2, w2);
+    }
   }
   constexpr int XPT = C * (DVP / 8) / NT;
   const int nxg = static_cast<int>(DV / 8);

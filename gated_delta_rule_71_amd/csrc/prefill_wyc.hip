@@ -100,6 +100,7 @@ hipError_t prefill_wyc_launch(const PrefillArgs<bf16_t>& p, int64_t nstate, int6
   a.nch = (p.T + 63) / 64;
   a.b_kind = p.b_kind;
   a.w_kind = p.w_kind;
+  a.alpha_kind = kChannel;
   const WycSizes z = wyc_sizes(nstate, p.T, DK, p.DV);
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   a.Qd = reinterpret_cast<__bf16*>(ws);

@@ -163,6 +163,46 @@ int gdr_decode_step(const gdr_problem* p, const void* q, const void* k, const vo
                     const void* log_alpha, const void* b, const void* w, float* S, void* o,
                     void* stream);
 
+/* Workspace bytes gdr_chunk_bwd needs for `p`; 0 for an invalid or unsupported
+ * problem.  Per 64-token chunk of every (batch, head): the chunk's affine map as
+ * for the per-channel forward (2 dk^2 + 2 dk dv + 132 dk + 128 dv + 20 bytes)
+ * and four bf16 dk x dv checkpoints (the state entering the chunk and the
+ * gradient of the state leaving it, each as rows and transposed), each array
+ * 256-byte aligned. */
+size_t gdr_chunk_bwd_workspace_bytes(const gdr_problem* p);
+
+/*
+ * Gradients of a chunkwise prefill: given dO (the gradient of every read-out)
+ * and dS_T (of the final state), the gradients of every input of gdr_chunk_fwd
+ * with the same problem.
+ *   q, k, v, log_alpha, b, w, S0   the forward's inputs (device, read only)
+ *   dO     [B,T,H,dv] io_dtype gradient of o
+ *   dS_T   [B,H,dk,dv] fp32 gradient of S_T; NULL means zeros
+ *   dq, dk [B,T,H,dk], dv [B,T,H,dv] io_dtype outputs
+ *   dlog_alpha, db, dw  io_dtype outputs shaped like log_alpha, b and w (each
+ *          ignored, and may be NULL, when that gate's kind is GDR_GATE_NONE);
+ *          with one shared beta passed as both b and w the caller adds db and dw
+ *   dS0    [B,H,dk,dv] fp32 gradient of S0; NULL means "not needed"
+ *   workspace, workspace_bytes  device scratch of at least
+ *          gdr_chunk_bwd_workspace_bytes(p) bytes, 16-byte aligned; calls that
+ *          share one workspace must not overlap in time.
+ * Outputs must not overlap the inputs or each other.  Supported: bf16, a scalar
+ * decay or none (both orders are then the same recurrence), any erase and
+ * write gate kinds, dk in {32, 64, 128}, dv a multiple of 16 up to 128, one q /
+ * k head per value head; GDR_ERR_UNSUPPORTED otherwise.
+ * Method: the adjoint of the chunk form of gdr_chunk_fwd ("Recurrent Memory",
+ * sections 03 and 04): the state at every chunk boundary by a forward pass over
+ * the chunk maps, the gradient of the state at every boundary by the transposed
+ * maps in reverse, and each chunk's input gradients from those two by matrix
+ * products, the transposed triangular solve and a suffix sum of the decay
+ * gradient inside the chunk.
+ */
+int gdr_chunk_bwd(const gdr_problem* p, const void* q, const void* k, const void* v,
+                  const void* log_alpha, const void* b, const void* w, const float* S0,
+                  const void* dO, const float* dS_T, void* dq, void* dk, void* dv,
+                  void* dlog_alpha, void* db, void* dw, float* dS0, void* workspace,
+                  size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -174,3 +174,48 @@ def test_python_binding_rejects_host_tensors():
         gdr.chunk_fwd(q, q, q)
     with pytest.raises(TypeError):
         gdr.chunk_fwd(q.float(), q, q)
+
+
+def bwd_ptrs():
+    step = 1 << 32
+    names = ("q", "k", "v", "la", "b", "w", "S0", "dO", "dS_T", "dq", "dk", "dv", "dla", "db", "dw",
+             "dS0")
+    return {n: (i + 1) * step for i, n in enumerate(names)}
+
+
+def bwd_call(p, ws=0, ws_bytes=0, **over):
+    a = bwd_ptrs()
+    a.update(over)
+    return N.chunk_bwd_raw(p, *[a[n] for n in ("q", "k", "v", "la", "b", "w", "S0", "dO", "dS_T", "dq",
+                                                "dk", "dv", "dla", "db", "dw", "dS0")], ws, ws_bytes, 0)
+
+
+def test_backward_workspace_and_validation():
+    sp = prob(alpha_kind=N.GATE_SCALAR, b_kind=N.GATE_SCALAR, w_kind=N.GATE_SCALAR)
+    # the per-channel forward's chunk map and four bf16 dk x dv checkpoints per 64-token chunk of
+    # every (batch, head), each array rounded up to 256 bytes
+    r = lambda n: (n + 255) // 256 * 256
+    ch = 2 * 3 * 2
+    need = r(ch * 128 * 128 * 2) + r(ch * 64 * 128 * 2) + r(ch * 128 * 128 * 2) + \
+        r(ch * 64 * 128 * 2) + r(ch * 132 * 4) + r(ch * 4) + 4 * r(ch * 128 * 128 * 2)
+    assert N.bwd_workspace_bytes(sp) == need
+    # outside the backward's scope: per-channel decay, fp32, dv > 128, grouped q / k heads
+    for p in (prob(), prob(alpha_kind=N.GATE_SCALAR, io_dtype=N.GDR_FP32),
+              prob(alpha_kind=N.GATE_SCALAR, dv=256), prob(alpha_kind=N.GATE_SCALAR, dk=16),
+              prob(alpha_kind=N.GATE_SCALAR, heads=4, qk_heads=2)):
+        assert N.bwd_workspace_bytes(p) == 0
+        assert bwd_call(p) == N.GDR_ERR_UNSUPPORTED
+    ws = 20 * (1 << 32)
+    assert bwd_call(sp, ws, need - 1) == N.GDR_ERR_WORKSPACE_TOO_SMALL
+    assert bwd_call(sp, 0, need) == N.GDR_ERR_INVALID_ARGUMENT
+    assert bwd_call(sp, ws + 8, need) == N.GDR_ERR_MISALIGNED
+    for name in ("q", "dO", "dq", "dk", "dv", "dla", "db", "dw"):
+        assert bwd_call(sp, ws, need, **{name: 0}) == N.GDR_ERR_INVALID_ARGUMENT, name
+    for name in ("dO", "dS_T", "dq", "dla", "dS0"):
+        assert bwd_call(sp, ws, need, **{name: bwd_ptrs()[name] + 4}) == N.GDR_ERR_MISALIGNED, name
+    # an output over an input, or over another output
+    assert bwd_call(sp, ws, need, dq=bwd_ptrs()["k"] + 64) == N.GDR_ERR_INVALID_ARGUMENT
+    assert bwd_call(sp, ws, need, dk=bwd_ptrs()["dq"] + 64) == N.GDR_ERR_INVALID_ARGUMENT
+    assert bwd_call(sp, ws, need, dS0=bwd_ptrs()["dS_T"]) == N.GDR_ERR_INVALID_ARGUMENT
+    # nothing to do
+    assert bwd_call(prob(alpha_kind=N.GATE_SCALAR, batch=0)) == N.GDR_OK
