@@ -199,8 +199,21 @@ __global__ __launch_bounds__(2 * DK) void bwd_chain_kernel(BwdArgs a) {
     }
   };
 
+  // e^{G_n} and D of a chunk, loaded one chunk ahead
+  float4 e4n[2];
+  bf16x4 d4n[2];
+  auto fetch_ed = [&](int64_t c) __attribute__((always_inline)) {
+    const int64_t cix = bh * nch + c;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int tl = 2 * w + u;
+      e4n[u] = *reinterpret_cast<const float4*>(a.Egn + cix * (DK + 4) + 16 * tl + 4 * g);
+      if (!REV) d4n[u] = *reinterpret_cast<const bf16x4*>(a.Dt + cix * DV * DK + tiled16(col, 16 * tl + 4 * g, DK));
+    }
+  };
   if (nch > 0) {
     fetch(REV ? nch - 1 : 0);
+    fetch_ed(REV ? nch - 1 : 0);
     stage(0);
   }
   for (int64_t it = 0; it < nch; ++it) {
@@ -211,8 +224,8 @@ __global__ __launch_bounds__(2 * DK) void bwd_chain_kernel(BwdArgs a) {
     *reinterpret_cast<F8*>(smem + 2 * BUF + (bs * NKB + w) * 1024 + lane * 16) = acc_pair_frag<__bf16>(S[0], S[1]);
     __bf16* ckR = (REV ? a.GR : a.SR) + cix * DK * DV;
     __bf16* ckT = (REV ? a.GT : a.ST) + cix * DV * DK;
-    float4 e4[2];
-    bf16x4 d4[2];
+    float4 e4[2] = {e4n[0], e4n[1]};
+    bf16x4 d4[2] = {d4n[0], d4n[1]};
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int tl = 2 * w + u;
@@ -222,10 +235,11 @@ __global__ __launch_bounds__(2 * DK) void bwd_chain_kernel(BwdArgs a) {
       *reinterpret_cast<bf16x4*>(ckT + tiled16(col, 16 * tl + 4 * g, DK)) = s4;
 #pragma unroll
       for (int i = 0; i < 4; ++i) ckR[tiled16(16 * tl + 4 * g + i, col, DV)] = s4[i];
-      e4[u] = *reinterpret_cast<const float4*>(a.Egn + cix * (DK + 4) + 16 * tl + 4 * g);
-      if (!REV) d4[u] = *reinterpret_cast<const bf16x4*>(a.Dt + cix * DV * DK + tiled16(col, 16 * tl + 4 * g, DK));
     }
-    if (it + 1 < nch) fetch(REV ? c - 1 : c + 1);
+    if (it + 1 < nch) {
+      fetch(REV ? c - 1 : c + 1);
+      fetch_ed(REV ? c - 1 : c + 1);
+    }
     lds_barrier();  // the exchange slot and the staged operands of chunk c are in
 
     const unsigned char* B = smem + bs * BUF;
@@ -299,13 +313,14 @@ struct BwdLocalLayout {
 };
 
 template <int DK>
-__global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a) {
+__global__ __launch_bounds__(512) void bwd_local_kernel(BwdArgs a) {
   using L = BwdLocalLayout<DK>;
   using MM = Mma<__bf16>;
   using F8 = MM::F8;
   static_assert(L::fits, "LDS layout exceeds the gfx950 workgroup limit");
   constexpr int C = L::C, LDT = L::LDT, LDX = L::LDX, LDD = L::LDD, LDA = L::LDA, LDI = L::LDI, LDL = L::LDL;
-  constexpr int NKB = DK / 32, NTD = DK / 16;
+  constexpr int NKB = DK / 32, NTD = DK / 16, NKVM = L::DVP / 32;
+  constexpr int NT = 512, NW = NT / 64;  // threads, waves
 
   __shared__ __attribute__((aligned(32))) unsigned char smem[L::total];
   __bf16* sQ = reinterpret_cast<__bf16*>(smem + L::oQ);
@@ -353,7 +368,7 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a) {
   const auto rws = make_rsrc(a.w_kind == kScalar ? a.wg + rr : a.v, a.w_kind == kScalar ? rng_1 : 0u);
   const auto rdo = make_rsrc(a.dO + rr * DV, rng_v);
   const auto rla = make_rsrc(a.alpha_kind == kScalar ? a.la + rr : a.q, a.alpha_kind == kScalar ? rng_1 : 0u);
-  for (int item = tid; item < C * (DK / 8); item += 256) {
+  for (int item = tid; item < C * (DK / 8); item += NT) {
     const int t = item / (DK / 8), d0 = (item % (DK / 8)) * 8;
     const uint32_t off = t * hdk + d0 * 2;
     const uint4 uq = buf_load16(rq, off), uk = buf_load16(rk, off);
@@ -377,7 +392,7 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a) {
     *reinterpret_cast<bf16x8*>(sC + t * LDT + d0) = cb;
   }
   // value rows, zero past d_v (up to the next multiple of 32, the contraction step)
-  for (int item = tid; item < C * (L::DVP / 8); item += 256) {
+  for (int item = tid; item < C * (L::DVP / 8); item += NT) {
     const int t = item / (L::DVP / 8), x0 = (item % (L::DVP / 8)) * 8;
     bf16x8 xb, ob;
     const bf16x8 zero8 = {};
@@ -409,7 +424,7 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a) {
     *reinterpret_cast<bf16x8*>(sU + t * LDX + x0) = zero8;
     *reinterpret_cast<bf16x8*>(sDU + t * LDX + x0) = zero8;
   }
-  for (int i = tid; i < C * LDD / 8; i += 256) reinterpret_cast<uint4*>(sM)[i] = make_uint4(0, 0, 0, 0);
+  for (int i = tid; i < C * LDD / 8; i += NT) reinterpret_cast<uint4*>(sM)[i] = make_uint4(0, 0, 0, 0);
   if (wave == 0) {
     // inclusive prefix sum of log alpha over the chunk (lane = token)
     float x = a.alpha_kind == kScalar ? bf16_to_f32(buf_load_u16(rla, lane * h1)) : 0.f;
@@ -430,7 +445,7 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a) {
 
   // ---- Gram tiles: M = Gamma . tril(Q K^T) (bf16), L = Gamma . strict_tril(C K^T) as -L below
   // the diagonal blocks and fp32 diagonal blocks ----
-  for (int job = wave; job < 20; job += 4) {
+  for (int job = wave; job < 20; job += NW) {
     const int grp = job / 10, tix = job % 10;
     const int ta = tix >= 6 ? 3 : tix >= 3 ? 2 : tix >= 1 ? 1 : 0, tb = tix - ta * (ta + 1) / 2;
     const __bf16* ar = (grp == 0 ? sQ : sC) + (16 * ta + l16) * LDT;
@@ -455,8 +470,8 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a) {
   lds_barrier();
   if (wave < 2 && lane < 32) wy_diag_inverses<LDL, LDI>(Ld, dInv, wave, lane, l16);
   lds_barrier();
-  // ---- T = (I + L)^{-1}: wave j forms column block j by blocked forward substitution ----
-  {
+  // ---- T = (I + L)^{-1}: wave j < 4 forms column block j by blocked forward substitution ----
+  if (wave < 4) {
     const int j = wave;
     bf16x4 af[6], tf[4];
 #pragma unroll
@@ -481,8 +496,8 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) tT[(16 * i + 4 * g + e) * LDD + 16 * j + l16] = static_cast<__bf16>(R[i][e]);
   }
-  // ---- V = X - Diag(gamma) C S_0, in place of X (wave: value tiles cv = wave, wave + 4) ----
-  for (int cv = wave; cv < NCV; cv += 4) {
+  // ---- V = X - Diag(gamma) C S_0, in place of X (wave: value tiles cv = wave, wave + NW) ----
+  for (int cv = wave; cv < NCV; cv += NW) {
     F8 sf[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) sf[kb] = tiled_row_frag(ST, DK, 16 * cv + l16, 32 * kb, g);
@@ -501,7 +516,7 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a) {
   }
   lds_barrier();
   // ---- U = T V ----
-  for (int cv = wave; cv < NCV; cv += 4) {
+  for (int cv = wave; cv < NCV; cv += NW) {
     F8 vf[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) vf[ks] = lds_col_frag(sX, LDX, 16 * cv + l16, 32 * ks, g, l16);
@@ -514,7 +529,7 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a) {
     }
   }
   // ---- dU = M^T dO + K_n dS_n (M^T row s: tokens t >= s) ----
-  for (int cv = wave; cv < NCV; cv += 4) {
+  for (int cv = wave; cv < NCV; cv += NW) {
     F8 gf[NKB], of[2];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) gf[kb] = tiled_row_frag(GT, DK, 16 * cv + l16, 32 * kb, g);
@@ -535,7 +550,7 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a) {
   }
   lds_barrier();
   // ---- dV = T^T dU, in place of V (T^T row s: tokens t >= s) ----
-  for (int cv = wave; cv < NCV; cv += 4) {
+  for (int cv = wave; cv < NCV; cv += NW) {
     F8 df[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) df[ks] = lds_col_frag(sDU, LDX, 16 * cv + l16, 32 * ks, g, l16);
@@ -571,13 +586,15 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a) {
   };
   // ---- dM = tril(dO U^T) and dL = -strict_tril(dV U^T); their products with M and L go to dg,
   // dM . Gamma replaces M and dL . Gamma replaces T ----
-  for (int job = wave; job < 20; job += 4) {
+  for (int job = wave; job < 20; job += NW) {
     const int grp = job / 10, tix = job % 10;
     const int ta = tix >= 6 ? 3 : tix >= 3 ? 2 : tix >= 1 ? 1 : 0, tb = tix - ta * (ta + 1) / 2;
     const __bf16* ar = (grp == 0 ? sO : sX) + (16 * ta + l16) * LDX;
     const __bf16* br = sU + (16 * tb + l16) * LDX;
     f32x4 acc = zero4();
-    for (int kv = 0; kv < NKV; ++kv) acc = MM::mma8(lds_pair_frag_k<L::DVP>(ar, 32 * kv, g), lds_pair_frag_k<L::DVP>(br, 32 * kv, g), acc);
+#pragma unroll
+    for (int kv = 0; kv < NKVM; ++kv)
+      if (kv < NKV) acc = MM::mma8(lds_pair_frag_k<L::DVP>(ar, 32 * kv, g), lds_pair_frag_k<L::DVP>(br, 32 * kv, g), acc);
     const int s = 16 * tb + l16;
     f32x4 e;
 #pragma unroll
@@ -602,15 +619,19 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a) {
   }
   lds_barrier();
 
-  // ---- dq, dc, dk tiles (wave: channel tiles tl = wave, wave + 4; all four token tiles) ----
+  // ---- dq, dc, dk tiles (wave: channel tiles tl = wave, wave + NW; all four token tiles) ----
   const auto sq_ = make_rsrc(a.dq + rr * DK, rng_k);
   const auto sk_ = make_rsrc(a.dk + rr * DK, rng_k);
   const auto sb_ = make_rsrc(a.b_kind == kChannel ? a.db + rr * DK : a.dq, a.b_kind == kChannel ? rng_k : 0u);
   float sdot = 0.f;  // <S_0, dS_n> over this wave's channel tiles
-  for (int tl = wave; tl < NTD; tl += 4) {
+  for (int tl = wave; tl < NTD; tl += NW) {
     const int ch = 16 * tl + l16;
-    F8 s0f[4], gnf[4];  // rows ch of S_0 and dS_n, k = value columns
-    for (int kv = 0; kv < NKV; ++kv) {
+    F8 s0f[NKVM], gnf[NKVM];  // rows ch of S_0 and dS_n, k = value columns
+    // (compile-time indices with a uniform guard: a register array indexed at run time becomes a
+    // chain of selects)
+#pragma unroll
+    for (int kv = 0; kv < NKVM; ++kv) {
+      if (kv >= NKV) break;
       const bool hiok = 32 * kv + 16 < DV;
       s0f[kv] = tiled_row_frag(SR, static_cast<int>(DV), ch, 32 * kv, g, hiok);
       gnf[kv] = tiled_row_frag(GR, static_cast<int>(DV), ch, 32 * kv, g, hiok);
@@ -627,7 +648,9 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a) {
 #pragma unroll
     for (int ta = 0; ta < 4; ++ta) {
       f32x4 aq = zero4(), ac = zero4(), ak = zero4();
-      for (int kv = 0; kv < NKV; ++kv) {
+#pragma unroll
+      for (int kv = 0; kv < NKVM; ++kv) {
+        if (kv >= NKV) break;
         aq = MM::mma8(lds_pair_frag_k<L::DVP>(sO + (16 * ta + l16) * LDX, 32 * kv, g), s0f[kv], aq);
         ac = MM::mma8(lds_pair_frag_k<L::DVP>(sX + (16 * ta + l16) * LDX, 32 * kv, g), s0f[kv], ac);
         ak = MM::mma8(lds_pair_frag_k<L::DVP>(sU + (16 * ta + l16) * LDX, 32 * kv, g), gnf[kv], ak);
@@ -711,7 +734,7 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a) {
   // ---- dv = w . dV and dw = v . dV ----
   const auto sv_ = make_rsrc(a.dv + rr * DV, rng_v);
   const auto swc = make_rsrc(a.w_kind == kChannel ? a.dw + rr * DV : a.dv, a.w_kind == kChannel ? rng_v : 0u);
-  for (int item = tid; item < C * (DV / 8); item += 256) {
+  for (int item = tid; item < C * (DV / 8); item += NT) {
     const int t = item / static_cast<int>(DV / 8), x0 = (item % static_cast<int>(DV / 8)) * 8;
     const uint32_t off = t * hdv + x0 * 2;
     float dx[8], vv[8], ww[8];

@@ -31,7 +31,7 @@ hipError_t launch_dk(WycArgs f, BwdArgs a, int64_t nstate, hipStream_t s) {
   const unsigned nsl = static_cast<unsigned>(nstate * (a.DV / 16));
   hipLaunchKernelGGL((bwd_chain_kernel<DK, false>), dim3(nsl), dim3(2 * DK), 0, s, a);
   hipLaunchKernelGGL((bwd_chain_kernel<DK, true>), dim3(nsl), dim3(2 * DK), 0, s, a);
-  hipLaunchKernelGGL((bwd_local_kernel<DK>), dim3((unsigned)nblk), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((bwd_local_kernel<DK>), dim3((unsigned)nblk), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 }  // namespace
