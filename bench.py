@@ -63,6 +63,26 @@ def prefill_bytes(wl):
     return n
 
 
+def backward_bytes(wl):
+    """Minimal HBM bytes of one backward call: the forward's inputs and do read once, every input
+    gradient written once, S0 read (if any) and dS0 written (dS_T is not passed here)."""
+    es = 2
+    rows = wl.B * wl.T * wl.H
+    gate = {"none": 0, "scalar": 1, "channel": wl.DK}
+    wgate = {"none": 0, "scalar": 1, "channel": wl.DV}
+    per_row = 2 * wl.DK + wl.DV + gate[wl.alpha] + gate[wl.b] + wgate[wl.w]
+    if wl.shared_beta and wl.b != "none":
+        per_row -= gate[wl.b]  # one buffer passed as both b and w
+    n = rows * (2 * per_row + wl.DV) * es  # inputs and their gradients; do
+    state = wl.B * wl.H * wl.DK * wl.DV * 4
+    return n + state * (2 if wl.s0_std > 0 else 1)
+
+
+def backward_supported(wl):
+    return (wl.dtype == "bf16" and wl.alpha != "channel" and wl.DV <= 128 and wl.DK in (32, 64, 128)
+            and (wl.HK in (0, wl.H)))
+
+
 def decode_bytes(wl):
     es = 2
     n_state = wl.B * wl.H
@@ -182,6 +202,44 @@ def time_decode(wl, n_steps, dev):
     return ms
 
 
+def time_backward(wl, steps, warmup, dev):
+    """gdr_chunk_bwd on the workload's inputs with a seeded output gradient (dS_T = None), the
+    workspace allocated once; mean of `steps` calls between HIP events on the launch stream."""
+    import torch
+    import gated_delta_rule_71_amd as gdr
+    import synth
+    x = synth.make_prefill(wl)
+    g = {n: (None if t is None else t.to(dev)) for n, t in x.items()}
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(wl.seed + 101)
+    do = torch.randn((wl.B, wl.T, wl.H, wl.DV), generator=gen, device=dev).to(torch.bfloat16)
+    prob = gdr.make_problem(wl.B, wl.H, wl.T, wl.DK, wl.DV, gdr._native.GDR_BF16,
+                            gdr._native.GATE_SCALAR if wl.alpha == "scalar" else gdr._native.GATE_NONE,
+                            {"none": 0, "scalar": 1, "channel": 2}[wl.b],
+                            {"none": 0, "scalar": 1, "channel": 2}[wl.w], 0)
+    need = gdr._native.bwd_workspace_bytes(prob)
+    ws = torch.empty((need,), dtype=torch.uint8, device=dev)
+    run = lambda: gdr.chunk_bwd(g["q"], g["k"], g["v"], g["log_alpha"], g["b"], g["w"], g["S0"], do,
+                                None, workspace=ws)
+    for _ in range(max(1, warmup)):
+        run()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    nb = backward_bytes(wl)
+    gbs = nb / (ms * 1e-3) / 1e9
+    return {"ms": ms, "tokens_per_s": wl.B * wl.T / (ms * 1e-3), "workspace_bytes": need,
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": gbs / PEAK_HBM_GBS, "algorithmic_bytes": nb,
+                         "scope": "one gdr_chunk_bwd call: chunk maps, two chains, chunk-local adjoint"}}
+
+
 def time_hooks(wl, dev, positions=64, reps=5):
     """State decomposition ("How Linear Attention Remembers", Analytical Framework): C_i^(t) of
     `positions` evenly spaced positions at the last token, batch row 0 of the workload, one
@@ -243,6 +301,8 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=None)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip timing gdr_chunk_bwd (run for bf16 scalar- or no-decay workloads)")
     ap.add_argument("--hooks", action="store_true",
                     help="also time the state-decomposition hook (64 positions, one sequence)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -316,6 +376,8 @@ def main():
                          "states_per_s": dw.B * dw.H / (ms * 1e-3), "value": gbs, "unit": "GB/s",
                          "hbm_frac": gbs / PEAK_HBM_GBS, "bytes_per_step": db,
                          "traffic": recorded_traffic("decode:decode")}
+    if not args.no_backward and backward_supported(wl):
+        out["backward"] = time_backward(wl, args.steps, args.warmup, dev)
     if args.hooks:
         out["hooks"] = time_hooks(wl, dev)
     if not args.no_cpu_baseline:
