@@ -122,6 +122,16 @@ __device__ __forceinline__ Mma<__bf16>::F8 lds_col_frag(const __bf16* base, int 
   return f;
 }
 
+// Sum over the 16 lanes of a row (lanes 16 r .. 16 r + 15), in every lane of the row: four DPP
+// row rotations (row_ror 8, 4, 2, 1), no LDS traffic.
+__device__ __forceinline__ float row_sum16(float x) {
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xf, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x124, 0xf, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x122, 0xf, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x121, 0xf, 0xf, false));
+  return x;
+}
+
 // ------------------------------------------------------------------ chains over the chunks
 
 // One workgroup per (state, 16 value columns); DK / 32 waves, wave w holding S's channel tiles
@@ -368,59 +378,102 @@ __global__ __launch_bounds__(512) void bwd_local_kernel(BwdArgs a) {
   const auto rws = make_rsrc(a.w_kind == kScalar ? a.wg + rr : a.v, a.w_kind == kScalar ? rng_1 : 0u);
   const auto rdo = make_rsrc(a.dO + rr * DV, rng_v);
   const auto rla = make_rsrc(a.alpha_kind == kScalar ? a.la + rr : a.q, a.alpha_kind == kScalar ? rng_1 : 0u);
-  for (int item = tid; item < C * (DK / 8); item += NT) {
-    const int t = item / (DK / 8), d0 = (item % (DK / 8)) * 8;
-    const uint32_t off = t * hdk + d0 * 2;
-    const uint4 uq = buf_load16(rq, off), uk = buf_load16(rk, off);
-    float kf[8], cf[8];
-    load8f(reinterpret_cast<const bf16_t*>(&uk), kf);
-    if (a.b_kind == kChannel) {
-      const uint4 ub = buf_load16(rbc, off);
-      load8f(reinterpret_cast<const bf16_t*>(&ub), cf);
+  // The checkpoint fragments each wave needs later (one value tile cv = wave and one channel tile
+  // tl = wave at most: d_v <= 128 and d_k <= 128 give at most NW of each) are loaded first, with
+  // the input rows, so that their latency is paid once.
+  static_assert(NTD <= NW && L::DVP / 16 <= NW, "one value tile and one channel tile per wave");
+  F8 stf[NKB], gtf[NKB], s0f[NKVM], gnf[NKVM];
+  if (wave < NCV) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) cf[j] *= kf[j];
-    } else {
-      const float bs = a.b_kind == kScalar ? bf16_to_f32(buf_load_u16(rbs, t * h1)) : 0.f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) cf[j] = bs * kf[j];
+    for (int kb = 0; kb < NKB; ++kb) {
+      stf[kb] = tiled_row_frag(ST, DK, 16 * wave + l16, 32 * kb, g);  // S_0 column, k = channels
+      gtf[kb] = tiled_row_frag(GT, DK, 16 * wave + l16, 32 * kb, g);  // dS_n column
     }
-    bf16x8 cb;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) cb[j] = static_cast<__bf16>(cf[j]);
-    *reinterpret_cast<uint4*>(sQ + t * LDT + d0) = uq;
-    *reinterpret_cast<uint4*>(sK + t * LDT + d0) = uk;
-    *reinterpret_cast<bf16x8*>(sC + t * LDT + d0) = cb;
   }
-  // value rows, zero past d_v (up to the next multiple of 32, the contraction step)
-  for (int item = tid; item < C * (L::DVP / 8); item += NT) {
-    const int t = item / (L::DVP / 8), x0 = (item % (L::DVP / 8)) * 8;
-    bf16x8 xb, ob;
-    const bf16x8 zero8 = {};
-    if (x0 < DV) {
-      const uint32_t off = t * hdv + x0 * 2;
-      const uint4 uv = buf_load16(rv, off), ud = buf_load16(rdo, off);
-      float xf[8];
-      load8f(reinterpret_cast<const bf16_t*>(&uv), xf);
-      if (a.w_kind == kChannel) {
-        const uint4 uw = buf_load16(rwc, off);
-        float wf[8];
-        load8f(reinterpret_cast<const bf16_t*>(&uw), wf);
+  if (wave < NTD) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) xf[j] *= wf[j];
-      } else if (a.w_kind == kScalar) {
-        const float ws = bf16_to_f32(buf_load_u16(rws, t * h1));
-#pragma unroll
-        for (int j = 0; j < 8; ++j) xf[j] *= ws;
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) xb[j] = static_cast<__bf16>(xf[j]);
-      ob = __builtin_bit_cast(bf16x8, ud);
-    } else {
-      xb = zero8;
-      ob = zero8;
+    for (int kv = 0; kv < NKVM; ++kv) {
+      if (kv >= NKV) break;
+      const bool hiok = 32 * kv + 16 < DV;
+      s0f[kv] = tiled_row_frag(SR, static_cast<int>(DV), 16 * wave + l16, 32 * kv, g, hiok);  // S_0 row
+      gnf[kv] = tiled_row_frag(GR, static_cast<int>(DV), 16 * wave + l16, 32 * kv, g, hiok);  // dS_n row
     }
-    *reinterpret_cast<bf16x8*>(sX + t * LDX + x0) = xb;
-    *reinterpret_cast<bf16x8*>(sO + t * LDX + x0) = ob;
+  }
+  // q, k (and b) rows: every load, then the stores to LDS
+  constexpr int NQI = (C * (DK / 8) + NT - 1) / NT, NVI = C * (L::DVP / 8) / NT;
+  uint4 uq[NQI], uk[NQI], ub[NQI];
+  uint16_t ubs[NQI];
+#pragma unroll
+  for (int j = 0; j < NQI; ++j) {
+    const int item = tid + NT * j;
+    const bool in = item < C * (DK / 8);
+    const int t = in ? item / (DK / 8) : 0, d0 = in ? (item % (DK / 8)) * 8 : 0;
+    const uint32_t off = in ? t * hdk + d0 * 2 : oob;
+    uq[j] = buf_load16(rq, off);
+    uk[j] = buf_load16(rk, off);
+    ub[j] = buf_load16(rbc, off);
+    ubs[j] = buf_load_u16(rbs, in ? t * h1 : oob);
+  }
+  uint4 uv[NVI], ud[NVI], uw[NVI];
+  uint16_t uws[NVI];
+#pragma unroll
+  for (int j = 0; j < NVI; ++j) {
+    const int item = tid + NT * j;
+    const int t = item / (L::DVP / 8), x0 = (item % (L::DVP / 8)) * 8;
+    const uint32_t off = x0 < DV ? t * hdv + x0 * 2 : oob;
+    uv[j] = buf_load16(rv, off);
+    ud[j] = buf_load16(rdo, off);
+    uw[j] = buf_load16(rwc, off);
+    uws[j] = buf_load_u16(rws, x0 < DV ? t * h1 : oob);
+  }
+#pragma unroll
+  for (int j = 0; j < NQI; ++j) {
+    const int item = tid + NT * j;
+    if (item < C * (DK / 8)) {
+      const int t = item / (DK / 8), d0 = (item % (DK / 8)) * 8;
+      float kf[8], cf[8];
+      load8f(reinterpret_cast<const bf16_t*>(&uk[j]), kf);
+      if (a.b_kind == kChannel) {
+        load8f(reinterpret_cast<const bf16_t*>(&ub[j]), cf);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) cf[e] *= kf[e];
+      } else {
+        const float bs = a.b_kind == kScalar ? bf16_to_f32(ubs[j]) : 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) cf[e] = bs * kf[e];
+      }
+      bf16x8 cb;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) cb[e] = static_cast<__bf16>(cf[e]);
+      *reinterpret_cast<uint4*>(sQ + t * LDT + d0) = uq[j];
+      *reinterpret_cast<uint4*>(sK + t * LDT + d0) = uk[j];
+      *reinterpret_cast<bf16x8*>(sC + t * LDT + d0) = cb;
+    }
+  }
+  // value rows (x = w . v and dO), zero past d_v up to the next multiple of 32 (the contraction
+  // step), and the padding of U and dU
+#pragma unroll
+  for (int j = 0; j < NVI; ++j) {
+    const int item = tid + NT * j;
+    const int t = item / (L::DVP / 8), x0 = (item % (L::DVP / 8)) * 8;
+    float xf[8];
+    load8f(reinterpret_cast<const bf16_t*>(&uv[j]), xf);
+    if (a.w_kind == kChannel) {
+      float wf[8];
+      load8f(reinterpret_cast<const bf16_t*>(&uw[j]), wf);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xf[e] *= wf[e];
+    } else if (a.w_kind == kScalar) {
+      const float ws = bf16_to_f32(uws[j]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xf[e] *= ws;
+    }
+    bf16x8 xb;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) xb[e] = static_cast<__bf16>(xf[e]);
+    const bf16x8 zero8 = {};
+    *reinterpret_cast<bf16x8*>(sX + t * LDX + x0) = xb;  // (zero past d_v: those loads read zero)
+    *reinterpret_cast<uint4*>(sO + t * LDX + x0) = ud[j];
     *reinterpret_cast<bf16x8*>(sU + t * LDX + x0) = zero8;
     *reinterpret_cast<bf16x8*>(sDU + t * LDX + x0) = zero8;
   }
@@ -497,15 +550,13 @@ __global__ __launch_bounds__(512) void bwd_local_kernel(BwdArgs a) {
       for (int e = 0; e < 4; ++e) tT[(16 * i + 4 * g + e) * LDD + 16 * j + l16] = static_cast<__bf16>(R[i][e]);
   }
   // ---- V = X - Diag(gamma) C S_0, in place of X (wave: value tiles cv = wave, wave + NW) ----
-  for (int cv = wave; cv < NCV; cv += NW) {
-    F8 sf[NKB];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) sf[kb] = tiled_row_frag(ST, DK, 16 * cv + l16, 32 * kb, g);
+  if (wave < NCV) {
+    const int cv = wave;
 #pragma unroll
     for (int ta = 0; ta < 4; ++ta) {
       f32x4 acc = zero4();
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) acc = MM::mma8(lds_pair_frag_k<DK>(sC + (16 * ta + l16) * LDT, 32 * kb, g), sf[kb], acc);
+      for (int kb = 0; kb < NKB; ++kb) acc = MM::mma8(lds_pair_frag_k<DK>(sC + (16 * ta + l16) * LDT, 32 * kb, g), stf[kb], acc);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = 16 * ta + 4 * g + i;
@@ -529,17 +580,16 @@ __global__ __launch_bounds__(512) void bwd_local_kernel(BwdArgs a) {
     }
   }
   // ---- dU = M^T dO + K_n dS_n (M^T row s: tokens t >= s) ----
-  for (int cv = wave; cv < NCV; cv += NW) {
-    F8 gf[NKB], of[2];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) gf[kb] = tiled_row_frag(GT, DK, 16 * cv + l16, 32 * kb, g);
+  if (wave < NCV) {
+    const int cv = wave;
+    F8 of[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) of[ks] = lds_col_frag(sO, LDX, 16 * cv + l16, 32 * ks, g, l16);
 #pragma unroll
     for (int ta = 0; ta < 4; ++ta) {
       f32x4 acc = zero4();
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) acc = MM::mma8(lds_pair_frag_k<DK>(sK + (16 * ta + l16) * LDT, 32 * kb, g), gf[kb], acc);
+      for (int kb = 0; kb < NKB; ++kb) acc = MM::mma8(lds_pair_frag_k<DK>(sK + (16 * ta + l16) * LDT, 32 * kb, g), gtf[kb], acc);
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[i] *= __expf(gn - fg[16 * ta + 4 * g + i]);
       if (ta < 2) acc = MM::mma8(lds_col_frag(sM, LDD, 16 * ta + l16, 0, g, l16), of[0], acc);
@@ -570,11 +620,7 @@ __global__ __launch_bounds__(512) void bwd_local_kernel(BwdArgs a) {
   auto dg_rows = [&](int ta, f32x4 r) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float x = r[i];
-      x += __shfl_xor(x, 1);
-      x += __shfl_xor(x, 2);
-      x += __shfl_xor(x, 4);
-      x += __shfl_xor(x, 8);
+      const float x = row_sum16(r[i]);
       if (l16 == 0) atomicAdd(&fdg[16 * ta + 4 * g + i], x);
     }
   };
@@ -623,18 +669,16 @@ __global__ __launch_bounds__(512) void bwd_local_kernel(BwdArgs a) {
   const auto sq_ = make_rsrc(a.dq + rr * DK, rng_k);
   const auto sk_ = make_rsrc(a.dk + rr * DK, rng_k);
   const auto sb_ = make_rsrc(a.b_kind == kChannel ? a.db + rr * DK : a.dq, a.b_kind == kChannel ? rng_k : 0u);
-  float sdot = 0.f;  // <S_0, dS_n> over this wave's channel tiles
-  for (int tl = wave; tl < NTD; tl += NW) {
+  float sdot = 0.f;   // <S_0, dS_n> over this wave's channel tiles
+  float ksall = 0.f;  // sum of e^{g_n - g_s} k_s . dK_n[s] over this wave's tiles
+  if (wave < NTD) {
+    const int tl = wave;
     const int ch = 16 * tl + l16;
-    F8 s0f[NKVM], gnf[NKVM];  // rows ch of S_0 and dS_n, k = value columns
-    // (compile-time indices with a uniform guard: a register array indexed at run time becomes a
-    // chain of selects)
+    // (s0f, gnf: rows ch of S_0 and dS_n, k = value columns; compile-time indices with a uniform
+    // guard, as a register array indexed at run time becomes a chain of selects)
 #pragma unroll
     for (int kv = 0; kv < NKVM; ++kv) {
       if (kv >= NKV) break;
-      const bool hiok = 32 * kv + 16 < DV;
-      s0f[kv] = tiled_row_frag(SR, static_cast<int>(DV), ch, 32 * kv, g, hiok);
-      gnf[kv] = tiled_row_frag(GR, static_cast<int>(DV), ch, 32 * kv, g, hiok);
 #pragma unroll
       for (int e = 0; e < 8; ++e) sdot += static_cast<float>(s0f[kv][e]) * static_cast<float>(gnf[kv][e]);
     }
@@ -669,14 +713,7 @@ __global__ __launch_bounds__(512) void bwd_local_kernel(BwdArgs a) {
         ksum += kv_ * ak[i];
       }
       dg_rows(ta, e);
-      // the end-of-chunk factor e^{g_n}: sum over every k_s . dK_n[s]
-      ksum += __shfl_xor(ksum, 1);
-      ksum += __shfl_xor(ksum, 2);
-      ksum += __shfl_xor(ksum, 4);
-      ksum += __shfl_xor(ksum, 8);
-      ksum += __shfl_xor(ksum, 16);
-      ksum += __shfl_xor(ksum, 32);
-      if (lane == 0) atomicAdd(&fdg[C - 1], ksum);
+      ksall += ksum;  // the end-of-chunk factor e^{g_n}: every k_s . dK_n[s], summed below
       // intra-chunk terms (dM . Gamma and dL . Gamma are lower triangular)
       const __bf16* dmr = sM + (16 * ta + l16) * LDD;
       const __bf16* dlr = tT + (16 * ta + l16) * LDD;
@@ -723,14 +760,15 @@ __global__ __launch_bounds__(512) void bwd_local_kernel(BwdArgs a) {
       }
     }
   }
-  // gamma_n <S_0, dS_n>
+  // gamma_n <S_0, dS_n> and the k . dK_n terms, both at the last token
+  sdot = __expf(gn) * sdot + ksall;
   sdot += __shfl_xor(sdot, 1);
   sdot += __shfl_xor(sdot, 2);
   sdot += __shfl_xor(sdot, 4);
   sdot += __shfl_xor(sdot, 8);
   sdot += __shfl_xor(sdot, 16);
   sdot += __shfl_xor(sdot, 32);
-  if (lane == 0) atomicAdd(&fdg[C - 1], __expf(gn) * sdot);
+  if (lane == 0) atomicAdd(&fdg[C - 1], sdot);
   // ---- dv = w . dV and dw = v . dV ----
   const auto sv_ = make_rsrc(a.dv + rr * DV, rng_v);
   const auto swc = make_rsrc(a.w_kind == kChannel ? a.dw + rr * DV : a.dv, a.w_kind == kChannel ? rng_v : 0u);
