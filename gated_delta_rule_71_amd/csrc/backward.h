@@ -25,9 +25,10 @@
 // Kernels (one call):
 //   1. the per-channel chunk-local kernel (the decay broadcast over channels) forms each chunk's
 //      affine map S_n = Ahat S_0 + D, O = Q' S_0 + Z' with Ahat = Diag(e^{G_n}) + A';
-//   2. bwd_chain_kernel<DK, false>: S_c = Ahat S_{c-1} + D chunk by chunk, storing S_{c-1};
-//   3. bwd_chain_kernel<DK, true>:  dS_{c-1} = Ahat^T dS_c + Q'^T dO_c in reverse, storing dS_c;
-//   4. bwd_local_kernel<DK>: every chunk at once, the adjoint above from S_{c-1} and dS_c.
+//   2. bwd_db_kernel<DK>: Q'^T dO_c for every chunk at once;
+//   3. bwd_chain_kernel<DK, false, NS>: S_c = Ahat S_{c-1} + D chunk by chunk, storing S_{c-1};
+//   4. bwd_chain_kernel<DK, true, NS>:  dS_{c-1} = Ahat^T dS_c + Q'^T dO_c in reverse, storing dS_c;
+//   5. bwd_local_kernel<DK>: every chunk at once, the adjoint above from S_{c-1} and dS_c.
 // The checkpoints are bf16, in two tiled layouts each: rows (S[dk][dv]) for products that
 // contract over the value columns, and transposed (S^T[dv][dk]) for those over the channels.
 #pragma once
@@ -58,6 +59,7 @@ struct BwdArgs {
   const __bf16* Qd;  // [cix][64][dk]   Q'
   const __bf16* Ad;  // [cix][dk][dk]   A'
   const __bf16* Dt;  // [cix][dv][dk]   D^T
+  __bf16* Dbt;       // [cix][dv][dk]   (Q'^T dO)^T, for the reverse chain
   const float* Egn;  // [cix][dk + 4]   e^{G_n}
   __bf16* SR;        // [cix][dk][dv]   S_{c-1}
   __bf16* ST;        // [cix][dv][dk]   S_{c-1}^T
@@ -134,36 +136,114 @@ __device__ __forceinline__ float row_sum16(float x) {
 
 // ------------------------------------------------------------------ chains over the chunks
 
-// One workgroup per (state, 16 value columns); DK / 32 waves, wave w holding S's channel tiles
-// 2 w and 2 w + 1 of the slice (the k-step w of the products).  Per chunk: the bf16 state goes to
-// LDS for the other waves (two exchange slots, so one barrier a chunk) and to the checkpoints;
-// the chunk's A' (and, in reverse, Q' and the dO slice) were staged in LDS during the previous
-// chunk; each wave forms its tiles of
-//   forward: S <- e^{G_n} . S + A' S + D
-//   reverse: S <- e^{G_n} . S + A'^T S + Q'^T dO
-// and stages the next chunk's operands from registers loaded before the products.
-template <int DK, bool REV>
-__global__ __launch_bounds__(2 * DK) void bwd_chain_kernel(BwdArgs a) {
+// Q'^T dO of every chunk, for the reverse chain (chunk-parallel): D_b^T [dv][dk] tiled like D^T.
+// One workgroup of four waves per chunk; Q' and the dO rows staged in LDS, lane output
+// D_b[16 tl + 4 g + i][16 cv + l16], i.e. four consecutive channels of row 16 cv + l16 of D_b^T.
+template <int DK>
+__global__ __launch_bounds__(256) void bwd_db_kernel(BwdArgs a) {
   using MM = Mma<__bf16>;
   using F8 = MM::F8;
-  constexpr int C = 64, NKB = DK / 32, NTD = DK / 16, NT = 64 * NKB;
-  constexpr int AB = DK * DK * 2, QB = C * DK * 2, OB = C * 16 * 2;
-  constexpr int BUF = AB + (REV ? QB + OB : 0);
-  constexpr int NA16 = AB / 16 / NT, NQ16 = QB / 16 / NT, NO16 = (128 + NT - 1) / NT;
-  static_assert(AB % (16 * NT) == 0 && QB % (16 * NT) == 0, "whole pieces per thread");
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * BUF + 2 * NKB * 1024];
+  constexpr int C = 64, NTD = DK / 16, LDO = 128 + 8;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[C * DK * 2 + C * LDO * 2];
+  __bf16* sQ = reinterpret_cast<__bf16*>(smem);
+  __bf16* sO = reinterpret_cast<__bf16*>(smem + C * DK * 2);
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t nch = a.nch, DV = a.DV, H = a.H;
+  const int64_t cix = blockIdx.x, bh = cix / nch, c = cix % nch;
+  const int64_t bi = bh / H, hi = bh % H, t0 = c * C;
+  const int NCV = static_cast<int>(DV / 16);
+  const uint4* Q = reinterpret_cast<const uint4*>(a.Qd + cix * C * DK);
+  for (int i = tid; i < C * DK / 8; i += 256) reinterpret_cast<uint4*>(sQ)[i] = Q[i];
+  const auto rd = make_rsrc(a.dO + ((bi * a.T + t0) * H + hi) * DV, wy_range(a.T - t0, H, DV));
+  const uint32_t hdv = static_cast<uint32_t>(H * DV * 2);
+  for (int item = tid; item < C * (DV / 8); item += 256) {
+    const int t = item / static_cast<int>(DV / 8), x0 = (item % static_cast<int>(DV / 8)) * 8;
+    *reinterpret_cast<uint4*>(sO + t * LDO + x0) = buf_load16(rd, t * hdv + x0 * 2);
+  }
+  lds_barrier();
+  __bf16* Db = a.Dbt + cix * DV * DK;
+  for (int job = wave; job < NTD * NCV; job += 4) {
+    const int tl = job % NTD, cv = job / NTD;
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+      acc = MM::mma8(tiled_col_frag(sQ, DK, 16 * tl + l16, 32 * ks, g, l16),
+                     lds_col_frag(sO, LDO, 16 * cv + l16, 32 * ks, g, l16), acc);
+    bf16x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = static_cast<__bf16>(acc[i]);
+    *reinterpret_cast<bf16x4*>(Db + tiled16(16 * cv + l16, 16 * tl + 4 * g, DK)) = o;
+  }
+}
+
+// The chains: per chunk c, in order (forward) or in reverse,
+//   forward: S <- e^{G_n} . S + A' S + D,      storing S_{c-1}
+//   reverse: S <- e^{G_n} . S + A'^T S + D_b,  storing dS_c   (D_b = Q'^T dO, above)
+// One workgroup per (state, NS x 16 value columns): NS x DK / 32 state waves, state wave sw holding
+// channel tiles 2 (sw % NKB) and 2 (sw % NKB) + 1 of slice sw / NKB in its accumulators, plus two
+// helper waves:
+//   wave 0 copies each chunk's A', the slices' D rows and e^{G_n} into LDS with direct-to-LDS
+//     loads, two chunks ahead (three buffers), and before each barrier waits for the next chunk's;
+//   wave 1 copies the checkpoints (the bf16 state the state waves leave in an exchange slot each
+//     chunk) to HBM, in both tiled layouts.
+// The state waves issue no global memory operation inside the loop; one barrier per chunk (the
+// exchange has two slots: a slot is rewritten two chunks later, after every wave has passed the
+// barrier in between).
+template <int DK, int NS>
+struct ChainLayout {
+  static constexpr int AB = DK * DK * 2;           // A' (tiled, as in HBM)
+  static constexpr int DB = NS * 16 * DK * 2;      // D^T rows of the slices (tiled rows, contiguous)
+  static constexpr int EB = ((DK + 4) * 4 + 15) / 16 * 16;  // e^{G_n}: (DK + 4) / 4 pieces of 16 bytes
+  static constexpr int BUF = (AB + DB + EB + 255) / 256 * 256;
+  static constexpr int NSW = NS * DK / 32;         // state waves
+  static constexpr int oX = 3 * BUF;               // exchange: [2][NSW][1 KB]
+  static constexpr int total = oX + 2 * NSW * 1024;
+  static constexpr bool fits = total <= kLdsLimit;
+  static constexpr int NDMA = AB / 1024 + DB / 1024 + 1;  // direct-to-LDS loads per chunk
+};
+
+template <int DK, bool REV, int NS>
+__global__ __launch_bounds__(64 * (2 + NS * DK / 32)) void bwd_chain_kernel(BwdArgs a) {
+  using L = ChainLayout<DK, NS>;
+  using MM = Mma<__bf16>;
+  using F8 = MM::F8;
+  static_assert(L::fits, "LDS layout exceeds the gfx950 workgroup limit");
+  static_assert(L::NDMA <= 60, "one chunk's loads must fit the vmcnt range");
+  constexpr int NKB = DK / 32, NSW = L::NSW;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[L::total];
 
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t DV = a.DV, H = a.H, nch = a.nch;
-  const int64_t nsl = DV / 16;
-  const int64_t bh = blockIdx.x / nsl;
-  const int sl = static_cast<int>(blockIdx.x % nsl);
-  const int64_t bi = bh / H, hi = bh % H;
-  const int col = 16 * sl + l16;  // this lane's value column
+  const int64_t nwg = DV / (16 * NS);  // workgroups per state
+  const int64_t bh = blockIdx.x / nwg;
+  const int sl0 = static_cast<int>(blockIdx.x % nwg) * NS;
+  const bool state = wave >= 2;
+  const int sw = state ? wave - 2 : 0;
+  const int sls = sl0 + sw / NKB, w = sw % NKB;  // this state wave's slice and k-step
+  const int col = 16 * sls + l16;
+  auto chunk_of = [&](int64_t it) { return REV ? nch - 1 - it : it; };
+  auto buf = [&](int64_t it) { return smem + (it % 3) * L::BUF; };
+  auto slot = [&](int64_t it) { return smem + L::oX + (it & 1) * NSW * 1024; };
 
+  // ---- wave 0: a chunk's operands into buffer it % 3 ----
+  const __bf16* Dsrc = REV ? a.Dbt : a.Dt;
+  auto dma = [&](int64_t it) {
+    const int64_t cix = bh * nch + chunk_of(it);
+    unsigned char* B = buf(it);
+    const auto rA = make_rsrc(a.Ad + cix * DK * DK, L::AB);
+#pragma unroll
+    for (int i = 0; i < L::AB / 1024; ++i) lds_dma16(rA, B + 1024 * i, 1024 * i + lane * 16);
+    const auto rD = make_rsrc(Dsrc + cix * DV * DK + static_cast<int64_t>(sl0) * 16 * DK, L::DB);
+#pragma unroll
+    for (int i = 0; i < L::DB / 1024; ++i) lds_dma16(rD, B + L::AB + 1024 * i, 1024 * i + lane * 16);
+    if (lane < (DK + 4) / 4) lds_dma16(make_rsrc(a.Egn + cix * (DK + 4), (DK + 4) * 4), B + L::AB + L::DB, lane * 16);
+  };
+
+  // ---- state waves: S (two channel tiles of one slice) ----
   f32x4 S[2];
-  {
+  if (state) {
     const float* init = REV ? a.dST : a.S0;
 #pragma unroll
     for (int u = 0; u < 2; ++u)
@@ -172,126 +252,92 @@ __global__ __launch_bounds__(2 * DK) void bwd_chain_kernel(BwdArgs a) {
         S[u][i] = init ? init[(bh * DK + 16 * (2 * w + u) + 4 * g + i) * DV + col] : 0.f;
   }
 
-  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));  // (a vector type stays in registers)
-  u32x4 ra[NA16], rq[REV ? NQ16 : 1], ro[NO16];
-  // (always inlined: the arrays stay in registers)
-  auto fetch = [&](int64_t c) __attribute__((always_inline)) {
-    const int64_t cix = bh * nch + c;
-    const u32x4* A = reinterpret_cast<const u32x4*>(a.Ad + cix * DK * DK);
-#pragma unroll
-    for (int j = 0; j < NA16; ++j) ra[j] = A[tid + NT * j];
-    if constexpr (REV) {
-      const u32x4* Q = reinterpret_cast<const u32x4*>(a.Qd + cix * C * DK);
-#pragma unroll
-      for (int j = 0; j < NQ16; ++j) rq[j] = Q[tid + NT * j];
-      const int64_t t0 = c * C;
-      const auto rd = make_rsrc(a.dO + ((bi * a.T + t0) * H + hi) * DV + 16 * sl, wy_range(a.T - t0, H, DV));
-      const uint32_t hdv = static_cast<uint32_t>(H * DV * 2);
-#pragma unroll
-      for (int j = 0; j < NO16; ++j) {
-        const int p = tid + NT * j;  // piece: token p / 2, half p % 2
-        ro[j] = __builtin_bit_cast(u32x4, buf_load16(rd, p < 128 ? (p >> 1) * hdv + (p & 1) * 16 : 0x80000000u));
-      }
-    }
-  };
-  auto stage = [&](int b) __attribute__((always_inline)) {
-    unsigned char* B = smem + b * BUF;
-#pragma unroll
-    for (int j = 0; j < NA16; ++j) *reinterpret_cast<u32x4*>(B + (tid + NT * j) * 16) = ra[j];
-    if constexpr (REV) {
-#pragma unroll
-      for (int j = 0; j < NQ16; ++j) *reinterpret_cast<u32x4*>(B + AB + (tid + NT * j) * 16) = rq[j];
-#pragma unroll
-      for (int j = 0; j < NO16; ++j) {
-        const int p = tid + NT * j;
-        if (p < 128) *reinterpret_cast<u32x4*>(B + AB + QB + p * 16) = ro[j];
-      }
-    }
-  };
-
-  // e^{G_n} and D of a chunk, loaded one chunk ahead
-  float4 e4n[2];
-  bf16x4 d4n[2];
-  auto fetch_ed = [&](int64_t c) __attribute__((always_inline)) {
-    const int64_t cix = bh * nch + c;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int tl = 2 * w + u;
-      e4n[u] = *reinterpret_cast<const float4*>(a.Egn + cix * (DK + 4) + 16 * tl + 4 * g);
-      if (!REV) d4n[u] = *reinterpret_cast<const bf16x4*>(a.Dt + cix * DV * DK + tiled16(col, 16 * tl + 4 * g, DK));
-    }
-  };
-  if (nch > 0) {
-    fetch(REV ? nch - 1 : 0);
-    fetch_ed(REV ? nch - 1 : 0);
-    stage(0);
+  if (wave == 0 && nch > 0) {
+    dma(0);
+    if (nch > 1) dma(1);
   }
   for (int64_t it = 0; it < nch; ++it) {
-    const int64_t c = REV ? nch - 1 - it : it;
-    const int64_t cix = bh * nch + c;
-    const int bs = static_cast<int>(it & 1);
-    // this wave's bf16 tiles to the exchange slot and the checkpoints
-    *reinterpret_cast<F8*>(smem + 2 * BUF + (bs * NKB + w) * 1024 + lane * 16) = acc_pair_frag<__bf16>(S[0], S[1]);
-    __bf16* ckR = (REV ? a.GR : a.SR) + cix * DK * DV;
-    __bf16* ckT = (REV ? a.GT : a.ST) + cix * DV * DK;
-    float4 e4[2] = {e4n[0], e4n[1]};
-    bf16x4 d4[2] = {d4n[0], d4n[1]};
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int tl = 2 * w + u;
-      bf16x4 s4;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) s4[i] = static_cast<__bf16>(S[u][i]);
-      *reinterpret_cast<bf16x4*>(ckT + tiled16(col, 16 * tl + 4 * g, DK)) = s4;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) ckR[tiled16(16 * tl + 4 * g + i, col, DV)] = s4[i];
+    if (state) {
+      // the state entering this step, bf16, for the other waves and the checkpoint copier
+      *reinterpret_cast<F8*>(slot(it) + sw * 1024 + lane * 16) = acc_pair_frag<__bf16>(S[0], S[1]);
+    } else if (wave == 0) {
+      // this chunk's loads in; the next chunk's (issued after them) may still be in flight
+      if (it + 1 < nch)
+        __builtin_amdgcn_s_waitcnt(wait_vmcnt(L::NDMA));
+      else
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     }
-    if (it + 1 < nch) {
-      fetch(REV ? c - 1 : c + 1);
-      fetch_ed(REV ? c - 1 : c + 1);
-    }
-    lds_barrier();  // the exchange slot and the staged operands of chunk c are in
-
-    const unsigned char* B = smem + bs * BUF;
-    const __bf16* sA = reinterpret_cast<const __bf16*>(B);
-    F8 sf[NKB];
+    lds_barrier_keep_vm();
+    if (state) {
+      const unsigned char* B = buf(it);
+      const __bf16* sA = reinterpret_cast<const __bf16*>(B);
+      const __bf16* sD = reinterpret_cast<const __bf16*>(B + L::AB);
+      const float* sE = reinterpret_cast<const float*>(B + L::AB + L::DB);
+      F8 sf[NKB];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) sf[kb] = *reinterpret_cast<const F8*>(smem + 2 * BUF + (bs * NKB + kb) * 1024 + lane * 16);
-    f32x4 acc[2];
+      for (int kb = 0; kb < NKB; ++kb)
+        sf[kb] = *reinterpret_cast<const F8*>(slot(it) + ((sw / NKB) * NKB + kb) * 1024 + lane * 16);
+      f32x4 acc[2];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      acc[u][0] = S[u][0] * e4[u].x + (REV ? 0.f : static_cast<float>(d4[u][0]));
-      acc[u][1] = S[u][1] * e4[u].y + (REV ? 0.f : static_cast<float>(d4[u][1]));
-      acc[u][2] = S[u][2] * e4[u].z + (REV ? 0.f : static_cast<float>(d4[u][2]));
-      acc[u][3] = S[u][3] * e4[u].w + (REV ? 0.f : static_cast<float>(d4[u][3]));
-    }
+      for (int u = 0; u < 2; ++u) {
+        const int tl = 2 * w + u;
+        const float4 e4 = *reinterpret_cast<const float4*>(sE + 16 * tl + 4 * g);
+        // D^T row col of this slice: tile row (sw / NKB), tile tl
+        const bf16x4 d4 = *reinterpret_cast<const bf16x4*>(sD + ((sw / NKB) * (DK / 16) + tl) * 256 + l16 * 16 + 4 * g);
+        acc[u][0] = S[u][0] * e4.x + static_cast<float>(d4[0]);
+        acc[u][1] = S[u][1] * e4.y + static_cast<float>(d4[1]);
+        acc[u][2] = S[u][2] * e4.z + static_cast<float>(d4[2]);
+        acc[u][3] = S[u][3] * e4.w + static_cast<float>(d4[3]);
+      }
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int tl = 2 * w + u;
+      for (int u = 0; u < 2; ++u) {
+        const int tl = 2 * w + u;
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const F8 af = REV ? tiled_col_frag(sA, DK, 16 * tl + l16, 32 * kb, g, l16)
-                          : tiled_row_frag(sA, DK, 16 * tl + l16, 32 * kb, g);
-        acc[u] = MM::mma8(af, sf[kb], acc[u]);
+        for (int kb = 0; kb < NKB; ++kb) {
+          const F8 af = REV ? tiled_col_frag(sA, DK, 16 * tl + l16, 32 * kb, g, l16)
+                            : tiled_row_frag(sA, DK, 16 * tl + l16, 32 * kb, g);
+          acc[u] = MM::mma8(af, sf[kb], acc[u]);
+        }
+      }
+      S[0] = acc[0];
+      S[1] = acc[1];
+    } else if (wave == 0) {
+      // buffer (it + 2) % 3 was last read in step it - 1, before this step's barrier
+      if (it + 2 < nch) dma(it + 2);
+    } else {
+      // checkpoint of this chunk: every state wave's slot entry, both layouts
+      const int64_t cix = bh * nch + chunk_of(it);
+      __bf16* ckR = (REV ? a.GR : a.SR) + cix * DK * DV;
+      __bf16* ckT = (REV ? a.GT : a.ST) + cix * DV * DK;
+      // Slot v holds channels 32 (v % NKB) .. + 31 of the 16 columns of slice v / NKB, lane
+      // (g, l16) element e carrying channel 4 g + (e & 3) + 16 (e >> 2) of column l16.  Transposed
+      // layout: each lane's eight channels as two 8-byte pieces.  Row layout: lane (r, h) gathers
+      // channel r's columns 8 h .. 8 h + 7 from eight lanes' slots and writes them as one
+      // 16-byte piece (three stores per slot, below the limit of a wave's outstanding stores).
+      const int r = lane >> 1, hh = lane & 1;
+      const int gr = (r & 15) >> 2, er = (r & 3) + ((r >> 4) << 2);
+#pragma unroll 2
+      for (int v = 0; v < NSW; ++v) {
+        const unsigned char* X = slot(it) + v * 1024;
+        const F8 f = *reinterpret_cast<const F8*>(X + lane * 16);
+        const int c_ = 16 * (sl0 + v / NKB) + l16, k0 = 32 * (v % NKB) + 4 * g;
+        bf16x4 lo, hi;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          lo[e] = f[e];
+          hi[e] = f[4 + e];
+        }
+        *reinterpret_cast<bf16x4*>(ckT + tiled16(c_, k0, DK)) = lo;
+        *reinterpret_cast<bf16x4*>(ckT + tiled16(c_, k0 + 16, DK)) = hi;
+        bf16x8 row;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          row[j] = *reinterpret_cast<const __bf16*>(X + (16 * gr + 8 * hh + j) * 16 + 2 * er);
+        *reinterpret_cast<bf16x8*>(ckR + tiled16(32 * (v % NKB) + r, 16 * (sl0 + v / NKB) + 8 * hh, DV)) = row;
       }
     }
-    if constexpr (REV) {
-      const __bf16* sQ = reinterpret_cast<const __bf16*>(B + AB);
-      const __bf16* sO = reinterpret_cast<const __bf16*>(B + AB + QB);
-      F8 of[2];
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) of[ks] = lds_col_frag(sO, 16, l16, 32 * ks, g, l16);
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-          acc[u] = MM::mma8(tiled_col_frag(sQ, DK, 16 * (2 * w + u) + l16, 32 * ks, g, l16), of[ks], acc[u]);
-    }
-    S[0] = acc[0];
-    S[1] = acc[1];
-    if (it + 1 < nch) stage(bs ^ 1);
   }
-  if (REV && a.dS0 != nullptr) {
+  if (REV && state && a.dS0 != nullptr) {
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll

@@ -8,7 +8,7 @@ size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 struct BwdSizes {
   size_t Qd, Ad, Dt, Zd, Egn, flag, ck;
-  size_t total() const { return Qd + Ad + Dt + Zd + Egn + flag + 4 * ck; }
+  size_t total() const { return Qd + Ad + Dt + Zd + Egn + flag + 5 * ck; }
 };
 
 BwdSizes bwd_sizes(int64_t nstate, int64_t T, int64_t DK, int64_t DV) {
@@ -24,13 +24,25 @@ BwdSizes bwd_sizes(int64_t nstate, int64_t T, int64_t DK, int64_t DV) {
   return s;
 }
 
+// the chains over 32 value columns a workgroup where d_v allows (the chunk's A' then serves two
+// slices), else 16
+template <int DK, bool REV>
+void launch_chain(const BwdArgs& a, int64_t nstate, hipStream_t s) {
+  if (a.DV % 32 == 0)
+    hipLaunchKernelGGL((bwd_chain_kernel<DK, REV, 2>), dim3((unsigned)(nstate * (a.DV / 32))),
+                       dim3(64 * (2 + 2 * DK / 32)), 0, s, a);
+  else
+    hipLaunchKernelGGL((bwd_chain_kernel<DK, REV, 1>), dim3((unsigned)(nstate * (a.DV / 16))),
+                       dim3(64 * (2 + DK / 32)), 0, s, a);
+}
+
 template <int DK>
 hipError_t launch_dk(WycArgs f, BwdArgs a, int64_t nstate, hipStream_t s) {
   const int64_t nblk = nstate * a.nch;
   hipLaunchKernelGGL((wyc_prep_kernel<DK, 128, 1>), dim3((unsigned)nblk), dim3(512), 0, s, f);
-  const unsigned nsl = static_cast<unsigned>(nstate * (a.DV / 16));
-  hipLaunchKernelGGL((bwd_chain_kernel<DK, false>), dim3(nsl), dim3(2 * DK), 0, s, a);
-  hipLaunchKernelGGL((bwd_chain_kernel<DK, true>), dim3(nsl), dim3(2 * DK), 0, s, a);
+  hipLaunchKernelGGL((bwd_db_kernel<DK>), dim3((unsigned)nblk), dim3(256), 0, s, a);
+  launch_chain<DK, false>(a, nstate, s);
+  launch_chain<DK, true>(a, nstate, s);
   hipLaunchKernelGGL((bwd_local_kernel<DK>), dim3((unsigned)nblk), dim3(512), 0, s, a);
   return hipGetLastError();
 }
@@ -108,6 +120,7 @@ hipError_t launch_backward(const bf16_t* q, const bf16_t* k, const bf16_t* v, co
   a.ST = reinterpret_cast<__bf16*>(ws + z.ck);
   a.GR = reinterpret_cast<__bf16*>(ws + 2 * z.ck);
   a.GT = reinterpret_cast<__bf16*>(ws + 3 * z.ck);
+  a.Dbt = reinterpret_cast<__bf16*>(ws + 4 * z.ck);
   a.T = T;
   a.H = H;
   a.DV = DV;

@@ -166,9 +166,9 @@ int gdr_decode_step(const gdr_problem* p, const void* q, const void* k, const vo
 /* Workspace bytes gdr_chunk_bwd needs for `p`; 0 for an invalid or unsupported
  * problem.  Per 64-token chunk of every (batch, head): the chunk's affine map as
  * for the per-channel forward (2 dk^2 + 2 dk dv + 132 dk + 128 dv + 20 bytes)
- * and four bf16 dk x dv checkpoints (the state entering the chunk and the
- * gradient of the state leaving it, each as rows and transposed), each array
- * 256-byte aligned. */
+ * and five bf16 dk x dv arrays: the checkpoints (the state entering the chunk
+ * and the gradient of the state leaving it, each as rows and transposed) and
+ * the chunk's Q'^T dO, each array 256-byte aligned. */
 size_t gdr_chunk_bwd_workspace_bytes(const gdr_problem* p);
 
 /*

@@ -192,12 +192,12 @@ def bwd_call(p, ws=0, ws_bytes=0, **over):
 
 def test_backward_workspace_and_validation():
     sp = prob(alpha_kind=N.GATE_SCALAR, b_kind=N.GATE_SCALAR, w_kind=N.GATE_SCALAR)
-    # the per-channel forward's chunk map and four bf16 dk x dv checkpoints per 64-token chunk of
+    # the per-channel forward's chunk map, four bf16 dk x dv checkpoints and Q'^T dO per 64-token chunk of
     # every (batch, head), each array rounded up to 256 bytes
     r = lambda n: (n + 255) // 256 * 256
     ch = 2 * 3 * 2
     need = r(ch * 128 * 128 * 2) + r(ch * 64 * 128 * 2) + r(ch * 128 * 128 * 2) + \
-        r(ch * 64 * 128 * 2) + r(ch * 132 * 4) + r(ch * 4) + 4 * r(ch * 128 * 128 * 2)
+        r(ch * 64 * 128 * 2) + r(ch * 132 * 4) + r(ch * 4) + 5 * r(ch * 128 * 128 * 2)
     assert N.bwd_workspace_bytes(sp) == need
     # outside the backward's scope: per-channel decay, fp32, dv > 128, grouped q / k heads
     for p in (prob(), prob(alpha_kind=N.GATE_SCALAR, io_dtype=N.GDR_FP32),
