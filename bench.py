@@ -68,19 +68,19 @@ def backward_bytes(wl):
     gradient written once, S0 read (if any) and dS0 written (dS_T is not passed here)."""
     es = 2
     rows = wl.B * wl.T * wl.H
+    qk_rows = wl.B * wl.T * (wl.HK or wl.H)
     gate = {"none": 0, "scalar": 1, "channel": wl.DK}
     wgate = {"none": 0, "scalar": 1, "channel": wl.DV}
-    per_row = 2 * wl.DK + wl.DV + gate[wl.alpha] + gate[wl.b] + wgate[wl.w]
+    per_row = wl.DV + gate[wl.alpha] + gate[wl.b] + wgate[wl.w]
     if wl.shared_beta and wl.b != "none":
         per_row -= gate[wl.b]  # one buffer passed as both b and w
-    n = rows * (2 * per_row + wl.DV) * es  # inputs and their gradients; do
+    n = (rows * (2 * per_row + wl.DV) + qk_rows * 4 * wl.DK) * es  # inputs, their gradients; do
     state = wl.B * wl.H * wl.DK * wl.DV * 4
     return n + state * (2 if wl.s0_std > 0 else 1)
 
 
 def backward_supported(wl):
-    return (wl.dtype == "bf16" and wl.alpha != "channel" and wl.DV <= 128 and wl.DK in (32, 64, 128)
-            and (wl.HK in (0, wl.H)))
+    return wl.dtype == "bf16" and wl.alpha != "channel" and wl.DV <= 128 and wl.DK in (32, 64, 128)
 
 
 def decode_bytes(wl):
@@ -216,7 +216,8 @@ def time_backward(wl, steps, warmup, dev):
     prob = gdr.make_problem(wl.B, wl.H, wl.T, wl.DK, wl.DV, gdr._native.GDR_BF16,
                             gdr._native.GATE_SCALAR if wl.alpha == "scalar" else gdr._native.GATE_NONE,
                             {"none": 0, "scalar": 1, "channel": 2}[wl.b],
-                            {"none": 0, "scalar": 1, "channel": 2}[wl.w], 0)
+                            {"none": 0, "scalar": 1, "channel": 2}[wl.w], 0,
+                            qk_heads=0 if wl.HK in (0, wl.H) else wl.HK)
     need = gdr._native.bwd_workspace_bytes(prob)
     ws = torch.empty((need,), dtype=torch.uint8, device=dev)
     run = lambda: gdr.chunk_bwd(g["q"], g["k"], g["v"], g["log_alpha"], g["b"], g["w"], g["S0"], do,

@@ -67,6 +67,8 @@ struct BwdArgs {
   __bf16* GT;        // [cix][dv][dk]   dS_c^T
   int64_t T, H, DV, nch;
   int alpha_kind, b_kind, w_kind;
+  int64_t Hk;  // q / k heads: value head h reads q / k head h / (H / Hk); with Hk < H, dq and dk
+               // are written per value head (into the workspace) and summed over each group after
 };
 
 // Transposing fragment of a tiled16 LDS matrix: lane (g, l16) gets element [k0 + 4 g + e] and
@@ -415,8 +417,10 @@ __global__ __launch_bounds__(512) void bwd_local_kernel(BwdArgs a) {
   const uint32_t oob = 0x80000000u;
   const uint32_t hdk = static_cast<uint32_t>(H * DK * 2), hdv = static_cast<uint32_t>(H * DV * 2), h1 = static_cast<uint32_t>(H * 2);
   const uint32_t rng_k = wy_range(left, H, DK), rng_v = wy_range(left, H, DV), rng_1 = wy_range(left, H, 1);
-  const auto rq = make_rsrc(a.q + rr * DK, rng_k);
-  const auto rk = make_rsrc(a.k + rr * DK, rng_k);
+  const uint32_t hqk = static_cast<uint32_t>(a.Hk * DK * 2);  // token stride of q and k
+  const int64_t rqk = (bi * a.T + t0) * a.Hk + hi / (H / a.Hk);
+  const auto rq = make_rsrc(a.q + rqk * DK, wy_range(left, a.Hk, DK));
+  const auto rk = make_rsrc(a.k + rqk * DK, wy_range(left, a.Hk, DK));
   const auto rbc = make_rsrc(a.b_kind == kChannel ? a.bg + rr * DK : a.q, a.b_kind == kChannel ? rng_k : 0u);
   const auto rbs = make_rsrc(a.b_kind == kScalar ? a.bg + rr : a.q, a.b_kind == kScalar ? rng_1 : 0u);
   const auto rv = make_rsrc(a.v + rr * DV, rng_v);
@@ -454,9 +458,9 @@ __global__ __launch_bounds__(512) void bwd_local_kernel(BwdArgs a) {
     const int item = tid + NT * j;
     const bool in = item < C * (DK / 8);
     const int t = in ? item / (DK / 8) : 0, d0 = in ? (item % (DK / 8)) * 8 : 0;
-    const uint32_t off = in ? t * hdk + d0 * 2 : oob;
-    uq[j] = buf_load16(rq, off);
-    uk[j] = buf_load16(rk, off);
+    const uint32_t off = in ? t * hdk + d0 * 2 : oob, offk = in ? t * hqk + d0 * 2 : oob;
+    uq[j] = buf_load16(rq, offk);
+    uk[j] = buf_load16(rk, offk);
     ub[j] = buf_load16(rbc, off);
     ubs[j] = buf_load_u16(rbs, in ? t * h1 : oob);
   }
@@ -861,6 +865,27 @@ __global__ __launch_bounds__(512) void bwd_local_kernel(BwdArgs a) {
     if (a.b_kind == kScalar) buf_store1((bf16_t*)nullptr, make_rsrc(a.db + rr, rng_1), off, fdw[C + lane]);
     if (a.w_kind == kScalar) buf_store1((bf16_t*)nullptr, make_rsrc(a.dw + rr, rng_1), off, fdw[lane]);
   }
+}
+
+// dq and dk of grouped heads: the per-value-head gradients (in the workspace) summed over the
+// H / Hk value heads that share each q / k head.  One thread per 8 channels of a q / k row.
+__global__ __launch_bounds__(256) void bwd_group_sum_kernel(const bf16_t* src, bf16_t* dst, int64_t rows,
+                                                            int64_t G, int64_t DK) {
+  const int64_t n8 = DK / 8;
+  const int64_t item = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (item >= rows * n8) return;
+  const int64_t r = item / n8, d0 = (item % n8) * 8;  // q / k row r = (b, t, hk)
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int64_t j = 0; j < G; ++j) {
+    float x[8];
+    load8f(src + (r * G + j) * DK + d0, x);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += x[e];
+  }
+  bf16x8 o;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = static_cast<__bf16>(acc[e]);
+  *reinterpret_cast<bf16x8*>(dst + r * DK + d0) = o;
 }
 
 }  // namespace gdr

@@ -7,11 +7,12 @@ namespace {
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 struct BwdSizes {
-  size_t Qd, Ad, Dt, Zd, Egn, flag, ck;
-  size_t total() const { return Qd + Ad + Dt + Zd + Egn + flag + 5 * ck; }
+  size_t Qd, Ad, Dt, Zd, Egn, flag, ck, grp;
+  size_t total() const { return Qd + Ad + Dt + Zd + Egn + flag + 5 * ck + 2 * grp; }
 };
 
-BwdSizes bwd_sizes(int64_t nstate, int64_t T, int64_t DK, int64_t DV) {
+// grouped: value-head rows B T H when q / k have fewer heads (dq and dk per value head), else 0
+BwdSizes bwd_sizes(int64_t nstate, int64_t T, int64_t DK, int64_t DV, int64_t grouped = 0) {
   const size_t ch = static_cast<size_t>(nstate) * static_cast<size_t>((T + 63) / 64);
   BwdSizes s;
   s.Qd = align256(ch * 64 * DK * 2);
@@ -21,6 +22,7 @@ BwdSizes bwd_sizes(int64_t nstate, int64_t T, int64_t DK, int64_t DV) {
   s.Egn = align256(ch * (DK + 4) * 4);
   s.flag = align256(ch * 4);
   s.ck = align256(ch * DK * DV * 2);
+  s.grp = align256(static_cast<size_t>(grouped) * DK * 2);
   return s;
 }
 
@@ -46,27 +48,35 @@ hipError_t launch_dk(WycArgs f, BwdArgs a, int64_t nstate, hipStream_t s) {
   hipLaunchKernelGGL((bwd_local_kernel<DK>), dim3((unsigned)nblk), dim3(512), 0, s, a);
   return hipGetLastError();
 }
+
+hipError_t group_sum(const bf16_t* src, bf16_t* dst, int64_t rows, int64_t G, int64_t DK, hipStream_t s) {
+  const int64_t items = rows * (DK / 8);
+  if (items > 0)
+    hipLaunchKernelGGL(bwd_group_sum_kernel, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, s, src, dst,
+                       rows, G, DK);
+  return hipGetLastError();
+}
 }  // namespace
 
-// bf16 I/O, a scalar decay or none, dk in {32, 64, 128}, dv a multiple of 16 up to 128, one
-// q / k head per value head.
-bool backward_supported(int io_dtype_bf16, int64_t DK, int64_t DV, int alpha_kind, bool shared_qk) {
-  return io_dtype_bf16 && shared_qk && (DK == 32 || DK == 64 || DK == 128) && DV % 16 == 0 && DV > 0 &&
-         DV <= 128 && alpha_kind != kChannel;
+// bf16 I/O, a scalar decay or none, dk in {32, 64, 128}, dv a multiple of 16 up to 128.
+bool backward_supported(int io_dtype_bf16, int64_t DK, int64_t DV, int alpha_kind) {
+  return io_dtype_bf16 && (DK == 32 || DK == 64 || DK == 128) && DV % 16 == 0 && DV > 0 && DV <= 128 &&
+         alpha_kind != kChannel;
 }
 
-size_t backward_workspace_bytes(int64_t nstate, int64_t T, int64_t DK, int64_t DV) {
-  return bwd_sizes(nstate, T, DK, DV).total();
+size_t backward_workspace_bytes(int64_t B, int64_t H, int64_t Hk, int64_t T, int64_t DK, int64_t DV) {
+  return bwd_sizes(B * H, T, DK, DV, Hk < H ? B * T * H : 0).total();
 }
 
 hipError_t launch_backward(const bf16_t* q, const bf16_t* k, const bf16_t* v, const bf16_t* la,
                            const bf16_t* bg, const bf16_t* wg, const float* S0, const bf16_t* dO,
                            const float* dST, bf16_t* dq, bf16_t* dk, bf16_t* dv, bf16_t* dla,
                            bf16_t* db, bf16_t* dw, float* dS0, int64_t B, int64_t T, int64_t H,
-                           int64_t DK, int64_t DV, int alpha_kind, int b_kind, int w_kind,
+                           int64_t Hk, int64_t DK, int64_t DV, int alpha_kind, int b_kind, int w_kind,
                            void* workspace, hipStream_t s) {
   const int64_t nstate = B * H;
-  const BwdSizes z = bwd_sizes(nstate, T, DK, DV);
+  const bool grouped = Hk < H;
+  const BwdSizes z = bwd_sizes(nstate, T, DK, DV, grouped ? B * T * H : 0);
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   WycArgs f{};
   f.q = q;
@@ -78,7 +88,7 @@ hipError_t launch_backward(const bf16_t* q, const bf16_t* k, const bf16_t* v, co
   f.T = T;
   f.H = H;
   f.DV = DV;
-  f.Hk = H;
+  f.Hk = Hk;
   f.nch = (T + 63) / 64;
   f.b_kind = b_kind;
   f.w_kind = w_kind;
@@ -121,6 +131,13 @@ hipError_t launch_backward(const bf16_t* q, const bf16_t* k, const bf16_t* v, co
   a.GR = reinterpret_cast<__bf16*>(ws + 2 * z.ck);
   a.GT = reinterpret_cast<__bf16*>(ws + 3 * z.ck);
   a.Dbt = reinterpret_cast<__bf16*>(ws + 4 * z.ck);
+  bf16_t* gq = reinterpret_cast<bf16_t*>(ws + 5 * z.ck);
+  bf16_t* gk = reinterpret_cast<bf16_t*>(ws + 5 * z.ck + z.grp);
+  a.Hk = Hk;
+  if (grouped) {  // per value head first
+    a.dq = gq;
+    a.dk = gk;
+  }
   a.T = T;
   a.H = H;
   a.DV = DV;
@@ -129,11 +146,16 @@ hipError_t launch_backward(const bf16_t* q, const bf16_t* k, const bf16_t* v, co
   a.b_kind = b_kind;
   a.w_kind = w_kind;
   if (nstate == 0 || T == 0) return hipSuccess;
+  hipError_t e;
   switch (DK) {
-    case 32: return launch_dk<32>(f, a, nstate, s);
-    case 64: return launch_dk<64>(f, a, nstate, s);
-    default: return launch_dk<128>(f, a, nstate, s);
+    case 32: e = launch_dk<32>(f, a, nstate, s); break;
+    case 64: e = launch_dk<64>(f, a, nstate, s); break;
+    default: e = launch_dk<128>(f, a, nstate, s); break;
   }
+  if (e != hipSuccess || !grouped) return e;
+  e = group_sum(gq, dq, B * T * Hk, H / Hk, DK, s);
+  if (e != hipSuccess) return e;
+  return group_sum(gk, dk, B * T * Hk, H / Hk, DK, s);
 }
 
 }  // namespace gdr

@@ -22,13 +22,13 @@ hipError_t launch_prefill(const IO* q, const IO* k, const IO* v, const IO* la, c
                           int b_kind, int w_kind, bool decay_first, void* workspace,
                           hipEvent_t mark, hipStream_t stream);
 bool prefill_supported(int io_dtype, int64_t DK, int64_t DV, int alpha_kind, bool decay_first);
-bool backward_supported(int io_dtype_bf16, int64_t DK, int64_t DV, int alpha_kind, bool shared_qk);
-size_t backward_workspace_bytes(int64_t nstate, int64_t T, int64_t DK, int64_t DV);
+bool backward_supported(int io_dtype_bf16, int64_t DK, int64_t DV, int alpha_kind);
+size_t backward_workspace_bytes(int64_t B, int64_t H, int64_t Hk, int64_t T, int64_t DK, int64_t DV);
 hipError_t launch_backward(const bf16_t* q, const bf16_t* k, const bf16_t* v, const bf16_t* la,
                            const bf16_t* bg, const bf16_t* wg, const float* S0, const bf16_t* dO,
                            const float* dST, bf16_t* dq, bf16_t* dk, bf16_t* dv, bf16_t* dla,
                            bf16_t* db, bf16_t* dw, float* dS0, int64_t B, int64_t T, int64_t H,
-                           int64_t DK, int64_t DV, int alpha_kind, int b_kind, int w_kind,
+                           int64_t Hk, int64_t DK, int64_t DV, int alpha_kind, int b_kind, int w_kind,
                            void* workspace, hipStream_t s);
 size_t prefill_workspace_bytes(int io_dtype, int64_t nstate, int64_t T, int64_t DK, int64_t DV,
                                int alpha_kind, int b_kind, bool decay_first);
@@ -234,14 +234,13 @@ GDR_EXPORT int gdr_decode_step(const gdr_problem* p, const void* q, const void* 
 
 namespace {
 bool bwd_supported(const gdr_problem* p) {
-  return gdr::backward_supported(p->io_dtype == GDR_BF16, p->dk, p->dv, p->alpha_kind,
-                                 qk_heads(p) == p->heads);
+  return gdr::backward_supported(p->io_dtype == GDR_BF16, p->dk, p->dv, p->alpha_kind);
 }
 }  // namespace
 
 GDR_EXPORT size_t gdr_chunk_bwd_workspace_bytes(const gdr_problem* p) {
   if (check_problem(p) != GDR_OK || !bwd_supported(p)) return 0;
-  return gdr::backward_workspace_bytes(p->batch * p->heads, p->seqlen, p->dk, p->dv);
+  return gdr::backward_workspace_bytes(p->batch, p->heads, qk_heads(p), p->seqlen, p->dk, p->dv);
 }
 
 GDR_EXPORT int gdr_chunk_bwd(const gdr_problem* p, const void* q, const void* k, const void* v,
@@ -257,6 +256,7 @@ GDR_EXPORT int gdr_chunk_bwd(const gdr_problem* p, const void* q, const void* k,
   if (!bwd_supported(p)) return GDR_ERR_UNSUPPORTED;
   const int64_t nstate = p->batch * p->heads;
   const int64_t rows = p->batch * p->seqlen * p->heads;
+  const int64_t qk_rows = p->batch * p->seqlen * qk_heads(p);
   if (nstate == 0) return GDR_OK;
   const int64_t sbytes = nstate * p->dk * p->dv * 4;
   if (rows > 0) {
@@ -274,13 +274,13 @@ GDR_EXPORT int gdr_chunk_bwd(const gdr_problem* p, const void* q, const void* k,
   auto gate_bytes = [&](int32_t kind, int64_t width) {
     return kind == GDR_GATE_SCALAR ? rows * 2 : kind == GDR_GATE_CHANNEL ? rows * width * 2 : 0;
   };
-  const Range outs[] = {range_of(dq, dq ? rows * p->dk * 2 : 0), range_of(dk, dk ? rows * p->dk * 2 : 0),
+  const Range outs[] = {range_of(dq, dq ? qk_rows * p->dk * 2 : 0), range_of(dk, dk ? qk_rows * p->dk * 2 : 0),
                         range_of(dv, rows * p->dv * 2),
                         range_of(dla_, gate_bytes(p->alpha_kind, p->dk)),
                         range_of(db_, gate_bytes(p->b_kind, p->dk)),
                         range_of(dw_, gate_bytes(p->w_kind, p->dv)),
                         range_of(dS0, dS0 ? sbytes : 0)};
-  const Range ins[] = {range_of(q, rows * p->dk * 2), range_of(k, rows * p->dk * 2),
+  const Range ins[] = {range_of(q, qk_rows * p->dk * 2), range_of(k, qk_rows * p->dk * 2),
                        range_of(v, rows * p->dv * 2),
                        range_of(gate_ptr(p->alpha_kind, log_alpha), gate_bytes(p->alpha_kind, p->dk)),
                        range_of(gate_ptr(p->b_kind, b), gate_bytes(p->b_kind, p->dk)),
@@ -300,7 +300,7 @@ GDR_EXPORT int gdr_chunk_bwd(const gdr_problem* p, const void* q, const void* k,
   const hipError_t e = gdr::launch_backward(
       (const T*)q, (const T*)k, (const T*)v, (const T*)gate_ptr(p->alpha_kind, log_alpha),
       (const T*)gate_ptr(p->b_kind, b), (const T*)gate_ptr(p->w_kind, w), S0, (const T*)dO, dS_T,
-      (T*)dq, (T*)dk, (T*)dv, (T*)dla_, (T*)db_, (T*)dw_, dS0, p->batch, p->seqlen, p->heads, p->dk,
+      (T*)dq, (T*)dk, (T*)dv, (T*)dla_, (T*)db_, (T*)dw_, dS0, p->batch, p->seqlen, p->heads, qk_heads(p), p->dk,
       p->dv, p->alpha_kind, p->b_kind, p->w_kind, workspace, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
 }

@@ -199,10 +199,15 @@ def test_backward_workspace_and_validation():
     need = r(ch * 128 * 128 * 2) + r(ch * 64 * 128 * 2) + r(ch * 128 * 128 * 2) + \
         r(ch * 64 * 128 * 2) + r(ch * 132 * 4) + r(ch * 4) + 5 * r(ch * 128 * 128 * 2)
     assert N.bwd_workspace_bytes(sp) == need
-    # outside the backward's scope: per-channel decay, fp32, dv > 128, grouped q / k heads
+    # grouped q / k heads: dq and dk per value head as well (bf16 [B, T, H, dk] each)
+    gp = prob(alpha_kind=N.GATE_SCALAR, heads=4, qk_heads=2)
+    chg = 2 * 4 * 2
+    assert N.bwd_workspace_bytes(gp) == (
+        r(chg * 128 * 128 * 2) + r(chg * 64 * 128 * 2) + r(chg * 128 * 128 * 2) + r(chg * 64 * 128 * 2) +
+        r(chg * 132 * 4) + r(chg * 4) + 5 * r(chg * 128 * 128 * 2) + 2 * r(2 * 70 * 4 * 128 * 2))
+    # outside the backward's scope: per-channel decay, fp32, dv > 128, dk = 16
     for p in (prob(), prob(alpha_kind=N.GATE_SCALAR, io_dtype=N.GDR_FP32),
-              prob(alpha_kind=N.GATE_SCALAR, dv=256), prob(alpha_kind=N.GATE_SCALAR, dk=16),
-              prob(alpha_kind=N.GATE_SCALAR, heads=4, qk_heads=2)):
+              prob(alpha_kind=N.GATE_SCALAR, dv=256), prob(alpha_kind=N.GATE_SCALAR, dk=16)):
         assert N.bwd_workspace_bytes(p) == 0
         assert bwd_call(p) == N.GDR_ERR_UNSUPPORTED
     ws = 20 * (1 << 32)

@@ -157,3 +157,26 @@ def test_backward_gdn_workload_sampled(dev):
         else:
             sel[n] = t[bi.to(t.device), :, hi.to(t.device)].unsqueeze(2)
     compare(sel, ref, "gdn sampled")
+
+
+@pytest.mark.parametrize("kind", ["gdn", "gdn_cb"])
+def test_backward_grouped_heads(dev, kind):
+    """Four value heads sharing two q / k heads: dq and dk are the sums, over the value heads of a
+    group, of the per-value-head gradients of the expanded problem."""
+    B, H, HK, T, D = 2, 4, 2, 140, 64
+    a_, b_, w_, shared = KINDS[kind]
+    wl = synth.Workload("t", B, H, T, D, D, "bf16", a_, b_, w_, shared, -2.0, 0.02, 81, HK=HK)
+    x = synth.make_prefill(wl)
+    rng = np.random.default_rng(82)
+    x["do"] = torch.from_numpy(rng.standard_normal((B, T, H, D)).astype(np.float32)).to(torch.bfloat16)
+    x["dS_T"] = torch.from_numpy((0.1 * rng.standard_normal((B, H, D, D))).astype(np.float32))
+    say("backward grouped", kind)
+    out = run(x, dev)
+    assert tuple(out["dq"].shape) == (B, T, HK, D)
+    xe = synth.expand_heads({n: x[n] for n in ("q", "k", "v", "log_alpha", "b", "w", "S0")}, H)
+    xe["do"], xe["dS_T"] = x["do"], x["dS_T"]
+    ref = reference(xe)
+    G = H // HK
+    for n in ("dq", "dk"):
+        ref[n] = ref[n].reshape(B, T, HK, G, D).sum(3)
+    compare(out, ref, "grouped %s" % kind)
