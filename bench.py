@@ -107,7 +107,8 @@ def kernel_source_digest():
 
 def recorded_traffic(key):
     """HBM bytes per launch for `key` ("prefill:<workload>" for a whole call, "prefill_prep:" and
-    "prefill_state:" for its two kernels, or "decode:<workload>") from the
+    "prefill_state:" for its two kernels, "backward:<workload>" for a gdr_chunk_bwd call, or
+    "decode:<workload>") from the
     committed rocprofv3 counter summary, scaled by the calibration copy; None when the summary
     is absent, has no such entry, or was taken on other kernel sources."""
     path = os.path.join(ROOT, "profiles", "hbm_counters.txt")
@@ -238,6 +239,7 @@ def time_backward(wl, steps, warmup, dev):
     return {"ms": ms, "tokens_per_s": wl.B * wl.T / (ms * 1e-3), "workspace_bytes": need,
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": gbs / PEAK_HBM_GBS, "algorithmic_bytes": nb,
+                         "traffic": recorded_traffic("backward:" + wl.name),
                          "scope": "one gdr_chunk_bwd call: chunk maps, two chains, chunk-local adjoint"}}
 
 
