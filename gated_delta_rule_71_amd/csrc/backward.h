@@ -219,8 +219,12 @@ __global__ __launch_bounds__(64 * (2 + NS * DK / 32)) void bwd_chain_kernel(BwdA
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t DV = a.DV, H = a.H, nch = a.nch;
   const int64_t nwg = DV / (16 * NS);  // workgroups per state
-  const int64_t bh = blockIdx.x / nwg;
-  const int sl0 = static_cast<int>(blockIdx.x % nwg) * NS;
+  // consecutive workgroup indices go to different XCDs (8, round robin): renumber so that the
+  // workgroups of one state share an XCD, and so its L2, for the chunk maps they all read
+  const int64_t nb = gridDim.x, bid = blockIdx.x;
+  const int64_t p = (nb % 8 == 0) ? (bid % 8) * (nb / 8) + bid / 8 : bid;
+  const int64_t bh = p / nwg;
+  const int sl0 = static_cast<int>(p % nwg) * NS;
   const bool state = wave >= 2;
   const int sw = state ? wave - 2 : 0;
   const int sls = sl0 + sw / NKB, w = sw % NKB;  // this state wave's slice and k-step

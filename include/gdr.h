@@ -168,7 +168,8 @@ int gdr_decode_step(const gdr_problem* p, const void* q, const void* k, const vo
  * for the per-channel forward (2 dk^2 + 2 dk dv + 132 dk + 128 dv + 20 bytes)
  * and five bf16 dk x dv arrays: the checkpoints (the state entering the chunk
  * and the gradient of the state leaving it, each as rows and transposed) and
- * the chunk's Q'^T dO, each array 256-byte aligned. */
+ * the chunk's Q'^T dO; with grouped q / k heads also dq and dk per value head
+ * (bf16 [B,T,H,dk] each).  Each array is 256-byte aligned. */
 size_t gdr_chunk_bwd_workspace_bytes(const gdr_problem* p);
 
 /*
@@ -188,8 +189,9 @@ size_t gdr_chunk_bwd_workspace_bytes(const gdr_problem* p);
  *          share one workspace must not overlap in time.
  * Outputs must not overlap the inputs or each other.  Supported: bf16, a scalar
  * decay or none (both orders are then the same recurrence), any erase and
- * write gate kinds, dk in {32, 64, 128}, dv a multiple of 16 up to 128, one q /
- * k head per value head; GDR_ERR_UNSUPPORTED otherwise.
+ * write gate kinds, dk in {32, 64, 128}, dv a multiple of 16 up to 128, and
+ * grouped q / k heads (dq and dk are then summed over the value heads that
+ * share each q / k head); GDR_ERR_UNSUPPORTED otherwise.
  * Method: the adjoint of the chunk form of gdr_chunk_fwd ("Recurrent Memory",
  * sections 03 and 04): the state at every chunk boundary by a forward pass over
  * the chunk maps, the gradient of the state at every boundary by the transposed
