@@ -80,7 +80,7 @@ def backward_bytes(wl):
 
 
 def backward_supported(wl):
-    return wl.dtype == "bf16" and wl.alpha != "channel" and wl.DV <= 128 and wl.DK in (32, 64, 128)
+    return wl.dtype == "bf16" and wl.alpha != "channel" and wl.DV <= 256 and wl.DK in (32, 64, 128)
 
 
 def decode_bytes(wl):

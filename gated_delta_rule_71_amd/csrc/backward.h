@@ -69,6 +69,10 @@ struct BwdArgs {
   int alpha_kind, b_kind, w_kind;
   int64_t Hk;  // q / k heads: value head h reads q / k head h / (H / Hk); with Hk < H, dq and dk
                // are written per value head (into the workspace) and summed over each group after
+  // chunk-local adjoint: value columns c0 .. c0 + DVh - 1 (DVh <= 128).  Every input gradient is a
+  // sum over value columns, so d_v = 256 runs as two launches whose dq, dk, d log alpha, db and
+  // (scalar) dw are added afterwards; dv and a per-channel dw are per column.
+  int c0, DVh;
 };
 
 // Transposing fragment of a tiled16 LDS matrix: lane (g, l16) gets element [k0 + 4 g + e] and
@@ -141,11 +145,11 @@ __device__ __forceinline__ float row_sum16(float x) {
 // Q'^T dO of every chunk, for the reverse chain (chunk-parallel): D_b^T [dv][dk] tiled like D^T.
 // One workgroup of four waves per chunk; Q' and the dO rows staged in LDS, lane output
 // D_b[16 tl + 4 g + i][16 cv + l16], i.e. four consecutive channels of row 16 cv + l16 of D_b^T.
-template <int DK>
+template <int DK, int DVP>
 __global__ __launch_bounds__(256) void bwd_db_kernel(BwdArgs a) {
   using MM = Mma<__bf16>;
   using F8 = MM::F8;
-  constexpr int C = 64, NTD = DK / 16, LDO = 128 + 8;
+  constexpr int C = 64, NTD = DK / 16, LDO = DVP + 8;
   __shared__ __attribute__((aligned(16))) unsigned char smem[C * DK * 2 + C * LDO * 2];
   __bf16* sQ = reinterpret_cast<__bf16*>(smem);
   __bf16* sO = reinterpret_cast<__bf16*>(smem + C * DK * 2);
@@ -411,7 +415,8 @@ __global__ __launch_bounds__(512) void bwd_local_kernel(BwdArgs a) {
   const int64_t t0 = c * C, left = a.T - t0;
   const int64_t rr = (bi * a.T + t0) * H + hi;
   const int64_t cix = bh * nch + c;
-  const int NCV = static_cast<int>(DV / 16), NKV = static_cast<int>((DV + 31) / 32);
+  const int c0 = a.c0, DVh = a.DVh;  // this launch's value columns
+  const int NCV = DVh / 16, NKV = (DVh + 31) / 32;
   const __bf16* SR = a.SR + cix * DK * DV;
   const __bf16* ST = a.ST + cix * DV * DK;
   const __bf16* GR = a.GR + cix * DK * DV;
@@ -420,17 +425,18 @@ __global__ __launch_bounds__(512) void bwd_local_kernel(BwdArgs a) {
   // ---- inputs into LDS; the gate prefix sums ----
   const uint32_t oob = 0x80000000u;
   const uint32_t hdk = static_cast<uint32_t>(H * DK * 2), hdv = static_cast<uint32_t>(H * DV * 2), h1 = static_cast<uint32_t>(H * 2);
-  const uint32_t rng_k = wy_range(left, H, DK), rng_v = wy_range(left, H, DV), rng_1 = wy_range(left, H, 1);
+  const uint32_t rng_k = wy_range(left, H, DK), rng_1 = wy_range(left, H, 1);
+  const uint32_t rng_v = wy_range(left, H, DV) - static_cast<uint32_t>(c0 * 2);  // from column c0
   const uint32_t hqk = static_cast<uint32_t>(a.Hk * DK * 2);  // token stride of q and k
   const int64_t rqk = (bi * a.T + t0) * a.Hk + hi / (H / a.Hk);
   const auto rq = make_rsrc(a.q + rqk * DK, wy_range(left, a.Hk, DK));
   const auto rk = make_rsrc(a.k + rqk * DK, wy_range(left, a.Hk, DK));
   const auto rbc = make_rsrc(a.b_kind == kChannel ? a.bg + rr * DK : a.q, a.b_kind == kChannel ? rng_k : 0u);
   const auto rbs = make_rsrc(a.b_kind == kScalar ? a.bg + rr : a.q, a.b_kind == kScalar ? rng_1 : 0u);
-  const auto rv = make_rsrc(a.v + rr * DV, rng_v);
-  const auto rwc = make_rsrc(a.w_kind == kChannel ? a.wg + rr * DV : a.v, a.w_kind == kChannel ? rng_v : 0u);
+  const auto rv = make_rsrc(a.v + rr * DV + c0, rng_v);
+  const auto rwc = make_rsrc(a.w_kind == kChannel ? a.wg + rr * DV + c0 : a.v, a.w_kind == kChannel ? rng_v : 0u);
   const auto rws = make_rsrc(a.w_kind == kScalar ? a.wg + rr : a.v, a.w_kind == kScalar ? rng_1 : 0u);
-  const auto rdo = make_rsrc(a.dO + rr * DV, rng_v);
+  const auto rdo = make_rsrc(a.dO + rr * DV + c0, rng_v);
   const auto rla = make_rsrc(a.alpha_kind == kScalar ? a.la + rr : a.q, a.alpha_kind == kScalar ? rng_1 : 0u);
   // The checkpoint fragments each wave needs later (one value tile cv = wave and one channel tile
   // tl = wave at most: d_v <= 128 and d_k <= 128 give at most NW of each) are loaded first, with
@@ -440,17 +446,17 @@ __global__ __launch_bounds__(512) void bwd_local_kernel(BwdArgs a) {
   if (wave < NCV) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      stf[kb] = tiled_row_frag(ST, DK, 16 * wave + l16, 32 * kb, g);  // S_0 column, k = channels
-      gtf[kb] = tiled_row_frag(GT, DK, 16 * wave + l16, 32 * kb, g);  // dS_n column
+      stf[kb] = tiled_row_frag(ST, DK, c0 + 16 * wave + l16, 32 * kb, g);  // S_0 column, k = channels
+      gtf[kb] = tiled_row_frag(GT, DK, c0 + 16 * wave + l16, 32 * kb, g);  // dS_n column
     }
   }
   if (wave < NTD) {
 #pragma unroll
     for (int kv = 0; kv < NKVM; ++kv) {
       if (kv >= NKV) break;
-      const bool hiok = 32 * kv + 16 < DV;
-      s0f[kv] = tiled_row_frag(SR, static_cast<int>(DV), 16 * wave + l16, 32 * kv, g, hiok);  // S_0 row
-      gnf[kv] = tiled_row_frag(GR, static_cast<int>(DV), 16 * wave + l16, 32 * kv, g, hiok);  // dS_n row
+      const bool hiok = 32 * kv + 16 < DVh;
+      s0f[kv] = tiled_row_frag(SR, static_cast<int>(DV), 16 * wave + l16, c0 + 32 * kv, g, hiok);  // S_0 row
+      gnf[kv] = tiled_row_frag(GR, static_cast<int>(DV), 16 * wave + l16, c0 + 32 * kv, g, hiok);  // dS_n row
     }
   }
   // q, k (and b) rows: every load, then the stores to LDS
@@ -474,11 +480,11 @@ __global__ __launch_bounds__(512) void bwd_local_kernel(BwdArgs a) {
   for (int j = 0; j < NVI; ++j) {
     const int item = tid + NT * j;
     const int t = item / (L::DVP / 8), x0 = (item % (L::DVP / 8)) * 8;
-    const uint32_t off = x0 < DV ? t * hdv + x0 * 2 : oob;
+    const uint32_t off = x0 < DVh ? t * hdv + x0 * 2 : oob;
     uv[j] = buf_load16(rv, off);
     ud[j] = buf_load16(rdo, off);
     uw[j] = buf_load16(rwc, off);
-    uws[j] = buf_load_u16(rws, x0 < DV ? t * h1 : oob);
+    uws[j] = buf_load_u16(rws, x0 < DVh ? t * h1 : oob);
   }
 #pragma unroll
   for (int j = 0; j < NQI; ++j) {
@@ -824,10 +830,10 @@ __global__ __launch_bounds__(512) void bwd_local_kernel(BwdArgs a) {
   sdot += __shfl_xor(sdot, 32);
   if (lane == 0) atomicAdd(&fdg[C - 1], sdot);
   // ---- dv = w . dV and dw = v . dV ----
-  const auto sv_ = make_rsrc(a.dv + rr * DV, rng_v);
-  const auto swc = make_rsrc(a.w_kind == kChannel ? a.dw + rr * DV : a.dv, a.w_kind == kChannel ? rng_v : 0u);
-  for (int item = tid; item < C * (DV / 8); item += NT) {
-    const int t = item / static_cast<int>(DV / 8), x0 = (item % static_cast<int>(DV / 8)) * 8;
+  const auto sv_ = make_rsrc(a.dv + rr * DV + c0, rng_v);
+  const auto swc = make_rsrc(a.w_kind == kChannel ? a.dw + rr * DV + c0 : a.dv, a.w_kind == kChannel ? rng_v : 0u);
+  for (int item = tid; item < C * (DVh / 8); item += NT) {
+    const int t = item / (DVh / 8), x0 = (item % (DVh / 8)) * 8;
     const uint32_t off = t * hdv + x0 * 2;
     float dx[8], vv[8], ww[8];
     load8f(reinterpret_cast<const bf16_t*>(sX + t * LDX + x0), dx);
@@ -871,25 +877,21 @@ __global__ __launch_bounds__(512) void bwd_local_kernel(BwdArgs a) {
   }
 }
 
-// dq and dk of grouped heads: the per-value-head gradients (in the workspace) summed over the
-// H / Hk value heads that share each q / k head.  One thread per 8 channels of a q / k row.
-__global__ __launch_bounds__(256) void bwd_group_sum_kernel(const bf16_t* src, bf16_t* dst, int64_t rows,
-                                                            int64_t G, int64_t DK) {
-  const int64_t n8 = DK / 8;
+// Partial gradients added up: dst[r][d] = sum over j < G of src0[r G + j][d] (+ src1[r G + j][d]).
+// Grouped heads: the per-value-head dq and dk summed over the H / Hk value heads that share each
+// q / k head; d_v = 256: the two column halves' partial sums.  One thread per element.
+__global__ __launch_bounds__(256) void bwd_sum_kernel(const bf16_t* src0, const bf16_t* src1, bf16_t* dst,
+                                                      int64_t rows, int64_t G, int64_t width) {
   const int64_t item = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (item >= rows * n8) return;
-  const int64_t r = item / n8, d0 = (item % n8) * 8;  // q / k row r = (b, t, hk)
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (item >= rows * width) return;
+  const int64_t r = item / width, d = item % width;
+  float acc = 0.f;
   for (int64_t j = 0; j < G; ++j) {
-    float x[8];
-    load8f(src + (r * G + j) * DK + d0, x);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] += x[e];
+    const int64_t i = (r * G + j) * width + d;
+    acc += bf16_to_f32(src0[i].x);
+    if (src1 != nullptr) acc += bf16_to_f32(src1[i].x);
   }
-  bf16x8 o;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) o[e] = static_cast<__bf16>(acc[e]);
-  *reinterpret_cast<bf16x8*>(dst + r * DK + d0) = o;
+  dst[item].x = f32_to_bf16(acc);
 }
 
 }  // namespace gdr

@@ -1,4 +1,4 @@
-// Host side of the backward pass: workspace carving and the four launches.
+// Host side of the backward pass: workspace carving and the launches.
 #include "backward.h"
 
 namespace gdr {
@@ -6,14 +6,26 @@ namespace gdr {
 namespace {
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
+// Workspace, per 64-token chunk of every state: the chunk map (as for the per-channel forward),
+// four checkpoints and Q'^T dO (bf16 dk x dv each).  Partial gradients, when the chunk-local
+// adjoint's sums are completed afterwards: dq and dk per value head and column half (grouped
+// heads or d_v > 128), and with d_v > 128 per half also db (per channel or scalar), d log alpha
+// and a scalar dw.
 struct BwdSizes {
-  size_t Qd, Ad, Dt, Zd, Egn, flag, ck, grp;
-  size_t total() const { return Qd + Ad + Dt + Zd + Egn + flag + 5 * ck + 2 * grp; }
+  size_t Qd, Ad, Dt, Zd, Egn, flag, ck;
+  size_t pqk;  // one partial dq (or dk): value-head rows x dk, bf16
+  size_t pg;   // one partial per-token gate gradient (dk wide for a per-channel b): bf16
+  int nh;      // column halves
+  bool partial_qk;
+  size_t total() const {
+    return Qd + Ad + Dt + Zd + Egn + flag + 5 * ck + (partial_qk ? 2 * nh * pqk : 0) +
+           (nh > 1 ? 3 * nh * pg : 0);
+  }
 };
 
-// grouped: value-head rows B T H when q / k have fewer heads (dq and dk per value head), else 0
-BwdSizes bwd_sizes(int64_t nstate, int64_t T, int64_t DK, int64_t DV, int64_t grouped = 0) {
-  const size_t ch = static_cast<size_t>(nstate) * static_cast<size_t>((T + 63) / 64);
+BwdSizes bwd_sizes(int64_t B, int64_t H, int64_t Hk, int64_t T, int64_t DK, int64_t DV) {
+  const size_t ch = static_cast<size_t>(B * H) * static_cast<size_t>((T + 63) / 64);
+  const size_t rows = static_cast<size_t>(B * T * H);
   BwdSizes s;
   s.Qd = align256(ch * 64 * DK * 2);
   s.Ad = align256(ch * DK * DK * 2);
@@ -22,7 +34,10 @@ BwdSizes bwd_sizes(int64_t nstate, int64_t T, int64_t DK, int64_t DV, int64_t gr
   s.Egn = align256(ch * (DK + 4) * 4);
   s.flag = align256(ch * 4);
   s.ck = align256(ch * DK * DV * 2);
-  s.grp = align256(static_cast<size_t>(grouped) * DK * 2);
+  s.nh = DV > 128 ? 2 : 1;
+  s.partial_qk = s.nh > 1 || Hk < H;
+  s.pqk = align256(rows * DK * 2);
+  s.pg = align256(rows * DK * 2);
   return s;
 }
 
@@ -38,34 +53,42 @@ void launch_chain(const BwdArgs& a, int64_t nstate, hipStream_t s) {
                        dim3(64 * (2 + DK / 32)), 0, s, a);
 }
 
+// halves: the chunk-local adjoint's argument sets, one per 128 value columns
 template <int DK>
-hipError_t launch_dk(WycArgs f, BwdArgs a, int64_t nstate, hipStream_t s) {
+hipError_t launch_dk(WycArgs f, const BwdArgs& a, const BwdArgs* halves, int nh, int64_t nstate,
+                     hipStream_t s) {
   const int64_t nblk = nstate * a.nch;
-  hipLaunchKernelGGL((wyc_prep_kernel<DK, 128, 1>), dim3((unsigned)nblk), dim3(512), 0, s, f);
-  hipLaunchKernelGGL((bwd_db_kernel<DK>), dim3((unsigned)nblk), dim3(256), 0, s, a);
+  if (a.DV <= 128) {
+    hipLaunchKernelGGL((wyc_prep_kernel<DK, 128, 1>), dim3((unsigned)nblk), dim3(512), 0, s, f);
+    hipLaunchKernelGGL((bwd_db_kernel<DK, 128>), dim3((unsigned)nblk), dim3(256), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((wyc_prep_kernel<DK, 256, 1>), dim3((unsigned)nblk), dim3(512), 0, s, f);
+    hipLaunchKernelGGL((bwd_db_kernel<DK, 256>), dim3((unsigned)nblk), dim3(256), 0, s, a);
+  }
   launch_chain<DK, false>(a, nstate, s);
   launch_chain<DK, true>(a, nstate, s);
-  hipLaunchKernelGGL((bwd_local_kernel<DK>), dim3((unsigned)nblk), dim3(512), 0, s, a);
+  for (int h = 0; h < nh; ++h)
+    hipLaunchKernelGGL((bwd_local_kernel<DK>), dim3((unsigned)nblk), dim3(512), 0, s, halves[h]);
   return hipGetLastError();
 }
 
-hipError_t group_sum(const bf16_t* src, bf16_t* dst, int64_t rows, int64_t G, int64_t DK, hipStream_t s) {
-  const int64_t items = rows * (DK / 8);
-  if (items > 0)
-    hipLaunchKernelGGL(bwd_group_sum_kernel, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, s, src, dst,
-                       rows, G, DK);
-  return hipGetLastError();
+void sum_parts(const bf16_t* s0, const bf16_t* s1, bf16_t* dst, int64_t rows, int64_t G, int64_t width,
+               hipStream_t s) {
+  const int64_t n = rows * width;
+  if (n > 0)
+    hipLaunchKernelGGL(bwd_sum_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, s0, s1, dst,
+                       rows, G, width);
 }
 }  // namespace
 
-// bf16 I/O, a scalar decay or none, dk in {32, 64, 128}, dv a multiple of 16 up to 128.
+// bf16 I/O, a scalar decay or none, dk in {32, 64, 128}, dv a multiple of 16 up to 256.
 bool backward_supported(int io_dtype_bf16, int64_t DK, int64_t DV, int alpha_kind) {
-  return io_dtype_bf16 && (DK == 32 || DK == 64 || DK == 128) && DV % 16 == 0 && DV > 0 && DV <= 128 &&
+  return io_dtype_bf16 && (DK == 32 || DK == 64 || DK == 128) && DV % 16 == 0 && DV > 0 && DV <= 256 &&
          alpha_kind != kChannel;
 }
 
 size_t backward_workspace_bytes(int64_t B, int64_t H, int64_t Hk, int64_t T, int64_t DK, int64_t DV) {
-  return bwd_sizes(B * H, T, DK, DV, Hk < H ? B * T * H : 0).total();
+  return bwd_sizes(B, H, Hk, T, DK, DV).total();
 }
 
 hipError_t launch_backward(const bf16_t* q, const bf16_t* k, const bf16_t* v, const bf16_t* la,
@@ -75,8 +98,8 @@ hipError_t launch_backward(const bf16_t* q, const bf16_t* k, const bf16_t* v, co
                            int64_t Hk, int64_t DK, int64_t DV, int alpha_kind, int b_kind, int w_kind,
                            void* workspace, hipStream_t s) {
   const int64_t nstate = B * H;
-  const bool grouped = Hk < H;
-  const BwdSizes z = bwd_sizes(nstate, T, DK, DV, grouped ? B * T * H : 0);
+  if (nstate == 0 || T == 0) return hipSuccess;
+  const BwdSizes z = bwd_sizes(B, H, Hk, T, DK, DV);
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   WycArgs f{};
   f.q = q;
@@ -131,13 +154,7 @@ hipError_t launch_backward(const bf16_t* q, const bf16_t* k, const bf16_t* v, co
   a.GR = reinterpret_cast<__bf16*>(ws + 2 * z.ck);
   a.GT = reinterpret_cast<__bf16*>(ws + 3 * z.ck);
   a.Dbt = reinterpret_cast<__bf16*>(ws + 4 * z.ck);
-  bf16_t* gq = reinterpret_cast<bf16_t*>(ws + 5 * z.ck);
-  bf16_t* gk = reinterpret_cast<bf16_t*>(ws + 5 * z.ck + z.grp);
-  a.Hk = Hk;
-  if (grouped) {  // per value head first
-    a.dq = gq;
-    a.dk = gk;
-  }
+  ws += 5 * z.ck;
   a.T = T;
   a.H = H;
   a.DV = DV;
@@ -145,17 +162,58 @@ hipError_t launch_backward(const bf16_t* q, const bf16_t* k, const bf16_t* v, co
   a.alpha_kind = alpha_kind;
   a.b_kind = b_kind;
   a.w_kind = w_kind;
-  if (nstate == 0 || T == 0) return hipSuccess;
+  a.Hk = Hk;
+  a.c0 = 0;
+  a.DVh = static_cast<int>(DV < 128 ? DV : 128);
+
+  // the chunk-local adjoint per column half, its summed outputs redirected to partial buffers
+  const int nh = z.nh;
+  BwdArgs halves[2] = {a, a};
+  bf16_t* pq[2] = {nullptr, nullptr};
+  bf16_t* pk[2] = {nullptr, nullptr};
+  bf16_t* pla[2] = {nullptr, nullptr};
+  bf16_t* pb[2] = {nullptr, nullptr};
+  bf16_t* pw[2] = {nullptr, nullptr};
+  for (int h = 0; h < nh; ++h) {
+    halves[h].c0 = 128 * h;
+    halves[h].DVh = static_cast<int>(DV - 128 * h < 128 ? DV - 128 * h : 128);
+    if (z.partial_qk) {
+      pq[h] = reinterpret_cast<bf16_t*>(ws);
+      pk[h] = reinterpret_cast<bf16_t*>(ws + z.pqk);
+      ws += 2 * z.pqk;
+      halves[h].dq = pq[h];
+      halves[h].dk = pk[h];
+    }
+  }
+  if (nh > 1) {
+    for (int h = 0; h < nh; ++h) {
+      pla[h] = reinterpret_cast<bf16_t*>(ws);
+      pb[h] = reinterpret_cast<bf16_t*>(ws + z.pg);
+      pw[h] = reinterpret_cast<bf16_t*>(ws + 2 * z.pg);
+      ws += 3 * z.pg;
+      halves[h].dla = pla[h];
+      halves[h].db = pb[h];
+      if (w_kind == kScalar) halves[h].dw = pw[h];  // (a per-channel dw is per column: direct)
+    }
+  }
   hipError_t e;
   switch (DK) {
-    case 32: e = launch_dk<32>(f, a, nstate, s); break;
-    case 64: e = launch_dk<64>(f, a, nstate, s); break;
-    default: e = launch_dk<128>(f, a, nstate, s); break;
+    case 32: e = launch_dk<32>(f, a, halves, nh, nstate, s); break;
+    case 64: e = launch_dk<64>(f, a, halves, nh, nstate, s); break;
+    default: e = launch_dk<128>(f, a, halves, nh, nstate, s); break;
   }
-  if (e != hipSuccess || !grouped) return e;
-  e = group_sum(gq, dq, B * T * Hk, H / Hk, DK, s);
   if (e != hipSuccess) return e;
-  return group_sum(gk, dk, B * T * Hk, H / Hk, DK, s);
+  const int64_t rows = B * T * H;
+  if (z.partial_qk) {
+    sum_parts(pq[0], pq[1], dq, B * T * Hk, H / Hk, DK, s);
+    sum_parts(pk[0], pk[1], dk, B * T * Hk, H / Hk, DK, s);
+  }
+  if (nh > 1) {
+    if (alpha_kind == kScalar) sum_parts(pla[0], pla[1], dla, rows, 1, 1, s);
+    if (b_kind != kNone) sum_parts(pb[0], pb[1], db, rows, 1, b_kind == kChannel ? DK : 1, s);
+    if (w_kind == kScalar) sum_parts(pw[0], pw[1], dw, rows, 1, 1, s);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace gdr

@@ -205,9 +205,17 @@ def test_backward_workspace_and_validation():
     assert N.bwd_workspace_bytes(gp) == (
         r(chg * 128 * 128 * 2) + r(chg * 64 * 128 * 2) + r(chg * 128 * 128 * 2) + r(chg * 64 * 128 * 2) +
         r(chg * 132 * 4) + r(chg * 4) + 5 * r(chg * 128 * 128 * 2) + 2 * r(2 * 70 * 4 * 128 * 2))
-    # outside the backward's scope: per-channel decay, fp32, dv > 128, dk = 16
+    # d_v = 256: the chunk-local adjoint runs per 128-column half, with partial dq, dk (per value
+    # head) and per-token gate gradients (three arrays of [B, T, H, dk] bf16) per half
+    wp = prob(alpha_kind=N.GATE_SCALAR, b_kind=N.GATE_SCALAR, w_kind=N.GATE_SCALAR, dv=256)
+    rows = 2 * 70 * 3
+    assert N.bwd_workspace_bytes(wp) == (
+        r(ch * 128 * 128 * 2) + r(ch * 64 * 128 * 2) + r(ch * 256 * 128 * 2) + r(ch * 64 * 256 * 2) +
+        r(ch * 132 * 4) + r(ch * 4) + 5 * r(ch * 128 * 256 * 2) + 2 * 2 * r(rows * 128 * 2) +
+        3 * 2 * r(rows * 128 * 2))
+    # outside the backward's scope: per-channel decay, fp32, dv > 256, dk = 16
     for p in (prob(), prob(alpha_kind=N.GATE_SCALAR, io_dtype=N.GDR_FP32),
-              prob(alpha_kind=N.GATE_SCALAR, dv=256), prob(alpha_kind=N.GATE_SCALAR, dk=16)):
+              prob(alpha_kind=N.GATE_SCALAR, dv=512), prob(alpha_kind=N.GATE_SCALAR, dk=16)):
         assert N.bwd_workspace_bytes(p) == 0
         assert bwd_call(p) == N.GDR_ERR_UNSUPPORTED
     ws = 20 * (1 << 32)

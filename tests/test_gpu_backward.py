@@ -97,7 +97,8 @@ def test_backward_small(dev, kind):
     compare(run(x, dev), reference(x), kind)
 
 
-@pytest.mark.parametrize("D,DV", [(32, 32), (64, 48), (64, 128), (128, 16), (32, 112)])
+@pytest.mark.parametrize("D,DV", [(32, 32), (64, 48), (64, 128), (128, 16), (32, 112), (128, 256), (64, 144),
+                                  (32, 192)])
 def test_backward_dims(dev, D, DV):
     x = case("gdn_cb", T=133, D=D, DV=DV, seed=41)
     say("backward dims", D, DV)
@@ -180,3 +181,22 @@ def test_backward_grouped_heads(dev, kind):
     for n in ("dq", "dk"):
         ref[n] = ref[n].reshape(B, T, HK, G, D).sum(3)
     compare(out, ref, "grouped %s" % kind)
+
+
+def test_backward_wide_values_grouped(dev):
+    """d_v = 256 (two column halves of the chunk-local adjoint) with grouped q / k heads and
+    per-channel erase and write gates: the partial sums of both kinds are added together."""
+    B, H, HK, T, D, DV = 1, 4, 2, 100, 64, 256
+    wl = synth.Workload("t", B, H, T, D, DV, "bf16", "scalar", "channel", "channel", False, -2.0, 0.02, 91, HK=HK)
+    x = synth.make_prefill(wl)
+    rng = np.random.default_rng(92)
+    x["do"] = torch.from_numpy(rng.standard_normal((B, T, H, DV)).astype(np.float32)).to(torch.bfloat16)
+    x["dS_T"] = torch.from_numpy((0.1 * rng.standard_normal((B, H, D, DV))).astype(np.float32))
+    say("backward wide grouped")
+    out = run(x, dev)
+    xe = synth.expand_heads({n: x[n] for n in ("q", "k", "v", "log_alpha", "b", "w", "S0")}, H)
+    xe["do"], xe["dS_T"] = x["do"], x["dS_T"]
+    ref = reference(xe)
+    for n in ("dq", "dk"):
+        ref[n] = ref[n].reshape(B, T, HK, H // HK, D).sum(3)
+    compare(out, ref, "wide grouped")
