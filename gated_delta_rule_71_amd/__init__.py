@@ -135,7 +135,7 @@ def chunk_bwd(q, k, v, log_alpha=None, b=None, w=None, S0=None, do=None, dS_T=No
     (q's dtype), dlog_alpha, db, dw (shaped like the gates; None for an absent gate) and dS0
     (float32).  With one shared beta passed as both b and w, its gradient is db + dw.  With
     grouped q / k heads, dq and dk are summed over the value heads that share them.  Raises
-    GdrError(GDR_ERR_UNSUPPORTED) outside bf16 with a scalar or no decay and dv <= 128."""
+    GdrError(GDR_ERR_UNSUPPORTED) outside bf16 with a scalar or no decay and dv <= 256."""
     torch = _torch()
     B, T, HQ, DK = q.shape
     H, DV = v.shape[2], v.shape[-1]

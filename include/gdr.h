@@ -189,7 +189,7 @@ size_t gdr_chunk_bwd_workspace_bytes(const gdr_problem* p);
  *          share one workspace must not overlap in time.
  * Outputs must not overlap the inputs or each other.  Supported: bf16, a scalar
  * decay or none (both orders are then the same recurrence), any erase and
- * write gate kinds, dk in {32, 64, 128}, dv a multiple of 16 up to 128, and
+ * write gate kinds, dk in {32, 64, 128}, dv a multiple of 16 up to 256, and
  * grouped q / k heads (dq and dk are then summed over the value heads that
  * share each q / k head); GDR_ERR_UNSUPPORTED otherwise.
  * Method: the adjoint of the chunk form of gdr_chunk_fwd ("Recurrent Memory",
