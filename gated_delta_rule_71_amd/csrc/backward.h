@@ -877,6 +877,12 @@ __global__ __launch_bounds__(512) void bwd_local_kernel(BwdArgs a) {
   }
 }
 
+// dS0 of an empty sequence: the state passes through unchanged, so dS0 = dS_T (zeros when absent).
+__global__ __launch_bounds__(256) void bwd_pass_state_kernel(const float* dST, float* dS0, int64_t n) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i < n) dS0[i] = dST != nullptr ? dST[i] : 0.f;
+}
+
 // Partial gradients added up: dst[r][d] = sum over j < G of src0[r G + j][d] (+ src1[r G + j][d]).
 // Grouped heads: the per-value-head dq and dk summed over the H / Hk value heads that share each
 // q / k head; d_v = 256: the two column halves' partial sums.  One thread per element.

@@ -98,7 +98,13 @@ hipError_t launch_backward(const bf16_t* q, const bf16_t* k, const bf16_t* v, co
                            int64_t Hk, int64_t DK, int64_t DV, int alpha_kind, int b_kind, int w_kind,
                            void* workspace, hipStream_t s) {
   const int64_t nstate = B * H;
-  if (nstate == 0 || T == 0) return hipSuccess;
+  if (nstate == 0) return hipSuccess;
+  if (T == 0) {
+    const int64_t n = nstate * DK * DV;
+    if (dS0 != nullptr)
+      hipLaunchKernelGGL(bwd_pass_state_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, dST, dS0, n);
+    return hipGetLastError();
+  }
   const BwdSizes z = bwd_sizes(B, H, Hk, T, DK, DV);
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   WycArgs f{};

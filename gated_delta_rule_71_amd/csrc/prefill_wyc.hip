@@ -34,7 +34,7 @@ void launch_state(WycArgs a, int64_t nstate, hipStream_t s) {
                      dim3(64 * (2 + NSW * SPLIT)), 0, s, a);
 }
 
-// MODE 0: no erase gate (either order), 1: erase then decay, 2: decay then erase
+// MODE 0: no erase gate (either order), 1: decay then erase, 2: erase then decay
 template <int DK, int MODE>
 hipError_t launch_mode(WycArgs a, int64_t nstate, hipEvent_t mark, hipStream_t s) {
   constexpr bool AZ = MODE == 0;

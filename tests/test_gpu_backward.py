@@ -105,6 +105,17 @@ def test_backward_dims(dev, D, DV):
     compare(run(x, dev), reference(x), "dk=%d dv=%d" % (D, DV))
 
 
+def test_backward_empty_sequence(dev):
+    """T = 0: no token, so dS0 = dS_T (and zeros without dS_T); the token gradients are empty."""
+    x = case("gdn", B=1, H=2, T=0, seed=49)
+    out = run(x, dev)
+    assert out["dq"].numel() == 0 and out["dv"].numel() == 0
+    np.testing.assert_array_equal(out["dS0"].cpu().numpy(), x["dS_T"].numpy())
+    x["dS_T"] = None
+    out = run(x, dev)
+    assert not out["dS0"].abs().max().item()
+
+
 @pytest.mark.parametrize("T", [1, 63, 64, 65, 128, 300])
 def test_backward_lengths(dev, T):
     x = case("gdn", B=1, H=2, T=T, seed=50 + T)
