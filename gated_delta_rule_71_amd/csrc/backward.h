@@ -115,6 +115,46 @@ __device__ __forceinline__ Mma<__bf16>::F8 tiled_row_frag(const __bf16* m, int n
   return f;
 }
 
+// The same two fragments from a tiled16 matrix staged in LDS with its rows 8 .. 15 of every tile
+// holding their two 16-byte pieces swapped: rows r and r + 8 of a tile then fall on different
+// banks for these reads (one tile is 512 bytes; unswizzled, rows r and r + 8 share banks).
+__device__ __forceinline__ int swz16(int r, int c) {  // element offset of (r, c) inside a tile
+  return (r & 15) * 16 + ((((c & 15) >> 3) ^ ((r & 15) >> 3)) << 3) + (c & 7);
+}
+__device__ __forceinline__ Mma<__bf16>::F8 tiled_row_frag_sw(const __bf16* m, int ncols, int row, int k0, int g) {
+  Mma<__bf16>::F8 f;
+  const int nt = ncols >> 4;
+  const __bf16* t0 = m + ((row >> 4) * nt + (k0 >> 4)) * 256;
+  const bf16x4 lo = *reinterpret_cast<const bf16x4*>(t0 + swz16(row, 4 * g));
+  const bf16x4 up = *reinterpret_cast<const bf16x4*>(t0 + 256 + swz16(row, 4 * g));
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    f[e] = lo[e];
+    f[4 + e] = up[e];
+  }
+  return f;
+}
+__device__ __forceinline__ Mma<__bf16>::F8 tiled_col_frag_sw(const __bf16* m, int ncols, int col, int k0, int g,
+                                                             int l16) {
+  Mma<__bf16>::F8 f;
+  const int nt = ncols >> 4, ct = col >> 4;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int r = k0 + 16 * h + 4 * g + (l16 >> 2);
+    const __bf16* p = m + ((r >> 4) * nt + ct) * 256 + swz16(r, 4 * (l16 & 3));
+    const bf16x4 v = lds_read_tr4(reinterpret_cast<const unsigned char*>(p));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) f[4 * h + e] = v[e];
+  }
+  return f;
+}
+// Global offset of the 16-byte piece that lands in LDS slot `lane` of a 1 KB (two-tile) copy in
+// the swizzled form above.
+__device__ __forceinline__ uint32_t swz16_src(int lane) {
+  const int r = (lane & 31) >> 1;
+  return static_cast<uint32_t>((lane >> 5) * 512 + r * 32 + (((lane & 1) ^ (r >> 3)) << 4));
+}
+
 // Transposing fragment of a row-major LDS array (pitch in elements): column `col`, rows
 // k0 + 4 g + e and k0 + 16 + 4 g + e.
 __device__ __forceinline__ Mma<__bf16>::F8 lds_col_frag(const __bf16* base, int pitch, int col, int k0,
@@ -243,8 +283,9 @@ __global__ __launch_bounds__(64 * (2 + NS * DK / 32)) void bwd_chain_kernel(BwdA
     const int64_t cix = bh * nch + chunk_of(it);
     unsigned char* B = buf(it);
     const auto rA = make_rsrc(a.Ad + cix * DK * DK, L::AB);
+    const uint32_t src = swz16_src(lane);  // A' in the swizzled tile form
 #pragma unroll
-    for (int i = 0; i < L::AB / 1024; ++i) lds_dma16(rA, B + 1024 * i, 1024 * i + lane * 16);
+    for (int i = 0; i < L::AB / 1024; ++i) lds_dma16(rA, B + 1024 * i, 1024 * i + src);
     const auto rD = make_rsrc(Dsrc + cix * DV * DK + static_cast<int64_t>(sl0) * 16 * DK, L::DB);
 #pragma unroll
     for (int i = 0; i < L::DB / 1024; ++i) lds_dma16(rD, B + L::AB + 1024 * i, 1024 * i + lane * 16);
@@ -304,8 +345,8 @@ __global__ __launch_bounds__(64 * (2 + NS * DK / 32)) void bwd_chain_kernel(BwdA
         const int tl = 2 * w + u;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
-          const F8 af = REV ? tiled_col_frag(sA, DK, 16 * tl + l16, 32 * kb, g, l16)
-                            : tiled_row_frag(sA, DK, 16 * tl + l16, 32 * kb, g);
+          const F8 af = REV ? tiled_col_frag_sw(sA, DK, 16 * tl + l16, 32 * kb, g, l16)
+                            : tiled_row_frag_sw(sA, DK, 16 * tl + l16, 32 * kb, g);
           acc[u] = MM::mma8(af, sf[kb], acc[u]);
         }
       }
