@@ -2,7 +2,7 @@
 chunk 64, bf16 inputs, fp32 state) and the Gated DeltaNet-2 decode step (256 x 32 states, 1000
 steps), on one MI355X, through the C ABI.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gdn|kda|gdn2|mamba2|gla|gdn_gqa]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gdn|kda|gdn2|mamba2|gla|gdn_gqa|gdn_d256]
                     [--decode-steps N] [--no-cpu-baseline] [--no-decode]
 
 Prints ONE JSON line.  `value` is prefill tokens/s (B*T / time per call) with inputs resident in
@@ -300,7 +300,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="gdn", choices=["gdn", "kda", "gdn2", "mamba2", "gla", "gdn_gqa"])
+    ap.add_argument("--workload", default="gdn", choices=["gdn", "kda", "gdn2", "mamba2", "gla", "gdn_gqa", "gdn_d256"])
     ap.add_argument("--decode-steps", type=int, default=None)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -232,6 +232,7 @@ hipError_t launch_decode(const IO* q, const IO* k, const IO* v, const IO* la, co
     case 32: return launch_decode_dk<IO, 32>(a, n, decay_first, stream);
     case 64: return launch_decode_dk<IO, 64>(a, n, decay_first, stream);
     case 128: return launch_decode_dk<IO, 128>(a, n, decay_first, stream);
+    case 256: return launch_decode_dk<IO, 256>(a, n, decay_first, stream);
     default: return hipErrorInvalidValue;
   }
 }

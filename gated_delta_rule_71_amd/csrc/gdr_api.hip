@@ -65,7 +65,7 @@ int check_problem(const gdr_problem* p) {
     return GDR_ERR_INVALID_ARGUMENT;
   if (p->batch >= kMaxDim || p->heads >= kMaxDim || p->seqlen >= kMaxDim)
     return GDR_ERR_INVALID_ARGUMENT;
-  if (p->dk != 16 && p->dk != 32 && p->dk != 64 && p->dk != 128) return GDR_ERR_UNSUPPORTED;
+  if (p->dk != 16 && p->dk != 32 && p->dk != 64 && p->dk != 128 && p->dk != 256) return GDR_ERR_UNSUPPORTED;
   if (p->dv % 16 != 0 || p->dv > 256) return GDR_ERR_UNSUPPORTED;
   if (p->chunk != 0 && p->chunk != 64) return GDR_ERR_UNSUPPORTED;
   // index arithmetic inside the kernels is 64-bit; grids are 32-bit
@@ -118,7 +118,7 @@ GDR_EXPORT const char* gdr_status_string(int status) {
       return "GDR_ERR_INVALID_ARGUMENT: NULL pointer, negative size, bad enum value, struct_size "
              "mismatch or overlapping output";
     case GDR_ERR_UNSUPPORTED:
-      return "GDR_ERR_UNSUPPORTED: dk must be 16/32/64/128, dv a multiple of 16 up to 256, chunk 64";
+      return "GDR_ERR_UNSUPPORTED: dk must be 16/32/64/128 (256: bf16, scalar, no or decay-first per-channel decay), dv a multiple of 16 up to 256, chunk 64";
     case GDR_ERR_MISALIGNED: return "GDR_ERR_MISALIGNED: tensor pointers must be 16-byte aligned";
     case GDR_ERR_WORKSPACE_TOO_SMALL: return "GDR_ERR_WORKSPACE_TOO_SMALL: workspace below the query";
     case GDR_ERR_HIP: return "GDR_ERR_HIP: the HIP runtime reported an error at launch";

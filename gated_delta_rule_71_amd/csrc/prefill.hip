@@ -45,6 +45,7 @@ bool fits_dk(int64_t DK, int mode, int nsw) {
     case 32: return prefill_fits<OT, 32>(mode, nsw);
     case 64: return prefill_fits<OT, 64>(mode, nsw);
     case 128: return prefill_fits<OT, 128>(mode, nsw);
+    case 256: return prefill_fits<OT, 256>(mode, nsw);
     default: return false;
   }
 }
@@ -113,7 +114,8 @@ hipError_t launch_prefill(const IO* q, const IO* k, const IO* v, const IO* la, c
       case 16: return prefill_bf16_dk16(a, nstate, mode, nsw, stream);
       case 32: return prefill_bf16_dk32(a, nstate, mode, nsw, stream);
       case 64: return prefill_bf16_dk64(a, nstate, mode, nsw, stream);
-      default: return prefill_bf16_dk128(a, nstate, mode, nsw, stream);
+      case 128: return prefill_bf16_dk128(a, nstate, mode, nsw, stream);
+      default: return prefill_bf16_dk256(a, nstate, mode, nsw, stream);
     }
   } else {
     if (!fits_dk<float>(DK, mode, 1)) return hipErrorInvalidValue;

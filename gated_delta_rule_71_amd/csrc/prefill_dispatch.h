@@ -55,6 +55,7 @@ hipError_t prefill_bf16_dk16(const PrefillArgs<bf16_t>&, int64_t, int, int, hipS
 hipError_t prefill_bf16_dk32(const PrefillArgs<bf16_t>&, int64_t, int, int, hipStream_t);
 hipError_t prefill_bf16_dk64(const PrefillArgs<bf16_t>&, int64_t, int, int, hipStream_t);
 hipError_t prefill_bf16_dk128(const PrefillArgs<bf16_t>&, int64_t, int, int, hipStream_t);
+hipError_t prefill_bf16_dk256(const PrefillArgs<bf16_t>&, int64_t, int, int, hipStream_t);
 hipError_t prefill_f32_any(const PrefillArgs<float>&, int64_t, int64_t, int, int, hipStream_t);
 
 }  // namespace gdr

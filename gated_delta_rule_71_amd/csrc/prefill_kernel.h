@@ -60,8 +60,11 @@ template <typename OT, int DK, int NSW, int MODE>
 struct PrefillLayout {
   static constexpr int C = 64;
   static constexpr int DVS = 16 * NSW;
-  static constexpr int LDT = DK + 8;  // row pitch of token-major operands (elements)
-  static constexpr int LDD = C + 8;   // row pitch of channel-major / 64-wide arrays
+  // row pitches (elements) of token-major operands and of channel-major / 64-wide arrays: padded
+  // by 8 against bank conflicts, except at dk = 256, whose unpadded layout is what fits in LDS
+  static constexpr int PAD = DK >= 256 ? 0 : 8;
+  static constexpr int LDT = DK + PAD;
+  static constexpr int LDD = C + PAD;
   static constexpr int LDI = 24;      // row pitch of the diagonal inverses
   static constexpr int ES = sizeof(OT);
   static constexpr bool TWO = MODE == 2;
@@ -216,6 +219,7 @@ __device__ __forceinline__ int swz(int row_key, int t) { return (((t >> 2) ^ row
 // N (1, 2 or 4) consecutive elements as one LDS store.
 template <int N>
 __device__ __forceinline__ void lds_store_run(__bf16* p, const __bf16* v) {
+  static_assert(N == 1 || N == 2 || N == 4, "runs of 1, 2 or 4 elements");
   uint32_t h[N];
 #pragma unroll
   for (int j = 0; j < N; ++j) h[j] = __builtin_bit_cast(uint16_t, v[j]);
@@ -229,6 +233,7 @@ __device__ __forceinline__ void lds_store_run(__bf16* p, const __bf16* v) {
 }
 template <int N>
 __device__ __forceinline__ void lds_store_run(float* p, const float* v) {
+  static_assert(N == 1 || N == 2 || N == 4, "runs of 1, 2 or 4 elements");
   if constexpr (N == 4) {
     *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
   } else if constexpr (N == 2) {
@@ -557,12 +562,17 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs<IO> a) {
         }
       }
       if (!(MODE != 0 && robust)) {
-        // channel-major rows d0..d0+7: this thread's TPS tokens as one store per row
-        const int pos = swz((d0 >> 3) & 15, ts * TPS);
+        // channel-major rows d0..d0+7: this thread's TPS tokens as one store per row and quad of
+        // 4 tokens (quads are swizzled apart, so a run of 8 at dk = 256 is two stores)
+        constexpr int RUN = TPS < 4 ? TPS : 4;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          lds_store_run<TPS>(dP + (d0 + j) * LDD + pos, pdp[j]);
-          if (TWO) lds_store_run<TPS>(dK + (d0 + j) * LDD + pos, pdk[j]);
+        for (int r0 = 0; r0 < TPS; r0 += RUN) {
+          const int pos = swz((d0 >> 3) & 15, ts * TPS + r0);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            lds_store_run<RUN>(dP + (d0 + j) * LDD + pos, pdp[j] + r0);
+            if (TWO) lds_store_run<RUN>(dK + (d0 + j) * LDD + pos, pdk[j] + r0);
+          }
         }
       }
     }

@@ -71,7 +71,10 @@ typedef enum { GDR_GATE_NONE = 0, GDR_GATE_SCALAR = 1, GDR_GATE_CHANNEL = 2 } gd
 typedef enum { GDR_ERASE_THEN_DECAY = 0, GDR_DECAY_THEN_ERASE = 1 } gdr_order;
 
 /* Problem description.  Set struct_size = sizeof(gdr_problem).
- * Supported: dk in {16, 32, 64, 128}; dv a multiple of 16 in [16, 256];
+ * Supported: dk in {16, 32, 64, 128}, and 256 for gdr_decode_step and for a
+ * bf16 gdr_chunk_fwd with a scalar decay, no decay or a per-channel decay
+ * applied before the erase (GDR_ERR_UNSUPPORTED otherwise); dv a multiple of
+ * 16 in [16, 256];
  * chunk == 64 (0 selects 64); batch, heads >= 0; seqlen >= 0 (any value: a
  * ragged last chunk is padded with identity tokens inside the kernel). */
 typedef struct {

@@ -19,6 +19,7 @@ Remembers" appendix table: H heads with d_k = d_v = 128):
   mamba2  B=4  H=16 T=4096   d=128  bf16, scalar decay, no erase, w = 1
   gla     B=4  H=16 T=4096   d=128  bf16, per-channel decay, no erase, w = 1
   gdn_gqa B=4  H=32 T=4096   d=128  bf16, as gdn with 16 shared q / k heads
+  gdn_d256 B=4 H=8  T=4096   d=256  bf16, as gdn at d_k = d_v = 256
 
 Distributions: q, k ~ N(0, 1) rows then L2-normalised; v ~ N(0, 1);
 beta, b, w = sigmoid(N(0, 1)); log alpha = -softplus(N(mu, 1)) with mu = 0 for
@@ -70,6 +71,9 @@ WORKLOADS = {
                        1005),
     # erase off with a per-channel decay (gated linear attention) at the Gated DeltaNet shapes; w = 1
     "gla": Workload("gla", 4, 16, 4096, 128, 128, "bf16", CHANNEL, NONE, NONE, False, -2.0, 0.0, 1007),
+    # Gated DeltaNet gates at d_k = d_v = 256 (half the heads, the same state bytes per head-pair)
+    "gdn_d256": Workload("gdn_d256", 4, 8, 4096, 256, 256, "bf16", SCALAR, SCALAR, SCALAR, True, -2.0, 0.0,
+                         1008),
     # Gated DeltaNet gates with grouped heads: 32 value heads sharing 16 query / key heads
     "gdn_gqa": Workload("gdn_gqa", 4, 32, 4096, 128, 128, "bf16", SCALAR, SCALAR, SCALAR, True, -2.0,
                         0.0, 1006, HK=16),

@@ -69,6 +69,8 @@ def big_apart():
     ("batch", -1, N.GDR_ERR_INVALID_ARGUMENT),
     ("seqlen", -5, N.GDR_ERR_INVALID_ARGUMENT),
     ("dk", 96, N.GDR_ERR_UNSUPPORTED),
+    ("dk", 256, N.GDR_ERR_UNSUPPORTED),  # per-channel decay after the erase does not fit at dk 256
+    ("io_dtype_dk256", None, N.GDR_ERR_UNSUPPORTED),  # fp32 at dk 256
     ("dk", 0, N.GDR_ERR_INVALID_ARGUMENT),
     ("dv", 40, N.GDR_ERR_UNSUPPORTED),
     ("dv", 512, N.GDR_ERR_UNSUPPORTED),
@@ -76,7 +78,10 @@ def big_apart():
 ])
 def test_bad_problem_fields(field, value, status):
     p = prob()
-    setattr(p, field, value)
+    if field == "io_dtype_dk256":
+        p.io_dtype, p.dk, p.alpha_kind = N.GDR_FP32, 256, N.GATE_SCALAR
+    else:
+        setattr(p, field, value)
     assert call(p, **big_apart()) == status
 
 

@@ -358,3 +358,43 @@ def test_decode_grouped_heads(dev):
     torch.cuda.synchronize()
     o = torch.cat(outs, dim=1)
     check(xr, o, S, "erase_then_decay", TOL["bf16"], "grouped decode")
+
+
+# ------------------------------------------------------------------ d_k = 256
+
+
+@pytest.mark.parametrize("kind,DV", [("gdn", 256), ("gdn", 64), ("la", 128), ("mamba2", 256),
+                                     ("deltanet", 64)])
+def test_prefill_dk256(dev, kind, DV):
+    """d_k = 256 (the all-modes kernel with unpadded LDS rows): scalar, no or channel-free gates."""
+    wl = case(kind, B=1, H=2, T=133, D=256, DV=DV, seed=101)
+    say("prefill dk256", kind, DV)
+    x = synth.make_prefill(wl)
+    o, S = run_gpu_prefill(x, dev)
+    torch.cuda.synchronize()
+    check(x, o, S, "erase_then_decay", TOL["bf16"], "dk256 %s dv=%d" % (kind, DV))
+
+
+def test_prefill_dk256_channel_decay_first(dev):
+    """d_k = 256 with a per-channel decay applied before the erase (KDA gates)."""
+    wl = case("kda", B=1, H=2, T=100, D=256, DV=64, seed=102)
+    say("prefill dk256 kda decay first")
+    x = synth.make_prefill(wl)
+    o, S = run_gpu_prefill(x, dev, order="decay_then_erase")
+    torch.cuda.synchronize()
+    check(x, o, S, "decay_then_erase", TOL["bf16"], "dk256 kda decay first")
+
+
+@pytest.mark.parametrize("kind,dtype", [("gdn2", "bf16"), ("gdn", "fp32")])
+def test_decode_dk256(dev, kind, dtype):
+    """One decode step at d_k = d_v = 256 against the oracle's single token from the same state."""
+    import gated_delta_rule_71_amd as gdr
+    from gpu_util import to_dev
+    wl = case(kind, B=3, H=2, T=1, D=256, DV=256, dtype=dtype, s0=0.02, seed=103)
+    say("decode dk256", kind, dtype)
+    x = synth.make_prefill(wl)
+    g = to_dev(x, dev)
+    S = g["S0"].clone()
+    o = gdr.decode_step(g["q"], g["k"], g["v"], g["log_alpha"], g["b"], g["w"], S)
+    torch.cuda.synchronize()
+    check(x, o, S, "erase_then_decay", TOL[dtype], "decode dk256 %s %s" % (kind, dtype))
