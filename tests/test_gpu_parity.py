@@ -266,8 +266,9 @@ def test_scalar_decay_workloads_full(dev, name):
     check(synth.expand_heads(x, wl.H), o, S, "erase_then_decay", TOL["bf16"], "%s full" % name)
 
 
-@pytest.mark.parametrize("name", ["kda", "gdn2", "gla"])
-def test_channel_workloads_sampled(dev, name):
+@pytest.mark.parametrize("name", ["kda", "gdn2", "gla", "gdn_d256"])
+def test_large_workloads_sampled(dev, name):
+    """The per-channel workloads and the d_k = 256 one at full size, eight states checked."""
     wl = synth.WORKLOADS[name]
     say("%s workload (sampled states)" % name, wl)
     x = synth.make_prefill(wl)
