@@ -90,3 +90,35 @@ def test_scalar_gates_are_equal_channels():
             np.testing.assert_allclose(gs[n], gc[n], rtol=1e-12, atol=1e-13, err_msg=n)
         for n in ("dlog_alpha", "db", "dw"):
             np.testing.assert_allclose(gs[n], gc[n].sum(-1), rtol=1e-12, atol=1e-13, err_msg=n)
+
+
+def test_linear_attention_gradients_in_closed_form():
+    """With no decay and no erase the read is o_t = q_t (S_0 + sum_{i<=t} k_i^T v_i) ("Recurrent
+    Memory: Write, Erase, Decay, Read", section 01: write S <- S + k^T v, read o = q S), so with
+    L = <dO, o> + <dS_T, S_T>:
+    dq_t = dO_t (S_0 + sum_{i<=t} k_i^T v_i)^T,  dk_i = sum_{t>=i} (dO_t . v_i) q_t + dS_T v_i^T,
+    dv_i = sum_{t>=i} (q_t . k_i) dO_t + k_i dS_T,  dS0 = dS_T + sum_t q_t^T dO_t,
+    written here with explicit loops, and the write gate w scales v (dw_i = dv_i . v_i)."""
+    rng = np.random.default_rng(21)
+    B, T, H, DK, DV = 1, 6, 1, 3, 4
+    q, k = rng.standard_normal((B, T, H, DK)), rng.standard_normal((B, T, H, DK))
+    v, S0 = rng.standard_normal((B, T, H, DV)), rng.standard_normal((B, H, DK, DV))
+    dO, dST = rng.standard_normal((B, T, H, DV)), rng.standard_normal((B, H, DK, DV))
+    w = np.ones((B, T, H))
+    g = backward(q, k, v, None, None, w, S0, dO, dST, order=0)
+    Q, K, V, D = q[0, :, 0], k[0, :, 0], v[0, :, 0], dO[0, :, 0]
+    s0, dst = S0[0, 0], dST[0, 0]
+    dq, dk, dv, ds0 = np.zeros((T, DK)), np.zeros((T, DK)), np.zeros((T, DV)), dst.copy()
+    for t in range(T):
+        St = s0 + sum(np.outer(K[i], V[i]) for i in range(t + 1))
+        dq[t] = St @ D[t]
+        ds0 += np.outer(Q[t], D[t])
+    for i in range(T):
+        dk[i] = sum((D[t] @ V[i]) * Q[t] for t in range(i, T)) + dst @ V[i]
+        dv[i] = sum((Q[t] @ K[i]) * D[t] for t in range(i, T)) + K[i] @ dst
+    np.testing.assert_allclose(g["dq"][0, :, 0], dq, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(g["dk"][0, :, 0], dk, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(g["dv"][0, :, 0], dv, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(g["dS0"][0, 0], ds0, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(g["dw"][0, :, 0], (dv * V).sum(-1), rtol=1e-12, atol=1e-12)
+    assert g["dlog_alpha"] is None and g["db"] is None
