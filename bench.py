@@ -17,7 +17,8 @@ once) divided by the mean call time from HIP events on the launch stream, agains
 `phases`) from profiles/hbm_counters.txt when that file was recorded on the current kernel
 sources, else null.  `mfma_frac` is algorithmic FLOP per second against the 2.5166 PFLOP/s
 dense bf16 peak.  `decode` reports state GB/s for the decode workload (the
-state is read and written once per step).  `cpu_baseline` times the fp64 oracle on the host.
+state is read and written once per step), and under `copy_reference` the rate of torch's copy
+kernel over the same bytes.  `cpu_baseline` times the fp64 oracle on the host.
 """
 import argparse
 import json
@@ -203,6 +204,27 @@ def time_decode(wl, n_steps, dev):
     return ms
 
 
+def time_copy(nbytes, reps, dev):
+    """GB/s (read + write) of torch's device-to-device copy of an fp32 tensor of `nbytes`: the
+    rate a plain streaming kernel reaches on this GPU, beside the decode step's."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
 def time_backward(wl, steps, warmup, dev):
     """gdr_chunk_bwd on the workload's inputs with a seeded output gradient (dS_T = None), the
     workspace allocated once; mean of `steps` calls between HIP events on the launch stream."""
@@ -379,6 +401,10 @@ def main():
                          "states_per_s": dw.B * dw.H / (ms * 1e-3), "value": gbs, "unit": "GB/s",
                          "hbm_frac": gbs / PEAK_HBM_GBS, "bytes_per_step": db,
                          "traffic": recorded_traffic("decode:decode")}
+        # the same bytes through torch's copy kernel: what a plain streaming kernel reaches
+        cgbs = time_copy(dw.B * dw.H * dw.DK * dw.DV * 4, 20, dev)
+        out["decode"]["copy_reference"] = {"GB/s": cgbs, "bytes": 2 * dw.B * dw.H * dw.DK * dw.DV * 4,
+                                           "decode_over_copy": gbs / cgbs}
     if not args.no_backward and backward_supported(wl):
         out["backward"] = time_backward(wl, args.steps, args.warmup, dev)
     if args.hooks:
