@@ -1,24 +1,27 @@
-"""Benchmark: chunkwise prefill of the Gated DeltaNet workload (B=4, H=16, T=4096, d_k=d_v=128,
-chunk 64, bf16 inputs, fp32 state) and the Gated DeltaNet-2 decode step (256 x 32 states, 1000
-steps), on one MI355X, through the C ABI.
+"""Benchmark: chunkwise prefill of the Gated DeltaNet-2 workload (B=1, H=16, T=32768, d_k=d_v=128,
+chunk 64, per-channel decay, erase gate b and write gate w, bf16 inputs, fp32 state with a nonzero
+S0) as the headline, the KDA and Gated DeltaNet prefills beside it, and the Gated DeltaNet-2 decode
+step (256 x 32 states, 1000 steps), on one MI355X, through the C ABI.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gdn|kda|gdn2|mamba2|gla|gdn_gqa|gdn_d256]
-                    [--decode-steps N] [--no-cpu-baseline] [--no-decode]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gdn2|kda|gdn|mamba2|gla|gdn_gqa|gdn_d256]
+                    [--also kda,gdn] [--decode-steps N] [--no-cpu-baseline] [--no-decode]
 
-Prints ONE JSON line.  `value` is prefill tokens/s (B*T / time per call) with inputs resident in
-HBM; a step is one gdr_chunk_fwd call over the whole batch.  Two input sets alternate between
-calls so that the 256 MB Infinity Cache cannot serve a call from the previous one.
-`roofline` is for one prefill call, which for bf16 inputs is two kernel launches (a chunk-local
-kernel over every chunk, then a per-state kernel that carries the state across chunks through a
-workspace): algorithmic HBM bytes per call (inputs read once, o and S_T written once, S0 read
-once) divided by the mean call time from HIP events on the launch stream, against MI355X's
-8 TB/s.  `phases` splits the call with an event recorded between the two launches
-(gdr_chunk_fwd_marked).  `traffic` is the measured HBM bytes per call (per kernel under
-`phases`) from profiles/hbm_counters.txt when that file was recorded on the current kernel
-sources, else null.  `mfma_frac` is algorithmic FLOP per second against the 2.5166 PFLOP/s
-dense bf16 peak.  `decode` reports state GB/s for the decode workload (the
-state is read and written once per step), and under `copy_reference` the rate of torch's copy
-kernel over the same bytes.  `cpu_baseline` times the fp64 oracle on the host.
+Prints ONE JSON line.  `value` is prefill tokens/s (B*T / time per call) of the headline workload
+with inputs resident in HBM; a step is one gdr_chunk_fwd call over the whole batch.  Two input sets
+alternate between calls so that the 256 MB Infinity Cache cannot serve a call from the previous
+one.  `roofline` is for one prefill call (all of its kernel launches): algorithmic HBM bytes per
+call (inputs read once, o and S_T written once, S0 read once) divided by the mean call time from
+HIP events on the launch stream, against MI355X's 8 TB/s; `flops` gives the same call against the
+2.5166 PFLOP/s dense bf16 matrix-core peak (algorithmic FLOP of the chunk form, triangular products
+at half).  `phases` splits the call with an event recorded after its first launch
+(gdr_chunk_fwd_marked).  `traffic` is the measured HBM bytes per call from
+profiles/hbm_counters.txt when that file was recorded on the current kernel sources, else null.
+`workloads` holds the same figures for the other prefill workloads (`--also`).  `decode` reports
+state GB/s for the decode workload (the state is read and written once per step), and under
+`copy_reference` the rate of torch's copy kernel over the same bytes.  `cpu_baseline` times the
+fp64 oracle on the host: the whole headline workload on the host threads it may use, and one state
+of it on one thread; its outputs also give `parity`, the headline call's errors against the oracle
+on the same inputs (max |o - o_ref| and the largest per-state relative Frobenius error of S_T).
 """
 import argparse
 import json
@@ -171,9 +174,12 @@ def time_prefill(wl, steps, warmup, dev):
     prep = [s.elapsed_time(m) for s, m in zip(starts, mids)]       # chunk-local kernel
     state = [m.elapsed_time(e) for m, e in zip(mids, ends)]        # per-state kernel
     mean = sum(per) / len(per)
+    call(0)  # set 0's outputs for the parity check
+    torch.cuda.synchronize()
     return dict(wall_s=wall, mean_ms=mean, median_ms=per[len(per) // 2], p10_ms=per[len(per) // 10],
                 p90_ms=per[(9 * len(per)) // 10], prep_ms=sum(prep) / len(prep),
-                state_ms=sum(state) / len(state), workspace_bytes=need)
+                state_ms=sum(state) / len(state), workspace_bytes=need,
+                o=outs[0], S_T=S_T[0])
 
 
 def time_decode(wl, n_steps, dev):
@@ -294,16 +300,7 @@ def time_hooks(wl, dev, positions=64, reps=5):
             "contributions_per_s": positions * wl.H / (ms * 1e-3)}
 
 
-def cpu_baseline(wl):
-    """The fp64 oracle, as it stands, on the host cores, on the whole prefill workload."""
-    import oracle
-    import synth
-    cores = len(os.sched_getaffinity(0))
-    threads = min(cores, 16)
-    x = synth.expand_heads(synth.make_prefill(wl), wl.H)
-    t0 = time.perf_counter()
-    oracle.forward(x["q"], x["k"], x["v"], x["log_alpha"], x["b"], x["w"], x["S0"], n_threads=threads)
-    dt = time.perf_counter() - t0
+def host_cpu():
     model = ""
     try:
         for line in open("/proc/cpuinfo"):
@@ -312,9 +309,84 @@ def cpu_baseline(wl):
                 break
     except OSError:
         pass
-    return {"value": wl.B * wl.T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": "whole %s workload (B=%d, H=%d, T=%d), fp64 recurrence, %.1f s wall on %s"
-                      % (wl.name, wl.B, wl.H, wl.T, dt, model or "host")}
+    return model or "host"
+
+
+def cpu_baseline(wl, pf):
+    """The fp64 oracle, as it stands, on the host: the whole workload on as many threads as this
+    process may use (at most 16, the host share of one GPU), and one (batch, head) state of it on
+    one thread.  Its outputs on input set 0 check the GPU call's outputs (`parity`)."""
+    import numpy as np
+    import oracle
+    import synth
+    host_cores = len(os.sched_getaffinity(0))
+    threads = min(host_cores, 16)
+    x = synth.expand_heads(synth.make_prefill(wl), wl.H)
+    t0 = time.perf_counter()
+    o_ref, S_ref = oracle.forward(x["q"], x["k"], x["v"], x["log_alpha"], x["b"], x["w"], x["S0"],
+                                  n_threads=threads)
+    dt = time.perf_counter() - t0
+    one = {n: (None if t is None else (t[:1, :1] if n == "S0" else t[:1, :, :1])) for n, t in x.items()}
+    t1 = time.perf_counter()
+    oracle.forward(one["q"], one["k"], one["v"], one["log_alpha"], one["b"], one["w"], one["S0"],
+                   n_threads=1)
+    dt1 = time.perf_counter() - t1
+    o = pf["o"].float().cpu().numpy().astype(np.float64)
+    S = pf["S_T"].cpu().numpy().astype(np.float64)
+    n = wl.B * wl.H
+    rel = (np.linalg.norm((S - S_ref).reshape(n, -1), axis=1) /
+           np.linalg.norm(S_ref.reshape(n, -1), axis=1)).max()
+    parity = {"max_abs_o": float(np.abs(o - o_ref).max()), "max_rel_frobenius_S_T": float(rel),
+              "tolerance": {"o": 2e-2, "S_T": 1e-2}, "states": n, "tokens": wl.B * wl.T,
+              "reference": "fp64 oracle on the same (bf16-rounded) inputs"}
+    base = {"value": wl.B * wl.T / dt, "unit": "tokens/s", "cores": threads, "host_cores": host_cores,
+            "kind": "oracle",
+            "sample": "whole %s workload (B=%d, H=%d, T=%d), fp64 recurrence on %d threads, %.1f s wall "
+                      "on %s" % (wl.name, wl.B, wl.H, wl.T, threads, dt, host_cpu()),
+            "one_core": {"value": wl.T / dt1, "unit": "tokens/s of one state (head-tokens/s)",
+                         "sample": "one state of %s (T=%d), 1 thread, %.1f s wall" % (wl.name, wl.T, dt1)}}
+    return base, parity
+
+
+def prefill_report(wl, pf):
+    """Throughput and rooflines of one prefill call of workload `wl` from time_prefill's result."""
+    two = wl.alpha == "channel"  # erase-then-decay with a per-channel decay: two key families
+    sec = pf["mean_ms"] * 1e-3
+    flops = flops_per_head_token(wl.DK, 64, two, wl.b != "none") * wl.B * wl.T * wl.H
+    nbytes = prefill_bytes(wl)
+    gbs = nbytes / sec / 1e9
+    tf = flops / sec / 1e12
+    return {
+        "tokens_per_s": wl.B * wl.T / sec,
+        "ms": pf["mean_ms"],
+        "kernel_ms": {"mean": pf["mean_ms"], "median": pf["median_ms"], "p10": pf["p10_ms"],
+                      "p90": pf["p90_ms"]},
+        "config": {"workload": wl.name, "batch": wl.B, "heads": wl.H, "qk_heads": wl.HK or wl.H,
+                   "seq_len": wl.T, "d_k": wl.DK, "d_v": wl.DV, "chunk": 64, "state": "fp32",
+                   "decay": wl.alpha, "erase_gate": wl.b, "write_gate": wl.w, "seed": wl.seed,
+                   "S0": "N(0, %g^2)" % wl.s0_std if wl.s0_std > 0 else "zero"},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": gbs / PEAK_HBM_GBS, "traffic": recorded_traffic("prefill:" + wl.name),
+                     "algorithmic_bytes": nbytes,
+                     "scope": "one gdr_chunk_fwd call (all of its kernel launches)"},
+        "flops": {"achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": tf / PEAK_BF16_TFLOPS,
+                  "algorithmic_flop": flops},
+        "phases": {"first_launch_ms": pf["prep_ms"], "rest_ms": pf["state_ms"],
+                   "traffic_first": recorded_traffic("prefill_prep:" + wl.name),
+                   "traffic_rest": recorded_traffic("prefill_state:" + wl.name)},
+        "workspace_bytes": pf["workspace_bytes"],
+    }
+
+
+def device_identity(dev):
+    import torch
+    p = torch.cuda.get_device_properties(dev)
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", ""), "cus": p.multi_processor_count,
+            "hbm_bytes": p.total_memory, "hip": torch.version.hip, "torch": torch.__version__}
+
+
+def progress(msg):
+    print("bench: " + msg, file=sys.stderr, flush=True)
 
 
 def main():
@@ -322,7 +394,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="gdn", choices=["gdn", "kda", "gdn2", "mamba2", "gla", "gdn_gqa", "gdn_d256"])
+    ap.add_argument("--workload", default="gdn2",
+                    choices=["gdn2", "kda", "gdn", "mamba2", "gla", "gdn_gqa", "gdn_d256"])
+    ap.add_argument("--also", default="kda,gdn",
+                    help="comma-separated prefill workloads timed beside the headline one ('' for none)")
     ap.add_argument("--decode-steps", type=int, default=None)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -351,16 +426,12 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     wl = synth.WORKLOADS[args.workload]
-    two = wl.alpha == "channel"  # erase-then-decay with a per-channel decay: two key families
     pf = time_prefill(wl, args.steps, args.warmup, dev)
-    tokens = wl.B * wl.T
-    sec = pf["mean_ms"] * 1e-3
-    flops = flops_per_head_token(wl.DK, 64, two, wl.b != "none") * wl.B * wl.T * wl.H
-    nbytes = prefill_bytes(wl)
-    achieved_gbs = nbytes / sec / 1e9
+    rep = prefill_report(wl, pf)
+    progress("%s prefill %.4f ms" % (wl.name, pf["mean_ms"]))
     out = {
         "metric": METRIC,
-        "value": tokens / sec,
+        "value": rep["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -371,29 +442,31 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded; shapes of the %s workload)" % wl.name,
-        "config": {"workload": wl.name, "batch": wl.B, "heads": wl.H, "qk_heads": wl.HK or wl.H,
-                   "seq_len": wl.T,
-                   "d_k": wl.DK, "d_v": wl.DV, "chunk": 64, "state": "fp32",
-                   "decay": wl.alpha, "erase_gate": wl.b, "write_gate": wl.w},
-        "kernel_ms": {"mean": pf["mean_ms"], "median": pf["median_ms"], "p10": pf["p10_ms"],
-                      "p90": pf["p90_ms"]},
-        "mfma_frac": flops / sec / (PEAK_BF16_TFLOPS * 1e12),
-        "tflops": flops / sec / 1e12,
-        "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": achieved_gbs / PEAK_HBM_GBS,
-                     "traffic": recorded_traffic("prefill:" + wl.name),
-                     "algorithmic_bytes": nbytes,
-                     "scope": "one gdr_chunk_fwd call: chunk-local kernel then per-state kernel"},
-        "phases": {"chunk_local": {"ms": pf["prep_ms"],
-                                   "traffic": recorded_traffic("prefill_prep:" + wl.name)},
-                   "state": {"ms": pf["state_ms"],
-                             "traffic": recorded_traffic("prefill_state:" + wl.name)}},
-        "workspace_bytes": pf["workspace_bytes"],
+        "config": rep["config"],
+        "kernel_ms": rep["kernel_ms"],
+        "mfma_frac": rep["flops"]["frac"],
+        "tflops": rep["flops"]["achieved"],
+        "roofline": rep["roofline"],
+        "flops": rep["flops"],
+        "phases": rep["phases"],
+        "workspace_bytes": rep["workspace_bytes"],
+        "device": device_identity(dev),
     }
+    extra = [n for n in args.also.split(",") if n and n != wl.name]
+    if extra:
+        out["workloads"] = {}
+        for name in extra:
+            w2 = synth.WORKLOADS[name]
+            p2 = time_prefill(w2, args.steps, args.warmup, dev)
+            r2 = prefill_report(w2, p2)
+            progress("%s prefill %.4f ms" % (name, p2["mean_ms"]))
+            del p2
+            out["workloads"][name] = r2
     if not args.no_decode:
         dw = synth.WORKLOADS["decode"]
         n = args.decode_steps or dw.steps
         ms = time_decode(dw, n, dev)
+        progress("decode %.1f us per step" % (ms * 1e3))
         db = decode_bytes(dw)
         gbs = db / (ms * 1e-3) / 1e9
         out["decode"] = {"workload": "decode", "batch": dw.B, "heads": dw.H, "d_k": dw.DK,
@@ -405,12 +478,18 @@ def main():
         cgbs = time_copy(dw.B * dw.H * dw.DK * dw.DV * 4, 20, dev)
         out["decode"]["copy_reference"] = {"GB/s": cgbs, "bytes": 2 * dw.B * dw.H * dw.DK * dw.DV * 4,
                                            "decode_over_copy": gbs / cgbs}
-    if not args.no_backward and backward_supported(wl):
-        out["backward"] = time_backward(wl, args.steps, args.warmup, dev)
+    if not args.no_backward:
+        # the first of the timed prefill workloads that the backward covers (a scalar or no decay)
+        bw = next((w for w in [wl] + [synth.WORKLOADS[n] for n in extra] if backward_supported(w)), None)
+        if bw is not None:
+            out["backward"] = time_backward(bw, args.steps, args.warmup, dev)
+            out["backward"]["workload"] = bw.name
+            progress("%s backward %.4f ms" % (bw.name, out["backward"]["ms"]))
     if args.hooks:
         out["hooks"] = time_hooks(wl, dev)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl)
+        out["cpu_baseline"], out["parity"] = cpu_baseline(wl, pf)
+        progress("oracle done: parity %s" % json.dumps(out["parity"]))
     print(json.dumps(out), flush=True)
 
 

@@ -65,6 +65,38 @@ def _check_contig(**tensors):
             raise ValueError("%s must be contiguous" % name)
 
 
+def _check_buffer(name, t, shape, dtype, device):
+    """A caller-supplied tensor the kernels read or write through a raw pointer: it must have
+    exactly this shape, dtype and device and be contiguous, or the kernels would touch memory
+    outside it (or a host address)."""
+    if t is None:
+        return
+    if t.device != device:
+        raise ValueError("%s is on %s; expected %s" % (name, t.device, device))
+    if t.dtype != dtype:
+        raise TypeError("%s has dtype %s; expected %s" % (name, t.dtype, dtype))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s; expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _check_workspace(workspace, need, device):
+    if workspace is None:
+        return
+    if workspace.device != device:
+        raise ValueError("workspace is on %s; expected %s" % (workspace.device, device))
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    if workspace.numel() * workspace.element_size() < need:
+        raise ValueError("workspace must be a device tensor of at least %d bytes" % need)
+
+
+def _require_gpu(dev):
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on a GPU (got %s)" % dev)
+
+
 def _stream(device):
     torch = _torch()
     return torch.cuda.current_stream(device).cuda_stream
@@ -83,34 +115,35 @@ def chunk_fwd(q, k, v, log_alpha=None, b=None, w=None, S0=None, order="erase_the
     B, T, HQ, DK = q.shape
     H, DV = v.shape[2], v.shape[-1]
     dt, dev = q.dtype, q.device
-    if k.shape != q.shape or tuple(v.shape[:2]) != (B, T) or HQ == 0 or H % HQ != 0:
+    if k.shape != q.shape or v.dim() != 4 or tuple(v.shape[:2]) != (B, T) or HQ == 0 or H % HQ != 0:
         raise ValueError("shape mismatch: q %s k %s v %s (v heads must be a multiple of q / k "
                          "heads)" % (tuple(q.shape), tuple(k.shape), tuple(v.shape)))
     if k.dtype != dt or v.dtype != dt or k.device != dev or v.device != dev:
         raise TypeError("q, k, v must share dtype and device")
-    if dev.type != "cuda":
-        raise ValueError("tensors must live on a GPU")
+    _io_dtype(q)
+    if order not in _ORDERS:
+        raise ValueError("order must be one of %s" % sorted(_ORDERS))
     ak = _gate_kind(log_alpha, B, T, H, DK, "log_alpha", dt, dev)
     bk = _gate_kind(b, B, T, H, DK, "b", dt, dev)
     wk = _gate_kind(w, B, T, H, DV, "w", dt, dev)
-    _check_contig(q=q, k=k, v=v, log_alpha=log_alpha, b=b, w=w, S0=S0, out=out)
-    if S0 is not None and (S0.dtype != torch.float32 or tuple(S0.shape) != (B, H, DK, DV)):
-        raise ValueError("S0 must be float32 [B,H,dk,dv]")
-    o = out if out is not None else torch.empty((B, T, H, DV), dtype=dt, device=dev)
-    if final_state is True:
-        S_T = torch.empty((B, H, DK, DV), dtype=torch.float32, device=dev)
-    elif final_state is False or final_state is None:
+    _check_contig(q=q, k=k, v=v, log_alpha=log_alpha, b=b, w=w)
+    _check_buffer("S0", S0, (B, H, DK, DV), torch.float32, dev)
+    _check_buffer("out", out, (B, T, H, DV), dt, dev)
+    if final_state is True or final_state is False or final_state is None:
         S_T = None
     else:
+        _check_buffer("final_state", final_state, (B, H, DK, DV), torch.float32, dev)
         S_T = final_state
-        _check_contig(final_state=S_T)
     prob = make_problem(B, H, T, DK, DV, _io_dtype(q), ak, bk, wk, _ORDERS[order],
                         qk_heads=0 if HQ == H else HQ)
     need = _native.workspace_bytes(prob)
+    _check_workspace(workspace, need, dev)
+    _require_gpu(dev)
+    o = out if out is not None else torch.empty((B, T, H, DV), dtype=dt, device=dev)
+    if final_state is True:
+        S_T = torch.empty((B, H, DK, DV), dtype=torch.float32, device=dev)
     if workspace is None:
         workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev) if need else None
-    elif workspace.device != dev or workspace.numel() * workspace.element_size() < need:
-        raise ValueError("workspace must be a device tensor of at least %d bytes" % need)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if phase_event is None:
         rc = _native.chunk_fwd_raw(prob, _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b),
@@ -135,33 +168,35 @@ def chunk_bwd(q, k, v, log_alpha=None, b=None, w=None, S0=None, do=None, dS_T=No
     (q's dtype), dlog_alpha, db, dw (shaped like the gates; None for an absent gate) and dS0
     (float32).  With one shared beta passed as both b and w, its gradient is db + dw.  With
     grouped q / k heads, dq and dk are summed over the value heads that share them.  Raises
-    GdrError(GDR_ERR_UNSUPPORTED) outside bf16 with a scalar or no decay and dv <= 256."""
+    GdrError(GDR_ERR_UNSUPPORTED) outside bf16 with a scalar or no decay, dk in {32, 64, 128}
+    and dv <= 256."""
     torch = _torch()
     B, T, HQ, DK = q.shape
     H, DV = v.shape[2], v.shape[-1]
     dt, dev = q.dtype, q.device
-    if k.shape != q.shape or tuple(v.shape[:2]) != (B, T) or HQ == 0 or H % HQ != 0:
+    if k.shape != q.shape or v.dim() != 4 or tuple(v.shape[:2]) != (B, T) or HQ == 0 or H % HQ != 0:
         raise ValueError("shape mismatch: q %s k %s v %s" % (tuple(q.shape), tuple(k.shape), tuple(v.shape)))
     if k.dtype != dt or v.dtype != dt or k.device != dev or v.device != dev:
         raise TypeError("q, k, v must share dtype and device")
-    if dev.type != "cuda":
-        raise ValueError("tensors must live on a GPU")
-    if do is None or tuple(do.shape) != tuple(v.shape) or do.dtype != dt or do.device != dev:
-        raise ValueError("do must be %s like v %s" % (dt, tuple(v.shape)))
+    _io_dtype(q)
+    if order not in _ORDERS:
+        raise ValueError("order must be one of %s" % sorted(_ORDERS))
+    if do is None:
+        raise ValueError("chunk_bwd needs do, the gradient of o")
+    _check_buffer("do", do, tuple(v.shape), dt, dev)
     ak = _gate_kind(log_alpha, B, T, H, DK, "log_alpha", dt, dev)
     bk = _gate_kind(b, B, T, H, DK, "b", dt, dev)
     wk = _gate_kind(w, B, T, H, DV, "w", dt, dev)
-    _check_contig(q=q, k=k, v=v, log_alpha=log_alpha, b=b, w=w, S0=S0, do=do, dS_T=dS_T)
-    for name, st in (("S0", S0), ("dS_T", dS_T)):
-        if st is not None and (st.dtype != torch.float32 or tuple(st.shape) != (B, H, DK, DV)):
-            raise ValueError("%s must be float32 [B,H,dk,dv]" % name)
+    _check_contig(q=q, k=k, v=v, log_alpha=log_alpha, b=b, w=w)
+    _check_buffer("S0", S0, (B, H, DK, DV), torch.float32, dev)
+    _check_buffer("dS_T", dS_T, (B, H, DK, DV), torch.float32, dev)
     prob = make_problem(B, H, T, DK, DV, _io_dtype(q), ak, bk, wk, _ORDERS[order],
                         qk_heads=0 if HQ == H else HQ)
     need = _native.bwd_workspace_bytes(prob)
+    _check_workspace(workspace, need, dev)
+    _require_gpu(dev)
     if workspace is None:
         workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
-    elif workspace.device != dev or workspace.numel() * workspace.element_size() < need:
-        raise ValueError("workspace must be a device tensor of at least %d bytes" % need)
     like = lambda x: None if x is None else torch.empty_like(x)
     g = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
          "dlog_alpha": like(log_alpha), "db": like(b), "dw": like(w),
@@ -199,16 +234,20 @@ def decode_step(q, k, v, log_alpha=None, b=None, w=None, S=None, order="erase_th
     if T != 1:
         raise ValueError("decode_step takes one token per sequence (T = 1)")
     dt, dev = q.dtype, q.device
-    if k.shape != q.shape or tuple(v.shape[:2]) != (B, 1) or HQ == 0 or H % HQ != 0:
+    if k.shape != q.shape or v.dim() != 4 or tuple(v.shape[:2]) != (B, 1) or HQ == 0 or H % HQ != 0:
         raise ValueError("shape mismatch (v heads must be a multiple of q / k heads)")
-    if k.dtype != dt or v.dtype != dt:
-        raise TypeError("q, k, v must share a dtype")
+    if k.dtype != dt or v.dtype != dt or k.device != dev or v.device != dev:
+        raise TypeError("q, k, v must share dtype and device")
+    _io_dtype(q)
+    if order not in _ORDERS:
+        raise ValueError("order must be one of %s" % sorted(_ORDERS))
     ak = _gate_kind(log_alpha, B, 1, H, DK, "log_alpha", dt, dev)
     bk = _gate_kind(b, B, 1, H, DK, "b", dt, dev)
     wk = _gate_kind(w, B, 1, H, DV, "w", dt, dev)
-    _check_contig(q=q, k=k, v=v, log_alpha=log_alpha, b=b, w=w, S=S, out=out)
-    if S.dtype != torch.float32 or tuple(S.shape) != (B, H, DK, DV):
-        raise ValueError("S must be float32 [B,H,dk,dv]")
+    _check_contig(q=q, k=k, v=v, log_alpha=log_alpha, b=b, w=w)
+    _check_buffer("S", S, (B, H, DK, DV), torch.float32, dev)
+    _check_buffer("out", out, (B, 1, H, DV), dt, dev)
+    _require_gpu(dev)
     o = out if out is not None else torch.empty((B, 1, H, DV), dtype=dt, device=dev)
     prob = make_problem(B, H, 1, DK, DV, _io_dtype(q), ak, bk, wk, _ORDERS[order],
                         qk_heads=0 if HQ == H else HQ)

@@ -1,13 +1,8 @@
 // Host entry for the chunkwise prefill: picks the kernel variant for a problem.
-#include <stdlib.h>
-#include <string.h>
-
 #include "prefill_dispatch.h"
 
 namespace gdr {
 
-bool prefill_scalar_ok(int64_t T, int64_t H, int64_t DK, int64_t DV, int b_kind);
-hipError_t prefill_scalar_launch(PrefillArgs<bf16_t> a, int64_t nstate, int64_t DK, hipStream_t s);
 bool prefill_wy_ok(int64_t DK, int64_t DV, int b_kind);
 size_t prefill_wy_workspace_bytes(int64_t nstate, int64_t T, int64_t DK, int64_t DV);
 hipError_t prefill_wy_launch(const PrefillArgs<bf16_t>& p, int64_t nstate, int64_t DK,
@@ -16,20 +11,11 @@ bool prefill_wyc_ok(int64_t DK, int64_t DV);
 size_t prefill_wyc_workspace_bytes(int64_t nstate, int64_t T, int64_t DK, int64_t DV, bool two);
 hipError_t prefill_wyc_launch(const PrefillArgs<bf16_t>& p, int64_t nstate, int64_t DK, bool two,
                               void* workspace, hipEvent_t mark, hipStream_t s);
+template <typename IO>
+hipError_t prefill_recur(const PrefillArgs<IO>& a, int64_t nstate, int64_t DK, bool decay_first,
+                         hipStream_t s);
 
 namespace {
-
-// Kernel family for bf16 problems: "wy" (default: chunk-local kernel + state kernel through a
-// workspace), "fused" (one pipelined kernel per problem, no workspace: the scalar-decay kernel or
-// the all-modes kernel) or "generic" (the all-modes kernel).  Set through GDR_PREFILL_IMPL for
-// comparisons.
-enum class ScalarImpl { kWy, kFused, kGeneric };
-ScalarImpl scalar_impl() {
-  const char* e = getenv("GDR_PREFILL_IMPL");
-  if (e && strcmp(e, "fused") == 0) return ScalarImpl::kFused;
-  if (e && strcmp(e, "generic") == 0) return ScalarImpl::kGeneric;
-  return ScalarImpl::kWy;
-}
 
 // MODE 0: scalar (or no) decay; 1: per-channel decay applied before the erase;
 // 2: per-channel decay applied after the erase (the unified equation's order).
@@ -50,15 +36,10 @@ bool fits_dk(int64_t DK, int mode, int nsw) {
   }
 }
 
-// State waves per workgroup for bf16: the widest slice (4, 2 or 1 x 16 columns) that
-// divides dv and fits in LDS, capped by GDR_PREFILL_NSW when that is set (tuning).
+// State waves per workgroup for bf16: the widest slice (2 or 1 x 16 columns) that divides dv
+// and fits in LDS.
 int choose_nsw_bf16(int64_t DK, int64_t DV, int mode) {
-  int cap = 2;
-  if (const char* e = getenv("GDR_PREFILL_NSW")) {
-    const int v = atoi(e);
-    if (v == 1 || v == 2 || v == 4) cap = v;
-  }
-  for (int nsw = cap; nsw >= 1; nsw /= 2)
+  for (int nsw = 2; nsw >= 1; nsw /= 2)
     if (DV % (16 * nsw) == 0 && fits_dk<__bf16>(DK, mode, nsw)) return nsw;
   return 0;
 }
@@ -72,15 +53,21 @@ hipError_t record_mark(hipEvent_t mark, hipStream_t stream) {
 
 size_t prefill_workspace_bytes(int io_dtype, int64_t nstate, int64_t T, int64_t DK, int64_t DV,
                                int alpha_kind, int b_kind, bool decay_first) {
-  if (io_dtype != 0 || scalar_impl() != ScalarImpl::kWy) return 0;
+  if (io_dtype != 0) return 0;
   if (alpha_kind != kChannel)
     return prefill_wy_ok(DK, DV, b_kind) ? prefill_wy_workspace_bytes(nstate, T, DK, DV) : 0;
   return prefill_wyc_ok(DK, DV) ? prefill_wyc_workspace_bytes(nstate, T, DK, DV, !decay_first) : 0;
 }
 
+// Every validated shape runs: the chunkwise kernels where their LDS layout fits, else the token
+// recurrence (dk >= 64 only; dk 16 and 32 always fit).
 bool prefill_supported(int io_dtype, int64_t DK, int64_t DV, int alpha_kind, bool decay_first) {
-  const int mode = prefill_mode(alpha_kind, decay_first);
   if (DV % 16 != 0) return false;
+  return DK == 16 || DK == 32 || DK == 64 || DK == 128 || DK == 256;
+}
+
+// Whether the chunkwise all-modes kernel fits this problem (else the token recurrence runs).
+bool chunk_kernel_fits(int io_dtype, int64_t DK, int64_t DV, int mode) {
   if (io_dtype == 0) return choose_nsw_bf16(DK, DV, mode) > 0;
   return fits_dk<float>(DK, mode, 1);
 }
@@ -96,19 +83,13 @@ hipError_t launch_prefill(const IO* q, const IO* k, const IO* v, const IO* la, c
   const int64_t nstate = B * H;
   if constexpr (sizeof(IO) == 2) {
     if (mode == 0) {
-      const ScalarImpl impl = scalar_impl();
-      if (impl == ScalarImpl::kWy && prefill_wy_ok(DK, DV, b_kind))
-        return prefill_wy_launch(a, nstate, DK, workspace, mark, stream);
-      if (impl == ScalarImpl::kFused && Hk == H && prefill_scalar_ok(T, H, DK, DV, b_kind)) {
-        if (const hipError_t e = record_mark(mark, stream); e != hipSuccess) return e;
-        return prefill_scalar_launch(a, nstate, DK, stream);
-      }
-    } else if (scalar_impl() == ScalarImpl::kWy && prefill_wyc_ok(DK, DV)) {
+      if (prefill_wy_ok(DK, DV, b_kind)) return prefill_wy_launch(a, nstate, DK, workspace, mark, stream);
+    } else if (prefill_wyc_ok(DK, DV)) {
       return prefill_wyc_launch(a, nstate, DK, mode == 2, workspace, mark, stream);
     }
     const int nsw = choose_nsw_bf16(DK, DV, mode);
-    if (nsw == 0) return hipErrorInvalidValue;
     if (const hipError_t e = record_mark(mark, stream); e != hipSuccess) return e;
+    if (nsw == 0) return prefill_recur(a, nstate, DK, decay_first, stream);
     a.nsl = static_cast<int>(DV / (16 * nsw));
     switch (DK) {
       case 16: return prefill_bf16_dk16(a, nstate, mode, nsw, stream);
@@ -118,8 +99,8 @@ hipError_t launch_prefill(const IO* q, const IO* k, const IO* v, const IO* la, c
       default: return prefill_bf16_dk256(a, nstate, mode, nsw, stream);
     }
   } else {
-    if (!fits_dk<float>(DK, mode, 1)) return hipErrorInvalidValue;
     if (const hipError_t e = record_mark(mark, stream); e != hipSuccess) return e;
+    if (!fits_dk<float>(DK, mode, 1)) return prefill_recur(a, nstate, DK, decay_first, stream);
     a.nsl = static_cast<int>(DV / 16);
     return prefill_f32_any(a, nstate, DK, mode, 1, stream);
   }

@@ -19,7 +19,6 @@
 #include "gdr_common.h"
 #include "mfma.h"
 #include "prefill_kernel.h"
-#include "prefill_scalar.h"
 
 // Phase markers: no-ops unless a profiling build defines them.
 #ifndef GDR_PMARK
@@ -30,6 +29,89 @@
 #endif
 
 namespace gdr {
+
+// Gram tiles of one key wave: row blocks RA and RB (16 rows each) of `rows` (k or q) against
+// the 16-row column blocks of k at or below them.  prod 0: A = beta_t k_t . k_i e^{G_t - G_i}
+// for i < t (off-diagonal blocks to gA as -A, diagonal blocks to Ld in fp32); prod 1:
+// M = q_t . k_i e^{G_t - G_i} for i <= t, stored as -M.  All fragments are read before the
+// first MFMA.
+template <int DK, int RA, int RB, int LDT, int LDD, int LDA, int LDL>
+__device__ __forceinline__ void scalar_gram_pair(const __bf16* rows, const __bf16* tK, int prod,
+                                                 int g, int l16, const float* sc, __bf16* gA,
+                                                 __bf16* gM, float* Ld) {
+  using MM = Mma<__bf16>;
+  using F8 = MM::F8;
+  constexpr int C = 64, NKB = DK / 32, NT = RA + RB + 2;
+  auto tile_a = [](int j) { return j <= RA ? RA : RB; };
+  auto tile_b = [](int j) { return j <= RA ? j : j - RA - 1; };
+  // Tiles are computed transposed (k block as the A operand) so that each lane ends up with four
+  // consecutive columns of one output row: one 8-byte store.  The diagonal tiles of A are
+  // computed upright and stored column-major in fp32 for the inverse.
+  auto diag_a = [&](int j) { return prod == 0 && tile_a(j) == tile_b(j); };
+  auto epilogue = [&](int j, const f32x4& acc) {
+    const int ta = tile_a(j), tb = tile_b(j);
+    if (diag_a(j)) {
+      const int cc = 16 * tb + l16;
+      const float gc = sc[cc];
+      const float4 gr4 = *reinterpret_cast<const float4*>(sc + 16 * ta + 4 * g);
+      const float4 br4 = *reinterpret_cast<const float4*>(sc + 3 * C + 16 * ta + 4 * g);
+      const float gr[4] = {gr4.x, gr4.y, gr4.z, gr4.w}, br[4] = {br4.x, br4.y, br4.z, br4.w};
+      float4 o;
+      float* ov = reinterpret_cast<float*>(&o);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * ta + 4 * g + i;
+        ov[i] = cc < r ? acc[i] * __expf(fminf(gr[i] - gc, 0.f)) * br[i] : 0.f;
+      }
+      *reinterpret_cast<float4*>(Ld + (ta * 16 + l16) * LDL + 4 * g) = o;  // column l16, rows 4g..
+      return;
+    }
+    const int r = 16 * ta + l16, cc0 = 16 * tb + 4 * g;
+    const float gr = sc[r], br = prod == 0 ? sc[3 * C + r] : 1.f;
+    const float4 gc4 = *reinterpret_cast<const float4*>(sc + cc0);
+    const float gc[4] = {gc4.x, gc4.y, gc4.z, gc4.w};
+    bf16x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int cc = cc0 + i;
+      const bool keep = prod == 0 ? (cc < r) : (cc <= r);
+      o[i] = static_cast<__bf16>(keep ? -acc[i] * __expf(fminf(gr - gc[i], 0.f)) * br : 0.f);
+    }
+    // one 8-byte store: the pitches are multiples of four elements and the arrays 16-byte aligned
+    __bf16* dst = prod == 1 ? gM + r * LDD + cc0 : gA + (r - 16) * LDA + cc0;
+    *reinterpret_cast<bf16x4*>(dst) = o;
+  };
+  F8 rf[NKB], cb[2][NKB];
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) {
+    rf[kb] = lds_load8(rows + (16 * RA + l16) * LDT + 32 * kb + 8 * g);
+    cb[0][kb] = lds_load8(tK + l16 * LDT + 32 * kb + 8 * g);
+  }
+  f32x4 acc[2];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    if (j == RA + 1) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) rf[kb] = lds_load8(rows + (16 * RB + l16) * LDT + 32 * kb + 8 * g);
+    }
+    if (j + 1 < NT) {
+      const int nb = tile_b(j + 1);
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+        cb[(j + 1) & 1][kb] = lds_load8(tK + (16 * nb + l16) * LDT + 32 * kb + 8 * g);
+    }
+    acc[j & 1] = zero4();
+    if (diag_a(j)) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) acc[j & 1] = MM::mma8(rf[kb], cb[j & 1][kb], acc[j & 1]);
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) acc[j & 1] = MM::mma8(cb[j & 1][kb], rf[kb], acc[j & 1]);
+    }
+    if (j > 0) epilogue(j - 1, acc[(j - 1) & 1]);
+  }
+  epilogue(NT - 1, acc[(NT - 1) & 1]);
+}
 
 struct WyArgs {
   const bf16_t* q;

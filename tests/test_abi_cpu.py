@@ -69,8 +69,7 @@ def big_apart():
     ("batch", -1, N.GDR_ERR_INVALID_ARGUMENT),
     ("seqlen", -5, N.GDR_ERR_INVALID_ARGUMENT),
     ("dk", 96, N.GDR_ERR_UNSUPPORTED),
-    ("dk", 256, N.GDR_ERR_UNSUPPORTED),  # per-channel decay after the erase does not fit at dk 256
-    ("io_dtype_dk256", None, N.GDR_ERR_UNSUPPORTED),  # fp32 at dk 256
+    ("dk", 48, N.GDR_ERR_UNSUPPORTED),
     ("dk", 0, N.GDR_ERR_INVALID_ARGUMENT),
     ("dv", 40, N.GDR_ERR_UNSUPPORTED),
     ("dv", 512, N.GDR_ERR_UNSUPPORTED),
@@ -78,10 +77,7 @@ def big_apart():
 ])
 def test_bad_problem_fields(field, value, status):
     p = prob()
-    if field == "io_dtype_dk256":
-        p.io_dtype, p.dk, p.alpha_kind = N.GDR_FP32, 256, N.GATE_SCALAR
-    else:
-        setattr(p, field, value)
+    setattr(p, field, value)
     assert call(p, **big_apart()) == status
 
 
@@ -237,3 +233,72 @@ def test_backward_workspace_and_validation():
     assert bwd_call(sp, ws, need, dS0=bwd_ptrs()["dS_T"]) == N.GDR_ERR_INVALID_ARGUMENT
     # nothing to do
     assert bwd_call(prob(alpha_kind=N.GATE_SCALAR, batch=0)) == N.GDR_OK
+
+
+def test_binding_checks_every_buffer_before_any_gpu_call():
+    """Caller buffers reach the kernels as raw pointers, so the binding checks the shape, dtype,
+    device and contiguity of each one (out, final_state, S0, the workspace, decode's S and out,
+    the backward's do, S0 and dS_T) before anything touches the GPU; the GPU requirement itself is
+    checked last.  Host tensors stand in for device ones here, a `meta` tensor for one on another
+    device."""
+    import torch
+    import gated_delta_rule_71_amd as gdr
+    bf, f32 = torch.bfloat16, torch.float32
+    B, T, H, D = 1, 4, 2, 16
+    q = torch.zeros(B, T, H, D, dtype=bf)
+    S = torch.zeros(B, H, D, D, dtype=f32)
+    meta = lambda t: torch.empty(t.shape, dtype=t.dtype, device="meta")
+    fwd = lambda **kw: gdr.chunk_fwd(q, q, q, **kw)
+    # everything well formed: the only objection left is the host device
+    with pytest.raises(ValueError, match="GPU"):
+        fwd(S0=S, out=torch.empty_like(q), final_state=S.clone())
+    bad = [
+        (ValueError, dict(out=torch.empty(B, T, H, D + 16, dtype=bf))),
+        (TypeError, dict(out=torch.empty_like(q, dtype=f32))),
+        (ValueError, dict(out=meta(q))),
+        (ValueError, dict(out=torch.empty(B, H, T, D, dtype=bf).transpose(1, 2))),
+        (ValueError, dict(final_state=torch.zeros(B, H, D, D + 16, dtype=f32))),
+        (TypeError, dict(final_state=torch.zeros(B, H, D, D, dtype=bf))),
+        (ValueError, dict(final_state=meta(S))),
+        (ValueError, dict(S0=meta(S))),
+        (TypeError, dict(S0=S.to(bf))),
+        (ValueError, dict(S0=torch.zeros(B, H, D, 2 * D, dtype=f32)[..., ::2])),
+        (ValueError, dict(order="backwards")),
+    ]
+    for exc, kw in bad:
+        with pytest.raises(exc):
+            fwd(**kw)
+    # a workspace on another device, or smaller than the problem needs
+    qb = torch.zeros(1, 70, 3, 128, dtype=bf)
+    la = torch.zeros(1, 70, 3, dtype=bf)
+    need = gdr.workspace_bytes(qb, qb, la, la, la)
+    assert need > 0
+    run = lambda ws: gdr.chunk_fwd(qb, qb, qb, la, la, la, workspace=ws)
+    with pytest.raises(ValueError, match="workspace"):
+        run(torch.empty(need, dtype=torch.uint8, device="meta"))
+    with pytest.raises(ValueError, match="workspace"):
+        run(torch.empty(need - 1, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="GPU"):
+        run(torch.empty(need, dtype=torch.uint8))
+    # decode: the state and the output
+    q1 = torch.zeros(B, 1, H, D, dtype=bf)
+    dec = lambda **kw: gdr.decode_step(q1, q1, q1, **kw)
+    with pytest.raises(ValueError, match="GPU"):
+        dec(S=S.clone(), out=torch.empty_like(q1))
+    for exc, kw in [(ValueError, dict(S=meta(S))), (TypeError, dict(S=S.to(bf))),
+                    (ValueError, dict(S=torch.zeros(B, H, D, D + 16, dtype=f32))),
+                    (ValueError, dict(S=S, out=torch.empty(B, 1, H, D + 16, dtype=bf))),
+                    (ValueError, dict(S=S, out=meta(q1))), (TypeError, dict(S=S, out=q1.float()))]:
+        with pytest.raises(exc):
+            dec(**kw)
+    with pytest.raises(ValueError):
+        dec()  # no state
+    # backward: do, S0, dS_T
+    bwd = lambda **kw: gdr.chunk_bwd(q, q, q, **kw)
+    with pytest.raises(ValueError, match="GPU"):
+        bwd(do=q.clone(), S0=S, dS_T=S.clone())
+    for exc, kw in [(ValueError, dict()), (ValueError, dict(do=meta(q))),
+                    (ValueError, dict(do=q, dS_T=meta(S))), (ValueError, dict(do=q, S0=meta(S))),
+                    (TypeError, dict(do=q, dS_T=S.to(bf))), (ValueError, dict(do=q[:, :2]))]:
+        with pytest.raises(exc):
+            bwd(**kw)

@@ -2,7 +2,8 @@
 (oracle.backward, fp64, pinned by finite differences), on the same bf16 inputs.
 
 Tolerance: every gradient tensor G (dq, dk, dv, d log alpha, db, dw, dS0) must satisfy
-||G - G_ref||_F <= 2e-2 ||G_ref||_F.  The path rounds its matrix-core operands to bf16 (unit
+||G - G_ref||_F <= 2e-2 ||G_ref||_F, as a whole and for each (batch, head) state, and its largest
+element error per state must stay within 2e-2 of that state's largest reference element.  The path rounds its matrix-core operands to bf16 (unit
 roundoff 2^-8) and keeps fp32 accumulators, like the forward (whose states meet 1e-2); the
 backward chains two such passes (the states, then their gradients) before the chunk-local
 products and rounds its outputs to bf16, so twice the forward's state bound."""
@@ -72,7 +73,18 @@ def run(x, dev, order="erase_then_decay"):
     return out
 
 
+def state_slices(name, shape):
+    """Index tuples of the (batch, head) states of a gradient tensor: [B, T, H(, D)] per token,
+    [B, H, dk, dv] for dS0."""
+    if name == "dS0":
+        return [(b, h) for b in range(shape[0]) for h in range(shape[1])]
+    return [(b, slice(None), h) for b in range(shape[0]) for h in range(shape[2])]
+
+
 def compare(out, ref, label):
+    """Every gradient tensor, whole and state by state: for each (batch, head) state s,
+    ||G_s - G_ref,s||_F <= REL ||G_ref,s||_F and max |G_s - G_ref,s| <= REL max |G_ref,s|, so that
+    an error confined to a few tokens or to one head cannot hide under the norm of the rest."""
     worst = 0.0
     for name in ("dq", "dk", "dv", "dlog_alpha", "db", "dw", "dS0"):
         r = ref[name]
@@ -84,9 +96,18 @@ def compare(out, ref, label):
         assert np.isfinite(got).all(), name
         den = np.linalg.norm(r)
         rel = float(np.linalg.norm(got - r) / den) if den > 0 else float(np.abs(got).max())
-        say("  %s %-10s rel %.3e" % (label, name, rel))
-        worst = max(worst, rel)
-        assert rel <= REL, (label, name, rel)
+        st_f, st_m = 0.0, 0.0
+        for ix in state_slices(name, r.shape):
+            rs, gs = r[ix], got[ix]
+            if rs.size == 0:
+                continue
+            nf, nm = np.linalg.norm(rs), np.abs(rs).max()
+            ef, em = np.linalg.norm(gs - rs), np.abs(gs - rs).max()
+            st_f = max(st_f, ef / nf if nf > 0 else ef)
+            st_m = max(st_m, em / nm if nm > 0 else em)
+        say("  %s %-10s rel %.3e  per state: Frobenius %.3e  max %.3e" % (label, name, rel, st_f, st_m))
+        worst = max(worst, rel, st_f, st_m)
+        assert rel <= REL and st_f <= REL and st_m <= REL, (label, name, rel, st_f, st_m)
     return worst
 
 
@@ -145,8 +166,8 @@ def test_backward_strong_decay(dev):
 
 
 def test_backward_gdn_workload_sampled(dev):
-    """The Gated DeltaNet workload at full size (B=4, H=16, T=4096, d=128); the oracle runs on two
-    sampled (batch, head) pairs."""
+    """The Gated DeltaNet workload at full size (B=4, H=16, T=4096, d=128); the oracle runs on eight
+    sampled (batch, head) pairs, one or two from each batch row."""
     wl = synth.WORKLOADS["gdn"]
     x = synth.make_prefill(wl)
     rng = np.random.default_rng(77)
@@ -154,7 +175,7 @@ def test_backward_gdn_workload_sampled(dev):
     x["dS_T"] = None
     say("backward gdn workload")
     out = run(x, dev)
-    pick = [(1, 5), (3, 14)]
+    pick = [(0, 0), (0, 9), (1, 5), (1, 15), (2, 3), (2, 12), (3, 7), (3, 14)]
     bi = torch.tensor([p[0] for p in pick])
     hi = torch.tensor([p[1] for p in pick])
     xs = subset_heads({n: x[n] for n in ("q", "k", "v", "log_alpha", "b", "w", "S0", "do")}, bi, hi)
