@@ -16,8 +16,9 @@ GATE_NONE, GATE_SCALAR, GATE_CHANNEL = 0, 1, 2
 ERASE_THEN_DECAY, DECAY_THEN_ERASE = 0, 1
 
 EXPORTED = ("gdr_abi_version", "gdr_status_string", "gdr_chunk_fwd_workspace_bytes",
-            "gdr_chunk_fwd", "gdr_chunk_fwd_marked", "gdr_decode_step", "gdr_chunk_bwd_workspace_bytes",
-            "gdr_chunk_bwd")
+            "gdr_chunk_fwd", "gdr_chunk_fwd_marked", "gdr_chunk_fwd_noalloc", "gdr_decode_step",
+            "gdr_chunk_bwd_workspace_bytes", "gdr_chunk_bwd")
+NOALLOC_SCRATCH_BYTES = 64 << 20  # GDR_NOALLOC_SCRATCH_BYTES
 
 
 class GdrProblem(ctypes.Structure):
@@ -73,6 +74,8 @@ def lib():
         L.gdr_chunk_fwd.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.gdr_chunk_fwd_marked.restype = ctypes.c_int
         L.gdr_chunk_fwd_marked.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
+        L.gdr_chunk_fwd_noalloc.restype = ctypes.c_int
+        L.gdr_chunk_fwd_noalloc.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.gdr_decode_step.restype = ctypes.c_int
         L.gdr_decode_step.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.gdr_chunk_bwd_workspace_bytes.restype = sz
@@ -109,6 +112,13 @@ def chunk_fwd_marked_raw(problem, q, k, v, la, b, w, S0, o, S_T, ws, ws_bytes, s
                                       la or None, b or None, w or None, S0 or None, o or None,
                                       S_T or None, ws or None, ws_bytes, stream or None,
                                       event or None)
+
+
+def chunk_fwd_noalloc_raw(problem, q, k, v, la, b, w, S0, o, S_T, stream):
+    """gdr_chunk_fwd_noalloc with integer device addresses (0 = NULL).  Returns the status."""
+    return lib().gdr_chunk_fwd_noalloc(ctypes.byref(problem), q or None, k or None, v or None,
+                                       la or None, b or None, w or None, S0 or None, o or None,
+                                       S_T or None, stream or None)
 
 
 def decode_step_raw(problem, q, k, v, la, b, w, S, o, stream):

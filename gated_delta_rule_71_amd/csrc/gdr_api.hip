@@ -1,8 +1,10 @@
 // C ABI of libgdr.so: argument validation and kernel dispatch.
-// Every check runs before the first HIP call, so a rejected call launches
-// nothing; the library keeps no mutable global state.
+// Every check runs before the first HIP call, so a rejected call launches nothing.  The only
+// mutable global state is the allocation-free prefill's scratch array and its per-device address.
 #include <stdint.h>
 #include <string.h>
+
+#include <mutex>
 
 #include "gdr.h"
 #include "gdr_common.h"
@@ -118,9 +120,12 @@ GDR_EXPORT const char* gdr_status_string(int status) {
       return "GDR_ERR_INVALID_ARGUMENT: NULL pointer, negative size, bad enum value, struct_size "
              "mismatch or overlapping output";
     case GDR_ERR_UNSUPPORTED:
-      return "GDR_ERR_UNSUPPORTED: dk must be 16/32/64/128 (256: bf16, scalar, no or decay-first per-channel decay), dv a multiple of 16 up to 256, chunk 64";
+      return "GDR_ERR_UNSUPPORTED: dk must be 16, 32, 64, 128 or 256, dv a multiple of 16 up to 256, "
+             "chunk 64; the backward also needs bf16, a scalar or no decay and dk 32, 64 or 128";
     case GDR_ERR_MISALIGNED: return "GDR_ERR_MISALIGNED: tensor pointers must be 16-byte aligned";
-    case GDR_ERR_WORKSPACE_TOO_SMALL: return "GDR_ERR_WORKSPACE_TOO_SMALL: workspace below the query";
+    case GDR_ERR_WORKSPACE_TOO_SMALL:
+      return "GDR_ERR_WORKSPACE_TOO_SMALL: workspace below the query (for gdr_chunk_fwd_noalloc: the "
+             "problem needs more than the library's GDR_NOALLOC_SCRATCH_BYTES array)";
     case GDR_ERR_HIP: return "GDR_ERR_HIP: the HIP runtime reported an error at launch";
     default: return "unknown gdr_status";
   }
@@ -133,9 +138,10 @@ GDR_EXPORT size_t gdr_chunk_fwd_workspace_bytes(const gdr_problem* p) {
 }
 
 namespace {
-int chunk_fwd(const gdr_problem* p, const void* q, const void* k, const void* v,
-              const void* log_alpha, const void* b, const void* w, const float* S0, void* o,
-              float* S_T, void* workspace, size_t workspace_bytes, void* stream, void* mark) {
+// Every check of a prefill call except those of the workspace.
+int check_fwd(const gdr_problem* p, const void* q, const void* k, const void* v,
+              const void* log_alpha, const void* b, const void* w, const float* S0, const void* o,
+              const float* S_T) {
   int rc = check_problem(p);
   if (rc != GDR_OK) return rc;
   rc = check_tensors(p, p->seqlen, q, k, v, log_alpha, b, w, o);
@@ -150,14 +156,18 @@ int chunk_fwd(const gdr_problem* p, const void* q, const void* k, const void* v,
   const int64_t rows = p->batch * p->seqlen * p->heads;
   if (S_T && rows && overlaps(range_of(S_T, sbytes), range_of(o, rows * p->dv * es)))
     return GDR_ERR_INVALID_ARGUMENT;
-  const bool decay_first = p->order == GDR_DECAY_THEN_ERASE;
-  if (!gdr::prefill_supported(p->io_dtype, p->dk, p->dv, p->alpha_kind, decay_first))
+  if (!gdr::prefill_supported(p->io_dtype, p->dk, p->dv, p->alpha_kind,
+                              p->order == GDR_DECAY_THEN_ERASE))
     return GDR_ERR_UNSUPPORTED;
-  const size_t need = gdr_chunk_fwd_workspace_bytes(p);
-  if (workspace_bytes < need) return GDR_ERR_WORKSPACE_TOO_SMALL;
-  if (need > 0 && workspace == nullptr) return GDR_ERR_INVALID_ARGUMENT;
-  if (need > 0 && !aligned16(workspace)) return GDR_ERR_MISALIGNED;
+  return GDR_OK;
+}
 
+// The launches of a validated prefill call.
+int launch_fwd(const gdr_problem* p, const void* q, const void* k, const void* v,
+               const void* log_alpha, const void* b, const void* w, const float* S0, void* o,
+               float* S_T, void* workspace, void* stream, void* mark) {
+  if (p->batch * p->heads == 0) return GDR_OK;
+  const bool decay_first = p->order == GDR_DECAY_THEN_ERASE;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;
   if (p->io_dtype == GDR_BF16) {
@@ -177,6 +187,19 @@ int chunk_fwd(const gdr_problem* p, const void* q, const void* k, const void* v,
   }
   return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
 }
+
+int chunk_fwd(const gdr_problem* p, const void* q, const void* k, const void* v,
+              const void* log_alpha, const void* b, const void* w, const float* S0, void* o,
+              float* S_T, void* workspace, size_t workspace_bytes, void* stream, void* mark) {
+  const int rc = check_fwd(p, q, k, v, log_alpha, b, w, S0, o, S_T);
+  if (rc != GDR_OK) return rc;
+  if (p->batch * p->heads == 0) return GDR_OK;
+  const size_t need = gdr_chunk_fwd_workspace_bytes(p);
+  if (workspace_bytes < need) return GDR_ERR_WORKSPACE_TOO_SMALL;
+  if (need > 0 && workspace == nullptr) return GDR_ERR_INVALID_ARGUMENT;
+  if (need > 0 && !aligned16(workspace)) return GDR_ERR_MISALIGNED;
+  return launch_fwd(p, q, k, v, log_alpha, b, w, S0, o, S_T, workspace, stream, mark);
+}
 }  // namespace
 
 GDR_EXPORT int gdr_chunk_fwd(const gdr_problem* p, const void* q, const void* k, const void* v,
@@ -194,6 +217,53 @@ GDR_EXPORT int gdr_chunk_fwd_marked(const gdr_problem* p, const void* q, const v
                                     void* phase_event) {
   return chunk_fwd(p, q, k, v, log_alpha, b, w, S0, o, S_T, workspace, workspace_bytes, stream,
                    phase_event);
+}
+
+// ---- the allocation-free prefill: its workspace is a file-scope device array ----
+
+namespace {
+
+constexpr size_t kScratchBytes = size_t(64) << 20;  // GDR_NOALLOC_SCRATCH_BYTES in gdr.h
+static_assert(kScratchBytes == GDR_NOALLOC_SCRATCH_BYTES, "header and library agree");
+
+// One copy per GPU the library runs on, for the life of the process.  Host code never uses this
+// name as an address: the device address comes from hipGetSymbolAddress, per device.
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up once per device (NULL on failure).
+void* scratch_address() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+GDR_EXPORT int gdr_chunk_fwd_noalloc(const gdr_problem* p, const void* q, const void* k,
+                                     const void* v, const void* log_alpha, const void* b,
+                                     const void* w, const float* S0, void* o, float* S_T,
+                                     void* stream) {
+  const int rc = check_fwd(p, q, k, v, log_alpha, b, w, S0, o, S_T);
+  if (rc != GDR_OK) return rc;
+  if (p->batch * p->heads == 0) return GDR_OK;
+  const size_t need = gdr_chunk_fwd_workspace_bytes(p);
+  if (need > kScratchBytes) return GDR_ERR_WORKSPACE_TOO_SMALL;
+  void* ws = nullptr;
+  if (need > 0) {
+    ws = scratch_address();
+    if (ws == nullptr) return GDR_ERR_HIP;
+  }
+  return launch_fwd(p, q, k, v, log_alpha, b, w, S0, o, S_T, ws, stream, nullptr);
 }
 
 GDR_EXPORT int gdr_decode_step(const gdr_problem* p, const void* q, const void* k, const void* v,

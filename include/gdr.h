@@ -40,9 +40,10 @@
  *   fp32 (GDR_FP32) matrix-core operands.
  * - Validation happens before any HIP call; a call that fails validation
  *   launches nothing and touches no memory.  A failed kernel launch returns
- *   GDR_ERR_HIP.  No exception or abort crosses the ABI.  The library keeps no
- *   mutable global state; concurrent calls on different streams are safe when
- *   their buffers do not overlap.
+ *   GDR_ERR_HIP.  No exception or abort crosses the ABI.  Apart from the
+ *   scratch array of gdr_chunk_fwd_noalloc, the library keeps no mutable global
+ *   state; concurrent calls on different streams are safe when their buffers
+ *   do not overlap.
  * - NaN or Inf in the inputs propagate to the outputs; they are not detected.
  */
 #ifndef GDR_H_
@@ -71,12 +72,15 @@ typedef enum { GDR_GATE_NONE = 0, GDR_GATE_SCALAR = 1, GDR_GATE_CHANNEL = 2 } gd
 typedef enum { GDR_ERASE_THEN_DECAY = 0, GDR_DECAY_THEN_ERASE = 1 } gdr_order;
 
 /* Problem description.  Set struct_size = sizeof(gdr_problem).
- * Supported: dk in {16, 32, 64, 128}, and 256 for gdr_decode_step and for a
- * bf16 gdr_chunk_fwd with a scalar decay, no decay or a per-channel decay
- * applied before the erase (GDR_ERR_UNSUPPORTED otherwise); dv a multiple of
- * 16 in [16, 256];
- * chunk == 64 (0 selects 64); batch, heads >= 0; seqlen >= 0 (any value: a
- * ragged last chunk is padded with identity tokens inside the kernel). */
+ * Supported by the prefill and the decode step: dk in {16, 32, 64, 128, 256},
+ * dv a multiple of 16 in [16, 256], both I/O types, every gate kind and both
+ * orders (GDR_ERR_UNSUPPORTED otherwise); the backward is narrower (see
+ * gdr_chunk_bwd).  chunk == 64 (0 selects 64); batch, heads >= 0; seqlen >= 0
+ * (any value: a ragged last chunk is padded with identity tokens inside the
+ * kernel).  Which kernels run: the chunkwise kernels where their LDS layout
+ * fits (every bf16 shape except dk = 256 with a per-channel decay after the
+ * erase; fp32 at dk <= 32, and at dk = 64 with a scalar, no or decay-first
+ * decay), else the recurrence token by token with the state in registers. */
 typedef struct {
   int32_t struct_size;
   int32_t io_dtype;   /* gdr_dtype */
@@ -151,6 +155,27 @@ int gdr_chunk_fwd_marked(const gdr_problem* p, const void* q, const void* k, con
                          const void* log_alpha, const void* b, const void* w, const float* S0,
                          void* o, float* S_T, void* workspace, size_t workspace_bytes,
                          void* stream, void* phase_event);
+
+/* Size of the device array gdr_chunk_fwd_noalloc takes its workspace from. */
+#define GDR_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * gdr_chunk_fwd for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same computation, with the workspace
+ * taken from a GDR_NOALLOC_SCRATCH_BYTES device array inside the library instead of a caller
+ * buffer.  The library holds one such array on every GPU it runs on until the process ends; its
+ * address is looked up on the first call with that GPU current.  The call allocates and frees
+ * nothing.  Arguments as for gdr_chunk_fwd.
+ *   GDR_ERR_WORKSPACE_TOO_SMALL  when gdr_chunk_fwd_workspace_bytes(p) exceeds
+ *                                GDR_NOALLOC_SCRATCH_BYTES (nothing is launched)
+ *   GDR_ERR_HIP                  when the array's address cannot be obtained
+ * Every call on one GPU shares that GPU's array: calls that overlap in time on one GPU (on
+ * different streams, or from different threads) race and must not be issued; calls in order on
+ * one stream are safe.  The array's contents on entry do not matter.
+ */
+int gdr_chunk_fwd_noalloc(const gdr_problem* p, const void* q, const void* k, const void* v,
+                          const void* log_alpha, const void* b, const void* w, const float* S0,
+                          void* o, float* S_T, void* stream);
 
 /*
  * One decode step (p->seqlen must be 1): for every (batch, head) applies the

@@ -302,3 +302,19 @@ def test_binding_checks_every_buffer_before_any_gpu_call():
                     (TypeError, dict(do=q, dS_T=S.to(bf))), (ValueError, dict(do=q[:, :2]))]:
         with pytest.raises(exc):
             bwd(**kw)
+
+
+def test_noalloc_rejects_problems_past_its_scratch():
+    """gdr_chunk_fwd_noalloc takes its workspace from a fixed device array: a problem that needs
+    more is GDR_ERR_WORKSPACE_TOO_SMALL before any HIP call (the addresses are never touched), and
+    it validates its arguments like gdr_chunk_fwd."""
+    p = prob(batch=1, heads=16, seqlen=32768)
+    assert N.workspace_bytes(p) > N.NOALLOC_SCRATCH_BYTES
+    a = big_apart()
+    args = [a[n] for n in ("q", "k", "v", "la", "b", "w", "S0", "o", "S_T")]
+    assert N.chunk_fwd_noalloc_raw(p, *args, 0) == N.GDR_ERR_WORKSPACE_TOO_SMALL
+    bad = dict(a, q=0)
+    assert N.chunk_fwd_noalloc_raw(prob(), *[bad[n] for n in ("q", "k", "v", "la", "b", "w", "S0", "o", "S_T")], 0) \
+        == N.GDR_ERR_INVALID_ARGUMENT
+    assert N.chunk_fwd_noalloc_raw(prob(dk=96), *args, 0) == N.GDR_ERR_UNSUPPORTED
+    assert N.chunk_fwd_noalloc_raw(prob(batch=0), *args, 0) == N.GDR_OK
