@@ -33,7 +33,7 @@ hipError_t launch_backward(const bf16_t* q, const bf16_t* k, const bf16_t* v, co
                            int64_t Hk, int64_t DK, int64_t DV, int alpha_kind, int b_kind, int w_kind,
                            void* workspace, hipStream_t s);
 size_t prefill_workspace_bytes(int io_dtype, int64_t nstate, int64_t T, int64_t DK, int64_t DV,
-                               int alpha_kind, int b_kind, bool decay_first);
+                               int alpha_kind, int b_kind, int w_kind, bool decay_first);
 }  // namespace gdr
 
 namespace {
@@ -134,7 +134,7 @@ GDR_EXPORT const char* gdr_status_string(int status) {
 GDR_EXPORT size_t gdr_chunk_fwd_workspace_bytes(const gdr_problem* p) {
   if (check_problem(p) != GDR_OK) return 0;
   return gdr::prefill_workspace_bytes(p->io_dtype, p->batch * p->heads, p->seqlen, p->dk, p->dv,
-                                      p->alpha_kind, p->b_kind, p->order == GDR_DECAY_THEN_ERASE);
+                                      p->alpha_kind, p->b_kind, p->w_kind, p->order == GDR_DECAY_THEN_ERASE);
 }
 
 namespace {

@@ -11,6 +11,10 @@ bool prefill_wyc_ok(int64_t DK, int64_t DV);
 size_t prefill_wyc_workspace_bytes(int64_t nstate, int64_t T, int64_t DK, int64_t DV, bool two);
 hipError_t prefill_wyc_launch(const PrefillArgs<bf16_t>& p, int64_t nstate, int64_t DK, bool two,
                               void* workspace, hipEvent_t mark, hipStream_t s);
+bool prefill_seg_ok(int64_t DK, int64_t DV, int alpha_kind, int b_kind, int w_kind, bool decay_first);
+size_t prefill_seg_workspace_bytes(int64_t nstate, int64_t T);
+hipError_t prefill_seg_launch(const PrefillArgs<bf16_t>& pa, int64_t nstate, bool two, void* workspace,
+                              hipEvent_t mark, hipStream_t s);
 template <typename IO>
 hipError_t prefill_recur(const PrefillArgs<IO>& a, int64_t nstate, int64_t DK, bool decay_first,
                          hipStream_t s);
@@ -52,8 +56,10 @@ hipError_t record_mark(hipEvent_t mark, hipStream_t stream) {
 }  // namespace
 
 size_t prefill_workspace_bytes(int io_dtype, int64_t nstate, int64_t T, int64_t DK, int64_t DV,
-                               int alpha_kind, int b_kind, bool decay_first) {
+                               int alpha_kind, int b_kind, int w_kind, bool decay_first) {
   if (io_dtype != 0) return 0;
+  if (prefill_seg_ok(DK, DV, alpha_kind, b_kind, w_kind, decay_first || alpha_kind != kChannel))
+    return prefill_seg_workspace_bytes(nstate, T);
   if (alpha_kind != kChannel)
     return prefill_wy_ok(DK, DV, b_kind) ? prefill_wy_workspace_bytes(nstate, T, DK, DV) : 0;
   return prefill_wyc_ok(DK, DV) ? prefill_wyc_workspace_bytes(nstate, T, DK, DV, !decay_first) : 0;
@@ -82,6 +88,10 @@ hipError_t launch_prefill(const IO* q, const IO* k, const IO* v, const IO* la, c
   PrefillArgs<IO> a{q, k, v, la, bg, wg, S0, o, S_T, T, H, DV, alpha_kind, b_kind, w_kind, 1, Hk};
   const int64_t nstate = B * H;
   if constexpr (sizeof(IO) == 2) {
+    // the fused segment kernel for d_k = d_v = 128 and the gates it is built for (a scalar decay
+    // commutes with the erase, so it takes the decay-first form)
+    if (prefill_seg_ok(DK, DV, alpha_kind, b_kind, w_kind, decay_first || alpha_kind != kChannel))
+      return prefill_seg_launch(a, nstate, mode == 2, workspace, mark, stream);
     if (mode == 0) {
       if (prefill_wy_ok(DK, DV, b_kind)) return prefill_wy_launch(a, nstate, DK, workspace, mark, stream);
     } else if (prefill_wyc_ok(DK, DV)) {

@@ -1,0 +1,987 @@
+// Chunkwise prefill as one fused kernel per (state, segment of chunks), for d_k = d_v = 128.
+//
+// Each workgroup walks the chunks of one segment of one state.  Per 32-token chunk it forms the
+// chunk's operands in LDS (prefix sums of log alpha, split factors, Gram products, the triangular
+// inverse, W and Y) and then advances the state, whose 128 value columns live in the MFMA
+// accumulators of its eight waves (wave w holds columns 16 w .. 16 w + 15, all 128 rows).  No
+// chunk data goes through HBM: the next chunk's inputs arrive in LDS by direct-to-LDS loads while
+// the current chunk is computed.
+//
+// Chunk form ("Recurrent Memory: Write, Erase, Decay, Read": section 03, the erase is linear and
+// reassociates over a chunk; section 04, the decay enters through prefix sums G_t of log alpha;
+// the Gated DeltaNet-2 abstract, a channel-wise decay absorbed into separate erase factors).  With
+// c = b . k, X = w . v and per-channel prefix sums G_t of log alpha from the chunk's start
+// (G_{-1} = 0, G_n = G_31):
+//   decay after the erase (MODE 2):
+//     Qs = q e^{G_t},  Ks = k e^{-G_t},  Cs = c e^{G_{t-1}},  Ps = k e^{-G_{t-1}},
+//     L_P = strict_tril(Cs Ps^T),  L_K = strict_tril(Cs Ks^T),  M_QK = tril(Qs Ks^T),
+//     M_QP = tril(Qs Ps^T),  T = (I + L_P)^{-1},  W = T Cs,  Y = T L_K X,
+//     R = W S + Y  (R_t = c_t S_{t-1}: the erase reads)
+//     O = Qs S - M_QP R + M_QK X,       S' = e^{G_n} . (S + Ks^T X - Ps^T R)
+//   decay before the erase (MODE 1; also a scalar decay, where both orders agree):
+//     Cs = c e^{G_t},  L = strict_tril(Cs Ks^T),  M = tril(Qs Ks^T),  T = (I + L)^{-1},
+//     W = T Cs,  Y = -T X,  R = W S + Y,  O = Qs S - M R,  S' = e^{G_n} . (S - Ks^T R)
+// Every factor lies in the fp32 and bf16 range while |G_t| <= 76 for all t of the chunk; the
+// Gram products only ever combine them as e^{G_t - G_s} with t >= s.  A chunk past that is run
+// token by token in fp32 on the register-resident state instead: exact for any gate values.
+//
+// Segments.  A state's chunks are split into segments so that enough workgroups run at once.  The
+// state entering segment s > 0 is not known when it starts, so its workgroup carries, next to the
+// state N from zero, the segment's transition Phi (dk x dk, from the identity: the same products
+// with X = 0), and writes for every chunk Q~ = (the chunk's read-out of Phi), a 32 x dk matrix:
+//   S_exit(s) = Phi_s S_enter(s) + N_s,   o_c = O_c(N) + Q~_c S_enter(s)
+// (the recurrence is affine in the state: "How Linear Attention Remembers", Analytical Framework).
+// A second kernel chains S_enter over the segments; a third adds Q~_c S_enter(s) to o.
+#pragma once
+#include "gdr_common.h"
+#include "mfma.h"
+#include "prefill_kernel.h"
+#include "prefill_wy.h"
+
+namespace gdr {
+
+struct SegArgs {
+  const bf16_t* q;
+  const bf16_t* k;
+  const bf16_t* v;
+  const bf16_t* la;
+  const bf16_t* bg;
+  const bf16_t* wg;
+  const float* S0;
+  bf16_t* o;
+  float* S_T;
+  __bf16* Qt;     // [state][nch][32][dk]  Q~ of every chunk of segments > 0, channels in pair order
+  float* Nseg;    // [state][nseg][dk][dv] state from zero over segment s (s > 0)
+  float* Pseg;    // [state][nseg][dk][dk] transition of segment s (s > 0)
+  float* Eseg;    // [state][nseg][dk][dv] slot 1: the state leaving segment 0
+  __bf16* Ebf;    // [state][nseg][dv][dk] the state entering segment s, bf16, transposed, pair order
+  int64_t T, H, Hk, nch;
+  int64_t nseg, L;  // segments per state, chunks per segment (the last may be shorter)
+  int alpha_kind, b_kind, w_kind;
+};
+
+constexpr float kSegSpanLimit = 76.f;
+constexpr int kSegC = 32;  // tokens per chunk
+
+__device__ __forceinline__ void unpack4(uint2 u, float* f) {
+  f[0] = __uint_as_float(u.x << 16);
+  f[1] = __uint_as_float(u.x & 0xffff0000u);
+  f[2] = __uint_as_float(u.y << 16);
+  f[3] = __uint_as_float(u.y & 0xffff0000u);
+}
+__device__ __forceinline__ uint2 pack4(const float* f) {
+  bf16x4 b;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) b[i] = static_cast<__bf16>(f[i]);
+  return __builtin_bit_cast(uint2, b);
+}
+__device__ __forceinline__ void buf_store8(__amdgpu_buffer_rsrc_t r, uint32_t off, uint2 v) {
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, off, 0, 0);
+}
+// x through an empty asm statement: the compiler can neither see its value nor move it out of a
+// loop, so what is derived from it is recomputed where it is used
+__device__ __forceinline__ int opaque_v(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+__device__ __forceinline__ uint2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+
+// One 16-byte direct-to-LDS load per lane from `bytes` bytes at `base` (pieces past them arrive as
+// zeros): lane L's piece lands at lds + 16 L.  Issued from an asm statement, so the compiler does
+// not count it as a write to LDS and inserts no wait for it before later LDS reads, which it would
+// otherwise do before every transposing read; the kernel waits for these loads itself
+// (s_waitcnt vmcnt(0), then a barrier) before anything reads the staging.
+__device__ __forceinline__ void seg_dma16(const void* base, uint32_t bytes, unsigned char* lds, uint32_t off) {
+  typedef int i32x4 __attribute__((ext_vector_type(4)));
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r.x = static_cast<int>(static_cast<uint32_t>(p));
+  r.y = static_cast<int>(static_cast<uint32_t>(p >> 32) & 0xffffu);  // stride 0, no swizzle
+  r.z = static_cast<int>(bytes);
+  r.w = 0x00020000;
+  const uint32_t m0 = static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) unsigned char*)lds));
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(m0), "v"(off), "s"(r)
+               : "memory", "m0");
+}
+
+// Position of channel ch in a row stored in pair order: within each block of 32 channels, the
+// 16-byte piece g holds channels 4 g .. 4 g + 3 and 16 + 4 g .. 16 + 4 g + 3, the k values lane
+// group g of an MFMA operand takes.
+__device__ __forceinline__ int seg_pair_pos(int ch) {
+  return (ch & ~31) + 8 * ((ch & 15) >> 2) + 4 * ((ch >> 4) & 1) + (ch & 3);
+}
+
+// Sums over the 16 lanes of a row (lanes 16 r .. 16 r + 15): the inclusive prefix up to this lane,
+// by DPP row shifts (lanes past the row's start add zero), and the value of the row's lane 15.
+template <int CTRL>
+__device__ __forceinline__ float dpp_row(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, true));
+}
+__device__ __forceinline__ float row_prefix16(float x) {
+  x += dpp_row<0x111>(x);  // row_shr:1
+  x += dpp_row<0x112>(x);  // row_shr:2
+  x += dpp_row<0x114>(x);  // row_shr:4
+  x += dpp_row<0x118>(x);  // row_shr:8
+  return x;
+}
+__device__ __forceinline__ float row_lane15(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x15f, 0xf, 0xf, false));
+}
+
+// Fragment of column `col` (this lane's, col = tile + l16) of a token-major LDS array over the 32
+// tokens of a chunk, in tile-pair order: lane holds tokens 4 g + (e & 3) + 16 (e >> 2).
+__device__ __forceinline__ bf16x8 seg_col_frag(const __bf16* base, int pitch, int col, int g, int l16) {
+  const int c0 = col - l16 + 4 * (l16 & 3), m_ = l16 >> 2;
+  bf16x8 f;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const bf16x4 v = lds_read_tr4(reinterpret_cast<const unsigned char*>(base + (16 * h + 4 * g + m_) * pitch + c0));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) f[4 * h + e] = v[e];
+  }
+  return f;
+}
+
+// Staging of one chunk's inputs in LDS: [32 tokens][128] bf16 per per-channel input, rows of 256
+// bytes without padding, the 16 pieces of 16 bytes of row t permuted by XOR with t & 15 (so that
+// the 16 rows one read touches fall on distinct banks); 32 bf16 per scalar gate.
+__device__ __forceinline__ int stage_off(int t, int c) {  // byte offset of element (t, c), c % 4 == 0
+  return t * 256 + ((((c >> 3) ^ t) & 15) << 4) + ((c & 4) << 1);
+}
+
+template <int MODE, int AK, int BK, int WK>
+struct SegLayout {
+  static constexpr int DK = 128, DV = 128, C = kSegC;
+  static constexpr bool TWO = MODE == 2;
+  static constexpr int LDT = DK + 8;  // token-major rows of dk (or dv) bf16
+  static constexpr int LDD = C + 8;   // rows of 32 x 32 matrices
+  static constexpr int LDA = 16 + 8;  // the off-diagonal block of -L_P (rows 16..31, cols 0..15), transposed
+  static constexpr int LDL = 20;
+  static constexpr int LDF = DK + 4;  // fp32 rows of the flagged-chunk decays
+  static constexpr int ROWS = C * LDT * 2;
+  static constexpr int MAT = C * LDD * 2;
+  static constexpr int oQ = 0;                          // Qs      [32][LDT]
+  static constexpr int oC = oQ + ROWS;                  // Cs, then W (in place)
+  static constexpr int oK = oC + ROWS;                  // Ks (MODE 1: -Ks)
+  static constexpr int oP = oK + ROWS;                  // -Ps (MODE 2)
+  static constexpr int oX = oP + (TWO ? ROWS : 0);      // X rows [32][LDT]
+  static constexpr int oA = oX + ROWS;                  // (-L_10)^T of L_P / L
+  static constexpr int oM = oA + 16 * LDA * 2;          // -M_QP (MODE 2) / -M [32][LDD]
+  static constexpr int oLK = oM + MAT;                  // L_K (MODE 2)
+  static constexpr int oMQK = oLK + (TWO ? MAT : 0);    // M_QK (MODE 2)
+  static constexpr int oLD = oMQK + (TWO ? MAT : 0);   // fp32 L_ii row-major [2][16][LDL]
+  static constexpr int oS = (oLD + 2 * 16 * LDL * 4 + 1023) / 1024 * 1024;  // staging of the next chunk
+  static constexpr int CH = C * DK * 2;                 // one per-channel input: 8 KB
+  static constexpr int SC = 256;                        // one scalar gate (32 bf16, padded)
+  static constexpr int sQ = oS, sK = sQ + CH, sV = sK + CH;
+  static constexpr int sLA = sV + CH;
+  static constexpr int sB = sLA + (AK == kChannel ? CH : SC);
+  static constexpr int sW = sB + (BK == kChannel ? CH : SC);
+  static constexpr int oO = sW + (WK == kChannel ? CH : SC);  // o rows [32][LDT] bf16, then Q~ rows
+  static constexpr int oAL = oO;                        // flagged chunks: decays [32][LDF] fp32 over o, Q~
+  static constexpr int oF0 = oO + 2 * ROWS > oAL + C * LDF * 4 ? oO + 2 * ROWS : oAL + C * LDF * 4;
+  static constexpr int oF = (oF0 + 15) / 16 * 16;       // fp32 e^{G_n} [DK]
+  static constexpr int oFL = oF + DK * 4;               // per-wave flags [8] (int)
+  static constexpr int total = oFL + 8 * 4;
+  static constexpr bool fits = total <= kLdsLimit;
+  static_assert(oX % 16 == 0 && oA % 16 == 0 && oM % 16 == 0 &&
+                    oLD % 16 == 0 && oFL % 16 == 0 && oS % 1024 == 0 && CH % 1024 == 0 && oO % 16 == 0 && oF % 16 == 0,
+                "aligned arrays (each 1 KB direct-to-LDS load of the staging fills 1 KB of LDS)");
+};
+
+// Forward substitution for D = (I + L)^{-1}, L strictly lower 16 x 16, two blocks at once: lane
+// (row i = l16, quarter g) holds row i of -L (all 16 entries) and D[i][4 g .. 4 g + 3].  At step
+// M, row M of D is final; a DPP row broadcast (row_newbcast:M) hands D[M][4 g + c] to every lane
+// of the 16-lane group, which adds -L[i][M] times it (a no-op for rows i <= M, where L[i][M] = 0).
+// The broadcast folds into the multiply-add as its DPP operand.
+template <int M>
+__device__ __forceinline__ void seg_inv_sweep(float (&d)[2][4], const float (&nl)[2][16]) {
+  if constexpr (M < 15) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const float dm =
+            __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, d[b][c]), 0x150 + M, 0xf, 0xf, true));
+        d[b][c] = fmaf(dm, nl[b][M], d[b][c]);
+      }
+    seg_inv_sweep<M + 1>(d, nl);
+  }
+}
+
+// Gate values at one token for four channels: a channel gate's four channels, a scalar gate's
+// value four times, or `none` (the absent gate's value) four times.
+template <int KIND>
+__device__ __forceinline__ void stage_gate4(const unsigned char* st, int t, int c, float none, float* f) {
+  if constexpr (KIND == kChannel) {
+    unpack4(*reinterpret_cast<const uint2*>(st + stage_off(t, c)), f);
+  } else if constexpr (KIND == kScalar) {
+    const float v = static_cast<float>(reinterpret_cast<const __bf16*>(st)[t]);
+    f[0] = f[1] = f[2] = f[3] = v;
+  } else {
+    f[0] = f[1] = f[2] = f[3] = none;
+  }
+}
+
+// The work of one (state, segment) workgroup of 8 waves.  PHI: the segment starts from an unknown
+// state, so the workgroup also carries the segment's transition and writes Q~ (every segment but
+// the first).  AK, BK, WK: the kinds of log alpha (scalar or channel), b (scalar or channel) and w
+// (none, scalar or channel), fixed at compile time.
+//
+// Waves 0-1 issue the direct-to-LDS loads of the next chunk's inputs and wait only for those;
+// waves 4-7 copy each chunk's read-outs from LDS to o (and Q~) at the start of the next chunk;
+// waves 2-7 form the chunk's Gram products.
+// The barriers inside the chunk loop wait for LDS operations only, so loads and stores in flight
+// stay in flight across them.
+template <int MODE, int AK, int BK, int WK, bool PHI>
+__device__ __forceinline__ void seg_body(const SegArgs& a, unsigned char* smem, int64_t bh, int64_t seg) {
+  using L = SegLayout<MODE, AK, BK, WK>;
+  using MM = Mma<__bf16>;
+  using F8 = MM::F8;
+  constexpr bool TWO = L::TWO;
+  constexpr int C = kSegC, DK = 128, DV = 128, LDT = L::LDT, LDD = L::LDD, LDA = L::LDA,
+                LDL = L::LDL, LDF = L::LDF, NT = 512;
+
+  __bf16* tQ = reinterpret_cast<__bf16*>(smem + L::oQ);
+  __bf16* tC = reinterpret_cast<__bf16*>(smem + L::oC);
+  __bf16* tK = reinterpret_cast<__bf16*>(smem + L::oK);
+  __bf16* tP = reinterpret_cast<__bf16*>(smem + L::oP);
+  __bf16* tX = reinterpret_cast<__bf16*>(smem + L::oX);
+  __bf16* gA = reinterpret_cast<__bf16*>(smem + L::oA);
+  __bf16* gM = reinterpret_cast<__bf16*>(smem + L::oM);
+  __bf16* gLK = reinterpret_cast<__bf16*>(smem + L::oLK);
+  __bf16* gMQK = reinterpret_cast<__bf16*>(smem + L::oMQK);
+  float* Ld = reinterpret_cast<float*>(smem + L::oLD);
+  __bf16* tO = reinterpret_cast<__bf16*>(smem + L::oO);         // o rows of the chunk
+  __bf16* tQt = tO + C * LDT;                                     // Q~ rows of the chunk
+  float* fAl = reinterpret_cast<float*>(smem + L::oAL);
+  float* fG = reinterpret_cast<float*>(smem + L::oF);   // e^{G_n}
+  int* sFlag = reinterpret_cast<int*>(smem + L::oFL);
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, g = lane >> 4, l16 = lane & 15;
+  const int64_t H = a.H, Hk = a.Hk, T = a.T, nch = a.nch;
+  const int64_t bi = bh / H, hi = bh % H, hk = hi / (H / Hk);
+  const int64_t c_begin = seg * a.L;
+  const int64_t c_end = c_begin + a.L < nch ? c_begin + a.L : nch;
+  const int ch0 = 16 * wave + 4 * g;  // this lane's four channels / value columns in the elementwise phases
+  const int col = 16 * wave + l16;    // this lane's column of the state tiles
+  const uint32_t hqk = static_cast<uint32_t>(Hk * DK * 2), hdk = static_cast<uint32_t>(H * DK * 2);
+  const uint32_t hdv = static_cast<uint32_t>(H * DV * 2), h1 = static_cast<uint32_t>(H * 2);
+
+  // tiles of -M_QP / -M, L_K and M_QK above the diagonal are never written but are read as zero
+  for (int i = tid; i < (L::oLD - L::oM) / 16; i += NT)
+    reinterpret_cast<uint4*>(smem + L::oM)[i] = make_uint4(0, 0, 0, 0);
+
+  // ---- state tiles: N (value column col) and Phi (channel column col), rows 16 m + 4 g + i ----
+  f32x4 SN[8], SP[8];
+  {
+    const float* S0 = (!PHI && a.S0 != nullptr) ? a.S0 + bh * DK * DV : nullptr;
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * m + 4 * g + i;
+        SN[m][i] = S0 ? S0[row * DV + col] : 0.f;
+        if constexpr (PHI) SP[m][i] = (row == col) ? 1.f : 0.f;
+      }
+  }
+
+  // ---- direct-to-LDS loads of chunk c's inputs (waves 0-3) ----
+  uint16_t scA = 0, scB = 0, scW = 0;  // wave 0, lane t: token t's scalar gates in flight
+  auto stage = [&](int64_t c, int lane) {
+    const int64_t t0 = c * C, left = T - t0;
+    const int64_t rr = (bi * T + t0) * H + hi;
+    const int64_t rqk = (bi * T + t0) * Hk + hk;
+    // a per-channel array is 8 loads of 1 KB (4 rows each); wave w < 2 takes loads 4 w .. 4 w + 3
+    auto rows = [&](const bf16_t* base, uint32_t bytes, uint32_t stride, int dst) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = 4 * wave + u, t = 4 * i + (lane >> 4), slot = lane & 15;
+        const int piece = (slot ^ t) & 15;
+        seg_dma16(base, bytes, smem + dst + 1024 * i, static_cast<uint32_t>(t) * stride + piece * 16);
+      }
+    };
+    // a scalar gate: one bf16 per token into a register of wave 0's lane t (written to LDS once
+    // the wave has waited for its loads)
+    auto scalar = [&](__amdgpu_buffer_rsrc_t r, uint16_t& dst) {
+      if (wave == 0 && lane < C) dst = buf_load_u16(r, static_cast<uint32_t>(lane) * h1);
+    };
+    rows(a.q + rqk * DK, wy_range(left, Hk, DK), hqk, L::sQ);
+    rows(a.k + rqk * DK, wy_range(left, Hk, DK), hqk, L::sK);
+    rows(a.v + rr * DV, wy_range(left, H, DV), hdv, L::sV);
+    if constexpr (AK == kChannel) rows(a.la + rr * DK, wy_range(left, H, DK), hdk, L::sLA);
+    if constexpr (AK == kScalar) scalar(make_rsrc(a.la + rr, wy_range(left, H, 1)), scA);
+    if constexpr (BK == kChannel) rows(a.bg + rr * DK, wy_range(left, H, DK), hdk, L::sB);
+    if constexpr (BK == kScalar) scalar(make_rsrc(a.bg + rr, wy_range(left, H, 1)), scB);
+    if constexpr (WK == kChannel) rows(a.wg + rr * DV, wy_range(left, H, DV), hdv, L::sW);
+    if constexpr (WK == kScalar) scalar(make_rsrc(a.wg + rr, wy_range(left, H, 1)), scW);
+  };
+
+  // ---- copies of a chunk's read-outs from LDS to o and Q~ (waves 4-7) ----
+  auto store_out = [&](int64_t c, int tid) {
+    const int64_t t0 = c * C, left = T - t0;
+    const auto ro = make_rsrc(a.o + ((bi * T + t0) * H + hi) * DV, wy_range(left, H, DV));
+    const int l = tid - 256;  // 0 .. 255
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {  // 512 pieces of 16 bytes: row l / 16 + 16 u, piece l % 16
+      const int t = (l >> 4) + 16 * u, piece = l & 15;
+      const uint4 v = *reinterpret_cast<const uint4*>(tO + t * LDT + 8 * piece);
+      buf_store16(ro, static_cast<uint32_t>(t) * hdv + piece * 16, v);
+      if constexpr (PHI) {  // Q~ in the pair order of its channels (seg_pair_pos)
+        const int cb = 32 * (piece >> 2) + 4 * (piece & 3);
+        const uint2 lo = *reinterpret_cast<const uint2*>(tQt + t * LDT + cb);
+        const uint2 hi = *reinterpret_cast<const uint2*>(tQt + t * LDT + cb + 16);
+        *reinterpret_cast<uint4*>(a.Qt + ((bh * nch + c) * C + t) * DK + 8 * piece) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      }
+    }
+  };
+
+  if (wave < 2 && c_begin < c_end) stage(c_begin, lane);
+  bool out_pending = false;  // (uniform) the read-outs of chunk c - 1 wait in LDS
+
+  for (int64_t c = c_begin; c < c_end; ++c) {
+    // lane-derived values again, from an opaque copy of the thread index: recomputing them costs
+    // a few adds, keeping them across the loop would cost registers the chunk needs
+    const int tid = opaque_v(threadIdx.x);
+    const int lane = tid & 63, g = lane >> 4, l16 = lane & 15;
+    const int ch0 = 16 * wave + 4 * g, col = 16 * wave + l16;
+    if (wave >= 4 && out_pending) store_out(c - 1, tid);
+    if (wave < 2) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // this wave's loads of chunk c
+    if (wave == 0 && lane < C) {
+      if constexpr (AK == kScalar) reinterpret_cast<uint16_t*>(smem + L::sLA)[lane] = scA;
+      if constexpr (BK == kScalar) reinterpret_cast<uint16_t*>(smem + L::sB)[lane] = scB;
+      if constexpr (WK == kScalar) reinterpret_cast<uint16_t*>(smem + L::sW)[lane] = scW;
+    }
+    lds_barrier_keep_vm();  // B0: chunk c's inputs are in LDS
+
+    const unsigned char* st = smem;
+    // ---- 1. prefix sums of log alpha over the chunk, per channel, inside the wave: this lane's
+    // tokens l16 + 16 j (j = 0, 1) of channels ch0 .. ch0 + 3 ----
+    float G[2][4], la[2][4];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      stage_gate4<AK>(st + L::sLA, l16 + 16 * j, ch0, 0.f, la[j]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) G[j][i] = row_prefix16(la[j][i]);
+    }
+    bool ok = true;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      G[1][i] += row_lane15(G[0][i]);  // + G_15
+      ok = ok && fabsf(G[0][i]) <= kSegSpanLimit && fabsf(G[1][i]) <= kSegSpanLimit;  // (NaN fails too)
+      if (l16 == 15) fG[ch0 + i] = __expf(G[1][i]);  // G_n = G_31
+    }
+    const bool wave_ok = __all(ok);
+    if (lane == 0) sFlag[wave] = wave_ok ? 0 : 1;
+
+    // ---- 2. split operands and X into LDS (rows l16 + 16 j, columns ch0 .. + 3) ----
+    // (all reads of both tokens first, so that their latencies overlap)
+    float q4[2][4], k4[2][4], c4[2][4], x4[2][4], w4[2][4];
+    {
+      uint2 rq[2], rk[2], rv[2], rb[2], rw[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int t = l16 + 16 * j;
+        rq[j] = *reinterpret_cast<const uint2*>(st + L::sQ + stage_off(t, ch0));
+        rk[j] = *reinterpret_cast<const uint2*>(st + L::sK + stage_off(t, ch0));
+        rv[j] = *reinterpret_cast<const uint2*>(st + L::sV + stage_off(t, ch0));
+        if constexpr (BK == kChannel) rb[j] = *reinterpret_cast<const uint2*>(st + L::sB + stage_off(t, ch0));
+        if constexpr (WK == kChannel) rw[j] = *reinterpret_cast<const uint2*>(st + L::sW + stage_off(t, ch0));
+        if constexpr (BK != kChannel) stage_gate4<BK>(st + L::sB, t, ch0, 0.f, c4[j]);
+        if constexpr (WK != kChannel) stage_gate4<WK>(st + L::sW, t, ch0, 1.f, w4[j]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        unpack4(rq[j], q4[j]);
+        unpack4(rk[j], k4[j]);
+        unpack4(rv[j], x4[j]);
+        if constexpr (BK == kChannel) unpack4(rb[j], c4[j]);
+        if constexpr (WK == kChannel) unpack4(rw[j], w4[j]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int t = l16 + 16 * j;
+      float oq[4], ok_[4], oc[4], op[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        c4[j][i] *= k4[j][i];
+        x4[j][i] *= w4[j][i];
+        const float eq = __expf(G[j][i]);  // e^{G_t}
+        oq[i] = q4[j][i] * eq;
+        ok_[i] = k4[j][i] * __builtin_amdgcn_rcpf(eq);  // e^{-G_t}
+        if (TWO) {
+          const float ep = __expf(G[j][i] - la[j][i]);  // e^{G_{t-1}}
+          oc[i] = c4[j][i] * ep;
+          op[i] = -k4[j][i] * __builtin_amdgcn_rcpf(ep);  // stored negated
+        } else {
+          oc[i] = c4[j][i] * eq;
+          ok_[i] = -ok_[i];  // stored negated
+        }
+      }
+      *reinterpret_cast<uint2*>(tQ + t * LDT + ch0) = pack4(oq);
+      *reinterpret_cast<uint2*>(tK + t * LDT + ch0) = pack4(ok_);
+      *reinterpret_cast<uint2*>(tC + t * LDT + ch0) = pack4(oc);
+      if (TWO) *reinterpret_cast<uint2*>(tP + t * LDT + ch0) = pack4(op);
+      *reinterpret_cast<uint2*>(tX + t * LDT + ch0) = pack4(x4[j]);
+    }
+    lds_barrier_keep_vm();  // B1
+    bool flagged;
+    {
+      const int4 f0 = reinterpret_cast<const int4*>(sFlag)[0], f1 = reinterpret_cast<const int4*>(sFlag)[1];
+      flagged = (f0.x | f0.y | f0.z | f0.w | f1.x | f1.y | f1.z | f1.w) != 0;
+    }
+
+    if (flagged) {
+      // ---- exact token path: raw rows into LDS (q, k, c = b . k; decays in fp32, over the o
+      // staging, which holds nothing pending: a chunk's outputs are stored at the next chunk's
+      // start), then the recurrence token by token on the register-resident tiles ----
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int t = l16 + 16 * j;
+        float k4[4], c4[4];
+        unpack4(*reinterpret_cast<const uint2*>(st + L::sK + stage_off(t, ch0)), k4);
+        stage_gate4<BK>(st + L::sB, t, ch0, 0.f, c4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) c4[i] *= k4[i];
+        *reinterpret_cast<uint2*>(tQ + t * LDT + ch0) = *reinterpret_cast<const uint2*>(st + L::sQ + stage_off(t, ch0));
+        *reinterpret_cast<uint2*>(tK + t * LDT + ch0) = pack4(k4);
+        *reinterpret_cast<uint2*>(tC + t * LDT + ch0) = pack4(c4);
+        *reinterpret_cast<float4*>(fAl + t * LDF + ch0) =
+            make_float4(__expf(la[j][0]), __expf(la[j][1]), __expf(la[j][2]), __expf(la[j][3]));
+      }
+      lds_barrier_keep_vm();
+      if (wave < 2 && c + 1 < c_end) stage(c + 1, lane);
+      const auto ro = make_rsrc(a.o + ((bi * T + c * C) * H + hi) * DV, wy_range(T - c * C, H, DV));
+      __bf16* qt = PHI ? a.Qt + (bh * nch + c) * C * DK : nullptr;
+      // one state tile through the chunk, token by token (one tile per loop keeps the values the
+      // loop carries to 32); is_n: an N tile (writes X, read-outs to o), else Phi (read-outs to Q~)
+      auto run_tile = [&](f32x4 (&S)[8], bool is_n) {
+#pragma unroll 1
+        for (int t = 0; t < C; ++t) {
+          auto rowv = [&](const __bf16* base, int m, float* f) {
+            unpack4(*reinterpret_cast<const uint2*>(base + t * LDT + 16 * m + 4 * g), f);
+          };
+          auto decay = [&](int m, float* f) {
+            const float4 al = *reinterpret_cast<const float4*>(fAl + t * LDF + 16 * m + 4 * g);
+            f[0] = al.x; f[1] = al.y; f[2] = al.z; f[3] = al.w;
+          };
+          float r = 0.f;
+#pragma unroll
+          for (int m = 0; m < 8; ++m) {
+            float c4[4], a4[4];
+            rowv(tC, m, c4);
+            if (!TWO) decay(m, a4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              if (!TWO) S[m][i] *= a4[i];  // decay first
+              r += c4[i] * S[m][i];
+            }
+          }
+          r += __shfl_xor(r, 16);
+          r += __shfl_xor(r, 32);
+          const float x = is_n ? static_cast<float>(tX[t * LDT + col]) : 0.f;
+          float y = 0.f;
+#pragma unroll
+          for (int m = 0; m < 8; ++m) {
+            float q4[4], k4[4], a4[4];
+            rowv(tQ, m, q4);
+            rowv(tK, m, k4);
+            if (TWO) decay(m, a4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              float sv = S[m][i] - k4[i] * r;
+              if (TWO) sv *= a4[i];
+              sv += k4[i] * x;
+              S[m][i] = sv;
+              y += q4[i] * sv;
+            }
+          }
+          y += __shfl_xor(y, 16);
+          y += __shfl_xor(y, 32);
+          if (g == 0) {
+            if (is_n)
+              __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, static_cast<__bf16>(y)),
+                                                    ro, static_cast<uint32_t>(t) * hdv + col * 2, 0, 0);
+            else
+              qt[t * DK + seg_pair_pos(col)] = static_cast<__bf16>(y);
+          }
+        }
+      };
+      run_tile(SN, true);
+      if constexpr (PHI) run_tile(SP, false);
+      lds_barrier_keep_vm();
+      // the decays overlaid the o staging; the Gram arrays' upper tiles still read zero
+      out_pending = false;
+      continue;
+    }
+
+    // ---- 3. the next chunk's inputs: their staging has been read ----
+    if (wave < 2 && c + 1 < c_end) stage(c + 1, lane);
+
+    // ---- 4. Gram tiles: 6 jobs = 2 row operands x 3 lower tile pairs (waves 2-7) ----
+    if (wave >= 2) {
+      const int job = wave - 2, grp = job / 3, tix = job % 3;
+      const int ta = tix >= 1 ? 1 : 0, tb = tix == 2 ? 1 : 0;
+      const __bf16* ar = (grp == 0 ? tC : tQ) + (16 * ta + l16) * LDT;
+      const __bf16* br = ((TWO && grp == 0) ? tP : tK) + (16 * tb + l16) * LDT;
+      const __bf16* cr = (grp == 0 ? tK : tP) + (16 * tb + l16) * LDT;
+      F8 fa[4], fb[4], fc[4];
+#pragma unroll
+      for (int kb = 0; kb < DK / 32; ++kb) {
+        fa[kb] = lds_load8(ar + 32 * kb + 8 * g);
+        fb[kb] = lds_load8(br + 32 * kb + 8 * g);
+        if (TWO) fc[kb] = lds_load8(cr + 32 * kb + 8 * g);
+      }
+      f32x4 acc1 = zero4(), acc2 = zero4();
+#pragma unroll
+      for (int kb = 0; kb < DK / 32; ++kb) {
+        acc1 = MM::mma8(fa[kb], fb[kb], acc1);
+        if (TWO) acc2 = MM::mma8(fa[kb], fc[kb], acc2);
+      }
+      // which: 0 = -L_P / -L (strict; the off-diagonal block transposed -> gA, the diagonal
+      // blocks -> Ld negated back), 1 = -M_QP / -M, 2 = L_K (strict), 3 = M_QK (inclusive).  The
+      // products against the negated key family (which 0 and 1) arrive negated.
+      auto store_tile = [&](int which, const f32x4& acc) {
+        const int r0 = 16 * ta + 4 * g, cc = 16 * tb + l16;
+        if (ta > tb) {
+          if (which == 0) {  // (-L_10)^T: row l16, columns 4 g .. 4 g + 3
+            float a4[4] = {acc[0], acc[1], acc[2], acc[3]};
+            *reinterpret_cast<uint2*>(gA + l16 * LDA + 4 * g) = pack4(a4);
+            return;
+          }
+          __bf16* dst = (which == 1 ? gM : which == 2 ? gLK : gMQK) + r0 * LDD + cc;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) dst[i * LDD] = static_cast<__bf16>(acc[i]);
+          return;
+        }
+        const bool strict = which == 0 || which == 2;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = r0 + i;
+          const float val = (strict ? (cc < r) : (cc <= r)) ? acc[i] : 0.f;
+          if (which == 0)
+            Ld[(ta * 16 + (r & 15)) * LDL + (cc & 15)] = -val;
+          else if (which == 1)
+            gM[r * LDD + cc] = static_cast<__bf16>(val);
+          else if (which == 2)
+            gLK[r * LDD + cc] = static_cast<__bf16>(val);
+          else
+            gMQK[r * LDD + cc] = static_cast<__bf16>(val);
+        }
+      };
+      if (TWO) {
+        store_tile(grp == 0 ? 0 : 3, acc1);
+        store_tile(grp == 0 ? 2 : 1, acc2);
+      } else {
+        store_tile(grp == 0 ? 0 : 1, acc1);
+      }
+    }
+    lds_barrier_keep_vm();  // B2
+
+    // ---- 5. the state.  U = Cs S (channel contraction, N and Phi), Z = L_K X (MODE 2) or -X;
+    // T = (I + L)^{-1} in every wave (seg_inv_sweep for the diagonal blocks, three small MFMAs for
+    // the off-diagonal one); R = T U + T Z; O^T = S^T Qs^T - R^T M^T (+ X^T M_QK^T); S update. ----
+    {
+      // operand loads first: their latencies overlap the conversions and the sweep
+      F8 cfr[2][4];  // rows 16 ta + l16 of Cs, channels 32 kb + pair(g)
+#pragma unroll
+      for (int ta = 0; ta < 2; ++ta)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) cfr[ta][kb] = lds_pair_frag_k<DK>(tC + (16 * ta + l16) * LDT, 32 * kb, g);
+      float nl[2][16];  // row l16 of -L_00 and -L_11
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) {
+          const float4 v = *reinterpret_cast<const float4*>(Ld + (16 * b + l16) * LDL + 4 * c4);
+          nl[b][4 * c4] = -v.x;
+          nl[b][4 * c4 + 1] = -v.y;
+          nl[b][4 * c4 + 2] = -v.z;
+          nl[b][4 * c4 + 3] = -v.w;
+        }
+      const bf16x4 nl10t = lds_load4(gA + l16 * LDA + 4 * g);  // (-L_10)^T [l16][4 g ..]
+      const F8 xf = seg_col_frag(tX, LDT, col, g, l16);        // X column col over the tokens
+      F8 lkf[2];
+      if (TWO) {
+#pragma unroll
+        for (int ta = 0; ta < 2; ++ta) lkf[ta] = lds_pair_frag_k<C>(gLK + (16 * ta + l16) * LDD, 0, g);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+
+      F8 sfN[4], sfP[4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        sfN[kb] = acc_pair_frag<__bf16>(SN[2 * kb], SN[2 * kb + 1]);
+        if constexpr (PHI) sfP[kb] = acc_pair_frag<__bf16>(SP[2 * kb], SP[2 * kb + 1]);
+      }
+      // U (the N and Phi tiles share each Cs fragment)
+      f32x4 UN[2], UP[2];
+#pragma unroll
+      for (int ta = 0; ta < 2; ++ta) {
+        UN[ta] = zero4();
+        UP[ta] = zero4();
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          UN[ta] = MM::mma8(cfr[ta][kb], sfN[kb], UN[ta]);
+          if constexpr (PHI) UP[ta] = MM::mma8(cfr[ta][kb], sfP[kb], UP[ta]);
+        }
+      }
+      F8 zf;  // Z over the tokens (k) for column col
+      if (TWO) {
+        const f32x4 z0 = MM::mma8(lkf[0], xf, zero4()), z1 = MM::mma8(lkf[1], xf, zero4());
+        zf = acc_pair_frag<__bf16>(z0, z1);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) zf[e] = -xf[e];
+      }
+      // T as A operands: rows 16 ta + l16, tokens in pair order.  The lane's sweep values are
+      // D_b[l16][4 g .. 4 g + 3], already that layout; T_10 arrives in it as the accumulator of
+      // T_10^T = D_0^T ((-L_10)^T D_1^T).
+      float d[2][4];
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) d[b][e] = (4 * g + e == l16) ? 1.f : 0.f;
+      seg_inv_sweep<0>(d, nl);
+      const bf16x4 d0 = __builtin_bit_cast(bf16x4, pack4(d[0])), d1 = __builtin_bit_cast(bf16x4, pack4(d[1]));
+      f32x4 id;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) id[e] = (4 * g + e == l16) ? 1.f : 0.f;
+      const f32x4 D0 = MM::mma4(d0, acc_frag4<__bf16>(id), zero4());                 // D_0[4 g + i][l16]
+      const f32x4 Qm = MM::mma4(nl10t, d1, zero4());                                  // (-L_10)^T D_1^T
+      const f32x4 T10t = MM::mma4(acc_frag4<__bf16>(D0), acc_frag4<__bf16>(Qm), zero4());  // T_10[l16][4 g + i]
+      F8 tf0, tf1;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        tf0[e] = d0[e];
+        tf0[4 + e] = static_cast<__bf16>(0.f);
+        tf1[e] = static_cast<__bf16>(T10t[e]);
+        tf1[4 + e] = d1[e];
+      }
+      // R = T (U + Z), tokens 16 ta + 4 g + i, column col
+      const F8 ufN = acc_pair_frag<__bf16>(UN[0], UN[1]);
+      F8 ufP;
+      if constexpr (PHI) ufP = acc_pair_frag<__bf16>(UP[0], UP[1]);
+      f32x4 RN[2], RP[2];
+      RN[0] = MM::mma8(tf0, ufN, MM::mma8(tf0, zf, zero4()));
+      RN[1] = MM::mma8(tf1, ufN, MM::mma8(tf1, zf, zero4()));
+      if constexpr (PHI) {
+        RP[0] = MM::mma8(tf0, ufP, zero4());
+        RP[1] = MM::mma8(tf1, ufP, zero4());
+      }
+      const F8 rfN = acc_pair_frag<__bf16>(RN[0], RN[1]);
+      F8 rfP;
+      if constexpr (PHI) rfP = acc_pair_frag<__bf16>(RP[0], RP[1]);
+      // O^T: lane holds O[token 16 ta + l16][column 16 w + 4 g + i], into the o (and Q~) staging
+#pragma unroll
+      for (int ta = 0; ta < 2; ++ta) {
+        F8 qf[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) qf[kb] = lds_pair_frag_k<DK>(tQ + (16 * ta + l16) * LDT, 32 * kb, g);
+        const F8 mf = lds_pair_frag_k<C>(gM + (16 * ta + l16) * LDD, 0, g);
+        F8 mqf;
+        if (TWO) mqf = lds_pair_frag_k<C>(gMQK + (16 * ta + l16) * LDD, 0, g);
+        f32x4 oN = zero4(), oP = zero4();
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          oN = MM::mma8(sfN[kb], qf[kb], oN);
+          if constexpr (PHI) oP = MM::mma8(sfP[kb], qf[kb], oP);
+        }
+        oN = MM::mma8(rfN, mf, oN);
+        if constexpr (PHI) oP = MM::mma8(rfP, mf, oP);
+        if (TWO) oN = MM::mma8(xf, mqf, oN);
+        const int t = 16 * ta + l16;
+        float o4[4] = {oN[0], oN[1], oN[2], oN[3]};
+        *reinterpret_cast<uint2*>(tO + t * LDT + ch0) = pack4(o4);
+        if constexpr (PHI) {
+          float p4[4] = {oP[0], oP[1], oP[2], oP[3]};
+          *reinterpret_cast<uint2*>(tQt + t * LDT + ch0) = pack4(p4);
+        }
+      }
+      // S update: S += Ks^T X + (-Ps)^T R (MODE 2) or S += (-Ks)^T R (MODE 1), then S = e^{G_n} . S
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const F8 kf = seg_col_frag(tK, LDT, 16 * m + l16, g, l16);
+        if (TWO) {
+          const F8 pf = seg_col_frag(tP, LDT, 16 * m + l16, g, l16);
+          SN[m] = MM::mma8(kf, xf, SN[m]);
+          SN[m] = MM::mma8(pf, rfN, SN[m]);
+          if constexpr (PHI) SP[m] = MM::mma8(pf, rfP, SP[m]);
+        } else {
+          SN[m] = MM::mma8(kf, rfN, SN[m]);
+          if constexpr (PHI) SP[m] = MM::mma8(kf, rfP, SP[m]);
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const float4 f = *reinterpret_cast<const float4*>(fG + 16 * m + 4 * g);
+        SN[m][0] *= f.x;
+        SN[m][1] *= f.y;
+        SN[m][2] *= f.z;
+        SN[m][3] *= f.w;
+        if constexpr (PHI) {
+          SP[m][0] *= f.x;
+          SP[m][1] *= f.y;
+          SP[m][2] *= f.z;
+          SP[m][3] *= f.w;
+        }
+      }
+    }
+    lds_barrier_keep_vm();  // B6: this chunk's operands are no longer read
+    out_pending = true;
+  }
+  if (wave >= 4 && out_pending) store_out(c_end - 1, tid);
+
+  // ---- end of the segment: the final state (one segment), or N, Phi and E_1 (from segment 0) ----
+  if (a.nseg == 1) {
+    if (a.S_T != nullptr) {
+      float* St = a.S_T + bh * DK * DV;
+#pragma unroll
+      for (int m = 0; m < 8; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) St[(16 * m + 4 * g + i) * DV + col] = SN[m][i];
+    }
+  } else {
+    const int64_t sb = bh * a.nseg + seg;
+    float* No = PHI ? a.Nseg + sb * DK * DV : a.Eseg + (sb + 1) * DK * DV;
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * m + 4 * g + i;
+        No[row * DV + col] = SN[m][i];
+        if constexpr (PHI) a.Pseg[sb * DK * DK + row * DK + col] = SP[m][i];
+      }
+  }
+}
+
+template <int MODE, int AK, int BK, int WK>
+__global__ __launch_bounds__(512) void seg_kernel(SegArgs a) {
+  using L = SegLayout<MODE, AK, BK, WK>;
+  static_assert(L::fits, "LDS layout exceeds the gfx950 workgroup limit");
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[L::total];
+  const int64_t bh = blockIdx.x / a.nseg, seg = blockIdx.x % a.nseg;
+  if (seg == 0)
+    seg_body<MODE, AK, BK, WK, false>(a, smem, bh, seg);
+  else
+    seg_body<MODE, AK, BK, WK, true>(a, smem, bh, seg);
+}
+
+// x = hi + lo in bf16 (hi the rounding of x, lo that of the remainder): products of such pairs
+// taken as hi hi + hi lo + lo hi carry about 16 significant bits, where one bf16 product keeps 8.
+__device__ __forceinline__ void seg_split8(const float* x, Mma<__bf16>::F8& hi, Mma<__bf16>::F8& lo) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    hi[e] = static_cast<__bf16>(x[e]);
+    lo[e] = static_cast<__bf16>(x[e] - static_cast<float>(hi[e]));
+  }
+}
+
+constexpr int kChainCols = 32;  // value columns per chain workgroup
+
+// ---- segment chain: E_{s+1} = Phi_s E_s + N_s ----
+// E_1 is segment 0's exit state (seg_kernel writes it to Eseg slot 1).  Writes every E_s
+// (1 <= s < nseg) as bf16, transposed and in pair order, into Ebf for the correction, and E_nseg
+// into S_T.  One workgroup of 4 waves per (state, 32 value columns); wave w computes rows
+// 32 w .. 32 w + 31 of E (two 16-row tiles by two 16-column tiles) on MFMA, in the three-term bf16
+// form of seg_split8 with fp32 accumulation.  The two row tiles of wave w are, as accumulators,
+// exactly the B operands of k block w for every wave: each step passes them through LDS.  The next
+// segment's Phi and N are loaded while the current product runs.
+__global__ __launch_bounds__(256) void seg_chain_kernel(SegArgs a) {
+  using MM = Mma<__bf16>;
+  using F8 = MM::F8;
+  constexpr int DK = 128, DV = 128, NB = DV / kChainCols;
+  __shared__ __attribute__((aligned(16))) uint4 sB[2][4][2][2][64];  // [buffer][kb][n][hi, lo][lane]
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
+  const int64_t bh = blockIdx.x / NB, c0 = (blockIdx.x % NB) * kChainCols;
+  const int64_t nseg = a.nseg;
+
+  f32x4 acc[2][2];  // [row tile 2 w + mt][column tile n]: rows 32 w + 16 mt + 4 g + i, column c0 + 16 n + l16
+  {
+    const float* E1 = a.Eseg + (bh * nseg + 1) * DK * DV;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int n = 0; n < 2; ++n)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[mt][n][i] = E1[(32 * w + 16 * mt + 4 * g + i) * DV + c0 + 16 * n + l16];
+  }
+  float4 ph[2][4][2];  // Phi rows 32 w + 16 mt + l16, channels 32 kb + 16 h + 4 g .. + 3
+  float nx[2][2][4];   // N at the accumulator positions
+  auto load_next = [&](int64_t s) {
+    const float* P = a.Pseg + (bh * nseg + s) * DK * DK;
+    const float* Nn = a.Nseg + (bh * nseg + s) * DK * DV;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          ph[mt][kb][h] = *reinterpret_cast<const float4*>(P + (32 * w + 16 * mt + l16) * DK + 32 * kb + 16 * h + 4 * g);
+#pragma unroll
+      for (int n = 0; n < 2; ++n)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) nx[mt][n][i] = Nn[(32 * w + 16 * mt + 4 * g + i) * DV + c0 + 16 * n + l16];
+    }
+  };
+  if (nseg > 1) load_next(1);
+  for (int64_t s = 1; s < nseg; ++s) {
+    const int buf = static_cast<int>(s & 1);
+    // E_s: its bf16 transposed copy and its B operands
+    __bf16* eb = a.Ebf + (bh * nseg + s) * DV * DK;
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        float e4[4] = {acc[mt][n][0], acc[mt][n][1], acc[mt][n][2], acc[mt][n][3]};
+        *reinterpret_cast<uint2*>(eb + (c0 + 16 * n + l16) * DK + 32 * w + 8 * g + 4 * mt) = pack4(e4);
+      }
+      float x[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[i] = acc[0][n][i];
+        x[4 + i] = acc[1][n][i];
+      }
+      F8 hi, lo;
+      seg_split8(x, hi, lo);
+      sB[buf][w][n][0][lane] = __builtin_bit_cast(uint4, hi);
+      sB[buf][w][n][1][lane] = __builtin_bit_cast(uint4, lo);
+    }
+    lds_barrier();
+    F8 ah[2][4], al[2][4];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const float x[8] = {ph[mt][kb][0].x, ph[mt][kb][0].y, ph[mt][kb][0].z, ph[mt][kb][0].w,
+                            ph[mt][kb][1].x, ph[mt][kb][1].y, ph[mt][kb][1].z, ph[mt][kb][1].w};
+        seg_split8(x, ah[mt][kb], al[mt][kb]);
+      }
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int n = 0; n < 2; ++n)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[mt][n][i] = nx[mt][n][i];
+    if (s + 1 < nseg) load_next(s + 1);
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int n = 0; n < 2; ++n) {
+        const F8 bh_ = __builtin_bit_cast(F8, sB[buf][kb][n][0][lane]);
+        const F8 bl_ = __builtin_bit_cast(F8, sB[buf][kb][n][1][lane]);
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          acc[mt][n] = MM::mma8(ah[mt][kb], bh_, acc[mt][n]);
+          acc[mt][n] = MM::mma8(ah[mt][kb], bl_, acc[mt][n]);
+          acc[mt][n] = MM::mma8(al[mt][kb], bh_, acc[mt][n]);
+        }
+      }
+  }
+  if (a.S_T != nullptr) {
+    float* St = a.S_T + bh * DK * DV;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int n = 0; n < 2; ++n)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) St[(32 * w + 16 * mt + 4 * g + i) * DV + c0 + 16 * n + l16] = acc[mt][n][i];
+  }
+}
+
+constexpr int kFixGroup = 8;  // chunks per correction workgroup
+
+// ---- correction: o_c += Q~_c E_s for every chunk c of segments s > 0 ----
+// One workgroup of 4 waves per (state, segment s > 0, group of up to 8 of its chunks); wave w takes
+// value column tiles 2 w, 2 w + 1 and keeps their rows of E_s^T as A operands for the whole group.
+// O^T tile (columns 16 n + 4 g + i, tokens 16 ta + l16) = E^T Q~^T: B = rows of Q~.  Both arrays
+// are stored in pair order, so every operand is one 16-byte load.  The next chunk's Q~ and o are
+// loaded while the current one is computed.
+__global__ __launch_bounds__(256) void seg_fix_kernel(SegArgs a) {
+  using MM = Mma<__bf16>;
+  using F8 = MM::F8;
+  constexpr int DK = 128, DV = 128, C = kSegC;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
+  const int64_t ngrp = (a.L + kFixGroup - 1) / kFixGroup;
+  int64_t blk = blockIdx.x;
+  const int64_t grp = blk % ngrp;
+  blk /= ngrp;
+  const int64_t s = 1 + blk % (a.nseg - 1), bh = blk / (a.nseg - 1);
+  const int64_t seg_end = (s + 1) * a.L < a.nch ? (s + 1) * a.L : a.nch;
+  const int64_t c0 = s * a.L + grp * kFixGroup;
+  const int64_t c1 = c0 + kFixGroup < seg_end ? c0 + kFixGroup : seg_end;
+  if (c0 >= c1) return;  // past the end of a shorter last segment
+  const int64_t bi = bh / a.H, hi = bh % a.H;
+  const uint32_t hdv = static_cast<uint32_t>(a.H * DV * 2);
+  const __bf16* eb = a.Ebf + (bh * a.nseg + s) * DV * DK;
+  F8 ef[2][4];
+#pragma unroll
+  for (int n = 0; n < 2; ++n)
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+      ef[n][kb] = *reinterpret_cast<const F8*>(eb + (16 * (2 * wave + n) + l16) * DK + 32 * kb + 8 * g);
+
+  F8 qf[2][4];
+  uint2 ov[2][2];
+  auto load = [&](int64_t c, F8 (&q)[2][4], uint2 (&o)[2][2]) {
+    const __bf16* qt = a.Qt + (bh * a.nch + c) * C * DK;
+    const int64_t t0 = c * C;
+    const auto ro = make_rsrc(a.o + ((bi * a.T + t0) * a.H + hi) * DV, wy_range(a.T - t0, a.H, DV));
+#pragma unroll
+    for (int ta = 0; ta < 2; ++ta) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) q[ta][kb] = *reinterpret_cast<const F8*>(qt + (16 * ta + l16) * DK + 32 * kb + 8 * g);
+      const uint32_t t = static_cast<uint32_t>(16 * ta + l16);
+#pragma unroll
+      for (int n = 0; n < 2; ++n) o[ta][n] = buf_load8(ro, t * hdv + (16 * (2 * wave + n) + 4 * g) * 2);
+    }
+  };
+  load(c0, qf, ov);
+  for (int64_t c = c0; c < c1; ++c) {
+    F8 qn[2][4];
+    uint2 on[2][2];
+    if (c + 1 < c1) load(c + 1, qn, on);
+    const int64_t t0 = c * C;
+    const auto ro = make_rsrc(a.o + ((bi * a.T + t0) * a.H + hi) * DV, wy_range(a.T - t0, a.H, DV));
+#pragma unroll
+    for (int ta = 0; ta < 2; ++ta) {
+      const uint32_t t = static_cast<uint32_t>(16 * ta + l16);
+#pragma unroll
+      for (int n = 0; n < 2; ++n) {
+        float o4[4];
+        unpack4(ov[ta][n], o4);
+        f32x4 acc;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = o4[i];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) acc = MM::mma8(ef[n][kb], qf[ta][kb], acc);
+        float r4[4] = {acc[0], acc[1], acc[2], acc[3]};
+        buf_store8(ro, t * hdv + (16 * (2 * wave + n) + 4 * g) * 2, pack4(r4));
+      }
+    }
+    if (c + 1 < c1) {
+#pragma unroll
+      for (int ta = 0; ta < 2; ++ta) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) qf[ta][kb] = qn[ta][kb];
+#pragma unroll
+        for (int n = 0; n < 2; ++n) ov[ta][n] = on[ta][n];
+      }
+    }
+  }
+}
+
+}  // namespace gdr

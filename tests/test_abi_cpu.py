@@ -131,24 +131,48 @@ def test_empty_problem_is_a_no_op():
     assert call(prob(heads=0), **big_apart()) == N.GDR_OK
 
 
+def seg_workspace(nstate, T):
+    """Workspace of the fused segment prefill (d_k = d_v = 128 with the Gated DeltaNet-2 or KDA
+    gates): each state's 32-token chunks split into ceil(256 / states) segments (at
+    most one per chunk); with more than one segment, Q~ (32 x 128 bf16) per chunk and, per segment, N, Phi,
+    the state leaving segment 0 (128 x 128 fp32 each) and the entering state (bf16), each array
+    rounded up to 256 bytes.  None with one segment per state."""
+    r = lambda n: (n + 255) // 256 * 256
+    nch = (T + 31) // 32
+    want = max(1, min(nch, -(-256 // nstate)))
+    L = -(-nch // want)
+    nseg = -(-nch // L)
+    if nseg <= 1:
+        return 0
+    per = nstate * nseg * 128 * 128
+    return r(nstate * nch * 32 * 128 * 2) + 3 * r(per * 4) + r(per * 2)
+
+
 def test_workspace_query_and_decode_validation():
-    # per-channel decay (either order): the chunk's affine map A' (dk x dk), Q' (64 x dk), D^T
-    # (dv x dk), Z' (64 x dv) in bf16, e^{G_n} (dk + 4 fp32) and a flag per 64-token chunk of every
-    # (batch, head), each array rounded up to 256 bytes
     r = lambda n: (n + 255) // 256 * 256
+    # the fused segment kernel's shapes and gates
+    assert N.workspace_bytes(prob()) == seg_workspace(6, 70) > 0
+    assert N.workspace_bytes(prob(order=N.DECAY_THEN_ERASE)) == seg_workspace(6, 70)
+    assert N.workspace_bytes(prob(batch=64, heads=8, seqlen=70)) == 0  # one segment per state
+    # per-channel decay elsewhere (either order): the chunk's affine map A' (dk x dk), Q' (64 x
+    # dk), D^T (dv x dk), Z' (64 x dv) in bf16, e^{G_n} (dk + 4 fp32) and a flag per 64-token chunk
+    # of every (batch, head), each array rounded up to 256 bytes
     ch = 2 * 3 * 2
-    two = r(ch * 128 * 128 * 2) + r(ch * 64 * 128 * 2) + r(ch * 128 * 128 * 2) + \
-        r(ch * 64 * 128 * 2) + r(ch * 132 * 4) + r(ch * 4)
-    assert N.workspace_bytes(prob()) == two
-    assert N.workspace_bytes(prob(order=N.DECAY_THEN_ERASE)) == two
-    # scalar decay in bf16: W (64 x dk), U (64 x dv), -M (64 x 64), all bf16, and 132 fp32 gate
-    # exponentials per 64-token chunk of every (batch, head), each array rounded up to 256 bytes
-    sp = prob(alpha_kind=N.GATE_SCALAR, b_kind=N.GATE_SCALAR, w_kind=N.GATE_SCALAR)
+    two = r(ch * 64 * 64 * 2) + r(ch * 64 * 64 * 2) + r(ch * 128 * 64 * 2) + \
+        r(ch * 64 * 128 * 2) + r(ch * 68 * 4) + r(ch * 4)
+    assert N.workspace_bytes(prob(dk=64)) == two
+    assert N.workspace_bytes(prob(dk=64, order=N.DECAY_THEN_ERASE)) == two
+    # scalar decay in bf16 with a scalar erase gate and no write gate: W (64 x dk), U (64 x dv), -M
+    # (64 x 64), all bf16, and 132 fp32 gate exponentials per 64-token chunk of every (batch, head),
+    # each array rounded up to 256 bytes
+    sp = prob(alpha_kind=N.GATE_SCALAR, b_kind=N.GATE_SCALAR, w_kind=N.GATE_NONE)
     chunks = 2 * 3 * 2  # batch 2, heads 3, ceil(70 / 64) = 2
-    r = lambda n: (n + 255) // 256 * 256
     need = r(chunks * 64 * 128 * 2) + r(chunks * 64 * 128 * 2) + r(chunks * 64 * 64 * 2) + \
         r(chunks * 132 * 4)
     assert N.workspace_bytes(sp) == need
+    # (a scalar decay takes this kernel with any write gate, d_k = d_v = 128 included)
+    assert N.workspace_bytes(prob(alpha_kind=N.GATE_SCALAR, b_kind=N.GATE_SCALAR,
+                                  w_kind=N.GATE_SCALAR)) == need
     assert N.workspace_bytes(prob(alpha_kind=N.GATE_SCALAR, b_kind=N.GATE_SCALAR, w_kind=N.GATE_SCALAR,
                                   io_dtype=N.GDR_FP32, dk=32, dv=32)) == 0
     a = big_apart()

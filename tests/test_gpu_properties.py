@@ -7,8 +7,8 @@
 - Column independence: the transition multiplies S from the left ("Recurrent Memory: Write,
   Erase, Decay, Read", section 05), so each value column of S and o evolves on its own.
   Permuting the columns of v (and of a per-channel write gate) and of S0 permutes those of o and
-  S_T; a state's result does not depend on how many other states share the call (which changes the
-  column slicing of the per-state kernels).
+  S_T; a state's result does not depend on how many other states share the call beyond rounding
+  (bit for bit where only the column slicing of a per-state kernel changes).
 - Determinism: the same call twice gives the same bits.
 - In place: S_T may be S0 (the header promises it) on every kernel family.
 - Parity at the shapes added to the boundary: the all-fp32 mode at d_k = 64, 128 and 256, bf16
@@ -140,13 +140,17 @@ def test_same_call_same_bits(dev, kind, D, DV, dtype):
     assert torch.equal(o1, o2) and torch.equal(S1, S2)
 
 
-@pytest.mark.parametrize("kind", ["gdn", "gdn2", "kda", "gla"])
-def test_state_result_does_not_depend_on_the_other_states(dev, kind):
-    """Two states alone, then the same two as the first heads of a 64-state call: the per-state
-    kernels take wider column slices with more states (and the chunk-local kernels see more
-    chunks), yet every column of a state follows the same arithmetic, so the bits agree."""
-    small = case(kind, B=1, H=2, T=300, seed=231)
-    big = case(kind, B=1, H=64, T=300, seed=232)
+@pytest.mark.parametrize("kind,D,segmented", [("gdn", 128, True), ("gdn2", 128, True), ("kda", 128, True),
+                                               ("gla", 128, False), ("gdn2", 64, False), ("kda", 32, False)])
+def test_state_result_among_other_states(dev, kind, D, segmented):
+    """Two states alone, then the same two as the first heads of a 64-state call.  Where the
+    column slicing of a per-state kernel changes with the number of states, every column still
+    follows the same arithmetic, so the bits agree.  The fused segment kernel (d_k = d_v = 128 with
+    the Gated DeltaNet, KDA and Gated DeltaNet-2 gates) splits each sequence into more segments
+    when there are fewer states, which moves rounding: there the two results agree within the
+    tolerance, and both meet it against the oracle."""
+    small = case(kind, B=1, H=2, T=300, D=D, seed=231)
+    big = case(kind, B=1, H=64, T=300, D=D, seed=232)
     xs, xb = synth.make_prefill(small), synth.make_prefill(big)
     for n in xs:
         if xs[n] is None:
@@ -160,8 +164,13 @@ def test_state_result_does_not_depend_on_the_other_states(dev, kind):
     o_b, S_b = fwd(gb)
     torch.cuda.synchronize()
     d_o, d_s = max_diff(o_s, o_b[:, :, :2]), max_diff(S_s, S_b[:, :2])
-    say("%s: 2 states alone vs among 64: max|do| = %.3e max|dS| = %.3e" % (kind, d_o, d_s))
-    assert d_o == 0.0 and d_s == 0.0
+    say("%s d%d: 2 states alone vs among 64: max|do| = %.3e max|dS| = %.3e" % (kind, D, d_o, d_s))
+    if not segmented:
+        assert d_o == 0.0 and d_s == 0.0
+    else:
+        check(xs, o_s, S_s, "erase_then_decay", TOL["bf16"], "%s alone" % kind)
+        check(xs, o_b[:, :, :2], S_b[:, :2], "erase_then_decay", TOL["bf16"], "%s among 64" % kind)
+        assert d_o <= TOL["bf16"][0]
 
 
 @pytest.mark.parametrize("kind,dtype", [("gdn", "bf16"), ("gdn2", "bf16"), ("gla", "bf16"), ("gdn2", "fp32")])
