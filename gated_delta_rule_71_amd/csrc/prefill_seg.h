@@ -50,10 +50,11 @@ struct SegArgs {
   const float* S0;
   bf16_t* o;
   float* S_T;
-  __bf16* Qt;     // [state][nch][32][dk]  Q~ of every chunk of segments > 0, channels in pair order
-  float* Nseg;    // [state][nseg][dk][dv] state from zero over segment s (s > 0)
+  __bf16* Qt;     // [state][nch] blocks of 32 x dk: Q~ of every chunk of segments > 0 (seg_qt_pos)
+  __bf16* On;     // [state][nch] blocks of 32 x dv: the read-out of N, same chunks (seg_on_pos)
+  float* Nseg;    // [state][nseg] blocks of dk x dv: state from zero over segment s > 0 (seg_acc_pos)
   float* Pseg;    // [state][nseg][dk][dk] transition of segment s (s > 0)
-  float* Eseg;    // [state][nseg][dk][dv] slot 1: the state leaving segment 0
+  float* Eseg;    // [state][nseg] blocks of dk x dv, slot 1: the state leaving segment 0 (seg_acc_pos)
   __bf16* Ebf;    // [state][nseg][dv][dk] the state entering segment s, bf16, transposed, pair order
   int64_t T, H, Hk, nch;
   int64_t nseg, L;  // segments per state, chunks per segment (the last may be shorter)
@@ -111,11 +112,22 @@ __device__ __forceinline__ void seg_dma16(const void* base, uint32_t bytes, unsi
                : "memory", "m0");
 }
 
-// Position of channel ch in a row stored in pair order: within each block of 32 channels, the
-// 16-byte piece g holds channels 4 g .. 4 g + 3 and 16 + 4 g .. 16 + 4 g + 3, the k values lane
-// group g of an MFMA operand takes.
-__device__ __forceinline__ int seg_pair_pos(int ch) {
-  return (ch & ~31) + 8 * ((ch & 15) >> 2) + 4 * ((ch >> 4) & 1) + (ch & 3);
+// Positions inside one chunk's block of the segment read-outs, in the order the correction kernel
+// takes them as MFMA operands, so that each of its loads is contiguous across the wave.  On holds
+// O[t][col] (the read-out of N) as the accumulators of the chunk kernel: [t / 16][col / 16][lane]
+// [4], lane = 16 ((col % 16) / 4) + t % 16.  Qt holds Q~[t][ch] as B operands over the channels:
+// [t / 16][ch / 32][lane][8], the 8 being channels 4 g .. 4 g + 3 and 16 + 4 g .. 16 + 4 g + 3 of
+// the 32-channel block, g = (ch % 16) / 4.
+// N and the state leaving segment 0 keep the chunk kernel's accumulator order:
+// [col / 16][row / 16][lane][4], lane = 16 ((row % 16) / 4) + col % 16, the 4 being row % 4.
+__device__ __forceinline__ int seg_acc_pos(int row, int col) {
+  return (((col >> 4) * 8 + (row >> 4)) * 64 + ((row & 15) >> 2) * 16 + (col & 15)) * 4 + (row & 3);
+}
+__device__ __forceinline__ int seg_on_pos(int t, int col) {
+  return (((t >> 4) * 8 + (col >> 4)) * 64 + ((col & 15) >> 2) * 16 + (t & 15)) * 4 + (col & 3);
+}
+__device__ __forceinline__ int seg_qt_pos(int t, int ch) {
+  return (((t >> 4) * 4 + (ch >> 5)) * 64 + ((ch & 15) >> 2) * 16 + (t & 15)) * 8 + ((ch >> 4) & 1) * 4 + (ch & 3);
 }
 
 // Sums over the 16 lanes of a row (lanes 16 r .. 16 r + 15): the inclusive prefix up to this lane,
@@ -184,9 +196,9 @@ struct SegLayout {
   static constexpr int sLA = sV + CH;
   static constexpr int sB = sLA + (AK == kChannel ? CH : SC);
   static constexpr int sW = sB + (BK == kChannel ? CH : SC);
-  static constexpr int oO = sW + (WK == kChannel ? CH : SC);  // o rows [32][LDT] bf16, then Q~ rows
-  static constexpr int oAL = oO;                        // flagged chunks: decays [32][LDF] fp32 over o, Q~
-  static constexpr int oF0 = oO + 2 * ROWS > oAL + C * LDF * 4 ? oO + 2 * ROWS : oAL + C * LDF * 4;
+  static constexpr int oO = sW + (WK == kChannel ? CH : SC);  // o rows [32][LDT] bf16 (first segment)
+  static constexpr int oAL = oO;                        // flagged chunks: decays [32][LDF] fp32 over o
+  static constexpr int oF0 = oO + ROWS > oAL + C * LDF * 4 ? oO + ROWS : oAL + C * LDF * 4;
   static constexpr int oF = (oF0 + 15) / 16 * 16;       // fp32 e^{G_n} [DK]
   static constexpr int oFL = oF + DK * 4;               // per-wave flags [8] (int)
   static constexpr int total = oFL + 8 * 4;
@@ -260,7 +272,6 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, unsigned char* smem, 
   __bf16* gMQK = reinterpret_cast<__bf16*>(smem + L::oMQK);
   float* Ld = reinterpret_cast<float*>(smem + L::oLD);
   __bf16* tO = reinterpret_cast<__bf16*>(smem + L::oO);         // o rows of the chunk
-  __bf16* tQt = tO + C * LDT;                                     // Q~ rows of the chunk
   float* fAl = reinterpret_cast<float*>(smem + L::oAL);
   float* fG = reinterpret_cast<float*>(smem + L::oF);   // e^{G_n}
   int* sFlag = reinterpret_cast<int*>(smem + L::oFL);
@@ -326,7 +337,8 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, unsigned char* smem, 
     if constexpr (WK == kScalar) scalar(make_rsrc(a.wg + rr, wy_range(left, H, 1)), scW);
   };
 
-  // ---- copies of a chunk's read-outs from LDS to o and Q~ (waves 4-7) ----
+  // ---- copies of a chunk's read-outs from LDS to o (waves 4-7; the first segment only: the others
+  // write theirs to On and Qt straight from the accumulators) ----
   auto store_out = [&](int64_t c, int tid) {
     const int64_t t0 = c * C, left = T - t0;
     const auto ro = make_rsrc(a.o + ((bi * T + t0) * H + hi) * DV, wy_range(left, H, DV));
@@ -336,12 +348,6 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, unsigned char* smem, 
       const int t = (l >> 4) + 16 * u, piece = l & 15;
       const uint4 v = *reinterpret_cast<const uint4*>(tO + t * LDT + 8 * piece);
       buf_store16(ro, static_cast<uint32_t>(t) * hdv + piece * 16, v);
-      if constexpr (PHI) {  // Q~ in the pair order of its channels (seg_pair_pos)
-        const int cb = 32 * (piece >> 2) + 4 * (piece & 3);
-        const uint2 lo = *reinterpret_cast<const uint2*>(tQt + t * LDT + cb);
-        const uint2 hi = *reinterpret_cast<const uint2*>(tQt + t * LDT + cb + 16);
-        *reinterpret_cast<uint4*>(a.Qt + ((bh * nch + c) * C + t) * DK + 8 * piece) = make_uint4(lo.x, lo.y, hi.x, hi.y);
-      }
     }
   };
 
@@ -464,6 +470,7 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, unsigned char* smem, 
       if (wave < 2 && c + 1 < c_end) stage(c + 1, lane);
       const auto ro = make_rsrc(a.o + ((bi * T + c * C) * H + hi) * DV, wy_range(T - c * C, H, DV));
       __bf16* qt = PHI ? a.Qt + (bh * nch + c) * C * DK : nullptr;
+      __bf16* on = PHI ? a.On + (bh * nch + c) * C * DV : nullptr;
       // one state tile through the chunk, token by token (one tile per loop keeps the values the
       // loop carries to 32); is_n: an N tile (writes X, read-outs to o), else Phi (read-outs to Q~)
       auto run_tile = [&](f32x4 (&S)[8], bool is_n) {
@@ -510,11 +517,13 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, unsigned char* smem, 
           y += __shfl_xor(y, 16);
           y += __shfl_xor(y, 32);
           if (g == 0) {
-            if (is_n)
+            if (!is_n)
+              qt[seg_qt_pos(t, col)] = static_cast<__bf16>(y);
+            else if (PHI)
+              on[seg_on_pos(t, col)] = static_cast<__bf16>(y);
+            else
               __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, static_cast<__bf16>(y)),
                                                     ro, static_cast<uint32_t>(t) * hdv + col * 2, 0, 0);
-            else
-              qt[t * DK + seg_pair_pos(col)] = static_cast<__bf16>(y);
           }
         }
       };
@@ -703,10 +712,15 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, unsigned char* smem, 
         if (TWO) oN = MM::mma8(xf, mqf, oN);
         const int t = 16 * ta + l16;
         float o4[4] = {oN[0], oN[1], oN[2], oN[3]};
-        *reinterpret_cast<uint2*>(tO + t * LDT + ch0) = pack4(o4);
         if constexpr (PHI) {
+          // straight from the accumulators: seg_on_pos / seg_qt_pos of (t, 16 w + 4 g)
           float p4[4] = {oP[0], oP[1], oP[2], oP[3]};
-          *reinterpret_cast<uint2*>(tQt + t * LDT + ch0) = pack4(p4);
+          __bf16* on = a.On + (bh * nch + c) * C * DV;
+          __bf16* qt = a.Qt + (bh * nch + c) * C * DK;
+          *reinterpret_cast<uint2*>(on + ((ta * 8 + wave) * 64 + lane) * 4) = pack4(o4);
+          *reinterpret_cast<uint2*>(qt + ((ta * 4 + (wave >> 1)) * 64 + lane) * 8 + (wave & 1) * 4) = pack4(p4);
+        } else {
+          *reinterpret_cast<uint2*>(tO + t * LDT + ch0) = pack4(o4);
         }
       }
       // S update: S += Ks^T X + (-Ps)^T R (MODE 2) or S += (-Ks)^T R (MODE 1), then S = e^{G_n} . S
@@ -739,7 +753,7 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, unsigned char* smem, 
       }
     }
     lds_barrier_keep_vm();  // B6: this chunk's operands are no longer read
-    out_pending = true;
+    out_pending = !PHI;
   }
   if (wave >= 4 && out_pending) store_out(c_end - 1, tid);
 
@@ -756,13 +770,13 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, unsigned char* smem, 
     const int64_t sb = bh * a.nseg + seg;
     float* No = PHI ? a.Nseg + sb * DK * DV : a.Eseg + (sb + 1) * DK * DV;
 #pragma unroll
-    for (int m = 0; m < 8; ++m)
+    for (int m = 0; m < 8; ++m) {
+      *reinterpret_cast<f32x4*>(No + ((wave * 8 + m) * 64 + lane) * 4) = SN[m];  // seg_acc_pos
+      if constexpr (PHI) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 16 * m + 4 * g + i;
-        No[row * DV + col] = SN[m][i];
-        if constexpr (PHI) a.Pseg[sb * DK * DK + row * DK + col] = SP[m][i];
+        for (int i = 0; i < 4; ++i) a.Pseg[sb * DK * DK + (16 * m + 4 * g + i) * DK + col] = SP[m][i];
       }
+    }
   }
 }
 
@@ -788,39 +802,42 @@ __device__ __forceinline__ void seg_split8(const float* x, Mma<__bf16>::F8& hi, 
   }
 }
 
-constexpr int kChainCols = 32;  // value columns per chain workgroup
 
 // ---- segment chain: E_{s+1} = Phi_s E_s + N_s ----
 // E_1 is segment 0's exit state (seg_kernel writes it to Eseg slot 1).  Writes every E_s
 // (1 <= s < nseg) as bf16, transposed and in pair order, into Ebf for the correction, and E_nseg
-// into S_T.  One workgroup of 4 waves per (state, 32 value columns); wave w computes rows
-// 32 w .. 32 w + 31 of E (two 16-row tiles by two 16-column tiles) on MFMA, in the three-term bf16
-// form of seg_split8 with fp32 accumulation.  The two row tiles of wave w are, as accumulators,
-// exactly the B operands of k block w for every wave: each step passes them through LDS.  The next
-// segment's Phi and N are loaded while the current product runs.
+// into S_T.  One workgroup of 4 waves per (state, 16 NT value columns); wave w computes rows
+// 32 w .. 32 w + 31 of E (two 16-row tiles by NT 16-column tiles) on MFMA, in the three-term
+// bf16 form of seg_split8 with fp32 accumulation (two partial sums over the k blocks, so that the
+// dependent MFMA chains are half as long).  The two row tiles of wave w are, as accumulators,
+// exactly the B operands of k block w for every wave: each step passes them through LDS.  Phi and
+// N are loaded two segments ahead of their use.
+template <int NT>
 __global__ __launch_bounds__(256) void seg_chain_kernel(SegArgs a) {
   using MM = Mma<__bf16>;
   using F8 = MM::F8;
-  constexpr int DK = 128, DV = 128, NB = DV / kChainCols;
-  __shared__ __attribute__((aligned(16))) uint4 sB[2][4][2][2][64];  // [buffer][kb][n][hi, lo][lane]
+  constexpr int DK = 128, DV = 128, kChainNT = NT, kChainCols = 16 * NT, NB = DV / kChainCols;
+  __shared__ __attribute__((aligned(16))) uint4 sB[2][4][kChainNT][2][64];  // [buffer][kb][n][hi, lo][lane]
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
   const int64_t bh = blockIdx.x / NB, c0 = (blockIdx.x % NB) * kChainCols;
   const int64_t nseg = a.nseg;
 
-  f32x4 acc[2][2];  // [row tile 2 w + mt][column tile n]: rows 32 w + 16 mt + 4 g + i, column c0 + 16 n + l16
+  f32x4 acc[2][kChainNT];  // [row tile 2 w + mt][column tile n]: rows 32 w + 16 mt + 4 g + i, column c0 + 16 n + l16
   {
+    // (seg_acc_pos: column tile c0 / 16 + n, row tile 2 w + mt, this lane)
     const float* E1 = a.Eseg + (bh * nseg + 1) * DK * DV;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int n = 0; n < 2; ++n)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[mt][n][i] = E1[(32 * w + 16 * mt + 4 * g + i) * DV + c0 + 16 * n + l16];
+      for (int n = 0; n < kChainNT; ++n)
+        acc[mt][n] = *reinterpret_cast<const f32x4*>(E1 + (((c0 / 16 + n) * 8 + 2 * w + mt) * 64 + lane) * 4);
   }
-  float4 ph[2][4][2];  // Phi rows 32 w + 16 mt + l16, channels 32 kb + 16 h + 4 g .. + 3
-  float nx[2][2][4];   // N at the accumulator positions
-  auto load_next = [&](int64_t s) {
+  // Phi rows 32 w + 16 mt + l16, channels 32 kb + 16 h + 4 g .. + 3, and N at the accumulator
+  // positions, of one segment
+  using PhiRegs = float4[2][4][2];
+  using NRegs = f32x4[2][kChainNT];
+  auto load = [&](int64_t s, PhiRegs& ph, NRegs& nx) {
     const float* P = a.Pseg + (bh * nseg + s) * DK * DK;
     const float* Nn = a.Nseg + (bh * nseg + s) * DK * DV;
 #pragma unroll
@@ -831,18 +848,17 @@ __global__ __launch_bounds__(256) void seg_chain_kernel(SegArgs a) {
         for (int h = 0; h < 2; ++h)
           ph[mt][kb][h] = *reinterpret_cast<const float4*>(P + (32 * w + 16 * mt + l16) * DK + 32 * kb + 16 * h + 4 * g);
 #pragma unroll
-      for (int n = 0; n < 2; ++n)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) nx[mt][n][i] = Nn[(32 * w + 16 * mt + 4 * g + i) * DV + c0 + 16 * n + l16];
+      for (int n = 0; n < kChainNT; ++n)
+        nx[mt][n] = *reinterpret_cast<const f32x4*>(Nn + (((c0 / 16 + n) * 8 + 2 * w + mt) * 64 + lane) * 4);
     }
   };
-  if (nseg > 1) load_next(1);
-  for (int64_t s = 1; s < nseg; ++s) {
+  // E_{s+1} = Phi_s E_s + N_s with E_s in acc
+  auto step = [&](int64_t s, const PhiRegs& ph, const NRegs& nx) {
     const int buf = static_cast<int>(s & 1);
     // E_s: its bf16 transposed copy and its B operands
     __bf16* eb = a.Ebf + (bh * nseg + s) * DV * DK;
 #pragma unroll
-    for (int n = 0; n < 2; ++n) {
+    for (int n = 0; n < kChainNT; ++n) {
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
         float e4[4] = {acc[mt][n][0], acc[mt][n][1], acc[mt][n][2], acc[mt][n][3]};
@@ -872,30 +888,64 @@ __global__ __launch_bounds__(256) void seg_chain_kernel(SegArgs a) {
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int n = 0; n < 2; ++n)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[mt][n][i] = nx[mt][n][i];
-    if (s + 1 < nseg) load_next(s + 1);
+      for (int n = 0; n < kChainNT; ++n) acc[mt][n] = nx[mt][n];
+    F8 bfr[4][kChainNT][2];  // all B operands first, so that their LDS latencies overlap
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int n = 0; n < 2; ++n) {
-        const F8 bh_ = __builtin_bit_cast(F8, sB[buf][kb][n][0][lane]);
-        const F8 bl_ = __builtin_bit_cast(F8, sB[buf][kb][n][1][lane]);
+      for (int n = 0; n < kChainNT; ++n)
+#pragma unroll
+        for (int hl = 0; hl < 2; ++hl) bfr[kb][n][hl] = __builtin_bit_cast(F8, sB[buf][kb][n][hl][lane]);
+    f32x4 acc2[2][kChainNT];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int n = 0; n < kChainNT; ++n) acc2[mt][n] = zero4();
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int n = 0; n < kChainNT; ++n) {
+        const F8 bh_ = bfr[kb][n][0], bl_ = bfr[kb][n][1];
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
-          acc[mt][n] = MM::mma8(ah[mt][kb], bh_, acc[mt][n]);
-          acc[mt][n] = MM::mma8(ah[mt][kb], bl_, acc[mt][n]);
-          acc[mt][n] = MM::mma8(al[mt][kb], bh_, acc[mt][n]);
+          f32x4& t = kb < 2 ? acc[mt][n] : acc2[mt][n];
+          t = MM::mma8(ah[mt][kb], bh_, t);
+          t = MM::mma8(ah[mt][kb], bl_, t);
+          t = MM::mma8(al[mt][kb], bh_, t);
         }
       }
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int n = 0; n < kChainNT; ++n)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[mt][n][i] += acc2[mt][n][i];
+  };
+  // two register sets, each loaded two segments ahead of its use; loads are unconditional (past
+  // the end they repeat the last segment, unused), so the compiler's wait before one set's use
+  // leaves the other set's loads in flight
+  if (nseg > 1) {
+    const int64_t last = nseg - 1;
+    PhiRegs pA, pB;
+    NRegs nA, nB;
+    load(1, pA, nA);
+    load(2 < last ? 2 : last, pB, nB);
+    __builtin_amdgcn_sched_barrier(0);
+    for (int64_t s = 1; s < nseg; s += 2) {
+      step(s, pA, nA);
+      load(s + 2 < last ? s + 2 : last, pA, nA);
+      __builtin_amdgcn_sched_barrier(0);
+      if (s + 1 < nseg) step(s + 1, pB, nB);
+      load(s + 3 < last ? s + 3 : last, pB, nB);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
   if (a.S_T != nullptr) {
     float* St = a.S_T + bh * DK * DV;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int n = 0; n < 2; ++n)
+      for (int n = 0; n < kChainNT; ++n)
 #pragma unroll
         for (int i = 0; i < 4; ++i) St[(32 * w + 16 * mt + 4 * g + i) * DV + c0 + 16 * n + l16] = acc[mt][n][i];
   }
@@ -903,25 +953,28 @@ __global__ __launch_bounds__(256) void seg_chain_kernel(SegArgs a) {
 
 constexpr int kFixGroup = 8;  // chunks per correction workgroup
 
-// ---- correction: o_c += Q~_c E_s for every chunk c of segments s > 0 ----
+// ---- correction: o_c = O_c(N) + Q~_c E_s for every chunk c of segments s > 0 ----
 // One workgroup of 4 waves per (state, segment s > 0, group of up to 8 of its chunks); wave w takes
-// value column tiles 2 w, 2 w + 1 and keeps their rows of E_s^T as A operands for the whole group.
-// O^T tile (columns 16 n + 4 g + i, tokens 16 ta + l16) = E^T Q~^T: B = rows of Q~.  Both arrays
-// are stored in pair order, so every operand is one 16-byte load.  The next chunk's Q~ and o are
-// loaded while the current one is computed.
+// value column tiles 2 w, 2 w + 1 and keeps their rows of E_s^T (Ebf: transposed, each 32-channel
+// block in the pair order of seg_qt_pos) as A operands for the whole group.  O^T tile (columns
+// 16 n + 4 g + i, tokens 16 ta + l16) = O(N)^T + E^T Q~^T: On supplies the accumulators and Qt the
+// B operands, each one load contiguous across the wave; o is only written.  The next chunk's loads
+// are issued before the current chunk's products.
 __global__ __launch_bounds__(256) void seg_fix_kernel(SegArgs a) {
   using MM = Mma<__bf16>;
   using F8 = MM::F8;
   constexpr int DK = 128, DV = 128, C = kSegC;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
-  const int64_t ngrp = (a.L + kFixGroup - 1) / kFixGroup;
-  int64_t blk = blockIdx.x;
-  const int64_t grp = blk % ngrp;
+  // (32-bit index arithmetic: the grid is far below 2^31 workgroups)
+  const uint32_t ngrp = static_cast<uint32_t>((a.L + kFixGroup - 1) / kFixGroup);
+  const uint32_t nsm1 = static_cast<uint32_t>(a.nseg - 1);
+  uint32_t blk = blockIdx.x;
+  const uint32_t grp = blk % ngrp;
   blk /= ngrp;
-  const int64_t s = 1 + blk % (a.nseg - 1), bh = blk / (a.nseg - 1);
+  const int64_t s = 1 + blk % nsm1, bh = blk / nsm1;
   const int64_t seg_end = (s + 1) * a.L < a.nch ? (s + 1) * a.L : a.nch;
-  const int64_t c0 = s * a.L + grp * kFixGroup;
+  const int64_t c0 = s * a.L + static_cast<int64_t>(grp) * kFixGroup;
   const int64_t c1 = c0 + kFixGroup < seg_end ? c0 + kFixGroup : seg_end;
   if (c0 >= c1) return;  // past the end of a shorter last segment
   const int64_t bi = bh / a.H, hi = bh % a.H;
@@ -934,26 +987,18 @@ __global__ __launch_bounds__(256) void seg_fix_kernel(SegArgs a) {
     for (int kb = 0; kb < 4; ++kb)
       ef[n][kb] = *reinterpret_cast<const F8*>(eb + (16 * (2 * wave + n) + l16) * DK + 32 * kb + 8 * g);
 
-  F8 qf[2][4];
-  uint2 ov[2][2];
   auto load = [&](int64_t c, F8 (&q)[2][4], uint2 (&o)[2][2]) {
     const __bf16* qt = a.Qt + (bh * a.nch + c) * C * DK;
-    const int64_t t0 = c * C;
-    const auto ro = make_rsrc(a.o + ((bi * a.T + t0) * a.H + hi) * DV, wy_range(a.T - t0, a.H, DV));
+    const __bf16* on = a.On + (bh * a.nch + c) * C * DV;
 #pragma unroll
     for (int ta = 0; ta < 2; ++ta) {
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) q[ta][kb] = *reinterpret_cast<const F8*>(qt + (16 * ta + l16) * DK + 32 * kb + 8 * g);
-      const uint32_t t = static_cast<uint32_t>(16 * ta + l16);
+      for (int kb = 0; kb < 4; ++kb) q[ta][kb] = *reinterpret_cast<const F8*>(qt + ((ta * 4 + kb) * 64 + lane) * 8);
 #pragma unroll
-      for (int n = 0; n < 2; ++n) o[ta][n] = buf_load8(ro, t * hdv + (16 * (2 * wave + n) + 4 * g) * 2);
+      for (int n = 0; n < 2; ++n) o[ta][n] = *reinterpret_cast<const uint2*>(on + ((ta * 8 + 2 * wave + n) * 64 + lane) * 4);
     }
   };
-  load(c0, qf, ov);
-  for (int64_t c = c0; c < c1; ++c) {
-    F8 qn[2][4];
-    uint2 on[2][2];
-    if (c + 1 < c1) load(c + 1, qn, on);
+  auto apply = [&](int64_t c, const F8 (&q)[2][4], const uint2 (&o)[2][2]) {
     const int64_t t0 = c * C;
     const auto ro = make_rsrc(a.o + ((bi * a.T + t0) * a.H + hi) * DV, wy_range(a.T - t0, a.H, DV));
 #pragma unroll
@@ -962,25 +1007,31 @@ __global__ __launch_bounds__(256) void seg_fix_kernel(SegArgs a) {
 #pragma unroll
       for (int n = 0; n < 2; ++n) {
         float o4[4];
-        unpack4(ov[ta][n], o4);
+        unpack4(o[ta][n], o4);
         f32x4 acc;
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[i] = o4[i];
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) acc = MM::mma8(ef[n][kb], qf[ta][kb], acc);
+        for (int kb = 0; kb < 4; ++kb) acc = MM::mma8(ef[n][kb], q[ta][kb], acc);
         float r4[4] = {acc[0], acc[1], acc[2], acc[3]};
         buf_store8(ro, t * hdv + (16 * (2 * wave + n) + 4 * g) * 2, pack4(r4));
       }
     }
-    if (c + 1 < c1) {
-#pragma unroll
-      for (int ta = 0; ta < 2; ++ta) {
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) qf[ta][kb] = qn[ta][kb];
-#pragma unroll
-        for (int n = 0; n < 2; ++n) ov[ta][n] = on[ta][n];
-      }
-    }
+  };
+  // two register sets, alternately loaded one chunk ahead (no copies between them, so the wait
+  // for one set's loads does not wait for the other's).  The loads are unconditional (past the
+  // group's end they repeat a chunk of it, unused), so that the compiler's count of loads in flight
+  // is the same on every path and its wait before a use leaves the other set's loads in flight.
+  F8 qa[2][4], qb[2][4];
+  uint2 oa[2][2], ob[2][2];
+  load(c0, qa, oa);
+  for (int64_t c = c0; c < c1; c += 2) {
+    load(c + 1 < c1 ? c + 1 : c, qb, ob);
+    __builtin_amdgcn_sched_barrier(0);  // (issue the loads before the products)
+    apply(c, qa, oa);
+    load(c + 2 < c1 ? c + 2 : c, qa, oa);
+    __builtin_amdgcn_sched_barrier(0);
+    if (c + 1 < c1) apply(c + 1, qb, ob);
   }
 }
 

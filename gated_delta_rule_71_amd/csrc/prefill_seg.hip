@@ -44,13 +44,14 @@ bool prefill_seg_ok(int64_t DK, int64_t DV, int alpha_kind, int b_kind, int w_ki
   return gdn2 || kda;
 }
 
-// Workspace of a segmented call (none for a single segment per state): Q~ of every chunk, and per
-// segment N, Phi, the state leaving segment 0 (fp32) and the entering states (bf16).
+// Workspace of a segmented call (none for a single segment per state): Q~ and the read-out of N of
+// every chunk, and per segment N, Phi, the state leaving segment 0 (fp32) and the entering states
+// (bf16).
 size_t prefill_seg_workspace_bytes(int64_t nstate, int64_t T) {
   const SegPlan p = seg_plan(nstate, T);
   if (p.nseg <= 1) return 0;
   const size_t per = static_cast<size_t>(nstate * p.nseg) * 128 * 128;
-  return align256(static_cast<size_t>(nstate * p.nch) * kSegC * 128 * 2) + 3 * align256(per * 4) +
+  return 2 * align256(static_cast<size_t>(nstate * p.nch) * kSegC * 128 * 2) + 3 * align256(per * 4) +
          align256(per * 2);
 }
 
@@ -81,6 +82,8 @@ hipError_t prefill_seg_launch(const PrefillArgs<bf16_t>& pa, int64_t nstate, boo
     const size_t per = static_cast<size_t>(nstate * p.nseg) * 128 * 128;
     a.Qt = reinterpret_cast<__bf16*>(w);
     w += align256(static_cast<size_t>(nstate * p.nch) * kSegC * 128 * 2);
+    a.On = reinterpret_cast<__bf16*>(w);
+    w += align256(static_cast<size_t>(nstate * p.nch) * kSegC * 128 * 2);
     a.Nseg = reinterpret_cast<float*>(w);
     w += align256(per * 4);
     a.Pseg = reinterpret_cast<float*>(w);
@@ -105,7 +108,11 @@ hipError_t prefill_seg_launch(const PrefillArgs<bf16_t>& pa, int64_t nstate, boo
   if (mark != nullptr)
     if (const hipError_t e = hipEventRecord(mark, s); e != hipSuccess) return e;
   if (p.nseg > 1) {
-    hipLaunchKernelGGL(seg_chain_kernel, dim3(static_cast<unsigned>(nstate * (128 / kChainCols))), dim3(256), 0, s, a);
+    // (16 columns per workgroup while that still leaves CUs free, else 32)
+    if (nstate * 8 <= kSegTargetGroups)
+      hipLaunchKernelGGL((seg_chain_kernel<1>), dim3(static_cast<unsigned>(nstate * 8)), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((seg_chain_kernel<2>), dim3(static_cast<unsigned>(nstate * 4)), dim3(256), 0, s, a);
     if (const hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     const int64_t ngrp = (p.L + kFixGroup - 1) / kFixGroup;
     hipLaunchKernelGGL(seg_fix_kernel, dim3(static_cast<unsigned>(nstate * (p.nseg - 1) * ngrp)), dim3(256), 0, s, a);

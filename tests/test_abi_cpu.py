@@ -133,10 +133,10 @@ def test_empty_problem_is_a_no_op():
 
 def seg_workspace(nstate, T):
     """Workspace of the fused segment prefill (d_k = d_v = 128 with the Gated DeltaNet-2 or KDA
-    gates): each state's 32-token chunks split into ceil(256 / states) segments (at
-    most one per chunk); with more than one segment, Q~ (32 x 128 bf16) per chunk and, per segment, N, Phi,
-    the state leaving segment 0 (128 x 128 fp32 each) and the entering state (bf16), each array
-    rounded up to 256 bytes.  None with one segment per state."""
+    gates): each state's 32-token chunks split into ceil(256 / states) segments (at most one per
+    chunk); with more than one segment, Q~ and the read-out of N (32 x 128 bf16 each) per chunk
+    and, per segment, N, Phi, the state leaving segment 0 (128 x 128 fp32 each) and the entering
+    state (bf16), each array rounded up to 256 bytes.  None with one segment per state."""
     r = lambda n: (n + 255) // 256 * 256
     nch = (T + 31) // 32
     want = max(1, min(nch, -(-256 // nstate)))
@@ -145,7 +145,7 @@ def seg_workspace(nstate, T):
     if nseg <= 1:
         return 0
     per = nstate * nseg * 128 * 128
-    return r(nstate * nch * 32 * 128 * 2) + 3 * r(per * 4) + r(per * 2)
+    return 2 * r(nstate * nch * 32 * 128 * 2) + 3 * r(per * 4) + r(per * 2)
 
 
 def test_workspace_query_and_decode_validation():
