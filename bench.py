@@ -49,6 +49,15 @@ def flops_per_head_token(d, C, channel_two_factor, erase=True):
     return 6 * d * d + 5 * C * d + C * C / 3.0
 
 
+def prefill_chunk(wl):
+    """Chunk length the library's kernels use for this workload: 32 in the segment kernel (bf16,
+    d_k = d_v = 128, per-channel decay with per-channel or scalar erase and write gates), 64
+    elsewhere."""
+    seg = (wl.dtype == "bf16" and wl.DK == 128 and wl.DV == 128 and wl.alpha == "channel" and
+           ((wl.b == "channel" and wl.w == "channel") or (wl.b == "scalar" and wl.w == "scalar")))
+    return 32 if seg else 64
+
+
 def prefill_bytes(wl):
     """Minimal HBM bytes of one prefill call: every input read once, o and S_T written once."""
     es = 2 if wl.dtype == "bf16" else 4
@@ -352,7 +361,8 @@ def prefill_report(wl, pf):
     """Throughput and rooflines of one prefill call of workload `wl` from time_prefill's result."""
     two = wl.alpha == "channel"  # erase-then-decay with a per-channel decay: two key families
     sec = pf["mean_ms"] * 1e-3
-    flops = flops_per_head_token(wl.DK, 64, two, wl.b != "none") * wl.B * wl.T * wl.H
+    chunk = prefill_chunk(wl)
+    flops = flops_per_head_token(wl.DK, chunk, two, wl.b != "none") * wl.B * wl.T * wl.H
     nbytes = prefill_bytes(wl)
     gbs = nbytes / sec / 1e9
     tf = flops / sec / 1e12
@@ -362,7 +372,7 @@ def prefill_report(wl, pf):
         "kernel_ms": {"mean": pf["mean_ms"], "median": pf["median_ms"], "p10": pf["p10_ms"],
                       "p90": pf["p90_ms"]},
         "config": {"workload": wl.name, "batch": wl.B, "heads": wl.H, "qk_heads": wl.HK or wl.H,
-                   "seq_len": wl.T, "d_k": wl.DK, "d_v": wl.DV, "chunk": 64, "state": "fp32",
+                   "seq_len": wl.T, "d_k": wl.DK, "d_v": wl.DV, "chunk": chunk, "state": "fp32",
                    "decay": wl.alpha, "erase_gate": wl.b, "write_gate": wl.w, "seed": wl.seed,
                    "S0": "N(0, %g^2)" % wl.s0_std if wl.s0_std > 0 else "zero"},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",

@@ -75,12 +75,20 @@ typedef enum { GDR_ERASE_THEN_DECAY = 0, GDR_DECAY_THEN_ERASE = 1 } gdr_order;
  * Supported by the prefill and the decode step: dk in {16, 32, 64, 128, 256},
  * dv a multiple of 16 in [16, 256], both I/O types, every gate kind and both
  * orders (GDR_ERR_UNSUPPORTED otherwise); the backward is narrower (see
- * gdr_chunk_bwd).  chunk == 64 (0 selects 64); batch, heads >= 0; seqlen >= 0
+ * gdr_chunk_bwd).  chunk == 64 or 0 (the same); batch, heads >= 0; seqlen >= 0
  * (any value: a ragged last chunk is padded with identity tokens inside the
- * kernel).  Which kernels run: the chunkwise kernels where their LDS layout
- * fits (every bf16 shape except dk = 256 with a per-channel decay after the
- * erase; fp32 at dk <= 32, and at dk = 64 with a scalar, no or decay-first
- * decay), else the recurrence token by token with the state in registers. */
+ * kernel).  The chunk length does not change the result, which equals the
+ * token-by-token recurrence up to rounding; the kernels block the chunkwise
+ * form in 64-token chunks, except the segment kernel, which uses 32.  Which
+ * kernels run:
+ *   bf16, dk = dv = 128, per-channel decay with per-channel (erase and write)
+ *     or scalar (both) gates, either order: the segment kernel (a state's
+ *     chunks split into segments run side by side, then linked);
+ *   other shapes: the chunkwise kernels where their LDS layout fits (every
+ *     bf16 shape except dk = 256 with a per-channel decay after the erase;
+ *     fp32 at dk <= 32, and at dk = 64 with a scalar, no or decay-first
+ *     decay), else the recurrence token by token with the state in
+ *     registers. */
 typedef struct {
   int32_t struct_size;
   int32_t io_dtype;   /* gdr_dtype */
@@ -102,10 +110,18 @@ int gdr_abi_version(void);
 const char* gdr_status_string(int status);
 
 /* Workspace bytes gdr_chunk_fwd needs for `p` (0 when none); 0 also for an
- * invalid problem.  bf16 problems with dk in {32, 64, 128} run as a
- * chunk-local kernel plus a per-state kernel that exchange per-chunk matrices
- * through the workspace, each array 256-byte aligned; per 64-token chunk of
- * every (batch, head) that is:
+ * invalid problem.  Each array below is rounded up to 256 bytes.
+ * Segment kernel (see gdr_problem): with S = batch * heads states and
+ * n = ceil(seqlen / 32) chunks each, a state's chunks split into
+ * m = ceil(n / L) segments of L = ceil(n / min(n, ceil(256 / S))) chunks.
+ * For m = 1 none; else two arrays of S * n * 32 * 128 bf16 (per chunk, the
+ * read-outs of the segment's state from zero and of its transition), three of
+ * S * m * 128 * 128 fp32 (per segment, its state from zero, its transition and
+ * the state leaving the first) and one of S * m * 128 * 128 bf16 (the state
+ * entering each segment).
+ * Other bf16 problems with dk in {32, 64, 128} run as a chunk-local kernel
+ * plus a per-state kernel that exchange per-chunk matrices through the
+ * workspace; per 64-token chunk of every (batch, head) that is:
  *   scalar (or no) decay, scalar (or no) erase gate: W (64 x dk), U (64 x dv)
  *     and the masked 64 x 64 read-out matrix, all bf16, and 132 floats of gate
  *     exponentials: 128 dk + 128 dv + 8720 bytes;
@@ -145,7 +161,8 @@ int gdr_chunk_fwd(const gdr_problem* p, const void* q, const void* k, const void
 /*
  * gdr_chunk_fwd with a timing marker.  When `phase_event` (a hipEvent_t) is
  * not NULL it is recorded on `stream` between the chunk-local kernel and the
- * per-state kernel, or just before the one kernel of a problem that runs as
+ * per-state kernel (for the segment kernel: after it, before the kernels that
+ * link the segments), or just before the one kernel of a problem that runs as
  * one.  With events recorded before and after the call, the caller can time
  * the two phases separately.  No event is recorded when the call fails
  * validation or when B * H is 0.  Otherwise identical to gdr_chunk_fwd;
