@@ -175,46 +175,55 @@ struct SegLayout {
   static constexpr int LDT = DK + 8;  // token-major rows of dk (or dv) bf16
   static constexpr int LDD = C + 8;   // rows of 32 x 32 matrices
   static constexpr int LDA = 16 + 8;  // the off-diagonal block of -L_P (rows 16..31, cols 0..15), transposed
-  static constexpr int LDL = 20;
-  static constexpr int LDF = DK + 4;  // fp32 rows of the flagged-chunk decays
+  static constexpr int LDL = 20;      // fp32 rows of the diagonal blocks of L_P / L
+  static constexpr int LDI = 24;      // bf16 rows of their inverses (over the same area)
   static constexpr int ROWS = C * LDT * 2;
   static constexpr int MAT = C * LDD * 2;
-  static constexpr int oQ = 0;                          // Qs      [32][LDT]
-  static constexpr int oC = oQ + ROWS;                  // Cs, then W (in place)
-  static constexpr int oK = oC + ROWS;                  // Ks (MODE 1: -Ks)
-  static constexpr int oP = oK + ROWS;                  // -Ps (MODE 2)
-  static constexpr int oX = oP + (TWO ? ROWS : 0);      // X rows [32][LDT]
-  static constexpr int oA = oX + ROWS;                  // (-L_10)^T of L_P / L
-  static constexpr int oM = oA + 16 * LDA * 2;          // -M_QP (MODE 2) / -M [32][LDD]
-  static constexpr int oLK = oM + MAT;                  // L_K (MODE 2)
-  static constexpr int oMQK = oLK + (TWO ? MAT : 0);    // M_QK (MODE 2)
-  static constexpr int oLD = oMQK + (TWO ? MAT : 0);   // fp32 L_ii row-major [2][16][LDL]
-  static constexpr int oS = (oLD + 2 * 16 * LDL * 4 + 1023) / 1024 * 1024;  // staging of the next chunk
+  // operand buffer of one chunk: Qs, Cs, Ks (MODE 1: -Ks), -Ps (MODE 2), X, each [32][LDT]
+  static constexpr int pQ = 0, pC = ROWS, pK = 2 * ROWS, pP = 3 * ROWS, pX = (TWO ? 4 : 3) * ROWS;
+  static constexpr int PB = pX + ROWS;
+  // Gram buffer of one chunk: (-L_10)^T [16][LDA], -M_QP / -M, L_K, M_QK [32][LDD] (the last two
+  // MODE 2 only), per diagonal block of L_P / L a [16][LDL] fp32 area: the block's rows, then its
+  // inverse D = (I + L_bb)^{-1} in bf16 [16][LDI]
+  static constexpr int gA = 0, gM = 16 * LDA * 2, gLK = gM + MAT, gMQK = gLK + (TWO ? MAT : 0);
+  static constexpr int gLD = gMQK + (TWO ? MAT : 0);
+  static constexpr int GB = gLD + 2 * 16 * LDL * 4;
+  // two of each (the chunk being advanced and the next one), then e^{G_n} [2][DK] fp32, the
+  // per-wave flags [8], and the staging of the inputs of the chunk after
+  static constexpr int oP0 = 0, oG0 = 2 * PB, oF = oG0 + 2 * GB, oFL = oF + 2 * DK * 4;
+  static constexpr int oS = (oFL + 8 * 4 + 1023) / 1024 * 1024;
   static constexpr int CH = C * DK * 2;                 // one per-channel input: 8 KB
   static constexpr int SC = 256;                        // one scalar gate (32 bf16, padded)
   static constexpr int sQ = oS, sK = sQ + CH, sV = sK + CH;
   static constexpr int sLA = sV + CH;
   static constexpr int sB = sLA + (AK == kChannel ? CH : SC);
   static constexpr int sW = sB + (BK == kChannel ? CH : SC);
-  static constexpr int oO = sW + (WK == kChannel ? CH : SC);  // o rows [32][LDT] bf16 (first segment)
-  static constexpr int oAL = oO;                        // flagged chunks: decays [32][LDF] fp32 over o
-  static constexpr int oF0 = oO + ROWS > oAL + C * LDF * 4 ? oO + ROWS : oAL + C * LDF * 4;
-  static constexpr int oF = (oF0 + 15) / 16 * 16;       // fp32 e^{G_n} [DK]
-  static constexpr int oFL = oF + DK * 4;               // per-wave flags [8] (int)
-  static constexpr int total = oFL + 8 * 4;
+  static constexpr int total = sW + (WK == kChannel ? CH : SC);
   static constexpr bool fits = total <= kLdsLimit;
-  static_assert(oX % 16 == 0 && oA % 16 == 0 && oM % 16 == 0 &&
-                    oLD % 16 == 0 && oFL % 16 == 0 && oS % 1024 == 0 && CH % 1024 == 0 && oO % 16 == 0 && oF % 16 == 0,
+  static_assert(PB % 16 == 0 && GB % 16 == 0 && gM % 16 == 0 && gLD % 16 == 0 && oF % 16 == 0 &&
+                    oFL % 16 == 0 && oS % 1024 == 0 && CH % 1024 == 0,
                 "aligned arrays (each 1 KB direct-to-LDS load of the staging fills 1 KB of LDS)");
 };
 
-// Forward substitution for D = (I + L)^{-1}, L strictly lower 16 x 16, two blocks at once: lane
-// (row i = l16, quarter g) holds row i of -L (all 16 entries) and D[i][4 g .. 4 g + 3].  At step
+// Forward substitution for D = (I + L)^{-1}, L strictly lower 16 x 16 (seg_inv_sweep2: two blocks
+// at once): lane (row i = l16, quarter g) holds row i of -L (all 16 entries) and
+// D[i][4 g .. 4 g + 3].  At step
 // M, row M of D is final; a DPP row broadcast (row_newbcast:M) hands D[M][4 g + c] to every lane
 // of the 16-lane group, which adds -L[i][M] times it (a no-op for rows i <= M, where L[i][M] = 0).
-// The broadcast folds into the multiply-add as its DPP operand.
 template <int M>
-__device__ __forceinline__ void seg_inv_sweep(float (&d)[2][4], const float (&nl)[2][16]) {
+__device__ __forceinline__ void seg_inv_sweep(float (&d)[4], const float (&nl)[16]) {
+  if constexpr (M < 15) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float dm =
+          __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, d[c]), 0x150 + M, 0xf, 0xf, true));
+      d[c] = fmaf(dm, nl[M], d[c]);
+    }
+    seg_inv_sweep<M + 1>(d, nl);
+  }
+}
+template <int M>
+__device__ __forceinline__ void seg_inv_sweep2(float (&d)[2][4], const float (&nl)[2][16]) {
   if constexpr (M < 15) {
 #pragma unroll
     for (int b = 0; b < 2; ++b)
@@ -224,7 +233,7 @@ __device__ __forceinline__ void seg_inv_sweep(float (&d)[2][4], const float (&nl
             __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, d[b][c]), 0x150 + M, 0xf, 0xf, true));
         d[b][c] = fmaf(dm, nl[b][M], d[b][c]);
       }
-    seg_inv_sweep<M + 1>(d, nl);
+    seg_inv_sweep2<M + 1>(d, nl);
   }
 }
 
@@ -241,17 +250,27 @@ __device__ __forceinline__ void stage_gate4(const unsigned char* st, int t, int 
     f[0] = f[1] = f[2] = f[3] = none;
   }
 }
+// One element (t, c) of a staged per-channel input.
+__device__ __forceinline__ float stage_elem(const unsigned char* st, int t, int c) {
+  return static_cast<float>(*reinterpret_cast<const __bf16*>(st + stage_off(t, c & ~3) + 2 * (c & 3)));
+}
 
 // The work of one (state, segment) workgroup of 8 waves.  PHI: the segment starts from an unknown
-// state, so the workgroup also carries the segment's transition and writes Q~ (every segment but
-// the first).  AK, BK, WK: the kinds of log alpha (scalar or channel), b (scalar or channel) and w
-// (none, scalar or channel), fixed at compile time.
+// state, so the workgroup also carries the segment's transition and writes the read-outs of N and
+// of Phi (On, Qt) for the correction (every segment but the first).  AK, BK, WK: the kinds of
+// log alpha (scalar or channel), b (scalar or channel) and w (none, scalar or channel).
 //
-// Waves 0-1 issue the direct-to-LDS loads of the next chunk's inputs and wait only for those;
-// waves 4-7 copy each chunk's read-outs from LDS to o (and Q~) at the start of the next chunk;
-// waves 2-7 form the chunk's Gram products.
-// The barriers inside the chunk loop wait for LDS operations only, so loads and stores in flight
-// stay in flight across them.
+// Two chunks are in flight: while the state advances through chunk c (its operands in buffer
+// c & 1), the scan, split and Gram products of chunk c + 1 fill the other buffer, and the inputs of
+// chunk c + 2 arrive in the staging.  One chunk takes three barriers:
+//   A0  the inputs of chunk c + 1 are in the staging
+//       split of c + 1 (all waves); then, for chunk c: U, T, R and the read-outs
+//   A1  the operands of c + 1 are in their buffer; its flags are known
+//       loads of chunk c + 2; the state update of c; Gram products of c + 1 (waves 2-7)
+//   A2
+// A chunk whose gates leave the range of the chunk form ("flagged") runs token by token from its
+// staged inputs; the loads of the chunk after it wait for that, and the pipeline refills.
+// The barriers wait for LDS operations only, so loads and stores stay in flight across them.
 template <int MODE, int AK, int BK, int WK, bool PHI>
 __device__ __forceinline__ void seg_body(const SegArgs& a, unsigned char* smem, int64_t bh, int64_t seg) {
   using L = SegLayout<MODE, AK, BK, WK>;
@@ -259,42 +278,30 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, unsigned char* smem, 
   using F8 = MM::F8;
   constexpr bool TWO = L::TWO;
   constexpr int C = kSegC, DK = 128, DV = 128, LDT = L::LDT, LDD = L::LDD, LDA = L::LDA,
-                LDL = L::LDL, LDF = L::LDF, NT = 512;
+                LDL = L::LDL, NT = 512;
 
-  __bf16* tQ = reinterpret_cast<__bf16*>(smem + L::oQ);
-  __bf16* tC = reinterpret_cast<__bf16*>(smem + L::oC);
-  __bf16* tK = reinterpret_cast<__bf16*>(smem + L::oK);
-  __bf16* tP = reinterpret_cast<__bf16*>(smem + L::oP);
-  __bf16* tX = reinterpret_cast<__bf16*>(smem + L::oX);
-  __bf16* gA = reinterpret_cast<__bf16*>(smem + L::oA);
-  __bf16* gM = reinterpret_cast<__bf16*>(smem + L::oM);
-  __bf16* gLK = reinterpret_cast<__bf16*>(smem + L::oLK);
-  __bf16* gMQK = reinterpret_cast<__bf16*>(smem + L::oMQK);
-  float* Ld = reinterpret_cast<float*>(smem + L::oLD);
-  __bf16* tO = reinterpret_cast<__bf16*>(smem + L::oO);         // o rows of the chunk
-  float* fAl = reinterpret_cast<float*>(smem + L::oAL);
-  float* fG = reinterpret_cast<float*>(smem + L::oF);   // e^{G_n}
   int* sFlag = reinterpret_cast<int*>(smem + L::oFL);
-
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63, g = lane >> 4, l16 = lane & 15;
   const int64_t H = a.H, Hk = a.Hk, T = a.T, nch = a.nch;
   const int64_t bi = bh / H, hi = bh % H, hk = hi / (H / Hk);
   const int64_t c_begin = seg * a.L;
   const int64_t c_end = c_begin + a.L < nch ? c_begin + a.L : nch;
-  const int ch0 = 16 * wave + 4 * g;  // this lane's four channels / value columns in the elementwise phases
-  const int col = 16 * wave + l16;    // this lane's column of the state tiles
   const uint32_t hqk = static_cast<uint32_t>(Hk * DK * 2), hdk = static_cast<uint32_t>(H * DK * 2);
   const uint32_t hdv = static_cast<uint32_t>(H * DV * 2), h1 = static_cast<uint32_t>(H * 2);
+  auto pbuf = [&](int par) { return smem + L::oP0 + par * L::PB; };
+  auto gbuf = [&](int par) { return smem + L::oG0 + par * L::GB; };
 
   // tiles of -M_QP / -M, L_K and M_QK above the diagonal are never written but are read as zero
-  for (int i = tid; i < (L::oLD - L::oM) / 16; i += NT)
-    reinterpret_cast<uint4*>(smem + L::oM)[i] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+    for (int i = tid; i < (L::gLD - L::gM) / 16; i += NT)
+      reinterpret_cast<uint4*>(gbuf(b) + L::gM)[i] = make_uint4(0, 0, 0, 0);
 
   // ---- state tiles: N (value column col) and Phi (channel column col), rows 16 m + 4 g + i ----
   f32x4 SN[8], SP[8];
   {
+    const int lane = tid & 63, g = lane >> 4, col = 16 * wave + (lane & 15);
     const float* S0 = (!PHI && a.S0 != nullptr) ? a.S0 + bh * DK * DV : nullptr;
 #pragma unroll
     for (int m = 0; m < 8; ++m)
@@ -306,72 +313,79 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, unsigned char* smem, 
       }
   }
 
-  // ---- direct-to-LDS loads of chunk c's inputs (waves 0-3) ----
+  // ---- direct-to-LDS loads of chunk c's inputs (every wave: one 1 KB load of each per-channel
+  // input; wave 0 also the scalar gates) ----
   uint16_t scA = 0, scB = 0, scW = 0;  // wave 0, lane t: token t's scalar gates in flight
+  // per input: this state's first row, its row stride, and the bytes from the first row to the end
+  // of the last (reads past that return zeros: the ragged last chunk)
+  struct In {
+    const unsigned char* p;
+    uint32_t stride;
+    int64_t end;
+  };
+  auto in_of = [&](const bf16_t* x, int64_t heads, int64_t head, int64_t width) {
+    const int64_t stride = heads * width * 2;
+    return In{reinterpret_cast<const unsigned char*>(x + (bi * T * heads + head) * width),
+              static_cast<uint32_t>(stride), (T - 1) * stride + width * 2};
+  };
+  const In inQ = in_of(a.q, Hk, hk, DK), inK = in_of(a.k, Hk, hk, DK), inV = in_of(a.v, H, hi, DV);
+  const In inA = in_of(a.la, H, hi, AK == kChannel ? DK : 1), inB = in_of(a.bg, H, hi, BK == kChannel ? DK : 1);
+  const In inW = in_of(a.wg, H, hi, WK == kChannel ? DV : 1);
   auto stage = [&](int64_t c, int lane) {
-    const int64_t t0 = c * C, left = T - t0;
-    const int64_t rr = (bi * T + t0) * H + hi;
-    const int64_t rqk = (bi * T + t0) * Hk + hk;
-    // a per-channel array is 8 loads of 1 KB (4 rows each); wave w < 2 takes loads 4 w .. 4 w + 3
-    auto rows = [&](const bf16_t* base, uint32_t bytes, uint32_t stride, int dst) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int i = 4 * wave + u, t = 4 * i + (lane >> 4), slot = lane & 15;
-        const int piece = (slot ^ t) & 15;
-        seg_dma16(base, bytes, smem + dst + 1024 * i, static_cast<uint32_t>(t) * stride + piece * 16);
-      }
+    const int64_t t0 = c * C;
+    // a per-channel array is 8 loads of 1 KB (rows 4 w .. 4 w + 3 for wave w)
+    auto rows = [&](const In& in, int dst) {
+      const int64_t off = t0 * in.stride, left = in.end - off;
+      const uint32_t bytes = static_cast<uint32_t>(left < 0x7fffffff ? left : 0x7fffffff);
+      const int t = 4 * wave + (lane >> 4), slot = lane & 15;
+      const int piece = (slot ^ t) & 15;
+      seg_dma16(in.p + off, bytes, smem + dst + 1024 * wave, static_cast<uint32_t>(t) * in.stride + piece * 16);
     };
     // a scalar gate: one bf16 per token into a register of wave 0's lane t (written to LDS once
     // the wave has waited for its loads)
-    auto scalar = [&](__amdgpu_buffer_rsrc_t r, uint16_t& dst) {
-      if (wave == 0 && lane < C) dst = buf_load_u16(r, static_cast<uint32_t>(lane) * h1);
+    auto scalar = [&](const In& in, uint16_t& dst) {
+      if (wave == 0 && lane < C) {
+        const int64_t off = t0 * in.stride, left = in.end - off;
+        const auto r = make_rsrc(in.p + off, static_cast<uint32_t>(left < 0x7fffffff ? left : 0x7fffffff));
+        dst = buf_load_u16(r, static_cast<uint32_t>(lane) * in.stride);
+      }
     };
-    rows(a.q + rqk * DK, wy_range(left, Hk, DK), hqk, L::sQ);
-    rows(a.k + rqk * DK, wy_range(left, Hk, DK), hqk, L::sK);
-    rows(a.v + rr * DV, wy_range(left, H, DV), hdv, L::sV);
-    if constexpr (AK == kChannel) rows(a.la + rr * DK, wy_range(left, H, DK), hdk, L::sLA);
-    if constexpr (AK == kScalar) scalar(make_rsrc(a.la + rr, wy_range(left, H, 1)), scA);
-    if constexpr (BK == kChannel) rows(a.bg + rr * DK, wy_range(left, H, DK), hdk, L::sB);
-    if constexpr (BK == kScalar) scalar(make_rsrc(a.bg + rr, wy_range(left, H, 1)), scB);
-    if constexpr (WK == kChannel) rows(a.wg + rr * DV, wy_range(left, H, DV), hdv, L::sW);
-    if constexpr (WK == kScalar) scalar(make_rsrc(a.wg + rr, wy_range(left, H, 1)), scW);
+    rows(inQ, L::sQ);
+    rows(inK, L::sK);
+    rows(inV, L::sV);
+    if constexpr (AK == kChannel) rows(inA, L::sLA);
+    if constexpr (AK == kScalar) scalar(inA, scA);
+    if constexpr (BK == kChannel) rows(inB, L::sB);
+    if constexpr (BK == kScalar) scalar(inB, scB);
+    if constexpr (WK == kChannel) rows(inW, L::sW);
+    if constexpr (WK == kScalar) scalar(inW, scW);
   };
-
-  // ---- copies of a chunk's read-outs from LDS to o (waves 4-7; the first segment only: the others
-  // write theirs to On and Qt straight from the accumulators) ----
-  auto store_out = [&](int64_t c, int tid) {
-    const int64_t t0 = c * C, left = T - t0;
-    const auto ro = make_rsrc(a.o + ((bi * T + t0) * H + hi) * DV, wy_range(left, H, DV));
-    const int l = tid - 256;  // 0 .. 255
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {  // 512 pieces of 16 bytes: row l / 16 + 16 u, piece l % 16
-      const int t = (l >> 4) + 16 * u, piece = l & 15;
-      const uint4 v = *reinterpret_cast<const uint4*>(tO + t * LDT + 8 * piece);
-      buf_store16(ro, static_cast<uint32_t>(t) * hdv + piece * 16, v);
-    }
-  };
-
-  if (wave < 2 && c_begin < c_end) stage(c_begin, lane);
-  bool out_pending = false;  // (uniform) the read-outs of chunk c - 1 wait in LDS
-
-  for (int64_t c = c_begin; c < c_end; ++c) {
-    // lane-derived values again, from an opaque copy of the thread index: recomputing them costs
-    // a few adds, keeping them across the loop would cost registers the chunk needs
-    const int tid = opaque_v(threadIdx.x);
-    const int lane = tid & 63, g = lane >> 4, l16 = lane & 15;
-    const int ch0 = 16 * wave + 4 * g, col = 16 * wave + l16;
-    if (wave >= 4 && out_pending) store_out(c - 1, tid);
-    if (wave < 2) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // this wave's loads of chunk c
+  // every wave waits for its staging loads; wave 0 then writes the scalar gates it holds
+  auto arrive = [&](int lane) {
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     if (wave == 0 && lane < C) {
       if constexpr (AK == kScalar) reinterpret_cast<uint16_t*>(smem + L::sLA)[lane] = scA;
       if constexpr (BK == kScalar) reinterpret_cast<uint16_t*>(smem + L::sB)[lane] = scB;
       if constexpr (WK == kScalar) reinterpret_cast<uint16_t*>(smem + L::sW)[lane] = scW;
     }
-    lds_barrier_keep_vm();  // B0: chunk c's inputs are in LDS
+  };
+  auto flagged_now = [&]() {
+    const int4 f0 = reinterpret_cast<const int4*>(sFlag)[0], f1 = reinterpret_cast<const int4*>(sFlag)[1];
+    return (f0.x | f0.y | f0.z | f0.w | f1.x | f1.y | f1.z | f1.w) != 0;
+  };
 
+  // ---- scan and split of the staged chunk into operand buffer par: prefix sums of log alpha over
+  // the chunk, per channel (this lane's tokens l16 + 16 j of channels ch0 .. ch0 + 3), e^{G_n},
+  // the wave's range flag, then the split operands and X ----
+  auto split = [&](int par, int lane) {
+    const int g = lane >> 4, l16 = lane & 15, ch0 = 16 * wave + 4 * g;
     const unsigned char* st = smem;
-    // ---- 1. prefix sums of log alpha over the chunk, per channel, inside the wave: this lane's
-    // tokens l16 + 16 j (j = 0, 1) of channels ch0 .. ch0 + 3 ----
+    __bf16* tQ = reinterpret_cast<__bf16*>(pbuf(par) + L::pQ);
+    __bf16* tC = reinterpret_cast<__bf16*>(pbuf(par) + L::pC);
+    __bf16* tK = reinterpret_cast<__bf16*>(pbuf(par) + L::pK);
+    __bf16* tP = reinterpret_cast<__bf16*>(pbuf(par) + L::pP);
+    __bf16* tX = reinterpret_cast<__bf16*>(pbuf(par) + L::pX);
+    float* fG = reinterpret_cast<float*>(smem + L::oF) + par * DK;
     float G[2][4], la[2][4];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -389,7 +403,6 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, unsigned char* smem, 
     const bool wave_ok = __all(ok);
     if (lane == 0) sFlag[wave] = wave_ok ? 0 : 1;
 
-    // ---- 2. split operands and X into LDS (rows l16 + 16 j, columns ch0 .. + 3) ----
     // (all reads of both tokens first, so that their latencies overlap)
     float q4[2][4], k4[2][4], c4[2][4], x4[2][4], w4[2][4];
     {
@@ -415,6 +428,27 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, unsigned char* smem, 
         if constexpr (WK == kChannel) unpack4(rw[j], w4[j]);
       }
     }
+    // e^{G_t} and e^{-G_t}; e^{G_{t-1}} and e^{-G_{t-1}} (decay after the erase) are the previous
+    // token's: the row's lane l16 - 1 (DPP row_shr:1), row lane 15 of the first 16 tokens for
+    // token 16, and 1 for token 0
+    float eq[2][4], er[2][4], ep[2][4], epr[2][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        eq[j][i] = __expf(G[j][i]);
+        er[j][i] = __builtin_amdgcn_rcpf(eq[j][i]);
+      }
+      if (TWO) {
+        const float e0 = dpp_row<0x111>(eq[0][i]), r0 = dpp_row<0x111>(er[0][i]);
+        const float e1 = dpp_row<0x111>(eq[1][i]), r1 = dpp_row<0x111>(er[1][i]);
+        const float e15 = row_lane15(eq[0][i]), r15 = row_lane15(er[0][i]);
+        ep[0][i] = l16 == 0 ? 1.f : e0;
+        epr[0][i] = l16 == 0 ? 1.f : r0;
+        ep[1][i] = l16 == 0 ? e15 : e1;
+        epr[1][i] = l16 == 0 ? r15 : r1;
+      }
+    }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int t = l16 + 16 * j;
@@ -423,15 +457,13 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, unsigned char* smem, 
       for (int i = 0; i < 4; ++i) {
         c4[j][i] *= k4[j][i];
         x4[j][i] *= w4[j][i];
-        const float eq = __expf(G[j][i]);  // e^{G_t}
-        oq[i] = q4[j][i] * eq;
-        ok_[i] = k4[j][i] * __builtin_amdgcn_rcpf(eq);  // e^{-G_t}
+        oq[i] = q4[j][i] * eq[j][i];
+        ok_[i] = k4[j][i] * er[j][i];
         if (TWO) {
-          const float ep = __expf(G[j][i] - la[j][i]);  // e^{G_{t-1}}
-          oc[i] = c4[j][i] * ep;
-          op[i] = -k4[j][i] * __builtin_amdgcn_rcpf(ep);  // stored negated
+          oc[i] = c4[j][i] * ep[j][i];
+          op[i] = -k4[j][i] * epr[j][i];  // stored negated
         } else {
-          oc[i] = c4[j][i] * eq;
+          oc[i] = c4[j][i] * eq[j][i];
           ok_[i] = -ok_[i];  // stored negated
         }
       }
@@ -441,323 +473,391 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, unsigned char* smem, 
       if (TWO) *reinterpret_cast<uint2*>(tP + t * LDT + ch0) = pack4(op);
       *reinterpret_cast<uint2*>(tX + t * LDT + ch0) = pack4(x4[j]);
     }
-    lds_barrier_keep_vm();  // B1
-    bool flagged;
-    {
-      const int4 f0 = reinterpret_cast<const int4*>(sFlag)[0], f1 = reinterpret_cast<const int4*>(sFlag)[1];
-      flagged = (f0.x | f0.y | f0.z | f0.w | f1.x | f1.y | f1.z | f1.w) != 0;
+  };
+
+  // ---- Gram tiles of operand buffer par into Gram buffer par: 6 jobs = 2 row operands x 3 lower
+  // tile pairs (waves 2-7) ----
+  auto gram = [&](int par, int lane) {
+    if (wave < 2) return;
+    const int g = lane >> 4, l16 = lane & 15;
+    const __bf16* tQ = reinterpret_cast<const __bf16*>(pbuf(par) + L::pQ);
+    const __bf16* tC = reinterpret_cast<const __bf16*>(pbuf(par) + L::pC);
+    const __bf16* tK = reinterpret_cast<const __bf16*>(pbuf(par) + L::pK);
+    const __bf16* tP = reinterpret_cast<const __bf16*>(pbuf(par) + L::pP);
+    __bf16* gA = reinterpret_cast<__bf16*>(gbuf(par) + L::gA);
+    __bf16* gM = reinterpret_cast<__bf16*>(gbuf(par) + L::gM);
+    __bf16* gLK = reinterpret_cast<__bf16*>(gbuf(par) + L::gLK);
+    __bf16* gMQK = reinterpret_cast<__bf16*>(gbuf(par) + L::gMQK);
+    float* Ld = reinterpret_cast<float*>(gbuf(par) + L::gLD);
+    const int job = wave - 2, grp = job / 3, tix = job % 3;
+    const int ta = tix >= 1 ? 1 : 0, tb = tix == 2 ? 1 : 0;
+    const __bf16* ar = (grp == 0 ? tC : tQ) + (16 * ta + l16) * LDT;
+    const __bf16* br = ((TWO && grp == 0) ? tP : tK) + (16 * tb + l16) * LDT;
+    const __bf16* cr = (grp == 0 ? tK : tP) + (16 * tb + l16) * LDT;
+    F8 fa[4], fb[4], fc[4];
+#pragma unroll
+    for (int kb = 0; kb < DK / 32; ++kb) {
+      fa[kb] = lds_load8(ar + 32 * kb + 8 * g);
+      fb[kb] = lds_load8(br + 32 * kb + 8 * g);
+      if (TWO) fc[kb] = lds_load8(cr + 32 * kb + 8 * g);
     }
-
-    if (flagged) {
-      // ---- exact token path: raw rows into LDS (q, k, c = b . k; decays in fp32, over the o
-      // staging, which holds nothing pending: a chunk's outputs are stored at the next chunk's
-      // start), then the recurrence token by token on the register-resident tiles ----
+    f32x4 acc1 = zero4(), acc2 = zero4();
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int t = l16 + 16 * j;
-        float k4[4], c4[4];
-        unpack4(*reinterpret_cast<const uint2*>(st + L::sK + stage_off(t, ch0)), k4);
-        stage_gate4<BK>(st + L::sB, t, ch0, 0.f, c4);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) c4[i] *= k4[i];
-        *reinterpret_cast<uint2*>(tQ + t * LDT + ch0) = *reinterpret_cast<const uint2*>(st + L::sQ + stage_off(t, ch0));
-        *reinterpret_cast<uint2*>(tK + t * LDT + ch0) = pack4(k4);
-        *reinterpret_cast<uint2*>(tC + t * LDT + ch0) = pack4(c4);
-        *reinterpret_cast<float4*>(fAl + t * LDF + ch0) =
-            make_float4(__expf(la[j][0]), __expf(la[j][1]), __expf(la[j][2]), __expf(la[j][3]));
-      }
-      lds_barrier_keep_vm();
-      if (wave < 2 && c + 1 < c_end) stage(c + 1, lane);
-      const auto ro = make_rsrc(a.o + ((bi * T + c * C) * H + hi) * DV, wy_range(T - c * C, H, DV));
-      __bf16* qt = PHI ? a.Qt + (bh * nch + c) * C * DK : nullptr;
-      __bf16* on = PHI ? a.On + (bh * nch + c) * C * DV : nullptr;
-      // one state tile through the chunk, token by token (one tile per loop keeps the values the
-      // loop carries to 32); is_n: an N tile (writes X, read-outs to o), else Phi (read-outs to Q~)
-      auto run_tile = [&](f32x4 (&S)[8], bool is_n) {
-#pragma unroll 1
-        for (int t = 0; t < C; ++t) {
-          auto rowv = [&](const __bf16* base, int m, float* f) {
-            unpack4(*reinterpret_cast<const uint2*>(base + t * LDT + 16 * m + 4 * g), f);
-          };
-          auto decay = [&](int m, float* f) {
-            const float4 al = *reinterpret_cast<const float4*>(fAl + t * LDF + 16 * m + 4 * g);
-            f[0] = al.x; f[1] = al.y; f[2] = al.z; f[3] = al.w;
-          };
-          float r = 0.f;
-#pragma unroll
-          for (int m = 0; m < 8; ++m) {
-            float c4[4], a4[4];
-            rowv(tC, m, c4);
-            if (!TWO) decay(m, a4);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              if (!TWO) S[m][i] *= a4[i];  // decay first
-              r += c4[i] * S[m][i];
-            }
-          }
-          r += __shfl_xor(r, 16);
-          r += __shfl_xor(r, 32);
-          const float x = is_n ? static_cast<float>(tX[t * LDT + col]) : 0.f;
-          float y = 0.f;
-#pragma unroll
-          for (int m = 0; m < 8; ++m) {
-            float q4[4], k4[4], a4[4];
-            rowv(tQ, m, q4);
-            rowv(tK, m, k4);
-            if (TWO) decay(m, a4);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              float sv = S[m][i] - k4[i] * r;
-              if (TWO) sv *= a4[i];
-              sv += k4[i] * x;
-              S[m][i] = sv;
-              y += q4[i] * sv;
-            }
-          }
-          y += __shfl_xor(y, 16);
-          y += __shfl_xor(y, 32);
-          if (g == 0) {
-            if (!is_n)
-              qt[seg_qt_pos(t, col)] = static_cast<__bf16>(y);
-            else if (PHI)
-              on[seg_on_pos(t, col)] = static_cast<__bf16>(y);
-            else
-              __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, static_cast<__bf16>(y)),
-                                                    ro, static_cast<uint32_t>(t) * hdv + col * 2, 0, 0);
-          }
-        }
-      };
-      run_tile(SN, true);
-      if constexpr (PHI) run_tile(SP, false);
-      lds_barrier_keep_vm();
-      // the decays overlaid the o staging; the Gram arrays' upper tiles still read zero
-      out_pending = false;
-      continue;
+    for (int kb = 0; kb < DK / 32; ++kb) {
+      acc1 = MM::mma8(fa[kb], fb[kb], acc1);
+      if (TWO) acc2 = MM::mma8(fa[kb], fc[kb], acc2);
     }
-
-    // ---- 3. the next chunk's inputs: their staging has been read ----
-    if (wave < 2 && c + 1 < c_end) stage(c + 1, lane);
-
-    // ---- 4. Gram tiles: 6 jobs = 2 row operands x 3 lower tile pairs (waves 2-7) ----
-    if (wave >= 2) {
-      const int job = wave - 2, grp = job / 3, tix = job % 3;
-      const int ta = tix >= 1 ? 1 : 0, tb = tix == 2 ? 1 : 0;
-      const __bf16* ar = (grp == 0 ? tC : tQ) + (16 * ta + l16) * LDT;
-      const __bf16* br = ((TWO && grp == 0) ? tP : tK) + (16 * tb + l16) * LDT;
-      const __bf16* cr = (grp == 0 ? tK : tP) + (16 * tb + l16) * LDT;
-      F8 fa[4], fb[4], fc[4];
-#pragma unroll
-      for (int kb = 0; kb < DK / 32; ++kb) {
-        fa[kb] = lds_load8(ar + 32 * kb + 8 * g);
-        fb[kb] = lds_load8(br + 32 * kb + 8 * g);
-        if (TWO) fc[kb] = lds_load8(cr + 32 * kb + 8 * g);
-      }
-      f32x4 acc1 = zero4(), acc2 = zero4();
-#pragma unroll
-      for (int kb = 0; kb < DK / 32; ++kb) {
-        acc1 = MM::mma8(fa[kb], fb[kb], acc1);
-        if (TWO) acc2 = MM::mma8(fa[kb], fc[kb], acc2);
-      }
-      // which: 0 = -L_P / -L (strict; the off-diagonal block transposed -> gA, the diagonal
-      // blocks -> Ld negated back), 1 = -M_QP / -M, 2 = L_K (strict), 3 = M_QK (inclusive).  The
-      // products against the negated key family (which 0 and 1) arrive negated.
-      auto store_tile = [&](int which, const f32x4& acc) {
-        const int r0 = 16 * ta + 4 * g, cc = 16 * tb + l16;
-        if (ta > tb) {
-          if (which == 0) {  // (-L_10)^T: row l16, columns 4 g .. 4 g + 3
-            float a4[4] = {acc[0], acc[1], acc[2], acc[3]};
-            *reinterpret_cast<uint2*>(gA + l16 * LDA + 4 * g) = pack4(a4);
-            return;
-          }
-          __bf16* dst = (which == 1 ? gM : which == 2 ? gLK : gMQK) + r0 * LDD + cc;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) dst[i * LDD] = static_cast<__bf16>(acc[i]);
+    // which: 0 = -L_P / -L (strict; the off-diagonal block transposed -> gA, the diagonal
+    // blocks -> Ld negated back), 1 = -M_QP / -M, 2 = L_K (strict), 3 = M_QK (inclusive).  The
+    // products against the negated key family (which 0 and 1) arrive negated.
+    auto store_tile = [&](int which, const f32x4& acc) {
+      const int r0 = 16 * ta + 4 * g, cc = 16 * tb + l16;
+      if (ta > tb) {
+        if (which == 0) {  // (-L_10)^T: row l16, columns 4 g .. 4 g + 3
+          float a4[4] = {acc[0], acc[1], acc[2], acc[3]};
+          *reinterpret_cast<uint2*>(gA + l16 * LDA + 4 * g) = pack4(a4);
           return;
         }
-        const bool strict = which == 0 || which == 2;
+        __bf16* dst = (which == 1 ? gM : which == 2 ? gLK : gMQK) + r0 * LDD + cc;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = r0 + i;
-          const float val = (strict ? (cc < r) : (cc <= r)) ? acc[i] : 0.f;
-          if (which == 0)
-            Ld[(ta * 16 + (r & 15)) * LDL + (cc & 15)] = -val;
-          else if (which == 1)
-            gM[r * LDD + cc] = static_cast<__bf16>(val);
-          else if (which == 2)
-            gLK[r * LDD + cc] = static_cast<__bf16>(val);
-          else
-            gMQK[r * LDD + cc] = static_cast<__bf16>(val);
-        }
-      };
-      if (TWO) {
-        store_tile(grp == 0 ? 0 : 3, acc1);
-        store_tile(grp == 0 ? 2 : 1, acc2);
-      } else {
-        store_tile(grp == 0 ? 0 : 1, acc1);
+        for (int i = 0; i < 4; ++i) dst[i * LDD] = static_cast<__bf16>(acc[i]);
+        return;
       }
+      const bool strict = which == 0 || which == 2;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = r0 + i;
+        const float val = (strict ? (cc < r) : (cc <= r)) ? acc[i] : 0.f;
+        if (which == 0)
+          Ld[(ta * 16 + (r & 15)) * LDL + (cc & 15)] = -val;
+        else if (which == 1)
+          gM[r * LDD + cc] = static_cast<__bf16>(val);
+        else if (which == 2)
+          gLK[r * LDD + cc] = static_cast<__bf16>(val);
+        else
+          gMQK[r * LDD + cc] = static_cast<__bf16>(val);
+      }
+    };
+    if (TWO) {
+      store_tile(grp == 0 ? 0 : 3, acc1);
+      store_tile(grp == 0 ? 2 : 1, acc2);
+    } else {
+      store_tile(grp == 0 ? 0 : 1, acc1);
     }
-    lds_barrier_keep_vm();  // B2
-
-    // ---- 5. the state.  U = Cs S (channel contraction, N and Phi), Z = L_K X (MODE 2) or -X;
-    // T = (I + L)^{-1} in every wave (seg_inv_sweep for the diagonal blocks, three small MFMAs for
-    // the off-diagonal one); R = T U + T Z; O^T = S^T Qs^T - R^T M^T (+ X^T M_QK^T); S update. ----
-    {
-      // operand loads first: their latencies overlap the conversions and the sweep
-      F8 cfr[2][4];  // rows 16 ta + l16 of Cs, channels 32 kb + pair(g)
+    // a diagonal block of L_P / L: its inverse D by seg_inv_sweep, from the rows this wave just
+    // wrote (the wave's own LDS writes precede its reads), over the same area
+    if (grp == 0 && ta == tb) {
+      float* Lb = Ld + ta * 16 * LDL;
+      float nl[16], d[4];
 #pragma unroll
-      for (int ta = 0; ta < 2; ++ta)
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) cfr[ta][kb] = lds_pair_frag_k<DK>(tC + (16 * ta + l16) * LDT, 32 * kb, g);
-      float nl[2][16];  // row l16 of -L_00 and -L_11
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int c4 = 0; c4 < 4; ++c4) {
-          const float4 v = *reinterpret_cast<const float4*>(Ld + (16 * b + l16) * LDL + 4 * c4);
-          nl[b][4 * c4] = -v.x;
-          nl[b][4 * c4 + 1] = -v.y;
-          nl[b][4 * c4 + 2] = -v.z;
-          nl[b][4 * c4 + 3] = -v.w;
-        }
-      const bf16x4 nl10t = lds_load4(gA + l16 * LDA + 4 * g);  // (-L_10)^T [l16][4 g ..]
-      const F8 xf = seg_col_frag(tX, LDT, col, g, l16);        // X column col over the tokens
-      F8 lkf[2];
-      if (TWO) {
-#pragma unroll
-        for (int ta = 0; ta < 2; ++ta) lkf[ta] = lds_pair_frag_k<C>(gLK + (16 * ta + l16) * LDD, 0, g);
+      for (int c4 = 0; c4 < 4; ++c4) {
+        const float4 v = *reinterpret_cast<const float4*>(Lb + l16 * LDL + 4 * c4);
+        nl[4 * c4] = -v.x;
+        nl[4 * c4 + 1] = -v.y;
+        nl[4 * c4 + 2] = -v.z;
+        nl[4 * c4 + 3] = -v.w;
       }
-      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) d[e] = (4 * g + e == l16) ? 1.f : 0.f;
+      seg_inv_sweep<0>(d, nl);
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): every lane's reads of the rows are done
+      *reinterpret_cast<uint2*>(reinterpret_cast<__bf16*>(Lb) + l16 * L::LDI + 4 * g) = pack4(d);
+    }
+  };
 
-      F8 sfN[4], sfP[4];
+  // ---- the state through chunk c, part 1: U = Cs S (channel contraction, N and Phi), Z = L_K X
+  // (MODE 2) or -X; T = (I + L)^{-1} (the diagonal blocks' inverses from the Gram waves, the
+  // off-diagonal block by three small MFMAs in every wave); R = T U + T Z; O^T = S^T Qs^T - R^T M^T (+ X^T M_QK^T),
+  // stored.  Leaves R (over the tokens) and X's column for part 2. ----
+  auto chain1 = [&](int64_t c, int par, int lane, F8& rfN, F8& rfP, F8& xf) {
+    const int g = lane >> 4, l16 = lane & 15, ch0 = 16 * wave + 4 * g, col = 16 * wave + l16;
+    const __bf16* tQ = reinterpret_cast<const __bf16*>(pbuf(par) + L::pQ);
+    const __bf16* tC = reinterpret_cast<const __bf16*>(pbuf(par) + L::pC);
+    const __bf16* tX = reinterpret_cast<const __bf16*>(pbuf(par) + L::pX);
+    const __bf16* gA = reinterpret_cast<const __bf16*>(gbuf(par) + L::gA);
+    const __bf16* gM = reinterpret_cast<const __bf16*>(gbuf(par) + L::gM);
+    const __bf16* gLK = reinterpret_cast<const __bf16*>(gbuf(par) + L::gLK);
+    const __bf16* gMQK = reinterpret_cast<const __bf16*>(gbuf(par) + L::gMQK);
+    const float* Ld = reinterpret_cast<const float*>(gbuf(par) + L::gLD);
+    // operand loads first: their latencies overlap the conversions and the sweep
+    F8 cfr[2][4];  // rows 16 ta + l16 of Cs, channels 32 kb + pair(g)
+#pragma unroll
+    for (int ta = 0; ta < 2; ++ta)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) cfr[ta][kb] = lds_pair_frag_k<DK>(tC + (16 * ta + l16) * LDT, 32 * kb, g);
+    // D_b[l16][4 g .. 4 g + 3] (the Gram waves' inverses of the diagonal blocks)
+    const bf16x4 d0 = lds_load4(reinterpret_cast<const __bf16*>(Ld) + l16 * L::LDI + 4 * g);
+    const bf16x4 d1 = lds_load4(reinterpret_cast<const __bf16*>(Ld + 16 * LDL) + l16 * L::LDI + 4 * g);
+    const bf16x4 nl10t = lds_load4(gA + l16 * LDA + 4 * g);  // (-L_10)^T [l16][4 g ..]
+    xf = seg_col_frag(tX, LDT, col, g, l16);                 // X column col over the tokens
+    F8 lkf[2];
+    if (TWO) {
+#pragma unroll
+      for (int ta = 0; ta < 2; ++ta) lkf[ta] = lds_pair_frag_k<C>(gLK + (16 * ta + l16) * LDD, 0, g);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    F8 sfN[4], sfP[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      sfN[kb] = acc_pair_frag<__bf16>(SN[2 * kb], SN[2 * kb + 1]);
+      if constexpr (PHI) sfP[kb] = acc_pair_frag<__bf16>(SP[2 * kb], SP[2 * kb + 1]);
+    }
+    // U (the N and Phi tiles share each Cs fragment)
+    f32x4 UN[2], UP[2];
+#pragma unroll
+    for (int ta = 0; ta < 2; ++ta) {
+      UN[ta] = zero4();
+      UP[ta] = zero4();
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        sfN[kb] = acc_pair_frag<__bf16>(SN[2 * kb], SN[2 * kb + 1]);
-        if constexpr (PHI) sfP[kb] = acc_pair_frag<__bf16>(SP[2 * kb], SP[2 * kb + 1]);
-      }
-      // U (the N and Phi tiles share each Cs fragment)
-      f32x4 UN[2], UP[2];
-#pragma unroll
-      for (int ta = 0; ta < 2; ++ta) {
-        UN[ta] = zero4();
-        UP[ta] = zero4();
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          UN[ta] = MM::mma8(cfr[ta][kb], sfN[kb], UN[ta]);
-          if constexpr (PHI) UP[ta] = MM::mma8(cfr[ta][kb], sfP[kb], UP[ta]);
-        }
-      }
-      F8 zf;  // Z over the tokens (k) for column col
-      if (TWO) {
-        const f32x4 z0 = MM::mma8(lkf[0], xf, zero4()), z1 = MM::mma8(lkf[1], xf, zero4());
-        zf = acc_pair_frag<__bf16>(z0, z1);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) zf[e] = -xf[e];
-      }
-      // T as A operands: rows 16 ta + l16, tokens in pair order.  The lane's sweep values are
-      // D_b[l16][4 g .. 4 g + 3], already that layout; T_10 arrives in it as the accumulator of
-      // T_10^T = D_0^T ((-L_10)^T D_1^T).
-      float d[2][4];
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) d[b][e] = (4 * g + e == l16) ? 1.f : 0.f;
-      seg_inv_sweep<0>(d, nl);
-      const bf16x4 d0 = __builtin_bit_cast(bf16x4, pack4(d[0])), d1 = __builtin_bit_cast(bf16x4, pack4(d[1]));
-      f32x4 id;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) id[e] = (4 * g + e == l16) ? 1.f : 0.f;
-      const f32x4 D0 = MM::mma4(d0, acc_frag4<__bf16>(id), zero4());                 // D_0[4 g + i][l16]
-      const f32x4 Qm = MM::mma4(nl10t, d1, zero4());                                  // (-L_10)^T D_1^T
-      const f32x4 T10t = MM::mma4(acc_frag4<__bf16>(D0), acc_frag4<__bf16>(Qm), zero4());  // T_10[l16][4 g + i]
-      F8 tf0, tf1;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        tf0[e] = d0[e];
-        tf0[4 + e] = static_cast<__bf16>(0.f);
-        tf1[e] = static_cast<__bf16>(T10t[e]);
-        tf1[4 + e] = d1[e];
-      }
-      // R = T (U + Z), tokens 16 ta + 4 g + i, column col
-      const F8 ufN = acc_pair_frag<__bf16>(UN[0], UN[1]);
-      F8 ufP;
-      if constexpr (PHI) ufP = acc_pair_frag<__bf16>(UP[0], UP[1]);
-      f32x4 RN[2], RP[2];
-      RN[0] = MM::mma8(tf0, ufN, MM::mma8(tf0, zf, zero4()));
-      RN[1] = MM::mma8(tf1, ufN, MM::mma8(tf1, zf, zero4()));
-      if constexpr (PHI) {
-        RP[0] = MM::mma8(tf0, ufP, zero4());
-        RP[1] = MM::mma8(tf1, ufP, zero4());
-      }
-      const F8 rfN = acc_pair_frag<__bf16>(RN[0], RN[1]);
-      F8 rfP;
-      if constexpr (PHI) rfP = acc_pair_frag<__bf16>(RP[0], RP[1]);
-      // O^T: lane holds O[token 16 ta + l16][column 16 w + 4 g + i], into the o (and Q~) staging
-#pragma unroll
-      for (int ta = 0; ta < 2; ++ta) {
-        F8 qf[4];
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) qf[kb] = lds_pair_frag_k<DK>(tQ + (16 * ta + l16) * LDT, 32 * kb, g);
-        const F8 mf = lds_pair_frag_k<C>(gM + (16 * ta + l16) * LDD, 0, g);
-        F8 mqf;
-        if (TWO) mqf = lds_pair_frag_k<C>(gMQK + (16 * ta + l16) * LDD, 0, g);
-        f32x4 oN = zero4(), oP = zero4();
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          oN = MM::mma8(sfN[kb], qf[kb], oN);
-          if constexpr (PHI) oP = MM::mma8(sfP[kb], qf[kb], oP);
-        }
-        oN = MM::mma8(rfN, mf, oN);
-        if constexpr (PHI) oP = MM::mma8(rfP, mf, oP);
-        if (TWO) oN = MM::mma8(xf, mqf, oN);
-        const int t = 16 * ta + l16;
-        float o4[4] = {oN[0], oN[1], oN[2], oN[3]};
-        if constexpr (PHI) {
-          // straight from the accumulators: seg_on_pos / seg_qt_pos of (t, 16 w + 4 g)
-          float p4[4] = {oP[0], oP[1], oP[2], oP[3]};
-          __bf16* on = a.On + (bh * nch + c) * C * DV;
-          __bf16* qt = a.Qt + (bh * nch + c) * C * DK;
-          *reinterpret_cast<uint2*>(on + ((ta * 8 + wave) * 64 + lane) * 4) = pack4(o4);
-          *reinterpret_cast<uint2*>(qt + ((ta * 4 + (wave >> 1)) * 64 + lane) * 8 + (wave & 1) * 4) = pack4(p4);
-        } else {
-          *reinterpret_cast<uint2*>(tO + t * LDT + ch0) = pack4(o4);
-        }
-      }
-      // S update: S += Ks^T X + (-Ps)^T R (MODE 2) or S += (-Ks)^T R (MODE 1), then S = e^{G_n} . S
-#pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        const F8 kf = seg_col_frag(tK, LDT, 16 * m + l16, g, l16);
-        if (TWO) {
-          const F8 pf = seg_col_frag(tP, LDT, 16 * m + l16, g, l16);
-          SN[m] = MM::mma8(kf, xf, SN[m]);
-          SN[m] = MM::mma8(pf, rfN, SN[m]);
-          if constexpr (PHI) SP[m] = MM::mma8(pf, rfP, SP[m]);
-        } else {
-          SN[m] = MM::mma8(kf, rfN, SN[m]);
-          if constexpr (PHI) SP[m] = MM::mma8(kf, rfP, SP[m]);
-        }
-      }
-#pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        const float4 f = *reinterpret_cast<const float4*>(fG + 16 * m + 4 * g);
-        SN[m][0] *= f.x;
-        SN[m][1] *= f.y;
-        SN[m][2] *= f.z;
-        SN[m][3] *= f.w;
-        if constexpr (PHI) {
-          SP[m][0] *= f.x;
-          SP[m][1] *= f.y;
-          SP[m][2] *= f.z;
-          SP[m][3] *= f.w;
-        }
+        UN[ta] = MM::mma8(cfr[ta][kb], sfN[kb], UN[ta]);
+        if constexpr (PHI) UP[ta] = MM::mma8(cfr[ta][kb], sfP[kb], UP[ta]);
       }
     }
-    lds_barrier_keep_vm();  // B6: this chunk's operands are no longer read
-    out_pending = !PHI;
+    F8 zf;  // Z over the tokens (k) for column col
+    if (TWO) {
+      const f32x4 z0 = MM::mma8(lkf[0], xf, zero4()), z1 = MM::mma8(lkf[1], xf, zero4());
+      zf = acc_pair_frag<__bf16>(z0, z1);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) zf[e] = -xf[e];
+    }
+    // T as A operands: rows 16 ta + l16, tokens in pair order.  D_b[l16][4 g .. 4 g + 3] is that
+    // layout already; T_10 arrives in it as the accumulator of T_10^T = D_0^T ((-L_10)^T D_1^T).
+    f32x4 id;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) id[e] = (4 * g + e == l16) ? 1.f : 0.f;
+    const f32x4 D0 = MM::mma4(d0, acc_frag4<__bf16>(id), zero4());                      // D_0[4 g + i][l16]
+    const f32x4 Qm = MM::mma4(nl10t, d1, zero4());                                       // (-L_10)^T D_1^T
+    const f32x4 T10t = MM::mma4(acc_frag4<__bf16>(D0), acc_frag4<__bf16>(Qm), zero4());  // T_10[l16][4 g + i]
+    F8 tf0, tf1;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      tf0[e] = d0[e];
+      tf0[4 + e] = static_cast<__bf16>(0.f);
+      tf1[e] = static_cast<__bf16>(T10t[e]);
+      tf1[4 + e] = d1[e];
+    }
+    // R = T (U + Z), tokens 16 ta + 4 g + i, column col
+    const F8 ufN = acc_pair_frag<__bf16>(UN[0], UN[1]);
+    F8 ufP;
+    if constexpr (PHI) ufP = acc_pair_frag<__bf16>(UP[0], UP[1]);
+    f32x4 RN[2], RP[2];
+    RN[0] = MM::mma8(tf0, ufN, MM::mma8(tf0, zf, zero4()));
+    RN[1] = MM::mma8(tf1, ufN, MM::mma8(tf1, zf, zero4()));
+    if constexpr (PHI) {
+      RP[0] = MM::mma8(tf0, ufP, zero4());
+      RP[1] = MM::mma8(tf1, ufP, zero4());
+    }
+    rfN = acc_pair_frag<__bf16>(RN[0], RN[1]);
+    if constexpr (PHI) rfP = acc_pair_frag<__bf16>(RP[0], RP[1]);
+    // O^T: lane holds O[token 16 ta + l16][column 16 w + 4 g + i]
+    const int64_t t0 = c * C;
+    const auto ro = make_rsrc(a.o + ((bi * T + t0) * H + hi) * DV, wy_range(T - t0, H, DV));
+#pragma unroll
+    for (int ta = 0; ta < 2; ++ta) {
+      F8 qf[4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) qf[kb] = lds_pair_frag_k<DK>(tQ + (16 * ta + l16) * LDT, 32 * kb, g);
+      const F8 mf = lds_pair_frag_k<C>(gM + (16 * ta + l16) * LDD, 0, g);
+      F8 mqf;
+      if (TWO) mqf = lds_pair_frag_k<C>(gMQK + (16 * ta + l16) * LDD, 0, g);
+      f32x4 oN = zero4(), oP = zero4();
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        oN = MM::mma8(sfN[kb], qf[kb], oN);
+        if constexpr (PHI) oP = MM::mma8(sfP[kb], qf[kb], oP);
+      }
+      oN = MM::mma8(rfN, mf, oN);
+      if constexpr (PHI) oP = MM::mma8(rfP, mf, oP);
+      if (TWO) oN = MM::mma8(xf, mqf, oN);
+      float o4[4] = {oN[0], oN[1], oN[2], oN[3]};
+      if constexpr (PHI) {
+        // straight from the accumulators: seg_on_pos / seg_qt_pos of (16 ta + l16, 16 w + 4 g)
+        float p4[4] = {oP[0], oP[1], oP[2], oP[3]};
+        __bf16* on = a.On + (bh * nch + c) * C * DV;
+        __bf16* qt = a.Qt + (bh * nch + c) * C * DK;
+        *reinterpret_cast<uint2*>(on + ((ta * 8 + wave) * 64 + lane) * 4) = pack4(o4);
+        *reinterpret_cast<uint2*>(qt + ((ta * 4 + (wave >> 1)) * 64 + lane) * 8 + (wave & 1) * 4) = pack4(p4);
+      } else {
+        buf_store8(ro, static_cast<uint32_t>(16 * ta + l16) * hdv + ch0 * 2, pack4(o4));
+      }
+    }
+  };
+
+  // ---- part 2: S += Ks^T X + (-Ps)^T R (MODE 2) or S += (-Ks)^T R (MODE 1), then
+  // S = e^{G_n} . S ----
+  auto chain2 = [&](int par, int lane, const F8& rfN, const F8& rfP, const F8& xf) {
+    const int g = lane >> 4, l16 = lane & 15;
+    const __bf16* tK = reinterpret_cast<const __bf16*>(pbuf(par) + L::pK);
+    const __bf16* tP = reinterpret_cast<const __bf16*>(pbuf(par) + L::pP);
+    const float* fG = reinterpret_cast<const float*>(smem + L::oF) + par * DK;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const F8 kf = seg_col_frag(tK, LDT, 16 * m + l16, g, l16);
+      if (TWO) {
+        const F8 pf = seg_col_frag(tP, LDT, 16 * m + l16, g, l16);
+        SN[m] = MM::mma8(kf, xf, SN[m]);
+        SN[m] = MM::mma8(pf, rfN, SN[m]);
+        if constexpr (PHI) SP[m] = MM::mma8(pf, rfP, SP[m]);
+      } else {
+        SN[m] = MM::mma8(kf, rfN, SN[m]);
+        if constexpr (PHI) SP[m] = MM::mma8(kf, rfP, SP[m]);
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const float4 f = *reinterpret_cast<const float4*>(fG + 16 * m + 4 * g);
+      SN[m][0] *= f.x;
+      SN[m][1] *= f.y;
+      SN[m][2] *= f.z;
+      SN[m][3] *= f.w;
+      if constexpr (PHI) {
+        SP[m][0] *= f.x;
+        SP[m][1] *= f.y;
+        SP[m][2] *= f.z;
+        SP[m][3] *= f.w;
+      }
+    }
+  };
+
+  // ---- a flagged chunk c, token by token in fp32 from its staged inputs, on the
+  // register-resident tiles: one tile per loop (keeps the values the loop carries to 32); is_n: an
+  // N tile (takes X, read-outs to o or On), else Phi (read-outs to Qt) ----
+  auto token = [&](int64_t c, int lane) {
+    const int g = lane >> 4, l16 = lane & 15, col = 16 * wave + l16;
+    const unsigned char* st = smem;
+    const int64_t t0 = c * C;
+    const auto ro = make_rsrc(a.o + ((bi * T + t0) * H + hi) * DV, wy_range(T - t0, H, DV));
+    __bf16* qt = PHI ? a.Qt + (bh * nch + c) * C * DK : nullptr;
+    __bf16* on = PHI ? a.On + (bh * nch + c) * C * DV : nullptr;
+    auto run_tile = [&](f32x4 (&S)[8], bool is_n) {
+#pragma unroll 1
+      for (int t = 0; t < C; ++t) {
+        auto decay = [&](int m, float* f) {
+          float l4[4];
+          stage_gate4<AK>(st + L::sLA, t, 16 * m + 4 * g, 0.f, l4);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) f[i] = __expf(l4[i]);
+        };
+        float r = 0.f;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          float k4[4], c4[4], a4[4];
+          unpack4(*reinterpret_cast<const uint2*>(st + L::sK + stage_off(t, 16 * m + 4 * g)), k4);
+          stage_gate4<BK>(st + L::sB, t, 16 * m + 4 * g, 0.f, c4);
+          if (!TWO) decay(m, a4);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if (!TWO) S[m][i] *= a4[i];  // decay first
+            r += c4[i] * k4[i] * S[m][i];
+          }
+        }
+        r += __shfl_xor(r, 16);
+        r += __shfl_xor(r, 32);
+        float x = 0.f;
+        if (is_n) {
+          float wv;
+          if constexpr (WK == kChannel) wv = stage_elem(st + L::sW, t, col);
+          else if constexpr (WK == kScalar) wv = static_cast<float>(reinterpret_cast<const __bf16*>(st + L::sW)[t]);
+          else wv = 1.f;
+          x = stage_elem(st + L::sV, t, col) * wv;
+        }
+        float y = 0.f;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          float q4[4], k4[4], a4[4];
+          unpack4(*reinterpret_cast<const uint2*>(st + L::sQ + stage_off(t, 16 * m + 4 * g)), q4);
+          unpack4(*reinterpret_cast<const uint2*>(st + L::sK + stage_off(t, 16 * m + 4 * g)), k4);
+          if (TWO) decay(m, a4);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float sv = S[m][i] - k4[i] * r;
+            if (TWO) sv *= a4[i];
+            sv += k4[i] * x;
+            S[m][i] = sv;
+            y += q4[i] * sv;
+          }
+        }
+        y += __shfl_xor(y, 16);
+        y += __shfl_xor(y, 32);
+        if (g == 0) {
+          if (!is_n)
+            qt[seg_qt_pos(t, col)] = static_cast<__bf16>(y);
+          else if (PHI)
+            on[seg_on_pos(t, col)] = static_cast<__bf16>(y);
+          else
+            __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, static_cast<__bf16>(y)),
+                                                  ro, static_cast<uint32_t>(t) * hdv + col * 2, 0, 0);
+        }
+      }
+    };
+    run_tile(SN, true);
+    if constexpr (PHI) run_tile(SP, false);
+  };
+
+  // ---- prologue: the first chunk's operands (and the loads of the second) ----
+  bool flag_cur = false;  // (uniform) chunk c is flagged
+  if (c_begin < c_end) {
+    const int lane = opaque_v(tid) & 63;
+    stage(c_begin, lane);
+    arrive(lane);
+    lds_barrier_keep_vm();
+    split(0, lane);
+    lds_barrier_keep_vm();
+    flag_cur = flagged_now();
+    if (!flag_cur) {
+      if (c_begin + 1 < c_end) stage(c_begin + 1, lane);
+      gram(0, lane);
+    }
+    lds_barrier_keep_vm();
   }
-  if (wave >= 4 && out_pending) store_out(c_end - 1, tid);
+
+  int par = 0;  // operand buffer of chunk c
+  for (int64_t c = c_begin; c < c_end; ++c, par ^= 1) {
+    // the lane from an opaque copy of the thread index: values derived from it are recomputed
+    // where used instead of being kept across the loop in registers the chunk needs
+    const int lane = opaque_v(tid) & 63;
+    const bool has_next = c + 1 < c_end;
+    bool flag_next = false;
+    if (flag_cur) {
+      // the staging still holds chunk c: nothing was loaded after it
+      token(c, lane);
+      lds_barrier_keep_vm();
+      if (has_next) {  // refill: chunk c + 1 from its loads to its Gram products
+        stage(c + 1, lane);
+        arrive(lane);
+        lds_barrier_keep_vm();
+        split(par ^ 1, lane);
+        lds_barrier_keep_vm();
+        flag_next = flagged_now();
+        if (!flag_next) {
+          if (c + 2 < c_end) stage(c + 2, lane);
+          gram(par ^ 1, lane);
+        }
+        lds_barrier_keep_vm();
+      }
+      flag_cur = flag_next;
+      continue;
+    }
+    arrive(lane);
+    lds_barrier_keep_vm();  // A0: chunk c + 1's inputs are in the staging
+    if (has_next) split(par ^ 1, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    F8 rfN, rfP, xf;
+    chain1(c, par, lane, rfN, rfP, xf);
+    lds_barrier_keep_vm();  // A1: chunk c + 1's operands are in their buffer, its flags known
+    if (has_next) flag_next = flagged_now();
+    if (has_next && !flag_next && c + 2 < c_end) stage(c + 2, lane);
+    chain2(par, lane, rfN, rfP, xf);
+    if (has_next && !flag_next) gram(par ^ 1, lane);
+    lds_barrier_keep_vm();  // A2
+    flag_cur = flag_next;
+  }
 
   // ---- end of the segment: the final state (one segment), or N, Phi and E_1 (from segment 0) ----
+  const int lane = tid & 63, g = lane >> 4, col = 16 * wave + (lane & 15);
   if (a.nseg == 1) {
     if (a.S_T != nullptr) {
       float* St = a.S_T + bh * DK * DV;
