@@ -51,10 +51,11 @@ def flops_per_head_token(d, C, channel_two_factor, erase=True):
 
 def prefill_chunk(wl):
     """Chunk length the library's kernels use for this workload: 32 in the segment kernel (bf16,
-    d_k = d_v = 128, per-channel decay with per-channel or scalar erase and write gates), 64
-    elsewhere."""
-    seg = (wl.dtype == "bf16" and wl.DK == 128 and wl.DV == 128 and wl.alpha == "channel" and
-           ((wl.b == "channel" and wl.w == "channel") or (wl.b == "scalar" and wl.w == "scalar")))
+    d_k = d_v = 128, per-channel decay with per-channel or scalar erase and write gates, or scalar
+    decay with scalar gates), 64 elsewhere."""
+    gates = ((wl.alpha == "channel" and wl.b == "channel" and wl.w == "channel") or
+             (wl.alpha in ("channel", "scalar") and wl.b == "scalar" and wl.w == "scalar"))
+    seg = wl.dtype == "bf16" and wl.DK == 128 and wl.DV == 128 and gates
     return 32 if seg else 64
 
 

@@ -33,15 +33,17 @@ SegPlan seg_plan(int64_t nstate, int64_t T) {
 }  // namespace
 
 // Gate combinations with an instantiation: the Gated DeltaNet-2 gates (per-channel decay, erase
-// and write gates) and the KDA gates (per-channel decay, one scalar beta as erase and write gate),
-// in either order.  Any other combination (a scalar decay among them) takes the two-kernel path,
-// which is the faster one there.
+// and write gates), the KDA gates (per-channel decay, one scalar beta as erase and write gate),
+// either order, and the Gated DeltaNet gates (scalar decay, scalar beta; a scalar decay commutes
+// with the erase, so it takes the decay-first form).  Any other combination takes the two-kernel
+// path.
 bool prefill_seg_ok(int64_t DK, int64_t DV, int alpha_kind, int b_kind, int w_kind, bool decay_first) {
-  (void)decay_first;
+  (void)decay_first;  // both orders are built
   if (DK != 128 || DV != 128) return false;
   const bool gdn2 = alpha_kind == kChannel && b_kind == kChannel && w_kind == kChannel;
   const bool kda = alpha_kind == kChannel && b_kind == kScalar && w_kind == kScalar;
-  return gdn2 || kda;
+  const bool gdn = alpha_kind == kScalar && b_kind == kScalar && w_kind == kScalar;
+  return gdn2 || kda || gdn;
 }
 
 // Workspace of a segmented call (none for a single segment per state): Q~ and the read-out of N of
@@ -95,8 +97,9 @@ hipError_t prefill_seg_launch(const PrefillArgs<bf16_t>& pa, int64_t nstate, boo
   if (nstate == 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>(nstate * p.nseg)), block(512);
   const bool bch = a.b_kind == kChannel;
-  if (a.alpha_kind != kChannel) return hipErrorInvalidValue;  // (prefill_seg_ok admits none)
-  if (two && bch)
+  if (a.alpha_kind == kScalar)
+    hipLaunchKernelGGL((seg_kernel<1, kScalar, kScalar, kScalar>), grid, block, 0, s, a);
+  else if (two && bch)
     hipLaunchKernelGGL((seg_kernel<2, kChannel, kChannel, kChannel>), grid, block, 0, s, a);
   else if (two)
     hipLaunchKernelGGL((seg_kernel<2, kChannel, kScalar, kScalar>), grid, block, 0, s, a);

@@ -82,8 +82,9 @@ typedef enum { GDR_ERASE_THEN_DECAY = 0, GDR_DECAY_THEN_ERASE = 1 } gdr_order;
  * form in 64-token chunks, except the segment kernel, which uses 32.  Which
  * kernels run:
  *   bf16, dk = dv = 128, per-channel decay with per-channel (erase and write)
- *     or scalar (both) gates, either order: the segment kernel (a state's
- *     chunks split into segments run side by side, then linked);
+ *     or scalar (both) gates, either order, or a scalar decay with scalar
+ *     erase and write gates: the segment kernel (a state's chunks split into
+ *     segments run side by side, then linked);
  *   other shapes: the chunkwise kernels where their LDS layout fits (every
  *     bf16 shape except dk = 256 with a per-channel decay after the erase;
  *     fp32 at dk <= 32, and at dk = 64 with a scalar, no or decay-first

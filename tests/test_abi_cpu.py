@@ -132,8 +132,8 @@ def test_empty_problem_is_a_no_op():
 
 
 def seg_workspace(nstate, T):
-    """Workspace of the fused segment prefill (d_k = d_v = 128 with the Gated DeltaNet-2 or KDA
-    gates): each state's 32-token chunks split into ceil(256 / states) segments (at most one per
+    """Workspace of the fused segment prefill (d_k = d_v = 128 with the Gated DeltaNet-2, KDA or
+    Gated DeltaNet gates): each state's 32-token chunks split into ceil(256 / states) segments (at most one per
     chunk); with more than one segment, Q~ and the read-out of N (32 x 128 bf16 each) per chunk
     and, per segment, N, Phi, the state leaving segment 0 (128 x 128 fp32 each) and the entering
     state (bf16), each array rounded up to 256 bytes.  None with one segment per state."""
@@ -154,6 +154,8 @@ def test_workspace_query_and_decode_validation():
     assert N.workspace_bytes(prob()) == seg_workspace(6, 70) > 0
     assert N.workspace_bytes(prob(order=N.DECAY_THEN_ERASE)) == seg_workspace(6, 70)
     assert N.workspace_bytes(prob(batch=64, heads=8, seqlen=70)) == 0  # one segment per state
+    assert N.workspace_bytes(prob(alpha_kind=N.GATE_SCALAR, b_kind=N.GATE_SCALAR,
+                                  w_kind=N.GATE_SCALAR)) == seg_workspace(6, 70)
     # per-channel decay elsewhere (either order): the chunk's affine map A' (dk x dk), Q' (64 x
     # dk), D^T (dv x dk), Z' (64 x dv) in bf16, e^{G_n} (dk + 4 fp32) and a flag per 64-token chunk
     # of every (batch, head), each array rounded up to 256 bytes
@@ -170,9 +172,6 @@ def test_workspace_query_and_decode_validation():
     need = r(chunks * 64 * 128 * 2) + r(chunks * 64 * 128 * 2) + r(chunks * 64 * 64 * 2) + \
         r(chunks * 132 * 4)
     assert N.workspace_bytes(sp) == need
-    # (a scalar decay takes this kernel with any write gate, d_k = d_v = 128 included)
-    assert N.workspace_bytes(prob(alpha_kind=N.GATE_SCALAR, b_kind=N.GATE_SCALAR,
-                                  w_kind=N.GATE_SCALAR)) == need
     assert N.workspace_bytes(prob(alpha_kind=N.GATE_SCALAR, b_kind=N.GATE_SCALAR, w_kind=N.GATE_SCALAR,
                                   io_dtype=N.GDR_FP32, dk=32, dv=32)) == 0
     a = big_apart()
