@@ -107,11 +107,13 @@ def decode_bytes(wl):
 
 def kernel_source_digest():
     """SHA-256 over the kernel sources and the build script: HBM counter figures recorded for
-    other sources no longer describe the kernels that run."""
+    other sources no longer describe the kernels that run.  The C ABI's argument validation
+    (gdr_api.hip) launches nothing and is left out."""
     import hashlib
     h = hashlib.sha256()
     pkg = os.path.join(ROOT, "gated_delta_rule_71_amd")
-    files = sorted(os.path.join("csrc", f) for f in os.listdir(os.path.join(pkg, "csrc")))
+    files = sorted(os.path.join("csrc", f) for f in os.listdir(os.path.join(pkg, "csrc"))
+                   if f != "gdr_api.hip")
     for rel in files + ["buildlib.py"]:
         h.update(rel.encode())
         with open(os.path.join(pkg, rel), "rb") as f:

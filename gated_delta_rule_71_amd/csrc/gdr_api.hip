@@ -39,6 +39,7 @@ size_t prefill_workspace_bytes(int io_dtype, int64_t nstate, int64_t T, int64_t 
 namespace {
 
 constexpr int64_t kMaxDim = int64_t(1) << 31;
+constexpr int64_t kMaxRows = int64_t(1) << 48;  // batch x seqlen x heads
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -72,6 +73,9 @@ int check_problem(const gdr_problem* p) {
   if (p->chunk != 0 && p->chunk != 64) return GDR_ERR_UNSUPPORTED;
   // index arithmetic inside the kernels is 64-bit; grids are 32-bit
   if (p->batch * p->heads >= kMaxDim / 64) return GDR_ERR_UNSUPPORTED;
+  // byte counts of the tensors (rows x width x 4 at most) and workspaces stay far inside int64
+  // (batch x heads < 2^25 and seqlen < 2^31 here, so the product itself cannot overflow)
+  if (p->batch * p->heads * p->seqlen >= kMaxRows) return GDR_ERR_UNSUPPORTED;
   return GDR_OK;
 }
 

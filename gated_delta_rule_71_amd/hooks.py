@@ -99,7 +99,10 @@ def replace_write(q, k, v, log_alpha=None, b=None, w=None, S0=None, position=0, 
     `donor` is a dict with the donor's "k", "v" and (optionally) "w" tensors of the same shapes;
     only their values at `position` are used.  The erase and decay at `position` stay the
     recipient's.  Returns (o, S_T): the blocked run plus the donor write carried through the
-    recipient's transitions (one ``chunk_fwd`` call over a batch of two)."""
+    recipient's transitions (one ``chunk_fwd`` call over a batch of two).  The two runs' outputs
+    are added in fp32 and o is rounded to the I/O dtype once more, so a bf16 o carries one rounding
+    beyond that of a single run (at most half a bf16 unit in the last place); S_T is the fp32 sum
+    of the two fp32 states."""
     torch = _torch()
     if donor is None:
         raise ValueError("replace_write needs the donor's tensors")
@@ -121,7 +124,7 @@ def replace_write(q, k, v, log_alpha=None, b=None, w=None, S0=None, position=0, 
     o, S = chunk_fwd(cat(q, None), torch.cat([k, k2], 0), torch.cat([v, v2], 0),
                      cat(log_alpha, None), cat(b, None), torch.cat([w_blocked, w_donor], 0), S0s,
                      order=order)
-    return o[:B] + o[B:], S[:B] + S[B:]
+    return (o[:B].float() + o[B:].float()).to(o.dtype), S[:B] + S[B:]
 
 
 def swap_state(q, k, v, log_alpha=None, b=None, w=None, S0=None, position=0, donor=None,

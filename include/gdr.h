@@ -77,7 +77,9 @@ typedef enum { GDR_ERASE_THEN_DECAY = 0, GDR_DECAY_THEN_ERASE = 1 } gdr_order;
  * orders (GDR_ERR_UNSUPPORTED otherwise); the backward is narrower (see
  * gdr_chunk_bwd).  chunk == 64 or 0 (the same); batch, heads >= 0; seqlen >= 0
  * (any value: a ragged last chunk is padded with identity tokens inside the
- * kernel).  The chunk length does not change the result, which equals the
+ * kernel).  Sizes: batch, heads and seqlen below 2^31 (GDR_ERR_INVALID_ARGUMENT
+ * otherwise), batch * heads below 2^25 and batch * heads * seqlen below 2^48
+ * (GDR_ERR_UNSUPPORTED otherwise).  The chunk length does not change the result, which equals the
  * token-by-token recurrence up to rounding; the kernels block the chunkwise
  * form in 64-token chunks, except the segment kernel, which uses 32.  Which
  * kernels run:
