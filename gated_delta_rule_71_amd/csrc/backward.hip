@@ -1,5 +1,5 @@
 // Host side of the backward pass: workspace carving and the launches.
-#include "backward.h"
+#include "backward_ch.h"
 
 namespace gdr {
 
@@ -53,6 +53,21 @@ void launch_chain(const BwdArgs& a, int64_t nstate, hipStream_t s) {
                        dim3(64 * (2 + DK / 32)), 0, s, a);
 }
 
+// Per-channel decay (dk = 128, dv 64 or 128): the chunk maps in the order MODE (2: erase first,
+// 1: decay first), the chains, then the chunk-local adjoint by matrix products for every chunk
+// whose gates stay in range and token by token for the others.
+template <int MODE>
+hipError_t launch_channel(WycArgs f, const BwdArgs& a, int64_t nstate, hipStream_t s) {
+  const int64_t nblk = nstate * a.nch;
+  hipLaunchKernelGGL((wyc_prep_kernel<128, 128, MODE>), dim3((unsigned)nblk), dim3(512), 0, s, f);
+  hipLaunchKernelGGL((bwd_db_kernel<128, 128>), dim3((unsigned)nblk), dim3(256), 0, s, a);
+  launch_chain<128, false>(a, nstate, s);
+  launch_chain<128, true>(a, nstate, s);
+  hipLaunchKernelGGL((bwd_chl_kernel<MODE>), dim3((unsigned)nblk), dim3(512), 0, s, a);
+  hipLaunchKernelGGL((bwd_chl_token_kernel<MODE>), dim3((unsigned)nblk), dim3((unsigned)(64 * (a.DV / 16))), 0, s, a);
+  return hipGetLastError();
+}
+
 // halves: the chunk-local adjoint's argument sets, one per 128 value columns
 template <int DK>
 hipError_t launch_dk(WycArgs f, const BwdArgs& a, const BwdArgs* halves, int nh, int64_t nstate,
@@ -81,10 +96,12 @@ void sum_parts(const bf16_t* s0, const bf16_t* s1, bf16_t* dst, int64_t rows, in
 }
 }  // namespace
 
-// bf16 I/O, a scalar decay or none, dk in {32, 64, 128}, dv a multiple of 16 up to 256.
+// bf16 I/O; a scalar decay or none with dk in {32, 64, 128} and dv a multiple of 16 up to 256,
+// or a per-channel decay with dk = 128 and dv 64 or 128.
 bool backward_supported(int io_dtype_bf16, int64_t DK, int64_t DV, int alpha_kind) {
-  return io_dtype_bf16 && (DK == 32 || DK == 64 || DK == 128) && DV % 16 == 0 && DV > 0 && DV <= 256 &&
-         alpha_kind != kChannel;
+  if (!io_dtype_bf16) return false;
+  if (alpha_kind == kChannel) return DK == 128 && (DV == 64 || DV == 128);
+  return (DK == 32 || DK == 64 || DK == 128) && DV % 16 == 0 && DV > 0 && DV <= 256;
 }
 
 size_t backward_workspace_bytes(int64_t B, int64_t H, int64_t Hk, int64_t T, int64_t DK, int64_t DV) {
@@ -96,7 +113,7 @@ hipError_t launch_backward(const bf16_t* q, const bf16_t* k, const bf16_t* v, co
                            const float* dST, bf16_t* dq, bf16_t* dk, bf16_t* dv, bf16_t* dla,
                            bf16_t* db, bf16_t* dw, float* dS0, int64_t B, int64_t T, int64_t H,
                            int64_t Hk, int64_t DK, int64_t DV, int alpha_kind, int b_kind, int w_kind,
-                           void* workspace, hipStream_t s) {
+                           bool decay_first, void* workspace, hipStream_t s) {
   const int64_t nstate = B * H;
   if (nstate == 0) return hipSuccess;
   if (T == 0) {
@@ -203,10 +220,15 @@ hipError_t launch_backward(const bf16_t* q, const bf16_t* k, const bf16_t* v, co
     }
   }
   hipError_t e;
-  switch (DK) {
-    case 32: e = launch_dk<32>(f, a, halves, nh, nstate, s); break;
-    case 64: e = launch_dk<64>(f, a, halves, nh, nstate, s); break;
-    default: e = launch_dk<128>(f, a, halves, nh, nstate, s); break;
+  if (alpha_kind == kChannel) {
+    // (d_v <= 128: one column half; the chunk-local kernels take every value column)
+    e = decay_first ? launch_channel<1>(f, halves[0], nstate, s) : launch_channel<2>(f, halves[0], nstate, s);
+  } else {
+    switch (DK) {
+      case 32: e = launch_dk<32>(f, a, halves, nh, nstate, s); break;
+      case 64: e = launch_dk<64>(f, a, halves, nh, nstate, s); break;
+      default: e = launch_dk<128>(f, a, halves, nh, nstate, s); break;
+    }
   }
   if (e != hipSuccess) return e;
   const int64_t rows = B * T * H;

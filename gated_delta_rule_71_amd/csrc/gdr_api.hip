@@ -31,7 +31,7 @@ hipError_t launch_backward(const bf16_t* q, const bf16_t* k, const bf16_t* v, co
                            const float* dST, bf16_t* dq, bf16_t* dk, bf16_t* dv, bf16_t* dla,
                            bf16_t* db, bf16_t* dw, float* dS0, int64_t B, int64_t T, int64_t H,
                            int64_t Hk, int64_t DK, int64_t DV, int alpha_kind, int b_kind, int w_kind,
-                           void* workspace, hipStream_t s);
+                           bool decay_first, void* workspace, hipStream_t s);
 size_t prefill_workspace_bytes(int io_dtype, int64_t nstate, int64_t T, int64_t DK, int64_t DV,
                                int alpha_kind, int b_kind, int w_kind, bool decay_first);
 }  // namespace gdr
@@ -375,6 +375,7 @@ GDR_EXPORT int gdr_chunk_bwd(const gdr_problem* p, const void* q, const void* k,
       (const T*)q, (const T*)k, (const T*)v, (const T*)gate_ptr(p->alpha_kind, log_alpha),
       (const T*)gate_ptr(p->b_kind, b), (const T*)gate_ptr(p->w_kind, w), S0, (const T*)dO, dS_T,
       (T*)dq, (T*)dk, (T*)dv, (T*)dla_, (T*)db_, (T*)dw_, dS0, p->batch, p->seqlen, p->heads, qk_heads(p), p->dk,
-      p->dv, p->alpha_kind, p->b_kind, p->w_kind, workspace, reinterpret_cast<hipStream_t>(stream));
+      p->dv, p->alpha_kind, p->b_kind, p->w_kind, p->order == GDR_DECAY_THEN_ERASE, workspace,
+      reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
 }

@@ -235,17 +235,22 @@ size_t gdr_chunk_bwd_workspace_bytes(const gdr_problem* p);
  *   workspace, workspace_bytes  device scratch of at least
  *          gdr_chunk_bwd_workspace_bytes(p) bytes, 16-byte aligned; calls that
  *          share one workspace must not overlap in time.
- * Outputs must not overlap the inputs or each other.  Supported: bf16, a scalar
- * decay or none (both orders are then the same recurrence), any erase and
- * write gate kinds, dk in {32, 64, 128}, dv a multiple of 16 up to 256, and
- * grouped q / k heads (dq and dk are then summed over the value heads that
- * share each q / k head); GDR_ERR_UNSUPPORTED otherwise.
+ * Outputs must not overlap the inputs or each other.  Supported: bf16 with
+ * any erase and write gate kinds and grouped q / k heads (dq and dk are then
+ * summed over the value heads that share each q / k head), and either
+ *   a scalar decay or none (both orders are then the same recurrence), dk in
+ *   {32, 64, 128}, dv a multiple of 16 up to 256; or
+ *   a per-channel decay (the Gated DeltaNet-2 and KDA gates), either order,
+ *   dk = 128 and dv 64 or 128;
+ * GDR_ERR_UNSUPPORTED otherwise.
  * Method: the adjoint of the chunk form of gdr_chunk_fwd ("Recurrent Memory",
  * sections 03 and 04): the state at every chunk boundary by a forward pass over
  * the chunk maps, the gradient of the state at every boundary by the transposed
  * maps in reverse, and each chunk's input gradients from those two by matrix
  * products, the transposed triangular solve and a suffix sum of the decay
- * gradient inside the chunk.
+ * gradient inside the chunk.  With a per-channel decay a chunk whose prefix
+ * sums of log alpha leave [-76, 76] (or are not finite) is differentiated
+ * token by token from its checkpoint instead, exactly for any gate values.
  */
 int gdr_chunk_bwd(const gdr_problem* p, const void* q, const void* k, const void* v,
                   const void* log_alpha, const void* b, const void* w, const float* S0,

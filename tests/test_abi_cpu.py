@@ -237,8 +237,14 @@ def test_backward_workspace_and_validation():
         r(ch * 128 * 128 * 2) + r(ch * 64 * 128 * 2) + r(ch * 256 * 128 * 2) + r(ch * 64 * 256 * 2) +
         r(ch * 132 * 4) + r(ch * 4) + 5 * r(ch * 128 * 256 * 2) + 2 * 2 * r(rows * 128 * 2) +
         3 * 2 * r(rows * 128 * 2))
-    # outside the backward's scope: per-channel decay, fp32, dv > 256, dk = 16
-    for p in (prob(), prob(alpha_kind=N.GATE_SCALAR, io_dtype=N.GDR_FP32),
+    # a per-channel decay at d_k = 128 and d_v 64 or 128, either order: the same arrays (the chunk
+    # maps of the per-channel forward, the checkpoints and Q'^T dO)
+    assert N.bwd_workspace_bytes(prob()) == need
+    assert N.bwd_workspace_bytes(prob(order=N.DECAY_THEN_ERASE, b_kind=N.GATE_SCALAR,
+                                      w_kind=N.GATE_SCALAR)) == need
+    assert N.bwd_workspace_bytes(prob(dv=64)) > 0
+    # outside the backward's scope: per-channel decay at other widths, fp32, dv > 256, dk = 16
+    for p in (prob(dk=64), prob(dv=256), prob(dv=96), prob(alpha_kind=N.GATE_SCALAR, io_dtype=N.GDR_FP32),
               prob(alpha_kind=N.GATE_SCALAR, dv=512), prob(alpha_kind=N.GATE_SCALAR, dk=16)):
         assert N.bwd_workspace_bytes(p) == 0
         assert bwd_call(p) == N.GDR_ERR_UNSUPPORTED

@@ -232,3 +232,104 @@ def test_backward_wide_values_grouped(dev):
     for n in ("dq", "dk"):
         ref[n] = ref[n].reshape(B, T, HK, H // HK, D).sum(3)
     compare(out, ref, "wide grouped")
+
+
+# ---- per-channel decay (the Gated DeltaNet-2 and KDA gates), d_k = 128 ----
+
+CH_KINDS = {  # (alpha, b, w, shared beta)
+    "gdn2": ("channel", "channel", "channel", False),
+    "kda": ("channel", "scalar", "scalar", True),
+    "gla": ("channel", "none", "none", False),
+    "gdn2_sw": ("channel", "channel", "scalar", False),
+}
+
+
+def ch_case(kind, B=1, H=2, T=150, DV=128, s0=0.02, seed=101, mu=-2.0):
+    a, b, w, shared = CH_KINDS[kind]
+    wl = synth.Workload("t", B, H, T, 128, DV, "bf16", a, b, w, shared, mu, s0, seed)
+    x = synth.make_prefill(wl)
+    rng = np.random.default_rng(seed + 1)
+    x["do"] = torch.from_numpy(rng.standard_normal((B, T, H, DV)).astype(np.float32)).to(torch.bfloat16)
+    x["dS_T"] = torch.from_numpy((0.1 * rng.standard_normal((B, H, 128, DV))).astype(np.float32))
+    return x
+
+
+@pytest.mark.parametrize("order", ["erase_then_decay", "decay_then_erase"])
+@pytest.mark.parametrize("kind", list(CH_KINDS))
+def test_backward_channel_decay(dev, kind, order):
+    """Per-channel decay in either order: chunks of 64 tokens (two whole, one ragged), S0 and
+    dS_T, against the token adjoint."""
+    x = ch_case(kind)
+    say("backward channel", kind, order)
+    compare(run(x, dev, order), reference(x, order=0 if order == "erase_then_decay" else 1),
+            "%s %s" % (kind, order))
+
+
+@pytest.mark.parametrize("T,DV", [(1, 128), (64, 64), (65, 128), (200, 64)])
+def test_backward_channel_shapes(dev, T, DV):
+    x = ch_case("gdn2", T=T, DV=DV, seed=110 + T)
+    say("backward channel shape", T, DV)
+    compare(run(x, dev), reference(x), "T=%d dv=%d" % (T, DV))
+
+
+@pytest.mark.parametrize("order", ["erase_then_decay", "decay_then_erase"])
+def test_backward_channel_flagged_chunks(dev, order):
+    """Chunks whose prefix sums of log alpha leave [-76, 76] take the token-by-token adjoint:
+    log alpha = -7 over the second chunk on half the channels (a span of 448 nats), and -3 over
+    the ragged last chunk, beside ordinary chunks."""
+    x = ch_case("gdn2", T=64 * 3 + 20, seed=121)
+    la = x["log_alpha"].clone()
+    la[:, 64:128, :, :64] = -7.0
+    la[:, 192:, :, 100:] = -3.0
+    x["log_alpha"] = la
+    say("backward channel flagged", order)
+    compare(run(x, dev, order), reference(x, order=0 if order == "erase_then_decay" else 1),
+            "flagged %s" % order)
+
+
+def test_backward_channel_grouped_heads(dev):
+    """KDA gates with four value heads over two q / k heads."""
+    B, H, HK, T = 1, 4, 2, 130
+    wl = synth.Workload("t", B, H, T, 128, 128, "bf16", "channel", "scalar", "scalar", True, -2.0, 0.02, 131,
+                        HK=HK)
+    x = synth.make_prefill(wl)
+    rng = np.random.default_rng(132)
+    x["do"] = torch.from_numpy(rng.standard_normal((B, T, H, 128)).astype(np.float32)).to(torch.bfloat16)
+    x["dS_T"] = torch.from_numpy((0.1 * rng.standard_normal((B, H, 128, 128))).astype(np.float32))
+    say("backward channel grouped")
+    out = run(x, dev)
+    xe = synth.expand_heads({n: x[n] for n in ("q", "k", "v", "log_alpha", "b", "w", "S0")}, H)
+    xe["do"], xe["dS_T"] = x["do"], x["dS_T"]
+    ref = reference(xe)
+    for n in ("dq", "dk"):
+        ref[n] = ref[n].reshape(B, T, HK, H // HK, 128).sum(3)
+    compare(out, ref, "channel grouped")
+
+
+@pytest.mark.parametrize("name,npick", [("kda", 8), ("gdn2", 2)])
+def test_backward_channel_workload_sampled(dev, name, npick):
+    """The KDA (B=2, H=32, T=8192) and Gated DeltaNet-2 (B=1, H=16, T=32768) workloads at full
+    size; the oracle's adjoint (which keeps every token's state in fp64) runs on eight sampled
+    (batch, head) states of KDA and two of the four times longer Gated DeltaNet-2 sequence."""
+    wl = synth.WORKLOADS[name]
+    x = synth.make_prefill(wl)
+    rng = np.random.default_rng(141)
+    x["do"] = torch.from_numpy(rng.standard_normal((wl.B, wl.T, wl.H, wl.DV)).astype(np.float32)).to(torch.bfloat16)
+    x["dS_T"] = None
+    say("backward channel workload", name)
+    out = run(x, dev)
+    pick = [(i % wl.B, (5 * i + 3) % wl.H) for i in range(npick)]
+    bi = torch.tensor([p[0] for p in pick])
+    hi = torch.tensor([p[1] for p in pick])
+    xs = subset_heads({n: x[n] for n in ("q", "k", "v", "log_alpha", "b", "w", "S0", "do")}, bi, hi)
+    xs["dS_T"] = None
+    ref = reference(xs)
+    sel = {}
+    for n, t in out.items():
+        if t is None:
+            sel[n] = None
+        elif n == "dS0":
+            sel[n] = t[bi.to(t.device), hi.to(t.device)].unsqueeze(1)
+        else:
+            sel[n] = t[bi.to(t.device), :, hi.to(t.device)].unsqueeze(2)
+    compare(sel, ref, "%s sampled" % name)
