@@ -65,6 +65,7 @@ struct BwdArgs {
   __bf16* ST;        // [cix][dv][dk]   S_{c-1}^T
   __bf16* GR;        // [cix][dk][dv]   dS_c
   __bf16* GT;        // [cix][dv][dk]   dS_c^T
+  int* cflag;        // [cix] per-channel chunk-local adjoint: 1 where the token-by-token kernel runs
   int64_t T, H, DV, nch;
   int alpha_kind, b_kind, w_kind;
   int64_t Hk;  // q / k heads: value head h reads q / k head h / (H / Hk); with Hk < H, dq and dk

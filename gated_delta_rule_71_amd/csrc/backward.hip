@@ -172,6 +172,7 @@ hipError_t launch_backward(const bf16_t* q, const bf16_t* k, const bf16_t* v, co
   a.Ad = f.Ad;
   a.Dt = f.Dt;
   a.Egn = f.Egn;
+  a.cflag = f.flag;  // (the chunk maps' flags are not read after the chains)
   a.SR = reinterpret_cast<__bf16*>(ws);
   a.ST = reinterpret_cast<__bf16*>(ws + z.ck);
   a.GR = reinterpret_cast<__bf16*>(ws + 2 * z.ck);

@@ -31,7 +31,7 @@
 // only ever pair them as e^{G_t - G_s} with t >= s, or with S_0 and dS_n as e^{G_t} and e^{G_n -
 // G_t}.  A chunk past that (or with a non-finite gate) is flagged: bwd_chl_kernel leaves it, and
 // bwd_chl_token_kernel differentiates it token by token in fp32 from its checkpoint, exactly for
-// any gate values.  Both kernels flag a chunk from the same sequential prefix sums.
+// any gate values.  bwd_chl_kernel records which chunks it left in a.cflag.
 #pragma once
 
 #include "backward.h"
@@ -67,27 +67,47 @@ __device__ __forceinline__ Mma<__bf16>::F8 chl_neg8(const Mma<__bf16>::F8& f) {
   return __builtin_bit_cast(Mma<__bf16>::F8, u);
 }
 
-// Per-channel prefix sums of log alpha over the chunk, by threads 0..127 (one channel each, tokens
-// in order, fp32): G[t][ch] into sG (64 x 128 fp32) and e^{G_63} into fGn; a chunk with any
-// |G_t| > 76 or a non-finite one sets *flag.  Tokens past the state's end read as log alpha = 0.
-// The caller zeroes *flag and places a barrier before and after.
-__device__ __forceinline__ void chl_prefix(const BwdArgs& a, int64_t rr, int64_t left, float* sG, float* fGn,
-                                           int* flag, int tid) {
-  if (tid >= 128) return;
+// Per-channel prefix sums of log alpha over the chunk by a workgroup of 512 threads (channel
+// tid % 128, tokens 16 (tid / 128) .. + 15; the four partial sums are joined through qtot, 4 x 128
+// fp32): G[t][ch] into sG (64 x 128 fp32) and, when fGn is given, e^{G_63} into fGn; a chunk with
+// any |G_t| > 76 or a non-finite one sets *flag.  Tokens past the state's end read as log alpha =
+// 0.  The loads (chl_prefix_load) are issued ahead of the sums, so that their latency overlaps
+// other work.  Every thread calls both; the caller zeroes *flag and places a barrier before and
+// after chl_prefix.
+struct ChlRaw {
+  uint16_t v[16];
+};
+__device__ __forceinline__ ChlRaw chl_prefix_load(const BwdArgs& a, int64_t rr, int64_t left, int tid) {
+  const int ch = tid & 127, q = tid >> 7;
   const auto rla = make_rsrc(a.la + rr * 128, wy_range(left, a.H, 128));
   const uint32_t hdk = static_cast<uint32_t>(a.H * 128 * 2);
-  uint16_t raw[64];
+  ChlRaw r;
 #pragma unroll
-  for (int t = 0; t < 64; ++t) raw[t] = buf_load_u16(rla, t * hdk + tid * 2);
-  float G = 0.f;
+  for (int u = 0; u < 16; ++u) r.v[u] = buf_load_u16(rla, (16 * q + u) * hdk + ch * 2);
+  return r;
+}
+__device__ __forceinline__ void chl_prefix(const ChlRaw& raw, float* sG, float* fGn, float* qtot, int* flag,
+                                           int tid) {
+  const int ch = tid & 127, q = tid >> 7;
+  float G[16];
+  float run = 0.f;
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    run += bf16_to_f32(raw.v[u]);
+    G[u] = run;
+  }
+  qtot[q * 128 + ch] = run;
+  lds_barrier();
+  float off = 0.f;
+  for (int j = 0; j < q; ++j) off += qtot[j * 128 + ch];
   bool ok = true;
 #pragma unroll
-  for (int t = 0; t < 64; ++t) {
-    G += bf16_to_f32(raw[t]);
-    ok = ok && fabsf(G) <= kChlSpanLimit;
-    sG[t * 128 + tid] = G;
+  for (int u = 0; u < 16; ++u) {
+    const float x = G[u] + off;
+    ok = ok && fabsf(x) <= kChlSpanLimit;
+    sG[(16 * q + u) * 128 + ch] = x;
   }
-  if (fGn != nullptr) fGn[tid] = __expf(G);
+  if (fGn != nullptr && q == 3) fGn[ch] = __expf(G[15] + off);
   if (!ok) atomicOr(flag, 1);
 }
 
@@ -107,9 +127,11 @@ struct ChlLayout {
   static constexpr int oT = (TWO ? oMQP : oMQK) + GRAM;
   // one value half: X, dO, R, and W (B' = Ch S_0 + L_K X, then dR, then dV)
   static constexpr int oX = oT + GRAM, oO = oX + HALF, oR = oO + HALF, oW = oR + HALF;
-  // fp32: e^{G_n} [128], sum_j dSh . Sh [128], scalar db [64], scalar dw [64], the flag
+  // fp32: e^{G_n} [128], sum_j dSh . Sh [128], scalar db [64], scalar dw [64], the flag; the
+  // partial sums of the prefix and suffix scans [4][128]
   static constexpr int oF = oW + HALF;
-  static constexpr int total = oF + (128 + 128 + 64 + 64 + 4) * 4;
+  static constexpr int oQT = oF + (128 + 128 + 64 + 64 + 4) * 4;
+  static constexpr int total = oQT + 4 * 128 * 4;
   // aliases: the prefix sums (fp32 [64][128]) over the half area in the prologue, the pieces of
   // the triangular inverse there too; after the products, G (again) and the per-token gate
   // gradients over the operand area, and (erase first) the gradients of G_{t-1} over the half area
@@ -121,9 +143,11 @@ struct ChlLayout {
   static constexpr bool fits = total <= kLdsLimit;
 };
 
-// One workgroup of 8 waves per (state, chunk); chunks flagged by chl_prefix are left to
-// bwd_chl_token_kernel.  Value columns are taken in halves of 64 (the per-half products in LDS);
-// the gradients summed over value columns accumulate in registers across the halves.
+// One workgroup of 8 waves per (state, chunk); chunks flagged by chl_prefix are marked in
+// a.cflag and left to bwd_chl_token_kernel.  Value columns are taken in halves of 64 (the per-half
+// products in LDS); the gradients summed over value columns accumulate in registers across the
+// halves.  Global operands (checkpoint fragments, input rows) are loaded ahead of the phase that
+// uses them, so that one load latency is paid per phase.
 template <int MODE>
 __global__ __launch_bounds__(512) void bwd_chl_kernel(BwdArgs a) {
   using L = ChlLayout<MODE>;
@@ -153,6 +177,7 @@ __global__ __launch_bounds__(512) void bwd_chl_kernel(BwdArgs a) {
   float* fdb = fGn + 256;
   float* fdw = fGn + 320;
   int* sFlag = reinterpret_cast<int*>(fGn + 384);
+  float* qtot = reinterpret_cast<float*>(smem + L::oQT);
   float* sG = reinterpret_cast<float*>(smem + L::oG);
   __bf16* gA = reinterpret_cast<__bf16*>(smem + L::oGA);
   float* Ld = reinterpret_cast<float*>(smem + L::oLD);
@@ -184,7 +209,7 @@ __global__ __launch_bounds__(512) void bwd_chl_kernel(BwdArgs a) {
   const auto rdo = make_rsrc(a.dO + rr * DV, rng_v);
 
   // ---- prologue: zero the Gram matrices (their upper tiles are read as zeros) and the sums;
-  // prefix sums and the flag ----
+  // the split's input rows and the rows of S_0 . dS_n are loaded before the prefix sums ----
   for (int i = tid; i < (L::oX - L::oLK) / 16; i += NT)
     reinterpret_cast<uint4*>(smem + L::oLK)[i] = make_uint4(0, 0, 0, 0);
   if (tid < 128) {
@@ -195,22 +220,67 @@ __global__ __launch_bounds__(512) void bwd_chl_kernel(BwdArgs a) {
     }
     if (tid == 0) *sFlag = 0;
   }
+  const ChlRaw la_raw = chl_prefix_load(a, rr, left, tid);
+  uint2 uq[4], uk[4], ub[4];  // item j: token tid / 32 + 16 j, channels 4 (tid % 32) ..
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int item = tid + NT * j, t = item >> 5, i0 = (item & 31) * 4;
+    uq[j] = chl_load8(rq, t * hqk + i0 * 2);
+    uk[j] = chl_load8(rk, t * hqk + i0 * 2);
+    if (a.b_kind == kChannel) {
+      ub[j] = chl_load8(rbc, t * hdk + i0 * 2);
+    } else {
+      ub[j].x = a.b_kind == kScalar ? buf_load_u16(rbs, t * h1) : 0u;
+      ub[j].y = 0u;
+    }
+  }
+  // sum_j S_0[ch][j] dS_n[ch][j]: channel tid / 4, columns (tid % 4) DV / 4 .. in 8-column pieces
+  // (a piece of a tiled16 row is 16 contiguous bytes)
+  const int dch = tid >> 2, dq4 = tid & 3, npc = static_cast<int>(DV / 32);
+  uint4 us0[4], udn[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    if (u < npc) {
+      const int col = dq4 * (npc * 8) + 8 * u;
+      const int64_t o = tiled16(dch, col, DV);
+      us0[u] = *reinterpret_cast<const uint4*>(SR + o);
+      udn[u] = *reinterpret_cast<const uint4*>(GR + o);
+    }
+  }
   lds_barrier();
-  chl_prefix(a, rr, left, sG, fGn, sFlag, tid);
+  chl_prefix(la_raw, sG, fGn, qtot, sFlag, tid);
   lds_barrier();
-  if (*sFlag != 0) return;  // (uniform) the token kernel takes this chunk
+  const bool flagged = *sFlag != 0;
+  if (tid == 0) a.cflag[cix] = flagged ? 1 : 0;
+  if (flagged) return;  // (uniform) the token kernel takes this chunk
+  {
+    float dot = 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (u < npc) {
+        float x[8], y[8];
+        load8f(reinterpret_cast<const bf16_t*>(&us0[u]), x);
+        load8f(reinterpret_cast<const bf16_t*>(&udn[u]), y);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dot += x[e] * y[e];
+      }
+    }
+    dot += __shfl_xor(dot, 1);
+    dot += __shfl_xor(dot, 2);
+    if (dq4 == 0) atomicAdd(&fdGn[dch], fGn[dch] * dot);  // e^{G_n} <S_0, dS_n> per channel
+  }
 
   // ---- split operands: 4 consecutive channels of one token per item ----
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int item = tid + NT * j, t = item >> 5, i0 = (item & 31) * 4;
     float q4[4], k4[4], c4[4], gt[4], gp[4];
-    chl_unpack4(chl_load8(rq, t * hqk + i0 * 2), q4);
-    chl_unpack4(chl_load8(rk, t * hqk + i0 * 2), k4);
+    chl_unpack4(uq[j], q4);
+    chl_unpack4(uk[j], k4);
     if (a.b_kind == kChannel) {
-      chl_unpack4(chl_load8(rbc, t * hdk + i0 * 2), c4);
+      chl_unpack4(ub[j], c4);
     } else {
-      const float bs = a.b_kind == kScalar ? bf16_to_f32(buf_load_u16(rbs, t * h1)) : 0.f;
+      const float bs = bf16_to_f32(static_cast<uint16_t>(ub[j].x));
       c4[0] = c4[1] = c4[2] = c4[3] = bs;
     }
     const float4 g4 = *reinterpret_cast<const float4*>(sG + t * 128 + i0);
@@ -232,6 +302,32 @@ __global__ __launch_bounds__(512) void bwd_chl_kernel(BwdArgs a) {
     if (TWO) *reinterpret_cast<uint2*>(sP + t * LDT + i0) = chl_pack4(op);
   }
   lds_barrier();
+
+  // the first half's v, w and dO rows and its B operands of dS_n and S_0, ahead of their use
+  const int pta = wave >> 1, pcv0 = 2 * (wave & 1);
+  const int st_t = tid >> 3, st_x0 = (tid & 7) * 8;
+  uint4 uv, udo, uw = make_uint4(0, 0, 0, 0);
+  uint16_t uws = 0;
+  auto load_rows = [&](int c0) {
+    const uint32_t off = st_t * hdv + (c0 + st_x0) * 2;
+    uv = buf_load16(rv, off);
+    udo = buf_load16(rdo, off);
+    if (a.w_kind == kChannel)
+      uw = buf_load16(rwc, off);
+    else if (a.w_kind == kScalar)
+      uws = buf_load_u16(rws, st_t * h1);
+  };
+  F8 dsf[2][4], s0c[2][4];
+  auto load_frags = [&](int c0) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        dsf[u][kb] = tiled_row_frag(GT, DK, c0 + 16 * (pcv0 + u) + l16, 32 * kb, g);
+        s0c[u][kb] = tiled_row_frag(ST, DK, c0 + 16 * (pcv0 + u) + l16, 32 * kb, g);
+      }
+  };
+  load_rows(0);
 
   // ---- Gram products: family 0 = L_P (to the inverse's pieces; decay first also to sLK as L),
   // 1 = L_K, 2 = M_QK, 3 = M_QP (decay first: families 0 and 2 only) ----
@@ -309,50 +405,43 @@ __global__ __launch_bounds__(512) void bwd_chl_kernel(BwdArgs a) {
   f32x4 aq[4], ak[4], ac[4], ap[4];
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi) aq[mi] = ak[mi] = ac[mi] = ap[mi] = zero4();
-  // [token x value] tiles of the per-half products: token tile pta, value tiles pcv0, pcv0 + 1
-  const int pta = wave >> 1, pcv0 = 2 * (wave & 1);
+  // ([token x value] tiles of the per-half products: token tile pta, value tiles pcv0, pcv0 + 1)
 
   const int nh = static_cast<int>(DV / DVH);
   for (int h = 0; h < nh; ++h) {
     const int c0 = DVH * h;
-    // ---- X = w . v and dO of this half ----
+    // ---- the half's v, w and dO rows (loaded a phase or a half ahead) into X and dO; dS_n (for
+    // dSh) and S_0 (for B') as B operands [k = channel][n = value column] of this wave's two value
+    // tiles ----
+    load_frags(c0);
     {
-      const int t = tid >> 3, x0 = (tid & 7) * 8;
-      const uint32_t off = t * hdv + (c0 + x0) * 2;
       float xf[8], wf[8];
-      const uint4 uv = buf_load16(rv, off);
       load8f(reinterpret_cast<const bf16_t*>(&uv), xf);
       if (a.w_kind == kChannel) {
-        const uint4 uw = buf_load16(rwc, off);
         load8f(reinterpret_cast<const bf16_t*>(&uw), wf);
       } else {
-        const float ws = a.w_kind == kScalar ? bf16_to_f32(buf_load_u16(rws, t * h1)) : 1.f;
+        const float ws = a.w_kind == kScalar ? bf16_to_f32(uws) : 1.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) wf[e] = ws;
       }
       bf16x8 xb;
 #pragma unroll
       for (int e = 0; e < 8; ++e) xb[e] = static_cast<__bf16>(xf[e] * wf[e]);
-      *reinterpret_cast<bf16x8*>(sX + t * LDX + x0) = xb;
-      *reinterpret_cast<uint4*>(sO + t * LDX + x0) = buf_load16(rdo, off);
+      *reinterpret_cast<bf16x8*>(sX + st_t * LDX + st_x0) = xb;
+      *reinterpret_cast<uint4*>(sO + st_t * LDX + st_x0) = udo;
+    }
+    // dSh = e^{G_n} . dS_n
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const float4 e0 = *reinterpret_cast<const float4*>(fGn + 32 * kb + 4 * g);
+      const float4 e1 = *reinterpret_cast<const float4*>(fGn + 32 * kb + 16 + 4 * g);
+      const float ee[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dsf[u][kb][e] = static_cast<__bf16>(static_cast<float>(dsf[u][kb][e]) * ee[e]);
     }
     lds_barrier();
-    // dSh = e^{G_n} . dS_n as B operands [k = channel][n = value column] for this wave's two
-    // value tiles (kept for dR and dX)
-    F8 dsf[2][4];
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const F8 f = tiled_row_frag(GT, DK, c0 + 16 * (pcv0 + u) + l16, 32 * kb, g);
-        const float4 e0 = *reinterpret_cast<const float4*>(fGn + 32 * kb + 4 * g);
-        const float4 e1 = *reinterpret_cast<const float4*>(fGn + 32 * kb + 16 + 4 * g);
-        const float ee[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
-        F8 o;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = static_cast<__bf16>(static_cast<float>(f[e]) * ee[e]);
-        dsf[u][kb] = o;
-      }
     // ---- B' = Ch S_0 + L_K X, into W ----
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -360,8 +449,7 @@ __global__ __launch_bounds__(512) void bwd_chl_kernel(BwdArgs a) {
       f32x4 acc = zero4();
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
-        acc = MM::mma8(lds_pair_frag_k<DK>(sC + (16 * pta + l16) * LDT, 32 * kb, g),
-                       tiled_row_frag(ST, DK, c0 + 16 * cv + l16, 32 * kb, g), acc);
+        acc = MM::mma8(lds_pair_frag_k<DK>(sC + (16 * pta + l16) * LDT, 32 * kb, g), s0c[u][kb], acc);
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
         if (ks <= (pta >> 1))
@@ -420,6 +508,17 @@ __global__ __launch_bounds__(512) void bwd_chl_kernel(BwdArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         sW[(16 * pta + 4 * g + i) * LDX + 16 * (pcv0 + u) + l16] = static_cast<__bf16>(dvt[u][i]);
+    // (v and w at this wave's output positions, for dv and dw below)
+    uint16_t ov[2][4], ow[2][4];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 16 * pta + 4 * g + i;
+        const uint32_t off = t * hdv + (c0 + 16 * (pcv0 + u) + l16) * 2;
+        ov[u][i] = buf_load_u16(rv, off);
+        ow[u][i] = a.w_kind == kChannel ? buf_load_u16(rwc, off) : a.w_kind == kScalar ? buf_load_u16(rws, t * h1) : 0;
+      }
     lds_barrier();
     // ---- dX = M_QK^T dO + Kh dSh + L_K^T dV: dv = w . dX, dw = v . dX ----
     {
@@ -445,12 +544,8 @@ __global__ __launch_bounds__(512) void bwd_chl_kernel(BwdArgs a) {
         for (int i = 0; i < 4; ++i) {
           const int t = 16 * pta + 4 * g + i;
           const uint32_t off = t * hdv + col * 2;
-          const float vv = bf16_to_f32(buf_load_u16(rv, off));
-          float ww = 1.f;
-          if (a.w_kind == kChannel)
-            ww = bf16_to_f32(buf_load_u16(rwc, off));
-          else if (a.w_kind == kScalar)
-            ww = bf16_to_f32(buf_load_u16(rws, t * h1));
+          const float vv = bf16_to_f32(ov[u][i]);
+          const float ww = a.w_kind == kNone ? 1.f : bf16_to_f32(ow[u][i]);
           buf_store1((bf16_t*)nullptr, sv_, off, acc[i] * ww);
           if (a.w_kind == kChannel) buf_store1((bf16_t*)nullptr, swc, off, acc[i] * vv);
           if (a.w_kind == kScalar) {
@@ -460,36 +555,18 @@ __global__ __launch_bounds__(512) void bwd_chl_kernel(BwdArgs a) {
         }
       }
     }
-    // ---- sum_j dSh . Sh for channel tile m = wave, Sh = S_0 + Kh^T X - Ph^T R ----
-    {
-      const int m = wave;
-      float part[4] = {0.f, 0.f, 0.f, 0.f};
+    if (h + 1 < nh) load_rows(c0 + DVH);  // the next half's rows
+    // ---- operand gradients: dO S_0^T, X dSh^T, dV S_0^T, -R dSh^T; their B operands
+    // [k = value column][n = channel] from the checkpoint rows ----
+    F8 s0r[4][2], gnr[4][2];
 #pragma unroll
-      for (int cv = 0; cv < 4; ++cv) {
-        const int col = c0 + 16 * cv + l16;
-        f32x4 acc, acc2 = zero4();
+    for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] = static_cast<float>(SR[tiled16(16 * m + 4 * g + i, col, DV)]);
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const F8 xf = lds_col_frag(sX, LDX, 16 * cv + l16, 32 * ks, g, l16);
-          const F8 rf = lds_col_frag(sR, LDX, 16 * cv + l16, 32 * ks, g, l16);
-          acc = MM::mma8(lds_col_frag(sK, LDT, 16 * m + l16, 32 * ks, g, l16), xf, acc);
-          acc2 = MM::mma8(lds_col_frag(sP, LDT, 16 * m + l16, 32 * ks, g, l16), rf, acc2);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = 16 * m + 4 * g + i;
-          const float ds = static_cast<float>(GR[tiled16(row, col, DV)]) * fGn[row];
-          part[i] += (acc[i] - acc2[i]) * ds;
-        }
+      for (int kv = 0; kv < 2; ++kv) {
+        const int ch = 16 * (om0 + mi) + l16;
+        s0r[mi][kv] = tiled_row_frag(SR, static_cast<int>(DV), ch, c0 + 32 * kv, g);
+        gnr[mi][kv] = tiled_row_frag(GR, static_cast<int>(DV), ch, c0 + 32 * kv, g);
       }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float x = row_sum16(part[i]);
-        if (l16 == 0) atomicAdd(&fdGn[16 * m + 4 * g + i], x);
-      }
-    }
     // ---- Gram gradients: dO X^T, -dO R^T, dV X^T, -dV R^T over this half's columns ----
 #pragma unroll
     for (int u = 0; u < NGJ; ++u) {
@@ -515,7 +592,6 @@ __global__ __launch_bounds__(512) void bwd_chl_kernel(BwdArgs a) {
         }
       }
     }
-    // ---- operand gradients: dO S_0^T, X dSh^T, dV S_0^T, -R dSh^T ----
 #pragma unroll
     for (int kv = 0; kv < 2; ++kv) {
       const F8 of = lds_pair_frag_k<DVH>(sO + (16 * ota + l16) * LDX, 32 * kv, g);
@@ -524,16 +600,13 @@ __global__ __launch_bounds__(512) void bwd_chl_kernel(BwdArgs a) {
       const F8 rf = chl_neg8(lds_pair_frag_k<DVH>(sR + (16 * ota + l16) * LDX, 32 * kv, g));
 #pragma unroll
       for (int mi = 0; mi < 4; ++mi) {
-        const int ch = 16 * (om0 + mi) + l16;
-        const F8 s0 = tiled_row_frag(SR, static_cast<int>(DV), ch, c0 + 32 * kv, g);
-        const F8 gr = tiled_row_frag(GR, static_cast<int>(DV), ch, c0 + 32 * kv, g);
-        const float en = fGn[ch];
+        const float en = fGn[16 * (om0 + mi) + l16];
         F8 ds;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) ds[e] = static_cast<__bf16>(static_cast<float>(gr[e]) * en);
-        aq[mi] = MM::mma8(of, s0, aq[mi]);
+        for (int e = 0; e < 8; ++e) ds[e] = static_cast<__bf16>(static_cast<float>(gnr[mi][kv][e]) * en);
+        aq[mi] = MM::mma8(of, s0r[mi][kv], aq[mi]);
         ak[mi] = MM::mma8(xf, ds, ak[mi]);
-        ac[mi] = MM::mma8(vf, s0, ac[mi]);
+        ac[mi] = MM::mma8(vf, s0r[mi][kv], ac[mi]);
         if (TWO)
           ap[mi] = MM::mma8(rf, ds, ap[mi]);
         else
@@ -542,6 +615,37 @@ __global__ __launch_bounds__(512) void bwd_chl_kernel(BwdArgs a) {
     }
     lds_barrier();  // the next half overwrites X, dO, R and W
   }
+
+  // ---- the rest of sum_j dSh . Sh per channel: with Sh = S_0 + Kh^T X - Ph^T R it is
+  // sum_t Kh[t] . (X dSh^T)[t] + Ph[t] . (-R dSh^T)[t], the accumulators of dKh and dPh so far ----
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi) {
+    const int ch = 16 * (om0 + mi) + l16;
+    float x = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 16 * ota + 4 * g + i;
+      x += static_cast<float>(sK[t * LDT + ch]) * ak[mi][i];
+      if (TWO) x += static_cast<float>(sP[t * LDT + ch]) * ap[mi][i];
+    }
+    x += __shfl_xor(x, 16);
+    x += __shfl_xor(x, 32);
+    if (g == 0) atomicAdd(&fdGn[ch], x);
+  }
+
+  // (q, k and b at this wave's accumulator positions, and log alpha again, for the outputs below)
+  uint16_t eq[4][4], ek[4][4], eb[4][4];
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 16 * ota + 4 * g + i, ch = 16 * (om0 + mi) + l16;
+      eq[mi][i] = buf_load_u16(rq, t * hqk + ch * 2);
+      ek[mi][i] = buf_load_u16(rk, t * hqk + ch * 2);
+      eb[mi][i] = a.b_kind == kChannel ? buf_load_u16(rbc, t * hdk + ch * 2)
+                                       : a.b_kind == kScalar ? buf_load_u16(rbs, t * h1) : 0;
+    }
+  const ChlRaw la_raw2 = chl_prefix_load(a, rr, left, tid);
 
   // ---- the Gram gradients (masked, bf16) over the half area: dM_QK, dM_QP, dL_K, dL_P (decay
   // first: dM, dL); their upper tiles read as zeros ----
@@ -606,7 +710,7 @@ __global__ __launch_bounds__(512) void bwd_chl_kernel(BwdArgs a) {
   float* sG2 = reinterpret_cast<float*>(smem + L::oG2);
   float* sdG = reinterpret_cast<float*>(smem + L::oDG);
   float* sdGp = reinterpret_cast<float*>(smem + L::oDGP);
-  chl_prefix(a, rr, left, sG2, nullptr, sFlag, tid);  // (the same sums as above)
+  chl_prefix(la_raw2, sG2, nullptr, qtot, sFlag, tid);  // (the same sums as above)
   lds_barrier();
   {
     const auto sq_ = make_rsrc(a.dq + rr * DK, rng_k);
@@ -620,13 +724,9 @@ __global__ __launch_bounds__(512) void bwd_chl_kernel(BwdArgs a) {
       for (int i = 0; i < 4; ++i) {
         const int t = 16 * ota + 4 * g + i;
         const float gt = sG2[t * 128 + ch], gp = t > 0 ? sG2[(t - 1) * 128 + ch] : 0.f;
-        const uint32_t offq = t * hqk + ch * 2, offv = t * hdk + ch * 2;
-        const float qv = bf16_to_f32(buf_load_u16(rq, offq)), kv = bf16_to_f32(buf_load_u16(rk, offq));
-        float bv = 0.f;
-        if (a.b_kind == kChannel)
-          bv = bf16_to_f32(buf_load_u16(rbc, offv));
-        else if (a.b_kind == kScalar)
-          bv = bf16_to_f32(buf_load_u16(rbs, t * h1));
+        const uint32_t offv = t * hdk + ch * 2;
+        const float qv = bf16_to_f32(eq[mi][i]), kv = bf16_to_f32(ek[mi][i]);
+        const float bv = a.b_kind == kNone ? 0.f : bf16_to_f32(eb[mi][i]);
         const float et = __expf(gt), ept = __expf(-gt);
         const float dq = aq[mi][i] * et;
         const float dkk = ak[mi][i] * ept;
@@ -654,19 +754,31 @@ __global__ __launch_bounds__(512) void bwd_chl_kernel(BwdArgs a) {
     }
   }
   lds_barrier();
-  // ---- d log alpha_t = sum over s >= t of dG_s (one channel per thread); scalar db and dw ----
-  if (tid < 128) {
-    const auto sla = make_rsrc(a.dla + rr * DK, rng_k);
-    float x = fdGn[tid];
-    for (int t = C - 1; t >= 0; --t) {
-      x += sdG[t * 128 + tid];
-      if (TWO && t + 1 < C) x += sdGp[(t + 1) * 128 + tid];
-      buf_store1((bf16_t*)nullptr, sla, t * hdk + tid * 2, x);
+  // ---- d log alpha_t = sum over s >= t of dG_s: channel tid % 128, tokens 16 (tid / 128) ..,
+  // the later quarters' totals through qtot; scalar db and dw ----
+  {
+    const int ch = tid & 127, q = tid >> 7;
+    float d[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int t = 16 * q + u;
+      d[u] = sdG[t * 128 + ch];
+      if (TWO && t + 1 < C) d[u] += sdGp[(t + 1) * 128 + ch];
     }
-  } else if (tid < 192) {
-    const int t = tid - 128;
-    if (a.b_kind == kScalar) buf_store1((bf16_t*)nullptr, make_rsrc(a.db + rr, rng_1), t * h1, fdb[t]);
-    if (a.w_kind == kScalar) buf_store1((bf16_t*)nullptr, make_rsrc(a.dw + rr, rng_1), t * h1, fdw[t]);
+    if (q == 3) d[15] += fdGn[ch];  // the end-of-chunk decay e^{G_n}
+#pragma unroll
+    for (int u = 14; u >= 0; --u) d[u] += d[u + 1];
+    qtot[q * 128 + ch] = d[0];
+    lds_barrier();
+    float off = 0.f;
+    for (int j = q + 1; j < 4; ++j) off += qtot[j * 128 + ch];
+    const auto sla = make_rsrc(a.dla + rr * DK, rng_k);
+#pragma unroll
+    for (int u = 0; u < 16; ++u) buf_store1((bf16_t*)nullptr, sla, (16 * q + u) * hdk + ch * 2, d[u] + off);
+    if (tid < 64) {
+      if (a.b_kind == kScalar) buf_store1((bf16_t*)nullptr, make_rsrc(a.db + rr, rng_1), tid * h1, fdb[tid]);
+      if (a.w_kind == kScalar) buf_store1((bf16_t*)nullptr, make_rsrc(a.dw + rr, rng_1), tid * h1, fdw[tid]);
+    }
   }
 }
 
@@ -686,16 +798,14 @@ template <int MODE>
 __global__ __launch_bounds__(512) void bwd_chl_token_kernel(BwdArgs a) {
   constexpr bool TWO = MODE == 2;
   constexpr int C = 64, DK = 128;
-  // LDS: prefix sums (for the flag), then the staged q, k, b, log alpha rows (bf16 [64][128]);
-  // per-wave partial sums [2][8 waves][5][128] fp32
-  __shared__ __attribute__((aligned(16))) unsigned char smem[4 * C * DK * 2 + 2 * 8 * 5 * 128 * 4 + 16];
-  float* sG = reinterpret_cast<float*>(smem);
+  // LDS: the staged q, k, b, log alpha rows (bf16 [64][128]); per-wave partial sums
+  // [2][8 waves][5][128] fp32
+  __shared__ __attribute__((aligned(16))) unsigned char smem[4 * C * DK * 2 + 2 * 8 * 5 * 128 * 4];
   __bf16* tq = reinterpret_cast<__bf16*>(smem);
   __bf16* tk = tq + C * DK;
   __bf16* tb = tk + C * DK;
   __bf16* tl = tb + C * DK;
   float* part = reinterpret_cast<float*>(smem + 4 * C * DK * 2);
-  int* sFlag = reinterpret_cast<int*>(smem + 4 * C * DK * 2 + 2 * 8 * 5 * 128 * 4);
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int NW = static_cast<int>(a.DV / 16);
@@ -709,12 +819,7 @@ __global__ __launch_bounds__(512) void bwd_chl_token_kernel(BwdArgs a) {
   const uint32_t hdv = static_cast<uint32_t>(H * DV * 2), h1 = static_cast<uint32_t>(H * 2);
   const uint32_t rng_k = wy_range(left, H, DK), rng_v = wy_range(left, H, DV), rng_1 = wy_range(left, H, 1);
 
-  if (tid == 0) *sFlag = 0;
-  lds_barrier();
-  chl_prefix(a, rr, left, sG, nullptr, sFlag, tid);
-  lds_barrier();
-  if (*sFlag == 0) return;  // (uniform) bwd_chl_kernel takes this chunk
-  lds_barrier();            // every wave has read the flag before the staging overwrites it
+  if (a.cflag[cix] == 0) return;  // bwd_chl_kernel took this chunk
 
   // ---- stage q, k, b (per channel, or the scalar in column 0), log alpha ----
   {
