@@ -331,15 +331,20 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, unsigned char* smem, 
   const In inQ = in_of(a.q, Hk, hk, DK), inK = in_of(a.k, Hk, hk, DK), inV = in_of(a.v, H, hi, DV);
   const In inA = in_of(a.la, H, hi, AK == kChannel ? DK : 1), inB = in_of(a.bg, H, hi, BK == kChannel ? DK : 1);
   const In inW = in_of(a.wg, H, hi, WK == kChannel ? DV : 1);
-  auto stage = [&](int64_t c, int lane) {
+  // two: waves 0 and 1 issue every load (four row groups each), else each wave its own group
+  auto stage = [&](int64_t c, int lane, bool two) {
     const int64_t t0 = c * C;
-    // a per-channel array is 8 loads of 1 KB (rows 4 w .. 4 w + 3 for wave w)
+    // a per-channel array is 8 loads of 1 KB (row group j: rows 4 j .. 4 j + 3)
     auto rows = [&](const In& in, int dst) {
       const int64_t off = t0 * in.stride, left = in.end - off;
       const uint32_t bytes = static_cast<uint32_t>(left < 0x7fffffff ? left : 0x7fffffff);
-      const int t = 4 * wave + (lane >> 4), slot = lane & 15;
-      const int piece = (slot ^ t) & 15;
-      seg_dma16(in.p + off, bytes, smem + dst + 1024 * wave, static_cast<uint32_t>(t) * in.stride + piece * 16);
+      const int slot = lane & 15;
+      for (int u = 0; u < (two ? 4 : 1); ++u) {
+        const int j = two ? 4 * wave + u : wave;
+        const int t = 4 * j + (lane >> 4);
+        const int piece = (slot ^ t) & 15;
+        seg_dma16(in.p + off, bytes, smem + dst + 1024 * j, static_cast<uint32_t>(t) * in.stride + piece * 16);
+      }
     };
     // a scalar gate: one bf16 per token into a register of wave 0's lane t (written to LDS once
     // the wave has waited for its loads)
@@ -477,8 +482,10 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, unsigned char* smem, 
 
   // ---- Gram tiles of operand buffer par into Gram buffer par: 6 jobs = 2 row operands x 3 lower
   // tile pairs (waves 2-7) ----
+  // Waves 2-7 take one tile pair each (job = wave - 2: row operand Cs or Qs, lower tile pair
+  // (ta, tb)); waves 0 and 1 form the diagonal tiles of L_P / L again and invert them, which the
+  // jobs with ta = tb then leave out.
   auto gram = [&](int par, int lane) {
-    if (wave < 2) return;
     const int g = lane >> 4, l16 = lane & 15;
     const __bf16* tQ = reinterpret_cast<const __bf16*>(pbuf(par) + L::pQ);
     const __bf16* tC = reinterpret_cast<const __bf16*>(pbuf(par) + L::pC);
@@ -489,8 +496,11 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, unsigned char* smem, 
     __bf16* gLK = reinterpret_cast<__bf16*>(gbuf(par) + L::gLK);
     __bf16* gMQK = reinterpret_cast<__bf16*>(gbuf(par) + L::gMQK);
     float* Ld = reinterpret_cast<float*>(gbuf(par) + L::gLD);
-    const int job = wave - 2, grp = job / 3, tix = job % 3;
-    const int ta = tix >= 1 ? 1 : 0, tb = tix == 2 ? 1 : 0;
+    const bool diag = wave < 2;
+    const int job = diag ? 0 : wave - 2, grp = diag ? 0 : job / 3, tix = job % 3;
+    const int ta = diag ? wave : tix >= 1 ? 1 : 0, tb = diag ? wave : tix == 2 ? 1 : 0;
+    const bool need2 = TWO && !diag;
+    if (!diag && grp == 0 && ta == tb && !TWO) return;  // (decay first: only L_P, formed by wave ta)
     const __bf16* ar = (grp == 0 ? tC : tQ) + (16 * ta + l16) * LDT;
     const __bf16* br = ((TWO && grp == 0) ? tP : tK) + (16 * tb + l16) * LDT;
     const __bf16* cr = (grp == 0 ? tK : tP) + (16 * tb + l16) * LDT;
@@ -499,13 +509,13 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, unsigned char* smem, 
     for (int kb = 0; kb < DK / 32; ++kb) {
       fa[kb] = lds_load8(ar + 32 * kb + 8 * g);
       fb[kb] = lds_load8(br + 32 * kb + 8 * g);
-      if (TWO) fc[kb] = lds_load8(cr + 32 * kb + 8 * g);
+      if (need2) fc[kb] = lds_load8(cr + 32 * kb + 8 * g);
     }
     f32x4 acc1 = zero4(), acc2 = zero4();
 #pragma unroll
     for (int kb = 0; kb < DK / 32; ++kb) {
       acc1 = MM::mma8(fa[kb], fb[kb], acc1);
-      if (TWO) acc2 = MM::mma8(fa[kb], fc[kb], acc2);
+      if (need2) acc2 = MM::mma8(fa[kb], fc[kb], acc2);
     }
     // which: 0 = -L_P / -L (strict; the off-diagonal block transposed -> gA, the diagonal
     // blocks -> Ld negated back), 1 = -M_QP / -M, 2 = L_K (strict), 3 = M_QK (inclusive).  The
@@ -538,15 +548,17 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, unsigned char* smem, 
           gMQK[r * LDD + cc] = static_cast<__bf16>(val);
       }
     };
-    if (TWO) {
-      store_tile(grp == 0 ? 0 : 3, acc1);
+    if (diag) {
+      store_tile(0, acc1);
+    } else if (TWO) {
+      if (grp != 0 || ta != tb) store_tile(grp == 0 ? 0 : 3, acc1);
       store_tile(grp == 0 ? 2 : 1, acc2);
     } else {
       store_tile(grp == 0 ? 0 : 1, acc1);
     }
     // a diagonal block of L_P / L: its inverse D by seg_inv_sweep, from the rows this wave just
     // wrote (the wave's own LDS writes precede its reads), over the same area
-    if (grp == 0 && ta == tb) {
+    if (diag) {
       float* Lb = Ld + ta * 16 * LDL;
       float nl[16], d[4];
 #pragma unroll
@@ -801,14 +813,14 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, unsigned char* smem, 
   bool flag_cur = false;  // (uniform) chunk c is flagged
   if (c_begin < c_end) {
     const int lane = opaque_v(tid) & 63;
-    stage(c_begin, lane);
+    stage(c_begin, lane, false);
     arrive(lane);
     lds_barrier_keep_vm();
     split(0, lane);
     lds_barrier_keep_vm();
     flag_cur = flagged_now();
     if (!flag_cur) {
-      if (c_begin + 1 < c_end) stage(c_begin + 1, lane);
+      if (c_begin + 1 < c_end) stage(c_begin + 1, lane, false);
       gram(0, lane);
     }
     lds_barrier_keep_vm();
@@ -826,14 +838,14 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, unsigned char* smem, 
       token(c, lane);
       lds_barrier_keep_vm();
       if (has_next) {  // refill: chunk c + 1 from its loads to its Gram products
-        stage(c + 1, lane);
+        stage(c + 1, lane, false);
         arrive(lane);
         lds_barrier_keep_vm();
         split(par ^ 1, lane);
         lds_barrier_keep_vm();
         flag_next = flagged_now();
         if (!flag_next) {
-          if (c + 2 < c_end) stage(c + 2, lane);
+          if (c + 2 < c_end) stage(c + 2, lane, false);
           gram(par ^ 1, lane);
         }
         lds_barrier_keep_vm();
@@ -849,9 +861,12 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, unsigned char* smem, 
     chain1(c, par, lane, rfN, rfP, xf);
     lds_barrier_keep_vm();  // A1: chunk c + 1's operands are in their buffer, its flags known
     if (has_next) flag_next = flagged_now();
-    if (has_next && !flag_next && c + 2 < c_end) stage(c + 2, lane);
     chain2(par, lane, rfN, rfP, xf);
-    if (has_next && !flag_next) gram(par ^ 1, lane);
+    if (has_next && !flag_next) {
+      // waves 0 and 1 issue the loads of chunk c + 2 (the others go on to the Gram products)
+      if (wave < 2 && c + 2 < c_end) stage(c + 2, lane, true);
+      gram(par ^ 1, lane);
+    }
     lds_barrier_keep_vm();  // A2
     flag_cur = flag_next;
   }
