@@ -318,14 +318,17 @@ __global__ __launch_bounds__(512) void bwd_chl_kernel(BwdArgs a) {
       uws = buf_load_u16(rws, st_t * h1);
   };
   F8 dsf[2][4], s0c[2][4];
-  auto load_frags = [&](int c0) {
+  auto load_s0c = [&](int c0) {
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        dsf[u][kb] = tiled_row_frag(GT, DK, c0 + 16 * (pcv0 + u) + l16, 32 * kb, g);
-        s0c[u][kb] = tiled_row_frag(ST, DK, c0 + 16 * (pcv0 + u) + l16, 32 * kb, g);
-      }
+      for (int kb = 0; kb < 4; ++kb) s0c[u][kb] = tiled_row_frag(ST, DK, c0 + 16 * (pcv0 + u) + l16, 32 * kb, g);
+  };
+  auto load_dsf = [&](int c0) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) dsf[u][kb] = tiled_row_frag(GT, DK, c0 + 16 * (pcv0 + u) + l16, 32 * kb, g);
   };
   load_rows(0);
 
@@ -413,7 +416,7 @@ __global__ __launch_bounds__(512) void bwd_chl_kernel(BwdArgs a) {
     // ---- the half's v, w and dO rows (loaded a phase or a half ahead) into X and dO; dS_n (for
     // dSh) and S_0 (for B') as B operands [k = channel][n = value column] of this wave's two value
     // tiles ----
-    load_frags(c0);
+    load_s0c(c0);
     {
       float xf[8], wf[8];
       load8f(reinterpret_cast<const bf16_t*>(&uv), xf);
@@ -429,17 +432,6 @@ __global__ __launch_bounds__(512) void bwd_chl_kernel(BwdArgs a) {
       for (int e = 0; e < 8; ++e) xb[e] = static_cast<__bf16>(xf[e] * wf[e]);
       *reinterpret_cast<bf16x8*>(sX + st_t * LDX + st_x0) = xb;
       *reinterpret_cast<uint4*>(sO + st_t * LDX + st_x0) = udo;
-    }
-    // dSh = e^{G_n} . dS_n
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const float4 e0 = *reinterpret_cast<const float4*>(fGn + 32 * kb + 4 * g);
-      const float4 e1 = *reinterpret_cast<const float4*>(fGn + 32 * kb + 16 + 4 * g);
-      const float ee[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) dsf[u][kb][e] = static_cast<__bf16>(static_cast<float>(dsf[u][kb][e]) * ee[e]);
     }
     lds_barrier();
     // ---- B' = Ch S_0 + L_K X, into W ----
@@ -473,6 +465,18 @@ __global__ __launch_bounds__(512) void bwd_chl_kernel(BwdArgs a) {
       for (int i = 0; i < 4; ++i) sR[(16 * pta + 4 * g + i) * LDX + 16 * cv + l16] = static_cast<__bf16>(acc[i]);
     }
     lds_barrier();
+    load_dsf(c0);
+    // dSh = e^{G_n} . dS_n
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const float4 e0 = *reinterpret_cast<const float4*>(fGn + 32 * kb + 4 * g);
+      const float4 e1 = *reinterpret_cast<const float4*>(fGn + 32 * kb + 16 + 4 * g);
+      const float ee[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dsf[u][kb][e] = static_cast<__bf16>(static_cast<float>(dsf[u][kb][e]) * ee[e]);
+    }
     // ---- dR = -(M_QP^T dO + Ph dSh), into W ----
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -560,13 +564,11 @@ __global__ __launch_bounds__(512) void bwd_chl_kernel(BwdArgs a) {
     // [k = value column][n = channel] from the checkpoint rows ----
     F8 s0r[4][2], gnr[4][2];
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-      for (int kv = 0; kv < 2; ++kv) {
-        const int ch = 16 * (om0 + mi) + l16;
-        s0r[mi][kv] = tiled_row_frag(SR, static_cast<int>(DV), ch, c0 + 32 * kv, g);
-        gnr[mi][kv] = tiled_row_frag(GR, static_cast<int>(DV), ch, c0 + 32 * kv, g);
-      }
+    for (int mi = 0; mi < 4; ++mi) {
+      const int ch = 16 * (om0 + mi) + l16;
+      s0r[mi][0] = tiled_row_frag(SR, static_cast<int>(DV), ch, c0, g);
+      gnr[mi][0] = tiled_row_frag(GR, static_cast<int>(DV), ch, c0, g);
+    }
     // ---- Gram gradients: dO X^T, -dO R^T, dV X^T, -dV R^T over this half's columns ----
 #pragma unroll
     for (int u = 0; u < NGJ; ++u) {
@@ -594,6 +596,14 @@ __global__ __launch_bounds__(512) void bwd_chl_kernel(BwdArgs a) {
     }
 #pragma unroll
     for (int kv = 0; kv < 2; ++kv) {
+      if (kv == 1) {
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) {
+          const int ch = 16 * (om0 + mi) + l16;
+          s0r[mi][1] = tiled_row_frag(SR, static_cast<int>(DV), ch, c0 + 32, g);
+          gnr[mi][1] = tiled_row_frag(GR, static_cast<int>(DV), ch, c0 + 32, g);
+        }
+      }
       const F8 of = lds_pair_frag_k<DVH>(sO + (16 * ota + l16) * LDX, 32 * kv, g);
       const F8 xf = lds_pair_frag_k<DVH>(sX + (16 * ota + l16) * LDX, 32 * kv, g);
       const F8 vf = lds_pair_frag_k<DVH>(sW + (16 * ota + l16) * LDX, 32 * kv, g);
