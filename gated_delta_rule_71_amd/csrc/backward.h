@@ -416,7 +416,11 @@ struct BwdLocalLayout {
   static constexpr int oI = oA + 48 * LDA * 2;      // inverses of the diagonal blocks
   static constexpr int oLD = oI + C * LDI * 2;      // fp32 diagonal blocks of L, column-major
   static constexpr int oF = oLD + C * LDL * 4;      // fp32 g, gamma, dg, b (scalar), dw and db sums
-  static constexpr int total = oF + 6 * C * 4;
+  // per-wave partial sums of d g and of a scalar db [8][C] each, and a scalar dw's per-item terms
+  // [C][16], added in a fixed order at the end (no float atomics: a call's bits do not depend on
+  // the order in which waves finish)
+  static constexpr int oP = oF + 6 * C * 4;
+  static constexpr int total = oP + (2 * 8 * C + 16 * C) * 4;
   static constexpr bool fits = total <= kLdsLimit;
 };
 
@@ -448,6 +452,9 @@ __global__ __launch_bounds__(512) void bwd_local_kernel(BwdArgs a) {
   float* fdg = fg + 2 * C;                              // d g_t
   float* fb = fg + 3 * C;                               // scalar b_t
   float* fdw = fg + 4 * C;                              // row sums of dw (scalar w), then of db
+  float* pdg = reinterpret_cast<float*>(smem + L::oP);  // [wave][C] partial d g
+  float* pdb = pdg + 8 * C;                             // [wave][C] partial scalar db
+  float* pdw = pdb + 8 * C;                             // [t][item] partial scalar dw
 
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -580,6 +587,7 @@ __global__ __launch_bounds__(512) void bwd_local_kernel(BwdArgs a) {
     *reinterpret_cast<bf16x8*>(sDU + t * LDX + x0) = zero8;
   }
   for (int i = tid; i < C * LDD / 8; i += NT) reinterpret_cast<uint4*>(sM)[i] = make_uint4(0, 0, 0, 0);
+  for (int i = tid; i < 2 * 8 * C; i += NT) pdg[i] = 0.f;  // (pdg and pdb)
   if (wave == 0) {
     // inclusive prefix sum of log alpha over the chunk (lane = token)
     float x = a.alpha_kind == kScalar ? bf16_to_f32(buf_load_u16(rla, lane * h1)) : 0.f;
@@ -719,18 +727,19 @@ __global__ __launch_bounds__(512) void bwd_local_kernel(BwdArgs a) {
 
   // row sums (over the 16 lanes of a group) and column sums (over the 4 groups and the 4
   // accumulator rows) of a 16 x 16 tile, added to fdg: + rows of tile row ta, - columns of tb
+  // (each into this wave's own partial row, in program order)
   auto dg_rows = [&](int ta, f32x4 r) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float x = row_sum16(r[i]);
-      if (l16 == 0) atomicAdd(&fdg[16 * ta + 4 * g + i], x);
+      if (l16 == 0) pdg[wave * C + 16 * ta + 4 * g + i] += x;
     }
   };
   auto dg_cols = [&](int tb, const f32x4& r) {
     float x = r[0] + r[1] + r[2] + r[3];
     x += __shfl_xor(x, 16);
     x += __shfl_xor(x, 32);
-    if (g == 0) atomicAdd(&fdg[16 * tb + l16], -x);
+    if (g == 0) pdg[wave * C + 16 * tb + l16] -= x;
   };
   // ---- dM = tril(dO U^T) and dL = -strict_tril(dV U^T); their products with M and L go to dg,
   // dM . Gamma replaces M and dL . Gamma replaces T ----
@@ -857,7 +866,7 @@ __global__ __launch_bounds__(512) void bwd_local_kernel(BwdArgs a) {
           x += __shfl_xor(x, 2);
           x += __shfl_xor(x, 4);
           x += __shfl_xor(x, 8);
-          if (l16 == 0) atomicAdd(&fdw[C + 16 * ta + 4 * g + i], x);
+          if (l16 == 0) pdb[wave * C + 16 * ta + 4 * g + i] += x;
         }
       }
     }
@@ -870,7 +879,7 @@ __global__ __launch_bounds__(512) void bwd_local_kernel(BwdArgs a) {
   sdot += __shfl_xor(sdot, 8);
   sdot += __shfl_xor(sdot, 16);
   sdot += __shfl_xor(sdot, 32);
-  if (lane == 0) atomicAdd(&fdg[C - 1], sdot);
+  if (lane == 0) pdg[wave * C + C - 1] += sdot;
   // ---- dv = w . dV and dw = v . dV ----
   const auto sv_ = make_rsrc(a.dv + rr * DV + c0, rng_v);
   const auto swc = make_rsrc(a.w_kind == kChannel ? a.dw + rr * DV + c0 : a.dv, a.w_kind == kChannel ? rng_v : 0u);
@@ -899,14 +908,22 @@ __global__ __launch_bounds__(512) void bwd_local_kernel(BwdArgs a) {
     }
     buf_store16(sv_, off, __builtin_bit_cast(uint4, ov));
     if (a.w_kind == kChannel) buf_store16(swc, off, __builtin_bit_cast(uint4, ow));
-    if (a.w_kind == kScalar) atomicAdd(&fdw[t], wsum);
+    if (a.w_kind == kScalar) pdw[t * 16 + item % (DVh / 8)] = wsum;
   }
   lds_barrier();
   // ---- per-token outputs: d log alpha (suffix sums of dg in the chunk), scalar db and dw ----
   if (wave == 0) {
     const uint32_t off = lane * h1;
+    float dgs = 0.f, dbs = 0.f, dws = 0.f;  // the partial sums in a fixed order
+    for (int w = 0; w < NW; ++w) {
+      dgs += pdg[w * C + lane];
+      dbs += pdb[w * C + lane];
+    }
+    for (int j = 0; j < DVh / 8; ++j) dws += pdw[lane * 16 + j];
+    fdw[lane] = dws;
+    fdw[C + lane] = dbs;
     if (a.alpha_kind == kScalar) {
-      float x = fdg[lane];
+      float x = dgs;
 #pragma unroll
       for (int d = 1; d < 64; d <<= 1) {
         const float y = __shfl_down(x, d);

@@ -127,11 +127,14 @@ struct ChlLayout {
   static constexpr int oT = (TWO ? oMQP : oMQK) + GRAM;
   // one value half: X, dO, R, and W (B' = Ch S_0 + L_K X, then dR, then dV)
   static constexpr int oX = oT + GRAM, oO = oX + HALF, oR = oO + HALF, oW = oR + HALF;
-  // fp32: e^{G_n} [128], sum_j dSh . Sh [128], scalar db [64], scalar dw [64], the flag; the
-  // partial sums of the prefix and suffix scans [4][128]
+  // fp32: e^{G_n} [128], (unused) [128], scalar db [64], (unused) [64], the flag; the partial
+  // sums of the prefix and suffix scans [4][128]
   static constexpr int oF = oW + HALF;
   static constexpr int oQT = oF + (128 + 128 + 64 + 64 + 4) * 4;
-  static constexpr int total = oQT + 4 * 128 * 4;
+  // fixed-order partial sums (no float atomics, so a call's bits do not depend on timing): the
+  // per-channel end-of-chunk terms [5][128] and a scalar dw's per-token terms [2][2][2][64]
+  static constexpr int oPS = oQT + 4 * 128 * 4;
+  static constexpr int total = oPS + (5 * 128 + 8 * 64) * 4;
   // aliases: the prefix sums (fp32 [64][128]) over the half area in the prologue, the pieces of
   // the triangular inverse there too; after the products, G (again) and the per-token gate
   // gradients over the operand area, and (erase first) the gradients of G_{t-1} over the half area
@@ -173,11 +176,11 @@ __global__ __launch_bounds__(512) void bwd_chl_kernel(BwdArgs a) {
   __bf16* sR = reinterpret_cast<__bf16*>(smem + L::oR);
   __bf16* sW = reinterpret_cast<__bf16*>(smem + L::oW);
   float* fGn = reinterpret_cast<float*>(smem + L::oF);
-  float* fdGn = fGn + 128;
   float* fdb = fGn + 256;
-  float* fdw = fGn + 320;
   int* sFlag = reinterpret_cast<int*>(fGn + 384);
   float* qtot = reinterpret_cast<float*>(smem + L::oQT);
+  float* pGn = reinterpret_cast<float*>(smem + L::oPS);  // [5][128]
+  float* pw = pGn + 5 * 128;                             // [half][wave & 1][u][64]
   float* sG = reinterpret_cast<float*>(smem + L::oG);
   __bf16* gA = reinterpret_cast<__bf16*>(smem + L::oGA);
   float* Ld = reinterpret_cast<float*>(smem + L::oLD);
@@ -212,12 +215,8 @@ __global__ __launch_bounds__(512) void bwd_chl_kernel(BwdArgs a) {
   // the split's input rows and the rows of S_0 . dS_n are loaded before the prefix sums ----
   for (int i = tid; i < (L::oX - L::oLK) / 16; i += NT)
     reinterpret_cast<uint4*>(smem + L::oLK)[i] = make_uint4(0, 0, 0, 0);
-  if (tid < 128) {
-    fdGn[tid] = 0.f;
-    if (tid < 64) {
-      fdb[tid] = 0.f;
-      fdw[tid] = 0.f;
-    }
+  if (tid < 64) {
+    fdb[tid] = 0.f;  // (two terms per token: their sum does not depend on the order)
     if (tid == 0) *sFlag = 0;
   }
   const ChlRaw la_raw = chl_prefix_load(a, rr, left, tid);
@@ -267,7 +266,7 @@ __global__ __launch_bounds__(512) void bwd_chl_kernel(BwdArgs a) {
     }
     dot += __shfl_xor(dot, 1);
     dot += __shfl_xor(dot, 2);
-    if (dq4 == 0) atomicAdd(&fdGn[dch], fGn[dch] * dot);  // e^{G_n} <S_0, dS_n> per channel
+    if (dq4 == 0) pGn[dch] = fGn[dch] * dot;  // e^{G_n} <S_0, dS_n> per channel
   }
 
   // ---- split operands: 4 consecutive channels of one token per item ----
@@ -554,7 +553,7 @@ __global__ __launch_bounds__(512) void bwd_chl_kernel(BwdArgs a) {
           if (a.w_kind == kChannel) buf_store1((bf16_t*)nullptr, swc, off, acc[i] * vv);
           if (a.w_kind == kScalar) {
             const float x = row_sum16(acc[i] * vv);
-            if (l16 == 0) atomicAdd(&fdw[t], x);
+            if (l16 == 0) pw[((h * 2 + (wave & 1)) * 2 + u) * 64 + t] = x;
           }
         }
       }
@@ -640,7 +639,7 @@ __global__ __launch_bounds__(512) void bwd_chl_kernel(BwdArgs a) {
     }
     x += __shfl_xor(x, 16);
     x += __shfl_xor(x, 32);
-    if (g == 0) atomicAdd(&fdGn[ch], x);
+    if (g == 0) pGn[(1 + ota) * 128 + ch] = x;
   }
 
   // (q, k and b at this wave's accumulator positions, and log alpha again, for the outputs below)
@@ -775,7 +774,8 @@ __global__ __launch_bounds__(512) void bwd_chl_kernel(BwdArgs a) {
       d[u] = sdG[t * 128 + ch];
       if (TWO && t + 1 < C) d[u] += sdGp[(t + 1) * 128 + ch];
     }
-    if (q == 3) d[15] += fdGn[ch];  // the end-of-chunk decay e^{G_n}
+    if (q == 3)  // the end-of-chunk decay e^{G_n}
+      d[15] += (((pGn[ch] + pGn[128 + ch]) + pGn[256 + ch]) + pGn[384 + ch]) + pGn[512 + ch];
 #pragma unroll
     for (int u = 14; u >= 0; --u) d[u] += d[u + 1];
     qtot[q * 128 + ch] = d[0];
@@ -787,7 +787,11 @@ __global__ __launch_bounds__(512) void bwd_chl_kernel(BwdArgs a) {
     for (int u = 0; u < 16; ++u) buf_store1((bf16_t*)nullptr, sla, (16 * q + u) * hdk + ch * 2, d[u] + off);
     if (tid < 64) {
       if (a.b_kind == kScalar) buf_store1((bf16_t*)nullptr, make_rsrc(a.db + rr, rng_1), tid * h1, fdb[tid]);
-      if (a.w_kind == kScalar) buf_store1((bf16_t*)nullptr, make_rsrc(a.dw + rr, rng_1), tid * h1, fdw[tid]);
+      if (a.w_kind == kScalar) {
+        float x = 0.f;
+        for (int j = 0; j < 4 * nh; ++j) x += pw[j * 64 + tid];
+        buf_store1((bf16_t*)nullptr, make_rsrc(a.dw + rr, rng_1), tid * h1, x);
+      }
     }
   }
 }
