@@ -264,10 +264,13 @@ __device__ __forceinline__ float stage_elem(const unsigned char* st, int t, int 
 // c & 1), the scan, split and Gram products of chunk c + 1 fill the other buffer, and the inputs of
 // chunk c + 2 arrive in the staging.  One chunk takes three barriers:
 //   A0  the inputs of chunk c + 1 are in the staging
-//       split of c + 1 (all waves); then, for chunk c: U, T, R and the read-outs
+//       split of c + 1 (all waves); then, for chunk c: U, T and R
 //   A1  the operands of c + 1 are in their buffer; its flags are known
-//       loads of chunk c + 2; the state update of c; Gram products of c + 1 (waves 2-7)
+//       loads of chunk c + 2 (waves 2 and 3); Gram products of c + 1; for chunk c: the read-outs
+//       and the state update
 //   A2
+// (The read-outs wait until after A1 so that the two windows carry about equal work: the split
+// is vector-ALU work that the first window cannot hide.)
 // A chunk whose gates leave the range of the chunk form ("flagged") runs token by token from its
 // staged inputs; the loads of the chunk after it wait for that, and the pipeline refills.
 // The barriers wait for LDS operations only, so loads and stores stay in flight across them.
@@ -331,7 +334,8 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, unsigned char* smem, 
   const In inQ = in_of(a.q, Hk, hk, DK), inK = in_of(a.k, Hk, hk, DK), inV = in_of(a.v, H, hi, DV);
   const In inA = in_of(a.la, H, hi, AK == kChannel ? DK : 1), inB = in_of(a.bg, H, hi, BK == kChannel ? DK : 1);
   const In inW = in_of(a.wg, H, hi, WK == kChannel ? DV : 1);
-  // two: waves 0 and 1 issue every load (four row groups each), else each wave its own group
+  // two: waves 2 and 3 issue every per-channel load (four row groups each) and wave 0 the scalar
+  // gates, else each wave its own row group
   auto stage = [&](int64_t c, int lane, bool two) {
     const int64_t t0 = c * C;
     // a per-channel array is 8 loads of 1 KB (row group j: rows 4 j .. 4 j + 3)
@@ -339,8 +343,9 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, unsigned char* smem, 
       const int64_t off = t0 * in.stride, left = in.end - off;
       const uint32_t bytes = static_cast<uint32_t>(left < 0x7fffffff ? left : 0x7fffffff);
       const int slot = lane & 15;
+      if (two && wave < 2) return;  // (wave 0: the scalar gates only)
       for (int u = 0; u < (two ? 4 : 1); ++u) {
-        const int j = two ? 4 * wave + u : wave;
+        const int j = two ? 4 * (wave - 2) + u : wave;
         const int t = 4 * j + (lane >> 4);
         const int piece = (slot ^ t) & 15;
         seg_dma16(in.p + off, bytes, smem + dst + 1024 * j, static_cast<uint32_t>(t) * in.stride + piece * 16);
@@ -533,20 +538,18 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, unsigned char* smem, 
         for (int i = 0; i < 4; ++i) dst[i * LDD] = static_cast<__bf16>(acc[i]);
         return;
       }
-      const bool strict = which == 0 || which == 2;
+      const int lim = (which == 0 || which == 2) ? cc + 1 : cc;  // keep rows r >= lim
+      if (which == 0) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = r0 + i;
-        const float val = (strict ? (cc < r) : (cc <= r)) ? acc[i] : 0.f;
-        if (which == 0)
-          Ld[(ta * 16 + (r & 15)) * LDL + (cc & 15)] = -val;
-        else if (which == 1)
-          gM[r * LDD + cc] = static_cast<__bf16>(val);
-        else if (which == 2)
-          gLK[r * LDD + cc] = static_cast<__bf16>(val);
-        else
-          gMQK[r * LDD + cc] = static_cast<__bf16>(val);
+        for (int i = 0; i < 4; ++i) {
+          const int r = r0 + i;
+          Ld[(ta * 16 + (r & 15)) * LDL + (cc & 15)] = r >= lim ? -acc[i] : 0.f;
+        }
+        return;
       }
+      __bf16* dst = (which == 1 ? gM : which == 2 ? gLK : gMQK) + r0 * LDD + cc;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[i * LDD] = static_cast<__bf16>(r0 + i >= lim ? acc[i] : 0.f);
     };
     if (diag) {
       store_tile(0, acc1);
@@ -579,17 +582,14 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, unsigned char* smem, 
 
   // ---- the state through chunk c, part 1: U = Cs S (channel contraction, N and Phi), Z = L_K X
   // (MODE 2) or -X; T = (I + L)^{-1} (the diagonal blocks' inverses from the Gram waves, the
-  // off-diagonal block by three small MFMAs in every wave); R = T U + T Z; O^T = S^T Qs^T - R^T M^T (+ X^T M_QK^T),
-  // stored.  Leaves R (over the tokens) and X's column for part 2. ----
-  auto chain1 = [&](int64_t c, int par, int lane, F8& rfN, F8& rfP, F8& xf) {
-    const int g = lane >> 4, l16 = lane & 15, ch0 = 16 * wave + 4 * g, col = 16 * wave + l16;
-    const __bf16* tQ = reinterpret_cast<const __bf16*>(pbuf(par) + L::pQ);
+  // off-diagonal block by three small MFMAs in every wave); R = T U + T Z.  Leaves R (over the
+  // tokens), X's column and S's bf16 fragments (sfN, sfP) for the read-outs and part 2. ----
+  auto chain1 = [&](int par, int lane, F8& rfN, F8& rfP, F8& xf, F8 (&sfN)[4], F8 (&sfP)[4]) {
+    const int g = lane >> 4, l16 = lane & 15, col = 16 * wave + l16;
     const __bf16* tC = reinterpret_cast<const __bf16*>(pbuf(par) + L::pC);
     const __bf16* tX = reinterpret_cast<const __bf16*>(pbuf(par) + L::pX);
     const __bf16* gA = reinterpret_cast<const __bf16*>(gbuf(par) + L::gA);
-    const __bf16* gM = reinterpret_cast<const __bf16*>(gbuf(par) + L::gM);
     const __bf16* gLK = reinterpret_cast<const __bf16*>(gbuf(par) + L::gLK);
-    const __bf16* gMQK = reinterpret_cast<const __bf16*>(gbuf(par) + L::gMQK);
     const float* Ld = reinterpret_cast<const float*>(gbuf(par) + L::gLD);
     // operand loads first: their latencies overlap the conversions and the sweep
     F8 cfr[2][4];  // rows 16 ta + l16 of Cs, channels 32 kb + pair(g)
@@ -609,7 +609,6 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, unsigned char* smem, 
     }
     __builtin_amdgcn_sched_barrier(0);
 
-    F8 sfN[4], sfP[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       sfN[kb] = acc_pair_frag<__bf16>(SN[2 * kb], SN[2 * kb + 1]);
@@ -664,6 +663,15 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, unsigned char* smem, 
     }
     rfN = acc_pair_frag<__bf16>(RN[0], RN[1]);
     if constexpr (PHI) rfP = acc_pair_frag<__bf16>(RP[0], RP[1]);
+  };
+  // ---- the read-outs of chunk c: O^T = S^T Qs^T - R^T M^T (+ X^T M_QK^T) from S's fragments as
+  // they entered the chunk; to o, or (a segment from an unknown state) O(N) and Q~ to On and Qt ----
+  auto readout = [&](int64_t c, int par, int lane, const F8& rfN, const F8& rfP, const F8& xf, const F8 (&sfN)[4],
+                     const F8 (&sfP)[4]) {
+    const int g = lane >> 4, l16 = lane & 15, ch0 = 16 * wave + 4 * g;
+    const __bf16* tQ = reinterpret_cast<const __bf16*>(pbuf(par) + L::pQ);
+    const __bf16* gM = reinterpret_cast<const __bf16*>(gbuf(par) + L::gM);
+    const __bf16* gMQK = reinterpret_cast<const __bf16*>(gbuf(par) + L::gMQK);
     // O^T: lane holds O[token 16 ta + l16][column 16 w + 4 g + i]
     const int64_t t0 = c * C;
     const auto ro = make_rsrc(a.o + ((bi * T + t0) * H + hi) * DV, wy_range(T - t0, H, DV));
@@ -857,16 +865,18 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, unsigned char* smem, 
     lds_barrier_keep_vm();  // A0: chunk c + 1's inputs are in the staging
     if (has_next) split(par ^ 1, lane);
     __builtin_amdgcn_sched_barrier(0);
-    F8 rfN, rfP, xf;
-    chain1(c, par, lane, rfN, rfP, xf);
+    F8 rfN, rfP, xf, sfN[4], sfP[4];
+    chain1(par, lane, rfN, rfP, xf, sfN, sfP);
     lds_barrier_keep_vm();  // A1: chunk c + 1's operands are in their buffer, its flags known
     if (has_next) flag_next = flagged_now();
-    chain2(par, lane, rfN, rfP, xf);
     if (has_next && !flag_next) {
-      // waves 0 and 1 issue the loads of chunk c + 2 (the others go on to the Gram products)
-      if (wave < 2 && c + 2 < c_end) stage(c + 2, lane, true);
+      // waves 2 and 3 issue the loads of chunk c + 2 (wave 0 its scalar gates); then the Gram
+      // products (waves 0 and 1 the diagonal blocks and their inverses)
+      if ((wave == 0 || wave == 2 || wave == 3) && c + 2 < c_end) stage(c + 2, lane, true);
       gram(par ^ 1, lane);
     }
+    readout(c, par, lane, rfN, rfP, xf, sfN, sfP);
+    chain2(par, lane, rfN, rfP, xf);
     lds_barrier_keep_vm();  // A2
     flag_cur = flag_next;
   }
