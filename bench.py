@@ -412,7 +412,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # untimed calls before each timed loop: at least ~50 ms of GPU work, so that the timed calls
+    # run at the clocks the GPU holds under load (the first few milliseconds after idle run slower)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="gdn2",
                     choices=["gdn2", "kda", "gdn", "mamba2", "gla", "gdn_gqa", "gdn_d256"])
     ap.add_argument("--also", default="kda,gdn",
