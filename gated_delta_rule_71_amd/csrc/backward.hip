@@ -41,11 +41,12 @@ BwdSizes bwd_sizes(int64_t B, int64_t H, int64_t Hk, int64_t T, int64_t DK, int6
   return s;
 }
 
-// the chains over 32 value columns a workgroup where d_v allows (the chunk's A' then serves two
-// slices), else 16
+// the chains over 32 value columns a workgroup where d_v allows and that still gives at least 128
+// workgroups (the chunk's A' then serves two slices), else 16 (twice the A' reads, but twice the
+// chains side by side: with few states the chip is otherwise mostly idle)
 template <int DK, bool REV>
 void launch_chain(const BwdArgs& a, int64_t nstate, hipStream_t s) {
-  if (a.DV % 32 == 0)
+  if (a.DV % 32 == 0 && nstate * (a.DV / 32) >= 128)
     hipLaunchKernelGGL((bwd_chain_kernel<DK, REV, 2>), dim3((unsigned)(nstate * (a.DV / 32))),
                        dim3(64 * (2 + 2 * DK / 32)), 0, s, a);
   else

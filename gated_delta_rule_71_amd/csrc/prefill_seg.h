@@ -63,6 +63,7 @@ struct SegArgs {
 
 constexpr float kSegSpanLimit = 76.f;
 constexpr int kSegC = 32;  // tokens per chunk
+constexpr int kSegThreads = 512;  // threads of a segment workgroup
 
 __device__ __forceinline__ void unpack4(uint2 u, float* f) {
   f[0] = __uint_as_float(u.x << 16);
@@ -863,7 +864,7 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, unsigned char* smem, 
     }
     arrive(lane);
     lds_barrier_keep_vm();  // A0: chunk c + 1's inputs are in the staging
-    if (has_next) split(par ^ 1, lane);
+    split(par ^ 1, lane);  // (past the segment's end: stale staging into an unused buffer)
     __builtin_amdgcn_sched_barrier(0);
     F8 rfN, rfP, xf, sfN[4], sfP[4];
     chain1(par, lane, rfN, rfP, xf, sfN, sfP);
@@ -906,7 +907,7 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, unsigned char* smem, 
 }
 
 template <int MODE, int AK, int BK, int WK>
-__global__ __launch_bounds__(512) void seg_kernel(SegArgs a) {
+__global__ __launch_bounds__(kSegThreads) void seg_kernel(SegArgs a) {
   using L = SegLayout<MODE, AK, BK, WK>;
   static_assert(L::fits, "LDS layout exceeds the gfx950 workgroup limit");
   __shared__ __attribute__((aligned(1024))) unsigned char smem[L::total];

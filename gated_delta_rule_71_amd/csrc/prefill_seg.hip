@@ -95,7 +95,7 @@ hipError_t prefill_seg_launch(const PrefillArgs<bf16_t>& pa, int64_t nstate, boo
     a.Ebf = reinterpret_cast<__bf16*>(w);
   }
   if (nstate == 0) return hipSuccess;
-  const dim3 grid(static_cast<unsigned>(nstate * p.nseg)), block(512);
+  const dim3 grid(static_cast<unsigned>(nstate * p.nseg)), block(kSegThreads);
   const bool bch = a.b_kind == kChannel;
   if (a.alpha_kind == kScalar)
     hipLaunchKernelGGL((seg_kernel<1, kScalar, kScalar, kScalar>), grid, block, 0, s, a);
