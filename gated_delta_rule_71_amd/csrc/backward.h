@@ -250,15 +250,15 @@ struct ChainLayout {
   static constexpr int NDMA = AB / 1024 + DB / 1024 + 1;  // direct-to-LDS loads per chunk
 };
 
+// One chain's workgroup bid of nb (the workgroups of that chain); smem: its ChainLayout.
 template <int DK, bool REV, int NS>
-__global__ __launch_bounds__(64 * (2 + NS * DK / 32)) void bwd_chain_kernel(BwdArgs a) {
+__device__ __forceinline__ void bwd_chain_body(const BwdArgs& a, int64_t nb, int64_t bid, unsigned char* smem) {
   using L = ChainLayout<DK, NS>;
   using MM = Mma<__bf16>;
   using F8 = MM::F8;
   static_assert(L::fits, "LDS layout exceeds the gfx950 workgroup limit");
   static_assert(L::NDMA <= 60, "one chunk's loads must fit the vmcnt range");
   constexpr int NKB = DK / 32, NSW = L::NSW;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[L::total];
 
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -266,7 +266,6 @@ __global__ __launch_bounds__(64 * (2 + NS * DK / 32)) void bwd_chain_kernel(BwdA
   const int64_t nwg = DV / (16 * NS);  // workgroups per state
   // consecutive workgroup indices go to different XCDs (8, round robin): renumber so that the
   // workgroups of one state share an XCD, and so its L2, for the chunk maps they all read
-  const int64_t nb = gridDim.x, bid = blockIdx.x;
   const int64_t p = (nb % 8 == 0) ? (bid % 8) * (nb / 8) + bid / 8 : bid;
   const int64_t bh = p / nwg;
   const int sl0 = static_cast<int>(p % nwg) * NS;
@@ -395,6 +394,26 @@ __global__ __launch_bounds__(64 * (2 + NS * DK / 32)) void bwd_chain_kernel(BwdA
 #pragma unroll
       for (int i = 0; i < 4; ++i) a.dS0[(bh * DK + 16 * (2 * w + u) + 4 * g + i) * DV + col] = S[u][i];
   }
+}
+
+template <int DK, bool REV, int NS>
+__global__ __launch_bounds__(64 * (2 + NS * DK / 32)) void bwd_chain_kernel(BwdArgs a) {
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[ChainLayout<DK, NS>::total];
+  bwd_chain_body<DK, REV, NS>(a, gridDim.x, blockIdx.x, smem);
+}
+
+// Both chains in one launch (they read the same chunk maps but depend on nothing the other
+// writes): the first half of the grid runs the forward chain, the second the reverse one.  For
+// problems whose chains each fill at most half the chip.  (The second half keeps the XCD
+// renumbering when the half is a multiple of 8.)
+template <int DK, int NS>
+__global__ __launch_bounds__(64 * (2 + NS * DK / 32)) void bwd_chains_kernel(BwdArgs a) {
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[ChainLayout<DK, NS>::total];
+  const int64_t half = gridDim.x / 2;
+  if (static_cast<int64_t>(blockIdx.x) < half)
+    bwd_chain_body<DK, false, NS>(a, half, blockIdx.x, smem);
+  else
+    bwd_chain_body<DK, true, NS>(a, half, blockIdx.x - half, smem);
 }
 
 // ------------------------------------------------------------------ chunk-local adjoint

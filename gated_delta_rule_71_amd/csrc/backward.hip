@@ -54,6 +54,21 @@ void launch_chain(const BwdArgs& a, int64_t nstate, hipStream_t s) {
                        dim3(64 * (2 + DK / 32)), 0, s, a);
 }
 
+// Both chains: side by side in one launch when together they still fit one workgroup per CU
+// (each chain alone would leave half the chip idle), else one after the other.
+constexpr int64_t kChipCUs = 256;  // MI355X compute units
+
+template <int DK>
+void launch_chains(const BwdArgs& a, int64_t nstate, hipStream_t s) {
+  const int64_t n16 = nstate * (a.DV / 16);  // 16-column workgroups per chain
+  if (2 * n16 <= kChipCUs) {
+    hipLaunchKernelGGL((bwd_chains_kernel<DK, 1>), dim3((unsigned)(2 * n16)), dim3(64 * (2 + DK / 32)), 0, s, a);
+    return;
+  }
+  launch_chain<DK, false>(a, nstate, s);
+  launch_chain<DK, true>(a, nstate, s);
+}
+
 // Per-channel decay (dk = 128, dv 64 or 128): the chunk maps in the order MODE (2: erase first,
 // 1: decay first), the chains, then the chunk-local adjoint by matrix products for every chunk
 // whose gates stay in range and token by token for the others.
@@ -62,8 +77,7 @@ hipError_t launch_channel(WycArgs f, const BwdArgs& a, int64_t nstate, hipStream
   const int64_t nblk = nstate * a.nch;
   hipLaunchKernelGGL((wyc_prep_kernel<128, 128, MODE>), dim3((unsigned)nblk), dim3(512), 0, s, f);
   hipLaunchKernelGGL((bwd_db_kernel<128, 128>), dim3((unsigned)nblk), dim3(256), 0, s, a);
-  launch_chain<128, false>(a, nstate, s);
-  launch_chain<128, true>(a, nstate, s);
+  launch_chains<128>(a, nstate, s);
   hipLaunchKernelGGL((bwd_chl_kernel<MODE>), dim3((unsigned)nblk), dim3(512), 0, s, a);
   hipLaunchKernelGGL((bwd_chl_token_kernel<MODE>), dim3((unsigned)nblk), dim3((unsigned)(64 * (a.DV / 16))), 0, s, a);
   return hipGetLastError();
@@ -81,8 +95,7 @@ hipError_t launch_dk(WycArgs f, const BwdArgs& a, const BwdArgs* halves, int nh,
     hipLaunchKernelGGL((wyc_prep_kernel<DK, 256, 1>), dim3((unsigned)nblk), dim3(512), 0, s, f);
     hipLaunchKernelGGL((bwd_db_kernel<DK, 256>), dim3((unsigned)nblk), dim3(256), 0, s, a);
   }
-  launch_chain<DK, false>(a, nstate, s);
-  launch_chain<DK, true>(a, nstate, s);
+  launch_chains<DK>(a, nstate, s);
   for (int h = 0; h < nh; ++h)
     hipLaunchKernelGGL((bwd_local_kernel<DK>), dim3((unsigned)nblk), dim3(512), 0, s, halves[h]);
   return hipGetLastError();
