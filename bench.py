@@ -18,7 +18,9 @@ at half).  `phases` splits the call with an event recorded after its first launc
 profiles/hbm_counters.txt when that file was recorded on the current kernel sources, else null.
 `workloads` holds the same figures for the other prefill workloads (`--also`).  `decode` reports
 state GB/s for the decode workload (the state is read and written once per step), and under
-`copy_reference` the rate of torch's copy kernel over the same bytes.  `cpu_baseline` times the
+`copy_reference` the rate of torch's copy kernel over the same bytes; `mfma_calibration` the bf16
+matrix-core rate of a register-only loop (gdr_mfma_probe), the reachable side of the 2.5166 PFLOP/s
+figure.  `cpu_baseline` times the
 fp64 oracle on the host: the whole headline workload on the host threads it may use, and one state
 of it on one thread; its outputs also give `parity`, the headline call's errors against the oracle
 on the same inputs (max |o - o_ref| and the largest per-state relative Frobenius error of S_T).
@@ -228,6 +230,29 @@ def time_decode(wl, n_steps, dev):
     return ms
 
 
+def time_mfma_probe(dev, blocks=1024, iters=20000):
+    """TFLOP/s of the library's register-only bf16 matrix-core loop (gdr_mfma_probe): the dense
+    rate the GPU sustains, beside the 2.5166 PFLOP/s vendor figure the roofline uses.  Four
+    512-thread workgroups per CU; checks the probe's exact result."""
+    import torch
+    import gated_delta_rule_71_amd as gdr
+    gdr.mfma_probe(100, blocks, dev)  # warm-up
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    out, flop = gdr.mfma_probe(iters, blocks, dev)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    if not bool((out == 4.0 * iters).all()):
+        raise RuntimeError("gdr_mfma_probe returned a wrong result")
+    tf = flop / (ms * 1e-3) / 1e12
+    return {"TFLOP/s": tf, "frac_of_peak": tf / PEAK_BF16_TFLOPS, "ms": ms, "flop": flop,
+            "kernel": "gdr_mfma_probe: 8 independent bf16 16x16x32 MFMA chains per wave, register "
+                      "operands, %d workgroups of 512 threads, %d steps" % (blocks, iters)}
+
+
 def time_copy(nbytes, reps, dev):
     """GB/s (read + write) of torch's device-to-device copy of an fp32 tensor of `nbytes`: the
     rate a plain streaming kernel reaches on this GPU, beside the decode step's."""
@@ -426,6 +451,8 @@ def main():
                     help="skip timing gdr_chunk_bwd (run for bf16 scalar- or no-decay workloads)")
     ap.add_argument("--hooks", action="store_true",
                     help="also time the state-decomposition hook (64 positions, one sequence)")
+    ap.add_argument("--no-calibration", action="store_true",
+                    help="skip the register-only matrix-core probe (mfma_calibration)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 1 GiB device copy (read 1 GiB, write 1 GiB): the "
                          "reference dispatch that scales rocprofv3 FETCH_SIZE / WRITE_SIZE")
@@ -473,6 +500,9 @@ def main():
         "workspace_bytes": rep["workspace_bytes"],
         "device": device_identity(dev),
     }
+    if not args.no_calibration:
+        out["mfma_calibration"] = time_mfma_probe(dev)
+        progress("mfma probe %.1f TFLOP/s" % out["mfma_calibration"]["TFLOP/s"])
     extra = [n for n in args.also.split(",") if n and n != wl.name]
     if extra:
         out["workloads"] = {}

@@ -258,6 +258,22 @@ def decode_step(q, k, v, log_alpha=None, b=None, w=None, S=None, order="erase_th
     return o
 
 
+def mfma_probe(iters, blocks, device=None):
+    """Calibration: runs gdr_mfma_probe (register-only bf16 16x16x32 products, 8 chains per wave,
+    512-thread workgroups) on the current stream and returns (out, flop): out holds one float per
+    wave, exactly 4 * iters; flop is the dense work of the call.  Timing is the caller's."""
+    torch = _torch()
+    dev = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+    _require_gpu(dev)
+    if iters < 0 or not 1 <= blocks <= 65535:
+        raise ValueError("iters >= 0 and 1 <= blocks <= 65535")
+    out = torch.empty((blocks * 8,), dtype=torch.float32, device=dev)
+    rc = _native.mfma_probe_raw(iters, blocks, _ptr(out), _stream(dev))
+    if rc != _native.GDR_OK:
+        raise GdrError(rc, "gdr_mfma_probe")
+    return out, _native.mfma_probe_flop(iters, blocks)
+
+
 def build():
     """Compile libgdr.so in-tree for gfx950 (hipcc)."""
     from .buildlib import build as _b

@@ -17,7 +17,7 @@ ERASE_THEN_DECAY, DECAY_THEN_ERASE = 0, 1
 
 EXPORTED = ("gdr_abi_version", "gdr_status_string", "gdr_chunk_fwd_workspace_bytes",
             "gdr_chunk_fwd", "gdr_chunk_fwd_marked", "gdr_chunk_fwd_noalloc", "gdr_decode_step",
-            "gdr_chunk_bwd_workspace_bytes", "gdr_chunk_bwd")
+            "gdr_chunk_bwd_workspace_bytes", "gdr_chunk_bwd", "gdr_mfma_probe", "gdr_mfma_probe_flop")
 NOALLOC_SCRATCH_BYTES = 64 << 20  # GDR_NOALLOC_SCRATCH_BYTES
 
 
@@ -82,6 +82,10 @@ def lib():
         L.gdr_chunk_bwd_workspace_bytes.argtypes = [pp]
         L.gdr_chunk_bwd.restype = ctypes.c_int
         L.gdr_chunk_bwd.argtypes = [pp] + [vp] * 17 + [sz, vp]
+        L.gdr_mfma_probe.restype = ctypes.c_int
+        L.gdr_mfma_probe.argtypes = [ctypes.c_int64, ctypes.c_int32, vp, vp]
+        L.gdr_mfma_probe_flop.restype = ctypes.c_int64
+        L.gdr_mfma_probe_flop.argtypes = [ctypes.c_int64, ctypes.c_int32]
         _lib = L
     return _lib
 
@@ -138,3 +142,11 @@ def chunk_bwd_raw(problem, q, k, v, la, b, w, S0, dO, dS_T, dq, dk, dv, dla, db,
     return lib().gdr_chunk_bwd(ctypes.byref(problem), n(q), n(k), n(v), n(la), n(b), n(w), n(S0),
                                n(dO), n(dS_T), n(dq), n(dk), n(dv), n(dla), n(db), n(dw), n(dS0),
                                n(ws), ws_bytes, n(stream))
+
+
+def mfma_probe_raw(iters, blocks, out, stream):
+    return lib().gdr_mfma_probe(int(iters), int(blocks), out, stream)
+
+
+def mfma_probe_flop(iters, blocks):
+    return lib().gdr_mfma_probe_flop(int(iters), int(blocks))

@@ -258,6 +258,17 @@ int gdr_chunk_bwd(const gdr_problem* p, const void* q, const void* k, const void
                   void* dlog_alpha, void* db, void* dw, float* dS0, void* workspace,
                   size_t workspace_bytes, void* stream);
 
+/* ---- calibration (context for the roofline figures; computes nothing of the method) ----
+ * gdr_mfma_probe: launches `blocks` workgroups of 512 threads on `stream`; each wave runs
+ * `iters` steps of 8 independent bf16 16x16x32 matrix-core products on register operands (no
+ * memory traffic) and writes one float to out[block * 8 + wave] (exactly 4 * iters: every
+ * operand element is 1/16).  `out` is a device buffer of at least 8 * blocks floats, owned by
+ * the caller.  Returns GDR_ERR_INVALID_ARGUMENT for iters < 0, blocks outside [1, 65535] or a
+ * NULL out, GDR_ERR_HIP if the launch fails.  gdr_mfma_probe_flop: the dense FLOP one such
+ * call performs (2 x 16 x 16 x 32 per product), for a rate from the caller's timing. */
+int gdr_mfma_probe(int64_t iters, int32_t blocks, float* out, void* stream);
+int64_t gdr_mfma_probe_flop(int64_t iters, int32_t blocks);
+
 #ifdef __cplusplus
 }
 #endif

@@ -347,3 +347,13 @@ def test_noalloc_rejects_problems_past_its_scratch():
         == N.GDR_ERR_INVALID_ARGUMENT
     assert N.chunk_fwd_noalloc_raw(prob(dk=96), *args, 0) == N.GDR_ERR_UNSUPPORTED
     assert N.chunk_fwd_noalloc_raw(prob(batch=0), *args, 0) == N.GDR_OK
+
+
+def test_mfma_probe_rejects_bad_arguments_and_counts_flop():
+    # validation returns before any HIP call
+    assert N.mfma_probe_raw(-1, 4, A, 0) == N.GDR_ERR_INVALID_ARGUMENT
+    assert N.mfma_probe_raw(10, 0, A, 0) == N.GDR_ERR_INVALID_ARGUMENT
+    assert N.mfma_probe_raw(10, 65536, A, 0) == N.GDR_ERR_INVALID_ARGUMENT
+    assert N.mfma_probe_raw(10, 4, None, 0) == N.GDR_ERR_INVALID_ARGUMENT
+    # 8 waves x 8 chains x (2 x 16 x 16 x 32) per step and workgroup
+    assert N.mfma_probe_flop(3, 5) == 3 * 5 * 8 * 8 * 2 * 16 * 16 * 32

@@ -269,3 +269,15 @@ def test_flagged_chunks_in_the_all_modes_kernel(dev, kind, D, DV, dtype, order):
     torch.cuda.synchronize()
     assert torch.isfinite(o.float()).all() and torch.isfinite(S).all()
     check(x, o, S, order, TOL[dtype], "flagged %s d%d/%d %s %s" % (kind, D, DV, dtype, order))
+
+
+def test_mfma_probe_exact_result(dev):
+    """The calibration probe's documented result: every operand element is 1/16, so each of a
+    wave's 8 x 4 accumulator elements gains 32/256 per step and their sum is 4 * iters."""
+    import gated_delta_rule_71_amd as gdr
+    say("mfma probe")
+    out, flop = gdr.mfma_probe(300, 6, dev)
+    torch.cuda.synchronize()
+    assert out.shape == (48,)
+    assert bool((out == 1200.0).all())
+    assert flop == 300 * 6 * 8 * 8 * 2 * 16 * 16 * 32
