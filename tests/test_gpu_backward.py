@@ -360,3 +360,17 @@ def test_backward_scalar_same_call_same_bits(dev, kind, DV):
         if a[n] is None:
             continue
         assert torch.equal(a[n], b[n]), n
+
+
+@pytest.mark.parametrize("kind,B,H", [("gdn", 2, 3), ("gdn", 4, 5), ("gdn", 4, 9),
+                                      ("gdn2", 2, 3), ("gdn2", 4, 5), ("gdn2", 4, 9)])
+def test_backward_chain_launch_forms(dev, kind, B, H):
+    """The three launch forms of the state chains at d_v = 128: both chains in one launch (at most
+    16 states), one after the other 16 columns wide (17 to 31 states), and 32 columns wide (32
+    states and more); every state against the token adjoint."""
+    if kind == "gdn":
+        x = case(kind, B=B, H=H, T=64 + 7, D=128, seed=171 + H)
+    else:
+        x = ch_case(kind, B=B, H=H, T=64 + 7, DV=128, seed=181 + H)
+    say("backward chain forms", kind, B * H, "states")
+    compare(run(x, dev), reference(x), "%s %d states" % (kind, B * H))
