@@ -946,7 +946,10 @@ __global__ __launch_bounds__(256) void seg_chain_kernel(SegArgs a) {
   __shared__ __attribute__((aligned(16))) uint4 sB[2][4][kChainNT][2][64];  // [buffer][kb][n][hi, lo][lane]
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
-  const int64_t bh = blockIdx.x / NB, c0 = (blockIdx.x % NB) * kChainCols;
+  // (the workgroups of one state on one XCD, so that its L2 serves them each segment's Phi)
+  const int64_t nb = gridDim.x, bid = blockIdx.x;
+  const int64_t p = (nb % 8 == 0) ? (bid % 8) * (nb / 8) + bid / 8 : bid;
+  const int64_t bh = p / NB, c0 = (p % NB) * kChainCols;
   const int64_t nseg = a.nseg;
 
   f32x4 acc[2][kChainNT];  // [row tile 2 w + mt][column tile n]: rows 32 w + 16 mt + 4 g + i, column c0 + 16 n + l16
@@ -1095,7 +1098,10 @@ __global__ __launch_bounds__(256) void seg_fix_kernel(SegArgs a) {
   // (32-bit index arithmetic: the grid is far below 2^31 workgroups)
   const uint32_t ngrp = static_cast<uint32_t>((a.L + kFixGroup - 1) / kFixGroup);
   const uint32_t nsm1 = static_cast<uint32_t>(a.nseg - 1);
-  uint32_t blk = blockIdx.x;
+  // consecutive workgroup indices go to different XCDs (8, round robin): renumber so that the
+  // groups of one (state, segment) share an XCD, and so its L2, for the entering state they all read
+  const uint32_t nb = gridDim.x, bid = blockIdx.x;
+  uint32_t blk = (nb % 8 == 0) ? (bid % 8) * (nb / 8) + bid / 8 : bid;
   const uint32_t grp = blk % ngrp;
   blk /= ngrp;
   const int64_t s = 1 + blk % nsm1, bh = blk / nsm1;
