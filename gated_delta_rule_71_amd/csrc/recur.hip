@@ -3,7 +3,9 @@
 // and bf16 at dk = 256 with a per-channel decay after the erase.
 //
 // One wave per (batch, head) and block of 16 value columns walks the tokens in order and keeps
-// its 16 columns of S in registers from S0 to S_T.  Per token, with c = b . k, x = w . v and
+// its 16 columns of S in registers from S0 to S_T.  The tokens' inputs arrive in LDS by
+// direct-to-LDS loads, a block of 8 tokens ahead of their use, so that the walk waits on the
+// memory latency once per block instead of once per token.  Per token, with c = b . k, x = w . v and
 // alpha = exp(log alpha) ("Recurrent Memory: Write, Erase, Decay, Read", section 05 for the
 // unified update, section 01 for the read; the read sees the token's own write):
 //
@@ -67,15 +69,53 @@ struct TokenIn {
 
 }  // namespace
 
+// One token's inputs in LDS: the rows of q and k and of per-channel log alpha and b (dk elements
+// each), then the 16 value columns of v and of a per-channel w of this wave's block.
+template <typename IO, int DK>
+struct RecurSlot {
+  static constexpr int EL = sizeof(IO), ROWB = DK * EL;
+  static constexpr int oQ = 0, oK = ROWB, oLA = 2 * ROWB, oB = 3 * ROWB, oV = 4 * ROWB, oW = oV + 64;
+  static constexpr int bytes = oW + 64;
+};
+
+// Direct-to-LDS load of 16 bytes per active lane: bytes 16 i .. 16 i + 15 past `off` of the buffer
+// `r` (zeros past its end) into LDS at m0 + 16 i for lane i.  Issued from an asm statement, so the
+// compiler inserts no wait for it; the kernel waits for its loads itself.  m0 and r are uniform.
+typedef int recur_i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ recur_i32x4 recur_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  recur_i32x4 r;
+  r.x = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(p)));
+  r.y = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(p >> 32) & 0xffffu));  // stride 0
+  r.z = __builtin_amdgcn_readfirstlane(static_cast<int>(bytes));
+  r.w = 0x00020000;
+  return r;
+}
+__device__ __forceinline__ uint32_t recur_m0(unsigned char* lds) {
+  return __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) unsigned char*)lds)));
+}
+__device__ __forceinline__ void recur_dma16(recur_i32x4 r, uint32_t m0, uint32_t off) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(m0), "v"(off), "s"(r)
+               : "memory", "m0");
+}
+
 template <typename IO, int DK, bool DECAY_FIRST>
 __global__ __launch_bounds__(64) void recur_kernel(PrefillArgs<IO> a) {
+  using SL = RecurSlot<IO, DK>;
   constexpr int R = DK / 16;  // rows per lane
+  constexpr int TB = 8;       // tokens per block: block b + 1 loads while block b is computed
+  constexpr int EL = SL::EL;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * TB * SL::bytes];
   const int lane = threadIdx.x;
   const int rg = lane >> 2, cq = lane & 3;
   const int d0 = rg * R;  // first row of this lane
   const int64_t nsl = a.DV / 16;
   const int64_t bh = blockIdx.x / nsl;
-  const int64_t col0 = (blockIdx.x % nsl) * 16 + 4 * cq;  // first column of this lane
+  const int64_t cb0 = (blockIdx.x % nsl) * 16;  // first column of this wave's block
+  const int64_t col0 = cb0 + 4 * cq;            // first column of this lane
   const int64_t H = a.H, DV = a.DV, T = a.T;
   const int64_t bi = bh / H, hi = bh % H;
   const int64_t Hk = a.Hk, hk = hi / (H / Hk);
@@ -96,74 +136,145 @@ __global__ __launch_bounds__(64) void recur_kernel(PrefillArgs<IO> a) {
     for (int i = 0; i < R; ++i) s[i][0] = s[i][1] = s[i][2] = s[i][3] = 0.f;
   }
 
-  auto fetch = [&](int64_t t, TokenIn<IO, R>& in) {
-    const int64_t row = (bi * T + t) * H + hi, qrow = (bi * T + t) * Hk + hk;
-    Run<IO, R>::load(a.q + qrow * DK + d0, in.q);
-    Run<IO, R>::load(a.k + qrow * DK + d0, in.k);
-    if (a.alpha_kind == kChannel) Run<IO, R>::load(a.la + row * DK + d0, in.la);
-    if (a.b_kind == kChannel) Run<IO, R>::load(a.bg + row * DK + d0, in.b);
-    Run<IO, 4>::load(a.v + row * DV + col0, in.v);
-    if (a.w_kind == kChannel) Run<IO, 4>::load(a.wg + row * DV + col0, in.w);
-    in.las = a.alpha_kind == kScalar ? ld(a.la, row) : 0.f;
-    in.bs = a.b_kind == kScalar ? ld(a.bg, row) : 0.f;
-    in.ws = a.w_kind == kScalar ? ld(a.wg, row) : 1.f;
+  // per input: this state's token-0 element, the row stride and the bytes to the end of its last
+  // row; each block of tokens addresses its loads from its own first token (64-bit base, 32-bit
+  // offsets under 8 row strides)
+  struct In {
+    const unsigned char* p;
+    int64_t stride;
+    int64_t end;
+  };
+  auto in_of = [&](const IO* x, int64_t heads, int64_t head, int64_t width, int64_t first) {
+    const int64_t stride = heads * width * EL;
+    return In{reinterpret_cast<const unsigned char*>(x + (bi * T * heads + head) * width + first), stride,
+              (T - 1) * stride + (width - first) * EL};
+  };
+  const In inQ = in_of(a.q, Hk, hk, DK, 0), inK = in_of(a.k, Hk, hk, DK, 0);
+  const In inV = in_of(a.v, H, hi, DV, cb0);
+  // (per-channel gates only: a scalar gate's element is not 16-byte aligned; those come through
+  // registers below)
+  const In inA = in_of(a.alpha_kind == kChannel ? a.la : a.q, a.alpha_kind == kChannel ? H : Hk,
+                       a.alpha_kind == kChannel ? hi : hk, DK, 0);
+  const In inB = in_of(a.b_kind == kChannel ? a.bg : a.q, a.b_kind == kChannel ? H : Hk,
+                       a.b_kind == kChannel ? hi : hk, DK, 0);
+  const In inW = in_of(a.w_kind == kChannel ? a.wg : a.v, H, hi, DV, cb0);
+  // block b's loads into its buffer, token u of the block into slot u: whole rows of q and k (and
+  // of per-channel gates), the block's 16 columns of v (and of a per-channel w)
+  auto dma_block = [&](int64_t b) {
+    unsigned char* buf = smem + (b & 1) * TB * SL::bytes;
+    const int64_t t0 = b * TB;
+    const int nt = static_cast<int>(T - t0 < TB ? T - t0 : TB);
+    auto rows = [&](const In& in, int dst, int nbytes) {
+      const int64_t left = in.end - t0 * in.stride;
+      const recur_i32x4 r = recur_rsrc(in.p + t0 * in.stride, static_cast<uint32_t>(left < 0x7fffffff ? left : 0x7fffffff));
+      for (int u = 0; u < nt; ++u) {
+        const uint32_t m0 = recur_m0(buf + u * SL::bytes + dst);
+        if (lane * 16 < nbytes) recur_dma16(r, m0, static_cast<uint32_t>(u * in.stride + lane * 16));
+      }
+    };
+    rows(inQ, SL::oQ, SL::ROWB);
+    rows(inK, SL::oK, SL::ROWB);
+    if (a.alpha_kind == kChannel) rows(inA, SL::oLA, SL::ROWB);
+    if (a.b_kind == kChannel) rows(inB, SL::oB, SL::ROWB);
+    rows(inV, SL::oV, 16 * EL);
+    if (a.w_kind == kChannel) rows(inW, SL::oW, 16 * EL);
+  };
+  // scalar gates of block b: lane u < 8 holds token u's (log alpha, b, w), loaded a block ahead
+  auto scalars_of = [&](int64_t b, float& la_, float& b_, float& w_) {
+    const int64_t t = b * TB + lane;
+    la_ = 0.f;
+    b_ = 0.f;
+    w_ = 1.f;
+    if (lane < TB && t < T) {
+      const int64_t row = (bi * T + t) * H + hi;
+      if (a.alpha_kind == kScalar) la_ = ld(a.la, row);
+      if (a.b_kind == kScalar) b_ = ld(a.bg, row);
+      if (a.w_kind == kScalar) w_ = ld(a.wg, row);
+    }
   };
 
-  TokenIn<IO, R> cur, nxt;
-  if (T > 0) fetch(0, cur);
-  for (int64_t t = 0; t < T; ++t) {
-    if (t + 1 < T) fetch(t + 1, nxt);  // the next token's loads stay in flight over this one
-    float al[R], cp[R], kp[R], qa[R];
-    float dqk = 0.f, dg = 0.f;
-#pragma unroll
-    for (int i = 0; i < R; ++i) {
-      const float lad = a.alpha_kind == kChannel ? cur.la[i] : cur.las;
-      const float bd = a.b_kind == kChannel ? cur.b[i] : cur.bs;
-      al[i] = a.alpha_kind == kNone ? 1.f : __expf(lad);
-      const float c = a.b_kind == kNone ? 0.f : bd * cur.k[i];
-      qa[i] = cur.q[i] * al[i];
-      dqk += cur.q[i] * cur.k[i];
-      if (DECAY_FIRST) {
-        cp[i] = c * al[i];
-        kp[i] = cur.k[i];
-      } else {
-        cp[i] = c;
-        kp[i] = al[i] * cur.k[i];
-      }
-      dg += cur.q[i] * kp[i];  // q . (alpha . k); q . k with the decay first
+  const int64_t nblk = (T + TB - 1) / TB;
+  float nla = 0.f, nb = 0.f, nw = 1.f;  // the next block's scalar gates
+  if (nblk > 0) {
+    dma_block(0);
+    scalars_of(0, nla, nb, nw);
+  }
+  for (int64_t b = 0; b < nblk; ++b) {
+    // block b's loads (issued one block ago) are in LDS; every store of block b - 1 is done
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    const float cla = nla, cbs = nb, cws = nw;
+    // block b + 1 into the other buffer, whose last reads (block b - 1) have returned
+    if (b + 1 < nblk) {
+      dma_block(b + 1);
+      scalars_of(b + 1, nla, nb, nw);
     }
-    float r[4] = {0.f, 0.f, 0.f, 0.f}, y[4] = {0.f, 0.f, 0.f, 0.f};
+    const unsigned char* buf = smem + (b & 1) * TB * SL::bytes;
+    const int nt = static_cast<int>(T - b * TB < TB ? T - b * TB : TB);
+    for (int u = 0; u < nt; ++u) {
+      const int64_t t = b * TB + u;
+      const unsigned char* slot = buf + u * SL::bytes;
+      TokenIn<IO, R> cur;
+      Run<IO, R>::load(reinterpret_cast<const IO*>(slot + SL::oQ) + d0, cur.q);
+      Run<IO, R>::load(reinterpret_cast<const IO*>(slot + SL::oK) + d0, cur.k);
+      if (a.alpha_kind == kChannel) Run<IO, R>::load(reinterpret_cast<const IO*>(slot + SL::oLA) + d0, cur.la);
+      if (a.b_kind == kChannel) Run<IO, R>::load(reinterpret_cast<const IO*>(slot + SL::oB) + d0, cur.b);
+      Run<IO, 4>::load(reinterpret_cast<const IO*>(slot + SL::oV) + 4 * cq, cur.v);
+      if (a.w_kind == kChannel) Run<IO, 4>::load(reinterpret_cast<const IO*>(slot + SL::oW) + 4 * cq, cur.w);
+      cur.las = __shfl(cla, u);
+      cur.bs = __shfl(cbs, u);
+      cur.ws = __shfl(cws, u);
+
+      float al[R], cp[R], kp[R], qa[R];
+      float dqk = 0.f, dg = 0.f;
 #pragma unroll
-    for (int i = 0; i < R; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        r[j] += cp[i] * s[i][j];
-        y[j] += qa[i] * s[i][j];
+      for (int i = 0; i < R; ++i) {
+        const float lad = a.alpha_kind == kChannel ? cur.la[i] : cur.las;
+        const float bd = a.b_kind == kChannel ? cur.b[i] : cur.bs;
+        al[i] = a.alpha_kind == kNone ? 1.f : __expf(lad);
+        const float c = a.b_kind == kNone ? 0.f : bd * cur.k[i];
+        qa[i] = cur.q[i] * al[i];
+        dqk += cur.q[i] * cur.k[i];
+        if (DECAY_FIRST) {
+          cp[i] = c * al[i];
+          kp[i] = cur.k[i];
+        } else {
+          cp[i] = c;
+          kp[i] = al[i] * cur.k[i];
+        }
+        dg += cur.q[i] * kp[i];  // q . (alpha . k); q . k with the decay first
       }
-    // sum over the 16 row groups: lanes of equal cq
+      float r[4] = {0.f, 0.f, 0.f, 0.f}, y[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int off = 4; off < 64; off <<= 1) {
+      for (int i = 0; i < R; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        r[j] += __shfl_xor(r[j], off);
-        y[j] += __shfl_xor(y[j], off);
+        for (int j = 0; j < 4; ++j) {
+          r[j] += cp[i] * s[i][j];
+          y[j] += qa[i] * s[i][j];
+        }
+      // sum over the 16 row groups: lanes of equal cq
+#pragma unroll
+      for (int off = 4; off < 64; off <<= 1) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          r[j] += __shfl_xor(r[j], off);
+          y[j] += __shfl_xor(y[j], off);
+        }
+        dqk += __shfl_xor(dqk, off);
+        dg += __shfl_xor(dg, off);
       }
-      dqk += __shfl_xor(dqk, off);
-      dg += __shfl_xor(dg, off);
+      float x[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) x[j] = cur.v[j] * (a.w_kind == kChannel ? cur.w[j] : cur.ws);
+#pragma unroll
+      for (int i = 0; i < R; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) s[i][j] = al[i] * s[i][j] - kp[i] * r[j] + cur.k[i] * x[j];
+      if (rg == 0) {
+        const int64_t orow = (bi * T + t) * H + hi;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) st(a.o, orow * DV + col0 + j, y[j] - dg * r[j] + dqk * x[j]);
+      }
     }
-    float x[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) x[j] = cur.v[j] * (a.w_kind == kChannel ? cur.w[j] : cur.ws);
-#pragma unroll
-    for (int i = 0; i < R; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) s[i][j] = al[i] * s[i][j] - kp[i] * r[j] + cur.k[i] * x[j];
-    if (rg == 0) {
-      const int64_t orow = (bi * T + t) * H + hi;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) st(a.o, orow * DV + col0 + j, y[j] - dg * r[j] + dqk * x[j]);
-    }
-    if (t + 1 < T) cur = nxt;
   }
   if (a.S_T != nullptr) {
     float* ST = a.S_T + bh * DK * DV;
