@@ -251,9 +251,22 @@ __global__ __launch_bounds__(64) void recur_kernel(PrefillArgs<IO> a) {
           r[j] += cp[i] * s[i][j];
           y[j] += qa[i] * s[i][j];
         }
-      // sum over the 16 row groups: lanes of equal cq
+      // sum over the 16 row groups (lanes of equal cq): inside each row of 16 lanes by DPP row
+      // rotations (8, then 4), then across the four rows by two lane exchanges
+      auto row_sum4 = [](float v) {
+        v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xf, 0xf, false));
+        v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x124, 0xf, 0xf, false));
+        return v;
+      };
 #pragma unroll
-      for (int off = 4; off < 64; off <<= 1) {
+      for (int j = 0; j < 4; ++j) {
+        r[j] = row_sum4(r[j]);
+        y[j] = row_sum4(y[j]);
+      }
+      dqk = row_sum4(dqk);
+      dg = row_sum4(dg);
+#pragma unroll
+      for (int off = 16; off < 64; off <<= 1) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           r[j] += __shfl_xor(r[j], off);
