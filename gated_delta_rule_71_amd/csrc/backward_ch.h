@@ -74,6 +74,12 @@ __device__ __forceinline__ Mma<__bf16>::F8 chl_neg8(const Mma<__bf16>::F8& f) {
 // 0.  The loads (chl_prefix_load) are issued ahead of the sums, so that their latency overlaps
 // other work.  Every thread calls both; the caller zeroes *flag and places a barrier before and
 // after chl_prefix.
+// x through an empty asm statement: values derived from it are formed where they are used.
+__device__ __forceinline__ int chl_opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 struct ChlRaw {
   uint16_t v[16];
 };
@@ -642,18 +648,39 @@ __global__ __launch_bounds__(512) void bwd_chl_kernel(BwdArgs a) {
     if (g == 0) pGn[(1 + ota) * 128 + ch] = x;
   }
 
-  // (q, k and b at this wave's accumulator positions, and log alpha again, for the outputs below)
+  // (q, k and b at this wave's accumulator positions, and log alpha again, for the outputs below;
+  // the lane's row and column come through an opaque copy of the thread index, so that the
+  // offsets are formed here rather than kept in registers, or spilled, from the kernel's start)
   uint16_t eq[4][4], ek[4][4], eb[4][4];
+  {
+    // (one loop per kind of b: a select between loads into one register would wait for the first)
+    const int tl = chl_opaque(tid) & 63, gq = tl >> 4, lq = tl & 15;
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
+    for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = 16 * ota + 4 * g + i, ch = 16 * (om0 + mi) + l16;
-      eq[mi][i] = buf_load_u16(rq, t * hqk + ch * 2);
-      ek[mi][i] = buf_load_u16(rk, t * hqk + ch * 2);
-      eb[mi][i] = a.b_kind == kChannel ? buf_load_u16(rbc, t * hdk + ch * 2)
-                                       : a.b_kind == kScalar ? buf_load_u16(rbs, t * h1) : 0;
+      for (int i = 0; i < 4; ++i) {
+        const int t = 16 * ota + 4 * gq + i, ch = 16 * (om0 + mi) + lq;
+        eq[mi][i] = buf_load_u16(rq, t * hqk + ch * 2);
+        ek[mi][i] = buf_load_u16(rk, t * hqk + ch * 2);
+      }
+    if (a.b_kind == kChannel) {
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          eb[mi][i] = buf_load_u16(rbc, (16 * ota + 4 * gq + i) * hdk + (16 * (om0 + mi) + lq) * 2);
+    } else if (a.b_kind == kScalar) {
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) eb[mi][i] = buf_load_u16(rbs, (16 * ota + 4 * gq + i) * h1);
+    } else {
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) eb[mi][i] = 0;
     }
+  }
   const ChlRaw la_raw2 = chl_prefix_load(a, rr, left, tid);
 
   // ---- the Gram gradients (masked, bf16) over the half area: dM_QK, dM_QP, dL_K, dL_P (decay
