@@ -232,12 +232,23 @@ __global__ __launch_bounds__(512) void bwd_chl_kernel(BwdArgs a) {
     const int item = tid + NT * j, t = item >> 5, i0 = (item & 31) * 4;
     uq[j] = chl_load8(rq, t * hqk + i0 * 2);
     uk[j] = chl_load8(rk, t * hqk + i0 * 2);
-    if (a.b_kind == kChannel) {
+  }
+  // (one loop per kind of b: a select between loads into one register would wait for the first)
+  if (a.b_kind == kChannel) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int item = tid + NT * j, t = item >> 5, i0 = (item & 31) * 4;
       ub[j] = chl_load8(rbc, t * hdk + i0 * 2);
-    } else {
-      ub[j].x = a.b_kind == kScalar ? buf_load_u16(rbs, t * h1) : 0u;
-      ub[j].y = 0u;
     }
+  } else if (a.b_kind == kScalar) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int t = (tid + NT * j) >> 5;
+      ub[j] = make_uint2(buf_load_u16(rbs, t * h1), 0u);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ub[j] = make_uint2(0u, 0u);
   }
   // sum_j S_0[ch][j] dS_n[ch][j]: channel tid / 4, columns (tid % 4) DV / 4 .. in 8-column pieces
   // (a piece of a tiled16 row is 16 contiguous bytes)
@@ -518,16 +529,30 @@ __global__ __launch_bounds__(512) void bwd_chl_kernel(BwdArgs a) {
       for (int i = 0; i < 4; ++i)
         sW[(16 * pta + 4 * g + i) * LDX + 16 * (pcv0 + u) + l16] = static_cast<__bf16>(dvt[u][i]);
     // (v and w at this wave's output positions, for dv and dw below)
+    // (one loop per kind of w: a select between loads into one register would wait for the first)
     uint16_t ov[2][4], ow[2][4];
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = 16 * pta + 4 * g + i;
-        const uint32_t off = t * hdv + (c0 + 16 * (pcv0 + u) + l16) * 2;
-        ov[u][i] = buf_load_u16(rv, off);
-        ow[u][i] = a.w_kind == kChannel ? buf_load_u16(rwc, off) : a.w_kind == kScalar ? buf_load_u16(rws, t * h1) : 0;
-      }
+      for (int i = 0; i < 4; ++i)
+        ov[u][i] = buf_load_u16(rv, (16 * pta + 4 * g + i) * hdv + (c0 + 16 * (pcv0 + u) + l16) * 2);
+    if (a.w_kind == kChannel) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          ow[u][i] = buf_load_u16(rwc, (16 * pta + 4 * g + i) * hdv + (c0 + 16 * (pcv0 + u) + l16) * 2);
+    } else if (a.w_kind == kScalar) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ow[u][i] = buf_load_u16(rws, (16 * pta + 4 * g + i) * h1);
+    } else {
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ow[u][i] = 0;
+    }
     lds_barrier();
     // ---- dX = M_QK^T dO + Kh dSh + L_K^T dV: dv = w . dX, dw = v . dX ----
     {
@@ -681,7 +706,7 @@ __global__ __launch_bounds__(512) void bwd_chl_kernel(BwdArgs a) {
         for (int i = 0; i < 4; ++i) eb[mi][i] = 0;
     }
   }
-  const ChlRaw la_raw2 = chl_prefix_load(a, rr, left, tid);
+  const ChlRaw la_raw2 = chl_prefix_load(a, rr, left, chl_opaque(tid));  // (offsets formed here again)
 
   // ---- the Gram gradients (masked, bf16) over the half area: dM_QK, dM_QP, dL_K, dL_P (decay
   // first: dM, dL); their upper tiles read as zeros ----
