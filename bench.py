@@ -95,14 +95,16 @@ def backward_bytes(wl):
     return n + state * (2 if wl.s0_std > 0 else 1)
 
 
-def backward_supported(wl):
-    """Whether gdr_chunk_bwd covers the workload: bf16, a scalar or no decay with d_k in
-    {32, 64, 128} and d_v up to 256, or a per-channel decay with d_k = 128 and d_v 64 or 128."""
-    if wl.dtype != "bf16":
-        return False
-    if wl.alpha == "channel":
-        return wl.DK == 128 and wl.DV in (64, 128)
-    return wl.DV <= 256 and wl.DK in (32, 64, 128)
+def backward_path(wl):
+    """Which backward gdr_chunk_bwd runs for the workload: the chunkwise adjoint for bf16 with a
+    scalar or no decay at d_k in {32, 64, 128} and d_v up to 256, or a per-channel decay at
+    d_k = 128 with d_v 64 or 128; the token adjoint for every other problem."""
+    if wl.dtype == "bf16":
+        if wl.alpha == "channel" and wl.DK == 128 and wl.DV in (64, 128):
+            return "chunkwise"
+        if wl.alpha != "channel" and wl.DV <= 256 and wl.DK in (32, 64, 128):
+            return "chunkwise"
+    return "token"
 
 
 def decode_bytes(wl):
@@ -311,7 +313,10 @@ def time_backward(wl, steps, warmup, dev):
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": gbs / PEAK_HBM_GBS, "algorithmic_bytes": nb,
                          "traffic": recorded_traffic("backward:" + wl.name),
-                         "scope": "one gdr_chunk_bwd call: chunk maps, two chains, chunk-local adjoint"}}
+                         "scope": ("one gdr_chunk_bwd call: chunk maps, two chains, chunk-local adjoint"
+                                   if backward_path(wl) == "chunkwise" else
+                                   "one gdr_chunk_bwd call: the token adjoint (forward checkpoints, "
+                                   "reverse walk, column-block sums)")}}
 
 
 def time_hooks(wl, dev, positions=64, reps=5):
@@ -448,7 +453,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true",
-                    help="skip timing gdr_chunk_bwd (run for bf16 scalar- or no-decay workloads)")
+                    help="skip timing gdr_chunk_bwd on the timed prefill workloads")
     ap.add_argument("--hooks", action="store_true",
                     help="also time the state-decomposition hook (64 positions, one sequence)")
     ap.add_argument("--no-calibration", action="store_true",
@@ -530,10 +535,13 @@ def main():
         out["decode"]["copy_reference"] = {"GB/s": cgbs, "bytes": 2 * dw.B * dw.H * dw.DK * dw.DV * 4,
                                            "decode_over_copy": gbs / cgbs}
     if not args.no_backward:
-        # every timed prefill workload that the backward covers; the first under "backward"
-        covered = [w for w in [wl] + [synth.WORKLOADS[n] for n in extra] if backward_supported(w)]
+        # every timed prefill workload; the first under "backward".  The token adjoint is tens of
+        # times slower than the chunkwise one: a few calls of it suffice
+        covered = [wl] + [synth.WORKLOADS[n] for n in extra]
         for i, bw in enumerate(covered):
-            r = time_backward(bw, args.steps, args.warmup, dev)
+            tok = backward_path(bw) == "token"
+            r = time_backward(bw, min(args.steps, 3) if tok else args.steps, 1 if tok else args.warmup, dev)
+            r["path"] = backward_path(bw)
             r["workload"] = bw.name
             progress("%s backward %.4f ms" % (bw.name, r["ms"]))
             if i == 0:

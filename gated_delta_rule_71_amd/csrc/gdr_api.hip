@@ -32,6 +32,13 @@ hipError_t launch_backward(const bf16_t* q, const bf16_t* k, const bf16_t* v, co
                            bf16_t* db, bf16_t* dw, float* dS0, int64_t B, int64_t T, int64_t H,
                            int64_t Hk, int64_t DK, int64_t DV, int alpha_kind, int b_kind, int w_kind,
                            bool decay_first, void* workspace, hipStream_t s);
+size_t backward_tok_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t DK, int64_t DV);
+hipError_t launch_backward_tok(bool io_bf16, const void* q, const void* k, const void* v, const void* la,
+                               const void* bg, const void* wg, const float* S0, const void* dO,
+                               const float* dST, void* dq, void* dk, void* dv, void* dla, void* db,
+                               void* dw, float* dS0, int64_t B, int64_t T, int64_t H, int64_t Hk,
+                               int64_t DK, int64_t DV, int alpha_kind, int b_kind, int w_kind,
+                               bool decay_first, void* workspace, hipStream_t s);
 size_t prefill_workspace_bytes(int io_dtype, int64_t nstate, int64_t T, int64_t DK, int64_t DV,
                                int alpha_kind, int b_kind, int w_kind, bool decay_first);
 }  // namespace gdr
@@ -125,7 +132,7 @@ GDR_EXPORT const char* gdr_status_string(int status) {
              "mismatch or overlapping output";
     case GDR_ERR_UNSUPPORTED:
       return "GDR_ERR_UNSUPPORTED: dk must be 16, 32, 64, 128 or 256, dv a multiple of 16 up to 256, "
-             "chunk 64; the backward also needs bf16, a scalar or no decay and dk 32, 64 or 128";
+             "chunk 64";
     case GDR_ERR_MISALIGNED: return "GDR_ERR_MISALIGNED: tensor pointers must be 16-byte aligned";
     case GDR_ERR_WORKSPACE_TOO_SMALL:
       return "GDR_ERR_WORKSPACE_TOO_SMALL: workspace below the query (for gdr_chunk_fwd_noalloc: the "
@@ -307,14 +314,17 @@ GDR_EXPORT int gdr_decode_step(const gdr_problem* p, const void* q, const void* 
 }
 
 namespace {
-bool bwd_supported(const gdr_problem* p) {
+// the chunkwise backward's shapes; every other valid problem runs the token adjoint
+bool bwd_chunkwise(const gdr_problem* p) {
   return gdr::backward_supported(p->io_dtype == GDR_BF16, p->dk, p->dv, p->alpha_kind);
 }
 }  // namespace
 
 GDR_EXPORT size_t gdr_chunk_bwd_workspace_bytes(const gdr_problem* p) {
-  if (check_problem(p) != GDR_OK || !bwd_supported(p)) return 0;
-  return gdr::backward_workspace_bytes(p->batch, p->heads, qk_heads(p), p->seqlen, p->dk, p->dv);
+  if (check_problem(p) != GDR_OK) return 0;
+  if (bwd_chunkwise(p))
+    return gdr::backward_workspace_bytes(p->batch, p->heads, qk_heads(p), p->seqlen, p->dk, p->dv);
+  return gdr::backward_tok_workspace_bytes(p->batch, p->heads, p->seqlen, p->dk, p->dv);
 }
 
 GDR_EXPORT int gdr_chunk_bwd(const gdr_problem* p, const void* q, const void* k, const void* v,
@@ -327,7 +337,6 @@ GDR_EXPORT int gdr_chunk_bwd(const gdr_problem* p, const void* q, const void* k,
   // the forward's inputs against one of the outputs (dv), then every output pairwise below
   rc = check_tensors(p, p->seqlen, q, k, v, log_alpha, b, w, dv);
   if (rc != GDR_OK) return rc;
-  if (!bwd_supported(p)) return GDR_ERR_UNSUPPORTED;
   const int64_t nstate = p->batch * p->heads;
   const int64_t rows = p->batch * p->seqlen * p->heads;
   const int64_t qk_rows = p->batch * p->seqlen * qk_heads(p);
@@ -345,21 +354,22 @@ GDR_EXPORT int gdr_chunk_bwd(const gdr_problem* p, const void* q, const void* k,
   for (const void* ptr : {(const void*)S0, dO, (const void*)dS_T, (const void*)dq, (const void*)dk,
                           dla_, db_, dw_, (const void*)dS0, (const void*)workspace})
     if (ptr && !aligned16(ptr)) return GDR_ERR_MISALIGNED;
+  const int64_t es = p->io_dtype == GDR_BF16 ? 2 : 4;
   auto gate_bytes = [&](int32_t kind, int64_t width) {
-    return kind == GDR_GATE_SCALAR ? rows * 2 : kind == GDR_GATE_CHANNEL ? rows * width * 2 : 0;
+    return kind == GDR_GATE_SCALAR ? rows * es : kind == GDR_GATE_CHANNEL ? rows * width * es : 0;
   };
-  const Range outs[] = {range_of(dq, dq ? qk_rows * p->dk * 2 : 0), range_of(dk, dk ? qk_rows * p->dk * 2 : 0),
-                        range_of(dv, rows * p->dv * 2),
+  const Range outs[] = {range_of(dq, dq ? qk_rows * p->dk * es : 0), range_of(dk, dk ? qk_rows * p->dk * es : 0),
+                        range_of(dv, rows * p->dv * es),
                         range_of(dla_, gate_bytes(p->alpha_kind, p->dk)),
                         range_of(db_, gate_bytes(p->b_kind, p->dk)),
                         range_of(dw_, gate_bytes(p->w_kind, p->dv)),
                         range_of(dS0, dS0 ? sbytes : 0)};
-  const Range ins[] = {range_of(q, qk_rows * p->dk * 2), range_of(k, qk_rows * p->dk * 2),
-                       range_of(v, rows * p->dv * 2),
+  const Range ins[] = {range_of(q, qk_rows * p->dk * es), range_of(k, qk_rows * p->dk * es),
+                       range_of(v, rows * p->dv * es),
                        range_of(gate_ptr(p->alpha_kind, log_alpha), gate_bytes(p->alpha_kind, p->dk)),
                        range_of(gate_ptr(p->b_kind, b), gate_bytes(p->b_kind, p->dk)),
                        range_of(gate_ptr(p->w_kind, w), gate_bytes(p->w_kind, p->dv)),
-                       range_of(S0, S0 ? sbytes : 0), range_of(dO, dO ? rows * p->dv * 2 : 0),
+                       range_of(S0, S0 ? sbytes : 0), range_of(dO, dO ? rows * p->dv * es : 0),
                        range_of(dS_T, dS_T ? sbytes : 0)};
   for (size_t i = 0; i < sizeof(outs) / sizeof(outs[0]); ++i) {
     for (const Range& r : ins)
@@ -370,12 +380,22 @@ GDR_EXPORT int gdr_chunk_bwd(const gdr_problem* p, const void* q, const void* k,
   const size_t need = gdr_chunk_bwd_workspace_bytes(p);
   if (workspace_bytes < need) return GDR_ERR_WORKSPACE_TOO_SMALL;
   if (need > 0 && workspace == nullptr) return GDR_ERR_INVALID_ARGUMENT;
-  using T = gdr::bf16_t;
-  const hipError_t e = gdr::launch_backward(
-      (const T*)q, (const T*)k, (const T*)v, (const T*)gate_ptr(p->alpha_kind, log_alpha),
-      (const T*)gate_ptr(p->b_kind, b), (const T*)gate_ptr(p->w_kind, w), S0, (const T*)dO, dS_T,
-      (T*)dq, (T*)dk, (T*)dv, (T*)dla_, (T*)db_, (T*)dw_, dS0, p->batch, p->seqlen, p->heads, qk_heads(p), p->dk,
-      p->dv, p->alpha_kind, p->b_kind, p->w_kind, p->order == GDR_DECAY_THEN_ERASE, workspace,
-      reinterpret_cast<hipStream_t>(stream));
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const bool df = p->order == GDR_DECAY_THEN_ERASE;
+  hipError_t e;
+  if (bwd_chunkwise(p)) {
+    using T = gdr::bf16_t;
+    e = gdr::launch_backward(
+        (const T*)q, (const T*)k, (const T*)v, (const T*)gate_ptr(p->alpha_kind, log_alpha),
+        (const T*)gate_ptr(p->b_kind, b), (const T*)gate_ptr(p->w_kind, w), S0, (const T*)dO, dS_T,
+        (T*)dq, (T*)dk, (T*)dv, (T*)dla_, (T*)db_, (T*)dw_, dS0, p->batch, p->seqlen, p->heads, qk_heads(p), p->dk,
+        p->dv, p->alpha_kind, p->b_kind, p->w_kind, df, workspace, st);
+  } else {
+    e = gdr::launch_backward_tok(p->io_dtype == GDR_BF16, q, k, v, gate_ptr(p->alpha_kind, log_alpha),
+                                 gate_ptr(p->b_kind, b), gate_ptr(p->w_kind, w), S0, dO, dS_T, dq, dk, dv,
+                                 (void*)dla_, (void*)db_, (void*)dw_, dS0, p->batch, p->seqlen, p->heads,
+                                 qk_heads(p), p->dk, p->dv, p->alpha_kind, p->b_kind, p->w_kind, df,
+                                 workspace, st);
+  }
   return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
 }

@@ -198,7 +198,8 @@ static void invalid_calls() {
   EXPECT_EQ(gdr_decode_step(&d, q, k, v, la, bb, w, static_cast<float*>(m.at(8 * X + 8)), o, nullptr),
             GDR_ERR_MISALIGNED);
   EXPECT_EQ(gdr_decode_step(&d, q, k, v, la, bb, w, static_cast<float*>(o), o, nullptr), GDR_ERR_INVALID_ARGUMENT);
-  // backward: unsupported per-channel decay, missing outputs, outputs overlapping inputs or each other
+  // backward: a per-channel decay at dk = 32 (the token adjoint) without its workspace, missing
+  // outputs, outputs overlapping inputs or each other
   gdr_problem g = problem(GDR_BF16, 1, 1, 64, 32, 32, 1, 1, 1, 0);
   void *dO = m.at(7 * X), *dq = m.at(9 * X), *dk = m.at(10 * X), *dv = m.at(11 * X), *dla = m.at(13 * X);
   void *db = m.at(14 * X), *dw = m.at(15 * X);
@@ -206,7 +207,7 @@ static void invalid_calls() {
   gdr_problem gc = g;
   gc.alpha_kind = 2;
   EXPECT_EQ(gdr_chunk_bwd(&gc, q, k, v, la, bb, w, nullptr, dO, nullptr, dq, dk, dv, dla, db, dw, dS0, nullptr, 0,
-                          nullptr), GDR_ERR_UNSUPPORTED);
+                          nullptr), GDR_ERR_WORKSPACE_TOO_SMALL);
   EXPECT_EQ(gdr_chunk_bwd(&g, q, k, v, la, bb, w, nullptr, nullptr, nullptr, dq, dk, dv, dla, db, dw, dS0, nullptr,
                           0, nullptr), GDR_ERR_INVALID_ARGUMENT);
   EXPECT_EQ(gdr_chunk_bwd(&g, q, k, v, la, bb, w, nullptr, dO, nullptr, q, dk, dv, dla, db, dw, dS0, nullptr, 0,

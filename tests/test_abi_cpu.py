@@ -243,11 +243,27 @@ def test_backward_workspace_and_validation():
     assert N.bwd_workspace_bytes(prob(order=N.DECAY_THEN_ERASE, b_kind=N.GATE_SCALAR,
                                       w_kind=N.GATE_SCALAR)) == need
     assert N.bwd_workspace_bytes(prob(dv=64)) > 0
-    # outside the backward's scope: per-channel decay at other widths, fp32, dv > 256, dk = 16
-    for p in (prob(dk=64), prob(dv=256), prob(dv=96), prob(alpha_kind=N.GATE_SCALAR, io_dtype=N.GDR_FP32),
-              prob(alpha_kind=N.GATE_SCALAR, dv=512), prob(alpha_kind=N.GATE_SCALAR, dk=16)):
-        assert N.bwd_workspace_bytes(p) == 0
-        assert bwd_call(p) == N.GDR_ERR_UNSUPPORTED
+    # every other valid problem takes the token adjoint: the state before every 8th token of
+    # every (batch, head) in fp32, and per 128-column block of the values four fp32 row
+    # gradients (dq, dk, d log alpha, db: dk wide) and four scalars per token
+    def tok_need(B=2, H=3, T=70, dk=128, dv=128):
+        nb, ncb, rows = (T + 7) // 8, (dv + 127) // 128, B * T * H
+        return r(B * H * nb * dk * dv * 4) + r(ncb * rows * 4 * dk * 4) + r(ncb * rows * 4 * 4)
+    for p, kw in ((prob(dk=64), dict(dk=64)), (prob(dv=256), dict(dv=256)), (prob(dv=96), dict(dv=96)),
+                  (prob(dk=256, dv=32), dict(dk=256, dv=32)),
+                  (prob(alpha_kind=N.GATE_SCALAR, io_dtype=N.GDR_FP32), {}),
+                  (prob(alpha_kind=N.GATE_SCALAR, dk=16), dict(dk=16)),
+                  (prob(io_dtype=N.GDR_FP32, seqlen=0), dict(T=0))):
+        assert N.bwd_workspace_bytes(p) == tok_need(**kw), kw
+    # outside every path: dv > 256
+    assert N.bwd_workspace_bytes(prob(alpha_kind=N.GATE_SCALAR, dv=512)) == 0
+    assert bwd_call(prob(alpha_kind=N.GATE_SCALAR, dv=512)) == N.GDR_ERR_UNSUPPORTED
+    # fp32 I/O: tensors of 4-byte elements (an output 256 bytes past dq's start overlaps it)
+    fp = prob(io_dtype=N.GDR_FP32)
+    fneed = tok_need()
+    assert bwd_call(fp, 20 * (1 << 32), fneed - 1) == N.GDR_ERR_WORKSPACE_TOO_SMALL
+    assert bwd_call(fp, 20 * (1 << 32), fneed, dk=bwd_ptrs()["dq"] + 2 * 70 * 3 * 128 * 2) == \
+        N.GDR_ERR_INVALID_ARGUMENT
     ws = 20 * (1 << 32)
     assert bwd_call(sp, ws, need - 1) == N.GDR_ERR_WORKSPACE_TOO_SMALL
     assert bwd_call(sp, 0, need) == N.GDR_ERR_INVALID_ARGUMENT
