@@ -167,9 +167,9 @@ def chunk_bwd(q, k, v, log_alpha=None, b=None, w=None, S0=None, do=None, dS_T=No
     final-state gradient ``dS_T`` (float32 [B,H,dk,dv] or None).  Returns a dict with dq, dk, dv
     (q's dtype), dlog_alpha, db, dw (shaped like the gates; None for an absent gate) and dS0
     (float32).  With one shared beta passed as both b and w, its gradient is db + dw.  With
-    grouped q / k heads, dq and dk are summed over the value heads that share them.  Raises
-    GdrError(GDR_ERR_UNSUPPORTED) outside bf16 with a scalar or no decay, dk in {32, 64, 128}
-    and dv <= 256."""
+    grouped q / k heads, dq and dk are summed over the value heads that share them.  Every
+    problem chunk_fwd accepts is supported: the chunkwise adjoint for the bf16 shapes of the
+    Gated DeltaNet, KDA and Gated DeltaNet-2 models, the exact token adjoint for the rest."""
     torch = _torch()
     B, T, HQ, DK = q.shape
     H, DV = v.shape[2], v.shape[-1]

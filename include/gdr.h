@@ -72,10 +72,9 @@ typedef enum { GDR_GATE_NONE = 0, GDR_GATE_SCALAR = 1, GDR_GATE_CHANNEL = 2 } gd
 typedef enum { GDR_ERASE_THEN_DECAY = 0, GDR_DECAY_THEN_ERASE = 1 } gdr_order;
 
 /* Problem description.  Set struct_size = sizeof(gdr_problem).
- * Supported by the prefill and the decode step: dk in {16, 32, 64, 128, 256},
- * dv a multiple of 16 in [16, 256], both I/O types, every gate kind and both
- * orders (GDR_ERR_UNSUPPORTED otherwise); the backward is narrower (see
- * gdr_chunk_bwd).  chunk == 64 or 0 (the same); batch, heads >= 0; seqlen >= 0
+ * Supported by the prefill, the decode step and the backward: dk in
+ * {16, 32, 64, 128, 256}, dv a multiple of 16 in [16, 256], both I/O types,
+ * every gate kind and both orders (GDR_ERR_UNSUPPORTED otherwise).  chunk == 64 or 0 (the same); batch, heads >= 0; seqlen >= 0
  * (any value: a ragged last chunk is padded with identity tokens inside the
  * kernel).  Sizes: batch, heads and seqlen below 2^31 (GDR_ERR_INVALID_ARGUMENT
  * otherwise), batch * heads below 2^25 and batch * heads * seqlen below 2^48
@@ -211,13 +210,18 @@ int gdr_decode_step(const gdr_problem* p, const void* q, const void* k, const vo
                     const void* log_alpha, const void* b, const void* w, float* S, void* o,
                     void* stream);
 
-/* Workspace bytes gdr_chunk_bwd needs for `p`; 0 for an invalid or unsupported
- * problem.  Per 64-token chunk of every (batch, head): the chunk's affine map as
- * for the per-channel forward (2 dk^2 + 2 dk dv + 132 dk + 128 dv + 20 bytes)
- * and five bf16 dk x dv arrays: the checkpoints (the state entering the chunk
- * and the gradient of the state leaving it, each as rows and transposed) and
- * the chunk's Q'^T dO; with grouped q / k heads also dq and dk per value head
- * (bf16 [B,T,H,dk] each).  Each array is 256-byte aligned. */
+/* Workspace bytes gdr_chunk_bwd needs for `p`; 0 for an invalid problem.
+ * Chunkwise adjoint (the shapes listed under gdr_chunk_bwd): per 64-token chunk
+ * of every (batch, head), the chunk's affine map as for the per-channel forward
+ * (2 dk^2 + 2 dk dv + 132 dk + 128 dv + 20 bytes) and five bf16 dk x dv arrays:
+ * the checkpoints (the state entering the chunk and the gradient of the state
+ * leaving it, each as rows and transposed) and the chunk's Q'^T dO; with
+ * grouped q / k heads also dq and dk per value head (bf16 [B,T,H,dk] each).
+ * Token adjoint (every other problem): the fp32 state before every 8th token of
+ * every (batch, head), B * H * ceil(T / 8) * dk * dv * 4 bytes, and per block of
+ * 128 value columns the fp32 column sums of four per-token row gradients,
+ * ceil(dv / 128) * B * T * H * (4 dk + 4) * 4 bytes.
+ * Each array is 256-byte aligned. */
 size_t gdr_chunk_bwd_workspace_bytes(const gdr_problem* p);
 
 /*
@@ -235,22 +239,28 @@ size_t gdr_chunk_bwd_workspace_bytes(const gdr_problem* p);
  *   workspace, workspace_bytes  device scratch of at least
  *          gdr_chunk_bwd_workspace_bytes(p) bytes, 16-byte aligned; calls that
  *          share one workspace must not overlap in time.
- * Outputs must not overlap the inputs or each other.  Supported: bf16 with
- * any erase and write gate kinds and grouped q / k heads (dq and dk are then
- * summed over the value heads that share each q / k head), and either
- *   a scalar decay or none (both orders are then the same recurrence), dk in
- *   {32, 64, 128}, dv a multiple of 16 up to 256; or
- *   a per-channel decay (the Gated DeltaNet-2 and KDA gates), either order,
- *   dk = 128 and dv 64 or 128;
- * GDR_ERR_UNSUPPORTED otherwise.
- * Method: the adjoint of the chunk form of gdr_chunk_fwd ("Recurrent Memory",
- * sections 03 and 04): the state at every chunk boundary by a forward pass over
- * the chunk maps, the gradient of the state at every boundary by the transposed
- * maps in reverse, and each chunk's input gradients from those two by matrix
- * products, the transposed triangular solve and a suffix sum of the decay
- * gradient inside the chunk.  With a per-channel decay a chunk whose prefix
- * sums of log alpha leave [-76, 76] (or are not finite) is differentiated
- * token by token from its checkpoint instead, exactly for any gate values.
+ * Outputs must not overlap the inputs or each other.  Every valid problem is
+ * supported (both I/O types, every gate kind, both orders, grouped q / k heads:
+ * dq and dk are then summed over the value heads that share each q / k head).
+ * Two methods, chosen by shape:
+ *   Chunkwise adjoint, for bf16 with a scalar decay or none (both orders are
+ *   then the same recurrence), dk in {32, 64, 128} and dv a multiple of 16 up
+ *   to 256, or a per-channel decay (the Gated DeltaNet-2 and KDA gates), either
+ *   order, dk = 128 and dv 64 or 128: the adjoint of the chunk form of
+ *   gdr_chunk_fwd ("Recurrent Memory", sections 03 and 04).  The state at
+ *   every chunk boundary by a forward pass over the chunk maps, the gradient of
+ *   the state at every boundary by the transposed maps in reverse, and each
+ *   chunk's input gradients from those two by matrix products, the transposed
+ *   triangular solve and a suffix sum of the decay gradient inside the chunk.
+ *   With a per-channel decay a chunk whose prefix sums of log alpha leave
+ *   [-76, 76] (or are not finite) is differentiated token by token from its
+ *   checkpoint instead, exactly for any gate values.
+ *   Token adjoint, for every other problem (the all-fp32 mode, dk = 16 and
+ *   256, a per-channel decay at other widths): the adjoint of the recurrence
+ *   itself ("Recurrent Memory", section 05), token by token in fp32, from
+ *   checkpoints of the state kept every 8 tokens.  Exact for any gate values;
+ *   tens of times slower than the chunkwise adjoint.
+ * Results are deterministic: every sum is taken in a fixed order.
  */
 int gdr_chunk_bwd(const gdr_problem* p, const void* q, const void* k, const void* v,
                   const void* log_alpha, const void* b, const void* w, const float* S0,
