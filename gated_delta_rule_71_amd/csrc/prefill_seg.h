@@ -1081,20 +1081,26 @@ __global__ __launch_bounds__(256) void seg_chain_kernel(SegArgs a) {
 }
 
 constexpr int kFixGroup = 8;  // chunks per correction workgroup
+constexpr int kFixRing = 4;   // chunk slots of the correction's LDS ring (inputs two chunks ahead)
 
 // ---- correction: o_c = O_c(N) + Q~_c E_s for every chunk c of segments s > 0 ----
 // One workgroup of 4 waves per (state, segment s > 0, group of up to 8 of its chunks); wave w takes
 // value column tiles 2 w, 2 w + 1 and keeps their rows of E_s^T (Ebf: transposed, each 32-channel
 // block in the pair order of seg_qt_pos) as A operands for the whole group.  O^T tile (columns
 // 16 n + 4 g + i, tokens 16 ta + l16) = O(N)^T + E^T Q~^T: On supplies the accumulators and Qt the
-// B operands, each one load contiguous across the wave; o is only written.  The next chunk's loads
-// are issued before the current chunk's products.
+// B operands; o is only written.  Each chunk's Qt and On blocks (8 KB each, contiguous) arrive in
+// a ring of four LDS slots by direct-to-LDS loads, every wave issuing a quarter of them, two chunks
+// ahead of their use: the slot refilled in iteration i held chunk i - 2, whose reads all waves
+// finished before the barrier of iteration i - 1.  So a chunk's 16 KB is read from HBM once per
+// workgroup (not once per wave) and no registers hold loads in flight; one barrier per chunk.
 __global__ __launch_bounds__(256) void seg_fix_kernel(SegArgs a) {
   using MM = Mma<__bf16>;
   using F8 = MM::F8;
   constexpr int DK = 128, DV = 128, C = kSegC;
+  constexpr int SLOT = 2 * C * DK * 2;  // Qt block, then On block
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[kFixRing * SLOT];
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, g = lane >> 4, l16 = lane & 15;
   // (32-bit index arithmetic: the grid is far below 2^31 workgroups)
   const uint32_t ngrp = static_cast<uint32_t>((a.L + kFixGroup - 1) / kFixGroup);
   const uint32_t nsm1 = static_cast<uint32_t>(a.nseg - 1);
@@ -1108,63 +1114,67 @@ __global__ __launch_bounds__(256) void seg_fix_kernel(SegArgs a) {
   const int64_t seg_end = (s + 1) * a.L < a.nch ? (s + 1) * a.L : a.nch;
   const int64_t c0 = s * a.L + static_cast<int64_t>(grp) * kFixGroup;
   const int64_t c1 = c0 + kFixGroup < seg_end ? c0 + kFixGroup : seg_end;
-  if (c0 >= c1) return;  // past the end of a shorter last segment
+  if (c0 >= c1) return;  // past the end of a shorter last segment (uniform: before any load)
+  const int n = static_cast<int>(c1 - c0);
   const int64_t bi = bh / a.H, hi = bh % a.H;
   const uint32_t hdv = static_cast<uint32_t>(a.H * DV * 2);
   const __bf16* eb = a.Ebf + (bh * a.nseg + s) * DV * DK;
   F8 ef[2][4];
 #pragma unroll
-  for (int n = 0; n < 2; ++n)
+  for (int nn = 0; nn < 2; ++nn)
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
-      ef[n][kb] = *reinterpret_cast<const F8*>(eb + (16 * (2 * wave + n) + l16) * DK + 32 * kb + 8 * g);
+      ef[nn][kb] = *reinterpret_cast<const F8*>(eb + (16 * (2 * wave + nn) + l16) * DK + 32 * kb + 8 * g);
 
-  auto load = [&](int64_t c, F8 (&q)[2][4], uint2 (&o)[2][2]) {
-    const __bf16* qt = a.Qt + (bh * a.nch + c) * C * DK;
-    const __bf16* on = a.On + (bh * a.nch + c) * C * DV;
+  // chunk c0 + i (clamped to the group's last chunk, so that every iteration issues the same
+  // number of loads) into slot `slot`: this wave's 1 KB pieces 2 wave, 2 wave + 1 of each block
+  auto issue = [&](int i, int slot) {
+    const int64_t c = c0 + (i < n ? i : n - 1);
+    const unsigned char* qt = reinterpret_cast<const unsigned char*>(a.Qt + (bh * a.nch + c) * C * DK);
+    const unsigned char* on = reinterpret_cast<const unsigned char*>(a.On + (bh * a.nch + c) * C * DV);
+    unsigned char* dst = ring + slot * SLOT;
 #pragma unroll
-    for (int ta = 0; ta < 2; ++ta) {
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) q[ta][kb] = *reinterpret_cast<const F8*>(qt + ((ta * 4 + kb) * 64 + lane) * 8);
-#pragma unroll
-      for (int n = 0; n < 2; ++n) o[ta][n] = *reinterpret_cast<const uint2*>(on + ((ta * 8 + 2 * wave + n) * 64 + lane) * 4);
+    for (int p = 0; p < 2; ++p) {
+      const int piece = 2 * wave + p;
+      seg_dma16(qt + piece * 1024, 1024, dst + piece * 1024, 16 * lane);
+      seg_dma16(on + piece * 1024, 1024, dst + C * DK * 2 + piece * 1024, 16 * lane);
     }
   };
-  auto apply = [&](int64_t c, const F8 (&q)[2][4], const uint2 (&o)[2][2]) {
-    const int64_t t0 = c * C;
+  constexpr int kLoadsPerChunk = 4;  // direct-to-LDS loads one wave issues per chunk
+  // s_waitcnt immediate: at most 2 chunks' loads outstanding (gfx9 encoding: vmcnt bits 3:0 and
+  // 15:14, expcnt and lgkmcnt at their maxima); loads complete in order, so chunk i's are done
+  constexpr int kWaitRing = 0x0F70 | (2 * kLoadsPerChunk & 0xF) | (((2 * kLoadsPerChunk >> 4) & 3) << 14);
+
+  issue(0, 0);
+  issue(1, 1);
+  for (int i = 0; i < n; ++i) {
+    issue(i + 2, (i + 2) & (kFixRing - 1));
+    __builtin_amdgcn_s_waitcnt(kWaitRing);
+    lds_barrier_keep_vm();  // every wave's pieces of chunk i are in
+    const unsigned char* slot = ring + (i & (kFixRing - 1)) * SLOT;
+    const int64_t t0 = (c0 + i) * C;
     const auto ro = make_rsrc(a.o + ((bi * a.T + t0) * a.H + hi) * DV, wy_range(a.T - t0, a.H, DV));
 #pragma unroll
     for (int ta = 0; ta < 2; ++ta) {
+      F8 q[4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) q[kb] = *reinterpret_cast<const F8*>(slot + ((ta * 4 + kb) * 64 + lane) * 16);
       const uint32_t t = static_cast<uint32_t>(16 * ta + l16);
 #pragma unroll
-      for (int n = 0; n < 2; ++n) {
+      for (int nn = 0; nn < 2; ++nn) {
         float o4[4];
-        unpack4(o[ta][n], o4);
+        unpack4(*reinterpret_cast<const uint2*>(slot + C * DK * 2 + ((ta * 8 + 2 * wave + nn) * 64 + lane) * 8), o4);
         f32x4 acc;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] = o4[i];
+        for (int e = 0; e < 4; ++e) acc[e] = o4[e];
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) acc = MM::mma8(ef[n][kb], q[ta][kb], acc);
+        for (int kb = 0; kb < 4; ++kb) acc = MM::mma8(ef[nn][kb], q[kb], acc);
         float r4[4] = {acc[0], acc[1], acc[2], acc[3]};
-        buf_store8(ro, t * hdv + (16 * (2 * wave + n) + 4 * g) * 2, pack4(r4));
+        buf_store8(ro, t * hdv + (16 * (2 * wave + nn) + 4 * g) * 2, pack4(r4));
       }
     }
-  };
-  // two register sets, alternately loaded one chunk ahead (no copies between them, so the wait
-  // for one set's loads does not wait for the other's).  The loads are unconditional (past the
-  // group's end they repeat a chunk of it, unused), so that the compiler's count of loads in flight
-  // is the same on every path and its wait before a use leaves the other set's loads in flight.
-  F8 qa[2][4], qb[2][4];
-  uint2 oa[2][2], ob[2][2];
-  load(c0, qa, oa);
-  for (int64_t c = c0; c < c1; c += 2) {
-    load(c + 1 < c1 ? c + 1 : c, qb, ob);
-    __builtin_amdgcn_sched_barrier(0);  // (issue the loads before the products)
-    apply(c, qa, oa);
-    load(c + 2 < c1 ? c + 2 : c, qa, oa);
-    __builtin_amdgcn_sched_barrier(0);
-    if (c + 1 < c1) apply(c + 1, qb, ob);
   }
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // the clamped loads past the group land before exit
 }
 
 }  // namespace gdr
