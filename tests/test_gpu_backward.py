@@ -489,3 +489,21 @@ def test_backward_d256_workload_sampled(dev):
         else:
             sel[n] = t[bi.to(t.device), :, hi.to(t.device)].unsqueeze(2)
     compare(sel, ref, "gdn_d256 sampled")
+
+
+@pytest.mark.parametrize("order", ["erase_then_decay", "decay_then_erase"])
+def test_backward_token_adjoint_extreme_gates(dev, order):
+    """The token adjoint has no chunk exponents to keep in range: decays of e^-60 (log alpha =
+    -60 over a stretch of tokens and channels), no decay (log alpha = 0) and full erasure (b = 1)
+    beside ordinary gates, in the all-fp32 mode at d_k = 64, against the fp64 adjoint."""
+    x = tok_case("gdn2", 64, 64, "fp32", B=1, H=2, T=45, seed=291)
+    la = x["log_alpha"].clone()
+    la[:, 10:20, :, :32] = -60.0
+    la[:, 30:38, :, 16:] = 0.0
+    x["log_alpha"] = la
+    b = x["b"].clone()
+    b[:, 5:9] = 1.0
+    x["b"] = b
+    say("backward token adjoint extreme gates", order)
+    o = 0 if order == "erase_then_decay" else 1
+    compare(run(x, dev, order), reference(x, order=o), "tok extreme %s" % order, rel_tol=REL32)
