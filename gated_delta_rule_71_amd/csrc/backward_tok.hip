@@ -16,7 +16,7 @@
 // and dv = w . dx, dw = v . dx, db = k . dc, d log alpha = a . da (a scalar gate sums its
 // channels).  Scalar gates: b, w or a is one value for every channel.
 //
-// Layout.  One workgroup of 8 waves per (batch, head) and block of up to 128 value columns; wave w
+// Layout.  One workgroup of 4 waves per (batch, head) and block of up to 64 value columns; wave w
 // holds columns 16 w .. 16 w + 15 of S and of G, lane l rows R (l / 4) .. R (l / 4) + R - 1
 // (R = dk / 16) and columns 4 (l % 4) .. 4 (l % 4) + 3 of them.  Sums over dk are the lane's own
 // rows and four exchanges across lanes of equal l % 4; sums over the value columns are the lane's
@@ -48,8 +48,9 @@ struct TokBwdArgs {
 namespace {
 
 constexpr int kTokB = 8;     // tokens per block (checkpoint interval)
-constexpr int kTokCols = 128;  // value columns per workgroup
-constexpr int kTokThreads = 512;
+constexpr int kTokCols = 64;  // value columns per workgroup
+constexpr int kTokThreads = 256;
+constexpr int kTokWaves = kTokThreads / 64;
 
 template <int DK>
 struct TokLds {
@@ -58,9 +59,9 @@ struct TokLds {
   static constexpr int iQ = 0, iK = iQ + kTokB * DK, iA = iK + kTokB * DK, iB = iA + kTokB * DK;
   static constexpr int iV = iB + kTokB * DK, iW = iV + kTokB * kTokCols, iD = iW + kTokB * kTokCols;
   static constexpr int iEnd = iD + kTokB * kTokCols;
-  // per token, two buffers: each wave's partial rows [8][4][DK] and scalars [8][4]
-  static constexpr int rRow = iEnd, rSc = rRow + 2 * 8 * 4 * DK;
-  static constexpr int floats = rSc + 2 * 8 * 4;
+  // per token, two buffers: each wave's partial rows [waves][4][DK] and scalars [waves][4]
+  static constexpr int rRow = iEnd, rSc = rRow + 2 * kTokWaves * 4 * DK;
+  static constexpr int floats = rSc + 2 * kTokWaves * 4;
 };
 
 template <int M>
@@ -131,7 +132,7 @@ __device__ __forceinline__ void tok_forward(float (&s)[DK / 16][4], const float*
 template <typename IO, int DK, bool DF>
 __global__ __launch_bounds__(kTokThreads) void bwd_tok_kernel(TokBwdArgs a) {
   constexpr int R = DK / 16;
-  constexpr bool CK_REG = R <= 4;  // the block's checkpoint kept in registers (else reread)
+  constexpr bool CK_REG = R <= 8;  // the block's checkpoint kept in registers (else reread)
   using LY = TokLds<DK>;
   __shared__ __attribute__((aligned(16))) float L[LY::floats];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -229,8 +230,8 @@ __global__ __launch_bounds__(kTokThreads) void bwd_tok_kernel(TokBwdArgs a) {
     load_block(t0, n);
     __syncthreads();
     for (int tt = n - 1; tt >= 0; --tt, par ^= 1) {
-      float* red = L + LY::rRow + par * (8 * 4 * DK);
-      float* sred = L + LY::rSc + par * (8 * 4);
+      float* red = L + LY::rRow + par * (kTokWaves * 4 * DK);
+      float* sred = L + LY::rSc + par * (kTokWaves * 4);
       if (active) {
         // the state before token tt
         if constexpr (CK_REG) {

@@ -219,8 +219,8 @@ int gdr_decode_step(const gdr_problem* p, const void* q, const void* k, const vo
  * grouped q / k heads also dq and dk per value head (bf16 [B,T,H,dk] each).
  * Token adjoint (every other problem): the fp32 state before every 8th token of
  * every (batch, head), B * H * ceil(T / 8) * dk * dv * 4 bytes, and per block of
- * 128 value columns the fp32 column sums of four per-token row gradients,
- * ceil(dv / 128) * B * T * H * (4 dk + 4) * 4 bytes.
+ * 64 value columns the fp32 column sums of four per-token row gradients,
+ * ceil(dv / 64) * B * T * H * (4 dk + 4) * 4 bytes.
  * Each array is 256-byte aligned. */
 size_t gdr_chunk_bwd_workspace_bytes(const gdr_problem* p);
 

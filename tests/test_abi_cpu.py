@@ -244,10 +244,10 @@ def test_backward_workspace_and_validation():
                                       w_kind=N.GATE_SCALAR)) == need
     assert N.bwd_workspace_bytes(prob(dv=64)) > 0
     # every other valid problem takes the token adjoint: the state before every 8th token of
-    # every (batch, head) in fp32, and per 128-column block of the values four fp32 row
+    # every (batch, head) in fp32, and per 64-column block of the values four fp32 row
     # gradients (dq, dk, d log alpha, db: dk wide) and four scalars per token
     def tok_need(B=2, H=3, T=70, dk=128, dv=128):
-        nb, ncb, rows = (T + 7) // 8, (dv + 127) // 128, B * T * H
+        nb, ncb, rows = (T + 7) // 8, (dv + 63) // 64, B * T * H
         return r(B * H * nb * dk * dv * 4) + r(ncb * rows * 4 * dk * 4) + r(ncb * rows * 4 * 4)
     for p, kw in ((prob(dk=64), dict(dk=64)), (prob(dv=256), dict(dv=256)), (prob(dv=96), dict(dv=96)),
                   (prob(dk=256, dv=32), dict(dk=256, dv=32)),
