@@ -464,7 +464,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the recurrence runs per (batch, head) state with no "
-              "communication, and this build has no multi-GPU path (--gpus %d requested)"
+              "communication, and the library has no multi-GPU path (--gpus %d requested)"
               % args.gpus, file=sys.stderr)
         sys.exit(2)
 
