@@ -24,8 +24,8 @@
 //
 // Order.  A first pass walks the tokens forward from S0 and stores the state before every 8th
 // token (the checkpoints).  The second walks the blocks of 8 tokens backward: for each token, last
-// first, it recomputes the state before it from the block's checkpoint and applies the adjoint
-// above.  Each token's column sums of the four row gradients (dq, dk, d log alpha, db) and the
+// first, it recomputes the state before it from the block's checkpoint, or from the state before
+// the block's fifth token (formed once per block), and applies the adjoint above.  Each token's column sums of the four row gradients (dq, dk, d log alpha, db) and the
 // scalar gates' sums are written per column block; a last kernel adds the blocks (and, with grouped
 // heads, the value heads of each q / k head) in a fixed order, so results do not depend on timing.
 #include "gdr_common.h"
@@ -48,6 +48,7 @@ struct TokBwdArgs {
 namespace {
 
 constexpr int kTokB = 8;     // tokens per block (checkpoint interval)
+constexpr int kTokMid = 4;   // the block's second restart point, kept in registers
 constexpr int kTokCols = 64;  // value columns per workgroup
 constexpr int kTokThreads = 256;
 constexpr int kTokWaves = kTokThreads / 64;
@@ -211,6 +212,7 @@ __global__ __launch_bounds__(kTokThreads) void bwd_tok_kernel(TokBwdArgs a) {
         g[i][c] = a.dST ? a.dST[(bh * DK + d0 + i) * DV + col0 + c] : 0.f;
   }
   float ckr[CK_REG ? R : 1][4];
+  float mid[R][4];
   int par = 0;
   for (int64_t j = nb - 1; j >= 0; --j) {
     const int64_t t0 = j * kTokB;
@@ -229,12 +231,39 @@ __global__ __launch_bounds__(kTokThreads) void bwd_tok_kernel(TokBwdArgs a) {
     __syncthreads();
     load_block(t0, n);
     __syncthreads();
+    // the state before token kTokMid of the block, from the checkpoint: tokens kTokMid .. n - 1
+    // restart from it, tokens 0 .. kTokMid - 1 from the checkpoint (16 forward steps a block
+    // instead of 28)
+    if (active && n > kTokMid) {
+      if constexpr (CK_REG) {
+#pragma unroll
+        for (int i = 0; i < R; ++i)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) mid[i][c] = ckr[i][c];
+      } else {
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+          const float4 u = *reinterpret_cast<const float4*>(ckp + i * DV);
+          mid[i][0] = u.x;
+          mid[i][1] = u.y;
+          mid[i][2] = u.z;
+          mid[i][3] = u.w;
+        }
+      }
+      for (int u = 0; u < kTokMid; ++u) tok_forward<DK, DF>(mid, L, u, d0, lc0);
+    }
     for (int tt = n - 1; tt >= 0; --tt, par ^= 1) {
       float* red = L + LY::rRow + par * (kTokWaves * 4 * DK);
       float* sred = L + LY::rSc + par * (kTokWaves * 4);
       if (active) {
         // the state before token tt
-        if constexpr (CK_REG) {
+        const int u0 = tt >= kTokMid ? kTokMid : 0;
+        if (tt >= kTokMid) {
+#pragma unroll
+          for (int i = 0; i < R; ++i)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) s[i][c] = mid[i][c];
+        } else if constexpr (CK_REG) {
 #pragma unroll
           for (int i = 0; i < R; ++i)
 #pragma unroll
@@ -249,7 +278,7 @@ __global__ __launch_bounds__(kTokThreads) void bwd_tok_kernel(TokBwdArgs a) {
             s[i][3] = u.w;
           }
         }
-        for (int u = 0; u < tt; ++u) tok_forward<DK, DF>(s, L, u, d0, lc0);
+        for (int u = u0; u < tt; ++u) tok_forward<DK, DF>(s, L, u, d0, lc0);
 
         const float* kq = L + LY::iQ + tt * DK + d0;
         const float* kk = L + LY::iK + tt * DK + d0;
